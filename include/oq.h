@@ -1,0 +1,221 @@
+/*
+ * oq.h -- C ABI of the rotated low-bit linear layer for AMD MI355X (gfx950).
+ *
+ * The layer (CentriQ, arXiv 2610.06260, Sec. 4.2 Eq. 5 and App. B.2 Eq. 9;
+ * OrbitQuant PR #25, "Default changes" and "Runtime work"):
+ *
+ *     y_t = alpha_t * sum_g s_w[o,g] * (q_a . q_w)_g  +  m_t * w1[o]  +  b[o]
+ *     q_a = Q_a( R (x_t - m_t 1) )
+ *
+ * R is a randomised permuted block-Hadamard rotation (one or two rounds of
+ * gather -> +-1 signs -> normalised Sylvester blocks of h = 32..1024) or a set
+ * of dense per-32-block transforms (WUSH review, "Core claim"); Q_a is the
+ * per-token absmax quantizer of CentriQ Eq. 1 (8, 6 or 4 bits) or MXFP4
+ * (E2M1 elements, one E8M0 scale per 32); weights are symmetric INT4 with
+ * one fp32 scale per row and group of input columns, or MXFP4.
+ *
+ * Conventions shared by every call
+ *   - Return value: OQ_OK (0) or one of the OQ_ERR_* codes.  On error nothing
+ *     has been enqueued; oq_last_error() returns a message for the calling
+ *     thread.  There is no fallback path: an unsupported request fails
+ *     (model card FLUX.1-schnell-OrbitQuant-W4A4, "Limitations": the fused
+ *     runtime fails loudly when its kernel is unavailable).
+ *   - Every data pointer is device memory owned by the caller.  The library
+ *     allocates no device memory except where a call says so
+ *     (oq_linear_fused with ws == NULL is rejected, not allocated).
+ *     Descriptor structs (oq_rot) are host memory, read during the call only.
+ *   - Calls are asynchronous on the caller's stream; none synchronises.
+ *   - Matrices are row-major.  Leading dimensions are in elements unless the
+ *     name ends in _bytes.  bfloat16 values are passed as uint16_t bits.
+ *   - Alignment: x, y and code/weight pointers 16 bytes; leading dimensions
+ *     such that every row starts 16-byte aligned.  Violations give
+ *     OQ_ERR_ALIGNMENT.
+ *   - Thread safety: calls may be made from several host threads; calls on
+ *     one stream execute in order.
+ */
+#ifndef OQ_H
+#define OQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  OQ_OK = 0,
+  OQ_ERR_INVALID_ARG = 1,   /* null pointer, bad size, bad enum value       */
+  OQ_ERR_UNSUPPORTED = 2,   /* well-formed request this build does not run  */
+  OQ_ERR_ALIGNMENT = 3,     /* pointer or leading dimension misaligned      */
+  OQ_ERR_WORKSPACE = 4,     /* workspace missing or too small               */
+  OQ_ERR_HIP = 5            /* the HIP runtime reported a launch error      */
+};
+
+/* rotation kinds */
+enum { OQ_ROT_RPBH = 1, OQ_ROT_DENSE32 = 2 };
+
+/* activation code formats (the value is the bit width for integer codes) */
+enum { OQ_A8 = 8, OQ_A6 = 6, OQ_A4 = 4, OQ_MXFP4 = 0x104 };
+
+/* weight formats for oq_quant_weight */
+enum { OQ_W4 = 4, OQ_W_MXFP4 = 0x104 };
+
+/*
+ * Rotation descriptor (host struct, device arrays).
+ *
+ * OQ_ROT_RPBH -- OrbitQuant PR #25 "Default changes" (independent extra
+ *   rounds); CentriQ related-work paragraph (randomly permuted block-Hadamard
+ *   basis); model card "Artifact Files" (stored deterministic rotation
+ *   metadata).  Round r maps v to B_h D_{s_r} P_{pi_r} v:
+ *     u[i] = signs[r][i] * v[perm[r][i]]    (gather over the whole width d)
+ *     v    = (1/sqrt h) H_h u  per block of h consecutive coordinates.
+ *   block: power of two in [32, 1024]; d % block == 0; rounds in {1, 2};
+ *   perm: int32 [rounds][d], each row a permutation of 0..d-1 (not checked);
+ *   signs: int8 [rounds][d] in {-1, +1}.
+ *   The float32 results follow one fixed order: butterfly stages of stride
+ *   1, 2, ..., h/2, each add/subtract rounded once, then a multiply by
+ *   RN32(1/sqrt h).
+ *
+ * OQ_ROT_DENSE32 -- WUSH review "Core claim": one transform per 32-block.
+ *   mats: bfloat16 [d/32][32][32] row-major, v_b = T_b x_b.  d % 32 == 0.
+ *   For weights (oq_quant_weight) mats_w is used instead: float32
+ *   [d/32][32][32], the inverse-transposes T_b^{-T}.
+ *   Activation-side float32 results are the exact value of T_b x_b rounded
+ *   once to float32 (bf16 x bf16 products summed in float64, which is exact
+ *   for ordinary activations).
+ */
+typedef struct {
+  int32_t kind;
+  int32_t d;
+  int32_t block;
+  int32_t rounds;
+  const int32_t *perm;
+  const int8_t *signs;
+  const uint16_t *mats;
+  const float *mats_w;
+} oq_rot;
+
+/* Message of the last failed call on this thread ("" if none). */
+const char *oq_last_error(void);
+
+/*
+ * oq_center -- CentriQ Sec. 4.2 Eq. 4: per-token mean and centered token.
+ *   mean[t] = RN32(RN64(sum_j x[t][j]) / d), the sum formed in float64
+ *             (exact whenever the row's exponent spread allows, which holds
+ *             for ordinary activations);
+ *   xc[t][j] = RN32(x[t][j] - mean[t]).
+ * x: bf16 [M][ldx]; xc: float32 [M][ldxc] (may be NULL to compute the mean
+ * only); mean: float32 [M].  M >= 0 (M == 0 enqueues nothing); 1 <= d <= 16384.
+ */
+int oq_center(const uint16_t *x, int64_t M, int32_t d, int64_t ldx,
+              float *xc, int64_t ldxc, float *mean, hipStream_t stream);
+
+/*
+ * oq_rotate -- the rotation of the online activation path (OrbitQuant PR #25
+ * "Runtime work": the whole pre-rotation in one kernel) with float32 output,
+ * optionally after centering (CentriQ Eq. 4-5: rotate the centered token).
+ * rot: required (RPBH or DENSE32); rot->d is the width.
+ * x: bf16 [M][ldx]; y: float32 [M][ldy]; mean: float32 [M], required iff
+ * center != 0 (DENSE32 does not support centering).
+ */
+int oq_rotate(const oq_rot *rot, const uint16_t *x, int64_t M, int64_t ldx,
+              int center, float *mean, float *y, int64_t ldy, hipStream_t stream);
+
+/*
+ * oq_quant_act -- fused (center) -> rotate -> quantize -> pack for the
+ * activations: CentriQ Eq. 1 (symmetric per-token absmax, alpha_t = r_t/qmax,
+ * qmax = 2^{b-1}-1) and OrbitQuant's absmax A8; MXFP4 per WUSH review.
+ *   codes for q = clamp(RNE(RN32(v * RN32(qmax / a))), -qmax, qmax) with
+ *   a = max(max_j |v_tj|, RN32(1e-10)) (model card: activation normalization
+ *   epsilon 1e-10); scale[t] = RN32(a / qmax).
+ * afmt OQ_A8, OQ_A6: int8 codes [M][ldc_bytes]; OQ_A4: two codes per byte,
+ *   element 2i in bits 3..0, two's complement, [M][ldc_bytes >= d/2];
+ *   scale float32 [M]; e8m0 must be NULL.
+ * afmt OQ_MXFP4 (rot->kind must be OQ_ROT_DENSE32, center == 0): E2M1 codes
+ *   two per byte as above, sign in bit 3; e8m0 uint8 [M][d/32] with
+ *   e = clamp(floor(log2 amax) - 2, -127, 127), byte = e + 127; scale NULL.
+ * rot may be NULL (no rotation; integer formats only, d = ldx's row width
+ *   given by the d argument).  mean: float32 [M], required iff center != 0.
+ */
+int oq_quant_act(const uint16_t *x, int64_t M, int32_t d, int64_t ldx,
+                 const oq_rot *rot, int center, int afmt,
+                 void *codes, int64_t ldc_bytes, float *scale, uint8_t *e8m0,
+                 float *mean, hipStream_t stream);
+
+/*
+ * oq_quant_weight -- offline weight path (CentriQ Sec. 3 "Hadamard
+ * rotation": W x = (W H^T)(H x); App. B.1: the weight absorbs P^T H^T;
+ * Eq. 4: w1 = W 1 in float32 from the unquantized weight).
+ *   Each row w of W [N][ldw] (float32) becomes R w (the same rotation as the
+ *   activations; for DENSE32 the inverse-transposes rot->mats_w are applied,
+ *   in float64 with one rounding to float32), then:
+ *   wfmt OQ_W4: symmetric absmax INT4 per (row, group of `group` input
+ *     columns), codes packed two per byte [N][K/2], scales float32 [N][K/group];
+ *   wfmt OQ_W_MXFP4: E2M1 codes [N][K/2] and E8M0 bytes [N][K/32] (group 32).
+ *   w1 (nullable): float32 [N], RN32 of the row sum of the input W (float64
+ *   accumulation).  rot may be NULL (no rotation).
+ * group: multiple of 32 dividing K (OQ_W4); K % 32 == 0.
+ */
+int oq_quant_weight(const float *w, int32_t N, int32_t K, int64_t ldw,
+                    const oq_rot *rot, int wfmt, int32_t group,
+                    uint8_t *codes, void *scales, float *w1, hipStream_t stream);
+
+/*
+ * oq_gemm_w4a8 -- int8-coded activations (OQ_A8 or OQ_A6 codes) times packed
+ * INT4 weights with the fp32 epilogue of CentriQ Eq. 5 / Eq. 9:
+ *   y[t][o] = bf16_RNE( a_scale[t] * sum_g w_scale[o][g] * acc_g[t][o]
+ *                       + mean[t] * w1[o] + bias[o] )
+ *   acc_g = exact int32 sum over the group's input columns.
+ * qa int8 [M][lda]; a_scale float32 [M]; w uint8 [N][K/2] (canonical
+ * nibbles); w_scale float32 [N][K/group]; mean and w1 both NULL or both set;
+ * bias nullable; y bf16 [M][ldy].  group: multiple of 32 dividing K.
+ * ws/ws_bytes: optional scratch, see oq_workspace_bytes(OQ_OP_GEMM_W4A8, ...).
+ */
+int oq_gemm_w4a8(const int8_t *qa, int64_t lda, const float *a_scale, int64_t M, int32_t K,
+                 const uint8_t *w, const float *w_scale, int32_t N, int32_t group,
+                 const float *mean, const float *w1, const float *bias,
+                 uint16_t *y, int64_t ldy, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * oq_gemm_w4a4 -- 4-bit activations times 4-bit weights.
+ *   afmt OQ_A4: qa nibbles [M][lda_bytes], a_scale float32 [M]; w canonical
+ *     INT4 nibbles [N][K/2], w_scale float32 [N][K/group]; epilogue as
+ *     oq_gemm_w4a8.
+ *   afmt OQ_MXFP4: qa E2M1 nibbles, a_scale uint8 E8M0 [M][K/32]; w E2M1
+ *     nibbles [N][K/2], w_scale uint8 E8M0 [N][K/32]; group must be 32;
+ *     y = bf16_RNE( sum_blocks 2^(ea+ew) sum_k fp4(a) fp4(w) + bias[o] );
+ *     mean/w1 must be NULL.
+ */
+int oq_gemm_w4a4(int afmt, const uint8_t *qa, int64_t lda_bytes, const void *a_scale,
+                 int64_t M, int32_t K, const uint8_t *w, const void *w_scale,
+                 int32_t N, int32_t group, const float *mean, const float *w1,
+                 const float *bias, uint16_t *y, int64_t ldy,
+                 void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * oq_linear_fused -- the whole layer: oq_quant_act into the workspace, then
+ * the matching GEMM, on one stream (CentriQ App. B.2: prologue quantizes
+ * each token tile once; rank-1 term and bias in the GEMM epilogue).
+ * afmt OQ_A8/OQ_A6/OQ_A4 with an RPBH rotation (or NULL), optional centering
+ * (then w1 is required); OQ_MXFP4 with a DENSE32 rotation and E8M0 w_scale.
+ * ws: device scratch of at least oq_workspace_bytes(OQ_OP_LINEAR, M, K, N, afmt).
+ */
+int oq_linear_fused(const uint16_t *x, int64_t M, int32_t K, int64_t ldx,
+                    const oq_rot *rot, int center, int afmt,
+                    const uint8_t *w, const void *w_scale, int32_t N, int32_t group,
+                    const float *w1, const float *bias, uint16_t *y, int64_t ldy,
+                    void *ws, size_t ws_bytes, hipStream_t stream);
+
+enum { OQ_OP_GEMM_W4A8 = 1, OQ_OP_GEMM_W4A4 = 2, OQ_OP_LINEAR = 3 };
+
+/* Scratch bytes a call needs (0 if none).  Pure host function. */
+size_t oq_workspace_bytes(int op, int64_t M, int32_t K, int32_t N, int afmt);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OQ_H */

@@ -1,0 +1,230 @@
+"""ctypes binding of liboq (include/oq.h): argument marshalling only.
+
+Every function here has the name of the C entry point it calls.  Tensors are
+PyTorch tensors on a HIP device (PyTorch provides device memory and the
+current stream); outputs that are not supplied are allocated with
+``torch.empty``.  All arithmetic runs in the library's HIP kernels; there is
+no other code path.  A non-zero status raises :class:`OQError`.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liboq.so")
+
+OQ_OK, OQ_ERR_INVALID_ARG, OQ_ERR_UNSUPPORTED, OQ_ERR_ALIGNMENT, OQ_ERR_WORKSPACE, OQ_ERR_HIP = range(6)
+OQ_ROT_RPBH, OQ_ROT_DENSE32 = 1, 2
+OQ_A8, OQ_A6, OQ_A4, OQ_MXFP4 = 8, 6, 4, 0x104
+OQ_W4, OQ_W_MXFP4 = 4, 0x104
+OQ_OP_GEMM_W4A8, OQ_OP_GEMM_W4A4, OQ_OP_LINEAR = 1, 2, 3
+
+
+class OQError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[oq error {code}] {msg}")
+        self.code = code
+
+
+class oq_rot(ctypes.Structure):
+    _fields_ = [
+        ("kind", ctypes.c_int32),
+        ("d", ctypes.c_int32),
+        ("block", ctypes.c_int32),
+        ("rounds", ctypes.c_int32),
+        ("perm", ctypes.c_void_p),
+        ("signs", ctypes.c_void_p),
+        ("mats", ctypes.c_void_p),
+        ("mats_w", ctypes.c_void_p),
+    ]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"liboq.so is not built ({LIB_PATH}); run __graft_entry__.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    sig = {
+        "oq_last_error": ([], ctypes.c_char_p),
+        "oq_center": ([vp, i64, i32, i64, vp, i64, vp, vp], ctypes.c_int),
+        "oq_rotate": ([vp, vp, i64, i64, ctypes.c_int, vp, vp, i64, vp], ctypes.c_int),
+        "oq_quant_act": ([vp, i64, i32, i64, vp, ctypes.c_int, ctypes.c_int, vp, i64, vp, vp, vp, vp], ctypes.c_int),
+        "oq_quant_weight": ([vp, i32, i32, i64, vp, ctypes.c_int, i32, vp, vp, vp, vp], ctypes.c_int),
+        "oq_gemm_w4a8": ([vp, i64, vp, i64, i32, vp, vp, i32, i32, vp, vp, vp, vp, i64, vp, sz, vp], ctypes.c_int),
+        "oq_gemm_w4a4": ([ctypes.c_int, vp, i64, vp, i64, i32, vp, vp, i32, i32, vp, vp, vp, vp, i64, vp, sz, vp], ctypes.c_int),
+        "oq_linear_fused": ([vp, i64, i32, i64, vp, ctypes.c_int, ctypes.c_int, vp, vp, i32, i32, vp, vp, vp, i64, vp, sz, vp], ctypes.c_int),
+        "oq_workspace_bytes": ([ctypes.c_int, i64, i32, i32, ctypes.c_int], sz),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
+    return lib
+
+
+_lib = _load()
+EXPORTED = ("oq_last_error", "oq_center", "oq_rotate", "oq_quant_act", "oq_quant_weight",
+            "oq_gemm_w4a8", "oq_gemm_w4a4", "oq_linear_fused", "oq_workspace_bytes")
+
+
+def lib():
+    return _lib
+
+
+def _check(rc: int):
+    if rc != OQ_OK:
+        raise OQError(rc, _lib.oq_last_error().decode("utf-8", "replace"))
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t: torch.Tensor):
+    if not t.is_cuda:
+        raise OQError(OQ_ERR_INVALID_ARG, "tensors must live on the GPU")
+    return t.device
+
+
+def _bits16(x: torch.Tensor) -> torch.Tensor:
+    if x.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise OQError(OQ_ERR_INVALID_ARG, "bfloat16 input expected (or its 16-bit pattern)")
+    return x
+
+
+class Rotation:
+    """Host descriptor plus the device arrays it points to (kept alive here)."""
+
+    def __init__(self, kind: int, d: int, block: int = 0, rounds: int = 0, perm=None, signs=None,
+                 mats=None, mats_w=None):
+        self.kind, self.d, self.block, self.rounds = kind, d, block, rounds
+        self.perm, self.signs, self.mats, self.mats_w = perm, signs, mats, mats_w
+        self.c = oq_rot(kind, d, block, rounds, _p(perm), _p(signs), _p(mats), _p(mats_w))
+
+    @staticmethod
+    def rpbh(perm: torch.Tensor, signs: torch.Tensor, block: int) -> "Rotation":
+        perm = perm.to(torch.int32).contiguous()
+        signs = signs.to(torch.int8).contiguous()
+        return Rotation(OQ_ROT_RPBH, perm.shape[-1], block, perm.shape[0], perm=perm, signs=signs)
+
+    @staticmethod
+    def dense32(mats_bits: torch.Tensor, mats_w: Optional[torch.Tensor] = None) -> "Rotation":
+        d = mats_bits.shape[0] * 32
+        return Rotation(OQ_ROT_DENSE32, d, 32, 1, mats=mats_bits.contiguous(),
+                        mats_w=None if mats_w is None else mats_w.to(torch.float32).contiguous())
+
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def _rref(rot: Optional[Rotation]):
+    return None if rot is None else rot.ref()
+
+
+def oq_center(x, xc=None, mean=None):
+    x = _bits16(x)
+    M, d = x.shape
+    dev = _dev(x)
+    if mean is None:
+        mean = torch.empty(M, dtype=torch.float32, device=dev)
+    ldxc = 0 if xc is None else xc.stride(0)
+    _check(_lib.oq_center(_p(x), M, d, x.stride(0), _p(xc), ldxc, _p(mean), _stream()))
+    return xc, mean
+
+
+def oq_rotate(rot: Rotation, x, center: bool = False, y=None, mean=None):
+    x = _bits16(x)
+    M = x.shape[0]
+    dev = _dev(x)
+    if y is None:
+        y = torch.empty((M, rot.d), dtype=torch.float32, device=dev)
+    if center and mean is None:
+        mean = torch.empty(M, dtype=torch.float32, device=dev)
+    _check(_lib.oq_rotate(rot.ref(), _p(x), M, x.stride(0), int(center), _p(mean), _p(y), y.stride(0), _stream()))
+    return y, mean
+
+
+def oq_quant_act(x, rot: Optional[Rotation], afmt: int, center: bool = False, codes=None, scale=None,
+                 e8m0=None, mean=None):
+    x = _bits16(x)
+    M, d = x.shape
+    dev = _dev(x)
+    if codes is None:
+        width = d if afmt in (OQ_A8, OQ_A6) else d // 2
+        codes = torch.empty((M, width), dtype=torch.int8 if afmt in (OQ_A8, OQ_A6) else torch.uint8, device=dev)
+    if afmt == OQ_MXFP4:
+        if e8m0 is None:
+            e8m0 = torch.empty((M, d // 32), dtype=torch.uint8, device=dev)
+    elif scale is None:
+        scale = torch.empty(M, dtype=torch.float32, device=dev)
+    if center and mean is None:
+        mean = torch.empty(M, dtype=torch.float32, device=dev)
+    _check(_lib.oq_quant_act(_p(x), M, d, x.stride(0), _rref(rot), int(center), afmt, _p(codes),
+                             codes.stride(0) * codes.element_size(), _p(scale), _p(e8m0), _p(mean), _stream()))
+    return {"codes": codes, "scale": scale, "e8m0": e8m0, "mean": mean}
+
+
+def oq_quant_weight(w, rot: Optional[Rotation], wfmt: int, group: int, codes=None, scales=None, w1=None,
+                    want_w1: bool = False):
+    N, K = w.shape
+    dev = _dev(w)
+    if codes is None:
+        codes = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = (torch.empty((N, K // 32), dtype=torch.uint8, device=dev) if wfmt == OQ_W_MXFP4
+                  else torch.empty((N, K // group), dtype=torch.float32, device=dev))
+    if want_w1 and w1 is None:
+        w1 = torch.empty(N, dtype=torch.float32, device=dev)
+    _check(_lib.oq_quant_weight(_p(w), N, K, w.stride(0), _rref(rot), wfmt, group, _p(codes), _p(scales),
+                                _p(w1), _stream()))
+    return {"codes": codes, "scales": scales, "w1": w1}
+
+
+def oq_gemm_w4a8(qa, a_scale, w, w_scale, N: int, group: int, mean=None, w1=None, bias=None, y=None,
+                 ws=None):
+    M, K = qa.shape
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=_dev(qa))
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(_lib.oq_gemm_w4a8(_p(qa), qa.stride(0), _p(a_scale), M, K, _p(w), _p(w_scale), N, group, _p(mean),
+                             _p(w1), _p(bias), _p(y), y.stride(0), _p(ws), wsb, _stream()))
+    return y
+
+
+def oq_gemm_w4a4(afmt: int, qa, a_scale, w, w_scale, N: int, group: int, mean=None, w1=None, bias=None,
+                 y=None, ws=None):
+    M = qa.shape[0]
+    K = qa.shape[1] * 2
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=_dev(qa))
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(_lib.oq_gemm_w4a4(afmt, _p(qa), qa.stride(0) * qa.element_size(), _p(a_scale), M, K, _p(w),
+                             _p(w_scale), N, group, _p(mean), _p(w1), _p(bias), _p(y), y.stride(0), _p(ws), wsb,
+                             _stream()))
+    return y
+
+
+def oq_workspace_bytes(op: int, M: int, K: int, N: int, afmt: int) -> int:
+    return int(_lib.oq_workspace_bytes(op, M, K, N, afmt))
+
+
+def oq_linear_fused(x, rot: Optional[Rotation], center: bool, afmt: int, w, w_scale, N: int, group: int,
+                    w1=None, bias=None, y=None, ws=None):
+    x = _bits16(x)
+    M, K = x.shape
+    dev = _dev(x)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    if ws is None:
+        ws = torch.empty(max(1, oq_workspace_bytes(OQ_OP_LINEAR, M, K, N, afmt)), dtype=torch.uint8, device=dev)
+    _check(_lib.oq_linear_fused(_p(x), M, K, x.stride(0), _rref(rot), int(center), afmt, _p(w), _p(w_scale), N,
+                                group, _p(w1), _p(bias), _p(y), y.stride(0), _p(ws), ws.numel(), _stream()))
+    return y

@@ -1,0 +1,324 @@
+// C-ABI entry points of liboq: argument validation and kernel dispatch.
+//
+// Every call validates all of its arguments before anything is enqueued and
+// returns an OQ_ERR_* code on the first violation (model card
+// FLUX.1-schnell-OrbitQuant-W4A4, "Limitations": the fused runtime fails
+// loudly rather than falling back).  Launch failures reported by the HIP
+// runtime become OQ_ERR_HIP.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "oq_internal.h"
+
+namespace oq {
+
+static thread_local char g_err[512] = "";
+
+void set_error(const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+}
+
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+namespace {
+
+inline bool al16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return OQ_OK;
+  return fail(OQ_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+// Validates a bf16 activation matrix [M][ldx] of row width d.
+int check_x(const char *fn, const uint16_t *x, int64_t M, int d, int64_t ldx) {
+  if (M < 0) return fail(OQ_ERR_INVALID_ARG, "%s: M must be >= 0 (got %lld)", fn, (long long)M);
+  if (M > 0 && !x) return fail(OQ_ERR_INVALID_ARG, "%s: x is NULL", fn);
+  if (d < 16 || d > 16384 || d % 16)
+    return fail(OQ_ERR_UNSUPPORTED, "%s: width d=%d must be a multiple of 16 in [16, 16384]", fn, d);
+  if (ldx < d) return fail(OQ_ERR_INVALID_ARG, "%s: ldx=%lld < d=%d", fn, (long long)ldx, d);
+  if (!al16(x) || (ldx * 2) % 16) return fail(OQ_ERR_ALIGNMENT, "%s: x rows must be 16-byte aligned", fn);
+  return OQ_OK;
+}
+
+// Fills RotArgs from an RPBH descriptor (or identity when rot == NULL).
+int rot_args(const char *fn, const oq_rot *rot, int d, RotArgs *ra) {
+  ra->rounds = 0;
+  ra->block = 16;
+  ra->perm = nullptr;
+  ra->signs = nullptr;
+  ra->c_h = 1.0f;
+  if (!rot) return OQ_OK;
+  if (rot->kind != OQ_ROT_RPBH) return fail(OQ_ERR_INVALID_ARG, "%s: expected an RPBH rotation", fn);
+  if (rot->d != d) return fail(OQ_ERR_INVALID_ARG, "%s: rot->d=%d differs from d=%d", fn, rot->d, d);
+  if (!is_pow2(rot->block) || rot->block < 32 || rot->block > 1024)
+    return fail(OQ_ERR_UNSUPPORTED, "%s: block=%d must be a power of two in [32, 1024]", fn, rot->block);
+  if (d % rot->block) return fail(OQ_ERR_INVALID_ARG, "%s: d=%d not a multiple of block=%d", fn, d, rot->block);
+  if (rot->rounds < 1 || rot->rounds > 2) return fail(OQ_ERR_UNSUPPORTED, "%s: rounds=%d must be 1 or 2", fn, rot->rounds);
+  if (!rot->perm || !rot->signs) return fail(OQ_ERR_INVALID_ARG, "%s: perm/signs are NULL", fn);
+  ra->rounds = rot->rounds;
+  ra->block = rot->block;
+  ra->perm = rot->perm;
+  ra->signs = rot->signs;
+  ra->c_h = (float)(1.0 / std::sqrt((double)rot->block));
+  return OQ_OK;
+}
+
+int check_dense(const char *fn, const oq_rot *rot, int d, bool weights) {
+  if (rot->d != d) return fail(OQ_ERR_INVALID_ARG, "%s: rot->d=%d differs from d=%d", fn, rot->d, d);
+  if (d % 32) return fail(OQ_ERR_INVALID_ARG, "%s: d=%d must be a multiple of 32", fn, d);
+  if (weights ? !rot->mats_w : !rot->mats) return fail(OQ_ERR_INVALID_ARG, "%s: transform matrices are NULL", fn);
+  return OQ_OK;
+}
+
+int qmax_of(int afmt) { return afmt == OQ_A8 ? 127 : afmt == OQ_A6 ? 31 : 7; }
+
+size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct LinearWs {
+  size_t codes, scale, mean, total;
+  int64_t ldc;
+};
+
+LinearWs linear_ws(int64_t M, int K, int afmt) {
+  LinearWs w;
+  w.ldc = (afmt == OQ_A8 || afmt == OQ_A6) ? K : K / 2;
+  w.ldc = (w.ldc + 15) & ~(int64_t)15;
+  w.codes = 0;
+  w.scale = align_up((size_t)M * w.ldc);
+  const size_t sbytes = afmt == OQ_MXFP4 ? (size_t)M * (K / 32) : (size_t)M * 4;
+  w.mean = align_up(w.scale + sbytes);
+  w.total = align_up(w.mean + (size_t)M * 4);
+  return w;
+}
+
+int check_gemm_common(const char *fn, const void *qa, int64_t lda_bytes, int64_t M, int K, const uint8_t *w,
+                      const void *w_scale, int N, const uint16_t *y, int64_t ldy, int64_t min_lda) {
+  if (M < 0 || N < 0) return fail(OQ_ERR_INVALID_ARG, "%s: negative M or N", fn);
+  if (K <= 0 || K % 64) return fail(OQ_ERR_UNSUPPORTED, "%s: K=%d must be a positive multiple of 64", fn, K);
+  if (M == 0 || N == 0) return OQ_OK;
+  if (!qa || !w || !w_scale || !y) return fail(OQ_ERR_INVALID_ARG, "%s: NULL operand", fn);
+  if (lda_bytes < min_lda) return fail(OQ_ERR_INVALID_ARG, "%s: lda too small", fn);
+  if (!al16(qa) || lda_bytes % 16 || !al16(w)) return fail(OQ_ERR_ALIGNMENT, "%s: codes must be 16-byte aligned rows", fn);
+  if (ldy < N) return fail(OQ_ERR_INVALID_ARG, "%s: ldy=%lld < N=%d", fn, (long long)ldy, N);
+  if (reinterpret_cast<uintptr_t>(y) & 1) return fail(OQ_ERR_ALIGNMENT, "%s: y misaligned", fn);
+  return OQ_OK;
+}
+
+int check_int_epilogue(const char *fn, int K, int group, const float *mean, const float *w1) {
+  if (group < 32 || group % 32 || K % group)
+    return fail(OQ_ERR_UNSUPPORTED, "%s: group=%d must be a multiple of 32 dividing K=%d", fn, group, K);
+  if ((mean == nullptr) != (w1 == nullptr)) return fail(OQ_ERR_INVALID_ARG, "%s: mean and w1 must be given together", fn);
+  return OQ_OK;
+}
+
+}  // namespace
+}  // namespace oq
+
+using namespace oq;
+
+extern "C" {
+
+const char *oq_last_error(void) { return g_err; }
+
+int oq_center(const uint16_t *x, int64_t M, int32_t d, int64_t ldx, float *xc, int64_t ldxc, float *mean,
+              hipStream_t stream) {
+  int rc = check_x("oq_center", x, M, d, ldx);
+  if (rc) return rc;
+  if (M > 0 && !mean) return fail(OQ_ERR_INVALID_ARG, "oq_center: mean is NULL");
+  if (xc && (ldxc < d || !al16(xc) || (ldxc * 4) % 16)) return fail(OQ_ERR_ALIGNMENT, "oq_center: bad xc layout");
+  g_err[0] = 0;
+  RotArgs ra;
+  rot_args("oq_center", nullptr, d, &ra);
+  return hip_status(launch_rpbh_quant(x, M, d, ldx, ra, 1, mean, OUT_F32, 0, xc, ldxc * 4, nullptr, stream),
+                    "oq_center");
+}
+
+int oq_rotate(const oq_rot *rot, const uint16_t *x, int64_t M, int64_t ldx, int center, float *mean, float *y,
+              int64_t ldy, hipStream_t stream) {
+  if (!rot) return fail(OQ_ERR_INVALID_ARG, "oq_rotate: rot is NULL");
+  const int d = rot->d;
+  int rc = check_x("oq_rotate", x, M, d, ldx);
+  if (rc) return rc;
+  if (M > 0 && !y) return fail(OQ_ERR_INVALID_ARG, "oq_rotate: y is NULL");
+  if (ldy < d || !al16(y) || (ldy * 4) % 16) return fail(OQ_ERR_ALIGNMENT, "oq_rotate: bad y layout");
+  if (center && !mean) return fail(OQ_ERR_INVALID_ARG, "oq_rotate: centering needs mean");
+  if (rot->kind == OQ_ROT_DENSE32) {
+    if (center) return fail(OQ_ERR_UNSUPPORTED, "oq_rotate: centering with a DENSE32 rotation");
+    rc = check_dense("oq_rotate", rot, d, false);
+    if (rc) return rc;
+    g_err[0] = 0;
+    return hip_status(launch_dense32(x, M, d, ldx, rot->mats, 0, y, ldy * 4, nullptr, stream), "oq_rotate");
+  }
+  RotArgs ra;
+  rc = rot_args("oq_rotate", rot, d, &ra);
+  if (rc) return rc;
+  g_err[0] = 0;
+  return hip_status(launch_rpbh_quant(x, M, d, ldx, ra, center ? 1 : 0, mean, OUT_F32, 0, y, ldy * 4, nullptr, stream),
+                    "oq_rotate");
+}
+
+int oq_quant_act(const uint16_t *x, int64_t M, int32_t d, int64_t ldx, const oq_rot *rot, int center, int afmt,
+                 void *codes, int64_t ldc_bytes, float *scale, uint8_t *e8m0, float *mean, hipStream_t stream) {
+  int rc = check_x("oq_quant_act", x, M, d, ldx);
+  if (rc) return rc;
+  if (M > 0 && !codes) return fail(OQ_ERR_INVALID_ARG, "oq_quant_act: codes is NULL");
+  if (!al16(codes) || ldc_bytes % 16) return fail(OQ_ERR_ALIGNMENT, "oq_quant_act: code rows must be 16-byte aligned");
+  if (afmt == OQ_MXFP4) {
+    if (!rot || rot->kind != OQ_ROT_DENSE32)
+      return fail(OQ_ERR_UNSUPPORTED, "oq_quant_act: MXFP4 activations need a DENSE32 rotation");
+    if (center) return fail(OQ_ERR_UNSUPPORTED, "oq_quant_act: centering is not defined for MXFP4 here");
+    if (ldc_bytes < d / 2) return fail(OQ_ERR_INVALID_ARG, "oq_quant_act: ldc_bytes < d/2");
+    if (M > 0 && !e8m0) return fail(OQ_ERR_INVALID_ARG, "oq_quant_act: e8m0 is NULL");
+    if (scale) return fail(OQ_ERR_INVALID_ARG, "oq_quant_act: scale must be NULL for MXFP4");
+    rc = check_dense("oq_quant_act", rot, d, false);
+    if (rc) return rc;
+    g_err[0] = 0;
+    return hip_status(launch_dense32(x, M, d, ldx, rot->mats, 1, codes, ldc_bytes, e8m0, stream), "oq_quant_act");
+  }
+  if (afmt != OQ_A8 && afmt != OQ_A6 && afmt != OQ_A4)
+    return fail(OQ_ERR_INVALID_ARG, "oq_quant_act: unknown afmt %d", afmt);
+  if (e8m0) return fail(OQ_ERR_INVALID_ARG, "oq_quant_act: e8m0 must be NULL for integer codes");
+  if (M > 0 && !scale) return fail(OQ_ERR_INVALID_ARG, "oq_quant_act: scale is NULL");
+  if (center && !mean) return fail(OQ_ERR_INVALID_ARG, "oq_quant_act: centering needs mean");
+  if (ldc_bytes < (afmt == OQ_A4 ? d / 2 : d)) return fail(OQ_ERR_INVALID_ARG, "oq_quant_act: ldc_bytes too small");
+  RotArgs ra;
+  rc = rot_args("oq_quant_act", rot, d, &ra);
+  if (rc) return rc;
+  g_err[0] = 0;
+  return hip_status(launch_rpbh_quant(x, M, d, ldx, ra, center ? 1 : 0, mean, afmt == OQ_A4 ? OUT_I4 : OUT_I8,
+                                      qmax_of(afmt), codes, ldc_bytes, scale, stream),
+                    "oq_quant_act");
+}
+
+int oq_quant_weight(const float *w, int32_t N, int32_t K, int64_t ldw, const oq_rot *rot, int wfmt, int32_t group,
+                    uint8_t *codes, void *scales, float *w1, hipStream_t stream) {
+  if (N < 0) return fail(OQ_ERR_INVALID_ARG, "oq_quant_weight: N < 0");
+  if (K < 32 || K > 16384 || K % 32) return fail(OQ_ERR_UNSUPPORTED, "oq_quant_weight: K=%d must be a multiple of 32 in [32, 16384]", K);
+  if (ldw < K) return fail(OQ_ERR_INVALID_ARG, "oq_quant_weight: ldw < K");
+  if (N > 0 && (!w || !codes || !scales)) return fail(OQ_ERR_INVALID_ARG, "oq_quant_weight: NULL pointer");
+  if (!al16(w) || (ldw * 4) % 16 || !al16(codes)) return fail(OQ_ERR_ALIGNMENT, "oq_quant_weight: misaligned");
+  if (wfmt == OQ_W_MXFP4) {
+    if (!rot || rot->kind != OQ_ROT_DENSE32) return fail(OQ_ERR_UNSUPPORTED, "oq_quant_weight: MXFP4 weights need DENSE32");
+    if (w1) return fail(OQ_ERR_UNSUPPORTED, "oq_quant_weight: w1 is produced for OQ_W4 only");
+    int rc = check_dense("oq_quant_weight", rot, K, true);
+    if (rc) return rc;
+    g_err[0] = 0;
+    return hip_status(launch_weight_dense32(w, N, K, ldw, rot->mats_w, codes, (uint8_t *)scales, nullptr, stream),
+                      "oq_quant_weight");
+  }
+  if (wfmt != OQ_W4) return fail(OQ_ERR_INVALID_ARG, "oq_quant_weight: unknown wfmt %d", wfmt);
+  if (!is_pow2(group) || group < 32 || group > 1024 || K % group)
+    return fail(OQ_ERR_UNSUPPORTED, "oq_quant_weight: group=%d must be a power of two in [32, 1024] dividing K", group);
+  RotArgs ra;
+  int rc = rot_args("oq_quant_weight", rot, K, &ra);
+  if (rc) return rc;
+  g_err[0] = 0;
+  return hip_status(launch_weight_rpbh(w, N, K, ldw, ra, group, codes, (float *)scales, w1, stream), "oq_quant_weight");
+}
+
+int oq_gemm_w4a8(const int8_t *qa, int64_t lda, const float *a_scale, int64_t M, int32_t K, const uint8_t *w,
+                 const float *w_scale, int32_t N, int32_t group, const float *mean, const float *w1,
+                 const float *bias, uint16_t *y, int64_t ldy, void *ws, size_t ws_bytes, hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  int rc = check_gemm_common("oq_gemm_w4a8", qa, lda, M, K, w, w_scale, N, y, ldy, K);
+  if (rc) return rc;
+  rc = check_int_epilogue("oq_gemm_w4a8", K, group, mean, w1);
+  if (rc) return rc;
+  if (M > 0 && !a_scale) return fail(OQ_ERR_INVALID_ARG, "oq_gemm_w4a8: a_scale is NULL");
+  g_err[0] = 0;
+  return hip_status(launch_gemm_int(qa, lda, 0, a_scale, M, K, w, w_scale, N, group, mean, w1, bias, y, ldy, stream),
+                    "oq_gemm_w4a8");
+}
+
+int oq_gemm_w4a4(int afmt, const uint8_t *qa, int64_t lda_bytes, const void *a_scale, int64_t M, int32_t K,
+                 const uint8_t *w, const void *w_scale, int32_t N, int32_t group, const float *mean, const float *w1,
+                 const float *bias, uint16_t *y, int64_t ldy, void *ws, size_t ws_bytes, hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  int rc = check_gemm_common("oq_gemm_w4a4", qa, lda_bytes, M, K, w, w_scale, N, y, ldy, K / 2);
+  if (rc) return rc;
+  if (M > 0 && N > 0 && !a_scale) return fail(OQ_ERR_INVALID_ARG, "oq_gemm_w4a4: a_scale is NULL");
+  if (afmt == OQ_MXFP4) {
+    if (group != 32) return fail(OQ_ERR_INVALID_ARG, "oq_gemm_w4a4: MXFP4 blocks are 32 (group=%d)", group);
+    if (mean || w1) return fail(OQ_ERR_UNSUPPORTED, "oq_gemm_w4a4: rank-1 restore is not defined for MXFP4 here");
+    g_err[0] = 0;
+    return hip_status(launch_gemm_mx(qa, lda_bytes, (const uint8_t *)a_scale, M, K, w, (const uint8_t *)w_scale, N,
+                                     bias, y, ldy, stream),
+                      "oq_gemm_w4a4");
+  }
+  if (afmt != OQ_A4) return fail(OQ_ERR_INVALID_ARG, "oq_gemm_w4a4: afmt must be OQ_A4 or OQ_MXFP4");
+  rc = check_int_epilogue("oq_gemm_w4a4", K, group, mean, w1);
+  if (rc) return rc;
+  g_err[0] = 0;
+  return hip_status(launch_gemm_int(qa, lda_bytes, 1, (const float *)a_scale, M, K, w, (const float *)w_scale, N,
+                                    group, mean, w1, bias, y, ldy, stream),
+                    "oq_gemm_w4a4");
+}
+
+size_t oq_workspace_bytes(int op, int64_t M, int32_t K, int32_t N, int afmt) {
+  (void)N;
+  if (op != OQ_OP_LINEAR || M < 0 || K <= 0) return 0;
+  return linear_ws(M, K, afmt).total;
+}
+
+int oq_linear_fused(const uint16_t *x, int64_t M, int32_t K, int64_t ldx, const oq_rot *rot, int center, int afmt,
+                    const uint8_t *w, const void *w_scale, int32_t N, int32_t group, const float *w1, const float *bias,
+                    uint16_t *y, int64_t ldy, void *ws, size_t ws_bytes, hipStream_t stream) {
+  const char *fn = "oq_linear_fused";
+  int rc = check_x(fn, x, M, K, ldx);
+  if (rc) return rc;
+  if (afmt != OQ_A8 && afmt != OQ_A6 && afmt != OQ_A4 && afmt != OQ_MXFP4)
+    return fail(OQ_ERR_INVALID_ARG, "%s: unknown afmt %d", fn, afmt);
+  const LinearWs L = linear_ws(M, K, afmt);
+  if (M > 0 && (!ws || ws_bytes < L.total))
+    return fail(OQ_ERR_WORKSPACE, "%s: workspace of %zu bytes required (got %zu)", fn, L.total, ws_bytes);
+  if (ws && !al16(ws)) return fail(OQ_ERR_ALIGNMENT, "%s: workspace must be 16-byte aligned", fn);
+  rc = check_gemm_common(fn, x, L.ldc, M, K, w, w_scale, N, y, ldy, 0);
+  if (rc) return rc;
+  char *wsb = static_cast<char *>(ws);
+  uint8_t *codes = reinterpret_cast<uint8_t *>(wsb + L.codes);
+  if (afmt == OQ_MXFP4) {
+    if (!rot || rot->kind != OQ_ROT_DENSE32) return fail(OQ_ERR_UNSUPPORTED, "%s: MXFP4 needs a DENSE32 rotation", fn);
+    if (center || w1) return fail(OQ_ERR_UNSUPPORTED, "%s: centering is not defined for MXFP4 here", fn);
+    if (group != 32) return fail(OQ_ERR_INVALID_ARG, "%s: MXFP4 blocks are 32 (group=%d)", fn, group);
+    rc = check_dense(fn, rot, K, false);
+    if (rc) return rc;
+    uint8_t *e8 = reinterpret_cast<uint8_t *>(wsb + L.scale);
+    g_err[0] = 0;
+    rc = hip_status(launch_dense32(x, M, K, ldx, rot->mats, 1, codes, L.ldc, e8, stream), fn);
+    if (rc) return rc;
+    return hip_status(launch_gemm_mx(codes, L.ldc, e8, M, K, w, (const uint8_t *)w_scale, N, bias, y, ldy, stream), fn);
+  }
+  rc = check_int_epilogue(fn, K, group, center ? w1 : nullptr, center ? w1 : nullptr);
+  if (rc) return rc;
+  if (center && !w1) return fail(OQ_ERR_INVALID_ARG, "%s: centering needs w1", fn);
+  RotArgs ra;
+  rc = rot_args(fn, rot, K, &ra);
+  if (rc) return rc;
+  float *scale = reinterpret_cast<float *>(wsb + L.scale);
+  float *mean = reinterpret_cast<float *>(wsb + L.mean);
+  g_err[0] = 0;
+  rc = hip_status(launch_rpbh_quant(x, M, K, ldx, ra, center ? 1 : 0, mean, afmt == OQ_A4 ? OUT_I4 : OUT_I8,
+                                    qmax_of(afmt), codes, L.ldc, scale, stream),
+                  fn);
+  if (rc) return rc;
+  return hip_status(launch_gemm_int(codes, L.ldc, afmt == OQ_A4 ? 1 : 0, scale, M, K, w, (const float *)w_scale, N, group,
+                                    center ? mean : nullptr, center ? w1 : nullptr, bias, y, ldy, stream),
+                    fn);
+}
+
+}  // extern "C"

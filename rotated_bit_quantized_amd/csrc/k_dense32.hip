@@ -1,0 +1,129 @@
+// K2: per-32-block dense transform followed by MXFP4 quantization, gfx950.
+//
+// WUSH review ("Core claim"): every quantization block of 32 coordinates has
+// its own transform; activations take T_b, weights its inverse-transpose.
+// The quantizer is RTN absmax MXFP4 (E2M1 elements, one E8M0 power-of-two
+// scale per 32; OCP MX v1.0 as cited by the review):
+//   e = clamp(floor(log2 amax) - 2, -127, 127), element = nearest E2M1 value
+//   of v * 2^-e with ties to the even code, saturating at 6, sign kept.
+//
+// Exactness: the transform is accumulated in float64 and rounded once to
+// float32.  For the activation side (bf16 x bf16 products) the float64 sum is
+// exact for ordinary data, so v = RN32(T_b x_b).
+//
+// Layout: lanes are tokens (rows); one wavefront covers 64 rows and a run of
+// blocks.  The block's matrix is staged in LDS as float64 and read as a
+// broadcast, each lane keeps its 32 inputs and 32 accumulators in registers,
+// so the per-block absmax needs no cross-lane traffic.
+#include "oq_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace oq {
+namespace {
+
+constexpr int BPW = 8;  // blocks per workgroup
+
+__device__ __forceinline__ uint32_t e2m1_code(float t) {
+  const float m = fabsf(t);
+  uint32_t c = (m > 0.25f) + (m >= 0.75f) + (m > 1.25f) + (m >= 1.75f) + (m > 2.5f) + (m >= 3.5f) + (m > 5.0f);
+  return c | ((__float_as_uint(t) >> 28) & 8u);
+}
+
+// IN_F32 selects the weight-side variant: float32 rows and float32 matrices.
+template <bool IN_F32, bool MX_OUT>
+__global__ void __launch_bounds__(64)
+dense32_kernel(const void *__restrict__ xin, int64_t M, int d, int64_t ldx, const void *__restrict__ mats,
+               void *__restrict__ out, int64_t ld_out_bytes, uint8_t *__restrict__ e8m0) {
+  __shared__ double T[32 * 32];
+  const int64_t row = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  const bool ok = row < M;
+  const int nb = d / 32;
+  const int b0 = blockIdx.y * BPW;
+  const int b1 = min(b0 + BPW, nb);
+  for (int b = b0; b < b1; ++b) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < 1024; e += 64) {
+      if (IN_F32)
+        T[e] = (double)static_cast<const float *>(mats)[(int64_t)b * 1024 + e];
+      else
+        T[e] = (double)__uint_as_float((uint32_t)static_cast<const uint16_t *>(mats)[(int64_t)b * 1024 + e] << 16);
+    }
+    __syncthreads();
+    if (!ok) continue;
+    double xd[32];
+    if (IN_F32) {
+      const float4 *src = reinterpret_cast<const float4 *>(static_cast<const float *>(xin) + row * ldx + b * 32);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float4 p = src[k];
+        xd[4 * k] = p.x; xd[4 * k + 1] = p.y; xd[4 * k + 2] = p.z; xd[4 * k + 3] = p.w;
+      }
+    } else {
+      const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(xin) + row * ldx + b * 32);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint4 p = src[k];
+        const uint32_t wd[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          xd[8 * k + 2 * q] = (double)bf16_lo(wd[q]);
+          xd[8 * k + 2 * q + 1] = (double)bf16_hi(wd[q]);
+        }
+      }
+    }
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      double acc = 0.0;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) acc = __builtin_fma(T[i * 32 + j], xd[j], acc);
+      v[i] = (float)acc;
+    }
+    char *orow = static_cast<char *>(out) + row * ld_out_bytes;
+    if (!MX_OUT) {
+      float4 *dst = reinterpret_cast<float4 *>(orow) + b * 8;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) dst[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+      continue;
+    }
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) a = fmaxf(a, fabsf(v[i]));
+    const int ef = (int)((__float_as_uint(a) >> 23) & 0xFF);
+    const int e = ef == 0 ? -127 : max(ef - 129, -127);
+    const float inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, exact
+    uint32_t wd[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 32; ++i) wd[i >> 3] |= e2m1_code(v[i] * inv) << (4 * (i & 7));
+    *reinterpret_cast<uint4 *>(orow + b * 16) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+    e8m0[row * nb + b] = (uint8_t)(e + 127);
+  }
+}
+
+template <bool IN_F32, bool MX_OUT>
+hipError_t launch(const void *x, int64_t M, int d, int64_t ldx, const void *mats, void *out,
+                  int64_t ld_out_bytes, uint8_t *e8m0, hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  const int nb = d / 32;
+  dim3 grid((unsigned)((M + 63) / 64), (unsigned)((nb + BPW - 1) / BPW));
+  hipLaunchKernelGGL((dense32_kernel<IN_F32, MX_OUT>), grid, dim3(64), 0, stream, x, M, d, ldx, mats, out,
+                     ld_out_bytes, e8m0);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_dense32(const uint16_t *x, int64_t M, int d, int64_t ldx, const uint16_t *mats, int mx_out,
+                          void *out, int64_t ld_out_bytes, uint8_t *e8m0, hipStream_t stream) {
+  if (mx_out) return launch<false, true>(x, M, d, ldx, mats, out, ld_out_bytes, e8m0, stream);
+  return launch<false, false>(x, M, d, ldx, mats, out, ld_out_bytes, e8m0, stream);
+}
+
+hipError_t launch_weight_dense32(const float *w, int N, int K, int64_t ldw, const float *mats_w,
+                                 uint8_t *codes, uint8_t *e8m0, float *w1, hipStream_t stream) {
+  (void)w1;
+  return launch<true, true>(w, N, K, ldw, mats_w, codes, K / 2, e8m0, stream);
+}
+
+}  // namespace oq

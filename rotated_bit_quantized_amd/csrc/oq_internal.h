@@ -1,0 +1,76 @@
+// Internal declarations shared by the gfx950 kernels and the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/oq.h"
+
+namespace oq {
+
+// ------------------------------------------------------------------ errors --
+void set_error(const char *fmt, ...);
+int fail(int code, const char *fmt, ...);
+
+// ------------------------------------------------------- numeric helpers --
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+
+// float32 -> bfloat16 bits, round to nearest even (finite values; NaN kept quiet)
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// activation code formats used inside the library (values of the public enum
+// for the integer widths; internal operand layouts are separate constants)
+enum OutMode : int {
+  OUT_F32 = 0,   // float32 rotated values (oq_rotate / oq_center)
+  OUT_I8 = 1,    // int8 codes (A8, A6)
+  OUT_I4 = 2,    // packed nibbles (A4)
+  OUT_W4G = 3,   // per-group INT4 codes + scales (offline weight fold)
+};
+
+// -------------------------------------------------------- kernel launchers --
+struct RotArgs {
+  int rounds;            // 0 = no rotation
+  int block;             // h
+  const int32_t *perm;   // [rounds][d]
+  const int8_t *signs;   // [rounds][d]
+  float c_h;             // RN32(1/sqrt h)
+};
+
+// K1: (center) -> RPBH rounds -> (quantize) per token row.
+hipError_t launch_rpbh_quant(const uint16_t *x, int64_t M, int d, int64_t ldx,
+                             const RotArgs &rot, int center, float *mean,
+                             int out_mode, int qmax, void *out, int64_t ld_out_bytes,
+                             float *scale, hipStream_t stream);
+
+// K2: dense per-32 transform -> (MXFP4 quantize | float32 out).
+hipError_t launch_dense32(const uint16_t *x, int64_t M, int d, int64_t ldx,
+                          const uint16_t *mats, int mx_out, void *out, int64_t ld_out_bytes,
+                          uint8_t *e8m0, hipStream_t stream);
+
+// K3/K4: integer-coded activations x packed INT4 weights, fp32 group epilogue.
+//   a_is_nibble: activations packed two per byte (A4) instead of int8.
+hipError_t launch_gemm_int(const void *qa, int64_t lda_bytes, int a_is_nibble,
+                           const float *a_scale, int64_t M, int K,
+                           const uint8_t *w, const float *w_scale, int N, int group,
+                           const float *mean, const float *w1, const float *bias,
+                           uint16_t *y, int64_t ldy, hipStream_t stream);
+
+// K5: MXFP4 x MXFP4 with E8M0 block scales (scaled FP4 MFMA).
+hipError_t launch_gemm_mx(const uint8_t *qa, int64_t lda_bytes, const uint8_t *a_e8m0,
+                          int64_t M, int K, const uint8_t *w, const uint8_t *w_e8m0, int N,
+                          const float *bias, uint16_t *y, int64_t ldy, hipStream_t stream);
+
+// Offline weight preparation.
+hipError_t launch_weight_rpbh(const float *w, int N, int K, int64_t ldw, const RotArgs &rot,
+                              int group, uint8_t *codes, float *scales, float *w1,
+                              hipStream_t stream);
+hipError_t launch_weight_dense32(const float *w, int N, int K, int64_t ldw, const float *mats_w,
+                                 uint8_t *codes, uint8_t *e8m0, float *w1, hipStream_t stream);
+
+}  // namespace oq
