@@ -1,0 +1,261 @@
+"""Benchmark of the rotated low-bit linear layer on one MI355X.
+
+A step is one pass of the whole hot path over one batch: the DiT-width W4A4
+workload (4096 tokens x 3072, one RPBH round with h = 1024, per-token absmax
+INT4 activations, INT4 weights with fp32 scales per 64 columns), rotated and
+quantized once and multiplied by both linears of that width (3072 -> 3072 and
+3072 -> 12288).  Inputs are resident in device memory before timing starts;
+the activation buffer is rotated through enough copies (> 512 MiB) that each
+step reads it from HBM rather than from the 256 MiB last-level cache.
+
+Prints one JSON line.  `value` is whole-step throughput in TOPS
+(2 M K (N1 + N2) integer multiply-adds per step / step time).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "rotated W4A8/W4A4 linear TOPS + rotate/quant µs/call at 4096 tokens; % roofline"
+PEAK_HBM_GBS = 8000.0
+PEAK_INT8_TOPS = 5000.0
+PEAK_FP4_TFLOPS = 10100.0
+
+
+def _src_hash(names):
+    h = hashlib.sha1()
+    for n in names:
+        with open(os.path.join(ROOT, "rotated_bit_quantized_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(profile_name, src_names):
+    """HBM bytes per launch from a committed counter summary, if it was taken
+    on the current kernel source; otherwise None."""
+    p = os.path.join(ROOT, "profiles", profile_name)
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except Exception:
+        return None
+    if d.get("source_sha1") != _src_hash(src_names):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def _setup(torch, oq, WL, cid, n_sets_bytes=600 << 20):
+    wl = WL.make_workload(cid)
+    s = wl.spec
+    dev = torch.device("cuda:0")
+    st = {"wl": wl, "spec": s}
+    if s.rot == "rpbh":
+        rot = oq.Rotation.rpbh(torch.from_numpy(wl.perm).to(dev), torch.from_numpy(wl.signs).to(dev), s.block)
+        ws = [oq.oq_quant_weight(torch.from_numpy(W).to(dev), rot, oq.OQ_W4, s.group, want_w1=s.center)
+              for W in wl.weights]
+    else:
+        rot = oq.Rotation.dense32(torch.from_numpy(wl.t_act_bits.view("int16")).to(dev),
+                                  torch.from_numpy(wl.t_wgt).to(dev))
+        ws = [oq.oq_quant_weight(torch.from_numpy(W).to(dev), rot, oq.OQ_W_MXFP4, 32) for W in wl.weights]
+    x0 = torch.from_numpy(wl.x_bits.view("int16")).to(dev)
+    nsets = max(1, -(-n_sets_bytes // (x0.numel() * 2)))
+    st["xs"] = [x0] + [x0.clone() for _ in range(nsets - 1)]
+    M, K = wl.M, wl.K
+    if s.afmt == oq.OQ_MXFP4:
+        st["codes"] = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+        st["e8m0"] = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+        st["scale"] = None
+    else:
+        st["codes"] = torch.empty((M, K if s.afmt in (8, 6) else K // 2),
+                                  dtype=torch.int8 if s.afmt in (8, 6) else torch.uint8, device=dev)
+        st["scale"] = torch.empty(M, dtype=torch.float32, device=dev)
+        st["e8m0"] = None
+    st["mean"] = torch.empty(M, dtype=torch.float32, device=dev) if s.center else None
+    st["ys"] = [torch.empty((M, W.shape[0]), dtype=torch.bfloat16, device=dev) for W in wl.weights]
+    st["rot"], st["ws"] = rot, ws
+    return st
+
+
+def _launches(oq, st, i):
+    """The kernels of one step as (name, thunk) pairs, in launch order."""
+    s = st["spec"]
+    x = st["xs"][i % len(st["xs"])]
+    out = []
+    out.append(("rotate_quant", lambda: oq.oq_quant_act(x, st["rot"], s.afmt, center=s.center, codes=st["codes"],
+                                                         scale=st["scale"], e8m0=st["e8m0"], mean=st["mean"])))
+    for j, (wq, y) in enumerate(zip(st["ws"], st["ys"])):
+        N = y.shape[1]
+        if s.afmt == oq.OQ_MXFP4:
+            f = (lambda wq=wq, y=y, N=N: oq.oq_gemm_w4a4(oq.OQ_MXFP4, st["codes"], st["e8m0"], wq["codes"],
+                                                         wq["scales"], N, 32, y=y))
+        elif s.afmt == oq.OQ_A4:
+            f = (lambda wq=wq, y=y, N=N: oq.oq_gemm_w4a4(oq.OQ_A4, st["codes"], st["scale"], wq["codes"],
+                                                         wq["scales"], N, s.group, mean=st["mean"],
+                                                         w1=wq["w1"], y=y))
+        else:
+            f = (lambda wq=wq, y=y, N=N: oq.oq_gemm_w4a8(st["codes"], st["scale"], wq["codes"], wq["scales"], N,
+                                                         s.group, mean=st["mean"], w1=wq["w1"], y=y))
+        out.append((f"gemm_n{N}", f))
+    return out
+
+
+def _time(torch, oq, st, steps, warmup):
+    for i in range(warmup):
+        for _, f in _launches(oq, st, i):
+            f()
+    torch.cuda.synchronize()
+    names = [n for n, _ in _launches(oq, st, 0)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        L = _launches(oq, st, i)
+        ev[i][0].record()
+        for k, (_, f) in enumerate(L):
+            f()
+            ev[i][k + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {n: 0.0 for n in names}
+    for i in range(steps):
+        for k, n in enumerate(names):
+            per[n] += ev[i][k].elapsed_time(ev[i][k + 1])
+    per = {n: v / steps for n, v in per.items()}          # ms per launch
+    total = ev[0][0].elapsed_time(ev[-1][-1]) / steps     # ms per step on the device
+    return total, wall / steps * 1e3, per
+
+
+def _act_bytes(spec, M, K):
+    if spec.afmt == 0x104:
+        return M * K * 2 + M * K // 2 + M * K // 32
+    code = M * K if spec.afmt in (8, 6) else M * K // 2
+    return M * K * 2 + code + 4 * M + (4 * M if spec.center else 0)
+
+
+def _cpu_baseline(WL, cid=2, target_s=12.0):
+    """The oracle (unmodified) on a bounded sample of the same workload: the
+    whole path for the first `rows` tokens against both linears."""
+    import numpy as np
+    from oracle import linear as OL
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = None
+    wl = WL.make_workload(cid)
+    s = wl.spec
+    wprep = [OL.prepare_weight_rpbh(W, wl.perm, wl.signs, s.block, s.group) for W in wl.weights]
+    rows = 32
+    while True:
+        t0 = time.perf_counter()
+        xb = wl.x_bits[:rows]
+        act = OL.activations_int(xb, wl.perm, wl.signs, s.block, s.afmt, s.center)
+        for wp in wprep:
+            OL.linear_int(act, wp, s.group)
+        dt = time.perf_counter() - t0
+        if dt >= target_s or rows >= wl.M:
+            break
+        rows = min(wl.M, max(rows * 2, int(rows * target_s / max(dt, 1e-3))))
+    ops = 2.0 * rows * wl.K * sum(wl.Ns)
+    cores = len(os.sched_getaffinity(0))
+    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": threads if threads else cores, "kind": "oracle",
+            "sample": f"{rows} of {wl.M} tokens of the 4096x3072 W4A4 workload through rotate+quantize and both "
+                      f"linears (3072 and 12288 outputs), {dt:.1f} s wall on {cores} host cores "
+                      f"(BLAS threads {threads})"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-config side table")
+    ap.add_argument("--only-step", action="store_true", help="time the step only (for profilers)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (the layer shards by tokens, "
+                                   "see the design notes)", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import rotated_bit_quantized_amd as oq
+    import workloads as WL
+
+    torch.cuda.set_device(0)
+    st = _setup(torch, oq, WL, 2)
+    wl, s = st["wl"], st["spec"]
+    M, K = wl.M, wl.K
+    ms_step, wall_ms, per = _time(torch, oq, st, args.steps, args.warmup)
+    ops = 2.0 * M * K * sum(wl.Ns)
+    value = ops / (ms_step * 1e-3) / 1e12
+
+    rq_us = per["rotate_quant"] * 1e3
+    rq_bytes = _act_bytes(s, M, K)
+    big = f"gemm_n{max(wl.Ns)}"
+    g_ms = per[big]
+    g_ops = 2.0 * M * K * max(wl.Ns)
+    achieved = g_ops / (g_ms * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4 codes on int8 MFMA, fp32 epilogue",
+        "data": "synthetic (seeded; N(0,1) activations with Student-t(3) on 1% of channels, N(0,0.02^2) weights)",
+        "config": {"workload": "c2_w4a4_dit_4096x3072->3072+12288", "tokens": M, "d_in": K,
+                   "d_out": list(wl.Ns), "rotation": f"rpbh h={s.block} rounds={s.rounds}",
+                   "act": "absmax int4 per token", "weight_group": s.group, "parallelism": "none (1 GPU)"},
+        "rotate_quant_us": round(rq_us, 3),
+        "rotate_quant_GBs": round(rq_bytes / (rq_us * 1e-6) / 1e9, 1),
+        "rotate_quant_hbm_frac": round(rq_bytes / (rq_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+        "gemm_us": {n: round(v * 1e3, 3) for n, v in per.items() if n.startswith("gemm")},
+        "host_wall_ms_per_step": round(wall_ms, 5),
+        "roofline": {"kernel": f"int4 GEMM 4096x3072 -> {max(wl.Ns)}", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_INT8_TOPS, 4),
+                     "traffic": _traffic("gemm_int_c2_traffic.json", ["k_gemm_int.hip"])},
+    }
+
+    if not args.no_configs and not args.only_step:
+        side = {}
+        for cid in (1, 3, 4, 5):
+            del st
+            torch.cuda.empty_cache()
+            st = _setup(torch, oq, WL, cid)
+            ms, _, per_c = _time(torch, oq, st, max(20, args.steps // 5), 5)
+            w2, s2 = st["wl"], st["spec"]
+            b = _act_bytes(s2, w2.M, w2.K)
+            peak = PEAK_FP4_TFLOPS if s2.afmt == 0x104 else PEAK_INT8_TOPS
+            e = {"rotate_quant_us": round(per_c["rotate_quant"] * 1e3, 3),
+                 "rotate_quant_hbm_frac": round(b / (per_c["rotate_quant"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+            for n, v in per_c.items():
+                if n.startswith("gemm"):
+                    Nn = int(n[6:])
+                    tops = 2.0 * w2.M * w2.K * Nn / (v * 1e-3) / 1e12
+                    e[n] = {"us": round(v * 1e3, 2), "TOPS": round(tops, 1), "frac": round(tops / peak, 4)}
+            e["step_ms"] = round(ms, 4)
+            side[s2.name] = e
+        result["other_configs"] = side
+
+    if not args.no_cpu_baseline and not args.only_step:
+        result["cpu_baseline"] = _cpu_baseline(WL)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
