@@ -57,10 +57,15 @@ def _setup(torch, oq, WL, cid, n_sets_bytes=600 << 20):
     s = wl.spec
     dev = torch.device("cuda:0")
     st = {"wl": wl, "spec": s}
+    st["tiled"] = s.rot == "rpbh" and s.group == 64 and s.afmt in (oq.OQ_A4, oq.OQ_A6)
     if s.rot == "rpbh":
         rot = oq.Rotation.rpbh(torch.from_numpy(wl.perm).to(dev), torch.from_numpy(wl.signs).to(dev), s.block)
         ws = [oq.oq_quant_weight(torch.from_numpy(W).to(dev), rot, oq.OQ_W4, s.group, want_w1=s.center)
               for W in wl.weights]
+        if st["tiled"]:  # offline: repack into the MFMA operand layout
+            for w, W in zip(ws, wl.weights):
+                t = oq.oq_prepack_w4(w["codes"], w["scales"], W.shape[0], wl.K)
+                w["codes"], w["scales"] = t["codes"], t["scales"]
     else:
         rot = oq.Rotation.dense32(torch.from_numpy(wl.t_act_bits.view("int16")).to(dev),
                                   torch.from_numpy(wl.t_wgt).to(dev))
@@ -73,6 +78,11 @@ def _setup(torch, oq, WL, cid, n_sets_bytes=600 << 20):
         st["codes"] = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
         st["e8m0"] = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
         st["scale"] = None
+    elif st["tiled"]:
+        planes = 2 if s.afmt == oq.OQ_A6 else 1
+        st["codes"] = torch.empty(planes * oq.oq_tiled_bytes(M, K), dtype=torch.uint8, device=dev)
+        st["scale"] = torch.empty(M, dtype=torch.float32, device=dev)
+        st["e8m0"] = None
     else:
         st["codes"] = torch.empty((M, K if s.afmt in (8, 6) else K // 2),
                                   dtype=torch.int8 if s.afmt in (8, 6) else torch.uint8, device=dev)
@@ -89,11 +99,16 @@ def _launches(oq, st, i):
     s = st["spec"]
     x = st["xs"][i % len(st["xs"])]
     out = []
-    out.append(("rotate_quant", lambda: oq.oq_quant_act(x, st["rot"], s.afmt, center=s.center, codes=st["codes"],
+    afmt = s.afmt | (oq.OQ_TILED if st["tiled"] else 0)
+    out.append(("rotate_quant", lambda: oq.oq_quant_act(x, st["rot"], afmt, center=s.center, codes=st["codes"],
                                                          scale=st["scale"], e8m0=st["e8m0"], mean=st["mean"])))
+    M, K = st["wl"].M, st["wl"].K
     for j, (wq, y) in enumerate(zip(st["ws"], st["ys"])):
         N = y.shape[1]
-        if s.afmt == oq.OQ_MXFP4:
+        if st["tiled"]:
+            f = (lambda wq=wq, y=y, N=N: oq.oq_gemm_w4a4(afmt, st["codes"], st["scale"], wq["codes"], wq["scales"],
+                                                         N, 64, mean=st["mean"], w1=wq["w1"], y=y, M=M, K=K))
+        elif s.afmt == oq.OQ_MXFP4:
             f = (lambda wq=wq, y=y, N=N: oq.oq_gemm_w4a4(oq.OQ_MXFP4, st["codes"], st["e8m0"], wq["codes"],
                                                          wq["scales"], N, 32, y=y))
         elif s.afmt == oq.OQ_A4:
@@ -215,7 +230,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 codes on int8 MFMA, fp32 epilogue",
+        "dtype": "int4 codes as fp6 e2m3 on the scaled fp6 MFMA (exact int sums), fp32 epilogue",
         "data": "synthetic (seeded; N(0,1) activations with Student-t(3) on 1% of channels, N(0,0.02^2) weights)",
         "config": {"workload": "c2_w4a4_dit_4096x3072->3072+12288", "tokens": M, "d_in": K,
                    "d_out": list(wl.Ns), "rotation": f"rpbh h={s.block} rounds={s.rounds}",
@@ -228,7 +243,7 @@ def main():
         "roofline": {"kernel": f"int4 GEMM 4096x3072 -> {max(wl.Ns)}", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_INT8_TOPS, 4),
-                     "traffic": _traffic("gemm_int_c2_traffic.json", ["k_gemm_int.hip"])},
+                     "traffic": _traffic("gemm_fp6_c2_traffic.json", ["k_gemm_fp6.hip"])},
     }
 
     if not args.no_configs and not args.only_step:

@@ -64,6 +64,26 @@ enum { OQ_A8 = 8, OQ_A6 = 6, OQ_A4 = 4, OQ_MXFP4 = 0x104 };
 enum { OQ_W4 = 4, OQ_W_MXFP4 = 0x104 };
 
 /*
+ * Operand layout flag, OR-ed into afmt (OQ_A4 | OQ_TILED, OQ_A6 | OQ_TILED):
+ * codes are stored as FP6 E2M3 values of the integer codes (exact for
+ * |q| <= 7) in the MFMA-tiled layout below, the layout the fast GEMM reads.
+ *   rows padded to a multiple of 32, K a multiple of 64; the 64 codes of
+ *   (row r, k-group kg = k / 64) form a 384-bit string with code j = k % 64 in
+ *   bits [6j, 6j+6); its six 8-byte chunks c = 0..5 sit at byte
+ *   ((r/32) * (K/64) + kg) * 1536 + c * 256 + (r % 32) * 8.
+ *   One plane is oq_tiled_bytes(rows, K) bytes.  OQ_A6 uses two planes:
+ *   q = 8 qh + ql with qh = floor(q / 8) in plane 0 and ql = q - 8 qh in
+ *   plane 1 (each in [-4, 7]).
+ * Weights for tiled GEMMs come from oq_prepack_w4 (same layout, one plane,
+ * plus scales transposed to [K/64][N_padded]).  The per-token scale
+ * (a_scale) and mean arrays are unchanged.  Tiled GEMMs require group == 64.
+ */
+enum { OQ_TILED = 0x10000 };
+
+/* Bytes of one plane of the tiled layout for `rows` rows of width K. */
+size_t oq_tiled_bytes(int64_t rows, int32_t K);
+
+/*
  * Rotation descriptor (host struct, device arrays).
  *
  * OQ_ROT_RPBH -- OrbitQuant PR #25 "Default changes" (independent extra
@@ -134,6 +154,8 @@ int oq_rotate(const oq_rot *rot, const uint16_t *x, int64_t M, int64_t ldx,
  * afmt OQ_A8, OQ_A6: int8 codes [M][ldc_bytes]; OQ_A4: two codes per byte,
  *   element 2i in bits 3..0, two's complement, [M][ldc_bytes >= d/2];
  *   scale float32 [M]; e8m0 must be NULL.
+ * afmt OQ_A4 | OQ_TILED, OQ_A6 | OQ_TILED: codes in the tiled FP6 layout
+ *   (planes * oq_tiled_bytes(M, d) bytes; d % 64 == 0; ldc_bytes ignored).
  * afmt OQ_MXFP4 (rot->kind must be OQ_ROT_DENSE32, center == 0): E2M1 codes
  *   two per byte as above, sign in bit 3; e8m0 uint8 [M][d/32] with
  *   e = clamp(floor(log2 amax) - 2, -127, 127), byte = e + 127; scale NULL.
@@ -184,6 +206,10 @@ int oq_gemm_w4a8(const int8_t *qa, int64_t lda, const float *a_scale, int64_t M,
  *   afmt OQ_A4: qa nibbles [M][lda_bytes], a_scale float32 [M]; w canonical
  *     INT4 nibbles [N][K/2], w_scale float32 [N][K/group]; epilogue as
  *     oq_gemm_w4a8.
+ *   afmt OQ_A4 | OQ_TILED or OQ_A6 | OQ_TILED: qa in the tiled layout (from
+ *     oq_quant_act with the same afmt; lda_bytes ignored), w and w_scale
+ *     from oq_prepack_w4, group 64; output bit-identical to the canonical
+ *     path on the same codes.
  *   afmt OQ_MXFP4: qa E2M1 nibbles, a_scale uint8 E8M0 [M][K/32]; w E2M1
  *     nibbles [N][K/2], w_scale uint8 E8M0 [N][K/32]; group must be 32;
  *     y = bf16_RNE( sum_blocks 2^(ea+ew) sum_k fp4(a) fp4(w) + bias[o] );
@@ -201,6 +227,8 @@ int oq_gemm_w4a4(int afmt, const uint8_t *qa, int64_t lda_bytes, const void *a_s
  * each token tile once; rank-1 term and bias in the GEMM epilogue).
  * afmt OQ_A8/OQ_A6/OQ_A4 with an RPBH rotation (or NULL), optional centering
  * (then w1 is required); OQ_MXFP4 with a DENSE32 rotation and E8M0 w_scale.
+ * afmt OQ_A4 | OQ_TILED or OQ_A6 | OQ_TILED: w/w_scale from oq_prepack_w4
+ * (group 64); activations are quantized straight into the tiled layout.
  * ws: device scratch of at least oq_workspace_bytes(OQ_OP_LINEAR, M, K, N, afmt).
  */
 int oq_linear_fused(const uint16_t *x, int64_t M, int32_t K, int64_t ldx,
@@ -208,6 +236,17 @@ int oq_linear_fused(const uint16_t *x, int64_t M, int32_t K, int64_t ldx,
                     const uint8_t *w, const void *w_scale, int32_t N, int32_t group,
                     const float *w1, const float *bias, uint16_t *y, int64_t ldy,
                     void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * oq_prepack_w4 -- repack canonical INT4 weights (oq_quant_weight OQ_W4
+ * output: codes [N][K/2], scales float32 [N][K/64]) into the tiled FP6
+ * layout for OQ_TILED GEMMs.  Values are unchanged (every INT4 code is an
+ * exact FP6 E2M3 value).  w_tiled: oq_tiled_bytes(N, K) bytes; w_scale_t:
+ * float32 [K/64][N rounded up to 32] (padding columns get scale 0).
+ * group must be 64.
+ */
+int oq_prepack_w4(const uint8_t *w, const float *w_scale, int32_t N, int32_t K, int32_t group,
+                  uint8_t *w_tiled, float *w_scale_t, hipStream_t stream);
 
 enum { OQ_OP_GEMM_W4A8 = 1, OQ_OP_GEMM_W4A4 = 2, OQ_OP_LINEAR = 3 };
 

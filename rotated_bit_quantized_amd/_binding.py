@@ -22,6 +22,7 @@ OQ_ROT_RPBH, OQ_ROT_DENSE32 = 1, 2
 OQ_A8, OQ_A6, OQ_A4, OQ_MXFP4 = 8, 6, 4, 0x104
 OQ_W4, OQ_W_MXFP4 = 4, 0x104
 OQ_OP_GEMM_W4A8, OQ_OP_GEMM_W4A4, OQ_OP_LINEAR = 1, 2, 3
+OQ_TILED = 0x10000
 
 
 class OQError(RuntimeError):
@@ -58,6 +59,8 @@ def _load():
         "oq_gemm_w4a4": ([ctypes.c_int, vp, i64, vp, i64, i32, vp, vp, i32, i32, vp, vp, vp, vp, i64, vp, sz, vp], ctypes.c_int),
         "oq_linear_fused": ([vp, i64, i32, i64, vp, ctypes.c_int, ctypes.c_int, vp, vp, i32, i32, vp, vp, vp, i64, vp, sz, vp], ctypes.c_int),
         "oq_workspace_bytes": ([ctypes.c_int, i64, i32, i32, ctypes.c_int], sz),
+        "oq_tiled_bytes": ([i64, i32], sz),
+        "oq_prepack_w4": ([vp, vp, i32, i32, i32, vp, vp, vp], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -68,7 +71,8 @@ def _load():
 
 _lib = _load()
 EXPORTED = ("oq_last_error", "oq_center", "oq_rotate", "oq_quant_act", "oq_quant_weight",
-            "oq_gemm_w4a8", "oq_gemm_w4a4", "oq_linear_fused", "oq_workspace_bytes")
+            "oq_gemm_w4a8", "oq_gemm_w4a4", "oq_linear_fused", "oq_workspace_bytes", "oq_tiled_bytes",
+            "oq_prepack_w4")
 
 
 def lib():
@@ -157,7 +161,10 @@ def oq_quant_act(x, rot: Optional[Rotation], afmt: int, center: bool = False, co
     x = _bits16(x)
     M, d = x.shape
     dev = _dev(x)
-    if codes is None:
+    if codes is None and afmt & OQ_TILED:
+        planes = 2 if (afmt & ~OQ_TILED) == OQ_A6 else 1
+        codes = torch.empty(max(1, planes * oq_tiled_bytes(M, d)), dtype=torch.uint8, device=dev)
+    elif codes is None:
         width = d if afmt in (OQ_A8, OQ_A6) else d // 2
         codes = torch.empty((M, width), dtype=torch.int8 if afmt in (OQ_A8, OQ_A6) else torch.uint8, device=dev)
     if afmt == OQ_MXFP4:
@@ -167,8 +174,9 @@ def oq_quant_act(x, rot: Optional[Rotation], afmt: int, center: bool = False, co
         scale = torch.empty(M, dtype=torch.float32, device=dev)
     if center and mean is None:
         mean = torch.empty(M, dtype=torch.float32, device=dev)
+    ldc = 0 if afmt & OQ_TILED else codes.stride(0) * codes.element_size()
     _check(_lib.oq_quant_act(_p(x), M, d, x.stride(0), _rref(rot), int(center), afmt, _p(codes),
-                             codes.stride(0) * codes.element_size(), _p(scale), _p(e8m0), _p(mean), _stream()))
+                             ldc, _p(scale), _p(e8m0), _p(mean), _stream()))
     return {"codes": codes, "scale": scale, "e8m0": e8m0, "mean": mean}
 
 
@@ -200,16 +208,36 @@ def oq_gemm_w4a8(qa, a_scale, w, w_scale, N: int, group: int, mean=None, w1=None
 
 
 def oq_gemm_w4a4(afmt: int, qa, a_scale, w, w_scale, N: int, group: int, mean=None, w1=None, bias=None,
-                 y=None, ws=None):
-    M = qa.shape[0]
-    K = qa.shape[1] * 2
+                 y=None, ws=None, M: Optional[int] = None, K: Optional[int] = None):
+    if afmt & OQ_TILED:
+        if M is None or K is None:
+            raise OQError(OQ_ERR_INVALID_ARG, "tiled operands need explicit M and K")
+        lda = 0
+    else:
+        M = qa.shape[0]
+        K = qa.shape[1] * 2
+        lda = qa.stride(0) * qa.element_size()
     if y is None:
         y = torch.empty((M, N), dtype=torch.bfloat16, device=_dev(qa))
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(_lib.oq_gemm_w4a4(afmt, _p(qa), qa.stride(0) * qa.element_size(), _p(a_scale), M, K, _p(w),
+    _check(_lib.oq_gemm_w4a4(afmt, _p(qa), lda, _p(a_scale), M, K, _p(w),
                              _p(w_scale), N, group, _p(mean), _p(w1), _p(bias), _p(y), y.stride(0), _p(ws), wsb,
                              _stream()))
     return y
+
+
+def oq_tiled_bytes(rows: int, K: int) -> int:
+    return int(_lib.oq_tiled_bytes(rows, K))
+
+
+def oq_prepack_w4(w, w_scale, N: int, K: int, group: int = 64, w_tiled=None, w_scale_t=None):
+    dev = _dev(w)
+    if w_tiled is None:
+        w_tiled = torch.empty(max(1, oq_tiled_bytes(N, K)), dtype=torch.uint8, device=dev)
+    if w_scale_t is None:
+        w_scale_t = torch.empty((K // 64, (N + 31) // 32 * 32), dtype=torch.float32, device=dev)
+    _check(_lib.oq_prepack_w4(_p(w), _p(w_scale), N, K, group, _p(w_tiled), _p(w_scale_t), _stream()))
+    return {"codes": w_tiled, "scales": w_scale_t}
 
 
 def oq_workspace_bytes(op: int, M: int, K: int, N: int, afmt: int) -> int:

@@ -94,10 +94,13 @@ struct LinearWs {
 
 LinearWs linear_ws(int64_t M, int K, int afmt) {
   LinearWs w;
-  w.ldc = (afmt == OQ_A8 || afmt == OQ_A6) ? K : K / 2;
+  const int base_fmt = afmt & ~OQ_TILED;
+  w.ldc = (base_fmt == OQ_A8 || base_fmt == OQ_A6) ? K : K / 2;
   w.ldc = (w.ldc + 15) & ~(int64_t)15;
   w.codes = 0;
-  w.scale = align_up((size_t)M * w.ldc);
+  const size_t code_bytes = (afmt & OQ_TILED) ? (size_t)(base_fmt == OQ_A6 ? 2 : 1) * tiled_bytes(M, K)
+                                              : (size_t)M * w.ldc;
+  w.scale = align_up(code_bytes);
   const size_t sbytes = afmt == OQ_MXFP4 ? (size_t)M * (K / 32) : (size_t)M * 4;
   w.mean = align_up(w.scale + sbytes);
   w.total = align_up(w.mean + (size_t)M * 4);
@@ -175,7 +178,8 @@ int oq_quant_act(const uint16_t *x, int64_t M, int32_t d, int64_t ldx, const oq_
   int rc = check_x("oq_quant_act", x, M, d, ldx);
   if (rc) return rc;
   if (M > 0 && !codes) return fail(OQ_ERR_INVALID_ARG, "oq_quant_act: codes is NULL");
-  if (!al16(codes) || ldc_bytes % 16) return fail(OQ_ERR_ALIGNMENT, "oq_quant_act: code rows must be 16-byte aligned");
+  if (!al16(codes) || (!(afmt & OQ_TILED) && ldc_bytes % 16))
+    return fail(OQ_ERR_ALIGNMENT, "oq_quant_act: code rows must be 16-byte aligned");
   if (afmt == OQ_MXFP4) {
     if (!rot || rot->kind != OQ_ROT_DENSE32)
       return fail(OQ_ERR_UNSUPPORTED, "oq_quant_act: MXFP4 activations need a DENSE32 rotation");
@@ -187,6 +191,24 @@ int oq_quant_act(const uint16_t *x, int64_t M, int32_t d, int64_t ldx, const oq_
     if (rc) return rc;
     g_err[0] = 0;
     return hip_status(launch_dense32(x, M, d, ldx, rot->mats, 1, codes, ldc_bytes, e8m0, stream), "oq_quant_act");
+  }
+  const bool tiled = (afmt & OQ_TILED) != 0;
+  const int base_fmt = afmt & ~OQ_TILED;
+  if (tiled) {
+    if (base_fmt != OQ_A4 && base_fmt != OQ_A6)
+      return fail(OQ_ERR_UNSUPPORTED, "oq_quant_act: the tiled layout exists for OQ_A4 and OQ_A6");
+    if (d % 64) return fail(OQ_ERR_UNSUPPORTED, "oq_quant_act: tiled codes need d %% 64 == 0 (d=%d)", d);
+    if (e8m0) return fail(OQ_ERR_INVALID_ARG, "oq_quant_act: e8m0 must be NULL for integer codes");
+    if (M > 0 && !scale) return fail(OQ_ERR_INVALID_ARG, "oq_quant_act: scale is NULL");
+    if (center && !mean) return fail(OQ_ERR_INVALID_ARG, "oq_quant_act: centering needs mean");
+    RotArgs ra;
+    rc = rot_args("oq_quant_act", rot, d, &ra);
+    if (rc) return rc;
+    g_err[0] = 0;
+    return hip_status(launch_rpbh_quant(x, M, d, ldx, ra, center ? 1 : 0, mean,
+                                        base_fmt == OQ_A4 ? OUT_FP6 : OUT_FP6X2, qmax_of(base_fmt), codes, 0,
+                                        scale, stream),
+                      "oq_quant_act");
   }
   if (afmt != OQ_A8 && afmt != OQ_A6 && afmt != OQ_A4)
     return fail(OQ_ERR_INVALID_ARG, "oq_quant_act: unknown afmt %d", afmt);
@@ -249,6 +271,21 @@ int oq_gemm_w4a4(int afmt, const uint8_t *qa, int64_t lda_bytes, const void *a_s
                  const float *bias, uint16_t *y, int64_t ldy, void *ws, size_t ws_bytes, hipStream_t stream) {
   (void)ws;
   (void)ws_bytes;
+  if (afmt & OQ_TILED) {
+    const int base_fmt = afmt & ~OQ_TILED;
+    int rc = check_gemm_common("oq_gemm_w4a4", qa, 16, M, K, w, w_scale, N, y, ldy, 0);
+    if (rc) return rc;
+    if (base_fmt != OQ_A4 && base_fmt != OQ_A6)
+      return fail(OQ_ERR_UNSUPPORTED, "oq_gemm_w4a4: tiled operands exist for OQ_A4 and OQ_A6");
+    if (group != 64) return fail(OQ_ERR_UNSUPPORTED, "oq_gemm_w4a4: tiled GEMM needs group 64 (got %d)", group);
+    rc = check_int_epilogue("oq_gemm_w4a4", K, group, mean, w1);
+    if (rc) return rc;
+    if (M > 0 && N > 0 && !a_scale) return fail(OQ_ERR_INVALID_ARG, "oq_gemm_w4a4: a_scale is NULL");
+    g_err[0] = 0;
+    return hip_status(launch_gemm_fp6(qa, base_fmt == OQ_A6 ? 2 : 1, (const float *)a_scale, M, K, w,
+                                      (const float *)w_scale, N, mean, w1, bias, y, ldy, stream),
+                      "oq_gemm_w4a4");
+  }
   int rc = check_gemm_common("oq_gemm_w4a4", qa, lda_bytes, M, K, w, w_scale, N, y, ldy, K / 2);
   if (rc) return rc;
   if (M > 0 && N > 0 && !a_scale) return fail(OQ_ERR_INVALID_ARG, "oq_gemm_w4a4: a_scale is NULL");
@@ -269,6 +306,22 @@ int oq_gemm_w4a4(int afmt, const uint8_t *qa, int64_t lda_bytes, const void *a_s
                     "oq_gemm_w4a4");
 }
 
+size_t oq_tiled_bytes(int64_t rows, int32_t K) {
+  if (rows < 0 || K <= 0) return 0;
+  return (size_t)tiled_bytes(rows, K);
+}
+
+int oq_prepack_w4(const uint8_t *w, const float *w_scale, int32_t N, int32_t K, int32_t group, uint8_t *w_tiled,
+                  float *w_scale_t, hipStream_t stream) {
+  if (N < 0) return fail(OQ_ERR_INVALID_ARG, "oq_prepack_w4: N < 0");
+  if (K <= 0 || K % 64) return fail(OQ_ERR_UNSUPPORTED, "oq_prepack_w4: K=%d must be a positive multiple of 64", K);
+  if (group != 64) return fail(OQ_ERR_UNSUPPORTED, "oq_prepack_w4: group must be 64 (got %d)", group);
+  if (N > 0 && (!w || !w_scale || !w_tiled || !w_scale_t)) return fail(OQ_ERR_INVALID_ARG, "oq_prepack_w4: NULL pointer");
+  if (!al16(w) || !al16(w_tiled)) return fail(OQ_ERR_ALIGNMENT, "oq_prepack_w4: misaligned");
+  g_err[0] = 0;
+  return hip_status(launch_prepack_w4(w, w_scale, N, K, w_tiled, w_scale_t, stream), "oq_prepack_w4");
+}
+
 size_t oq_workspace_bytes(int op, int64_t M, int32_t K, int32_t N, int afmt) {
   (void)N;
   if (op != OQ_OP_LINEAR || M < 0 || K <= 0) return 0;
@@ -281,6 +334,35 @@ int oq_linear_fused(const uint16_t *x, int64_t M, int32_t K, int64_t ldx, const 
   const char *fn = "oq_linear_fused";
   int rc = check_x(fn, x, M, K, ldx);
   if (rc) return rc;
+  if (afmt & OQ_TILED) {
+    const int base_fmt = afmt & ~OQ_TILED;
+    if (base_fmt != OQ_A4 && base_fmt != OQ_A6)
+      return fail(OQ_ERR_UNSUPPORTED, "%s: tiled operands exist for OQ_A4 and OQ_A6", fn);
+    if (K % 64) return fail(OQ_ERR_UNSUPPORTED, "%s: tiled operands need K %% 64 == 0", fn);
+    if (group != 64) return fail(OQ_ERR_UNSUPPORTED, "%s: tiled GEMM needs group 64 (got %d)", fn, group);
+    const LinearWs L = linear_ws(M, K, afmt);
+    if (M > 0 && (!ws || ws_bytes < L.total))
+      return fail(OQ_ERR_WORKSPACE, "%s: workspace of %zu bytes required (got %zu)", fn, L.total, ws_bytes);
+    if (ws && !al16(ws)) return fail(OQ_ERR_ALIGNMENT, "%s: workspace must be 16-byte aligned", fn);
+    rc = check_gemm_common(fn, x, 16, M, K, w, w_scale, N, y, ldy, 0);
+    if (rc) return rc;
+    if (center && !w1) return fail(OQ_ERR_INVALID_ARG, "%s: centering needs w1", fn);
+    RotArgs ra;
+    rc = rot_args(fn, rot, K, &ra);
+    if (rc) return rc;
+    char *wsb = static_cast<char *>(ws);
+    uint8_t *codes = reinterpret_cast<uint8_t *>(wsb + L.codes);
+    float *scale = reinterpret_cast<float *>(wsb + L.scale);
+    float *mean = reinterpret_cast<float *>(wsb + L.mean);
+    g_err[0] = 0;
+    rc = hip_status(launch_rpbh_quant(x, M, K, ldx, ra, center ? 1 : 0, mean, base_fmt == OQ_A4 ? OUT_FP6 : OUT_FP6X2,
+                                      qmax_of(base_fmt), codes, 0, scale, stream),
+                    fn);
+    if (rc) return rc;
+    return hip_status(launch_gemm_fp6(codes, base_fmt == OQ_A6 ? 2 : 1, scale, M, K, w, (const float *)w_scale, N,
+                                      center ? mean : nullptr, center ? w1 : nullptr, bias, y, ldy, stream),
+                      fn);
+  }
   if (afmt != OQ_A8 && afmt != OQ_A6 && afmt != OQ_A4 && afmt != OQ_MXFP4)
     return fail(OQ_ERR_INVALID_ARG, "%s: unknown afmt %d", fn, afmt);
   const LinearWs L = linear_ws(M, K, afmt);

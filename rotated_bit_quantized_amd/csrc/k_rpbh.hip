@@ -221,6 +221,35 @@ rpbh_quant_kernel(const void *__restrict__ xin, int64_t M, int d, int64_t ldx,
       const float tq = __builtin_rintf(v[j] * inv);
       q[j] = (int)fminf(fmaxf(tq, -fq), fq);
     }
+    if (MODE == OUT_FP6 || MODE == OUT_FP6X2) {
+      // tiled layout: (row, k-group) tile of 6 x 8-byte chunks; this thread's
+      // 16 values are 96 bits starting at bit 6 * (base % 32) of its half
+      const int kg = base >> 6, hf = (base >> 5) & 1, j0 = base & 31;
+      uint8_t *tile = static_cast<uint8_t *>(out) + ((row >> 5) * (d >> 6) + kg) * 1536 + (row & 31) * 8;
+      const int64_t pstride = tiled_bytes(M, d);
+#pragma unroll
+      for (int p = 0; p < (MODE == OUT_FP6X2 ? 2 : 1); ++p) {
+        uint32_t c[E];
+#pragma unroll
+        for (int j = 0; j < E; ++j)
+          c[j] = fp6_e2m3_of_int(MODE == OUT_FP6 ? q[j] : (p == 0 ? (q[j] >> 3) : (q[j] & 7)));
+        uint64_t lo = 0;
+#pragma unroll
+        for (int j = 0; j < 10; ++j) lo |= (uint64_t)c[j] << (6 * j);
+        lo |= (uint64_t)(c[10] & 0xFu) << 60;
+        const uint32_t w0 = (uint32_t)lo, w1 = (uint32_t)(lo >> 32);
+        const uint32_t w2 = (c[10] >> 4) | (c[11] << 2) | (c[12] << 8) | (c[13] << 14) | (c[14] << 20) | (c[15] << 26);
+        uint8_t *tp = tile + p * pstride;
+        if (j0 == 0) {
+          *reinterpret_cast<uint2 *>(tp + (3 * hf) * 256) = make_uint2(w0, w1);
+          *reinterpret_cast<uint32_t *>(tp + (3 * hf + 1) * 256) = w2;
+        } else {
+          *reinterpret_cast<uint32_t *>(tp + (3 * hf + 1) * 256 + 4) = w0;
+          *reinterpret_cast<uint2 *>(tp + (3 * hf + 2) * 256) = make_uint2(w1, w2);
+        }
+      }
+      continue;
+    }
     char *orow = reinterpret_cast<char *>(out) + row * ld_out_bytes;
     if (MODE == OUT_I8) {
       uint32_t wd[4];
@@ -267,6 +296,8 @@ hipError_t launch_mode(int mode, const uint16_t *x, int64_t M, int d, int64_t ld
     case OUT_F32: return launch_t<ROUNDS, OUT_F32, false>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, 0, stream);
     case OUT_I8: return launch_t<ROUNDS, OUT_I8, false>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, 0, stream);
     case OUT_I4: return launch_t<ROUNDS, OUT_I4, false>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, 0, stream);
+    case OUT_FP6: return launch_t<ROUNDS, OUT_FP6, false>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, 0, stream);
+    case OUT_FP6X2: return launch_t<ROUNDS, OUT_FP6X2, false>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, 0, stream);
   }
   return hipErrorInvalidValue;
 }

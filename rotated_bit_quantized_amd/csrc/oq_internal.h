@@ -24,6 +24,19 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// FP6 E2M3 bit pattern of an integer code q in [-7, 7] (exact: sign bit 5,
+// exponent bits 4..3 with bias 1, mantissa bits 2..0).  The magnitude goes
+// through an 8-entry byte table held in two dwords (v_perm_b32).
+__device__ __forceinline__ uint32_t fp6_e2m3_of_int(int q) {
+  const uint32_t a = (uint32_t)(q < 0 ? -q : q);
+  // |q| = 0..7 -> 0x00 0x08 0x10 0x14 0x18 0x1A 0x1C 0x1E
+  const uint32_t code = __builtin_amdgcn_perm(0x1E1C1A18u, 0x14100800u, a) & 0xFFu;
+  return code | (q < 0 ? 0x20u : 0u);
+}
+
+// bytes of one plane of the tiled FP6 operand layout (rows padded to 32)
+__host__ __device__ inline int64_t tiled_bytes(int64_t rows, int K) { return (rows + 31) / 32 * (K / 64) * 1536; }
+
 // activation code formats used inside the library (values of the public enum
 // for the integer widths; internal operand layouts are separate constants)
 enum OutMode : int {
@@ -31,6 +44,8 @@ enum OutMode : int {
   OUT_I8 = 1,    // int8 codes (A8, A6)
   OUT_I4 = 2,    // packed nibbles (A4)
   OUT_W4G = 3,   // per-group INT4 codes + scales (offline weight fold)
+  OUT_FP6 = 4,   // A4 codes as FP6 E2M3 in the tiled MFMA operand layout
+  OUT_FP6X2 = 5, // A6 codes split q = 8 qh + ql into two tiled FP6 planes
 };
 
 // -------------------------------------------------------- kernel launchers --
@@ -60,6 +75,13 @@ hipError_t launch_gemm_int(const void *qa, int64_t lda_bytes, int a_is_nibble,
                            const uint8_t *w, const float *w_scale, int N, int group,
                            const float *mean, const float *w1, const float *bias,
                            uint16_t *y, int64_t ldy, hipStream_t stream);
+
+// Tiled FP6 GEMM (A4: planes = 1, A6: planes = 2); weights from prepack.
+hipError_t launch_gemm_fp6(const uint8_t *A, int planes, const float *a_scale, int64_t M, int K, const uint8_t *W,
+                           const float *wst, int N, const float *mean, const float *w1, const float *bias,
+                           uint16_t *y, int64_t ldy, hipStream_t stream);
+hipError_t launch_prepack_w4(const uint8_t *w, const float *ws, int N, int K, uint8_t *out, float *out_s,
+                             hipStream_t stream);
 
 // K5: MXFP4 x MXFP4 with E8M0 block scales (scaled FP4 MFMA).
 hipError_t launch_gemm_mx(const uint8_t *qa, int64_t lda_bytes, const uint8_t *a_e8m0,
