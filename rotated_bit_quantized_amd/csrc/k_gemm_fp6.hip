@@ -25,8 +25,12 @@
 // Workgroup: WM x WN wavefronts, each computing 128 x 64 outputs (4 x 2 MFMA
 // tiles of 32 x 32).  The k loop walks the 64-wide groups; each group's A, B
 // and scale tiles are copied global -> LDS with global_load_lds_dwordx4
-// (no register staging) into a 3-stage ring, one barrier per group.
+// (no register staging) into a 4-stage ring, one barrier per group.
 #include "oq_internal.h"
+
+#ifndef FP6_STAGES
+#define FP6_STAGES 3
+#endif
 
 namespace oq {
 namespace {
@@ -36,7 +40,6 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int CHUNK_TILE = 1536;  // bytes of one 32-row x 64-k tile
-constexpr int STAGES = 3;
 
 __device__ __forceinline__ void dma16(const void *g, void *lds_wave_base) {
   __builtin_amdgcn_global_load_lds(g, (lds_void *)lds_wave_base, 16, 0, 0);
@@ -50,8 +53,25 @@ __device__ __forceinline__ v8i frag(const uint8_t *tile, int half, int r) {
   return (v8i){(int)a.x, (int)a.y, (int)b.x, (int)b.y, (int)c.x, (int)c.y, 0, 0};
 }
 
-template <int WM, int WN, int PLANES>
+// s_waitcnt vmcnt(n) for a wave-uniform runtime n (the immediate must be a
+// constant, so dispatch over the possible values; n above C waits for C)
+template <int C>
+__device__ __forceinline__ void wait_vmcnt_le(int n) {
+  if (n >= C) {
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (C & 0xF) | ((C >> 4) << 14));
+    return;
+  }
+  if constexpr (C > 0) wait_vmcnt_le<C - 1>(n);
+}
+
+template <int UPW, int AHEAD>
+__device__ __forceinline__ void wait_copies(int n) {
+  wait_vmcnt_le<UPW * AHEAD>(n);
+}
+
+template <int WM, int WN, int PLANES, int NSTAGE>
 struct Cfg {
+  static constexpr int STAGES = NSTAGE;
   static constexpr int BM = 128 * WM, BN = 64 * WN;
   static constexpr int A_BYTES = PLANES * (BM / 32) * CHUNK_TILE;
   static constexpr int B_BYTES = (BN / 32) * CHUNK_TILE;
@@ -60,16 +80,21 @@ struct Cfg {
   static constexpr int UNITS = STAGE / 1024;          // 1 KiB DMA units per stage
   static constexpr int WAVES = WM * WN;
   static constexpr int UPW = (UNITS + WAVES - 1) / WAVES;
+  // after the ring: the workgroup's per-row activation scale and mean
+  static constexpr int ROWS_OFF = STAGES * STAGE;
+  static constexpr int LDS_BYTES = ROWS_OFF + 2 * BM * 4;
   static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "stage regions must be whole units");
+  static_assert(STAGES >= 3 && STAGES <= 6, "prefetch depth");
 };
 
-template <int WM, int WN, int PLANES>
+template <int WM, int WN, int PLANES, int NSTAGE>
 __global__ void __launch_bounds__(64 * WM * WN)
 gemm_fp6_kernel(const uint8_t *__restrict__ A, int64_t a_plane_bytes, const float *__restrict__ a_scale, int64_t M,
                 int K, const uint8_t *__restrict__ W, const float *__restrict__ wst, int N, int Np,
                 const float *__restrict__ mean, const float *__restrict__ w1, const float *__restrict__ bias,
                 uint16_t *__restrict__ y, int64_t ldy) {
-  using C = Cfg<WM, WN, PLANES>;
+  using C = Cfg<WM, WN, PLANES, NSTAGE>;
+  constexpr int STAGES = C::STAGES;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -108,15 +133,17 @@ gemm_fp6_kernel(const uint8_t *__restrict__ A, int64_t a_plane_bytes, const floa
       inc[q] = (int64_t)Np * 4;
     }
   }
+  const int nq = (C::UNITS - wave + C::WAVES - 1) / C::WAVES;  // units this wave copies per group
 
-  auto issue = [&](int ks) {
+  auto issue_unit = [&](int q, int ks) {
     uint8_t *stage = smem + (ks % STAGES) * C::STAGE;
+    if (uoff[q] >= 0) dma16(src[q] + (int64_t)ks * inc[q], stage + uoff[q]);
+  };
+  auto issue = [&](int ks) {
 #pragma unroll
-    for (int q = 0; q < C::UPW; ++q)
-      if (uoff[q] >= 0) dma16(src[q] + (int64_t)ks * inc[q], stage + uoff[q]);
+    for (int q = 0; q < C::UPW; ++q) issue_unit(q, ks);
   };
 
-  const int nq = (C::UNITS - wave + C::WAVES - 1) / C::WAVES;  // units this wave copies per group
   const int wm = wave / WN, wn = wave % WN;
   const int r = lane & 31, half = lane >> 5;
 
@@ -128,78 +155,136 @@ gemm_fp6_kernel(const uint8_t *__restrict__ A, int64_t a_plane_bytes, const floa
 #pragma unroll
       for (int e = 0; e < 16; ++e) F[i][j][e] = 0.f;
 
-  issue(0);
-  if (G > 1) issue(1);
-  for (int ks = 0; ks < G; ++ks) {
-    // wait until this wave's copies for group ks have landed: the copies of
-    // group ks+1 (nq per wave) may still be in flight
-    if (ks + 1 < G) {
-      if (nq == C::UPW)
-        __builtin_amdgcn_s_waitcnt(0x0F70 | (C::UPW & 0xF));
-      else
-        __builtin_amdgcn_s_waitcnt(0x0F70 | ((C::UPW - 1) & 0xF));
-    } else {
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    }
-    // a bare barrier: the wait above already covers this wave's copies, and a
-    // fenced __syncthreads() would also drain the copies of group ks+1
-    __builtin_amdgcn_s_barrier();
-    if (ks + 2 < G) issue(ks + 2);
-
-    const uint8_t *stage = smem + (ks % STAGES) * C::STAGE;
-    const uint8_t *sA = stage;
-    const uint8_t *sB = stage + C::A_BYTES;
-    const float *sS = reinterpret_cast<const float *>(stage + C::A_BYTES + C::B_BYTES);
-    v8i b[2];
-    float s[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      b[j] = frag(sB + (wn * 2 + j) * CHUNK_TILE, half, r);
-      s[j] = sS[wn * 64 + 32 * j + r];
-    }
-    // software pipeline over the 8 tiles: the MFMA of tile t+1 is issued
-    // before the fp32 updates of tile t, so the matrix core and the VALU overlap
-    v16f dprev = (v16f){};
-#pragma unroll
-    for (int t = 0; t <= 8; ++t) {
-      v16f dnext;
-      if (t < 8) {
-        const int i = t >> 1, j = t & 1;
-        const v8i a = frag(sA + (wm * 4 + i) * CHUNK_TILE, half, r);
-        if (PLANES == 2) {
-          const v8i a2 = frag(sA + (C::BM / 32) * CHUNK_TILE + (wm * 4 + i) * CHUNK_TILE, half, r);
-          dnext = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b[j], (v16f){}, 2, 2, 0, 130, 0, 127);
-          dnext = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a2, b[j], dnext, 2, 2, 0, 127, 0, 127);
-        } else {
-          dnext = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b[j], (v16f){}, 2, 2, 0, 127, 0, 127);
-        }
-      }
-      if (t > 0) {
-        const int i = (t - 1) >> 1, j = (t - 1) & 1;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) F[i][j][e] = __builtin_fmaf(s[j], dprev[e], F[i][j][e]);
-      }
-      if (t < 8) dprev = dnext;
-    }
+  // per-row scale and mean of this workgroup's rows, read by the epilogue;
+  // the first barrier of the k loop publishes them
+  float *lds_alpha = reinterpret_cast<float *>(smem + C::ROWS_OFF);
+  float *lds_mean = lds_alpha + C::BM;
+  for (int t = threadIdx.x; t < C::BM; t += 64 * C::WAVES) {
+    const int64_t row = m0 + t;
+    lds_alpha[t] = row < M ? a_scale[row] : 0.f;
+    lds_mean[t] = (mean && row < M) ? mean[row] : 0.f;
   }
 
-  // ---- epilogue: y = a_scale * F + mean * w1 + bias (same order as the int8 kernel)
+#pragma unroll
+  for (int p = 0; p < STAGES - 1; ++p)
+    if (p < G) issue(p);
+
+  // Each group's 8 tiles t = (i, j) run as MFMA(t+1) then the 16 fp32 updates
+  // of tile t, with hard scheduling fences so the matrix core works on tile
+  // t+1 while the VALU folds tile t.  The updates of the last tile of group
+  // ks run after the barrier of group ks+1, under its LDS fragment reads.
+  v16f dlast = (v16f){};
+  float slast = 0.f;
+  for (int ks = 0; ks < G; ++ks) {
+    // this wave's copies of group ks have landed once at most the copies of
+    // the groups issued after it (nq per group) are outstanding
+    const int ahead = min(STAGES - 2, G - 1 - ks);
+    wait_copies<C::UPW, STAGES - 2>(nq == C::UPW ? ahead * C::UPW : ahead * (C::UPW - 1));
+    // a bare barrier: the wait above covers this wave's copies; a fenced
+    // __syncthreads() would also drain the copies still in flight
+    __builtin_amdgcn_s_barrier();
+    const bool refill = ks + STAGES - 1 < G;  // refills the stage consumed at ks-1
+
+    const uint8_t *stage = smem + (ks % STAGES) * C::STAGE;
+    const uint8_t *sA = stage + (wm * 4) * CHUNK_TILE;
+    const uint8_t *sB = stage + C::A_BYTES + (wn * 2) * CHUNK_TILE;
+    const float *sS = reinterpret_cast<const float *>(stage + C::A_BYTES + C::B_BYTES) + wn * 64 + r;
+    const v8i b0 = frag(sB, half, r), b1 = frag(sB + CHUNK_TILE, half, r);
+    const float s0 = sS[0], s1 = sS[32];
+    v8i a[4], a2[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = frag(sA + i * CHUNK_TILE, half, r);
+      if (PLANES == 2) a2[i] = frag(sA + (C::BM / 32) * CHUNK_TILE + i * CHUNK_TILE, half, r);
+    }
+    // last tile of the previous group (zero contribution before the first)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) F[3][1][e] = __builtin_fmaf(slast, dlast[e], F[3][1][e]);
+    __builtin_amdgcn_sched_barrier(0);
+
+    v16f dprev;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int i = t >> 1;
+      const v8i &bb = (t & 1) ? b1 : b0;
+      v16f dt;
+      if (PLANES == 2) {
+        dt = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], bb, (v16f){}, 2, 2, 0, 130, 0, 127);
+        dt = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a2[i], bb, dt, 2, 2, 0, 127, 0, 127);
+      } else {
+        dt = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], bb, (v16f){}, 2, 2, 0, 127, 0, 127);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // this wave's copies for group ks+STAGES-1 go out one per tile, so a
+      // full copy queue stalls one tile instead of the whole group
+      if (t < C::UPW && refill) {
+        issue_unit(t, ks + STAGES - 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (t > 0) {
+        const int ip = (t - 1) >> 1, jp = (t - 1) & 1;
+        const float sp = jp ? s1 : s0;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) F[ip][jp][e] = __builtin_fmaf(sp, dprev[e], F[ip][jp][e]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      dprev = dt;
+    }
+    dlast = dprev;
+    slast = s1;
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) F[3][1][e] = __builtin_fmaf(slast, dlast[e], F[3][1][e]);
+
+  // ---- epilogue: y = a_scale * F + mean * w1 + bias (same order as the int8
+  // kernel), converted to bf16 and staged per 32-row slab in LDS so that the
+  // global writes are full 16-byte runs (8 lanes cover one 128-byte row piece)
+  float w1v[2] = {0.f, 0.f}, bv[2] = {0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int col = n0 + wn * 64 + 32 * j + r;
+    if (col < N) {
+      if (mean) w1v[j] = w1[col];
+      if (bias) bv[j] = bias[col];
+    }
+  }
+  __syncthreads();  // every wave is done with the ring; reuse it for staging
+  constexpr int SROW = 144;  // padded bytes per staged row of 64 bf16
+  uint8_t *stg = smem + wave * (32 * SROW);
+  const bool vec_ok = ((reinterpret_cast<uintptr_t>(y) & 15) == 0) && (ldy % 8 == 0);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int64_t row = m0 + wm * 128 + 32 * i + (e >> 2) * 8 + half * 4 + (e & 3);
-      if (row >= M) continue;
-      const float al = a_scale[row];
-      const float mu = mean ? mean[row] : 0.f;
+      const int rr = (e >> 2) * 8 + half * 4 + (e & 3);
+      const int rl = wm * 128 + 32 * i + rr;
+      const float al = lds_alpha[rl];
+      const float mu = lds_mean[rl];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int col = n0 + wn * 64 + 32 * j + r;
-        if (col >= N) continue;
         float v = al * F[i][j][e];
-        if (mean) v = __builtin_fmaf(mu, w1[col], v);
-        if (bias) v = v + bias[col];
-        y[row * ldy + col] = f32_to_bf16_rne(v);
+        if (mean) v = __builtin_fmaf(mu, w1v[j], v);
+        if (bias) v = v + bv[j];
+        *reinterpret_cast<uint16_t *>(stg + rr * SROW + (32 * j + r) * 2) = f32_to_bf16_rne(v);
+      }
+    }
+    // read back 16 bytes per lane: rows lane/8 + 8q, columns (lane%8)*8 .. +7
+    const int cl = (lane & 7) * 8;
+    const int col = n0 + wn * 64 + cl;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int rr = (lane >> 3) + 8 * q;
+      const int64_t row = m0 + wm * 128 + 32 * i + rr;
+      const uint4 v = *reinterpret_cast<const uint4 *>(stg + rr * SROW + cl * 2);
+      if (row >= M) continue;
+      uint16_t *dst = y + row * ldy + col;
+      if (vec_ok && col + 8 <= N) {
+        *reinterpret_cast<uint4 *>(dst) = v;
+      } else {
+        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          if (col + c < N) dst[c] = (uint16_t)(wv[c >> 1] >> (16 * (c & 1)));
       }
     }
   }
@@ -245,22 +330,22 @@ __global__ void prepack_w4_kernel(const uint8_t *__restrict__ w, const float *__
   if (half == 0) out_s[(int64_t)kg * Np + row] = row < N ? ws[(int64_t)row * G + kg] : 0.f;
 }
 
-template <int WM, int WN, int PLANES>
+template <int WM, int WN, int PLANES, int NSTAGE>
 hipError_t launch_cfg(const uint8_t *A, int64_t a_plane_bytes, const float *a_scale, int64_t M, int K,
                       const uint8_t *W, const float *wst, int N, int Np, const float *mean, const float *w1,
                       const float *bias, uint16_t *y, int64_t ldy, hipStream_t stream) {
-  using C = Cfg<WM, WN, PLANES>;
-  const size_t lds = (size_t)STAGES * C::STAGE;
+  using C = Cfg<WM, WN, PLANES, NSTAGE>;
+  const size_t lds = (size_t)C::LDS_BYTES;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)gemm_fp6_kernel<WM, WN, PLANES>,
+    hipError_t e = hipFuncSetAttribute((const void *)gemm_fp6_kernel<WM, WN, PLANES, NSTAGE>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   dim3 grid((unsigned)((N + C::BN - 1) / C::BN), (unsigned)((M + C::BM - 1) / C::BM));
-  hipLaunchKernelGGL((gemm_fp6_kernel<WM, WN, PLANES>), grid, dim3(64 * C::WAVES), lds, stream, A, a_plane_bytes,
-                     a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy);
+  hipLaunchKernelGGL((gemm_fp6_kernel<WM, WN, PLANES, NSTAGE>), grid, dim3(64 * C::WAVES), lds, stream, A,
+                     a_plane_bytes, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy);
   return hipGetLastError();
 }
 
@@ -272,8 +357,8 @@ hipError_t launch_gemm_fp6(const uint8_t *A, int planes, const float *a_scale, i
   if (M == 0 || N == 0) return hipSuccess;
   const int Np = (N + 31) / 32 * 32;
   const int64_t plane = tiled_bytes(M, K);
-  if (planes == 2) return launch_cfg<2, 4, 2>(A, plane, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy, stream);
-  return launch_cfg<2, 4, 1>(A, plane, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy, stream);
+  if (planes == 2) return launch_cfg<2, 4, 2, 3>(A, plane, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy, stream);
+  return launch_cfg<2, 4, 1, FP6_STAGES>(A, plane, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy, stream);
 }
 
 hipError_t launch_prepack_w4(const uint8_t *w, const float *ws, int N, int K, uint8_t *out, float *out_s,

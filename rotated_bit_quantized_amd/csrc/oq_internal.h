@@ -16,12 +16,9 @@ int fail(int code, const char *fmt, ...);
 __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
 
-// float32 -> bfloat16 bits, round to nearest even (finite values; NaN kept quiet)
+// float32 -> bfloat16 bits, IEEE round to nearest even (gfx950 v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (uint16_t)((u >> 16) | 0x40);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 // FP6 E2M3 bit pattern of an integer code q in [-7, 7] (exact: sign bit 5,
