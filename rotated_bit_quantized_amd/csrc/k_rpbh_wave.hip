@@ -1,0 +1,432 @@
+// K1 (activation path): per-token (center) -> RPBH rounds -> absmax quantize
+// -> pack, one wavefront per token row, gfx950.
+//
+// Same arithmetic as the workgroup kernel in k_rpbh.hip (CentriQ Sec. 4.2
+// Eq. 4 centering; OrbitQuant PR #25 RPBH rounds; CentriQ Sec. 3 Eq. 1
+// absmax codes), organised so that the row loop has no workgroup barrier:
+//   * lane l owns, for each 1024-wide slot s of the row, the 16 consecutive
+//     coordinates 1024 s + 16 l + j (j = 0..15);
+//   * each wave keeps its row in LDS twice, as +x and -x; the gather offset
+//     of output i points into the copy whose sign is s_r[i], so the gather
+//     applies the sign.  The offsets of every round live in a workgroup LDS
+//     table written once, read per row with 16-byte loads;
+//   * the first round gathers bfloat16 copies (the loaded words and their
+//     sign-flipped twins, no conversion on the write side); centering
+//     subtracts s_i m after the gather, which equals s_i RN32(x - m);
+//     a second round gathers float32 copies of the first round's outputs;
+//   * butterfly stages of stride 1..8 run in registers, strides 16..h/2
+//     exchange between lanes (DPP for lane distance 1 and 2, ds_swizzle for
+//     4, 8, 16, ds_bpermute for 32), each output rounded once:
+//     low lane a + b, high lane a - b (an fma with +-1);
+//   * when h is a power of 4, 1/sqrt(h) is a power of two: the per-round
+//     multiply is exact and is deferred into the quantization scale
+//     (identical codes and scales; the float32 output mode applies it);
+//   * the row range (absmax) is a wavefront reduction.
+#include "oq_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace oq {
+namespace {
+
+constexpr int WAVES_PER_WG = 4;
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef unsigned v6u __attribute__((ext_vector_type(6)));
+
+__device__ __forceinline__ float xlane(float v, int lg) {
+  const int iv = __float_as_int(v);
+  switch (lg) {
+    case 0: return __int_as_float(__builtin_amdgcn_mov_dpp(iv, 0xB1, 0xF, 0xF, true));  // lane ^ 1
+    case 1: return __int_as_float(__builtin_amdgcn_mov_dpp(iv, 0x4E, 0xF, 0xF, true));  // lane ^ 2
+    case 2: return __int_as_float(__builtin_amdgcn_ds_swizzle(iv, 0x1F | (4 << 10)));
+    case 3: return __int_as_float(__builtin_amdgcn_ds_swizzle(iv, 0x1F | (8 << 10)));
+    case 4: return __int_as_float(__builtin_amdgcn_ds_swizzle(iv, 0x1F | (16 << 10)));
+    default: return __shfl_xor(v, 32);
+  }
+}
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+template <int SLOTS>
+__device__ __forceinline__ void fwht_row(float (&v)[SLOTS][16], int lane, int nl) {
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s)
+#pragma unroll
+    for (int st = 1; st < 16; st <<= 1)
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if ((j & st) == 0) {
+          const float a = v[s][j], b = v[s][j + st];
+          v[s][j] = a + b;
+          v[s][j + st] = a - b;
+        }
+#pragma unroll
+  for (int lg = 0; lg < 6; ++lg) {
+    const int mm = 1 << lg;
+    if (mm >= nl) break;
+    const float sg = (lane & mm) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[s][j] = __builtin_fmaf(v[s][j], sg, xlane(v[s][j], lg));
+  }
+}
+
+// Stores the 16 codes of two slots (a: coordinates base..base+15, b: the same
+// 1024 further on) in the tiled layout (see k_gemm_fp6.hip): 16 consecutive
+// codes are the 96-bit string at bit 6 (base % 32) of their half of the
+// k-group.  The codes arrive as integer-valued floats (+0 for zero) and are
+// converted with v_cvt_scalef32_2xpk16_fp6_f32 (exact: |t| <= 7 or a plane of
+// it), which interleaves its sources: field 2k from src0[k], 2k+1 from
+// src1[k].  part: 0 the codes, 1 the high plane floor(t/8), 2 the low plane
+// t - 8 floor(t/8).
+__device__ __forceinline__ void store_fp6_pair(const float (&ta)[16], const float (&tb)[16], int part,
+                                               uint8_t *tile_row, int base, bool wa, bool wb) {
+  v16f s0, s1;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    float e0 = k < 8 ? ta[2 * k] : tb[2 * k - 16];
+    float e1 = k < 8 ? ta[2 * k + 1] : tb[2 * k - 15];
+    if (part) {
+      const float h0 = __builtin_floorf(e0 * 0.125f), h1 = __builtin_floorf(e1 * 0.125f);
+      e0 = part == 1 ? h0 + 0.0f : __builtin_fmaf(h0, -8.0f, e0);
+      e1 = part == 1 ? h1 + 0.0f : __builtin_fmaf(h1, -8.0f, e1);
+    }
+    s0[k] = e0;
+    s1[k] = e1;
+  }
+  const v6u pk = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(s0, s1, 1.0f);
+  // base % 64 is 16 j0' with j0' in 0..3 (lane parity picks the half word)
+  const int kg = base >> 6, hf = (base >> 5) & 1, j0 = base & 31;
+  uint8_t *tp = tile_row + kg * 1536 + (3 * hf) * 256;
+  // slot b lies 1024 coordinates on: 16 k-groups further, same half and offset
+  uint8_t *tq = tp + 16 * 1536;
+  if (j0 == 0) {
+    if (wa) {
+      *reinterpret_cast<uint2 *>(tp) = make_uint2(pk[0], pk[1]);
+      *reinterpret_cast<uint32_t *>(tp + 256) = pk[2];
+    }
+    if (wb) {
+      *reinterpret_cast<uint2 *>(tq) = make_uint2(pk[3], pk[4]);
+      *reinterpret_cast<uint32_t *>(tq + 256) = pk[5];
+    }
+  } else {
+    if (wa) {
+      *reinterpret_cast<uint32_t *>(tp + 256 + 4) = pk[0];
+      *reinterpret_cast<uint2 *>(tp + 512) = make_uint2(pk[1], pk[2]);
+    }
+    if (wb) {
+      *reinterpret_cast<uint32_t *>(tq + 256 + 4) = pk[3];
+      *reinterpret_cast<uint2 *>(tq + 512) = make_uint2(pk[4], pk[5]);
+    }
+  }
+}
+
+// LDS: [offset table: ROUNDS x SLOTS x 4 x 64 lanes x 4 ints][per wave: row copies]
+template <int SLOTS, int ROUNDS>
+struct WaveLds {
+  static constexpr int TABLE = (ROUNDS > 0 ? ROUNDS : 1) * SLOTS * 1024 * 4;
+  static constexpr int ROWBUF = (ROUNDS == 2 ? 8 : 4) * SLOTS * 1024;  // 2 copies, float32 if 2 rounds
+  static constexpr int TOTAL = TABLE + WAVES_PER_WG * ROWBUF;
+};
+
+template <int SLOTS, int ROUNDS>
+__global__ void __launch_bounds__(64 * WAVES_PER_WG)
+rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, const int32_t *__restrict__ perm,
+                 const int8_t *__restrict__ signs, int h, float c_h, int pow4, int center,
+                 float *__restrict__ mean_out, int mode, int qmax, void *__restrict__ out, int64_t ld_out_bytes,
+                 float *__restrict__ scale_out) {
+  using L = WaveLds<SLOTS, ROUNDS>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  int *table = reinterpret_cast<int *>(lds_raw);
+  uint8_t *buf = lds_raw + L::TABLE + wave * L::ROWBUF;
+  const int nl = h >> 4;  // lanes per Hadamard block
+
+  // ---- offset table: byte offsets into this wave's [+row | -row] buffer;
+  // round 1 copies are bf16 (2 bytes), round 2 copies float32
+  for (int t = threadIdx.x; t < (ROUNDS > 0 ? ROUNDS : 0) * SLOTS * 1024; t += 64 * WAVES_PER_WG) {
+    const int r = t / (SLOTS * 1024);
+    const int rem = t % (SLOTS * 1024);
+    const int s = rem / 1024, l = (rem / 16) % 64, j = rem % 16;
+    const int i = 1024 * s + 16 * l + j;
+    int o = 0;
+    if (i < d) {
+      const int src = perm[(int64_t)r * d + i] + (signs[(int64_t)r * d + i] < 0 ? d : 0);
+      o = src * (r == 0 ? 2 : 4);
+    }
+    table[(((r * SLOTS + s) * 4 + (j >> 2)) * 64 + l) * 4 + (j & 3)] = o;
+  }
+  __syncthreads();
+
+  bool act[SLOTS];
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s) act[s] = 1024 * s + 16 * lane < d;
+  const float c_all = (ROUNDS == 0 || !pow4) ? 1.0f : (ROUNDS == 2 ? c_h * c_h : c_h);  // deferred, exact
+  const int neg_from = 2 * d;  // round-1 byte offsets at or above this hit the -x copy
+
+  const int64_t step = (int64_t)gridDim.x * WAVES_PER_WG;
+  // the next row's words are loaded while the current row is processed (the
+  // index is clamped to the last row, so the final prefetch stays in bounds);
+  // lanes beyond the row end read their own first word instead
+  uint4 nxt[SLOTS][2];
+  auto load_row = [&](int64_t rr) {
+    const uint16_t *xr = x + (rr < M ? rr : M - 1) * ldx;
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) {
+      const uint4 *src = reinterpret_cast<const uint4 *>(xr + (act[s] ? 1024 * s + 16 * lane : 0));
+      nxt[s][0] = src[0];
+      nxt[s][1] = src[1];
+    }
+  };
+  int64_t row = (int64_t)blockIdx.x * WAVES_PER_WG + wave;
+  if (row < M) load_row(row);
+  for (; row < M; row += step) {
+    float v[SLOTS][16];
+    uint4 raw[SLOTS][2];
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) {
+      raw[s][0] = nxt[s][0];
+      raw[s][1] = nxt[s][1];
+    }
+    load_row(row + step);
+
+    float m = 0.f;
+    if (center) {
+      double sum = 0.0;
+#pragma unroll
+      for (int s = 0; s < SLOTS; ++s) {
+        const uint32_t w[8] = {raw[s][0].x, raw[s][0].y, raw[s][0].z, raw[s][0].w,
+                               raw[s][1].x, raw[s][1].y, raw[s][1].z, raw[s][1].w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (act[s]) sum += (double)bf16_lo(w[k]) + (double)bf16_hi(w[k]);
+      }
+      sum = wave_sum_d(sum);
+      m = (float)(sum / (double)d);
+      if (lane == 0) mean_out[row] = m;
+    }
+
+    if (ROUNDS == 0) {
+#pragma unroll
+      for (int s = 0; s < SLOTS; ++s) {
+        const uint32_t w[8] = {raw[s][0].x, raw[s][0].y, raw[s][0].z, raw[s][0].w,
+                               raw[s][1].x, raw[s][1].y, raw[s][1].z, raw[s][1].w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          v[s][2 * k] = act[s] ? bf16_lo(w[k]) - m : 0.f;
+          v[s][2 * k + 1] = act[s] ? bf16_hi(w[k]) - m : 0.f;
+        }
+      }
+    }
+
+    if (ROUNDS >= 1) {
+      // round 1 writer: bf16 +row and -row at natural coordinates
+#pragma unroll
+      for (int s = 0; s < SLOTS; ++s) {
+        if (!act[s]) continue;
+        const int p0 = 1024 * s + 16 * lane;
+        uint4 *dp = reinterpret_cast<uint4 *>(buf + 2 * p0);
+        uint4 *dn = reinterpret_cast<uint4 *>(buf + 2 * (p0 + d));
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const uint4 w = raw[s][k];
+          dp[k] = w;
+          dn[k] = make_uint4(w.x ^ 0x80008000u, w.y ^ 0x80008000u, w.z ^ 0x80008000u, w.w ^ 0x80008000u);
+        }
+      }
+      // gather (the wave's own LDS writes are ordered before its reads);
+      // centering: s x - s m = s RN32(x - m), one rounding
+#pragma unroll
+      for (int s = 0; s < SLOTS; ++s) {
+        const int4 *tb = reinterpret_cast<const int4 *>(table) + (s * 4) * 64 + lane;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int4 o4 = tb[k * 64];
+          const int oo[4] = {o4.x, o4.y, o4.z, o4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float g = __uint_as_float((uint32_t)(*reinterpret_cast<const uint16_t *>(buf + oo[e])) << 16);
+            const float mm = oo[e] >= neg_from ? -m : m;
+            v[s][4 * k + e] = act[s] ? (center ? g - mm : g) : 0.f;
+          }
+        }
+      }
+      fwht_row<SLOTS>(v, lane, nl);
+      if (!pow4) {
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) v[s][j] = v[s][j] * c_h;
+      }
+    }
+
+    if (ROUNDS == 2) {
+      // round 2 writer: float32 +row and -row
+#pragma unroll
+      for (int s = 0; s < SLOTS; ++s) {
+        if (!act[s]) continue;
+        const int p0 = 1024 * s + 16 * lane;
+        float4 *dp = reinterpret_cast<float4 *>(buf + 4 * p0);
+        float4 *dn = reinterpret_cast<float4 *>(buf + 4 * (p0 + d));
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          dp[k] = make_float4(v[s][4 * k], v[s][4 * k + 1], v[s][4 * k + 2], v[s][4 * k + 3]);
+          dn[k] = make_float4(-v[s][4 * k], -v[s][4 * k + 1], -v[s][4 * k + 2], -v[s][4 * k + 3]);
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < SLOTS; ++s) {
+        const int4 *tb = reinterpret_cast<const int4 *>(table) + ((SLOTS + s) * 4) * 64 + lane;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int4 o4 = tb[k * 64];
+          const int oo[4] = {o4.x, o4.y, o4.z, o4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[s][4 * k + e] = act[s] ? *reinterpret_cast<const float *>(buf + oo[e]) : 0.f;
+        }
+      }
+      fwht_row<SLOTS>(v, lane, nl);
+      if (!pow4) {
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) v[s][j] = v[s][j] * c_h;
+      }
+    }
+
+    if (mode == OUT_F32) {
+#pragma unroll
+      for (int s = 0; s < SLOTS; ++s) {
+        if (!act[s] || !out) continue;
+        float4 *dst = reinterpret_cast<float4 *>(static_cast<char *>(out) + row * ld_out_bytes) + (1024 * s + 16 * lane) / 4;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          dst[k] = make_float4(v[s][4 * k] * c_all, v[s][4 * k + 1] * c_all, v[s][4 * k + 2] * c_all,
+                               v[s][4 * k + 3] * c_all);
+      }
+      continue;
+    }
+
+    float a = 0.f;
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) a = fmaxf(a, fabsf(v[s][j]));  // inactive slots hold 0
+#pragma unroll
+    for (int lg = 0; lg < 6; ++lg) a = fmaxf(a, xlane(a, lg));
+    a = fmaxf(a * c_all, 1e-10f);  // c_all is a power of two: exact
+    const float fq = (float)qmax;
+    const float alpha = __fdiv_rn(a, fq);
+    const float inv = __fdiv_rn(fq, a) * c_all;  // exact rescale of the deferred factor
+    if (lane == 0) scale_out[row] = alpha;
+
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) {
+      if (!act[s] || mode == OUT_FP6 || mode == OUT_FP6X2) continue;
+      int q[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) q[j] = (int)fminf(fmaxf(__builtin_rintf(v[s][j] * inv), -fq), fq);
+      const int base = 1024 * s + 16 * lane;
+      if (mode == OUT_I8) {
+        uint32_t wd[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          wd[k] = (uint32_t)(q[4 * k] & 0xFF) | ((uint32_t)(q[4 * k + 1] & 0xFF) << 8) |
+                  ((uint32_t)(q[4 * k + 2] & 0xFF) << 16) | ((uint32_t)(q[4 * k + 3] & 0xFF) << 24);
+        *reinterpret_cast<uint4 *>(static_cast<char *>(out) + row * ld_out_bytes + base) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+      } else if (mode == OUT_I4) {
+        uint32_t wd[2] = {0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 16; ++j) wd[j >> 3] |= (uint32_t)(q[j] & 0xF) << (4 * (j & 7));
+        *reinterpret_cast<uint2 *>(static_cast<char *>(out) + row * ld_out_bytes + base / 2) = make_uint2(wd[0], wd[1]);
+      }
+    }
+    if (mode == OUT_FP6 || mode == OUT_FP6X2) {
+      // tiled layout (see k_gemm_fp6.hip): this lane's 16 codes of slot s are
+      // the 96-bit string at bit 6*(base % 32) of its half of the k-group.
+      // Codes are formed as floats (integer-valued, |t| <= qmax, +0 for zero)
+      // and converted two slots at a time with v_cvt_scalef32_2xpk16_fp6_f32,
+      // which interleaves its two sources field by field.
+      uint8_t *tb = static_cast<uint8_t *>(out) + ((row >> 5) * (d >> 6)) * 1536 + (row & 31) * 8;
+      const int64_t pstride = tiled_bytes(M, d);
+#pragma unroll
+      for (int s0 = 0; s0 < SLOTS; s0 += 2) {
+        const bool two = s0 + 1 < SLOTS;
+        float ta[16], tbv[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          ta[j] = __builtin_amdgcn_fmed3f(__builtin_rintf(v[s0][j] * inv), -fq, fq) + 0.0f;
+          tbv[j] = two ? __builtin_amdgcn_fmed3f(__builtin_rintf(v[two ? s0 + 1 : s0][j] * inv), -fq, fq) + 0.0f : 0.0f;
+        }
+        const bool wa = act[s0], wb = two && act[two ? s0 + 1 : s0];
+        if (mode == OUT_FP6) {
+          store_fp6_pair(ta, tbv, 0, tb, 1024 * s0 + 16 * lane, wa, wb);
+        } else {
+          store_fp6_pair(ta, tbv, 1, tb, 1024 * s0 + 16 * lane, wa, wb);
+          store_fp6_pair(ta, tbv, 2, tb + pstride, 1024 * s0 + 16 * lane, wa, wb);
+        }
+      }
+    }
+  }
+}
+
+template <int SLOTS, int ROUNDS>
+hipError_t launch_w(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotArgs &rot, int center, float *mean,
+                    int mode, int qmax, void *out, int64_t ld_out_bytes, float *scale, hipStream_t stream) {
+  using L = WaveLds<SLOTS, ROUNDS>;
+  const size_t lds = (size_t)L::TOTAL;
+  static bool attr_set = false;
+  if (!attr_set && lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute((const void *)rpbh_wave_kernel<SLOTS, ROUNDS>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  // two or more rows per wave so the offset table is amortised
+  int64_t grid = (M + 2 * WAVES_PER_WG - 1) / (2 * WAVES_PER_WG);
+  if (grid > 1024) grid = 1024;
+  if (grid < 1) grid = 1;
+  const int h = ROUNDS ? rot.block : 16;
+  const int pow4 = ROUNDS && ((__builtin_ctz((unsigned)h) & 1) == 0);
+  hipLaunchKernelGGL((rpbh_wave_kernel<SLOTS, ROUNDS>), dim3((unsigned)grid), dim3(64 * WAVES_PER_WG), lds, stream, x,
+                     M, d, ldx, rot.perm, rot.signs, h, rot.c_h, pow4, center, mean, mode, qmax, out, ld_out_bytes,
+                     scale);
+  return hipGetLastError();
+}
+
+template <int SLOTS>
+hipError_t launch_r(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotArgs &rot, int center, float *mean,
+                    int mode, int qmax, void *out, int64_t ld_out_bytes, float *scale, hipStream_t stream) {
+  switch (rot.rounds) {
+    case 0: return launch_w<SLOTS, 0>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, stream);
+    case 1: return launch_w<SLOTS, 1>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, stream);
+    case 2: return launch_w<SLOTS, 2>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool rpbh_wave_supported(int d) { return d >= 16 && d <= 4096 && d % 16 == 0; }
+
+hipError_t launch_rpbh_wave(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotArgs &rot, int center,
+                            float *mean, int mode, int qmax, void *out, int64_t ld_out_bytes, float *scale,
+                            hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  switch ((d + 1023) / 1024) {
+    case 1: return launch_r<1>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, stream);
+    case 2: return launch_r<2>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, stream);
+    case 3: return launch_r<3>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, stream);
+    case 4: return launch_r<4>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace oq

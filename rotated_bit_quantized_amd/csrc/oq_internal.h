@@ -60,6 +60,12 @@ hipError_t launch_rpbh_quant(const uint16_t *x, int64_t M, int d, int64_t ldx,
                              int out_mode, int qmax, void *out, int64_t ld_out_bytes,
                              float *scale, hipStream_t stream);
 
+// K1, one wavefront per row (activation rows of width d <= 4096).
+bool rpbh_wave_supported(int d);
+hipError_t launch_rpbh_wave(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotArgs &rot, int center,
+                            float *mean, int mode, int qmax, void *out, int64_t ld_out_bytes, float *scale,
+                            hipStream_t stream);
+
 // K2: dense per-32 transform -> (MXFP4 quantize | float32 out).
 hipError_t launch_dense32(const uint16_t *x, int64_t M, int d, int64_t ldx,
                           const uint16_t *mats, int mx_out, void *out, int64_t ld_out_bytes,
