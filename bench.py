@@ -123,6 +123,8 @@ def _launches(oq, st, i):
 
 
 def _time(torch, oq, st, steps, warmup):
+    """Device time per step and per launch (HIP events on the launch stream,
+    which is torch's current stream: the binding launches there)."""
     for i in range(warmup):
         for _, f in _launches(oq, st, i):
             f()
@@ -139,13 +141,74 @@ def _time(torch, oq, st, steps, warmup):
             ev[i][k + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = {n: 0.0 for n in names}
-    for i in range(steps):
-        for k, n in enumerate(names):
-            per[n] += ev[i][k].elapsed_time(ev[i][k + 1])
-    per = {n: v / steps for n, v in per.items()}          # ms per launch
-    total = ev[0][0].elapsed_time(ev[-1][-1]) / steps     # ms per step on the device
-    return total, wall / steps * 1e3, per
+    samples = {n: [ev[i][k].elapsed_time(ev[i][k + 1]) for i in range(steps)] for k, n in enumerate(names)}
+    per = {n: sum(v) / steps for n, v in samples.items()}  # ms per launch (mean)
+    total = ev[0][0].elapsed_time(ev[-1][-1]) / steps       # ms per step on the device
+    return total, wall / steps * 1e3, per, samples
+
+
+def _pct(v, q):
+    v = sorted(v)
+    return v[min(len(v) - 1, max(0, int(round(q * (len(v) - 1)))))]
+
+
+def _dist_us(v):
+    return {"median": round(_pct(v, 0.5) * 1e3, 3), "p10": round(_pct(v, 0.1) * 1e3, 3),
+            "p90": round(_pct(v, 0.9) * 1e3, 3)}
+
+
+def _time_fused(torch, oq, st, reps, warmup):
+    """oq_linear_fused (rotate/quant + GEMM in one call) for the widest linear."""
+    s = st["spec"]
+    j = max(range(len(st["ys"])), key=lambda i: st["ys"][i].shape[1])
+    wq, y = st["ws"][j], st["ys"][j]
+    N = y.shape[1]
+    afmt = s.afmt | (oq.OQ_TILED if st["tiled"] else 0)
+    ws = torch.empty(oq.oq_workspace_bytes(oq.OQ_OP_LINEAR, st["wl"].M, st["wl"].K, N, afmt),
+                     dtype=torch.uint8, device=y.device)
+
+    def call(i):
+        oq.oq_linear_fused(st["xs"][i % len(st["xs"])], st["rot"], s.center, afmt, wq["codes"], wq["scales"], N,
+                           s.group, w1=wq["w1"], y=y, ws=ws)
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
+        call(i)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    v = [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+    return N, sum(v) / reps, v
+
+
+def _copy_reference(torch, nbytes=1 << 30, reps=3):
+    """A plain device-to-device copy of known size, launched beside the
+    profiled kernels so that HBM byte counters can be scaled by what they
+    read for a transfer whose size is known."""
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    return nbytes
+
+
+def _gpu_state():
+    """Clock and power state as rocm-smi reports it (read only)."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"], capture_output=True, text=True,
+                           timeout=20)
+        d = json.loads(r.stdout)
+        card = d[sorted(d)[0]]
+        keep = {k: v for k, v in card.items() if any(t in k.lower() for t in ("sclk", "mclk", "power"))}
+        return keep or None
+    except Exception:
+        return None
 
 
 def _act_bytes(spec, M, K):
@@ -195,10 +258,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-config side table")
     ap.add_argument("--only-step", action="store_true", help="time the step only (for profilers)")
+    ap.add_argument("--copy-ref", action="store_true",
+                    help="also run a 1 GiB device copy (counter calibration under a profiler)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (the layer shards by tokens, "
-                                   "see the design notes)", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this benchmark runs on one GPU; --gpus must be 1 (the layer would shard by "
+                                   "tokens with replicated weights; no multi-GPU path is built)", "n_gpus": args.gpus}))
         sys.exit(2)
 
     import torch
@@ -209,7 +274,9 @@ def main():
     st = _setup(torch, oq, WL, 2)
     wl, s = st["wl"], st["spec"]
     M, K = wl.M, wl.K
-    ms_step, wall_ms, per = _time(torch, oq, st, args.steps, args.warmup)
+    ms_step, wall_ms, per, samples = _time(torch, oq, st, args.steps, args.warmup)
+    if args.copy_ref:
+        _copy_reference(torch)
     ops = 2.0 * M * K * sum(wl.Ns)
     value = ops / (ms_step * 1e-3) / 1e12
 
@@ -239,6 +306,7 @@ def main():
         "rotate_quant_GBs": round(rq_bytes / (rq_us * 1e-6) / 1e9, 1),
         "rotate_quant_hbm_frac": round(rq_bytes / (rq_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
         "gemm_us": {n: round(v * 1e3, 3) for n, v in per.items() if n.startswith("gemm")},
+        "per_launch_us": {n: _dist_us(v) for n, v in samples.items()},
         "host_wall_ms_per_step": round(wall_ms, 5),
         "roofline": {"kernel": f"int4 GEMM 4096x3072 -> {max(wl.Ns)}", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
@@ -246,13 +314,18 @@ def main():
                      "traffic": _traffic("gemm_fp6_c2_traffic.json", ["k_gemm_fp6.hip"])},
     }
 
+    if not args.only_step:
+        nf, fm, fv = _time_fused(torch, oq, st, max(20, args.steps // 2), 5)
+        result["linear_fused_us"] = {"d_out": nf, "mean": round(fm * 1e3, 3), **_dist_us(fv)}
+        result["gpu_state"] = _gpu_state()
+
     if not args.no_configs and not args.only_step:
         side = {}
         for cid in (1, 3, 4, 5):
             del st
             torch.cuda.empty_cache()
             st = _setup(torch, oq, WL, cid)
-            ms, _, per_c = _time(torch, oq, st, max(20, args.steps // 5), 5)
+            ms, _, per_c, _ = _time(torch, oq, st, max(20, args.steps // 5), 5)
             w2, s2 = st["wl"], st["spec"]
             b = _act_bytes(s2, w2.M, w2.K)
             peak = PEAK_FP4_TFLOPS if s2.afmt == 0x104 else PEAK_INT8_TOPS
@@ -264,6 +337,8 @@ def main():
                     tops = 2.0 * w2.M * w2.K * Nn / (v * 1e-3) / 1e12
                     e[n] = {"us": round(v * 1e3, 2), "TOPS": round(tops, 1), "frac": round(tops / peak, 4)}
             e["step_ms"] = round(ms, 4)
+            nf, fm, _ = _time_fused(torch, oq, st, 20, 3)
+            e["linear_fused_us"] = {"d_out": nf, "mean": round(fm * 1e3, 3)}
             side[s2.name] = e
         result["other_configs"] = side
 

@@ -48,7 +48,7 @@ extern "C" {
 enum {
   OQ_OK = 0,
   OQ_ERR_INVALID_ARG = 1,   /* null pointer, bad size, bad enum value       */
-  OQ_ERR_UNSUPPORTED = 2,   /* well-formed request this build does not run  */
+  OQ_ERR_UNSUPPORTED = 2,   /* well-formed request this library does not run */
   OQ_ERR_ALIGNMENT = 3,     /* pointer or leading dimension misaligned      */
   OQ_ERR_WORKSPACE = 4,     /* workspace missing or too small               */
   OQ_ERR_HIP = 5            /* the HIP runtime reported a launch error      */

@@ -16,7 +16,7 @@ Sources:
   Microscaling (MX) v1.0 specification, which defines MXFP4 as E2M1 elements
   sharing one E8M0 power-of-two scale per 32.
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
   * round() is round-half-to-even;
   * x / alpha is evaluated as RN32(x * RN32(qmax / a)), one division per token;
   * an all-zero token uses max(a, eps32) with eps32 = RN32(1e-10), so every

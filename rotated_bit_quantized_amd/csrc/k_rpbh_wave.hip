@@ -150,7 +150,7 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
   const int nl = h >> 4;  // lanes per Hadamard block
 
   // ---- offset table: byte offsets into this wave's [+row | -row] buffer;
-  // round 1 copies are bf16 (2 bytes), round 2 copies float32
+  // first-round copies are bf16 (2 bytes), second-round copies float32
   for (int t = threadIdx.x; t < (ROUNDS > 0 ? ROUNDS : 0) * SLOTS * 1024; t += 64 * WAVES_PER_WG) {
     const int r = t / (SLOTS * 1024);
     const int rem = t % (SLOTS * 1024);
@@ -169,7 +169,7 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
 #pragma unroll
   for (int s = 0; s < SLOTS; ++s) act[s] = 1024 * s + 16 * lane < d;
   const float c_all = (ROUNDS == 0 || !pow4) ? 1.0f : (ROUNDS == 2 ? c_h * c_h : c_h);  // deferred, exact
-  const int neg_from = 2 * d;  // round-1 byte offsets at or above this hit the -x copy
+  const int neg_from = 2 * d;  // first-round byte offsets at or above this hit the -x copy
 
   const int64_t step = (int64_t)gridDim.x * WAVES_PER_WG;
   // the next row's words are loaded while the current row is processed (the
@@ -227,7 +227,7 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
     }
 
     if (ROUNDS >= 1) {
-      // round 1 writer: bf16 +row and -row at natural coordinates
+      // first-round writer: bf16 +row and -row at natural coordinates
 #pragma unroll
       for (int s = 0; s < SLOTS; ++s) {
         if (!act[s]) continue;
@@ -268,7 +268,7 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
     }
 
     if (ROUNDS == 2) {
-      // round 2 writer: float32 +row and -row
+      // second-round writer: float32 +row and -row
 #pragma unroll
       for (int s = 0; s < SLOTS; ++s) {
         if (!act[s]) continue;

@@ -1,6 +1,6 @@
 """Comparison rules shared by the GPU parity tests.
 
-Rules (from the acceptance criteria, with the readings listed in the design doc):
+Rules (the acceptance criteria of the layer, with the readings of the pages stated below):
   * integer codes and scale bytes: bit-exact, except elements the oracle flags
     as lying within 1e-6 relative of a rounding boundary; mismatches among
     flagged elements are counted and must stay below 1e-4 of all elements;

@@ -60,6 +60,18 @@ def test_identity_metadata_reduces_to_block_sylvester():
     assert np.max(np.abs(v[:, 1:])) < 1e-12
 
 
+def test_two_identity_rounds_are_the_identity():
+    # the normalised Sylvester block is symmetric and orthogonal, so with an
+    # identity permutation and all-plus signs two rounds give back the input
+    d, h = 512, 128
+    perm = np.tile(np.arange(d, dtype=np.int32), (2, 1))
+    signs = np.ones((2, d), dtype=np.int8)
+    x = np.random.default_rng(17).standard_normal((3, d))
+    np.testing.assert_allclose(R.rpbh_fp64(x, perm, signs, h), x, rtol=0, atol=1e-13)
+    # and a wrong stage order or a missing scale would not: one round is not the identity
+    assert np.max(np.abs(R.rpbh_fp64(x, perm[:1], signs[:1], h) - x)) > 0.1
+
+
 def test_norm_and_row_sum_split():
     # CentriQ App. C.5, Eq. 10: R x = R x^c + xbar R 1 (R linear)
     d, h = 1024, 128

@@ -17,9 +17,9 @@ settings studied on the pages (OrbitQuant PR #25 "Default changes" and
 
 Seeds: ``numpy.random.Generator(PCG64(SeedSequence([config_id, stream])))``
 with fixed stream numbers (0 activations, 1 and 11 weights of the first and
-second linear, 2 outlier channels, 3/4 permutation/signs of round 1, 5/6 of
-round 2, 7/8 the dense transform's diagonal and orthogonal factor, 9 the
-per-token adaLN mean and gain).
+second linear, 2 outlier channels, 3/4 permutation/signs of the first
+rotation round, 5/6 of the second, 7/8 the dense transform's diagonal and
+orthogonal factor, 9 the per-token adaLN mean and gain).
 
 Bit conventions (inputs are defined by their bits):
   * activations: drawn in float64, rounded to float32 (nearest), then to
