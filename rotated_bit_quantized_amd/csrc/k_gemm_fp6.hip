@@ -41,9 +41,6 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int CHUNK_TILE = 1536;  // bytes of one 32-row x 64-k tile
 
-__device__ __forceinline__ void dma16(const void *g, void *lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void *)lds_wave_base, 16, 0, 0);
-}
 
 __device__ __forceinline__ v8i frag(const uint8_t *tile, int half, int r) {
   const uint8_t *p = tile + (3 * half) * 256 + r * 8;
@@ -96,8 +93,9 @@ gemm_fp6_kernel(const uint8_t *__restrict__ A, int64_t a_plane_bytes, const floa
   using C = Cfg<WM, WN, PLANES, NSTAGE>;
   constexpr int STAGES = C::STAGES;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const uint32_t smem_addr = lds_addr_of(smem);
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = K / 64;
   const int64_t m0 = (int64_t)blockIdx.y * C::BM;
   const int n0 = blockIdx.x * C::BN;
@@ -136,8 +134,7 @@ gemm_fp6_kernel(const uint8_t *__restrict__ A, int64_t a_plane_bytes, const floa
   const int nq = (C::UNITS - wave + C::WAVES - 1) / C::WAVES;  // units this wave copies per group
 
   auto issue_unit = [&](int q, int ks) {
-    uint8_t *stage = smem + (ks % STAGES) * C::STAGE;
-    if (uoff[q] >= 0) dma16(src[q] + (int64_t)ks * inc[q], stage + uoff[q]);
+    if (uoff[q] >= 0) dma_lds16(src[q] + (int64_t)ks * inc[q], smem_addr + (ks % STAGES) * C::STAGE + uoff[q]);
   };
   auto issue = [&](int ks) {
 #pragma unroll

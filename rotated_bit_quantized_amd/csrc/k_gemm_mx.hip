@@ -12,6 +12,8 @@
 // loaded straight from the code rows; the accumulator carries the whole K.
 #include "oq_internal.h"
 
+#include <type_traits>
+
 namespace oq {
 namespace {
 
@@ -85,12 +87,266 @@ gemm_mx_kernel(const uint8_t *__restrict__ qa, int64_t lda, const uint8_t *__res
   }
 }
 
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int C>
+__device__ __forceinline__ void mx_wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (C & 0xF) | ((C >> 4) << 14));
+}
+
+// Tiled variant: WM x WN wavefronts, each owning TM x TN MFMA tiles of 32 x 32
+// (accumulators carry the whole K).  Each stage holds 128 k (two MFMA k-steps):
+//   A: (BM/32) row blocks x 2 k-halves of 1 KiB, laid out so lane l of the
+//      fragment finds its 16 bytes at offset 16 l (row l % 32, k-half l / 32);
+//   B: the same for the weight rows;
+//   SA, SB: one 32-bit word per row = the four E8M0 bytes of the stage's 128 k.
+// All of it is copied global -> LDS with global_load_lds (16-byte units for
+// codes, 4-byte units for scales) into an NSTAGE ring, one barrier per stage.
+template <int WM, int WN, int TM, int TN, int NSTAGE>
+struct MxCfg {
+  static constexpr int WAVES = WM * WN;
+  static constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
+  static constexpr int A_BYTES = (BM / 32) * 2 * 1024, B_BYTES = (BN / 32) * 2 * 1024;
+  static constexpr int SA_BYTES = BM * 4, SB_BYTES = BN * 4;
+  static constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES;
+  static constexpr int U16 = (A_BYTES + B_BYTES) / 1024;  // 16-byte-per-lane units
+  static constexpr int U4 = (SA_BYTES + SB_BYTES) / 256;  // 4-byte-per-lane units
+  static constexpr int P16 = U16 / WAVES, P4 = (U4 + WAVES - 1) / WAVES;
+  static_assert(U16 % WAVES == 0, "code units must divide evenly among the waves");
+  static_assert(NSTAGE >= 2 && NSTAGE <= 4, "ring depth");
+};
+
+template <int WM, int WN, int TM, int TN, int NSTAGE>
+__global__ void __launch_bounds__(64 * WM * WN)
+gemm_mx_tiled_kernel(const uint8_t *__restrict__ qa, int64_t lda, const uint8_t *__restrict__ ea, int64_t M, int K,
+                     const uint8_t *__restrict__ w, const uint8_t *__restrict__ ew, int N,
+                     const float *__restrict__ bias, uint16_t *__restrict__ y, int64_t ldy) {
+  using C = MxCfg<WM, WN, TM, TN, NSTAGE>;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int KB = K / 32;
+  const int S = K / 128;  // stages
+  const int64_t m0 = (int64_t)blockIdx.y * C::BM;
+  const int n0 = blockIdx.x * C::BN;
+
+  // ---- per-lane DMA sources (stage 0) and LDS offsets of this wave's units
+  const uint8_t *src16[C::P16];
+  int off16[C::P16];
+#pragma unroll
+  for (int q = 0; q < C::P16; ++q) {
+    const int u = wave + q * C::WAVES;
+    const int r = lane & 31, hf = lane >> 5;
+    if (u < C::A_BYTES / 1024) {
+      const int blk = u >> 1, kk = u & 1;
+      int64_t row = m0 + 32 * blk + r;
+      if (row > M - 1) row = M - 1;
+      src16[q] = qa + row * lda + 32 * kk + 16 * hf;
+    } else {
+      const int v = u - C::A_BYTES / 1024;
+      const int blk = v >> 1, kk = v & 1;
+      int row = n0 + 32 * blk + r;
+      if (row > N - 1) row = N - 1;
+      src16[q] = w + (int64_t)row * (K / 2) + 32 * kk + 16 * hf;
+    }
+    off16[q] = u * 1024;
+  }
+  const uint8_t *src4[C::P4];
+  int off4[C::P4];
+#pragma unroll
+  for (int q = 0; q < C::P4; ++q) {
+    const int u = wave + q * C::WAVES;
+    off4[q] = -1;
+    src4[q] = ea;
+    if (u < C::SA_BYTES / 256) {
+      int64_t row = m0 + 64 * u + lane;
+      if (row > M - 1) row = M - 1;
+      src4[q] = ea + row * KB;
+      off4[q] = C::A_BYTES + C::B_BYTES + u * 256;
+    } else if (u < C::U4) {
+      const int v = u - C::SA_BYTES / 256;
+      int row = n0 + 64 * v + lane;
+      if (row > N - 1) row = N - 1;
+      src4[q] = ew + (int64_t)row * KB;
+      off4[q] = C::A_BYTES + C::B_BYTES + C::SA_BYTES + v * 256;
+    }
+  }
+  // number of DMA instructions this wave issues per stage
+  const int n4 = (C::U4 - wave + C::WAVES - 1) / C::WAVES;
+  const int per_stage = C::P16 + n4;
+
+  // One static LDS array per ring slot and the k loop unrolled by the ring
+  // depth, so that every slot reference is a compile-time choice of array:
+  // the compiler can then tell that copies in flight into the other slots do
+  // not alias this slot's reads, and waits only for the copies of this slot.
+  __shared__ __attribute__((aligned(16))) uint8_t ring0[C::STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t ring1[C::STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t ring2[NSTAGE > 2 ? C::STAGE : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t ring3[NSTAGE > 3 ? C::STAGE : 16];
+  auto slot = [&](auto jc) -> uint8_t * {
+    constexpr int j = decltype(jc)::value;
+    if constexpr (j == 0) return ring0;
+    else if constexpr (j == 1) return ring1;
+    else if constexpr (j == 2) return ring2;
+    else return ring3;
+  };
+  auto issue = [&](auto jc, int ks) {
+    const uint32_t base = lds_addr_of(slot(jc));
+#pragma unroll
+    for (int q = 0; q < C::P16; ++q) dma_lds16(src16[q] + (int64_t)ks * 64, base + off16[q]);
+#pragma unroll
+    for (int q = 0; q < C::P4; ++q)
+      if (off4[q] >= 0) dma_lds4(src4[q] + (int64_t)ks * 4, base + off4[q]);
+  };
+
+  const int wm = wave / WN, wn = wave % WN;
+  const int r = lane & 31, hf = lane >> 5;
+  v16f acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = (v16f){};
+
+  if (0 < S) issue(std::integral_constant<int, 0>{}, 0);
+  if (1 < S) issue(std::integral_constant<int, 1>{}, 1);
+  if constexpr (NSTAGE > 3)
+    if (2 < S) issue(std::integral_constant<int, 2>{}, 2);
+
+  // one stage: slot J holds k-slice ks
+  auto body = [&](auto jc, int ks) {
+    constexpr int J = decltype(jc)::value;
+    // this wave's copies of slot J are done once at most the copies of the
+    // stages issued after it are outstanding; the barrier then publishes
+    // every wave's copies of slot J
+    const int ahead = min(NSTAGE - 2, S - 1 - ks);
+    if (ahead == NSTAGE - 2 && per_stage == C::P16 + C::P4)
+      mx_wait_vmcnt<(NSTAGE - 2) * (C::P16 + C::P4)>();
+    else if (ahead == NSTAGE - 2)
+      mx_wait_vmcnt<(NSTAGE - 2) * (C::P16 + C::P4 - 1)>();
+    else
+      mx_wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    // refill the slot consumed at ks - 1 (every wave is past it)
+    if (ks + NSTAGE - 1 < S) issue(std::integral_constant<int, (J + NSTAGE - 1) % NSTAGE>{}, ks + NSTAGE - 1);
+
+    const uint8_t *stage = slot(jc);
+    const uint32_t *sA = reinterpret_cast<const uint32_t *>(stage + C::A_BYTES + C::B_BYTES);
+    const uint32_t *sB = sA + C::BM;
+    uint32_t wa[TM], wb[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) wa[i] = sA[wm * 32 * TM + 32 * i + r];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) wb[j] = sB[wn * 32 * TN + 32 * j + r];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      v8i A[TM], B[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const uint4 p = *reinterpret_cast<const uint4 *>(stage + ((wm * TM + i) * 2 + kk) * 1024 + 16 * lane);
+        A[i] = (v8i){(int)p.x, (int)p.y, (int)p.z, (int)p.w, 0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const uint4 p = *reinterpret_cast<const uint4 *>(stage + C::A_BYTES + ((wn * TN + j) * 2 + kk) * 1024 + 16 * lane);
+        B[j] = (v8i){(int)p.x, (int)p.y, (int)p.z, (int)p.w, 0, 0, 0, 0};
+      }
+      const int sh = 8 * (2 * kk + hf);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[i], B[j], acc[i][j], 4, 4, 0,
+                                                                      (int)((wa[i] >> sh) & 0xFF), 0,
+                                                                      (int)((wb[j] >> sh) & 0xFF));
+    }
+  };
+
+  for (int ks = 0; ks < S; ks += NSTAGE) {
+    body(std::integral_constant<int, 0>{}, ks);
+    if (ks + 1 < S) body(std::integral_constant<int, 1>{}, ks + 1);
+    if constexpr (NSTAGE > 2)
+      if (ks + 2 < S) body(std::integral_constant<int, 2>{}, ks + 2);
+    if constexpr (NSTAGE > 3)
+      if (ks + 3 < S) body(std::integral_constant<int, 3>{}, ks + 3);
+  }
+
+  // ---- epilogue: + bias, bf16, staged per 32-row slab in LDS for 16-byte stores
+  float bv[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int col = n0 + wn * 32 * TN + 32 * j + r;
+    bv[j] = (bias && col < N) ? bias[col] : 0.f;
+  }
+  __syncthreads();  // every wave is done with the ring
+  constexpr int SROW = 64 * TN + 16;  // bytes per staged row (32 TN bf16 + pad)
+  constexpr int PER_SLOT = C::STAGE / (32 * SROW);  // staging areas per ring slot
+  static_assert(PER_SLOT * NSTAGE >= C::WAVES, "epilogue staging must fit in the ring");
+  const int sw = wave / PER_SLOT, so = (wave % PER_SLOT) * (32 * SROW);
+  uint8_t *stg = (sw == 0 ? ring0 : sw == 1 ? ring1 : sw == 2 ? ring2 : ring3) + so;
+  const bool vec_ok = ((reinterpret_cast<uintptr_t>(y) & 15) == 0) && (ldy % 8 == 0);
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int rr = (e >> 2) * 8 + hf * 4 + (e & 3);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        float v = acc[i][j][e];
+        if (bias) v = v + bv[j];
+        *reinterpret_cast<uint16_t *>(stg + rr * SROW + (32 * j + r) * 2) = f32_to_bf16_rne(v);
+      }
+    }
+    // 16 bytes per lane: 4 TN lanes cover one staged row
+    constexpr int LPR = 4 * TN, RPP = 64 / LPR;
+    const int cl = (lane % LPR) * 8;
+    const int col = n0 + wn * 32 * TN + cl;
+#pragma unroll
+    for (int q = 0; q < 32 / RPP; ++q) {
+      const int rr = lane / LPR + RPP * q;
+      const int64_t row = m0 + wm * 32 * TM + 32 * i + rr;
+      const uint4 v = *reinterpret_cast<const uint4 *>(stg + rr * SROW + cl * 2);
+      if (row >= M) continue;
+      uint16_t *dst = y + row * ldy + col;
+      if (vec_ok && col + 8 <= N) {
+        *reinterpret_cast<uint4 *>(dst) = v;
+      } else {
+        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          if (col + c < N) dst[c] = (uint16_t)(wv[c >> 1] >> (16 * (c & 1)));
+      }
+    }
+  }
+}
+
+template <int WM, int WN, int TM, int TN, int NSTAGE>
+hipError_t launch_mx_tiled(const uint8_t *qa, int64_t lda, const uint8_t *ea, int64_t M, int K, const uint8_t *w,
+                           const uint8_t *ew, int N, const float *bias, uint16_t *y, int64_t ldy,
+                           hipStream_t stream) {
+  using C = MxCfg<WM, WN, TM, TN, NSTAGE>;
+  dim3 grid((unsigned)((N + C::BN - 1) / C::BN), (unsigned)((M + C::BM - 1) / C::BM));
+  hipLaunchKernelGGL((gemm_mx_tiled_kernel<WM, WN, TM, TN, NSTAGE>), grid, dim3(64 * C::WAVES), 0, stream, qa, lda,
+                     ea, M, K, w, ew, N, bias, y, ldy);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm_mx(const uint8_t *qa, int64_t lda_bytes, const uint8_t *a_e8m0, int64_t M, int K,
                           const uint8_t *w, const uint8_t *w_e8m0, int N, const float *bias, uint16_t *y,
                           int64_t ldy, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
+  // the staged kernel copies the four E8M0 bytes of a 128-wide k-slice as one
+  // 32-bit word and the codes in 16-byte pieces
+  const bool tiled = K % 128 == 0 && lda_bytes % 16 == 0 && ((reinterpret_cast<uintptr_t>(qa) | reinterpret_cast<uintptr_t>(w)) & 15) == 0 &&
+                     ((reinterpret_cast<uintptr_t>(a_e8m0) | reinterpret_cast<uintptr_t>(w_e8m0)) & 3) == 0;
+  if (tiled) {
+#ifndef MX_CFG
+    return launch_mx_tiled<2, 4, 4, 2, 3>(qa, lda_bytes, a_e8m0, M, K, w, w_e8m0, N, bias, y, ldy, stream);
+#else
+    return launch_mx_tiled<MX_CFG>(qa, lda_bytes, a_e8m0, M, K, w, w_e8m0, N, bias, y, ldy, stream);
+#endif
+  }
   dim3 grid((unsigned)((N + 127) / 128), (unsigned)((M + 127) / 128));
   hipLaunchKernelGGL(gemm_mx_kernel, grid, dim3(256), 0, stream, qa, lda_bytes, a_e8m0, M, K, w, w_e8m0, N,
                      bias, y, ldy);

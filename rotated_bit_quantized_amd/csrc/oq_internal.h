@@ -24,6 +24,30 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 // FP6 E2M3 bit pattern of an integer code q in [-7, 7] (exact: sign bit 5,
 // exponent bits 4..3 with bias 1, mantissa bits 2..0).  The magnitude goes
 // through an 8-entry byte table held in two dwords (v_perm_b32).
+// Global -> LDS copies: each lane moves 16 (or 4) bytes from its own global
+// address to lds_addr + lane * 16 (or * 4); lds_addr is wave-uniform and goes
+// to M0.  Written as inline asm on purpose: the compiler would otherwise
+// treat the copy as an LDS store of unknown extent and wait for every copy in
+// flight before each later LDS read, which turns a multi-stage ring into a
+// serial one.  Callers order copies and reads with explicit vmcnt waits and
+// workgroup barriers.  The asm has no register outputs.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma_lds16(const void *g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma_lds4(const void *g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_addr)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// byte address of an LDS object, for dma_lds*
+__device__ __forceinline__ uint32_t lds_addr_of(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)p;
+}
+
 __device__ __forceinline__ uint32_t fp6_e2m3_of_int(int q) {
   const uint32_t a = (uint32_t)(q < 0 ? -q : q);
   // |q| = 0..7 -> 0x00 0x08 0x10 0x14 0x18 0x1A 0x1C 0x1E

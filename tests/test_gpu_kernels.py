@@ -235,17 +235,21 @@ def test_gemm_int(oq, M, N, K, group, afmt, rank1, bias):
     say("  within 1 bf16 ulp:", frac)
 
 
-@pytest.mark.parametrize("M,N,K", [(130, 96, 256), (64, 256, 4096), (7, 32, 64)])
-def test_gemm_mx(oq, M, N, K):
-    say("case gemm_mx", M, N, K)
+@pytest.mark.parametrize("M,N,K,bias", [(130, 96, 256, True), (64, 256, 4096, True), (7, 32, 64, True),
+                                         (300, 600, 1152, True), (1, 40, 128, False), (513, 257, 384, False),
+                                         (260, 300, 192, True)])
+def test_gemm_mx(oq, M, N, K, bias):
+    # K % 128 == 0 runs the LDS-staged kernel (several stages, ragged M and N
+    # tiles, a single stage at K = 128), other K the direct-load kernel
+    say("case gemm_mx", M, N, K, bias)
     rng = np.random.default_rng(M + N + K)
     ca = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
     cw = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
     ea = rng.integers(118, 136, size=(M, K // 32)).astype(np.uint8)
     ew = rng.integers(118, 136, size=(N, K // 32)).astype(np.uint8)
-    b = rng.normal(0, 1, size=N).astype(np.float32)
+    b = rng.normal(0, 1, size=N).astype(np.float32) if bias else None
     y = oq.oq_gemm_w4a4(oq.OQ_MXFP4, to_dev(OQ.pack_nibbles(ca)), to_dev(ea), to_dev(OQ.pack_nibbles(cw)),
-                        to_dev(ew), N, 32, bias=to_dev(b))
+                        to_dev(ew), N, 32, bias=None if b is None else to_dev(b))
     torch.cuda.synchronize()
     y_ref, S = OG.gemm_mx(OQ.mx_dequant(ca, ea), OQ.mx_dequant(cw, ew), b)
     check_output(to_host(y), y_ref, S, K // 32, "gemm_mx")
