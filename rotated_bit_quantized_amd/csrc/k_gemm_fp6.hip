@@ -28,6 +28,8 @@
 // (no register staging) into a 4-stage ring, one barrier per group.
 #include "oq_internal.h"
 
+#include <type_traits>
+
 #ifndef FP6_STAGES
 #define FP6_STAGES 3
 #endif
@@ -346,6 +348,253 @@ hipError_t launch_cfg(const uint8_t *A, int64_t a_plane_bytes, const float *a_sc
   return hipGetLastError();
 }
 
+
+// ---------------------------------------------------------------------------
+// Single-plane kernel with the fragments of the next k-group prefetched into
+// registers while the current group computes.  Workgroup 256 x 256 (8 waves
+// of 128 x 64), a 3-slot ring of one k-group per slot, one barrier per group:
+//   group g start: own copies of stage g+1 done (vmcnt) and own LDS reads of
+//   slot g done (lgkmcnt) -> barrier -> refill slot g with stage g+3;
+//   during group g: A fragments of g+1 are loaded into a[i] right after the
+//   last MFMA that reads a[i]; B fragments and scales of g+1 go to a second
+//   set of registers.  So every group starts with its operands in registers.
+// Copies use an SGPR base per unit plus a loop-invariant per-lane offset;
+// every wave issues exactly 3 code units (1 KiB) and 1 scale unit (256 B,
+// waves w and w+4 copy the same bytes) per stage, so the vmcnt values are
+// compile-time constants.  The loop is unrolled by the ring depth, so LDS
+// addresses are immediates.
+// ---------------------------------------------------------------------------
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16_s(const void *sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_addr)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4_s(const void *sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_addr)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int C>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (C & 0xF) | ((C >> 4) << 14));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+struct V2 {
+  static constexpr int WAVES = 8, BM = 256, BN = 256, NSLOT = 3;
+  static constexpr int A_BYTES = (BM / 32) * CHUNK_TILE, B_BYTES = (BN / 32) * CHUNK_TILE;
+  static constexpr int S_BYTES = BN * 4;
+  static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
+  static constexpr int ROWS_OFF = NSLOT * STAGE;
+  static constexpr int LDS_BYTES = ROWS_OFF + 2 * BM * 4;
+  static constexpr int PER_STAGE = 4;  // copy instructions per wave per stage
+};
+
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_scale, int64_t M, int K,
+                   const uint8_t *__restrict__ W, const float *__restrict__ wst, int N, int Np,
+                   const float *__restrict__ mean, const float *__restrict__ w1, const float *__restrict__ bias,
+                   uint16_t *__restrict__ y, int64_t ldy) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const uint32_t lds0 = lds_addr_of(smem);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int G = K / 64;
+  const int64_t m0 = (int64_t)blockIdx.y * V2::BM;
+  const int n0 = blockIdx.x * V2::BN;
+  const int64_t mblocks = (M + 31) / 32;
+  const int nblocks = Np / 32;
+
+  // ---- copy units of this wave (stage 0 addresses; k-group kg adds kg * 1536)
+  const uint8_t *cbase[3];
+  uint32_t coff[3], clds[3];
+#pragma unroll
+  for (int q = 0; q < 3; ++q) {
+    const int u = wave + 8 * q;  // 0..23: 12 A units then 12 B units
+    const int o = 1024 * u + 16 * lane;
+    if (u < 12) {
+      int64_t rb = m0 / 32 + o / CHUNK_TILE;
+      if (rb > mblocks - 1) rb = mblocks - 1;
+      cbase[q] = A;
+      coff[q] = (uint32_t)(rb * G * CHUNK_TILE + o % CHUNK_TILE);
+    } else {
+      const int oo = o - V2::A_BYTES;
+      int cb = n0 / 32 + oo / CHUNK_TILE;
+      if (cb > nblocks - 1) cb = nblocks - 1;
+      cbase[q] = W;
+      coff[q] = (uint32_t)((int64_t)cb * G * CHUNK_TILE + oo % CHUNK_TILE);
+    }
+    clds[q] = 1024u * u;
+  }
+  const int sc = wave & 3;  // scale chunk: columns n0 + 64 sc + lane
+  int scol = n0 + 64 * sc + lane;
+  if (scol > Np - 1) scol = Np - 1;
+  const uint32_t soff = 4u * scol, slds = V2::A_BYTES + V2::B_BYTES + 256u * sc;
+
+  auto issue = [&](int slot, int kg) {
+    const uint32_t base = lds0 + slot * V2::STAGE;
+#pragma unroll
+    for (int q = 0; q < 3; ++q) dma16_s(cbase[q] + (int64_t)kg * CHUNK_TILE, coff[q], base + clds[q]);
+    dma4_s(wst + (int64_t)kg * Np, soff, base + slds);
+  };
+
+  const int wm = wave >> 2, wn = wave & 3;
+  const int r = lane & 31, half = lane >> 5;
+  const uint8_t *fa = smem + (wm * 4) * CHUNK_TILE + (3 * half) * 256 + r * 8;
+  const uint8_t *fb = smem + V2::A_BYTES + (wn * 2) * CHUNK_TILE + (3 * half) * 256 + r * 8;
+  const float *fs = reinterpret_cast<const float *>(smem + V2::A_BYTES + V2::B_BYTES) + wn * 64 + r;
+
+  float F[4][2][16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) F[i][j][e] = 0.f;
+
+  float *lds_alpha = reinterpret_cast<float *>(smem + V2::ROWS_OFF);
+  float *lds_mean = lds_alpha + V2::BM;
+  for (int t = threadIdx.x; t < V2::BM; t += 512) {
+    const int64_t row = m0 + t;
+    lds_alpha[t] = row < M ? a_scale[row] : 0.f;
+    lds_mean[t] = (mean && row < M) ? mean[row] : 0.f;
+  }
+
+  // ---- prologue: stages 0..2 in flight, group 0's operands loaded
+  issue(0, 0);
+  if (G > 1) issue(1, 1);
+  if (G > 2) issue(2, 2);
+  if (G > 2) wait_vm<2 * V2::PER_STAGE>();
+  else if (G > 1) wait_vm<V2::PER_STAGE>();
+  else wait_vm<0>();
+  __builtin_amdgcn_s_barrier();
+  v8i a[4], b0, b1;
+  float s0, s1, ns0 = 0.f, ns1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a[i] = frag(fa + i * CHUNK_TILE, 0, 0);
+  b0 = frag(fb, 0, 0);
+  b1 = frag(fb + CHUNK_TILE, 0, 0);
+  s0 = fs[0];
+  s1 = fs[32];
+
+  auto body = [&](auto jc, int g) {
+    constexpr int J = decltype(jc)::value;
+    constexpr int JN = (J + 1) % V2::NSLOT;
+    if (g + 2 < G) wait_vm<V2::PER_STAGE>();
+    else wait_vm<0>();
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+    if (g + 3 < G) issue(J, g + 3);
+    __builtin_amdgcn_sched_barrier(0);
+
+    v16f dprev;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int i = t >> 1;
+      const v8i &bb = (t & 1) ? b1 : b0;
+      const v16f dt = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], bb, (v16f){}, 2, 2, 0, 127, 0, 127);
+      __builtin_amdgcn_sched_barrier(0);
+      if (t > 0) {
+        const int ip = (t - 1) >> 1, jp = (t - 1) & 1;
+        const float sp = jp ? s1 : s0;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) F[ip][jp][e] = __builtin_fmaf(sp, dprev[e], F[ip][jp][e]);
+      }
+      // operands are reloaded with the next group's values right after their
+      // last MFMA: a[i] after tile 2i+1, b0 after tile 6, b1 after tile 7
+      // (after the last group this reads a stale slot that is never used)
+      if (t & 1) a[i] = frag(fa + JN * V2::STAGE + i * CHUNK_TILE, 0, 0);
+      if (t == 6) b0 = frag(fb + JN * V2::STAGE, 0, 0);
+      if (t == 7) {
+        b1 = frag(fb + JN * V2::STAGE + CHUNK_TILE, 0, 0);
+        ns0 = fs[JN * V2::STAGE / 4];
+        ns1 = fs[JN * V2::STAGE / 4 + 32];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      dprev = dt;
+    }
+    // last tile: its MFMA was issued one tile ago
+#pragma unroll
+    for (int e = 0; e < 16; ++e) F[3][1][e] = __builtin_fmaf(s1, dprev[e], F[3][1][e]);
+    s0 = ns0;
+    s1 = ns1;
+  };
+
+  for (int g = 0; g < G; g += V2::NSLOT) {
+    body(std::integral_constant<int, 0>{}, g);
+    if (g + 1 < G) body(std::integral_constant<int, 1>{}, g + 1);
+    if (g + 2 < G) body(std::integral_constant<int, 2>{}, g + 2);
+  }
+
+  // ---- epilogue (as in the kernel above)
+  float w1v[2] = {0.f, 0.f}, bv[2] = {0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int col = n0 + wn * 64 + 32 * j + r;
+    if (col < N) {
+      if (mean) w1v[j] = w1[col];
+      if (bias) bv[j] = bias[col];
+    }
+  }
+  __syncthreads();
+  constexpr int SROW = 144;
+  uint8_t *stg = smem + wave * (32 * SROW);
+  const bool vec_ok = ((reinterpret_cast<uintptr_t>(y) & 15) == 0) && (ldy % 8 == 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int rr = (e >> 2) * 8 + half * 4 + (e & 3);
+      const int rl = wm * 128 + 32 * i + rr;
+      const float al = lds_alpha[rl];
+      const float mu = lds_mean[rl];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        float v = al * F[i][j][e];
+        if (mean) v = __builtin_fmaf(mu, w1v[j], v);
+        if (bias) v = v + bv[j];
+        *reinterpret_cast<uint16_t *>(stg + rr * SROW + (32 * j + r) * 2) = f32_to_bf16_rne(v);
+      }
+    }
+    const int cl = (lane & 7) * 8;
+    const int col = n0 + wn * 64 + cl;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int rr = (lane >> 3) + 8 * q;
+      const int64_t row = m0 + wm * 128 + 32 * i + rr;
+      const uint4 v = *reinterpret_cast<const uint4 *>(stg + rr * SROW + cl * 2);
+      if (row >= M) continue;
+      uint16_t *dst = y + row * ldy + col;
+      if (vec_ok && col + 8 <= N) {
+        *reinterpret_cast<uint4 *>(dst) = v;
+      } else {
+        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          if (col + c < N) dst[c] = (uint16_t)(wv[c >> 1] >> (16 * (c & 1)));
+      }
+    }
+  }
+}
+
+hipError_t launch_v2(const uint8_t *A, const float *a_scale, int64_t M, int K, const uint8_t *W, const float *wst,
+                     int N, int Np, const float *mean, const float *w1, const float *bias, uint16_t *y, int64_t ldy,
+                     hipStream_t stream) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void *)gemm_fp6_v2_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       V2::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  dim3 grid((unsigned)((N + V2::BN - 1) / V2::BN), (unsigned)((M + V2::BM - 1) / V2::BM));
+  hipLaunchKernelGGL(gemm_fp6_v2_kernel, grid, dim3(512), V2::LDS_BYTES, stream, A, a_scale, M, K, W, wst, N, Np,
+                     mean, w1, bias, y, ldy);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm_fp6(const uint8_t *A, int planes, const float *a_scale, int64_t M, int K, const uint8_t *W,
@@ -355,6 +604,9 @@ hipError_t launch_gemm_fp6(const uint8_t *A, int planes, const float *a_scale, i
   const int Np = (N + 31) / 32 * 32;
   const int64_t plane = tiled_bytes(M, K);
   if (planes == 2) return launch_cfg<2, 4, 2, 3>(A, plane, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy, stream);
+  // the prefetching kernel addresses operands with 32-bit offsets from their base
+  if (tiled_bytes(M, K) < (int64_t(1) << 32) && tiled_bytes(Np, K) < (int64_t(1) << 32))
+    return launch_v2(A, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy, stream);
   return launch_cfg<2, 4, 1, FP6_STAGES>(A, plane, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy, stream);
 }
 
