@@ -67,10 +67,11 @@ enum { OQ_W4 = 4, OQ_W_MXFP4 = 0x104 };
  * Operand layout flag, OR-ed into afmt (OQ_A4 | OQ_TILED, OQ_A6 | OQ_TILED):
  * codes are stored as FP6 E2M3 values of the integer codes (exact for
  * |q| <= 7) in the MFMA-tiled layout below, the layout the fast GEMM reads.
- *   rows padded to a multiple of 32, K a multiple of 64; the 64 codes of
- *   (row r, k-group kg = k / 64) form a 384-bit string with code j = k % 64 in
- *   bits [6j, 6j+6); its six 8-byte chunks c = 0..5 sit at byte
- *   ((r/32) * (K/64) + kg) * 1536 + c * 256 + (r % 32) * 8.
+ *   rows padded to a multiple of 32, K a multiple of 64; tile (r/32, kg =
+ *   k / 64) is 1536 bytes at ((r/32) * (K/64) + kg) * 1536.  Within it, the
+ *   32 codes of row r and k-half h (k = 64 kg + 32 h + j, j = 0..31) form a
+ *   192-bit string with code j in bits [6j, 6j+6); with l = 32 h + r % 32,
+ *   its bytes 0..15 sit at tile + 16 l and bytes 16..23 at tile + 1024 + 8 l.
  *   One plane is oq_tiled_bytes(rows, K) bytes.  OQ_A6 uses two planes:
  *   q = 8 qh + ql with qh = floor(q / 8) in plane 0 and ql = q - 8 qh in
  *   plane 1 (each in [-4, 7]).

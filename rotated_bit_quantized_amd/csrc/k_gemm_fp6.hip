@@ -14,12 +14,11 @@
 // bit-identical outputs.
 //
 // Tiled operand layout (rows padded to a multiple of 32, K a multiple of 64):
-//   row r, k-group kg = k / 64 occupies 48 bytes split into six 8-byte chunks;
-//   chunk c of (r, kg) is at ((r/32) * (K/64) + kg) * 1536 + c * 256 + (r%32) * 8
-//   and holds bits [64c, 64c + 64) of the 384-bit string in which value
-//   j = k % 64 occupies bits [6j, 6j + 6).  Lane l of an MFMA fragment (row
-//   l % 32, k-half l / 32) reads chunks 3(l/32) .. 3(l/32)+2: 24 bytes = its
-//   32 FP6 values, and the 32 lanes of a half read 256 contiguous bytes.
+//   tile (r/32, kg = k / 64) is 1536 contiguous bytes.  Lane l of an MFMA
+//   fragment (row l % 32, k-half l / 32) needs the 32 FP6 values of its row and
+//   half as a 192-bit string (value j in bits [6j, 6j + 6)); its bytes 0..15
+//   sit at tile + 16 l and bytes 16..23 at tile + 1024 + 8 l, so a fragment is
+//   one 16-byte and one 8-byte LDS read per lane, both conflict-free.
 // Weight scales are stored transposed, [K/64][N_padded] float32.
 //
 // Workgroup: WM x WN wavefronts, each computing 128 x 64 outputs (4 x 2 MFMA
@@ -33,6 +32,12 @@
 #ifndef FP6_STAGES
 #define FP6_STAGES 3
 #endif
+#ifndef FP6_SLOTS
+#define FP6_SLOTS 4
+#endif
+#ifndef FP6_PAIRED
+#define FP6_PAIRED true
+#endif
 
 namespace oq {
 namespace {
@@ -44,12 +49,16 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int CHUNK_TILE = 1536;  // bytes of one 32-row x 64-k tile
 
 
+// MFMA operand of lane l (row l % 32, k-half l / 32) from one tile: its 24
+// bytes are at tile + 16 l (16 bytes) and tile + 1024 + 8 l (8 bytes)
+__device__ __forceinline__ v8i frag_at(const uint8_t *main16, const uint8_t *tail8) {
+  const uint4 a = *reinterpret_cast<const uint4 *>(main16);
+  const uint2 b = *reinterpret_cast<const uint2 *>(tail8);
+  return (v8i){(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, 0, 0};
+}
 __device__ __forceinline__ v8i frag(const uint8_t *tile, int half, int r) {
-  const uint8_t *p = tile + (3 * half) * 256 + r * 8;
-  const uint2 a = *reinterpret_cast<const uint2 *>(p);
-  const uint2 b = *reinterpret_cast<const uint2 *>(p + 256);
-  const uint2 c = *reinterpret_cast<const uint2 *>(p + 512);
-  return (v8i){(int)a.x, (int)a.y, (int)b.x, (int)b.y, (int)c.x, (int)c.y, 0, 0};
+  const int l = 32 * half + r;
+  return frag_at(tile + 16 * l, tile + 1024 + 8 * l);
 }
 
 // s_waitcnt vmcnt(n) for a wave-uniform runtime n (the immediate must be a
@@ -322,10 +331,10 @@ __global__ void prepack_w4_kernel(const uint8_t *__restrict__ w, const float *__
     bits[b >> 5] |= c[j] << (b & 31);
     if ((b & 31) > 26) bits[(b >> 5) + 1] |= c[j] >> (32 - (b & 31));
   }
-  uint8_t *tile = out + ((int64_t)(row / 32) * G + kg) * CHUNK_TILE + (row % 32) * 8;
-#pragma unroll
-  for (int q = 0; q < 3; ++q)
-    *reinterpret_cast<uint2 *>(tile + (3 * half + q) * 256) = make_uint2(bits[2 * q], bits[2 * q + 1]);
+  uint8_t *tile = out + ((int64_t)(row / 32) * G + kg) * CHUNK_TILE;
+  const int l = 32 * half + row % 32;
+  *reinterpret_cast<uint4 *>(tile + 16 * l) = make_uint4(bits[0], bits[1], bits[2], bits[3]);
+  *reinterpret_cast<uint2 *>(tile + 1024 + 8 * l) = make_uint2(bits[4], bits[5]);
   if (half == 0) out_s[(int64_t)kg * Np + row] = row < N ? ws[(int64_t)row * G + kg] : 0.f;
 }
 
@@ -382,21 +391,26 @@ __device__ __forceinline__ void wait_vm() {
 }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-struct V2 {
-  static constexpr int WAVES = 8, BM = 256, BN = 256, NSLOT = 3;
+template <int NSLOT_>
+struct V2C {
+  static constexpr int WAVES = 8, BM = 256, BN = 256, NSLOT = NSLOT_;
   static constexpr int A_BYTES = (BM / 32) * CHUNK_TILE, B_BYTES = (BN / 32) * CHUNK_TILE;
   static constexpr int S_BYTES = BN * 4;
   static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
   static constexpr int ROWS_OFF = NSLOT * STAGE;
-  static constexpr int LDS_BYTES = ROWS_OFF + 2 * BM * 4;
+  static constexpr int SROW = 144;  // padded bytes per staged output row of 64 bf16
+  static constexpr int STG_OFF = ROWS_OFF + 2 * BM * 4;  // per-wave epilogue staging
+  static constexpr int LDS_BYTES = STG_OFF + WAVES * 32 * SROW;
   static constexpr int PER_STAGE = 4;  // copy instructions per wave per stage
 };
 
+template <int NSLOT, bool PAIRED>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_scale, int64_t M, int K,
                    const uint8_t *__restrict__ W, const float *__restrict__ wst, int N, int Np,
                    const float *__restrict__ mean, const float *__restrict__ w1, const float *__restrict__ bias,
                    uint16_t *__restrict__ y, int64_t ldy) {
+  using V2 = V2C<NSLOT>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const uint32_t lds0 = lds_addr_of(smem);
   const int lane = threadIdx.x & 63;
@@ -442,8 +456,9 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_sc
 
   const int wm = wave >> 2, wn = wave & 3;
   const int r = lane & 31, half = lane >> 5;
-  const uint8_t *fa = smem + (wm * 4) * CHUNK_TILE + (3 * half) * 256 + r * 8;
-  const uint8_t *fb = smem + V2::A_BYTES + (wn * 2) * CHUNK_TILE + (3 * half) * 256 + r * 8;
+  const uint8_t *fa = smem + (wm * 4) * CHUNK_TILE + 16 * lane;  // + 1024 - 8 lane: the 8-byte part
+  const uint8_t *fb = smem + V2::A_BYTES + (wn * 2) * CHUNK_TILE + 16 * lane;
+  const int tail = 1024 - 8 * lane;
   const float *fs = reinterpret_cast<const float *>(smem + V2::A_BYTES + V2::B_BYTES) + wn * 64 + r;
 
   float F[4][2][16];
@@ -462,33 +477,32 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_sc
     lds_mean[t] = (mean && row < M) ? mean[row] : 0.f;
   }
 
-  // ---- prologue: stages 0..2 in flight, group 0's operands loaded
+  // ---- prologue: stages 0..NSLOT-1 in flight, group 0's operands loaded
   issue(0, 0);
-  if (G > 1) issue(1, 1);
-  if (G > 2) issue(2, 2);
-  if (G > 2) wait_vm<2 * V2::PER_STAGE>();
+#pragma unroll
+  for (int p = 1; p < (PAIRED ? 3 : NSLOT); ++p)
+    if (p < G) issue(p, p);
+  // stage 0 is complete once at most the later prologue stages are outstanding
+  // (the paired schedule issues stages 0..2 only and waits for all of them)
+  if (PAIRED) wait_vm<0>();
+  else if (NSLOT > 3 && G > 3) wait_vm<3 * V2::PER_STAGE>();
+  else if (G > 2) wait_vm<2 * V2::PER_STAGE>();
   else if (G > 1) wait_vm<V2::PER_STAGE>();
   else wait_vm<0>();
   __builtin_amdgcn_s_barrier();
   v8i a[4], b0, b1;
   float s0, s1, ns0 = 0.f, ns1 = 0.f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) a[i] = frag(fa + i * CHUNK_TILE, 0, 0);
-  b0 = frag(fb, 0, 0);
-  b1 = frag(fb + CHUNK_TILE, 0, 0);
+  for (int i = 0; i < 4; ++i) a[i] = frag_at(fa + i * CHUNK_TILE, fa + i * CHUNK_TILE + tail);
+  b0 = frag_at(fb, fb + tail);
+  b1 = frag_at(fb + CHUNK_TILE, fb + CHUNK_TILE + tail);
   s0 = fs[0];
   s1 = fs[32];
 
-  auto body = [&](auto jc, int g) {
-    constexpr int J = decltype(jc)::value;
-    constexpr int JN = (J + 1) % V2::NSLOT;
-    if (g + 2 < G) wait_vm<V2::PER_STAGE>();
-    else wait_vm<0>();
-    wait_lgkm0();
-    __builtin_amdgcn_s_barrier();
-    if (g + 3 < G) issue(J, g + 3);
-    __builtin_amdgcn_sched_barrier(0);
-
+  // one k-group: MFMAs of group g from registers, the next group's operands
+  // (stage g+1, slot JN) read into the registers as they free up
+  auto group = [&](auto jnc) {
+    constexpr int JN = decltype(jnc)::value;
     v16f dprev;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
@@ -504,11 +518,11 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_sc
       }
       // operands are reloaded with the next group's values right after their
       // last MFMA: a[i] after tile 2i+1, b0 after tile 6, b1 after tile 7
-      // (after the last group this reads a stale slot that is never used)
-      if (t & 1) a[i] = frag(fa + JN * V2::STAGE + i * CHUNK_TILE, 0, 0);
-      if (t == 6) b0 = frag(fb + JN * V2::STAGE, 0, 0);
+      // (after the last group this reads a settled slot that is never used)
+      if (t & 1) a[i] = frag_at(fa + JN * V2::STAGE + i * CHUNK_TILE, fa + JN * V2::STAGE + i * CHUNK_TILE + tail);
+      if (t == 6) b0 = frag_at(fb + JN * V2::STAGE, fb + JN * V2::STAGE + tail);
       if (t == 7) {
-        b1 = frag(fb + JN * V2::STAGE + CHUNK_TILE, 0, 0);
+        b1 = frag_at(fb + JN * V2::STAGE + CHUNK_TILE, fb + JN * V2::STAGE + CHUNK_TILE + tail);
         ns0 = fs[JN * V2::STAGE / 4];
         ns1 = fs[JN * V2::STAGE / 4 + 32];
       }
@@ -522,13 +536,54 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_sc
     s1 = ns1;
   };
 
-  for (int g = 0; g < G; g += V2::NSLOT) {
-    body(std::integral_constant<int, 0>{}, g);
-    if (g + 1 < G) body(std::integral_constant<int, 1>{}, g + 1);
-    if (g + 2 < G) body(std::integral_constant<int, 2>{}, g + 2);
+  if constexpr (!PAIRED) {
+    // one barrier per group: stage g in slot g % NSLOT
+    auto body = [&](auto jc, int g) {
+      constexpr int J = decltype(jc)::value;
+      // own copies of stage g+1 are complete once at most the stages issued
+      // after it (g+2 .. g+NSLOT-1) are outstanding
+      if (NSLOT > 3 && g + 3 < G) wait_vm<2 * V2::PER_STAGE>();
+      else if (g + 2 < G) wait_vm<V2::PER_STAGE>();
+      else wait_vm<0>();
+      wait_lgkm0();
+      __builtin_amdgcn_s_barrier();
+      if (g + NSLOT < G) issue(J, g + NSLOT);
+      __builtin_amdgcn_sched_barrier(0);
+      group(std::integral_constant<int, (J + 1) % NSLOT>{});
+    };
+    for (int g = 0; g < G; g += V2::NSLOT) {
+      body(std::integral_constant<int, 0>{}, g);
+      if (g + 1 < G) body(std::integral_constant<int, 1>{}, g + 1);
+      if (g + 2 < G) body(std::integral_constant<int, 2>{}, g + 2);
+      if constexpr (NSLOT > 3)
+        if (g + 3 < G) body(std::integral_constant<int, 3>{}, g + 3);
+    }
+  } else {
+    // one barrier per two groups (4 slots, stage s in slot s % 4): before
+    // groups g, g+1 every wave's copies of stages g+1 and g+2 are complete
+    // and published, and the slots of stages g-1 and g (read into registers
+    // during the previous two groups) are refilled with stages g+3 and g+4
+    static_assert(NSLOT == 4, "paired schedule uses four slots");
+    auto pair = [&](auto pc, int g) {
+      constexpr int P = decltype(pc)::value;  // g % 4 == 2 P
+      wait_lgkm0();
+      wait_vm<0>();
+      __builtin_amdgcn_s_barrier();
+      if (g + 3 < G) issue((2 * P + 3) % 4, g + 3);
+      if (g + 4 < G) issue((2 * P + 4) % 4, g + 4);
+      __builtin_amdgcn_sched_barrier(0);
+      group(std::integral_constant<int, (2 * P + 1) % 4>{});
+      if (g + 1 < G) group(std::integral_constant<int, (2 * P + 2) % 4>{});
+    };
+    for (int g = 0; g < G; g += 4) {
+      pair(std::integral_constant<int, 0>{}, g);
+      if (g + 2 < G) pair(std::integral_constant<int, 1>{}, g + 2);
+    }
   }
 
-  // ---- epilogue (as in the kernel above)
+  // ---- epilogue: y = a_scale * F + mean * w1 + bias (same order as the other
+  // kernels), bf16, staged per 32-row slab in this wave's own LDS area (no
+  // workgroup barrier) so that the global writes are 16-byte runs
   float w1v[2] = {0.f, 0.f}, bv[2] = {0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -538,24 +593,29 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_sc
       if (bias) bv[j] = bias[col];
     }
   }
-  __syncthreads();
-  constexpr int SROW = 144;
-  uint8_t *stg = smem + wave * (32 * SROW);
+  constexpr int SROW = V2::SROW;
+  uint8_t *stg = smem + V2::STG_OFF + wave * (32 * SROW);
   const bool vec_ok = ((reinterpret_cast<uintptr_t>(y) & 15) == 0) && (ldy % 8 == 0);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int rr = (e >> 2) * 8 + half * 4 + (e & 3);
-      const int rl = wm * 128 + 32 * i + rr;
-      const float al = lds_alpha[rl];
-      const float mu = lds_mean[rl];
+    for (int e4 = 0; e4 < 4; ++e4) {
+      // rows (e4 * 8 + half * 4 + 0..3) of this 32-row slab: one 16-byte read each
+      const int rl = wm * 128 + 32 * i + e4 * 8 + half * 4;
+      const float4 al4 = *reinterpret_cast<const float4 *>(lds_alpha + rl);
+      const float4 mu4 = mean ? *reinterpret_cast<const float4 *>(lds_mean + rl) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float al[4] = {al4.x, al4.y, al4.z, al4.w}, mu[4] = {mu4.x, mu4.y, mu4.z, mu4.w};
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        float v = al * F[i][j][e];
-        if (mean) v = __builtin_fmaf(mu, w1v[j], v);
-        if (bias) v = v + bv[j];
-        *reinterpret_cast<uint16_t *>(stg + rr * SROW + (32 * j + r) * 2) = f32_to_bf16_rne(v);
+      for (int e1 = 0; e1 < 4; ++e1) {
+        const int e = 4 * e4 + e1;
+        const int rr = e4 * 8 + half * 4 + e1;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          float v = al[e1] * F[i][j][e];
+          if (mean) v = __builtin_fmaf(mu[e1], w1v[j], v);
+          if (bias) v = v + bv[j];
+          *reinterpret_cast<uint16_t *>(stg + rr * SROW + (32 * j + r) * 2) = f32_to_bf16_rne(v);
+        }
       }
     }
     const int cl = (lane & 7) * 8;
@@ -579,19 +639,21 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_sc
   }
 }
 
+template <int NSLOT, bool PAIRED>
 hipError_t launch_v2(const uint8_t *A, const float *a_scale, int64_t M, int K, const uint8_t *W, const float *wst,
                      int N, int Np, const float *mean, const float *w1, const float *bias, uint16_t *y, int64_t ldy,
                      hipStream_t stream) {
+  using V2 = V2C<NSLOT>;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)gemm_fp6_v2_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       V2::LDS_BYTES);
+    hipError_t e = hipFuncSetAttribute((const void *)gemm_fp6_v2_kernel<NSLOT, PAIRED>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, V2::LDS_BYTES);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   dim3 grid((unsigned)((N + V2::BN - 1) / V2::BN), (unsigned)((M + V2::BM - 1) / V2::BM));
-  hipLaunchKernelGGL(gemm_fp6_v2_kernel, grid, dim3(512), V2::LDS_BYTES, stream, A, a_scale, M, K, W, wst, N, Np,
-                     mean, w1, bias, y, ldy);
+  hipLaunchKernelGGL((gemm_fp6_v2_kernel<NSLOT, PAIRED>), grid, dim3(512), V2::LDS_BYTES, stream, A, a_scale, M, K, W, wst,
+                     N, Np, mean, w1, bias, y, ldy);
   return hipGetLastError();
 }
 
@@ -606,7 +668,7 @@ hipError_t launch_gemm_fp6(const uint8_t *A, int planes, const float *a_scale, i
   if (planes == 2) return launch_cfg<2, 4, 2, 3>(A, plane, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy, stream);
   // the prefetching kernel addresses operands with 32-bit offsets from their base
   if (tiled_bytes(M, K) < (int64_t(1) << 32) && tiled_bytes(Np, K) < (int64_t(1) << 32))
-    return launch_v2(A, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy, stream);
+    return launch_v2<FP6_SLOTS, FP6_PAIRED>(A, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy, stream);
   return launch_cfg<2, 4, 1, FP6_STAGES>(A, plane, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy, stream);
 }
 

@@ -222,10 +222,12 @@ rpbh_quant_kernel(const void *__restrict__ xin, int64_t M, int d, int64_t ldx,
       q[j] = (int)fminf(fmaxf(tq, -fq), fq);
     }
     if (MODE == OUT_FP6 || MODE == OUT_FP6X2) {
-      // tiled layout: (row, k-group) tile of 6 x 8-byte chunks; this thread's
-      // 16 values are 96 bits starting at bit 6 * (base % 32) of its half
+      // tiled layout (see k_gemm_fp6.hip): this thread's 16 values are the
+      // first or second 96 bits of the 192-bit string of (row, k-half), whose
+      // bytes 0..15 sit at tile + 16 l and bytes 16..23 at tile + 1024 + 8 l
       const int kg = base >> 6, hf = (base >> 5) & 1, j0 = base & 31;
-      uint8_t *tile = static_cast<uint8_t *>(out) + ((row >> 5) * (d >> 6) + kg) * 1536 + (row & 31) * 8;
+      const int l = 32 * hf + (int)(row & 31);
+      uint8_t *tile = static_cast<uint8_t *>(out) + ((row >> 5) * (d >> 6) + kg) * 1536;
       const int64_t pstride = tiled_bytes(M, d);
 #pragma unroll
       for (int p = 0; p < (MODE == OUT_FP6X2 ? 2 : 1); ++p) {
@@ -241,11 +243,11 @@ rpbh_quant_kernel(const void *__restrict__ xin, int64_t M, int d, int64_t ldx,
         const uint32_t w2 = (c[10] >> 4) | (c[11] << 2) | (c[12] << 8) | (c[13] << 14) | (c[14] << 20) | (c[15] << 26);
         uint8_t *tp = tile + p * pstride;
         if (j0 == 0) {
-          *reinterpret_cast<uint2 *>(tp + (3 * hf) * 256) = make_uint2(w0, w1);
-          *reinterpret_cast<uint32_t *>(tp + (3 * hf + 1) * 256) = w2;
+          *reinterpret_cast<uint2 *>(tp + 16 * l) = make_uint2(w0, w1);
+          *reinterpret_cast<uint32_t *>(tp + 16 * l + 8) = w2;
         } else {
-          *reinterpret_cast<uint32_t *>(tp + (3 * hf + 1) * 256 + 4) = w0;
-          *reinterpret_cast<uint2 *>(tp + (3 * hf + 2) * 256) = make_uint2(w1, w2);
+          *reinterpret_cast<uint32_t *>(tp + 16 * l + 12) = w0;
+          *reinterpret_cast<uint2 *>(tp + 1024 + 8 * l) = make_uint2(w1, w2);
         }
       }
       continue;

@@ -78,15 +78,17 @@ __device__ __forceinline__ void fwht_row(float (&v)[SLOTS][16], int lane, int nl
 }
 
 // Stores the 16 codes of two slots (a: coordinates base..base+15, b: the same
-// 1024 further on) in the tiled layout (see k_gemm_fp6.hip): 16 consecutive
-// codes are the 96-bit string at bit 6 (base % 32) of their half of the
-// k-group.  The codes arrive as integer-valued floats (+0 for zero) and are
-// converted with v_cvt_scalef32_2xpk16_fp6_f32 (exact: |t| <= 7 or a plane of
-// it), which interleaves its sources: field 2k from src0[k], 2k+1 from
-// src1[k].  part: 0 the codes, 1 the high plane floor(t/8), 2 the low plane
+// 1024 further on) of row 32 t + rr in the tiled layout (see k_gemm_fp6.hip):
+// the 32 codes of (row, k-half h) form a 192-bit string whose bytes 0..15 sit
+// at tile + 16 l and bytes 16..23 at tile + 1024 + 8 l, l = 32 h + rr; this
+// lane's 16 codes are its first (base % 32 == 0) or second 96 bits.
+// The codes arrive as integer-valued floats (+0 for zero) and are converted
+// with v_cvt_scalef32_2xpk16_fp6_f32 (exact: |t| <= 7 or a plane of it),
+// which interleaves its sources: field 2k from src0[k], 2k+1 from src1[k].
+// part: 0 the codes, 1 the high plane floor(t/8), 2 the low plane
 // t - 8 floor(t/8).
 __device__ __forceinline__ void store_fp6_pair(const float (&ta)[16], const float (&tb)[16], int part,
-                                               uint8_t *tile_row, int base, bool wa, bool wb) {
+                                               uint8_t *tile_base, int rr, int base, bool wa, bool wb) {
   v16f s0, s1;
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
@@ -101,28 +103,29 @@ __device__ __forceinline__ void store_fp6_pair(const float (&ta)[16], const floa
     s1[k] = e1;
   }
   const v6u pk = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(s0, s1, 1.0f);
-  // base % 64 is 16 j0' with j0' in 0..3 (lane parity picks the half word)
   const int kg = base >> 6, hf = (base >> 5) & 1, j0 = base & 31;
-  uint8_t *tp = tile_row + kg * 1536 + (3 * hf) * 256;
-  // slot b lies 1024 coordinates on: 16 k-groups further, same half and offset
-  uint8_t *tq = tp + 16 * 1536;
+  const int l = 32 * hf + rr;
+  uint8_t *tm = tile_base + kg * 1536 + 16 * l;         // bytes 0..15 of the string
+  uint8_t *tt = tile_base + kg * 1536 + 1024 + 8 * l;   // bytes 16..23
+  // slot b lies 1024 coordinates on: 16 k-groups further
+  constexpr int SB = 16 * 1536;
   if (j0 == 0) {
     if (wa) {
-      *reinterpret_cast<uint2 *>(tp) = make_uint2(pk[0], pk[1]);
-      *reinterpret_cast<uint32_t *>(tp + 256) = pk[2];
+      *reinterpret_cast<uint2 *>(tm) = make_uint2(pk[0], pk[1]);
+      *reinterpret_cast<uint32_t *>(tm + 8) = pk[2];
     }
     if (wb) {
-      *reinterpret_cast<uint2 *>(tq) = make_uint2(pk[3], pk[4]);
-      *reinterpret_cast<uint32_t *>(tq + 256) = pk[5];
+      *reinterpret_cast<uint2 *>(tm + SB) = make_uint2(pk[3], pk[4]);
+      *reinterpret_cast<uint32_t *>(tm + SB + 8) = pk[5];
     }
   } else {
     if (wa) {
-      *reinterpret_cast<uint32_t *>(tp + 256 + 4) = pk[0];
-      *reinterpret_cast<uint2 *>(tp + 512) = make_uint2(pk[1], pk[2]);
+      *reinterpret_cast<uint32_t *>(tm + 12) = pk[0];
+      *reinterpret_cast<uint2 *>(tt) = make_uint2(pk[1], pk[2]);
     }
     if (wb) {
-      *reinterpret_cast<uint32_t *>(tq + 256 + 4) = pk[3];
-      *reinterpret_cast<uint2 *>(tq + 512) = make_uint2(pk[4], pk[5]);
+      *reinterpret_cast<uint32_t *>(tm + SB + 12) = pk[3];
+      *reinterpret_cast<uint2 *>(tt + SB) = make_uint2(pk[4], pk[5]);
     }
   }
 }
@@ -354,7 +357,8 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
       // Codes are formed as floats (integer-valued, |t| <= qmax, +0 for zero)
       // and converted two slots at a time with v_cvt_scalef32_2xpk16_fp6_f32,
       // which interleaves its two sources field by field.
-      uint8_t *tb = static_cast<uint8_t *>(out) + ((row >> 5) * (d >> 6)) * 1536 + (row & 31) * 8;
+      uint8_t *tb = static_cast<uint8_t *>(out) + ((row >> 5) * (d >> 6)) * 1536;
+      const int rr = (int)(row & 31);
       const int64_t pstride = tiled_bytes(M, d);
 #pragma unroll
       for (int s0 = 0; s0 < SLOTS; s0 += 2) {
@@ -367,10 +371,10 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
         }
         const bool wa = act[s0], wb = two && act[two ? s0 + 1 : s0];
         if (mode == OUT_FP6) {
-          store_fp6_pair(ta, tbv, 0, tb, 1024 * s0 + 16 * lane, wa, wb);
+          store_fp6_pair(ta, tbv, 0, tb, rr, 1024 * s0 + 16 * lane, wa, wb);
         } else {
-          store_fp6_pair(ta, tbv, 1, tb, 1024 * s0 + 16 * lane, wa, wb);
-          store_fp6_pair(ta, tbv, 2, tb + pstride, 1024 * s0 + 16 * lane, wa, wb);
+          store_fp6_pair(ta, tbv, 1, tb, rr, 1024 * s0 + 16 * lane, wa, wb);
+          store_fp6_pair(ta, tbv, 2, tb + pstride, rr, 1024 * s0 + 16 * lane, wa, wb);
         }
       }
     }

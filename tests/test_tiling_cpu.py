@@ -2,7 +2,7 @@
 definition (CPU only)."""
 import numpy as np
 
-from tiling import e2m3, split_a6, tile
+from tiling import e2m3, row_mask, split_a6, tile
 
 
 def _decode_e2m3(f):
@@ -19,13 +19,23 @@ def test_e2m3_exact_for_int4_codes():
 
 def test_tile_bit_placement():
     codes = np.zeros((32, 64), dtype=np.int64)
-    codes[5, 0] = 1      # code 0 -> bits 0..5 of chunk 0, row 5
-    codes[7, 33] = -7    # code 33 -> bits 198..203 -> chunk 3, bits 6..11
-    t = tile(codes).reshape(6, 32, 8)
-    assert t[0, 5, 0] == 0x08
-    val = int.from_bytes(bytes(t[3, 7]), "little")
+    codes[5, 0] = 1      # row 5, half 0, code 0 -> bits 0..5 of lane 5's string (byte 16*5)
+    codes[7, 33] = -7    # row 7, half 1, code 1 -> bits 6..11 of lane 39's string
+    codes[2, 31] = 2     # row 2, half 0, code 31 -> bits 186..191 -> byte 23 -> tail byte 7 of lane 2
+    t = tile(codes)
+    assert t[16 * 5] == 0x08
+    val = int.from_bytes(bytes(t[16 * 39:16 * 39 + 2]), "little")
     assert (val >> 6) & 0x3F == 0x3E
-    assert t.sum() == 0x08 + sum(bytes(t[3, 7]))
+    assert t[1024 + 8 * 2 + 7] == (0x10 << 2) & 0xFF      # 2 -> 0x10 in E2M3, bits 2..7 of byte 23
+    assert int(t.sum()) == 0x08 + sum(bytes(t[16 * 39:16 * 39 + 2])) + ((0x10 << 2) & 0xFF)
+
+
+def test_row_mask():
+    m = row_mask(40, 128).reshape(2, 2, 1536)
+    assert m[0].all()                                 # rows 0..31 all live
+    assert m[1, :, 16 * 7].all() and not m[1, :, 16 * 8].any()        # row 39 live, row 40 not (half 0)
+    assert m[1, :, 16 * (32 + 7)].all() and not m[1, :, 16 * (32 + 8)].any()
+    assert m[1, :, 1024 + 8 * 7].all() and not m[1, :, 1024 + 8 * 8].any()
 
 
 def test_a6_split():

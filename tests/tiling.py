@@ -1,8 +1,9 @@
 """NumPy writer of the tiled FP6 operand layout, from its definition in
 include/oq.h (a data layout, no arithmetic of the method): rows padded to 32,
-the 64 codes of (row r, k-group kg) form a 384-bit string with code j in bits
-[6j, 6j+6); chunk c (8 bytes) of it sits at
-((r/32) * (K/64) + kg) * 1536 + c * 256 + (r % 32) * 8.
+K a multiple of 64, tile (r/32, kg = k/64) of 1536 bytes at
+((r/32) * (K/64) + kg) * 1536.  The 32 codes of row r and k-half h form a
+192-bit string with code j in bits [6j, 6j+6); with l = 32 h + r % 32, its
+bytes 0..15 sit at tile + 16 l and bytes 16..23 at tile + 1024 + 8 l.
 FP6 E2M3: sign bit 5, exponent bits 4..3 (bias 1), mantissa bits 2..0."""
 import numpy as np
 
@@ -18,6 +19,20 @@ def e2m3(q):
     return E2M3_OF_INT[np.abs(q)] | np.where(q < 0, np.uint64(0x20), np.uint64(0))
 
 
+def _strings(codes: np.ndarray) -> np.ndarray:
+    """int codes [Rp, K] -> the 24-byte strings [Rp, K/64, 2, 24] of (row, kg, half)."""
+    Rp, K = codes.shape
+    G = K // 64
+    f = e2m3(codes).reshape(Rp, G, 2, 32)
+    out = np.zeros((Rp, G, 2, 24), dtype=np.uint8)
+    for j in range(32):
+        for b in range(6):
+            pos = 6 * j + b
+            bit = ((f[..., j] >> np.uint64(b)) & np.uint64(1)).astype(np.uint8)
+            out[..., pos // 8] |= (bit << (pos % 8)).astype(np.uint8)
+    return out
+
+
 def tile(codes: np.ndarray) -> np.ndarray:
     """int codes [R, K] in [-7, 7] -> tiled bytes (R padded to 32)."""
     R, K = codes.shape
@@ -26,17 +41,25 @@ def tile(codes: np.ndarray) -> np.ndarray:
     G = K // 64
     c = np.zeros((Rp, K), dtype=np.int64)
     c[:R] = codes
-    f = e2m3(c).reshape(Rp, G, 64)
-    out = np.zeros((Rp // 32, G, 6, 32, 8), dtype=np.uint8)
-    for j in range(64):
-        bit = 6 * j
-        for b in range(6):
-            pos = bit + b
-            chunk, inchunk = pos // 64, pos % 64
-            byte, bitpos = inchunk // 8, inchunk % 8
-            v = ((f[:, :, j] >> np.uint64(b)) & np.uint64(1)).astype(np.uint8)  # [Rp, G]
-            out[:, :, chunk, :, byte] |= (v.reshape(Rp // 32, 32, G).transpose(0, 2, 1) << bitpos).astype(np.uint8)
+    st = _strings(c).reshape(Rp // 32, 32, G, 2, 24).transpose(0, 2, 3, 1, 4)  # [rb, kg, h, r, 24]
+    out = np.zeros((Rp // 32, G, 1536), dtype=np.uint8)
+    out[:, :, :1024] = st[..., :16].reshape(Rp // 32, G, 1024)   # l = 32 h + r, 16 bytes each
+    out[:, :, 1024:] = st[..., 16:].reshape(Rp // 32, G, 512)    # 8 bytes each
     return out.reshape(-1)
+
+
+def row_mask(R: int, K: int) -> np.ndarray:
+    """Boolean mask over the tiled bytes of R rows (padded to 32): True where the
+    byte belongs to a row < R (padding rows are never written by the kernels)."""
+    Rp = (R + 31) // 32 * 32
+    G = K // 64
+    rows = np.arange(Rp).reshape(Rp // 32, 32)
+    live = rows < R                                              # [rb, r]
+    lane = np.concatenate([live, live], axis=1)                  # l = 32 h + r
+    m = np.zeros((Rp // 32, G, 1536), dtype=bool)
+    m[:, :, :1024] = np.repeat(lane, 16, axis=1)[:, None, :]
+    m[:, :, 1024:] = np.repeat(lane, 8, axis=1)[:, None, :]
+    return m.reshape(-1)
 
 
 def split_a6(q):
