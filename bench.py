@@ -70,11 +70,21 @@ def _setup(torch, oq, WL, cid, n_sets_bytes=600 << 20):
         rot = oq.Rotation.dense32(torch.from_numpy(wl.t_act_bits.view("int16")).to(dev),
                                   torch.from_numpy(wl.t_wgt).to(dev))
         ws = [oq.oq_quant_weight(torch.from_numpy(W).to(dev), rot, oq.OQ_W_MXFP4, 32) for W in wl.weights]
+        st["tiled"] = wl.K % 128 == 0
+        if st["tiled"]:  # offline: repack into the MFMA operand layout
+            for w, W in zip(ws, wl.weights):
+                t = oq.oq_prepack_mx(w["codes"], w["scales"], W.shape[0], wl.K)
+                w["codes"], w["scales"] = t["codes"], t["scales"]
     x0 = torch.from_numpy(wl.x_bits.view("int16")).to(dev)
     nsets = max(1, -(-n_sets_bytes // (x0.numel() * 2)))
     st["xs"] = [x0] + [x0.clone() for _ in range(nsets - 1)]
     M, K = wl.M, wl.K
-    if s.afmt == oq.OQ_MXFP4:
+    if s.afmt == oq.OQ_MXFP4 and st["tiled"]:
+        nb = oq.oq_tiled_mx_bytes(M, K)
+        st["codes"] = torch.empty(nb, dtype=torch.uint8, device=dev)
+        st["e8m0"] = torch.empty(nb // 16, dtype=torch.uint8, device=dev)
+        st["scale"] = None
+    elif s.afmt == oq.OQ_MXFP4:
         st["codes"] = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
         st["e8m0"] = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
         st["scale"] = None
@@ -105,7 +115,10 @@ def _launches(oq, st, i):
     M, K = st["wl"].M, st["wl"].K
     for j, (wq, y) in enumerate(zip(st["ws"], st["ys"])):
         N = y.shape[1]
-        if st["tiled"]:
+        if st["tiled"] and s.afmt == oq.OQ_MXFP4:
+            f = (lambda wq=wq, y=y, N=N: oq.oq_gemm_w4a4(afmt, st["codes"], st["e8m0"], wq["codes"], wq["scales"],
+                                                         N, 32, y=y, M=M, K=K))
+        elif st["tiled"]:
             f = (lambda wq=wq, y=y, N=N: oq.oq_gemm_w4a4(afmt, st["codes"], st["scale"], wq["codes"], wq["scales"],
                                                          N, 64, mean=st["mean"], w1=wq["w1"], y=y, M=M, K=K))
         elif s.afmt == oq.OQ_MXFP4:

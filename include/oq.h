@@ -78,11 +78,27 @@ enum { OQ_W4 = 4, OQ_W_MXFP4 = 0x104 };
  * Weights for tiled GEMMs come from oq_prepack_w4 (same layout, one plane,
  * plus scales transposed to [K/64][N_padded]).  The per-token scale
  * (a_scale) and mean arrays are unchanged.  Tiled GEMMs require group == 64.
+ *
+ * OQ_MXFP4 | OQ_TILED (K a multiple of 128): the MXFP4 codes and E8M0 scales
+ * in the layout the MXFP4 GEMM copies whole:
+ *   codes: rows padded to 32; tile (r/32, kg = k / 64) is 1024 bytes at
+ *     ((r/32) * (K/64) + kg) * 1024; the 16 bytes of row r and k-half h (32
+ *     E2M1 codes, code j in bits [4j, 4j+4), the bytes of the row-major
+ *     layout) sit at tile + 16 (32 h + r % 32).  oq_tiled_mx_bytes(rows, K).
+ *   scales: one 32-bit word per (128-wide k-slice s, row r) at byte
+ *     (s * rows_padded + r) * 4, holding the E8M0 bytes of the blocks
+ *     4s .. 4s+3 in order; oq_tiled_mx_bytes(rows, K) / 16 bytes, 4-byte
+ *     aligned.  Padding rows carry zero codes.
+ * Weights come from oq_prepack_mx.
  */
 enum { OQ_TILED = 0x10000 };
 
-/* Bytes of one plane of the tiled layout for `rows` rows of width K. */
+/* Bytes of one plane of the tiled FP6 layout for `rows` rows of width K. */
 size_t oq_tiled_bytes(int64_t rows, int32_t K);
+
+/* Bytes of the tiled MXFP4 codes for `rows` rows of width K (the scale words
+ * take a sixteenth of that). */
+size_t oq_tiled_mx_bytes(int64_t rows, int32_t K);
 
 /*
  * Rotation descriptor (host struct, device arrays).
@@ -248,6 +264,17 @@ int oq_linear_fused(const uint16_t *x, int64_t M, int32_t K, int64_t ldx,
  */
 int oq_prepack_w4(const uint8_t *w, const float *w_scale, int32_t N, int32_t K, int32_t group,
                   uint8_t *w_tiled, float *w_scale_t, hipStream_t stream);
+
+/*
+ * oq_prepack_mx -- repack canonical MXFP4 weights (oq_quant_weight
+ * OQ_W_MXFP4 output: codes [N][K/2], E8M0 [N][K/32]) into the tiled MXFP4
+ * layout for OQ_MXFP4 | OQ_TILED GEMMs.  Values are unchanged.  w_tiled:
+ * oq_tiled_mx_bytes(N, K) bytes; w_e8m0_tiled: a sixteenth of that, 4-byte
+ * aligned (padding rows get zero codes and the unit scale 127).
+ * K must be a multiple of 128.
+ */
+int oq_prepack_mx(const uint8_t *w, const uint8_t *w_e8m0, int32_t N, int32_t K,
+                  uint8_t *w_tiled, uint8_t *w_e8m0_tiled, hipStream_t stream);
 
 enum { OQ_OP_GEMM_W4A8 = 1, OQ_OP_GEMM_W4A4 = 2, OQ_OP_LINEAR = 3 };
 

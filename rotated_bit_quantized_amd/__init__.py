@@ -11,5 +11,5 @@ from ._binding import (  # noqa: F401
     OQ_ROT_DENSE32, OQ_ROT_RPBH, OQ_TILED,
     OQ_ERR_ALIGNMENT, OQ_ERR_HIP, OQ_ERR_INVALID_ARG, OQ_ERR_UNSUPPORTED, OQ_ERR_WORKSPACE,
     lib, oq_center, oq_gemm_w4a4, oq_gemm_w4a8, oq_linear_fused, oq_quant_act, oq_quant_weight,
-    oq_rotate, oq_workspace_bytes, oq_tiled_bytes, oq_prepack_w4,
+    oq_rotate, oq_workspace_bytes, oq_tiled_bytes, oq_prepack_w4, oq_tiled_mx_bytes, oq_prepack_mx,
 )

@@ -61,6 +61,8 @@ def _load():
         "oq_workspace_bytes": ([ctypes.c_int, i64, i32, i32, ctypes.c_int], sz),
         "oq_tiled_bytes": ([i64, i32], sz),
         "oq_prepack_w4": ([vp, vp, i32, i32, i32, vp, vp, vp], ctypes.c_int),
+        "oq_tiled_mx_bytes": ([i64, i32], sz),
+        "oq_prepack_mx": ([vp, vp, i32, i32, vp, vp, vp], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -72,7 +74,7 @@ def _load():
 _lib = _load()
 EXPORTED = ("oq_last_error", "oq_center", "oq_rotate", "oq_quant_act", "oq_quant_weight",
             "oq_gemm_w4a8", "oq_gemm_w4a4", "oq_linear_fused", "oq_workspace_bytes", "oq_tiled_bytes",
-            "oq_prepack_w4")
+            "oq_prepack_w4", "oq_tiled_mx_bytes", "oq_prepack_mx")
 
 
 def lib():
@@ -161,13 +163,19 @@ def oq_quant_act(x, rot: Optional[Rotation], afmt: int, center: bool = False, co
     x = _bits16(x)
     M, d = x.shape
     dev = _dev(x)
-    if codes is None and afmt & OQ_TILED:
+    mx_tiled = afmt == (OQ_MXFP4 | OQ_TILED)
+    if codes is None and mx_tiled:
+        codes = torch.empty(max(16, oq_tiled_mx_bytes(M, d)), dtype=torch.uint8, device=dev)
+    elif codes is None and afmt & OQ_TILED:
         planes = 2 if (afmt & ~OQ_TILED) == OQ_A6 else 1
         codes = torch.empty(max(1, planes * oq_tiled_bytes(M, d)), dtype=torch.uint8, device=dev)
     elif codes is None:
         width = d if afmt in (OQ_A8, OQ_A6) else d // 2
         codes = torch.empty((M, width), dtype=torch.int8 if afmt in (OQ_A8, OQ_A6) else torch.uint8, device=dev)
-    if afmt == OQ_MXFP4:
+    if mx_tiled:
+        if e8m0 is None:
+            e8m0 = torch.empty(max(4, oq_tiled_mx_bytes(M, d) // 16), dtype=torch.uint8, device=dev)
+    elif afmt == OQ_MXFP4:
         if e8m0 is None:
             e8m0 = torch.empty((M, d // 32), dtype=torch.uint8, device=dev)
     elif scale is None:
@@ -238,6 +246,21 @@ def oq_prepack_w4(w, w_scale, N: int, K: int, group: int = 64, w_tiled=None, w_s
         w_scale_t = torch.empty((K // 64, (N + 31) // 32 * 32), dtype=torch.float32, device=dev)
     _check(_lib.oq_prepack_w4(_p(w), _p(w_scale), N, K, group, _p(w_tiled), _p(w_scale_t), _stream()))
     return {"codes": w_tiled, "scales": w_scale_t}
+
+
+def oq_tiled_mx_bytes(rows: int, K: int) -> int:
+    return int(_lib.oq_tiled_mx_bytes(rows, K))
+
+
+def oq_prepack_mx(w, w_e8m0, N: int, K: int, w_tiled=None, w_e8m0_tiled=None):
+    dev = _dev(w)
+    nb = oq_tiled_mx_bytes(N, K)
+    if w_tiled is None:
+        w_tiled = torch.empty(max(16, nb), dtype=torch.uint8, device=dev)
+    if w_e8m0_tiled is None:
+        w_e8m0_tiled = torch.empty(max(4, nb // 16), dtype=torch.uint8, device=dev)
+    _check(_lib.oq_prepack_mx(_p(w), _p(w_e8m0), N, K, _p(w_tiled), _p(w_e8m0_tiled), _stream()))
+    return {"codes": w_tiled, "scales": w_e8m0_tiled}
 
 
 def oq_workspace_bytes(op: int, M: int, K: int, N: int, afmt: int) -> int:

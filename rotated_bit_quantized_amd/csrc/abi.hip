@@ -98,10 +98,14 @@ LinearWs linear_ws(int64_t M, int K, int afmt) {
   w.ldc = (base_fmt == OQ_A8 || base_fmt == OQ_A6) ? K : K / 2;
   w.ldc = (w.ldc + 15) & ~(int64_t)15;
   w.codes = 0;
-  const size_t code_bytes = (afmt & OQ_TILED) ? (size_t)(base_fmt == OQ_A6 ? 2 : 1) * tiled_bytes(M, K)
-                                              : (size_t)M * w.ldc;
+  size_t code_bytes = (afmt & OQ_TILED) ? (size_t)(base_fmt == OQ_A6 ? 2 : 1) * tiled_bytes(M, K)
+                                        : (size_t)M * w.ldc;
+  size_t sbytes = base_fmt == OQ_MXFP4 ? (size_t)M * (K / 32) : (size_t)M * 4;
+  if (afmt == (OQ_MXFP4 | OQ_TILED)) {
+    code_bytes = (size_t)tiled_mx_bytes(M, K);
+    sbytes = code_bytes / 16;
+  }
   w.scale = align_up(code_bytes);
-  const size_t sbytes = afmt == OQ_MXFP4 ? (size_t)M * (K / 32) : (size_t)M * 4;
   w.mean = align_up(w.scale + sbytes);
   w.total = align_up(w.mean + (size_t)M * 4);
   return w;
@@ -180,6 +184,19 @@ int oq_quant_act(const uint16_t *x, int64_t M, int32_t d, int64_t ldx, const oq_
   if (M > 0 && !codes) return fail(OQ_ERR_INVALID_ARG, "oq_quant_act: codes is NULL");
   if (!al16(codes) || (!(afmt & OQ_TILED) && ldc_bytes % 16))
     return fail(OQ_ERR_ALIGNMENT, "oq_quant_act: code rows must be 16-byte aligned");
+  if (afmt == (OQ_MXFP4 | OQ_TILED)) {
+    if (!rot || rot->kind != OQ_ROT_DENSE32)
+      return fail(OQ_ERR_UNSUPPORTED, "oq_quant_act: MXFP4 activations need a DENSE32 rotation");
+    if (center) return fail(OQ_ERR_UNSUPPORTED, "oq_quant_act: centering is not defined for MXFP4 here");
+    if (d % 128) return fail(OQ_ERR_UNSUPPORTED, "oq_quant_act: tiled MXFP4 needs d %% 128 == 0 (d=%d)", d);
+    if (M > 0 && !e8m0) return fail(OQ_ERR_INVALID_ARG, "oq_quant_act: e8m0 is NULL");
+    if (reinterpret_cast<uintptr_t>(e8m0) & 3) return fail(OQ_ERR_ALIGNMENT, "oq_quant_act: e8m0 must be 4-byte aligned");
+    if (scale) return fail(OQ_ERR_INVALID_ARG, "oq_quant_act: scale must be NULL for MXFP4");
+    rc = check_dense("oq_quant_act", rot, d, false);
+    if (rc) return rc;
+    g_err[0] = 0;
+    return hip_status(launch_dense32(x, M, d, ldx, rot->mats, 2, codes, 0, e8m0, stream), "oq_quant_act");
+  }
   if (afmt == OQ_MXFP4) {
     if (!rot || rot->kind != OQ_ROT_DENSE32)
       return fail(OQ_ERR_UNSUPPORTED, "oq_quant_act: MXFP4 activations need a DENSE32 rotation");
@@ -196,7 +213,7 @@ int oq_quant_act(const uint16_t *x, int64_t M, int32_t d, int64_t ldx, const oq_
   const int base_fmt = afmt & ~OQ_TILED;
   if (tiled) {
     if (base_fmt != OQ_A4 && base_fmt != OQ_A6)
-      return fail(OQ_ERR_UNSUPPORTED, "oq_quant_act: the tiled layout exists for OQ_A4 and OQ_A6");
+      return fail(OQ_ERR_UNSUPPORTED, "oq_quant_act: the tiled layout exists for OQ_A4, OQ_A6 and OQ_MXFP4");
     if (d % 64) return fail(OQ_ERR_UNSUPPORTED, "oq_quant_act: tiled codes need d %% 64 == 0 (d=%d)", d);
     if (e8m0) return fail(OQ_ERR_INVALID_ARG, "oq_quant_act: e8m0 must be NULL for integer codes");
     if (M > 0 && !scale) return fail(OQ_ERR_INVALID_ARG, "oq_quant_act: scale is NULL");
@@ -271,12 +288,26 @@ int oq_gemm_w4a4(int afmt, const uint8_t *qa, int64_t lda_bytes, const void *a_s
                  const float *bias, uint16_t *y, int64_t ldy, void *ws, size_t ws_bytes, hipStream_t stream) {
   (void)ws;
   (void)ws_bytes;
+  if (afmt == (OQ_MXFP4 | OQ_TILED)) {
+    int rc = check_gemm_common("oq_gemm_w4a4", qa, 16, M, K, w, w_scale, N, y, ldy, 0);
+    if (rc) return rc;
+    if (K % 128) return fail(OQ_ERR_UNSUPPORTED, "oq_gemm_w4a4: tiled MXFP4 needs K %% 128 == 0 (K=%d)", K);
+    if (group != 32) return fail(OQ_ERR_INVALID_ARG, "oq_gemm_w4a4: MXFP4 blocks are 32 (group=%d)", group);
+    if (mean || w1) return fail(OQ_ERR_UNSUPPORTED, "oq_gemm_w4a4: rank-1 restore is not defined for MXFP4 here");
+    if (M > 0 && N > 0 && !a_scale) return fail(OQ_ERR_INVALID_ARG, "oq_gemm_w4a4: a_scale is NULL");
+    if ((reinterpret_cast<uintptr_t>(a_scale) | reinterpret_cast<uintptr_t>(w_scale)) & 3)
+      return fail(OQ_ERR_ALIGNMENT, "oq_gemm_w4a4: tiled E8M0 scale words must be 4-byte aligned");
+    g_err[0] = 0;
+    return hip_status(launch_gemm_mx(1, qa, 0, (const uint8_t *)a_scale, M, K, w, (const uint8_t *)w_scale, N, bias,
+                                     y, ldy, stream),
+                      "oq_gemm_w4a4");
+  }
   if (afmt & OQ_TILED) {
     const int base_fmt = afmt & ~OQ_TILED;
     int rc = check_gemm_common("oq_gemm_w4a4", qa, 16, M, K, w, w_scale, N, y, ldy, 0);
     if (rc) return rc;
     if (base_fmt != OQ_A4 && base_fmt != OQ_A6)
-      return fail(OQ_ERR_UNSUPPORTED, "oq_gemm_w4a4: tiled operands exist for OQ_A4 and OQ_A6");
+      return fail(OQ_ERR_UNSUPPORTED, "oq_gemm_w4a4: tiled operands exist for OQ_A4, OQ_A6 and OQ_MXFP4");
     if (group != 64) return fail(OQ_ERR_UNSUPPORTED, "oq_gemm_w4a4: tiled GEMM needs group 64 (got %d)", group);
     rc = check_int_epilogue("oq_gemm_w4a4", K, group, mean, w1);
     if (rc) return rc;
@@ -293,7 +324,7 @@ int oq_gemm_w4a4(int afmt, const uint8_t *qa, int64_t lda_bytes, const void *a_s
     if (group != 32) return fail(OQ_ERR_INVALID_ARG, "oq_gemm_w4a4: MXFP4 blocks are 32 (group=%d)", group);
     if (mean || w1) return fail(OQ_ERR_UNSUPPORTED, "oq_gemm_w4a4: rank-1 restore is not defined for MXFP4 here");
     g_err[0] = 0;
-    return hip_status(launch_gemm_mx(qa, lda_bytes, (const uint8_t *)a_scale, M, K, w, (const uint8_t *)w_scale, N,
+    return hip_status(launch_gemm_mx(0, qa, lda_bytes, (const uint8_t *)a_scale, M, K, w, (const uint8_t *)w_scale, N,
                                      bias, y, ldy, stream),
                       "oq_gemm_w4a4");
   }
@@ -322,6 +353,22 @@ int oq_prepack_w4(const uint8_t *w, const float *w_scale, int32_t N, int32_t K, 
   return hip_status(launch_prepack_w4(w, w_scale, N, K, w_tiled, w_scale_t, stream), "oq_prepack_w4");
 }
 
+size_t oq_tiled_mx_bytes(int64_t rows, int32_t K) {
+  if (rows < 0 || K <= 0) return 0;
+  return (size_t)tiled_mx_bytes(rows, K);
+}
+
+int oq_prepack_mx(const uint8_t *w, const uint8_t *w_e8m0, int32_t N, int32_t K, uint8_t *w_tiled,
+                  uint8_t *w_e8m0_tiled, hipStream_t stream) {
+  if (N < 0) return fail(OQ_ERR_INVALID_ARG, "oq_prepack_mx: N < 0");
+  if (K <= 0 || K % 128) return fail(OQ_ERR_UNSUPPORTED, "oq_prepack_mx: K=%d must be a positive multiple of 128", K);
+  if (N > 0 && (!w || !w_e8m0 || !w_tiled || !w_e8m0_tiled)) return fail(OQ_ERR_INVALID_ARG, "oq_prepack_mx: NULL pointer");
+  if (!al16(w) || !al16(w_tiled) || (reinterpret_cast<uintptr_t>(w_e8m0_tiled) & 3))
+    return fail(OQ_ERR_ALIGNMENT, "oq_prepack_mx: misaligned");
+  g_err[0] = 0;
+  return hip_status(launch_prepack_mx(w, w_e8m0, N, K, w_tiled, w_e8m0_tiled, stream), "oq_prepack_mx");
+}
+
 size_t oq_workspace_bytes(int op, int64_t M, int32_t K, int32_t N, int afmt) {
   (void)N;
   if (op != OQ_OP_LINEAR || M < 0 || K <= 0) return 0;
@@ -334,10 +381,33 @@ int oq_linear_fused(const uint16_t *x, int64_t M, int32_t K, int64_t ldx, const 
   const char *fn = "oq_linear_fused";
   int rc = check_x(fn, x, M, K, ldx);
   if (rc) return rc;
+  if (afmt == (OQ_MXFP4 | OQ_TILED)) {
+    if (!rot || rot->kind != OQ_ROT_DENSE32) return fail(OQ_ERR_UNSUPPORTED, "%s: MXFP4 needs a DENSE32 rotation", fn);
+    if (center || w1) return fail(OQ_ERR_UNSUPPORTED, "%s: centering is not defined for MXFP4 here", fn);
+    if (group != 32) return fail(OQ_ERR_INVALID_ARG, "%s: MXFP4 blocks are 32 (group=%d)", fn, group);
+    if (K % 128) return fail(OQ_ERR_UNSUPPORTED, "%s: tiled MXFP4 needs K %% 128 == 0", fn);
+    const LinearWs L = linear_ws(M, K, afmt);
+    if (M > 0 && (!ws || ws_bytes < L.total))
+      return fail(OQ_ERR_WORKSPACE, "%s: workspace of %zu bytes required (got %zu)", fn, L.total, ws_bytes);
+    if (ws && !al16(ws)) return fail(OQ_ERR_ALIGNMENT, "%s: workspace must be 16-byte aligned", fn);
+    rc = check_gemm_common(fn, x, 16, M, K, w, w_scale, N, y, ldy, 0);
+    if (rc) return rc;
+    if (reinterpret_cast<uintptr_t>(w_scale) & 3)
+      return fail(OQ_ERR_ALIGNMENT, "%s: tiled E8M0 scale words must be 4-byte aligned", fn);
+    rc = check_dense(fn, rot, K, false);
+    if (rc) return rc;
+    char *wsb = static_cast<char *>(ws);
+    uint8_t *codes = reinterpret_cast<uint8_t *>(wsb + L.codes);
+    uint8_t *e8 = reinterpret_cast<uint8_t *>(wsb + L.scale);
+    g_err[0] = 0;
+    rc = hip_status(launch_dense32(x, M, K, ldx, rot->mats, 2, codes, 0, e8, stream), fn);
+    if (rc) return rc;
+    return hip_status(launch_gemm_mx(1, codes, 0, e8, M, K, w, (const uint8_t *)w_scale, N, bias, y, ldy, stream), fn);
+  }
   if (afmt & OQ_TILED) {
     const int base_fmt = afmt & ~OQ_TILED;
     if (base_fmt != OQ_A4 && base_fmt != OQ_A6)
-      return fail(OQ_ERR_UNSUPPORTED, "%s: tiled operands exist for OQ_A4 and OQ_A6", fn);
+      return fail(OQ_ERR_UNSUPPORTED, "%s: tiled operands exist for OQ_A4, OQ_A6 and OQ_MXFP4", fn);
     if (K % 64) return fail(OQ_ERR_UNSUPPORTED, "%s: tiled operands need K %% 64 == 0", fn);
     if (group != 64) return fail(OQ_ERR_UNSUPPORTED, "%s: tiled GEMM needs group 64 (got %d)", fn, group);
     const LinearWs L = linear_ws(M, K, afmt);
@@ -383,7 +453,7 @@ int oq_linear_fused(const uint16_t *x, int64_t M, int32_t K, int64_t ldx, const 
     g_err[0] = 0;
     rc = hip_status(launch_dense32(x, M, K, ldx, rot->mats, 1, codes, L.ldc, e8, stream), fn);
     if (rc) return rc;
-    return hip_status(launch_gemm_mx(codes, L.ldc, e8, M, K, w, (const uint8_t *)w_scale, N, bias, y, ldy, stream), fn);
+    return hip_status(launch_gemm_mx(0, codes, L.ldc, e8, M, K, w, (const uint8_t *)w_scale, N, bias, y, ldy, stream), fn);
   }
   rc = check_int_epilogue(fn, K, group, center ? w1 : nullptr, center ? w1 : nullptr);
   if (rc) return rc;

@@ -101,6 +101,109 @@ dense32_kernel(const void *__restrict__ xin, int64_t M, int d, int64_t ldx, cons
   }
 }
 
+
+// Activation path (bf16 in, MXFP4 out), one workgroup per 32-block b and 512
+// tokens; lane = token, two tokens per lane (t and t + 64 within its wave's
+// 128).  T_b is widened to float64 and stored transposed in LDS, the lanes'
+// inputs go to LDS as float32 ([j][token][thread], conflict-free); then for
+// each input j every lane accumulates x_j times column j of T into its 2 x 32
+// float64 sums (broadcast 16-byte LDS reads, each feeding four FMAs).  Every
+// output is summed over j in order with one rounding per FMA; the sum is exact
+// for these operands (bf16 x bf16 products), so v = RN32(T_b x_b) as above.
+// Elements are converted with v_cvt_scalef32_pk_fp4_f32 on v * 2^-e (exact
+// power-of-two scaling): round to nearest E2M1 value, ties to the even code,
+// saturating, sign kept (checked against the rule above on the device).
+// TILED writes the MFMA-tiled MXFP4 layout (see include/oq.h), else row-major
+// codes [M][ldc] and E8M0 bytes [M][d/32].
+constexpr int MXK_TOK = 512;  // tokens per workgroup
+
+template <bool TILED>
+__global__ void __launch_bounds__(256)
+dense32_mx_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, const uint16_t *__restrict__ mats,
+                  uint8_t *__restrict__ codes, int64_t ldc, uint8_t *__restrict__ e8m0) {
+  __shared__ __attribute__((aligned(16))) double Tt[32 * 32];  // Tt[j][i] = T[i][j]
+  __shared__ float xs[32][2][256];                              // xs[j][u][thread]
+  const int b = blockIdx.y;
+  const int nb = d / 32;
+  for (int e = threadIdx.x; e < 1024; e += 256)
+    Tt[(e & 31) * 32 + (e >> 5)] = (double)__uint_as_float((uint32_t)mats[(int64_t)b * 1024 + e] << 16);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t t0 = (int64_t)blockIdx.x * MXK_TOK + wave * 128 + lane;
+  const int64_t tk[2] = {t0, t0 + 64};
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const bool ok = tk[u] < M;
+    const uint4 *src = reinterpret_cast<const uint4 *>(x + (ok ? tk[u] : 0) * ldx + b * 32);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint4 p = ok ? src[k] : make_uint4(0u, 0u, 0u, 0u);
+      const uint32_t wd[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        xs[8 * k + 2 * q][u][threadIdx.x] = bf16_lo(wd[q]);
+        xs[8 * k + 2 * q + 1][u][threadIdx.x] = bf16_hi(wd[q]);
+      }
+    }
+  }
+  __syncthreads();
+  double acc[2][32];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int i = 0; i < 32; ++i) acc[u][i] = 0.0;
+#pragma unroll 2
+  for (int j = 0; j < 32; ++j) {
+    const double x0 = (double)xs[j][0][threadIdx.x];
+    const double x1 = (double)xs[j][1][threadIdx.x];
+    const double2 *tcol = reinterpret_cast<const double2 *>(&Tt[j * 32]);
+#pragma unroll
+    for (int i = 0; i < 32; i += 2) {
+      const double2 tp = tcol[i / 2];
+      acc[0][i] = __builtin_fma(tp.x, x0, acc[0][i]);
+      acc[1][i] = __builtin_fma(tp.x, x1, acc[1][i]);
+      acc[0][i + 1] = __builtin_fma(tp.y, x0, acc[0][i + 1]);
+      acc[1][i + 1] = __builtin_fma(tp.y, x1, acc[1][i + 1]);
+    }
+  }
+  float v[2][32];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[u][i] = (float)acc[u][i];
+  const int64_t Mp = (M + 31) / 32 * 32;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int64_t t = tk[u];
+    if (t >= M) continue;
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) a = fmaxf(a, fabsf(v[u][i]));
+    const int ef = (int)((__float_as_uint(a) >> 23) & 0xFF);
+    const int e = ef == 0 ? -127 : max(ef - 129, -127);
+    const float inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, a normal number for e >= -127
+    uint32_t wd[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t w = 0u;
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[u][8 * q] * inv, v[u][8 * q + 1] * inv, 1.0f, 0);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[u][8 * q + 2] * inv, v[u][8 * q + 3] * inv, 1.0f, 1);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[u][8 * q + 4] * inv, v[u][8 * q + 5] * inv, 1.0f, 2);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[u][8 * q + 6] * inv, v[u][8 * q + 7] * inv, 1.0f, 3);
+      wd[q] = w;
+    }
+    const uint8_t sb = (uint8_t)(e + 127);
+    if (TILED) {
+      const int kg = b >> 1, hf = b & 1;
+      uint8_t *tile = codes + ((t >> 5) * (d >> 6) + kg) * 1024;
+      *reinterpret_cast<uint4 *>(tile + 16 * (32 * hf + (int)(t & 31))) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+      e8m0[((int64_t)(b >> 2) * Mp + t) * 4 + (b & 3)] = sb;
+    } else {
+      *reinterpret_cast<uint4 *>(codes + t * ldc + b * 16) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+      e8m0[t * nb + b] = sb;
+    }
+  }
+}
+
 template <bool IN_F32, bool MX_OUT>
 hipError_t launch(const void *x, int64_t M, int d, int64_t ldx, const void *mats, void *out,
                   int64_t ld_out_bytes, uint8_t *e8m0, hipStream_t stream) {
@@ -116,7 +219,17 @@ hipError_t launch(const void *x, int64_t M, int d, int64_t ldx, const void *mats
 
 hipError_t launch_dense32(const uint16_t *x, int64_t M, int d, int64_t ldx, const uint16_t *mats, int mx_out,
                           void *out, int64_t ld_out_bytes, uint8_t *e8m0, hipStream_t stream) {
-  if (mx_out) return launch<false, true>(x, M, d, ldx, mats, out, ld_out_bytes, e8m0, stream);
+  if (mx_out) {
+    if (M == 0) return hipSuccess;
+    dim3 grid((unsigned)((M + MXK_TOK - 1) / MXK_TOK), (unsigned)(d / 32));
+    if (mx_out == 2)
+      hipLaunchKernelGGL(dense32_mx_kernel<true>, grid, dim3(256), 0, stream, x, M, d, ldx, mats,
+                         static_cast<uint8_t *>(out), ld_out_bytes, e8m0);
+    else
+      hipLaunchKernelGGL(dense32_mx_kernel<false>, grid, dim3(256), 0, stream, x, M, d, ldx, mats,
+                         static_cast<uint8_t *>(out), ld_out_bytes, e8m0);
+    return hipGetLastError();
+  }
   return launch<false, false>(x, M, d, ldx, mats, out, ld_out_bytes, e8m0, stream);
 }
 

@@ -117,7 +117,10 @@ struct MxCfg {
   static_assert(NSTAGE >= 2 && NSTAGE <= 4, "ring depth");
 };
 
-template <int WM, int WN, int TM, int TN, int NSTAGE>
+// TIN: operands in the MFMA-tiled MXFP4 layout (include/oq.h): every copy
+// unit is then one contiguous KiB of codes or 256 bytes of scale words;
+// otherwise row-major codes and E8M0 bytes, each unit gathering 32 rows.
+template <int WM, int WN, int TM, int TN, int NSTAGE, bool TIN>
 __global__ void __launch_bounds__(64 * WM * WN)
 gemm_mx_tiled_kernel(const uint8_t *__restrict__ qa, int64_t lda, const uint8_t *__restrict__ ea, int64_t M, int K,
                      const uint8_t *__restrict__ w, const uint8_t *__restrict__ ew, int N,
@@ -131,6 +134,9 @@ gemm_mx_tiled_kernel(const uint8_t *__restrict__ qa, int64_t lda, const uint8_t 
   const int n0 = blockIdx.x * C::BN;
 
   // ---- per-lane DMA sources (stage 0) and LDS offsets of this wave's units
+  const int64_t Mp = (M + 31) / 32 * 32;
+  const int Np = (N + 31) / 32 * 32;
+  const int G = K / 64;
   const uint8_t *src16[C::P16];
   int off16[C::P16];
 #pragma unroll
@@ -139,38 +145,55 @@ gemm_mx_tiled_kernel(const uint8_t *__restrict__ qa, int64_t lda, const uint8_t 
     const int r = lane & 31, hf = lane >> 5;
     if (u < C::A_BYTES / 1024) {
       const int blk = u >> 1, kk = u & 1;
-      int64_t row = m0 + 32 * blk + r;
-      if (row > M - 1) row = M - 1;
-      src16[q] = qa + row * lda + 32 * kk + 16 * hf;
+      if (TIN) {
+        int64_t rb = m0 / 32 + blk;
+        if (rb > Mp / 32 - 1) rb = Mp / 32 - 1;
+        src16[q] = qa + (rb * G + kk) * 1024 + 16 * lane;
+      } else {
+        int64_t row = m0 + 32 * blk + r;
+        if (row > M - 1) row = M - 1;
+        src16[q] = qa + row * lda + 32 * kk + 16 * hf;
+      }
     } else {
       const int v = u - C::A_BYTES / 1024;
       const int blk = v >> 1, kk = v & 1;
-      int row = n0 + 32 * blk + r;
-      if (row > N - 1) row = N - 1;
-      src16[q] = w + (int64_t)row * (K / 2) + 32 * kk + 16 * hf;
+      if (TIN) {
+        int cb = n0 / 32 + blk;
+        if (cb > Np / 32 - 1) cb = Np / 32 - 1;
+        src16[q] = w + ((int64_t)cb * G + kk) * 1024 + 16 * lane;
+      } else {
+        int row = n0 + 32 * blk + r;
+        if (row > N - 1) row = N - 1;
+        src16[q] = w + (int64_t)row * (K / 2) + 32 * kk + 16 * hf;
+      }
     }
     off16[q] = u * 1024;
   }
   const uint8_t *src4[C::P4];
   int off4[C::P4];
+  int64_t inc4[C::P4];
 #pragma unroll
   for (int q = 0; q < C::P4; ++q) {
     const int u = wave + q * C::WAVES;
     off4[q] = -1;
     src4[q] = ea;
+    inc4[q] = 4;
     if (u < C::SA_BYTES / 256) {
       int64_t row = m0 + 64 * u + lane;
-      if (row > M - 1) row = M - 1;
-      src4[q] = ea + row * KB;
+      if (row > (TIN ? Mp : M) - 1) row = (TIN ? Mp : M) - 1;
+      src4[q] = TIN ? ea + row * 4 : ea + row * KB;
+      inc4[q] = TIN ? Mp * 4 : 4;
       off4[q] = C::A_BYTES + C::B_BYTES + u * 256;
     } else if (u < C::U4) {
       const int v = u - C::SA_BYTES / 256;
       int row = n0 + 64 * v + lane;
-      if (row > N - 1) row = N - 1;
-      src4[q] = ew + (int64_t)row * KB;
+      if (row > (TIN ? Np : N) - 1) row = (TIN ? Np : N) - 1;
+      src4[q] = TIN ? ew + (int64_t)row * 4 : ew + (int64_t)row * KB;
+      inc4[q] = TIN ? (int64_t)Np * 4 : 4;
       off4[q] = C::A_BYTES + C::B_BYTES + C::SA_BYTES + v * 256;
     }
   }
+  const int64_t inc16 = TIN ? 2048 : 64;  // bytes of codes per stage of 128 k
   // number of DMA instructions this wave issues per stage
   const int n4 = (C::U4 - wave + C::WAVES - 1) / C::WAVES;
   const int per_stage = C::P16 + n4;
@@ -193,10 +216,10 @@ gemm_mx_tiled_kernel(const uint8_t *__restrict__ qa, int64_t lda, const uint8_t 
   auto issue = [&](auto jc, int ks) {
     const uint32_t base = lds_addr_of(slot(jc));
 #pragma unroll
-    for (int q = 0; q < C::P16; ++q) dma_lds16(src16[q] + (int64_t)ks * 64, base + off16[q]);
+    for (int q = 0; q < C::P16; ++q) dma_lds16(src16[q] + (int64_t)ks * inc16, base + off16[q]);
 #pragma unroll
     for (int q = 0; q < C::P4; ++q)
-      if (off4[q] >= 0) dma_lds4(src4[q] + (int64_t)ks * 4, base + off4[q]);
+      if (off4[q] >= 0) dma_lds4(src4[q] + (int64_t)ks * inc4[q], base + off4[q]);
   };
 
   const int wm = wave / WN, wn = wave % WN;
@@ -320,36 +343,78 @@ gemm_mx_tiled_kernel(const uint8_t *__restrict__ qa, int64_t lda, const uint8_t 
 }
 
 template <int WM, int WN, int TM, int TN, int NSTAGE>
-hipError_t launch_mx_tiled(const uint8_t *qa, int64_t lda, const uint8_t *ea, int64_t M, int K, const uint8_t *w,
-                           const uint8_t *ew, int N, const float *bias, uint16_t *y, int64_t ldy,
+hipError_t launch_mx_tiled(bool tin, const uint8_t *qa, int64_t lda, const uint8_t *ea, int64_t M, int K,
+                           const uint8_t *w, const uint8_t *ew, int N, const float *bias, uint16_t *y, int64_t ldy,
                            hipStream_t stream) {
   using C = MxCfg<WM, WN, TM, TN, NSTAGE>;
   dim3 grid((unsigned)((N + C::BN - 1) / C::BN), (unsigned)((M + C::BM - 1) / C::BM));
-  hipLaunchKernelGGL((gemm_mx_tiled_kernel<WM, WN, TM, TN, NSTAGE>), grid, dim3(64 * C::WAVES), 0, stream, qa, lda,
-                     ea, M, K, w, ew, N, bias, y, ldy);
+  if (tin)
+    hipLaunchKernelGGL((gemm_mx_tiled_kernel<WM, WN, TM, TN, NSTAGE, true>), grid, dim3(64 * C::WAVES), 0, stream,
+                       qa, lda, ea, M, K, w, ew, N, bias, y, ldy);
+  else
+    hipLaunchKernelGGL((gemm_mx_tiled_kernel<WM, WN, TM, TN, NSTAGE, false>), grid, dim3(64 * C::WAVES), 0, stream,
+                       qa, lda, ea, M, K, w, ew, N, bias, y, ldy);
   return hipGetLastError();
+}
+
+// canonical MXFP4 weights (codes [N][K/2], E8M0 [N][K/32]) -> tiled layout:
+// one thread per (row < Np, k-group, half): 16 code bytes, plus the four scale
+// bytes of a 128-wide k-slice from the thread of its first k-group and half 0.
+// Rows N..Np-1 get zero codes and unit scales.
+__global__ void prepack_mx_kernel(const uint8_t *__restrict__ w, const uint8_t *__restrict__ ew, int N, int Np, int K,
+                                  uint8_t *__restrict__ out, uint8_t *__restrict__ out_s) {
+  const int G = K / 64;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)Np * G * 2) return;
+  const int half = (int)(idx & 1);
+  const int64_t rg = idx >> 1;
+  const int kg = (int)(rg % G);
+  const int row = (int)(rg / G);
+  uint4 c = make_uint4(0u, 0u, 0u, 0u);
+  if (row < N) c = *reinterpret_cast<const uint4 *>(w + (int64_t)row * (K / 2) + kg * 32 + half * 16);
+  *reinterpret_cast<uint4 *>(out + ((int64_t)(row / 32) * G + kg) * 1024 + 16 * (32 * half + row % 32)) = c;
+  if (half == 0 && (kg & 1) == 0) {
+    uint32_t sw = 0x7F7F7F7Fu;
+    if (row < N) {
+      const uint8_t *sp = ew + (int64_t)row * (K / 32) + 2 * kg;
+      sw = (uint32_t)sp[0] | ((uint32_t)sp[1] << 8) | ((uint32_t)sp[2] << 16) | ((uint32_t)sp[3] << 24);
+    }
+    *reinterpret_cast<uint32_t *>(out_s + ((int64_t)(kg / 2) * Np + row) * 4) = sw;
+  }
 }
 
 }  // namespace
 
-hipError_t launch_gemm_mx(const uint8_t *qa, int64_t lda_bytes, const uint8_t *a_e8m0, int64_t M, int K,
-                          const uint8_t *w, const uint8_t *w_e8m0, int N, const float *bias, uint16_t *y,
+hipError_t launch_gemm_mx(int tiled_in, const uint8_t *qa, int64_t lda_bytes, const uint8_t *a_e8m0, int64_t M,
+                          int K, const uint8_t *w, const uint8_t *w_e8m0, int N, const float *bias, uint16_t *y,
                           int64_t ldy, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   // the staged kernel copies the four E8M0 bytes of a 128-wide k-slice as one
-  // 32-bit word and the codes in 16-byte pieces
-  const bool tiled = K % 128 == 0 && lda_bytes % 16 == 0 && ((reinterpret_cast<uintptr_t>(qa) | reinterpret_cast<uintptr_t>(w)) & 15) == 0 &&
-                     ((reinterpret_cast<uintptr_t>(a_e8m0) | reinterpret_cast<uintptr_t>(w_e8m0)) & 3) == 0;
-  if (tiled) {
+  // 32-bit word and the codes in 16-byte pieces (tiled operands always qualify)
+  const bool staged = tiled_in || (K % 128 == 0 && lda_bytes % 16 == 0 &&
+                                   ((reinterpret_cast<uintptr_t>(qa) | reinterpret_cast<uintptr_t>(w)) & 15) == 0 &&
+                                   ((reinterpret_cast<uintptr_t>(a_e8m0) | reinterpret_cast<uintptr_t>(w_e8m0)) & 3) == 0);
+  if (staged) {
 #ifndef MX_CFG
-    return launch_mx_tiled<2, 4, 4, 2, 3>(qa, lda_bytes, a_e8m0, M, K, w, w_e8m0, N, bias, y, ldy, stream);
+    return launch_mx_tiled<2, 4, 4, 2, 3>(tiled_in != 0, qa, lda_bytes, a_e8m0, M, K, w, w_e8m0, N, bias, y, ldy,
+                                          stream);
 #else
-    return launch_mx_tiled<MX_CFG>(qa, lda_bytes, a_e8m0, M, K, w, w_e8m0, N, bias, y, ldy, stream);
+    return launch_mx_tiled<MX_CFG>(tiled_in != 0, qa, lda_bytes, a_e8m0, M, K, w, w_e8m0, N, bias, y, ldy, stream);
 #endif
   }
   dim3 grid((unsigned)((N + 127) / 128), (unsigned)((M + 127) / 128));
   hipLaunchKernelGGL(gemm_mx_kernel, grid, dim3(256), 0, stream, qa, lda_bytes, a_e8m0, M, K, w, w_e8m0, N,
                      bias, y, ldy);
+  return hipGetLastError();
+}
+
+hipError_t launch_prepack_mx(const uint8_t *w, const uint8_t *w_e8m0, int N, int K, uint8_t *out, uint8_t *out_s,
+                             hipStream_t stream) {
+  if (N == 0) return hipSuccess;
+  const int Np = (N + 31) / 32 * 32;
+  const int64_t total = (int64_t)Np * (K / 64) * 2;
+  hipLaunchKernelGGL(prepack_mx_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, w, w_e8m0, N, Np,
+                     K, out, out_s);
   return hipGetLastError();
 }
 

@@ -90,7 +90,8 @@ hipError_t launch_rpbh_wave(const uint16_t *x, int64_t M, int d, int64_t ldx, co
                             float *mean, int mode, int qmax, void *out, int64_t ld_out_bytes, float *scale,
                             hipStream_t stream);
 
-// K2: dense per-32 transform -> (MXFP4 quantize | float32 out).
+// K2: dense per-32 transform -> (MXFP4 quantize | float32 out); mx_out: 0 float32,
+// 1 row-major codes + E8M0, 2 tiled MXFP4 layout.
 hipError_t launch_dense32(const uint16_t *x, int64_t M, int d, int64_t ldx,
                           const uint16_t *mats, int mx_out, void *out, int64_t ld_out_bytes,
                           uint8_t *e8m0, hipStream_t stream);
@@ -110,10 +111,16 @@ hipError_t launch_gemm_fp6(const uint8_t *A, int planes, const float *a_scale, i
 hipError_t launch_prepack_w4(const uint8_t *w, const float *ws, int N, int K, uint8_t *out, float *out_s,
                              hipStream_t stream);
 
-// K5: MXFP4 x MXFP4 with E8M0 block scales (scaled FP4 MFMA).
-hipError_t launch_gemm_mx(const uint8_t *qa, int64_t lda_bytes, const uint8_t *a_e8m0,
+// K5: MXFP4 x MXFP4 with E8M0 block scales (scaled FP4 MFMA); tiled_in: both
+// operands in the tiled MXFP4 layout (codes + scale words), else row-major.
+hipError_t launch_gemm_mx(int tiled_in, const uint8_t *qa, int64_t lda_bytes, const uint8_t *a_e8m0,
                           int64_t M, int K, const uint8_t *w, const uint8_t *w_e8m0, int N,
                           const float *bias, uint16_t *y, int64_t ldy, hipStream_t stream);
+hipError_t launch_prepack_mx(const uint8_t *w, const uint8_t *w_e8m0, int N, int K, uint8_t *out, uint8_t *out_s,
+                             hipStream_t stream);
+// bytes of the tiled MXFP4 codes of `rows` rows (rows padded to 32); the
+// scale words take a sixteenth of that
+inline int64_t tiled_mx_bytes(int64_t rows, int K) { return (rows + 31) / 32 * 32 * (int64_t)(K / 2); }
 
 // Offline weight preparation.
 hipError_t launch_weight_rpbh(const float *w, int N, int K, int64_t ldw, const RotArgs &rot,

@@ -2,7 +2,7 @@
 definition (CPU only)."""
 import numpy as np
 
-from tiling import e2m3, row_mask, split_a6, tile
+from tiling import e2m3, row_mask, row_mask_mx, split_a6, tile, tile_mx
 
 
 def _decode_e2m3(f):
@@ -43,3 +43,21 @@ def test_a6_split():
     qh, ql = split_a6(q)
     np.testing.assert_array_equal(8 * qh + ql, q)
     assert qh.min() >= -4 and qh.max() <= 3 and ql.min() >= 0 and ql.max() <= 7
+
+
+def test_tile_mx_placement():
+    R, K = 40, 256
+    codes = np.zeros((R, K // 2), dtype=np.uint8)
+    e8 = np.full((R, K // 32), 127, dtype=np.uint8)
+    codes[33, 80] = 0xA5        # row 33 (block 1, r 1), k = 160..161: kg 2, half 1, byte 0 of its 16
+    e8[33, 5] = 130             # block 5 -> k-slice 1, byte 1
+    t, s = tile_mx(codes, e8)
+    G, Rp = K // 64, 64
+    assert t.size == Rp * K // 2 and s.size == Rp * K // 32
+    off = (1 * G + 2) * 1024 + 16 * (32 * 1 + 1)
+    assert t[off] == 0xA5 and int(t.sum()) == 0xA5
+    assert s[(1 * Rp + 33) * 4 + 1] == 130
+    assert np.count_nonzero(s != 127) == 1
+    m = row_mask_mx(R, K).reshape(Rp // 32, G, 2, 32, 16)
+    assert m[1, :, :, 7].all() and not m[1, :, :, 8].any()
+

@@ -67,3 +67,34 @@ def split_a6(q):
     q = np.asarray(q, dtype=np.int64)
     qh = np.floor_divide(q, 8)
     return qh, q - 8 * qh
+
+
+def tile_mx(codes: np.ndarray, e8m0: np.ndarray):
+    """Row-major MXFP4 codes [R, K/2] (two E2M1 codes per byte) and E8M0 bytes
+    [R, K/32] -> (tiled codes, tiled scale words) as defined in include/oq.h:
+    tile (r/32, kg) of 1024 bytes holds at 16 (32 h + r % 32) the 16 code bytes
+    of row r, k-half h; the scale word of (k-slice s, row r) sits at byte
+    (s * Rp + r) * 4 with the E8M0 bytes of blocks 4s..4s+3.  Padding rows get
+    zero codes and scale 127."""
+    R, Kh = codes.shape
+    K = 2 * Kh
+    assert K % 128 == 0 and e8m0.shape == (R, K // 32)
+    Rp = (R + 31) // 32 * 32
+    G = K // 64
+    c = np.zeros((Rp, Kh), dtype=np.uint8)
+    c[:R] = codes
+    e = np.full((Rp, K // 32), 127, dtype=np.uint8)
+    e[:R] = e8m0
+    t = c.reshape(Rp // 32, 32, G, 2, 16).transpose(0, 2, 3, 1, 4)   # [rb, kg, h, r, 16]
+    tiled = np.ascontiguousarray(t).reshape(-1)
+    sc = e.reshape(Rp, K // 128, 4).transpose(1, 0, 2)               # [s, r, 4]
+    return tiled, np.ascontiguousarray(sc).reshape(-1)
+
+
+def row_mask_mx(R: int, K: int) -> np.ndarray:
+    """Boolean mask over the tiled MXFP4 code bytes of R rows: True for rows < R."""
+    Rp = (R + 31) // 32 * 32
+    G = K // 64
+    live = (np.arange(Rp) < R).reshape(Rp // 32, 1, 1, 32, 1)
+    return np.broadcast_to(live, (Rp // 32, G, 2, 32, 16)).reshape(-1)
+
