@@ -227,7 +227,8 @@ def _gpu_state():
 def _act_bytes(spec, M, K):
     if spec.afmt == 0x104:
         return M * K * 2 + M * K // 2 + M * K // 32
-    code = M * K if spec.afmt in (8, 6) else M * K // 2
+    # densely packed codes: 8, 6 or 4 bits each
+    code = {8: M * K, 6: M * K * 3 // 4}.get(spec.afmt, M * K // 2)
     return M * K * 2 + code + 4 * M + (4 * M if spec.center else 0)
 
 
