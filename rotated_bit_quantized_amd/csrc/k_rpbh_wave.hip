@@ -14,10 +14,17 @@
 //     sign-flipped twins, no conversion on the write side); centering
 //     subtracts s_i m after the gather, which equals s_i RN32(x - m);
 //     a second round gathers float32 copies of the first round's outputs;
-//   * butterfly stages of stride 1..8 run in registers, strides 16..h/2
-//     exchange between lanes (DPP for lane distance 1 and 2, ds_swizzle for
-//     4, 8, 16, ds_bpermute for 32), each output rounded once:
-//     low lane a + b, high lane a - b (an fma with +-1);
+//   * butterfly stages of stride 1..8 run in registers; strides 16..h/2
+//     pair lanes.  Those stages keep each value up to a per-lane sign:
+//     every lane adds c times its partner's value (c = -1 on the lane whose
+//     index bit is set), which yields a + b on the low lane and -(a - b) on
+//     the high lane, each rounded once; the sign the high lanes pick up is a
+//     fixed pattern, applied when the values are used.  As an accumulate of
+//     a DPP operand this is one v_fmac_f32_dpp per value for lane distances
+//     1, 2 (quad_perm), and for the half-row and row mirrors, which pair
+//     lane l with l ^ 7 and l ^ 15: lanes are renumbered so that those
+//     pairings flip exactly one index bit (index_lane below).  Distances 16
+//     and 32 use ds_swizzle and ds_bpermute;
 //   * when h is a power of 4, 1/sqrt(h) is a power of two: the per-round
 //     multiply is exact and is deferred into the quantization scale
 //     (identical codes and scales; the float32 output mode applies it);
@@ -52,8 +59,44 @@ __device__ __forceinline__ double wave_sum_d(double v) {
   return v;
 }
 
+// Index lane of physical lane `lane` when a Hadamard block spans 2^n lanes.
+// Lane-bit stage k flips index bit k and pairs lanes differing by p_k, with
+// p = (1, 2, 7, 15) for k < 4 (the DPP patterns) and 2^k above; the physical
+// lane is the GF(2) sum of b_k p_k over the index bits b_k, inverted here.
+// Bits above the block are unchanged.
+__device__ __forceinline__ int index_lane(int lane, int n) {
+  const int l0 = lane & 1, l1 = (lane >> 1) & 1, l2 = (lane >> 2) & 1, l3 = (lane >> 3) & 1;
+  if (n <= 2) return lane;
+  if (n == 3) return (lane & ~7) | (l2 << 2) | ((l1 ^ l2) << 1) | (l0 ^ l2);
+  return (lane & ~15) | (l3 << 3) | ((l2 ^ l3) << 2) | ((l1 ^ l2) << 1) | (l0 ^ l2);
+}
+
+// v[j] += c * v[j] of the partner lane, 16 values, partner by DPP pattern.
+// The s_nop covers the wait states a DPP read needs after a VALU write of
+// its source (and after a VALU write of EXEC).
+#define OQ_FMAC_DPP(i, CTRL) "v_fmac_f32_dpp %" #i ", %" #i ", %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"
+#define OQ_FMAC_DPP16(CTRL)                                                                                   \
+  "s_nop 4\n\t" OQ_FMAC_DPP(0, CTRL) OQ_FMAC_DPP(1, CTRL) OQ_FMAC_DPP(2, CTRL) OQ_FMAC_DPP(3, CTRL)           \
+      OQ_FMAC_DPP(4, CTRL) OQ_FMAC_DPP(5, CTRL) OQ_FMAC_DPP(6, CTRL) OQ_FMAC_DPP(7, CTRL) OQ_FMAC_DPP(8, CTRL) \
+          OQ_FMAC_DPP(9, CTRL) OQ_FMAC_DPP(10, CTRL) OQ_FMAC_DPP(11, CTRL) OQ_FMAC_DPP(12, CTRL)             \
+              OQ_FMAC_DPP(13, CTRL) OQ_FMAC_DPP(14, CTRL) OQ_FMAC_DPP(15, CTRL)
+#define OQ_V16_OPERANDS(v)                                                                                   \
+  "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]), "+v"(v[8]), \
+      "+v"(v[9]), "+v"(v[10]), "+v"(v[11]), "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15])
+
+template <int K>
+__device__ __forceinline__ void dpp_stage(float (&v)[16], float c) {
+  if constexpr (K == 0) asm(OQ_FMAC_DPP16("quad_perm:[1,0,3,2]") : OQ_V16_OPERANDS(v) : "v"(c));
+  if constexpr (K == 1) asm(OQ_FMAC_DPP16("quad_perm:[2,3,0,1]") : OQ_V16_OPERANDS(v) : "v"(c));
+  if constexpr (K == 2) asm(OQ_FMAC_DPP16("row_half_mirror") : OQ_V16_OPERANDS(v) : "v"(c));
+  if constexpr (K == 3) asm(OQ_FMAC_DPP16("row_mirror") : OQ_V16_OPERANDS(v) : "v"(c));
+}
+
+// Un-normalised FWHT of each 2^(n+4)-coordinate block; stage order strides
+// 1, 2, ..., as in the oracle.  c[k] = -1 where index-lane bit k is set.
+// On return lane values carry the sign (-1)^popcount(index lane mod 2^n).
 template <int SLOTS>
-__device__ __forceinline__ void fwht_row(float (&v)[SLOTS][16], int lane, int nl) {
+__device__ __forceinline__ void fwht_row(float (&v)[SLOTS][16], int n, const float (&c)[6]) {
 #pragma unroll
   for (int s = 0; s < SLOTS; ++s)
 #pragma unroll
@@ -65,16 +108,28 @@ __device__ __forceinline__ void fwht_row(float (&v)[SLOTS][16], int lane, int nl
           v[s][j] = a + b;
           v[s][j + st] = a - b;
         }
+  if (n > 0)
 #pragma unroll
-  for (int lg = 0; lg < 6; ++lg) {
-    const int mm = 1 << lg;
-    if (mm >= nl) break;
-    const float sg = (lane & mm) ? -1.0f : 1.0f;
+    for (int s = 0; s < SLOTS; ++s) dpp_stage<0>(v[s], c[0]);
+  if (n > 1)
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) dpp_stage<1>(v[s], c[1]);
+  if (n > 2)
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) dpp_stage<2>(v[s], c[2]);
+  if (n > 3)
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) dpp_stage<3>(v[s], c[3]);
+  if (n > 4)
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) v[s][j] = __builtin_fmaf(v[s][j], sg, xlane(v[s][j], lg));
-  }
+      for (int j = 0; j < 16; ++j) v[s][j] = __builtin_fmaf(xlane(v[s][j], 4), c[4], v[s][j]);
+  if (n > 5)
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[s][j] = __builtin_fmaf(xlane(v[s][j], 5), c[5], v[s][j]);
 }
 
 // Stores the 16 codes of two slots (a: coordinates base..base+15, b: the same
@@ -138,11 +193,13 @@ struct WaveLds {
   static constexpr int TOTAL = TABLE + WAVES_PER_WG * ROWBUF;
 };
 
-template <int SLOTS, int ROUNDS>
+// mode (OUT_*) is a template argument: one kernel body per output keeps the
+// register count of each near what its own path needs.
+template <int SLOTS, int ROUNDS, int mode>
 __global__ void __launch_bounds__(64 * WAVES_PER_WG)
 rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, const int32_t *__restrict__ perm,
                  const int8_t *__restrict__ signs, int h, float c_h, int pow4, int center,
-                 float *__restrict__ mean_out, int mode, int qmax, void *__restrict__ out, int64_t ld_out_bytes,
+                 float *__restrict__ mean_out, int qmax, void *__restrict__ out, int64_t ld_out_bytes,
                  float *__restrict__ scale_out) {
   using L = WaveLds<SLOTS, ROUNDS>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
@@ -150,29 +207,48 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
   const int wave = threadIdx.x >> 6;
   int *table = reinterpret_cast<int *>(lds_raw);
   uint8_t *buf = lds_raw + L::TABLE + wave * L::ROWBUF;
-  const int nl = h >> 4;  // lanes per Hadamard block
+  const int nlog = __builtin_ctz((unsigned)h) - 4;  // a Hadamard block spans 2^nlog lanes
+  const int il = index_lane(lane, nlog);             // this lane holds coordinates 16 il + j of each slot
+
+  // act: this lane's coordinates of slot s exist (index lane); ld: its
+  // physical 16-coordinate chunk of the row exists (loads, first-round copies)
+  bool act[SLOTS], ld[SLOTS];
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s) {
+    act[s] = 1024 * s + 16 * il < d;
+    ld[s] = 1024 * s + 16 * lane < d;
+  }
+  const float c_all = (ROUNDS == 0 || !pow4) ? 1.0f : (ROUNDS == 2 ? c_h * c_h : c_h);  // deferred, exact
+  float cst[6];
+#pragma unroll
+  for (int k = 0; k < 6; ++k) cst[k] = ((il >> k) & 1) ? -1.0f : 1.0f;
+  // sign the lane-bit stages leave on this lane's values
+  const float sg = (__builtin_popcount(il & ((1 << nlog) - 1)) & 1) ? -1.0f : 1.0f;
+  const int neg_from = 2 * d;  // first-round byte offsets at or above this hit the -x copy
 
   // ---- offset table: byte offsets into this wave's [+row | -row] buffer;
-  // first-round copies are bf16 (2 bytes), second-round copies float32
-  for (int t = threadIdx.x; t < (ROUNDS > 0 ? ROUNDS : 0) * SLOTS * 1024; t += 64 * WAVES_PER_WG) {
-    const int r = t / (SLOTS * 1024);
-    const int rem = t % (SLOTS * 1024);
-    const int s = rem / 1024, l = (rem / 16) % 64, j = rem % 16;
-    const int i = 1024 * s + 16 * l + j;
-    int o = 0;
-    if (i < d) {
-      const int src = perm[(int64_t)r * d + i] + (signs[(int64_t)r * d + i] < 0 ? d : 0);
-      o = src * (r == 0 ? 2 : 4);
-    }
-    table[(((r * SLOTS + s) * 4 + (j >> 2)) * 64 + l) * 4 + (j & 3)] = o;
-  }
-  __syncthreads();
-
-  bool act[SLOTS];
+  // first-round copies are bf16 (2 bytes), second-round copies float32.
+  // Entry (r, s, lane l, j) is coordinate 1024 s + 16 index_lane(l) + j;
+  // each task fills 4 consecutive j.  All its loads are issued before the
+  // first row's, so the table is built while that row is in flight.
+  constexpr int TASKS = (ROUNDS > 0 ? ROUNDS : 0) * SLOTS * 256;
+  constexpr int NT = (TASKS + 64 * WAVES_PER_WG - 1) / (64 * WAVES_PER_WG);
+  int pv[NT > 0 ? NT : 1][4], sv[NT > 0 ? NT : 1][4];
 #pragma unroll
-  for (int s = 0; s < SLOTS; ++s) act[s] = 1024 * s + 16 * lane < d;
-  const float c_all = (ROUNDS == 0 || !pow4) ? 1.0f : (ROUNDS == 2 ? c_h * c_h : c_h);  // deferred, exact
-  const int neg_from = 2 * d;  // first-round byte offsets at or above this hit the -x copy
+  for (int k = 0; k < NT; ++k) {
+    const int q = threadIdx.x + k * 64 * WAVES_PER_WG;
+    const int r = q / (SLOTS * 256), rem = q % (SLOTS * 256);
+    const int s = rem / 256, l = (rem / 4) % 64, j0 = 4 * (rem % 4);
+    const int i0 = 1024 * s + 16 * index_lane(l, nlog) + j0;
+    // unconditional loads (index 0 for entries that do not exist, which the
+    // table step below zeroes) so that none waits for another
+    const int64_t b = (q < TASKS && i0 < d) ? (int64_t)r * d + i0 : 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      pv[k][e] = perm[b + e];
+      sv[k][e] = signs[b + e];
+    }
+  }
 
   const int64_t step = (int64_t)gridDim.x * WAVES_PER_WG;
   // the next row's words are loaded while the current row is processed (the
@@ -183,13 +259,29 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
     const uint16_t *xr = x + (rr < M ? rr : M - 1) * ldx;
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s) {
-      const uint4 *src = reinterpret_cast<const uint4 *>(xr + (act[s] ? 1024 * s + 16 * lane : 0));
+      const uint4 *src = reinterpret_cast<const uint4 *>(xr + (ld[s] ? 1024 * s + 16 * lane : 0));
       nxt[s][0] = src[0];
       nxt[s][1] = src[1];
     }
   };
   int64_t row = (int64_t)blockIdx.x * WAVES_PER_WG + wave;
-  if (row < M) load_row(row);
+  load_row(row);  // unconditional (clamped index): the table's waits then leave it in flight
+
+#pragma unroll
+  for (int k = 0; k < NT; ++k) {
+    const int q = threadIdx.x + k * 64 * WAVES_PER_WG;
+    if (q >= TASKS) continue;
+    const int r = q / (SLOTS * 256), rem = q % (SLOTS * 256);
+    const int s = rem / 256, l = (rem / 4) % 64, jq = rem % 4;
+    const int i0 = 1024 * s + 16 * index_lane(l, nlog) + 4 * jq;
+    int o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      o[e] = i0 < d ? (pv[k][e] + (sv[k][e] < 0 ? d : 0)) * (r == 0 ? 2 : 4) : 0;
+    reinterpret_cast<int4 *>(table)[((r * SLOTS + s) * 4 + jq) * 64 + l] = make_int4(o[0], o[1], o[2], o[3]);
+  }
+  __syncthreads();
+
   for (; row < M; row += step) {
     float v[SLOTS][16];
     uint4 raw[SLOTS][2];
@@ -209,22 +301,22 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
                                raw[s][1].x, raw[s][1].y, raw[s][1].z, raw[s][1].w};
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-          if (act[s]) sum += (double)bf16_lo(w[k]) + (double)bf16_hi(w[k]);
+          if (ld[s]) sum += (double)bf16_lo(w[k]) + (double)bf16_hi(w[k]);
       }
       sum = wave_sum_d(sum);
       m = (float)(sum / (double)d);
       if (lane == 0) mean_out[row] = m;
     }
 
-    if (ROUNDS == 0) {
+    if (ROUNDS == 0) {  // no lane stages: il == lane
 #pragma unroll
       for (int s = 0; s < SLOTS; ++s) {
         const uint32_t w[8] = {raw[s][0].x, raw[s][0].y, raw[s][0].z, raw[s][0].w,
                                raw[s][1].x, raw[s][1].y, raw[s][1].z, raw[s][1].w};
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          v[s][2 * k] = act[s] ? bf16_lo(w[k]) - m : 0.f;
-          v[s][2 * k + 1] = act[s] ? bf16_hi(w[k]) - m : 0.f;
+          v[s][2 * k] = ld[s] ? bf16_lo(w[k]) - m : 0.f;
+          v[s][2 * k + 1] = ld[s] ? bf16_hi(w[k]) - m : 0.f;
         }
       }
     }
@@ -233,7 +325,7 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
       // first-round writer: bf16 +row and -row at natural coordinates
 #pragma unroll
       for (int s = 0; s < SLOTS; ++s) {
-        if (!act[s]) continue;
+        if (!ld[s]) continue;
         const int p0 = 1024 * s + 16 * lane;
         uint4 *dp = reinterpret_cast<uint4 *>(buf + 2 * p0);
         uint4 *dn = reinterpret_cast<uint4 *>(buf + 2 * (p0 + d));
@@ -245,7 +337,9 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
         }
       }
       // gather (the wave's own LDS writes are ordered before its reads);
-      // centering: s x - s m = s RN32(x - m), one rounding
+      // centering: s x - s m = s RN32(x - m), one rounding.  Lanes past the
+      // row end read word 0: their blocks are never stored and are left out
+      // of the range
 #pragma unroll
       for (int s = 0; s < SLOTS; ++s) {
         const int4 *tb = reinterpret_cast<const int4 *>(table) + (s * 4) * 64 + lane;
@@ -257,11 +351,11 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
           for (int e = 0; e < 4; ++e) {
             const float g = __uint_as_float((uint32_t)(*reinterpret_cast<const uint16_t *>(buf + oo[e])) << 16);
             const float mm = oo[e] >= neg_from ? -m : m;
-            v[s][4 * k + e] = act[s] ? (center ? g - mm : g) : 0.f;
+            v[s][4 * k + e] = center ? g - mm : g;
           }
         }
       }
-      fwht_row<SLOTS>(v, lane, nl);
+      fwht_row<SLOTS>(v, nlog, cst);
       if (!pow4) {
 #pragma unroll
         for (int s = 0; s < SLOTS; ++s)
@@ -271,13 +365,14 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
     }
 
     if (ROUNDS == 2) {
-      // second-round writer: float32 +row and -row
+      // second-round writer: float32 +row and -row; the lane's values are
+      // sg times the first round's outputs, so sg picks the copy they go to
 #pragma unroll
       for (int s = 0; s < SLOTS; ++s) {
         if (!act[s]) continue;
-        const int p0 = 1024 * s + 16 * lane;
-        float4 *dp = reinterpret_cast<float4 *>(buf + 4 * p0);
-        float4 *dn = reinterpret_cast<float4 *>(buf + 4 * (p0 + d));
+        const int p0 = 1024 * s + 16 * il;
+        float4 *dp = reinterpret_cast<float4 *>(buf + 4 * (sg > 0.f ? p0 : p0 + d));
+        float4 *dn = reinterpret_cast<float4 *>(buf + 4 * (sg > 0.f ? p0 + d : p0));
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           dp[k] = make_float4(v[s][4 * k], v[s][4 * k + 1], v[s][4 * k + 2], v[s][4 * k + 3]);
@@ -292,10 +387,10 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
           const int4 o4 = tb[k * 64];
           const int oo[4] = {o4.x, o4.y, o4.z, o4.w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[s][4 * k + e] = act[s] ? *reinterpret_cast<const float *>(buf + oo[e]) : 0.f;
+          for (int e = 0; e < 4; ++e) v[s][4 * k + e] = *reinterpret_cast<const float *>(buf + oo[e]);
         }
       }
-      fwht_row<SLOTS>(v, lane, nl);
+      fwht_row<SLOTS>(v, nlog, cst);
       if (!pow4) {
 #pragma unroll
         for (int s = 0; s < SLOTS; ++s)
@@ -305,29 +400,32 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
     }
 
     if (mode == OUT_F32) {
+      const float co = c_all * sg;  // exact: both are powers of two up to sign
 #pragma unroll
       for (int s = 0; s < SLOTS; ++s) {
         if (!act[s] || !out) continue;
-        float4 *dst = reinterpret_cast<float4 *>(static_cast<char *>(out) + row * ld_out_bytes) + (1024 * s + 16 * lane) / 4;
+        float4 *dst = reinterpret_cast<float4 *>(static_cast<char *>(out) + row * ld_out_bytes) + (1024 * s + 16 * il) / 4;
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          dst[k] = make_float4(v[s][4 * k] * c_all, v[s][4 * k + 1] * c_all, v[s][4 * k + 2] * c_all,
-                               v[s][4 * k + 3] * c_all);
+          dst[k] = make_float4(v[s][4 * k] * co, v[s][4 * k + 1] * co, v[s][4 * k + 2] * co, v[s][4 * k + 3] * co);
       }
       continue;
     }
 
     float a = 0.f;
 #pragma unroll
-    for (int s = 0; s < SLOTS; ++s)
+    for (int s = 0; s < SLOTS; ++s) {
+      float as = 0.f;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) a = fmaxf(a, fabsf(v[s][j]));  // inactive slots hold 0
+      for (int j = 0; j < 16; ++j) as = fmaxf(as, fabsf(v[s][j]));
+      if (act[s]) a = fmaxf(a, as);
+    }
 #pragma unroll
     for (int lg = 0; lg < 6; ++lg) a = fmaxf(a, xlane(a, lg));
     a = fmaxf(a * c_all, 1e-10f);  // c_all is a power of two: exact
     const float fq = (float)qmax;
     const float alpha = __fdiv_rn(a, fq);
-    const float inv = __fdiv_rn(fq, a) * c_all;  // exact rescale of the deferred factor
+    const float inv = __fdiv_rn(fq, a) * (c_all * sg);  // exact rescale: deferred factor and lane sign
     if (lane == 0) scale_out[row] = alpha;
 
 #pragma unroll
@@ -336,7 +434,7 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
       int q[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) q[j] = (int)fminf(fmaxf(__builtin_rintf(v[s][j] * inv), -fq), fq);
-      const int base = 1024 * s + 16 * lane;
+      const int base = 1024 * s + 16 * il;
       if (mode == OUT_I8) {
         uint32_t wd[4];
 #pragma unroll
@@ -354,9 +452,11 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
     if (mode == OUT_FP6 || mode == OUT_FP6X2) {
       // tiled layout (see k_gemm_fp6.hip): this lane's 16 codes of slot s are
       // the 96-bit string at bit 6*(base % 32) of its half of the k-group.
-      // Codes are formed as floats (integer-valued, |t| <= qmax, +0 for zero)
-      // and converted two slots at a time with v_cvt_scalef32_2xpk16_fp6_f32,
-      // which interleaves its two sources field by field.
+      // Codes are formed as floats (integer-valued, +0 for zero) and
+      // converted two slots at a time with v_cvt_scalef32_2xpk16_fp6_f32,
+      // which interleaves its two sources field by field.  No clamp: with
+      // a = max |v| and inv = RN32(qmax / a), |v inv| <= qmax (1 + 2^-24)^2,
+      // so RNE gives |t| <= qmax, as the clamp to +-qmax would.
       uint8_t *tb = static_cast<uint8_t *>(out) + ((row >> 5) * (d >> 6)) * 1536;
       const int rr = (int)(row & 31);
       const int64_t pstride = tiled_bytes(M, d);
@@ -366,29 +466,29 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
         float ta[16], tbv[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          ta[j] = __builtin_amdgcn_fmed3f(__builtin_rintf(v[s0][j] * inv), -fq, fq) + 0.0f;
-          tbv[j] = two ? __builtin_amdgcn_fmed3f(__builtin_rintf(v[two ? s0 + 1 : s0][j] * inv), -fq, fq) + 0.0f : 0.0f;
+          ta[j] = __builtin_rintf(v[s0][j] * inv) + 0.0f;
+          tbv[j] = two ? __builtin_rintf(v[two ? s0 + 1 : s0][j] * inv) + 0.0f : 0.0f;
         }
         const bool wa = act[s0], wb = two && act[two ? s0 + 1 : s0];
         if (mode == OUT_FP6) {
-          store_fp6_pair(ta, tbv, 0, tb, rr, 1024 * s0 + 16 * lane, wa, wb);
+          store_fp6_pair(ta, tbv, 0, tb, rr, 1024 * s0 + 16 * il, wa, wb);
         } else {
-          store_fp6_pair(ta, tbv, 1, tb, rr, 1024 * s0 + 16 * lane, wa, wb);
-          store_fp6_pair(ta, tbv, 2, tb + pstride, rr, 1024 * s0 + 16 * lane, wa, wb);
+          store_fp6_pair(ta, tbv, 1, tb, rr, 1024 * s0 + 16 * il, wa, wb);
+          store_fp6_pair(ta, tbv, 2, tb + pstride, rr, 1024 * s0 + 16 * il, wa, wb);
         }
       }
     }
   }
 }
 
-template <int SLOTS, int ROUNDS>
-hipError_t launch_w(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotArgs &rot, int center, float *mean,
-                    int mode, int qmax, void *out, int64_t ld_out_bytes, float *scale, hipStream_t stream) {
+template <int SLOTS, int ROUNDS, int MODE>
+hipError_t launch_m(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotArgs &rot, int center, float *mean,
+                    int qmax, void *out, int64_t ld_out_bytes, float *scale, hipStream_t stream) {
   using L = WaveLds<SLOTS, ROUNDS>;
   const size_t lds = (size_t)L::TOTAL;
   static bool attr_set = false;
   if (!attr_set && lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void *)rpbh_wave_kernel<SLOTS, ROUNDS>,
+    hipError_t e = hipFuncSetAttribute((const void *)rpbh_wave_kernel<SLOTS, ROUNDS, MODE>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
@@ -399,10 +499,23 @@ hipError_t launch_w(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotA
   if (grid < 1) grid = 1;
   const int h = ROUNDS ? rot.block : 16;
   const int pow4 = ROUNDS && ((__builtin_ctz((unsigned)h) & 1) == 0);
-  hipLaunchKernelGGL((rpbh_wave_kernel<SLOTS, ROUNDS>), dim3((unsigned)grid), dim3(64 * WAVES_PER_WG), lds, stream, x,
-                     M, d, ldx, rot.perm, rot.signs, h, rot.c_h, pow4, center, mean, mode, qmax, out, ld_out_bytes,
-                     scale);
+  hipLaunchKernelGGL((rpbh_wave_kernel<SLOTS, ROUNDS, MODE>), dim3((unsigned)grid), dim3(64 * WAVES_PER_WG), lds,
+                     stream, x, M, d, ldx, rot.perm, rot.signs, h, rot.c_h, pow4, center, mean, qmax, out,
+                     ld_out_bytes, scale);
   return hipGetLastError();
+}
+
+template <int SLOTS, int ROUNDS>
+hipError_t launch_w(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotArgs &rot, int center, float *mean,
+                    int mode, int qmax, void *out, int64_t ld_out_bytes, float *scale, hipStream_t stream) {
+  switch (mode) {
+    case OUT_F32: return launch_m<SLOTS, ROUNDS, OUT_F32>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, stream);
+    case OUT_I8: return launch_m<SLOTS, ROUNDS, OUT_I8>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, stream);
+    case OUT_I4: return launch_m<SLOTS, ROUNDS, OUT_I4>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, stream);
+    case OUT_FP6: return launch_m<SLOTS, ROUNDS, OUT_FP6>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, stream);
+    case OUT_FP6X2: return launch_m<SLOTS, ROUNDS, OUT_FP6X2>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int SLOTS>
