@@ -117,7 +117,8 @@ size_t oq_tiled_mx_bytes(int64_t rows, int32_t K);
  *   RN32(1/sqrt h).
  *
  * OQ_ROT_DENSE32 -- WUSH review "Core claim": one transform per 32-block.
- *   mats: bfloat16 [d/32][32][32] row-major, v_b = T_b x_b.  d % 32 == 0.
+ *   mats: bfloat16 [d/32][32][32] row-major, v_b = T_b x_b, 16-byte aligned.
+ *   d % 32 == 0.
  *   For weights (oq_quant_weight) mats_w is used instead: float32
  *   [d/32][32][32], the inverse-transposes T_b^{-T}.
  *   Activation-side float32 results are the exact value of T_b x_b rounded

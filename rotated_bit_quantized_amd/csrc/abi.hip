@@ -80,6 +80,8 @@ int check_dense(const char *fn, const oq_rot *rot, int d, bool weights) {
   if (rot->d != d) return fail(OQ_ERR_INVALID_ARG, "%s: rot->d=%d differs from d=%d", fn, rot->d, d);
   if (d % 32) return fail(OQ_ERR_INVALID_ARG, "%s: d=%d must be a multiple of 32", fn, d);
   if (weights ? !rot->mats_w : !rot->mats) return fail(OQ_ERR_INVALID_ARG, "%s: transform matrices are NULL", fn);
+  if (!weights && (reinterpret_cast<uintptr_t>(rot->mats) & 15))
+    return fail(OQ_ERR_ALIGNMENT, "%s: rot->mats must be 16-byte aligned", fn);
   return OQ_OK;
 }
 

@@ -7,14 +7,14 @@
 //   e = clamp(floor(log2 amax) - 2, -127, 127), element = nearest E2M1 value
 //   of v * 2^-e with ties to the even code, saturating at 6, sign kept.
 //
-// Exactness: the transform is accumulated in float64 and rounded once to
-// float32.  For the activation side (bf16 x bf16 products) the float64 sum is
-// exact for ordinary data, so v = RN32(T_b x_b).
-//
-// Layout: lanes are tokens (rows); one wavefront covers 64 rows and a run of
-// blocks.  The block's matrix is staged in LDS as float64 and read as a
-// broadcast, each lane keeps its 32 inputs and 32 accumulators in registers,
-// so the per-block absmax needs no cross-lane traffic.
+// Two kernels.  dense32_kernel (float32 rotated output for oq_rotate, and the
+// weight side) accumulates the transform in float64 and rounds once to
+// float32; for bf16 x bf16 products the float64 sum is exact for ordinary
+// data, so v = RN32(T_b x_b).  Lanes are rows there; the block's matrix is
+// staged in LDS as float64 and read as a broadcast.
+// dense32_mx_mfma_kernel (the activation MXFP4 path) forms the products on the
+// matrix cores and falls back to the same exact float64 sum wherever the
+// float32 accumulation could change a code or a block exponent (below).
 #include "oq_internal.h"
 
 #pragma clang fp contract(off)
@@ -102,105 +102,295 @@ dense32_kernel(const void *__restrict__ xin, int64_t M, int d, int64_t ldx, cons
 }
 
 
-// Activation path (bf16 in, MXFP4 out), one workgroup per 32-block b and 512
-// tokens; lane = token, two tokens per lane (t and t + 64 within its wave's
-// 128).  T_b is widened to float64 and stored transposed in LDS, the lanes'
-// inputs go to LDS as float32 ([j][token][thread], conflict-free); then for
-// each input j every lane accumulates x_j times column j of T into its 2 x 32
-// float64 sums (broadcast 16-byte LDS reads, each feeding four FMAs).  Every
-// output is summed over j in order with one rounding per FMA; the sum is exact
-// for these operands (bf16 x bf16 products), so v = RN32(T_b x_b) as above.
-// Elements are converted with v_cvt_scalef32_pk_fp4_f32 on v * 2^-e (exact
-// power-of-two scaling): round to nearest E2M1 value, ties to the even code,
+// Activation path (bf16 in, MXFP4 out) on the matrix cores.  For block b and
+// 32 tokens, D = T_b X_b^T by two v_mfma_f32_32x32x16_bf16 over the 32
+// inputs: lane l holds token l % 32 and outputs i = 8 (r / 4) + 4 (l / 32)
+// + r % 4 in accumulator registers r = 0..15.  A second product
+// |T_b| |X_b|^T gives s_i = sum_j |T_ij x_j| (sign bits cleared).
+//
+// The matrix cores add in float32, so their S'_i may differ from the value the
+// codes are defined on, v_i = RN32(sum_j T_ij x_j) (exact products, one
+// rounding).  Float32 accumulation of 32 products and an accumulator, with up
+// to one ulp per addition (truncation allowed), is off by at most
+// 34 * 2^-23 s_i; flushed subnormal products add at most 2^-120.  With the
+// RN32 step, s' >= s (1 - 2^-17) and the roundings of S' -+ D below,
+// D = 2^-17 max_i s'_i + 2^-119 bounds |v_i - S'_i| for every output of the
+// block.  An element's code is taken from S' when the codes of S'_i - D and
+// S'_i + D agree (E2M1 rounding is monotone), the block exponent when the
+// exponents of a' - D and a' + D agree (a' = max |S'|); otherwise the value is
+// recomputed exactly from the bf16 operands in LDS (float64 sum of the exact
+// products in input order, rounded once, as in the float32 path above) and the
+// code, or the whole block, is redone from exact values.
+//
+// Codes come from v_cvt_scalef32_pk_fp4_f32 with scale 2^e, which divides by
+// it (exact for a power of two): nearest E2M1 value, ties to the even code,
 // saturating, sign kept (checked against the rule above on the device).
+// A workgroup covers 4 consecutive blocks (T_b and |T_b| staged in LDS) and
+// MXM_TOK tokens, 4 waves of MXM_TPW tiles of 32 tokens; each token's x
+// words for the 4 blocks (256 contiguous bytes) are loaded one tile ahead.
 // TILED writes the MFMA-tiled MXFP4 layout (see include/oq.h), else row-major
 // codes [M][ldc] and E8M0 bytes [M][d/32].
-constexpr int MXK_TOK = 512;  // tokens per workgroup
+constexpr int MXM_NBG = 4;                     // 32-blocks per workgroup
+constexpr int MXM_TPW = 4;                     // 32-token tiles per wave
+constexpr int MXM_TOK = 4 * MXM_TPW * 32;      // tokens per workgroup
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) {
+  bf16x8_t r;
+  __builtin_memcpy(&r, &u, 16);
+  return r;
+}
+
+// unbiased E8M0 exponent of a block whose largest magnitude is a >= 0
+__device__ __forceinline__ int mx_exponent(float a) {
+  const int ef = (int)((__float_as_uint(a) >> 23) & 0xFF);
+  return ef == 0 ? -127 : max(ef - 129, -127);
+}
+
+// (value in lane l % 32, value in lane l % 32 + 32), in every lane
+__device__ __forceinline__ void half_pair(uint32_t v, uint32_t &lo, uint32_t &hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  lo = r[0];
+  hi = r[1];
+}
+
+__device__ __forceinline__ float max_halves(float v) {
+  uint32_t a, b;
+  half_pair(__float_as_uint(v), a, b);
+  return fmaxf(__uint_as_float(a), __uint_as_float(b));
+}
+
+// codes of y[r] / sc for this lane's 16 outputs; word k nibble n is r = 8k + n
+__device__ __forceinline__ void pack16(const float (&y)[16], float sc, uint32_t (&w)[2]) {
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    uint32_t o = 0u;
+    o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, y[8 * k], y[8 * k + 1], sc, 0);
+    o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, y[8 * k + 2], y[8 * k + 3], sc, 1);
+    o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, y[8 * k + 4], y[8 * k + 5], sc, 2);
+    o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, y[8 * k + 6], y[8 * k + 7], sc, 3);
+    w[k] = o;
+  }
+}
 
 template <bool TILED>
-__global__ void __launch_bounds__(256)
-dense32_mx_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, const uint16_t *__restrict__ mats,
-                  uint8_t *__restrict__ codes, int64_t ldc, uint8_t *__restrict__ e8m0) {
-  __shared__ __attribute__((aligned(16))) double Tt[32 * 32];  // Tt[j][i] = T[i][j]
-  __shared__ float xs[32][2][256];                              // xs[j][u][thread]
-  const int b = blockIdx.y;
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+dense32_mx_mfma_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx,
+                       const uint16_t *__restrict__ mats, uint8_t *__restrict__ codes, int64_t ldc,
+                       uint8_t *__restrict__ e8m0) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ts[2][MXM_NBG * 1024];  // [0] T_b, [1] |T_b|, row-major
+  __shared__ float Vs[4][16 * 64];                                         // per wave: values [r][lane]
   const int nb = d / 32;
-  for (int e = threadIdx.x; e < 1024; e += 256)
-    Tt[(e & 31) * 32 + (e >> 5)] = (double)__uint_as_float((uint32_t)mats[(int64_t)b * 1024 + e] << 16);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t t0 = (int64_t)blockIdx.x * MXK_TOK + wave * 128 + lane;
-  const int64_t tk[2] = {t0, t0 + 64};
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const bool ok = tk[u] < M;
-    const uint4 *src = reinterpret_cast<const uint4 *>(x + (ok ? tk[u] : 0) * ldx + b * 32);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint4 p = ok ? src[k] : make_uint4(0u, 0u, 0u, 0u);
-      const uint32_t wd[4] = {p.x, p.y, p.z, p.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        xs[8 * k + 2 * q][u][threadIdx.x] = bf16_lo(wd[q]);
-        xs[8 * k + 2 * q + 1][u][threadIdx.x] = bf16_hi(wd[q]);
-      }
-    }
+  const int b0 = blockIdx.y * MXM_NBG;
+  const int nbw = min(MXM_NBG, nb - b0);
+  for (int q = threadIdx.x; q < nbw * 128; q += 256) {
+    const uint4 w = reinterpret_cast<const uint4 *>(mats + (int64_t)b0 * 1024)[q];
+    reinterpret_cast<uint4 *>(Ts[0])[q] = w;
+    reinterpret_cast<uint4 *>(Ts[1])[q] =
+        make_uint4(w.x & 0x7FFF7FFFu, w.y & 0x7FFF7FFFu, w.z & 0x7FFF7FFFu, w.w & 0x7FFF7FFFu);
   }
   __syncthreads();
-  double acc[2][32];
-#pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int i = 0; i < 32; ++i) acc[u][i] = 0.0;
-#pragma unroll 2
-  for (int j = 0; j < 32; ++j) {
-    const double x0 = (double)xs[j][0][threadIdx.x];
-    const double x1 = (double)xs[j][1][threadIdx.x];
-    const double2 *tcol = reinterpret_cast<const double2 *>(&Tt[j * 32]);
-#pragma unroll
-    for (int i = 0; i < 32; i += 2) {
-      const double2 tp = tcol[i / 2];
-      acc[0][i] = __builtin_fma(tp.x, x0, acc[0][i]);
-      acc[1][i] = __builtin_fma(tp.x, x1, acc[1][i]);
-      acc[0][i + 1] = __builtin_fma(tp.y, x0, acc[0][i + 1]);
-      acc[1][i + 1] = __builtin_fma(tp.y, x1, acc[1][i + 1]);
-    }
-  }
-  float v[2][32];
-#pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int i = 0; i < 32; ++i) v[u][i] = (float)acc[u][i];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = lane >> 5, tl = lane & 31;
   const int64_t Mp = (M + 31) / 32 * 32;
+  float *vs = Vs[wave];
+
+  // x words of one tile: [block][k-step] = inputs 16 s + 8 h .. + 7 of token tl.
+  // Two buffers swap roles from tile to tile (no copy between them, so the
+  // compiler's wait for a tile's words never covers the next tile's loads).
+  uint4 xA[MXM_NBG][2], xB[MXM_NBG][2];
+  auto load_x = [&](int tile, uint4 (&dst)[MXM_NBG][2]) {
+    int64_t t = (int64_t)blockIdx.x * MXM_TOK + tile * 32 + tl;
+    if (t >= M) t = M - 1;  // rows past the end read the last row; nothing of theirs is stored
+    const uint16_t *xr = x + t * ldx + b0 * 32 + 8 * h;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int64_t t = tk[u];
-    if (t >= M) continue;
-    float a = 0.f;
+    for (int b = 0; b < MXM_NBG; ++b) {
+      const int bb = b < nbw ? b : nbw - 1;  // a short last group reloads its last block
 #pragma unroll
-    for (int i = 0; i < 32; ++i) a = fmaxf(a, fabsf(v[u][i]));
-    const int ef = (int)((__float_as_uint(a) >> 23) & 0xFF);
-    const int e = ef == 0 ? -127 : max(ef - 129, -127);
-    const float inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, a normal number for e >= -127
-    uint32_t wd[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint32_t w = 0u;
-      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[u][8 * q] * inv, v[u][8 * q + 1] * inv, 1.0f, 0);
-      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[u][8 * q + 2] * inv, v[u][8 * q + 3] * inv, 1.0f, 1);
-      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[u][8 * q + 4] * inv, v[u][8 * q + 5] * inv, 1.0f, 2);
-      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[u][8 * q + 6] * inv, v[u][8 * q + 7] * inv, 1.0f, 3);
-      wd[q] = w;
+      for (int s = 0; s < 2; ++s) dst[b][s] = *reinterpret_cast<const uint4 *>(xr + bb * 32 + 16 * s);
     }
-    const uint8_t sb = (uint8_t)(e + 127);
-    if (TILED) {
-      const int kg = b >> 1, hf = b & 1;
-      uint8_t *tile = codes + ((t >> 5) * (d >> 6) + kg) * 1024;
-      *reinterpret_cast<uint4 *>(tile + 16 * (32 * hf + (int)(t & 31))) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-      e8m0[((int64_t)(b >> 2) * Mp + t) * 4 + (b & 3)] = sb;
-    } else {
-      *reinterpret_cast<uint4 *>(codes + t * ldc + b * 16) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-      e8m0[t * nb + b] = sb;
+  };
+  // one tile: prefetch the next tile's words into xn, process xa; false when
+  // the tile lies past the last token
+  auto tile = [&](int tt, uint4 (&xa)[MXM_NBG][2], uint4 (&xn)[MXM_NBG][2]) -> bool {
+    const int64_t tbase = (int64_t)blockIdx.x * MXM_TOK + (wave + 4 * tt) * 32;
+    if (tbase >= M) return false;
+    if (tt + 1 < MXM_TPW) load_x(wave + 4 * (tt + 1), xn);
+    const int64_t t = tbase + tl;
+    const bool valid = t < M;
+    uint32_t scw = 0u;  // E8M0 bytes of the group's blocks (tiled layout stores them as one word)
+
+    // the products of block b + 1 are issued before block b is quantized
+    f32x16_t acc[2], sig[2];
+    auto products = [&](int b, f32x16_t &ac, f32x16_t &sg) {
+      ac = f32x16_t{};
+      sg = f32x16_t{};
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int off = b * 1024 + tl * 32 + 16 * s + 8 * h;  // A: T_b[i = tl][j = 16 s + 8 h + e]
+        const uint4 ta = *reinterpret_cast<const uint4 *>(&Ts[0][off]);
+        const uint4 tb = *reinterpret_cast<const uint4 *>(&Ts[1][off]);
+        const uint4 xv = xa[b][s];
+        const uint4 xb = make_uint4(xv.x & 0x7FFF7FFFu, xv.y & 0x7FFF7FFFu, xv.z & 0x7FFF7FFFu, xv.w & 0x7FFF7FFFu);
+        ac = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ta), as_bf16x8(xv), ac, 0, 0, 0);
+        sg = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(tb), as_bf16x8(xb), sg, 0, 0, 0);
+      }
+    };
+    products(0, acc[0], sig[0]);
+
+#pragma unroll
+    for (int b = 0; b < MXM_NBG; ++b) {
+      if (b >= nbw) break;
+      if (b + 1 < nbw) products(b + 1, acc[(b + 1) & 1], sig[(b + 1) & 1]);
+      const int bg = b0 + b;
+      const f32x16_t &ac = acc[b & 1];
+      float am = 0.f, sm = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        am = fmaxf(am, fabsf(ac[r]));
+        sm = fmaxf(sm, sig[b & 1][r]);
+      }
+      am = max_halves(am);
+      sm = max_halves(sm);
+      const float da = __builtin_fmaf(sm, 0x1p-17f, 0x1p-119f);
+      int e = mx_exponent(am);
+      // tiny blocks (e < -100, e.g. all zero) always take the exact path
+      const bool blk = e < -100 || mx_exponent(fmaxf(am - da, 0.f)) != mx_exponent(am + da);
+      float sc = __uint_as_float((uint32_t)(127 + max(e, -126)) << 23);  // 2^e, normal
+      // codes of S' - D and S' + D; word k nibble n is register r = 8 k + n
+      uint32_t wl[2], wh[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int r = 8 * k;
+        uint32_t ol = 0u, oh = 0u;
+        ol = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(ol, ac[r] - da, ac[r + 1] - da, sc, 0);
+        oh = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(oh, ac[r] + da, ac[r + 1] + da, sc, 0);
+        ol = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(ol, ac[r + 2] - da, ac[r + 3] - da, sc, 1);
+        oh = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(oh, ac[r + 2] + da, ac[r + 3] + da, sc, 1);
+        ol = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(ol, ac[r + 4] - da, ac[r + 5] - da, sc, 2);
+        oh = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(oh, ac[r + 4] + da, ac[r + 5] + da, sc, 2);
+        ol = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(ol, ac[r + 6] - da, ac[r + 7] - da, sc, 3);
+        oh = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(oh, ac[r + 6] + da, ac[r + 7] + da, sc, 3);
+        wl[k] = ol;
+        wh[k] = oh;
+      }
+      const uint32_t d0 = wl[0] ^ wh[0], d1 = wl[1] ^ wh[1];
+      const bool need = valid && (blk || (d0 | d1) != 0u);
+      if (__ballot(need) != 0ull) {
+        // all 32 inputs of the token: this lane's half and its partner's
+        uint4 xin[4];  // inputs 8 q .. 8 q + 7
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const uint4 o = xa[b][s];
+          const uint32_t ow[4] = {o.x, o.y, o.z, o.w};
+          uint32_t pw[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            uint32_t lw, hw;
+            half_pair(ow[k], lw, hw);
+            pw[k] = h ? lw : hw;
+          }
+          const uint4 p = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+          xin[2 * s] = h ? p : o;
+          xin[2 * s + 1] = h ? o : p;
+        }
+        // exact value of output r of this lane's token: float64 sum of the
+        // exact products in input order, rounded once
+        auto exact = [&](int r) -> float {
+          const int i = 8 * (r >> 2) + 4 * h + (r & 3);
+          const uint4 *trow = reinterpret_cast<const uint4 *>(&Ts[0][b * 1024 + i * 32]);
+          double s64 = 0.0;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint4 tw = trow[q];
+            const uint32_t tws[4] = {tw.x, tw.y, tw.z, tw.w};
+            const uint32_t xws[4] = {xin[q].x, xin[q].y, xin[q].z, xin[q].w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              s64 = __builtin_fma((double)bf16_lo(tws[k]), (double)bf16_lo(xws[k]), s64);
+              s64 = __builtin_fma((double)bf16_hi(tws[k]), (double)bf16_hi(xws[k]), s64);
+            }
+          }
+          return (float)s64;
+        };
+        // certain exponent: redo the outputs whose two codes differ and
+        // patch their nibbles
+        const bool el = valid && !blk;
+#pragma unroll 1
+        for (int r = 0; r < 16; ++r) {
+          const bool f = el && (((r < 8 ? d0 : d1) >> (4 * (r & 7))) & 0xFu) != 0u;
+          if (__ballot(f) == 0ull) continue;
+          if (f) {
+            const float ve = exact(r);
+            const uint32_t c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, ve, ve, sc, 0) & 0xFu;
+            const int sh = 4 * (r & 7);
+            if (r < 8)
+              wl[0] = (wl[0] & ~(0xFu << sh)) | (c << sh);
+            else
+              wl[1] = (wl[1] & ~(0xFu << sh)) | (c << sh);
+          }
+        }
+        // uncertain exponent (both lanes of the token): redo all 32 outputs,
+        // take the exponent from them, recode the block
+        const bool bl = valid && blk;
+        if (__ballot(bl) != 0ull) {
+#pragma unroll 1
+          for (int r = 0; r < 16; ++r)
+            if (bl) vs[r * 64 + lane] = exact(r);
+          float ve[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) ve[r] = vs[r * 64 + lane];  // meaningful where bl
+          float ae = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) ae = fmaxf(ae, fabsf(ve[r]));
+          ae = max_halves(ae);
+          const int eb = mx_exponent(ae);
+          float mul = 1.0f, sb = __uint_as_float((uint32_t)(127 + max(eb, -126)) << 23);
+          if (eb < -126) {  // 2^-127 is not a normal scale: multiply by 2^127 (exact) instead
+            mul = 0x1p127f;
+            sb = 1.0f;
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) ve[r] *= mul;
+          uint32_t wb[2];
+          pack16(ve, sb, wb);
+          if (bl) {
+            e = eb;
+            wl[0] = wb[0];
+            wl[1] = wb[1];
+          }
+        }
+      }
+      // this lane has bytes 4 q + 2 h, 4 q + 2 h + 1 of the token's 16; the
+      // lane pair swaps halves so that lane h stores bytes 8 h .. 8 h + 7
+      uint32_t p0, p1;
+      half_pair(h ? wl[0] : wl[1], p0, p1);
+      const uint32_t rcv = h ? p0 : p1;
+      const uint2 o = h ? make_uint2((rcv & 0xFFFFu) | (wl[1] << 16), (rcv >> 16) | (wl[1] & 0xFFFF0000u))
+                        : make_uint2((wl[0] & 0xFFFFu) | (rcv << 16), (wl[0] >> 16) | (rcv & 0xFFFF0000u));
+      if (valid) {
+        if (TILED) {
+          uint8_t *tile = codes + ((t >> 5) * (d >> 6) + (bg >> 1)) * 1024;
+          *reinterpret_cast<uint2 *>(tile + 16 * (32 * (bg & 1) + tl) + 8 * h) = o;
+        } else {
+          *reinterpret_cast<uint2 *>(codes + t * ldc + bg * 16 + 8 * h) = o;
+          if (h == 0) e8m0[t * nb + bg] = (uint8_t)(e + 127);
+        }
+      }
+      scw |= (uint32_t)(e + 127) << (8 * b);
     }
+    if (TILED && valid && h == 0)  // the group is 4 aligned blocks when TILED (d % 128 == 0)
+      *reinterpret_cast<uint32_t *>(e8m0 + ((int64_t)(b0 >> 2) * Mp + t) * 4) = scw;
+    return true;
+  };
+  static_assert(MXM_TPW % 2 == 0, "tiles are taken in pairs");
+  load_x(wave, xA);
+  for (int tt = 0; tt < MXM_TPW; tt += 2) {
+    if (!tile(tt, xA, xB)) break;
+    if (!tile(tt + 1, xB, xA)) break;
   }
 }
 
@@ -221,12 +411,13 @@ hipError_t launch_dense32(const uint16_t *x, int64_t M, int d, int64_t ldx, cons
                           void *out, int64_t ld_out_bytes, uint8_t *e8m0, hipStream_t stream) {
   if (mx_out) {
     if (M == 0) return hipSuccess;
-    dim3 grid((unsigned)((M + MXK_TOK - 1) / MXK_TOK), (unsigned)(d / 32));
+    const int nb = d / 32;
+    dim3 grid((unsigned)((M + MXM_TOK - 1) / MXM_TOK), (unsigned)((nb + MXM_NBG - 1) / MXM_NBG));
     if (mx_out == 2)
-      hipLaunchKernelGGL(dense32_mx_kernel<true>, grid, dim3(256), 0, stream, x, M, d, ldx, mats,
+      hipLaunchKernelGGL(dense32_mx_mfma_kernel<true>, grid, dim3(256), 0, stream, x, M, d, ldx, mats,
                          static_cast<uint8_t *>(out), ld_out_bytes, e8m0);
     else
-      hipLaunchKernelGGL(dense32_mx_kernel<false>, grid, dim3(256), 0, stream, x, M, d, ldx, mats,
+      hipLaunchKernelGGL(dense32_mx_mfma_kernel<false>, grid, dim3(256), 0, stream, x, M, d, ldx, mats,
                          static_cast<uint8_t *>(out), ld_out_bytes, e8m0);
     return hipGetLastError();
   }

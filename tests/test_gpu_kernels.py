@@ -177,6 +177,57 @@ def test_dense32_rotate_and_mx(oq, M, K):
     check_codes(codes, ref["codes"], ref["flags"], "mx codes")
 
 
+def _boundary_case(M, K, seed):
+    """Signed-permutation transforms and inputs on E2M1 rounding midpoints,
+    grid points and powers of two, so that products are exact, many elements
+    sit exactly on a tie and many block maxima are powers of two (exponent
+    boundaries): the cases where a float32-accumulated value cannot decide
+    the code and the exact recompute must."""
+    rng = np.random.default_rng(seed)
+    nb = K // 32
+    T = np.zeros((nb, 32, 32), dtype=np.float32)
+    for b in range(nb):
+        T[b, np.arange(32), rng.permutation(32)] = rng.choice([-1.0, 1.0], size=32)
+    mags = np.array([0.0, 0.25, 0.5, 0.75, 1.0, 1.25, 1.5, 1.75, 2.0, 2.5, 3.0, 3.5, 4.0, 5.0, 6.0, 7.0, 8.0],
+                    dtype=np.float32)
+    x = rng.choice(mags, size=(M, K)) * rng.choice([-1.0, 1.0], size=(M, K))
+    x = x * np.repeat(np.exp2(rng.integers(-20, 20, size=(M, nb))), 32, axis=1)
+    return WL.f32_to_bf16_bits(x.astype(np.float32)), WL.f32_to_bf16_bits(T)
+
+
+@pytest.mark.parametrize("M,K", [(97, 256), (64, 4096)])
+def test_dense32_mx_boundaries_exact(oq, M, K):
+    say("case dense32 mx boundaries", M, K)
+    xb, tb = _boundary_case(M, K, M + K)
+    rot = oq.Rotation.dense32(to_dev(tb))
+    ref = OL.activations_mx(xb, tb)
+    for afmt in (oq.OQ_MXFP4, oq.OQ_MXFP4 | oq.OQ_TILED):
+        out = oq.oq_quant_act(to_dev(xb), rot, afmt)
+        torch.cuda.synchronize()
+        if afmt & oq.OQ_TILED:
+            Mp = (M + 31) // 32 * 32
+            sb = to_host(out["e8m0"])[:Mp * K // 32].reshape(K // 128, Mp, 4)[:, :M].transpose(1, 0, 2)
+            np.testing.assert_array_equal(sb.reshape(M, K // 32), ref["scale_bytes"])
+            continue
+        np.testing.assert_array_equal(to_host(out["e8m0"]), ref["scale_bytes"])
+        np.testing.assert_array_equal(OQ.unpack_nibbles(to_host(out["codes"])), ref["codes"])
+
+
+def test_dense32_mx_every_element(oq):
+    """1536 tokens x 4096 (6.3M elements, config-5 width): every code and
+    scale byte against the oracle."""
+    M, K = 1536, 4096
+    say("case dense32 mx every element", M, K)
+    wl = WL.make_workload(5, M=M, K=K, Ns=(16,))
+    rot = oq.Rotation.dense32(to_dev(wl.t_act_bits))
+    out = oq.oq_quant_act(to_dev(wl.x_bits), rot, oq.OQ_MXFP4)
+    torch.cuda.synchronize()
+    ref = OL.activations_mx(wl.x_bits, wl.t_act_bits)
+    np.testing.assert_array_equal(to_host(out["e8m0"]), ref["scale_bytes"])
+    n = check_codes(OQ.unpack_nibbles(to_host(out["codes"])), ref["codes"], ref["flags"], "mx codes")
+    say(f"  codes differing on exempt elements: {n}")
+
+
 def test_weight_dense32(oq):
     say("case weight dense32")
     wl = WL.make_workload(5, M=4, K=512, Ns=(48,))
