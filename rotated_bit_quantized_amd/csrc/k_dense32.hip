@@ -218,7 +218,10 @@ dense32_mx_mfma_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t
   auto tile = [&](int tt, uint4 (&xa)[MXM_NBG][2], uint4 (&xn)[MXM_NBG][2]) -> bool {
     const int64_t tbase = (int64_t)blockIdx.x * MXM_TOK + (wave + 4 * tt) * 32;
     if (tbase >= M) return false;
-    if (tt + 1 < MXM_TPW) load_x(wave + 4 * (tt + 1), xn);
+    // unconditional, so that the compiler's wait for this tile's words never
+    // merges with a path without these loads; the last tile reloads its own
+    // (cached) rows
+    load_x(wave + 4 * (tt + 1 < MXM_TPW ? tt + 1 : tt), xn);
     const int64_t t = tbase + tl;
     const bool valid = t < M;
     uint32_t scw = 0u;  // E8M0 bytes of the group's blocks (tiled layout stores them as one word)
