@@ -11,6 +11,7 @@ Sources:
   activation transform.
   OrbitQuant PR #25 "Default changes": absmax INT8 at A8; the configurations
   also use 6- and 4-bit absmax codes (Eq. 1 with b = 6, 4).
+  CentriQ Sec. 4.2 "Scale and grid": the percentile range in place of absmax.
 """
 from __future__ import annotations
 
@@ -45,15 +46,17 @@ def prepare_weight_dense32(W, t_wgt):
             "block_flags": bflag, "packed": quant.pack_nibbles(codes)}
 
 
-def activations_int(x_bits, perm, signs, block, afmt_bits, center):
-    """Online activation path: (mean) -> (center) -> RPBH -> absmax codes."""
+def activations_int(x_bits, perm, signs, block, afmt_bits, center, pctl=False):
+    """Online activation path: (mean) -> (center) -> RPBH -> absmax codes, or
+    percentile-scaled codes (CentriQ Sec. 4.2 "Scale and grid") with pctl."""
     x32 = quant.bf16_to_f32(x_bits)
     m = None
     if center:
         m = quant.token_mean(x32)
         x32 = quant.center(x32, m)
-    v = rotation.rpbh_fp32(x32, perm, signs, block)
-    q, alpha, flag = quant.quant_token_int(v, quant.qmax_for_bits(afmt_bits))
+    v = rotation.rpbh_fp32(x32, perm, signs, block) if perm is not None else x32
+    quantize = quant.quant_token_pctl if pctl else quant.quant_token_int
+    q, alpha, flag = quantize(v, quant.qmax_for_bits(afmt_bits))
     return {"mean": m, "rotated": v, "codes": q, "alpha": alpha, "flags": flag}
 
 

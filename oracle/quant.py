@@ -9,6 +9,12 @@ Sources:
   magnitude of the token.
   CentriQ Sec. 4.2 "Activation path", Eq. 4: the token is centered over its n
   native channels, x^c = x - mean(x) 1; the mean is restored as a rank-1 term.
+  CentriQ Sec. 4.2 "Activation path", "Scale and grid", and App. B.3
+  (Table 3): the percentile scale.  The token's spread is the empirical
+  rho-quantile of the rotated magnitudes divided by the half-normal quantile
+  Phi^-1((1 + rho) / 2); the range is gamma* times that spread, with
+  rho = 0.9995 and gamma* = 2.5591 fixed for all layers, and Eq. 1 then
+  clips codes beyond the range.
   FLUX.1-schnell-OrbitQuant-W4A4 model card, "Quantization": activation
   normalization epsilon 1e-10; packed INT4 module tensors ("Artifact Files").
   WUSH review, "Core claim" and Fig. 2 caption: RTN AbsMax block quantizers,
@@ -22,6 +28,13 @@ Readings where the pages are silent:
   * an all-zero token uses max(a, eps32) with eps32 = RN32(1e-10), so every
     code is 0 and the scale is eps32 / qmax;
   * the mean is m = RN32(RN64(S) / d) with S the exact coordinate sum;
+  * percentile scale: the empirical rho-quantile interpolates linearly
+    between the order statistics k = floor(rho (n - 1)) and k + 1 of the
+    magnitudes (ascending, 0-based), in float64; the range is
+    r = RN32((q * gamma*) / z) with z = Phi^-1(1 - 0.00025) (the upper tail
+    (1 - rho) / 2 taken as the decimal 0.00025), evaluated in that order in
+    float64; gamma* = 2.5591 (Table 3; the text rounds it to 2.56); the
+    scale and codes then follow the absmax rule with r in place of a;
   * INT4 packing: element 2i in bits 3..0, element 2i+1 in bits 7..4, 4-bit
     two's complement;
   * E8M0 shared exponent e = clamp(floor(log2 a) - 2, -127, 127) (the MX
@@ -111,6 +124,51 @@ def quant_token_int(v32: np.ndarray, qmax: int):
     v32 = np.asarray(v32, dtype=np.float32)
     a = np.max(np.abs(v32), axis=-1)
     alpha, inv = absmax_scale(a, qmax)
+    q, flag = round_codes(v32, inv[..., None], qmax)
+    return q, alpha, flag
+
+
+PCTL_RHO = 0.9995
+PCTL_GAMMA = 2.5591
+PCTL_TAIL = 0.00025  # (1 - rho) / 2
+
+
+def std_normal_upper_quantile(tail: float) -> float:
+    """x with Phi(-x) = tail, i.e. Phi^-1(1 - tail): bisection on
+    erfc(x / sqrt 2) / 2 = tail (the upper tail keeps full float64 precision),
+    run until the bracket cannot shrink."""
+    lo, hi = 0.0, 40.0
+    while True:
+        mid = 0.5 * (lo + hi)
+        if mid <= lo or mid >= hi:
+            break
+        if 0.5 * math.erfc(mid / math.sqrt(2.0)) > tail:
+            lo = mid
+        else:
+            hi = mid
+    return hi
+
+
+def pctl_range(v32: np.ndarray, rho: float = PCTL_RHO, gamma: float = PCTL_GAMMA) -> np.ndarray:
+    """Percentile range per token (last axis): r = RN32((q * gamma) / z), q the
+    linearly interpolated empirical rho-quantile of the magnitudes."""
+    a = np.sort(np.abs(np.asarray(v32, dtype=np.float32)).astype(np.float64), axis=-1)
+    n = a.shape[-1]
+    h = rho * (n - 1)
+    k = int(math.floor(h))
+    f = h - k
+    lo = a[..., k]
+    hi = a[..., min(k + 1, n - 1)]
+    q = lo + f * (hi - lo)
+    z = std_normal_upper_quantile(PCTL_TAIL)
+    return ((q * gamma) / z).astype(np.float32)
+
+
+def quant_token_pctl(v32: np.ndarray, qmax: int):
+    """Per-token quantizer of Eq. 1 with the percentile range (codes beyond
+    the range clip to +-qmax).  Returns (codes int32, alpha float32, flags)."""
+    v32 = np.asarray(v32, dtype=np.float32)
+    alpha, inv = absmax_scale(pctl_range(v32), qmax)
     q, flag = round_codes(v32, inv[..., None], qmax)
     return q, alpha, flag
 

@@ -136,3 +136,69 @@ def test_nibble_pack_roundtrip():
     c = np.arange(16, dtype=np.uint8)
     np.testing.assert_array_equal(Q.unpack_nibbles(Q.pack_nibbles(c[None]))[0], c)
     assert Q.pack_nibbles(np.array([[0x3, 0xC]]))[0, 0] == 0xC3
+
+
+# ---- percentile scale (CentriQ Sec. 4.2 "Scale and grid", App. B.3 Table 3)
+
+def test_normal_quantile_against_scipy():
+    stats = pytest.importorskip("scipy.stats")
+    z = Q.std_normal_upper_quantile(Q.PCTL_TAIL)
+    assert abs(z - stats.norm.isf(0.00025)) <= 2e-15 * z
+    assert abs(z - stats.norm.ppf(0.99975)) <= 1e-12 * z
+    for tail in (0.5, 0.1, 1e-3, 1e-6):
+        assert abs(Q.std_normal_upper_quantile(tail) - stats.norm.isf(tail)) <= 1e-14 * max(1.0, stats.norm.isf(tail))
+
+
+@pytest.mark.parametrize("n", [16, 100, 1920, 3072, 4096, 5000])
+def test_percentile_is_the_linear_empirical_quantile(n):
+    # numpy's "linear" method (Hyndman-Fan type 7) is an independent
+    # implementation of the same interpolated order statistic
+    rng = np.random.default_rng(n)
+    v = (rng.standard_normal((5, n)) * rng.uniform(0.1, 10, size=(5, 1))).astype(np.float32)
+    r = Q.pctl_range(v).astype(np.float64)
+    z = Q.std_normal_upper_quantile(Q.PCTL_TAIL)
+    q_np = np.quantile(np.abs(v).astype(np.float64), Q.PCTL_RHO, axis=-1, method="linear")
+    want = (q_np * Q.PCTL_GAMMA / z).astype(np.float32).astype(np.float64)
+    assert np.all(np.abs(r - want) <= np.spacing(want.astype(np.float32)).astype(np.float64))
+
+
+def test_percentile_constant_row_and_spread_of_gaussian_rows():
+    z = Q.std_normal_upper_quantile(Q.PCTL_TAIL)
+    c = np.full((1, 3072), -0.75, dtype=np.float32)
+    assert Q.pctl_range(c)[0] == np.float32(0.75 * Q.PCTL_GAMMA / z)
+    rng = np.random.default_rng(3)
+    sig = np.array([0.01, 1.0, 300.0])
+    v = (rng.standard_normal((3, 1 << 17)) * sig[:, None]).astype(np.float32)
+    sig_hat = Q.pctl_range(v).astype(np.float64) / Q.PCTL_GAMMA
+    assert np.all(np.abs(sig_hat / sig - 1) < 0.05)
+
+
+def test_gamma_star_minimizes_4bit_gaussian_error():
+    # the pages choose gamma* as the minimizer of clipping plus rounding error
+    # of a 4-bit grid for Gaussian input: it beats clips 15% tighter and wider
+    rng = np.random.default_rng(11)
+    v = rng.standard_normal((1, 1 << 21)).astype(np.float32)
+
+    def mse(gamma):
+        r = Q.pctl_range(v, gamma=gamma)
+        alpha, inv = Q.absmax_scale(r, 7)
+        q, _ = Q.round_codes(v, inv[..., None], 7)
+        return float(np.mean((alpha[..., None].astype(np.float64) * q - v) ** 2))
+
+    e0 = mse(Q.PCTL_GAMMA)
+    assert e0 < mse(0.85 * Q.PCTL_GAMMA) and e0 < mse(1.15 * Q.PCTL_GAMMA)
+
+
+@pytest.mark.parametrize("qmax", [7, 31, 127])
+def test_percentile_codes_clip_beyond_the_range(qmax):
+    rng = np.random.default_rng(qmax)
+    v = rng.standard_normal((8, 1024)).astype(np.float32)
+    v[:, 7] = 40.0  # far beyond the range: clipped
+    q, alpha, flag = Q.quant_token_pctl(v, qmax)
+    r = Q.pctl_range(v)
+    assert np.all(q[:, 7] == qmax)
+    assert np.all(np.abs(q) <= qmax)
+    assert np.allclose(alpha, r / np.float32(qmax), rtol=2 ** -23)
+    inside = np.abs(v) <= 0.9 * r[:, None]
+    err = np.abs(alpha[:, None].astype(np.float64) * q - v)
+    assert np.all(err[inside] <= 0.5 * alpha.astype(np.float64)[:, None].repeat(1024, 1)[inside] * (1 + 1e-6))
