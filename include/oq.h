@@ -93,6 +93,18 @@ enum { OQ_W4 = 4, OQ_W_MXFP4 = 0x104 };
  */
 enum { OQ_TILED = 0x10000 };
 
+/*
+ * Scale flag, OR-ed into afmt for integer activation codes (OQ_A8, OQ_A6,
+ * OQ_A4, tiled or not) in oq_quant_act and oq_linear_fused -- CentriQ Sec.
+ * 4.2 "Scale and grid" and App. B.3 Table 3: the token's range is
+ *   r = RN32((q * 2.5591) / Phi^-1(0.99975))      (evaluated in float64),
+ * q the 0.9995-quantile of the d rotated magnitudes, interpolated linearly
+ * between the order statistics floor(0.9995 (d - 1)) and the next one
+ * (ascending); then alpha = RN32(r / qmax) and codes clip to +-qmax as in
+ * Eq. 1.  Needs d % 16 == 0 and 16 <= d <= 4096; not for MXFP4.
+ */
+enum { OQ_SCALE_PCTL = 0x20000 };
+
 /* Bytes of one plane of the tiled FP6 layout for `rows` rows of width K. */
 size_t oq_tiled_bytes(int64_t rows, int32_t K);
 

@@ -23,6 +23,7 @@ OQ_A8, OQ_A6, OQ_A4, OQ_MXFP4 = 8, 6, 4, 0x104
 OQ_W4, OQ_W_MXFP4 = 4, 0x104
 OQ_OP_GEMM_W4A8, OQ_OP_GEMM_W4A4, OQ_OP_LINEAR = 1, 2, 3
 OQ_TILED = 0x10000
+OQ_SCALE_PCTL = 0x20000
 
 
 class OQError(RuntimeError):
@@ -163,26 +164,27 @@ def oq_quant_act(x, rot: Optional[Rotation], afmt: int, center: bool = False, co
     x = _bits16(x)
     M, d = x.shape
     dev = _dev(x)
-    mx_tiled = afmt == (OQ_MXFP4 | OQ_TILED)
+    fmt = afmt & ~OQ_SCALE_PCTL  # the scale flag does not change the buffers
+    mx_tiled = fmt == (OQ_MXFP4 | OQ_TILED)
     if codes is None and mx_tiled:
         codes = torch.empty(max(16, oq_tiled_mx_bytes(M, d)), dtype=torch.uint8, device=dev)
-    elif codes is None and afmt & OQ_TILED:
-        planes = 2 if (afmt & ~OQ_TILED) == OQ_A6 else 1
+    elif codes is None and fmt & OQ_TILED:
+        planes = 2 if (fmt & ~OQ_TILED) == OQ_A6 else 1
         codes = torch.empty(max(1, planes * oq_tiled_bytes(M, d)), dtype=torch.uint8, device=dev)
     elif codes is None:
-        width = d if afmt in (OQ_A8, OQ_A6) else d // 2
-        codes = torch.empty((M, width), dtype=torch.int8 if afmt in (OQ_A8, OQ_A6) else torch.uint8, device=dev)
+        width = d if fmt in (OQ_A8, OQ_A6) else d // 2
+        codes = torch.empty((M, width), dtype=torch.int8 if fmt in (OQ_A8, OQ_A6) else torch.uint8, device=dev)
     if mx_tiled:
         if e8m0 is None:
             e8m0 = torch.empty(max(4, oq_tiled_mx_bytes(M, d) // 16), dtype=torch.uint8, device=dev)
-    elif afmt == OQ_MXFP4:
+    elif fmt == OQ_MXFP4:
         if e8m0 is None:
             e8m0 = torch.empty((M, d // 32), dtype=torch.uint8, device=dev)
     elif scale is None:
         scale = torch.empty(M, dtype=torch.float32, device=dev)
     if center and mean is None:
         mean = torch.empty(M, dtype=torch.float32, device=dev)
-    ldc = 0 if afmt & OQ_TILED else codes.stride(0) * codes.element_size()
+    ldc = 0 if fmt & OQ_TILED else codes.stride(0) * codes.element_size()
     _check(_lib.oq_quant_act(_p(x), M, d, x.stride(0), _rref(rot), int(center), afmt, _p(codes),
                              ldc, _p(scale), _p(e8m0), _p(mean), _stream()))
     return {"codes": codes, "scale": scale, "e8m0": e8m0, "mean": mean}

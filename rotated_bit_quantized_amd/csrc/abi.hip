@@ -87,6 +87,41 @@ int check_dense(const char *fn, const oq_rot *rot, int d, bool weights) {
 
 int qmax_of(int afmt) { return afmt == OQ_A8 ? 127 : afmt == OQ_A6 ? 31 : 7; }
 
+// x with Phi(-x) = tail (the standard normal upper quantile), by bisection on
+// erfc(x / sqrt 2) / 2 = tail until the bracket cannot shrink
+double upper_normal_quantile(double tail) {
+  double lo = 0.0, hi = 40.0;
+  for (;;) {
+    const double mid = 0.5 * (lo + hi);
+    if (mid <= lo || mid >= hi) break;
+    if (0.5 * std::erfc(mid / std::sqrt(2.0)) > tail)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  return hi;
+}
+
+// CentriQ Sec. 4.2 "Scale and grid", App. B.3 Table 3: rho = 0.9995, gamma* =
+// 2.5591; the rho-quantile of d magnitudes interpolates between the order
+// statistics k = floor(rho (d - 1)) and k + 1 (ascending), i.e. the
+// (d - k)-th and (d - k - 1)-th largest.
+int pctl_setup(const char *fn, int afmt, int d, PctlArgs *pa) {
+  const int base = afmt & ~OQ_TILED;
+  if (base != OQ_A8 && base != OQ_A6 && base != OQ_A4)
+    return fail(OQ_ERR_UNSUPPORTED, "%s: OQ_SCALE_PCTL applies to integer activation codes", fn);
+  if (!rpbh_wave_supported(d))
+    return fail(OQ_ERR_UNSUPPORTED, "%s: OQ_SCALE_PCTL needs d %% 16 == 0 and 16 <= d <= 4096 (d=%d)", fn, d);
+  const double h = 0.9995 * (double)(d - 1);
+  const double k = std::floor(h);
+  pa->rank = d - (int)k;
+  pa->frac = h - k;
+  pa->gamma = 2.5591;
+  pa->z = upper_normal_quantile(0.00025);
+  if (pa->rank < 2 || pa->rank > 4) return fail(OQ_ERR_UNSUPPORTED, "%s: percentile rank %d", fn, pa->rank);
+  return OQ_OK;
+}
+
 size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct LinearWs {
@@ -183,6 +218,14 @@ int oq_quant_act(const uint16_t *x, int64_t M, int32_t d, int64_t ldx, const oq_
                  void *codes, int64_t ldc_bytes, float *scale, uint8_t *e8m0, float *mean, hipStream_t stream) {
   int rc = check_x("oq_quant_act", x, M, d, ldx);
   if (rc) return rc;
+  PctlArgs pa;
+  const PctlArgs *pp = nullptr;
+  if (afmt & OQ_SCALE_PCTL) {
+    afmt &= ~OQ_SCALE_PCTL;
+    rc = pctl_setup("oq_quant_act", afmt, d, &pa);
+    if (rc) return rc;
+    pp = &pa;
+  }
   if (M > 0 && !codes) return fail(OQ_ERR_INVALID_ARG, "oq_quant_act: codes is NULL");
   if (!al16(codes) || (!(afmt & OQ_TILED) && ldc_bytes % 16))
     return fail(OQ_ERR_ALIGNMENT, "oq_quant_act: code rows must be 16-byte aligned");
@@ -226,7 +269,7 @@ int oq_quant_act(const uint16_t *x, int64_t M, int32_t d, int64_t ldx, const oq_
     g_err[0] = 0;
     return hip_status(launch_rpbh_quant(x, M, d, ldx, ra, center ? 1 : 0, mean,
                                         base_fmt == OQ_A4 ? OUT_FP6 : OUT_FP6X2, qmax_of(base_fmt), codes, 0,
-                                        scale, stream),
+                                        scale, stream, pp),
                       "oq_quant_act");
   }
   if (afmt != OQ_A8 && afmt != OQ_A6 && afmt != OQ_A4)
@@ -240,7 +283,7 @@ int oq_quant_act(const uint16_t *x, int64_t M, int32_t d, int64_t ldx, const oq_
   if (rc) return rc;
   g_err[0] = 0;
   return hip_status(launch_rpbh_quant(x, M, d, ldx, ra, center ? 1 : 0, mean, afmt == OQ_A4 ? OUT_I4 : OUT_I8,
-                                      qmax_of(afmt), codes, ldc_bytes, scale, stream),
+                                      qmax_of(afmt), codes, ldc_bytes, scale, stream, pp),
                     "oq_quant_act");
 }
 
@@ -374,7 +417,7 @@ int oq_prepack_mx(const uint8_t *w, const uint8_t *w_e8m0, int32_t N, int32_t K,
 size_t oq_workspace_bytes(int op, int64_t M, int32_t K, int32_t N, int afmt) {
   (void)N;
   if (op != OQ_OP_LINEAR || M < 0 || K <= 0) return 0;
-  return linear_ws(M, K, afmt).total;
+  return linear_ws(M, K, afmt & ~OQ_SCALE_PCTL).total;
 }
 
 int oq_linear_fused(const uint16_t *x, int64_t M, int32_t K, int64_t ldx, const oq_rot *rot, int center, int afmt,
@@ -383,6 +426,14 @@ int oq_linear_fused(const uint16_t *x, int64_t M, int32_t K, int64_t ldx, const 
   const char *fn = "oq_linear_fused";
   int rc = check_x(fn, x, M, K, ldx);
   if (rc) return rc;
+  PctlArgs pa;
+  const PctlArgs *pp = nullptr;
+  if (afmt & OQ_SCALE_PCTL) {
+    afmt &= ~OQ_SCALE_PCTL;
+    rc = pctl_setup(fn, afmt, K, &pa);
+    if (rc) return rc;
+    pp = &pa;
+  }
   if (afmt == (OQ_MXFP4 | OQ_TILED)) {
     if (!rot || rot->kind != OQ_ROT_DENSE32) return fail(OQ_ERR_UNSUPPORTED, "%s: MXFP4 needs a DENSE32 rotation", fn);
     if (center || w1) return fail(OQ_ERR_UNSUPPORTED, "%s: centering is not defined for MXFP4 here", fn);
@@ -428,7 +479,7 @@ int oq_linear_fused(const uint16_t *x, int64_t M, int32_t K, int64_t ldx, const 
     float *mean = reinterpret_cast<float *>(wsb + L.mean);
     g_err[0] = 0;
     rc = hip_status(launch_rpbh_quant(x, M, K, ldx, ra, center ? 1 : 0, mean, base_fmt == OQ_A4 ? OUT_FP6 : OUT_FP6X2,
-                                      qmax_of(base_fmt), codes, 0, scale, stream),
+                                      qmax_of(base_fmt), codes, 0, scale, stream, pp),
                     fn);
     if (rc) return rc;
     return hip_status(launch_gemm_fp6(codes, base_fmt == OQ_A6 ? 2 : 1, scale, M, K, w, (const float *)w_scale, N,
@@ -467,7 +518,7 @@ int oq_linear_fused(const uint16_t *x, int64_t M, int32_t K, int64_t ldx, const 
   float *mean = reinterpret_cast<float *>(wsb + L.mean);
   g_err[0] = 0;
   rc = hip_status(launch_rpbh_quant(x, M, K, ldx, ra, center ? 1 : 0, mean, afmt == OQ_A4 ? OUT_I4 : OUT_I8,
-                                    qmax_of(afmt), codes, L.ldc, scale, stream),
+                                    qmax_of(afmt), codes, L.ldc, scale, stream, pp),
                   fn);
   if (rc) return rc;
   return hip_status(launch_gemm_int(codes, L.ldc, afmt == OQ_A4 ? 1 : 0, scale, M, K, w, (const float *)w_scale, N, group,

@@ -28,7 +28,10 @@
 //   * when h is a power of 4, 1/sqrt(h) is a power of two: the per-round
 //     multiply is exact and is deferred into the quantization scale
 //     (identical codes and scales; the float32 output mode applies it);
-//   * the row range (absmax) is a wavefront reduction.
+//   * the row range (absmax) is a wavefront reduction; with the percentile
+//     range (CentriQ Sec. 4.2 "Scale and grid") each lane keeps its four
+//     largest magnitudes and the wavefront merges those lists, which gives the
+//     order statistics the interpolated 0.9995-quantile needs for d <= 4096.
 #include "oq_internal.h"
 
 #pragma clang fp contract(off)
@@ -195,12 +198,12 @@ struct WaveLds {
 
 // mode (OUT_*) is a template argument: one kernel body per output keeps the
 // register count of each near what its own path needs.
-template <int SLOTS, int ROUNDS, int mode>
+template <int SLOTS, int ROUNDS, int mode, bool PCTL>
 __global__ void __launch_bounds__(64 * WAVES_PER_WG)
 rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, const int32_t *__restrict__ perm,
                  const int8_t *__restrict__ signs, int h, float c_h, int pow4, int center,
                  float *__restrict__ mean_out, int qmax, void *__restrict__ out, int64_t ld_out_bytes,
-                 float *__restrict__ scale_out) {
+                 float *__restrict__ scale_out, PctlArgs pa) {
   using L = WaveLds<SLOTS, ROUNDS>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
   const int lane = threadIdx.x & 63;
@@ -413,16 +416,46 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
     }
 
     float a = 0.f;
+    if constexpr (PCTL) {
+      // the four largest magnitudes of the row, t[0] >= .. >= t[3]; a lane's
+      // own list first (-1 for coordinates past the row end), then the
+      // wavefront merges lists (each insertion keeps the multiset's top four)
+      float t[4] = {-1.f, -1.f, -1.f, -1.f};
+      auto ins = [&](float xv) {
+        t[3] = __builtin_amdgcn_fmed3f(t[3], t[2], xv);
+        t[2] = __builtin_amdgcn_fmed3f(t[2], t[1], xv);
+        t[1] = __builtin_amdgcn_fmed3f(t[1], t[0], xv);
+        t[0] = fmaxf(t[0], xv);
+      };
 #pragma unroll
-    for (int s = 0; s < SLOTS; ++s) {
-      float as = 0.f;
+      for (int s = 0; s < SLOTS; ++s)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) as = fmaxf(as, fabsf(v[s][j]));
-      if (act[s]) a = fmaxf(a, as);
+        for (int j = 0; j < 16; ++j) ins(act[s] ? fabsf(v[s][j]) : -1.f);
+#pragma unroll
+      for (int lg = 0; lg < 6; ++lg) {
+        const float p0 = xlane(t[0], lg), p1 = xlane(t[1], lg), p2 = xlane(t[2], lg), p3 = xlane(t[3], lg);
+        ins(p0);
+        ins(p1);
+        ins(p2);
+        ins(p3);
+      }
+      const float lo = pa.rank == 4 ? t[3] : (pa.rank == 3 ? t[2] : t[1]);
+      const float hi = pa.rank == 4 ? t[2] : (pa.rank == 3 ? t[1] : t[0]);
+      const double lo64 = (double)(lo * c_all), hi64 = (double)(hi * c_all);  // c_all: exact
+      const double q = lo64 + pa.frac * (hi64 - lo64);
+      a = fmaxf((float)((q * pa.gamma) / pa.z), 1e-10f);
+    } else {
+#pragma unroll
+      for (int s = 0; s < SLOTS; ++s) {
+        float as = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) as = fmaxf(as, fabsf(v[s][j]));
+        if (act[s]) a = fmaxf(a, as);
+      }
+#pragma unroll
+      for (int lg = 0; lg < 6; ++lg) a = fmaxf(a, xlane(a, lg));
+      a = fmaxf(a * c_all, 1e-10f);  // c_all is a power of two: exact
     }
-#pragma unroll
-    for (int lg = 0; lg < 6; ++lg) a = fmaxf(a, xlane(a, lg));
-    a = fmaxf(a * c_all, 1e-10f);  // c_all is a power of two: exact
     const float fq = (float)qmax;
     const float alpha = __fdiv_rn(a, fq);
     const float inv = __fdiv_rn(fq, a) * (c_all * sg);  // exact rescale: deferred factor and lane sign
@@ -454,9 +487,10 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
       // the 96-bit string at bit 6*(base % 32) of its half of the k-group.
       // Codes are formed as floats (integer-valued, +0 for zero) and
       // converted two slots at a time with v_cvt_scalef32_2xpk16_fp6_f32,
-      // which interleaves its two sources field by field.  No clamp: with
-      // a = max |v| and inv = RN32(qmax / a), |v inv| <= qmax (1 + 2^-24)^2,
-      // so RNE gives |t| <= qmax, as the clamp to +-qmax would.
+      // which interleaves its two sources field by field.  With the absmax
+      // range no clamp is needed: a = max |v| and inv = RN32(qmax / a) give
+      // |v inv| <= qmax (1 + 2^-24)^2, so RNE gives |t| <= qmax; the
+      // percentile range clips.
       uint8_t *tb = static_cast<uint8_t *>(out) + ((row >> 5) * (d >> 6)) * 1536;
       const int rr = (int)(row & 31);
       const int64_t pstride = tiled_bytes(M, d);
@@ -466,8 +500,14 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
         float ta[16], tbv[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          ta[j] = __builtin_rintf(v[s0][j] * inv) + 0.0f;
-          tbv[j] = two ? __builtin_rintf(v[two ? s0 + 1 : s0][j] * inv) + 0.0f : 0.0f;
+          float ra = __builtin_rintf(v[s0][j] * inv);
+          float rb = two ? __builtin_rintf(v[two ? s0 + 1 : s0][j] * inv) : 0.0f;
+          if constexpr (PCTL) {
+            ra = __builtin_amdgcn_fmed3f(ra, -fq, fq);
+            rb = __builtin_amdgcn_fmed3f(rb, -fq, fq);
+          }
+          ta[j] = ra + 0.0f;
+          tbv[j] = rb + 0.0f;
         }
         const bool wa = act[s0], wb = two && act[two ? s0 + 1 : s0];
         if (mode == OUT_FP6) {
@@ -481,14 +521,14 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
   }
 }
 
-template <int SLOTS, int ROUNDS, int MODE>
+template <int SLOTS, int ROUNDS, int MODE, bool PCTL>
 hipError_t launch_m(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotArgs &rot, int center, float *mean,
-                    int qmax, void *out, int64_t ld_out_bytes, float *scale, hipStream_t stream) {
+                    int qmax, void *out, int64_t ld_out_bytes, float *scale, const PctlArgs &pa, hipStream_t stream) {
   using L = WaveLds<SLOTS, ROUNDS>;
   const size_t lds = (size_t)L::TOTAL;
   static bool attr_set = false;
   if (!attr_set && lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void *)rpbh_wave_kernel<SLOTS, ROUNDS, MODE>,
+    hipError_t e = hipFuncSetAttribute((const void *)rpbh_wave_kernel<SLOTS, ROUNDS, MODE, PCTL>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
@@ -499,32 +539,45 @@ hipError_t launch_m(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotA
   if (grid < 1) grid = 1;
   const int h = ROUNDS ? rot.block : 16;
   const int pow4 = ROUNDS && ((__builtin_ctz((unsigned)h) & 1) == 0);
-  hipLaunchKernelGGL((rpbh_wave_kernel<SLOTS, ROUNDS, MODE>), dim3((unsigned)grid), dim3(64 * WAVES_PER_WG), lds,
+  hipLaunchKernelGGL((rpbh_wave_kernel<SLOTS, ROUNDS, MODE, PCTL>), dim3((unsigned)grid), dim3(64 * WAVES_PER_WG), lds,
                      stream, x, M, d, ldx, rot.perm, rot.signs, h, rot.c_h, pow4, center, mean, qmax, out,
-                     ld_out_bytes, scale);
+                     ld_out_bytes, scale, pa);
   return hipGetLastError();
+}
+
+template <int SLOTS, int ROUNDS, int MODE>
+hipError_t launch_p(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotArgs &rot, int center, float *mean,
+                    int qmax, void *out, int64_t ld_out_bytes, float *scale, const PctlArgs *pctl, hipStream_t stream) {
+  if (pctl) {
+    if constexpr (MODE == OUT_F32) return hipErrorInvalidValue;
+    else return launch_m<SLOTS, ROUNDS, MODE, true>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, *pctl, stream);
+  }
+  return launch_m<SLOTS, ROUNDS, MODE, false>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale,
+                                              PctlArgs{0, 0.0, 0.0, 1.0}, stream);
 }
 
 template <int SLOTS, int ROUNDS>
 hipError_t launch_w(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotArgs &rot, int center, float *mean,
-                    int mode, int qmax, void *out, int64_t ld_out_bytes, float *scale, hipStream_t stream) {
+                    int mode, int qmax, void *out, int64_t ld_out_bytes, float *scale, const PctlArgs *pctl,
+                    hipStream_t stream) {
   switch (mode) {
-    case OUT_F32: return launch_m<SLOTS, ROUNDS, OUT_F32>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, stream);
-    case OUT_I8: return launch_m<SLOTS, ROUNDS, OUT_I8>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, stream);
-    case OUT_I4: return launch_m<SLOTS, ROUNDS, OUT_I4>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, stream);
-    case OUT_FP6: return launch_m<SLOTS, ROUNDS, OUT_FP6>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, stream);
-    case OUT_FP6X2: return launch_m<SLOTS, ROUNDS, OUT_FP6X2>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, stream);
+    case OUT_F32: return launch_p<SLOTS, ROUNDS, OUT_F32>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, pctl, stream);
+    case OUT_I8: return launch_p<SLOTS, ROUNDS, OUT_I8>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, pctl, stream);
+    case OUT_I4: return launch_p<SLOTS, ROUNDS, OUT_I4>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, pctl, stream);
+    case OUT_FP6: return launch_p<SLOTS, ROUNDS, OUT_FP6>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, pctl, stream);
+    case OUT_FP6X2: return launch_p<SLOTS, ROUNDS, OUT_FP6X2>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, pctl, stream);
   }
   return hipErrorInvalidValue;
 }
 
 template <int SLOTS>
 hipError_t launch_r(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotArgs &rot, int center, float *mean,
-                    int mode, int qmax, void *out, int64_t ld_out_bytes, float *scale, hipStream_t stream) {
+                    int mode, int qmax, void *out, int64_t ld_out_bytes, float *scale, const PctlArgs *pctl,
+                    hipStream_t stream) {
   switch (rot.rounds) {
-    case 0: return launch_w<SLOTS, 0>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, stream);
-    case 1: return launch_w<SLOTS, 1>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, stream);
-    case 2: return launch_w<SLOTS, 2>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, stream);
+    case 0: return launch_w<SLOTS, 0>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, pctl, stream);
+    case 1: return launch_w<SLOTS, 1>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, pctl, stream);
+    case 2: return launch_w<SLOTS, 2>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, pctl, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -535,13 +588,14 @@ bool rpbh_wave_supported(int d) { return d >= 16 && d <= 4096 && d % 16 == 0; }
 
 hipError_t launch_rpbh_wave(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotArgs &rot, int center,
                             float *mean, int mode, int qmax, void *out, int64_t ld_out_bytes, float *scale,
-                            hipStream_t stream) {
+                            hipStream_t stream, const PctlArgs *pctl) {
   if (M == 0) return hipSuccess;
+  if (pctl && (pctl->rank < 2 || pctl->rank > 4)) return hipErrorInvalidValue;
   switch ((d + 1023) / 1024) {
-    case 1: return launch_r<1>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, stream);
-    case 2: return launch_r<2>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, stream);
-    case 3: return launch_r<3>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, stream);
-    case 4: return launch_r<4>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, stream);
+    case 1: return launch_r<1>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, pctl, stream);
+    case 2: return launch_r<2>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, pctl, stream);
+    case 3: return launch_r<3>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, pctl, stream);
+    case 4: return launch_r<4>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, pctl, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -78,17 +78,29 @@ struct RotArgs {
   float c_h;             // RN32(1/sqrt h)
 };
 
-// K1: (center) -> RPBH rounds -> (quantize) per token row.
+// Percentile range of a token (CentriQ Sec. 4.2 "Scale and grid"):
+// r = RN32((q * gamma) / z), q = lo + frac (hi - lo) in float64, where lo and
+// hi are the rank-th and (rank-1)-th largest magnitudes of the row.
+struct PctlArgs {
+  int rank;     // 2..4 for rows of at most 4096
+  double frac;  // rho (n - 1) - floor(rho (n - 1))
+  double gamma;
+  double z;     // Phi^-1((1 + rho) / 2)
+};
+
+// K1: (center) -> RPBH rounds -> (quantize) per token row; pctl selects the
+// percentile range instead of absmax (integer outputs, rows the wave kernel
+// takes only).
 hipError_t launch_rpbh_quant(const uint16_t *x, int64_t M, int d, int64_t ldx,
                              const RotArgs &rot, int center, float *mean,
                              int out_mode, int qmax, void *out, int64_t ld_out_bytes,
-                             float *scale, hipStream_t stream);
+                             float *scale, hipStream_t stream, const PctlArgs *pctl = nullptr);
 
 // K1, one wavefront per row (activation rows of width d <= 4096).
 bool rpbh_wave_supported(int d);
 hipError_t launch_rpbh_wave(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotArgs &rot, int center,
                             float *mean, int mode, int qmax, void *out, int64_t ld_out_bytes, float *scale,
-                            hipStream_t stream);
+                            hipStream_t stream, const PctlArgs *pctl = nullptr);
 
 // K2: dense per-32 transform -> (MXFP4 quantize | float32 out); mx_out: 0 float32,
 // 1 row-major codes + E8M0, 2 tiled MXFP4 layout.

@@ -155,3 +155,62 @@ def test_tiled_layer(oq, cid, M, N):
           "w1": None if w1 is None else to_host(w1)}
     y_ref, S = OL.linear_int(a, wp, s.group)
     check_output(to_host(y_t), y_ref, S, wl.K // 64, "tiled layer")
+
+
+@pytest.mark.parametrize("M,K,h,rounds,center,afmt", [(70, 3072, 1024, 1, False, 4), (37, 1024, 128, 1, True, 4),
+                                                      (33, 1920, 128, 2, False, 6), (9, 4096, 1024, 2, True, 8),
+                                                      (65, 256, 32, 1, False, 8), (3, 32, 32, 0, False, 4)])
+def test_percentile_scale(oq, M, K, h, rounds, center, afmt):
+    """OQ_SCALE_PCTL (CentriQ Sec. 4.2 "Scale and grid"): scales equal to the
+    oracle's, codes bit-exact outside the rounding-boundary exemption, the
+    tiled writer bit-identical to the canonical one."""
+    say("case percentile", M, K, h, rounds, center, afmt)
+    rng = np.random.default_rng(M + K)
+    x = rng.standard_normal((M, K)) * rng.uniform(0.5, 4, size=(M, 1)) + (1.5 if center else 0.0)
+    x[:, 3] *= 30.0  # an outlier channel the percentile range clips
+    xb = WL.f32_to_bf16_bits(x.astype(np.float32))
+    if rounds:
+        perm, signs = _meta(K, h, rounds, 13)
+        rot = oq.Rotation.rpbh(to_dev(perm), to_dev(signs), h)
+    else:
+        perm = signs = rot = None
+    fmt = afmt | oq.OQ_SCALE_PCTL
+    canon = oq.oq_quant_act(to_dev(xb), rot, fmt, center=center)
+    tiled = oq.oq_quant_act(to_dev(xb), rot, fmt | oq.OQ_TILED, center=center) if afmt in (4, 6) and K % 64 == 0 else None
+    torch.cuda.synchronize()
+    ref = OL.activations_int(xb, perm, signs, h, afmt, center, pctl=True)
+    np.testing.assert_array_equal(to_host(canon["scale"]), ref["alpha"])
+    codes = to_host(canon["codes"])
+    codes = OQ.unpack_int4(codes.view(np.uint8)) if afmt == 4 else codes.astype(np.int32)
+    check_codes(codes, ref["codes"], ref["flags"], "percentile codes")
+    qmax = OQ.qmax_for_bits(afmt)
+    assert np.any(np.abs(codes) == qmax), "the outlier channel should clip"
+    if tiled is not None:
+        got = to_host(tiled["codes"])
+        plane = oq.oq_tiled_bytes(M, K)
+        live = row_mask(M, K)
+        if afmt == 4:
+            np.testing.assert_array_equal(got[:plane][live], tile(codes)[live])
+        else:
+            qh, ql = split_a6(codes)
+            np.testing.assert_array_equal(got[:plane][live], tile(qh)[live])
+            np.testing.assert_array_equal(got[plane:2 * plane][live], tile(ql)[live])
+        np.testing.assert_array_equal(to_host(tiled["scale"]), to_host(canon["scale"]))
+
+
+def test_percentile_layer_fused(oq):
+    """oq_linear_fused with the percentile scale equals the separate calls."""
+    wl = WL.make_workload(2, M=130, Ns=(256,))
+    rot = oq.Rotation.rpbh(to_dev(wl.perm), to_dev(wl.signs), 1024)
+    wq = oq.oq_quant_weight(to_dev(wl.weights[0]), rot, oq.OQ_W4, 64)
+    wt = oq.oq_prepack_w4(wq["codes"], wq["scales"], 256, wl.K)
+    fmt = oq.OQ_A4 | oq.OQ_TILED | oq.OQ_SCALE_PCTL
+    x = to_dev(wl.x_bits)
+    y_f = oq.oq_linear_fused(x, rot, False, fmt, wt["codes"], wt["scales"], 256, 64)
+    act = oq.oq_quant_act(x, rot, fmt)
+    y_s = oq.oq_gemm_w4a4(oq.OQ_A4 | oq.OQ_TILED, act["codes"], act["scale"], wt["codes"], wt["scales"], 256, 64,
+                          M=130, K=wl.K)
+    torch.cuda.synchronize()
+    assert torch.equal(y_f.view(torch.int16), y_s.view(torch.int16))
+    ref = OL.activations_int(wl.x_bits, wl.perm, wl.signs, 1024, 4, False, pctl=True)
+    np.testing.assert_array_equal(to_host(act["scale"]), ref["alpha"])
