@@ -197,6 +197,29 @@ def _time_fused(torch, oq, st, reps, warmup):
     return N, sum(v) / reps, v
 
 
+def _time_pctl(torch, oq, st, reps, warmup):
+    """The rotate/quant launch with the percentile activation scale
+    (OQ_SCALE_PCTL) in place of absmax, same inputs and outputs."""
+    s = st["spec"]
+    afmt = s.afmt | oq.OQ_SCALE_PCTL | (oq.OQ_TILED if st["tiled"] else 0)
+
+    def call(i):
+        oq.oq_quant_act(st["xs"][i % len(st["xs"])], st["rot"], afmt, center=s.center, codes=st["codes"],
+                        scale=st["scale"], e8m0=st["e8m0"], mean=st["mean"])
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
+        call(i)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    v = [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+    return sum(v) / reps, v
+
+
 def _copy_reference(torch, nbytes=1 << 30, reps=3):
     """A plain device-to-device copy of known size, launched beside the
     profiled kernels so that HBM byte counters can be scaled by what they
@@ -331,6 +354,9 @@ def main():
     if not args.only_step:
         nf, fm, fv = _time_fused(torch, oq, st, max(20, args.steps // 2), 5)
         result["linear_fused_us"] = {"d_out": nf, "mean": round(fm * 1e3, 3), **_dist_us(fv)}
+        pm, pv = _time_pctl(torch, oq, st, max(20, args.steps // 2), 5)
+        result["rotate_quant_pctl_us"] = {"mean": round(pm * 1e3, 3), **_dist_us(pv),
+                                          "hbm_frac": round(rq_bytes / (pm * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
         result["gpu_state"] = _gpu_state()
 
     if not args.no_configs and not args.only_step:
