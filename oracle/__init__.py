@@ -18,7 +18,9 @@ what the layer computes, written from the pages:
   * Pith review of WUSH (arXiv 2512.00956), "Core claim": per-block transform
     pair with T_x = T_w^{-T}, RTN absmax MXFP4 block quantizers with G = 32;
   * FLUX.1-schnell-OrbitQuant-W4A4 model card, "Quantization" table: rotation
-    rpbh, activation normalization epsilon 1e-10.
+    rpbh, activation normalization epsilon 1e-10, codebook lloyd_max;
+  * OrbitQuant PR #25 ("Default changes") and CentriQ Sec. 2 ("Related work"):
+    Lloyd-Max activation codes from the post-rotation marginal.
 
 Floating point: values are computed in float64 (the mathematics) and, where
 the integer codes depend on float32 rounding, in one fixed float32 evaluation
@@ -30,5 +32,7 @@ Modules:
   quant     mean, centering, absmax integer codes, INT4 packing, MXFP4 codec
   gemm      grouped integer products, fp32-scale epilogue, MXFP4 product
   linear    offline weight preparation and the whole forward pass
+  lloyd_max Lloyd-Max codebook of the sphere marginal, nearest-level codes,
+            the float16 dequantizing product
 """
-from . import hadamard, rotation, quant, gemm, linear  # noqa: F401
+from . import hadamard, rotation, quant, gemm, linear, lloyd_max  # noqa: F401
