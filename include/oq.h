@@ -289,9 +289,89 @@ int oq_prepack_w4(const uint8_t *w, const float *w_scale, int32_t N, int32_t K, 
 int oq_prepack_mx(const uint8_t *w, const uint8_t *w_e8m0, int32_t N, int32_t K,
                   uint8_t *w_tiled, uint8_t *w_e8m0_tiled, hipStream_t stream);
 
-enum { OQ_OP_GEMM_W4A8 = 1, OQ_OP_GEMM_W4A4 = 2, OQ_OP_LINEAR = 3 };
+/*
+ * Lloyd-Max activation path (OrbitQuant PR #25, "Default changes": Lloyd-Max
+ * codes are the method's activation quantizer below 8 bits, with codebooks
+ * built per layer width by a Newton solver; CentriQ Sec. 2 "Related work":
+ * the codebook comes from the post-rotation marginal; model card
+ * FLUX.1-schnell-OrbitQuant-W4A4, "Quantization": codebook lloyd_max,
+ * activation normalization epsilon 1e-10).
+ *
+ * The marginal is that of one coordinate T of a point uniform on the unit
+ * sphere S^{d-1}, density proportional to (1 - t^2)^((d-3)/2); tokens are
+ * normalised by their RMS, so levels are for U = sqrt(d) T (variance 1).
+ */
 
-/* Scratch bytes a call needs (0 if none).  Pure host function. */
+/*
+ * oq_lloyd_max_levels -- host function, no device work.  levels: host
+ * float64 [2^bits], ascending: the minimum-MSE quantizer levels of U (every
+ * level the mean of U over its cell, every boundary the midpoint of its two
+ * levels), solved by Newton's method on those conditions.  d >= 3,
+ * bits in [1, 8].  OQ_ERR_UNSUPPORTED if the solve does not converge.
+ */
+int oq_lloyd_max_levels(int32_t d, int32_t bits, double *levels);
+
+/*
+ * oq_lloyd_max_tables -- host function: the stored codebook the kernels use.
+ * levels_f16: host uint16 [2^bits], the levels rounded to float16 (RNE);
+ * thresholds: host float32 [2^bits - 1], the exact midpoints of adjacent
+ * float16 levels (so a code is the nearest stored level).  Copy both to the
+ * device for oq_quant_act_lm / oq_gemm_lm.
+ */
+int oq_lloyd_max_tables(int32_t d, int32_t bits, uint16_t *levels_f16, float *thresholds);
+
+/* bytes of the tiled float16 operand layout for `rows` rows (K % 16 == 0) */
+size_t oq_tiled_f16_bytes(int64_t rows, int32_t K);
+
+/*
+ * oq_quant_act_lm -- fused (center) -> RPBH rotate -> Lloyd-Max codes.
+ *   rho_t = max(RN32(sqrt(S_t / d)), RN32(1e-10)), S_t the float64 sum of
+ *   squares of the rotated float32 values; u = RN32(v RN32(1 / rho_t));
+ *   code = number of thresholds strictly below u (ties go to the lower level).
+ *   scale[t] = rho_t (float32 [M]).
+ * tiled == 0: codes are level indices, two per byte (element 2i in bits
+ *   3..0) for bits <= 4, else one byte each, rows of ldc_bytes (multiple of 16).
+ * tiled != 0: codes receives the float16 levels themselves in the tiled
+ *   float16 layout (oq_tiled_f16_bytes(M, d) bytes; ldc_bytes ignored), the
+ *   operand oq_gemm_lm takes directly.
+ * levels_f16 / thresholds: device copies of oq_lloyd_max_tables' output for
+ * the same bits.  rot: RPBH or NULL; d <= 4096.  mean as in oq_quant_act.
+ */
+int oq_quant_act_lm(const uint16_t *x, int64_t M, int32_t d, int64_t ldx, const oq_rot *rot, int center,
+                    int32_t bits, int tiled, const uint16_t *levels_f16, const float *thresholds,
+                    void *codes, int64_t ldc_bytes, float *scale, float *mean, hipStream_t stream);
+
+/*
+ * oq_prepack_w16 -- dequantize canonical INT4 weights (oq_quant_weight OQ_W4
+ * output) to W16[o][k] = RN16(w_scale[o][k / group] * q[o][k]) (the exact
+ * product rounded once) in the tiled float16 layout: oq_tiled_f16_bytes(N, K)
+ * bytes, padding rows zero.  K % 32 == 0; group a multiple of 32 dividing K.
+ */
+int oq_prepack_w16(const uint8_t *w, const float *w_scale, int32_t N, int32_t K, int32_t group,
+                   uint16_t *w16_tiled, hipStream_t stream);
+
+/*
+ * oq_gemm_lm -- Lloyd-Max activations times dequantized weights:
+ *   y[t][o] = bf16_RNE( a_scale[t] * sum_k A16[t][k] W16[o][k]
+ *                       + mean[t] * w1[o] + bias[o] )
+ *   A16 the float16 level of each code; products exact in float32, summed in
+ *   float32 on the float16 matrix cores.
+ * tiled != 0: qa is oq_quant_act_lm's tiled output (lda_bytes, levels_f16 and
+ *   ws unused).  tiled == 0: qa holds level indices as oq_quant_act_lm writes
+ *   them for `bits`, rows of lda_bytes; levels_f16 (device) expands them into
+ *   ws, which needs oq_workspace_bytes(OQ_OP_GEMM_LM, M, K, N, 0) bytes.
+ * w16_tiled from oq_prepack_w16; a_scale float32 [M]; mean and w1 both NULL
+ * or both set; bias nullable; y bf16 [M][ldy].  K % 32 == 0.
+ */
+int oq_gemm_lm(int32_t bits, int tiled, const void *qa, int64_t lda_bytes, const float *a_scale, int64_t M,
+               int32_t K, const uint16_t *levels_f16, const uint16_t *w16_tiled, int32_t N, const float *mean,
+               const float *w1, const float *bias, uint16_t *y, int64_t ldy, void *ws, size_t ws_bytes,
+               hipStream_t stream);
+
+enum { OQ_OP_GEMM_W4A8 = 1, OQ_OP_GEMM_W4A4 = 2, OQ_OP_LINEAR = 3, OQ_OP_GEMM_LM = 4 };
+
+/* Scratch bytes a call needs (0 if none).  Pure host function.  For
+ * OQ_OP_GEMM_LM, afmt is OQ_TILED for tiled activations, else 0. */
 size_t oq_workspace_bytes(int op, int64_t M, int32_t K, int32_t N, int afmt);
 
 #ifdef __cplusplus

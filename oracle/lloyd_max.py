@@ -159,16 +159,46 @@ def codebook_tables(d: int, bits: int):
 
 
 # ---------------------------------------------------------------- quantizer
-def rms_scale(v32: np.ndarray) -> np.ndarray:
-    """rho_t = max(RN32(sqrt(RN64(S_t) / d)), RN32(1e-10)), S_t the exact sum
-    of squares of the float32 rotated coordinates."""
+def rms_f64(v32: np.ndarray) -> np.ndarray:
+    """sqrt(RN64(S_t) / d) in float64, S_t the exact sum of squares of the
+    float32 rotated coordinates (each square is exact in float64)."""
     v32 = np.asarray(v32, dtype=np.float32)
     d = v32.shape[1]
-    out = np.empty(v32.shape[0], dtype=np.float32)
+    out = np.empty(v32.shape[0], dtype=np.float64)
     for t in range(v32.shape[0]):
         S = math.fsum(float(x) * float(x) for x in v32[t])
-        out[t] = np.float32(math.sqrt(S / d))
-    return np.maximum(out, EPS32)
+        out[t] = math.sqrt(S / d)
+    return out
+
+
+def rms_scale(v32: np.ndarray) -> np.ndarray:
+    """rho_t = max(RN32(sqrt(RN64(S_t) / d)), RN32(1e-10))."""
+    return np.maximum(rms_f64(v32).astype(np.float32), EPS32)
+
+
+def rms_near_midpoint(v32: np.ndarray) -> np.ndarray:
+    """Tokens whose float64 RMS lies within 1e-12 (relative) of a float32
+    rounding midpoint: a sum of squares taken in another (equally valid)
+    float64 order may round rho to the neighbouring float32 there."""
+    r = rms_f64(v32)
+    f = r.astype(np.float32)
+    up = np.nextafter(f, np.float32(np.inf)).astype(np.float64)
+    dn = np.nextafter(f, np.float32(-np.inf)).astype(np.float64)
+    f = f.astype(np.float64)
+    gap = np.minimum(np.abs(0.5 * (f + up) - r), np.abs(0.5 * (f + dn) - r))
+    return gap <= 1e-12 * np.abs(r)
+
+
+def boundary_flags(v32: np.ndarray, rho: np.ndarray, thr32: np.ndarray) -> np.ndarray:
+    """Elements whose u = RN32(v RN32(1 / rho)) lies within 1e-6 (relative)
+    of a decision threshold (the rounding-boundary exemption)."""
+    v32 = np.asarray(v32, dtype=np.float32)
+    inv = (np.float32(1.0) / np.asarray(rho, np.float32)).astype(np.float32)
+    u = (v32 * inv[:, None]).astype(np.float32).astype(np.float64)
+    t = np.asarray(thr32, np.float64)
+    i = np.clip(np.searchsorted(t, u), 1, t.size - 1) if t.size > 1 else np.zeros(u.shape, np.int64)
+    near = np.minimum(np.abs(u - t[i]), np.abs(u - t[np.maximum(i - 1, 0)]))
+    return near <= 1e-6 * np.abs(u)
 
 
 def quant_token_lm(v32: np.ndarray, thr32: np.ndarray):

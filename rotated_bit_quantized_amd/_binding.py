@@ -12,6 +12,7 @@ import ctypes
 import os
 from typing import Optional
 
+import numpy as np
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -21,7 +22,7 @@ OQ_OK, OQ_ERR_INVALID_ARG, OQ_ERR_UNSUPPORTED, OQ_ERR_ALIGNMENT, OQ_ERR_WORKSPAC
 OQ_ROT_RPBH, OQ_ROT_DENSE32 = 1, 2
 OQ_A8, OQ_A6, OQ_A4, OQ_MXFP4 = 8, 6, 4, 0x104
 OQ_W4, OQ_W_MXFP4 = 4, 0x104
-OQ_OP_GEMM_W4A8, OQ_OP_GEMM_W4A4, OQ_OP_LINEAR = 1, 2, 3
+OQ_OP_GEMM_W4A8, OQ_OP_GEMM_W4A4, OQ_OP_LINEAR, OQ_OP_GEMM_LM = 1, 2, 3, 4
 OQ_TILED = 0x10000
 OQ_SCALE_PCTL = 0x20000
 
@@ -64,6 +65,14 @@ def _load():
         "oq_prepack_w4": ([vp, vp, i32, i32, i32, vp, vp, vp], ctypes.c_int),
         "oq_tiled_mx_bytes": ([i64, i32], sz),
         "oq_prepack_mx": ([vp, vp, i32, i32, vp, vp, vp], ctypes.c_int),
+        "oq_lloyd_max_levels": ([i32, i32, vp], ctypes.c_int),
+        "oq_lloyd_max_tables": ([i32, i32, vp, vp], ctypes.c_int),
+        "oq_tiled_f16_bytes": ([i64, i32], sz),
+        "oq_quant_act_lm": ([vp, i64, i32, i64, vp, ctypes.c_int, i32, ctypes.c_int, vp, vp, vp, i64, vp, vp, vp],
+                            ctypes.c_int),
+        "oq_prepack_w16": ([vp, vp, i32, i32, i32, vp, vp], ctypes.c_int),
+        "oq_gemm_lm": ([i32, ctypes.c_int, vp, i64, vp, i64, i32, vp, vp, i32, vp, vp, vp, vp, i64, vp, sz, vp],
+                       ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -75,7 +84,8 @@ def _load():
 _lib = _load()
 EXPORTED = ("oq_last_error", "oq_center", "oq_rotate", "oq_quant_act", "oq_quant_weight",
             "oq_gemm_w4a8", "oq_gemm_w4a4", "oq_linear_fused", "oq_workspace_bytes", "oq_tiled_bytes",
-            "oq_prepack_w4", "oq_tiled_mx_bytes", "oq_prepack_mx")
+            "oq_prepack_w4", "oq_tiled_mx_bytes", "oq_prepack_mx", "oq_lloyd_max_levels", "oq_lloyd_max_tables",
+            "oq_tiled_f16_bytes", "oq_quant_act_lm", "oq_prepack_w16", "oq_gemm_lm")
 
 
 def lib():
@@ -280,4 +290,74 @@ def oq_linear_fused(x, rot: Optional[Rotation], center: bool, afmt: int, w, w_sc
         ws = torch.empty(max(1, oq_workspace_bytes(OQ_OP_LINEAR, M, K, N, afmt)), dtype=torch.uint8, device=dev)
     _check(_lib.oq_linear_fused(_p(x), M, K, x.stride(0), _rref(rot), int(center), afmt, _p(w), _p(w_scale), N,
                                 group, _p(w1), _p(bias), _p(y), y.stride(0), _p(ws), ws.numel(), _stream()))
+    return y
+
+
+# ---------------------------------------------------------------- Lloyd-Max path
+def oq_lloyd_max_levels(d: int, bits: int) -> np.ndarray:
+    """Host call: float64 levels [2^bits] of the Lloyd-Max codebook for width d."""
+    out = np.zeros(1 << bits, dtype=np.float64)
+    _check(_lib.oq_lloyd_max_levels(d, bits, out.ctypes.data_as(ctypes.c_void_p)))
+    return out
+
+
+def oq_lloyd_max_tables(d: int, bits: int):
+    """Host call: (float16 level bits uint16 [2^bits], float32 thresholds [2^bits - 1])."""
+    lv = np.zeros(1 << bits, dtype=np.uint16)
+    thr = np.zeros((1 << bits) - 1, dtype=np.float32)
+    _check(_lib.oq_lloyd_max_tables(d, bits, lv.ctypes.data_as(ctypes.c_void_p),
+                                    thr.ctypes.data_as(ctypes.c_void_p)))
+    return lv, thr
+
+
+def oq_tiled_f16_bytes(rows: int, K: int) -> int:
+    return int(_lib.oq_tiled_f16_bytes(rows, K))
+
+
+def oq_quant_act_lm(x, rot: Optional[Rotation], bits: int, levels, thresholds, tiled: bool = False,
+                    center: bool = False, codes=None, scale=None, mean=None):
+    """levels: device uint16/int16 float16 bits [2^bits]; thresholds: device float32."""
+    x = _bits16(x)
+    M, d = x.shape
+    dev = _dev(x)
+    if codes is None and tiled:
+        codes = torch.empty(max(16, oq_tiled_f16_bytes(M, d)), dtype=torch.uint8, device=dev)
+    elif codes is None:
+        codes = torch.empty((M, d // 2 if bits <= 4 else d), dtype=torch.uint8, device=dev)
+    if scale is None:
+        scale = torch.empty(M, dtype=torch.float32, device=dev)
+    if center and mean is None:
+        mean = torch.empty(M, dtype=torch.float32, device=dev)
+    ldc = 0 if tiled else codes.stride(0) * codes.element_size()
+    _check(_lib.oq_quant_act_lm(_p(x), M, d, x.stride(0), _rref(rot), int(center), bits, int(tiled), _p(levels),
+                                _p(thresholds), _p(codes), ldc, _p(scale), _p(mean), _stream()))
+    return {"codes": codes, "scale": scale, "mean": mean}
+
+
+def oq_prepack_w16(w, w_scale, N: int, K: int, group: int, w16=None):
+    dev = _dev(w)
+    if w16 is None:
+        w16 = torch.empty(max(16, oq_tiled_f16_bytes(N, K)) // 2, dtype=torch.int16, device=dev)
+    _check(_lib.oq_prepack_w16(_p(w), _p(w_scale), N, K, group, _p(w16), _stream()))
+    return w16
+
+
+def oq_gemm_lm(bits: int, qa, a_scale, w16, N: int, levels=None, tiled: bool = False, mean=None, w1=None,
+               bias=None, y=None, ws=None, M: Optional[int] = None, K: Optional[int] = None):
+    if tiled:
+        if M is None or K is None:
+            raise OQError(OQ_ERR_INVALID_ARG, "tiled operands need explicit M and K")
+        lda = 0
+    else:
+        M = qa.shape[0]
+        K = qa.shape[1] * (2 if bits <= 4 else 1)
+        lda = qa.stride(0) * qa.element_size()
+        if ws is None:
+            ws = torch.empty(max(16, oq_workspace_bytes(OQ_OP_GEMM_LM, M, K, N, 0)), dtype=torch.uint8,
+                             device=_dev(qa))
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=_dev(qa))
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(_lib.oq_gemm_lm(bits, int(tiled), _p(qa), lda, _p(a_scale), M, K, _p(levels), _p(w16), N, _p(mean),
+                           _p(w1), _p(bias), _p(y), y.stride(0), _p(ws), wsb, _stream()))
     return y

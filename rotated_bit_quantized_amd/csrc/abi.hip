@@ -122,6 +122,46 @@ int pctl_setup(const char *fn, int afmt, int d, PctlArgs *pa) {
   return OQ_OK;
 }
 
+// float64 -> float16 bits, round to nearest even (host)
+uint16_t f64_to_f16_rne(double x) {
+  const uint16_t sign = std::signbit(x) ? 0x8000u : 0u;
+  const double a = std::fabs(x);
+  if (a == 0.0) return sign;
+  if (!(a < 65520.0)) return sign | 0x7C00u;  // rounds to infinity (or NaN input)
+  int e;
+  (void)std::frexp(a, &e);                       // a = m 2^e, m in [0.5, 1)
+  int E = e - 1;                                 // a = 1.f 2^E
+  const int qexp = (E < -14 ? -14 : E) - 10;     // value of the last float16 bit
+  const double r = std::nearbyint(std::ldexp(a, -qexp));  // exact scaling, RNE (default mode)
+  uint32_t bits;
+  if (E < -14) {
+    bits = (uint32_t)r;  // subnormal; r == 1024 is the smallest normal
+  } else {
+    double rr = r;
+    if (rr >= 2048.0) {
+      rr *= 0.5;
+      ++E;
+    }
+    if (E > 15) return sign | 0x7C00u;
+    bits = ((uint32_t)(E + 15) << 10) | ((uint32_t)rr - 1024u);
+  }
+  return sign | (uint16_t)bits;
+}
+
+float f16_to_f32(uint16_t h) {
+  const uint32_t e = (h >> 10) & 0x1F, m = h & 0x3FF;
+  float v;
+  if (e == 0) v = std::ldexp((float)m, -24);
+  else if (e == 31) v = m ? NAN : INFINITY;
+  else v = std::ldexp((float)(m | 0x400), (int)e - 25);
+  return (h & 0x8000) ? -v : v;
+}
+
+int check_lm_bits(const char *fn, int bits) {
+  if (bits < 1 || bits > 8) return fail(OQ_ERR_UNSUPPORTED, "%s: bits=%d must be in [1, 8]", fn, bits);
+  return OQ_OK;
+}
+
 size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct LinearWs {
@@ -416,7 +456,9 @@ int oq_prepack_mx(const uint8_t *w, const uint8_t *w_e8m0, int32_t N, int32_t K,
 
 size_t oq_workspace_bytes(int op, int64_t M, int32_t K, int32_t N, int afmt) {
   (void)N;
-  if (op != OQ_OP_LINEAR || M < 0 || K <= 0) return 0;
+  if (M < 0 || K <= 0) return 0;
+  if (op == OQ_OP_GEMM_LM) return (afmt & OQ_TILED) ? 0 : (size_t)tiled_f16_bytes(M, K);
+  if (op != OQ_OP_LINEAR) return 0;
   return linear_ws(M, K, afmt & ~OQ_SCALE_PCTL).total;
 }
 
@@ -526,4 +568,122 @@ int oq_linear_fused(const uint16_t *x, int64_t M, int32_t K, int64_t ldx, const 
                     fn);
 }
 
+// ------------------------------------------------------------ Lloyd-Max path
+int oq_lloyd_max_levels(int32_t d, int32_t bits, double *levels) {
+  int rc = check_lm_bits("oq_lloyd_max_levels", bits);
+  if (rc) return rc;
+  if (d < 3) return fail(OQ_ERR_INVALID_ARG, "oq_lloyd_max_levels: d=%d must be >= 3", d);
+  if (!levels) return fail(OQ_ERR_INVALID_ARG, "oq_lloyd_max_levels: levels is NULL");
+  const double res = lloyd_max_solve(d, bits, levels);
+  if (!(res >= 0.0) || res > 1e-10)
+    return fail(OQ_ERR_UNSUPPORTED, "oq_lloyd_max_levels: no convergence for d=%d bits=%d (residual %g)", d, bits, res);
+  g_err[0] = 0;
+  return OQ_OK;
+}
+
+int oq_lloyd_max_tables(int32_t d, int32_t bits, uint16_t *levels_f16, float *thresholds) {
+  if (!levels_f16 || !thresholds) return fail(OQ_ERR_INVALID_ARG, "oq_lloyd_max_tables: NULL output");
+  int rc = check_lm_bits("oq_lloyd_max_tables", bits);
+  if (rc) return rc;
+  double lv[256];
+  rc = oq_lloyd_max_levels(d, bits, lv);
+  if (rc) return rc;
+  const int L = 1 << bits;
+  for (int i = 0; i < L; ++i) levels_f16[i] = f64_to_f16_rne(lv[i]);
+  for (int i = 0; i + 1 < L; ++i) {
+    const float a = f16_to_f32(levels_f16[i]), b = f16_to_f32(levels_f16[i + 1]);
+    if (!(a < b)) return fail(OQ_ERR_UNSUPPORTED, "oq_lloyd_max_tables: float16 levels %d, %d coincide", i, i + 1);
+    thresholds[i] = (a + b) * 0.5f;
+    if ((double)thresholds[i] != 0.5 * ((double)a + (double)b))
+      return fail(OQ_ERR_UNSUPPORTED, "oq_lloyd_max_tables: midpoint %d is not exact in float32", i);
+  }
+  g_err[0] = 0;
+  return OQ_OK;
+}
+
+size_t oq_tiled_f16_bytes(int64_t rows, int32_t K) {
+  if (rows < 0 || K <= 0 || K % 16) return 0;
+  return (size_t)tiled_f16_bytes(rows, K);
+}
+
+int oq_quant_act_lm(const uint16_t *x, int64_t M, int32_t d, int64_t ldx, const oq_rot *rot, int center,
+                    int32_t bits, int tiled, const uint16_t *levels_f16, const float *thresholds, void *codes,
+                    int64_t ldc_bytes, float *scale, float *mean, hipStream_t stream) {
+  const char *fn = "oq_quant_act_lm";
+  int rc = check_x(fn, x, M, d, ldx);
+  if (rc) return rc;
+  rc = check_lm_bits(fn, bits);
+  if (rc) return rc;
+  if (!rpbh_wave_supported(d)) return fail(OQ_ERR_UNSUPPORTED, "%s: d=%d must be at most 4096", fn, d);
+  if (M == 0) return OQ_OK;
+  if (!codes || !scale) return fail(OQ_ERR_INVALID_ARG, "%s: codes or scale is NULL", fn);
+  if (!levels_f16 || !thresholds) return fail(OQ_ERR_INVALID_ARG, "%s: the codebook tables are NULL", fn);
+  if ((reinterpret_cast<uintptr_t>(levels_f16) & 1) || (reinterpret_cast<uintptr_t>(thresholds) & 3))
+    return fail(OQ_ERR_ALIGNMENT, "%s: codebook tables misaligned", fn);
+  if (!al16(codes)) return fail(OQ_ERR_ALIGNMENT, "%s: codes must be 16-byte aligned", fn);
+  if (!tiled) {
+    if (ldc_bytes % 16) return fail(OQ_ERR_ALIGNMENT, "%s: code rows must be 16-byte aligned", fn);
+    if (ldc_bytes < (bits <= 4 ? d / 2 : d)) return fail(OQ_ERR_INVALID_ARG, "%s: ldc_bytes too small", fn);
+  }
+  if (center && !mean) return fail(OQ_ERR_INVALID_ARG, "%s: centering needs mean", fn);
+  RotArgs ra;
+  rc = rot_args(fn, rot, d, &ra);
+  if (rc) return rc;
+  const LmArgs la{bits, thresholds, levels_f16};
+  const int mode = tiled ? OUT_LMF16 : (bits <= 4 ? OUT_LM4 : OUT_LM8);
+  g_err[0] = 0;
+  return hip_status(launch_rpbh_quant(x, M, d, ldx, ra, center ? 1 : 0, mean, mode, 0, codes, tiled ? 0 : ldc_bytes,
+                                      scale, stream, nullptr, &la),
+                    fn);
+}
+
+int oq_prepack_w16(const uint8_t *w, const float *w_scale, int32_t N, int32_t K, int32_t group, uint16_t *w16_tiled,
+                   hipStream_t stream) {
+  const char *fn = "oq_prepack_w16";
+  if (N < 0) return fail(OQ_ERR_INVALID_ARG, "%s: N < 0", fn);
+  if (K <= 0 || K % 32) return fail(OQ_ERR_UNSUPPORTED, "%s: K=%d must be a positive multiple of 32", fn, K);
+  if (group < 32 || group % 32 || K % group)
+    return fail(OQ_ERR_UNSUPPORTED, "%s: group=%d must be a multiple of 32 dividing K=%d", fn, group, K);
+  if (N > 0 && (!w || !w_scale || !w16_tiled)) return fail(OQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (!al16(w) || !al16(w16_tiled)) return fail(OQ_ERR_ALIGNMENT, "%s: misaligned", fn);
+  g_err[0] = 0;
+  return hip_status(launch_prepack_w16(w, w_scale, N, K, group, reinterpret_cast<uint8_t *>(w16_tiled), stream), fn);
+}
+
+int oq_gemm_lm(int32_t bits, int tiled, const void *qa, int64_t lda_bytes, const float *a_scale, int64_t M,
+               int32_t K, const uint16_t *levels_f16, const uint16_t *w16_tiled, int32_t N, const float *mean,
+               const float *w1, const float *bias, uint16_t *y, int64_t ldy, void *ws, size_t ws_bytes,
+               hipStream_t stream) {
+  const char *fn = "oq_gemm_lm";
+  int rc = check_lm_bits(fn, bits);
+  if (rc) return rc;
+  if (M < 0 || N < 0) return fail(OQ_ERR_INVALID_ARG, "%s: negative M or N", fn);
+  if (K <= 0 || K % 32) return fail(OQ_ERR_UNSUPPORTED, "%s: K=%d must be a positive multiple of 32", fn, K);
+  if ((mean == nullptr) != (w1 == nullptr)) return fail(OQ_ERR_INVALID_ARG, "%s: mean and w1 must be given together", fn);
+  if (M == 0 || N == 0) return OQ_OK;
+  if (!qa || !a_scale || !w16_tiled || !y) return fail(OQ_ERR_INVALID_ARG, "%s: NULL operand", fn);
+  if (!al16(qa) || !al16(w16_tiled)) return fail(OQ_ERR_ALIGNMENT, "%s: operands must be 16-byte aligned", fn);
+  if (ldy < N) return fail(OQ_ERR_INVALID_ARG, "%s: ldy=%lld < N=%d", fn, (long long)ldy, N);
+  if (reinterpret_cast<uintptr_t>(y) & 1) return fail(OQ_ERR_ALIGNMENT, "%s: y misaligned", fn);
+  const uint8_t *A = static_cast<const uint8_t *>(qa);
+  g_err[0] = 0;
+  if (!tiled) {
+    if (lda_bytes % 16 || lda_bytes < (bits <= 4 ? K / 2 : K))
+      return fail(OQ_ERR_INVALID_ARG, "%s: lda_bytes must be a multiple of 16 covering a row of codes", fn);
+    if (!levels_f16 || (reinterpret_cast<uintptr_t>(levels_f16) & 1))
+      return fail(OQ_ERR_INVALID_ARG, "%s: canonical codes need the float16 levels", fn);
+    const size_t need = (size_t)tiled_f16_bytes(M, K);
+    if (!ws || ws_bytes < need || !al16(ws))
+      return fail(OQ_ERR_WORKSPACE, "%s: workspace of %zu bytes (16-byte aligned) needed", fn, need);
+    rc = hip_status(launch_lm_expand(A, lda_bytes, bits <= 4, levels_f16, 1 << bits, M, K,
+                                     static_cast<uint8_t *>(ws), stream), fn);
+    if (rc) return rc;
+    A = static_cast<const uint8_t *>(ws);
+  }
+  return hip_status(launch_gemm_f16(A, a_scale, M, K, reinterpret_cast<const uint8_t *>(w16_tiled), N, mean, w1,
+                                    bias, y, ldy, stream),
+                    fn);
+}
+
 }  // extern "C"
+

@@ -1,0 +1,314 @@
+// Lloyd-Max activation GEMM on the gfx950 float16 MFMA, with the weight
+// prepack and the code -> level expansion that produce its operands.
+//
+// Arithmetic (OrbitQuant PR #25, "Default changes": Lloyd-Max activation
+// codes; CentriQ Eq. 5 / Eq. 9 for the scale and rank-1 epilogue):
+//   y[t][o] = bf16( rho_t * sum_k A16[t][k] W16[o][k] + m_t w1[o] + b[o] )
+// A16 is the float16 level of each activation code, W16 = RN16(s q) the
+// dequantized INT4 weight (code q, group scale s).  A float16 x float16
+// product is exact in float32; v_mfma_f32_32x32x16_f16 sums the products in
+// float32, so the only roundings are the accumulation's and the epilogue's.
+//
+// Tiled operand layout (rows padded to a multiple of 32, K a multiple of 16):
+// chunk (r / 32, k / 16) is 1 KiB; lane l of an MFMA fragment (row l % 32,
+// k 8 (l / 32) .. + 7) finds its 8 float16 at chunk + 16 l, so a fragment is
+// one 16-byte LDS read per lane, conflict-free.
+//
+// Workgroup 256 x 256 outputs, 8 wavefronts in a 2 x 4 grid, each 128 x 64
+// (4 x 2 MFMA tiles accumulated in place).  k advances in stages of 32 (two
+// chunks per 32-row block): every wave copies 4 KiB of each stage global ->
+// LDS with global_load_lds_dwordx4 into a 4-slot ring, one barrier per stage.
+#include "oq_internal.h"
+
+namespace oq {
+namespace {
+
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+constexpr int F16_BM = 256, F16_BN = 256;
+constexpr int F16_KC = 2;  // 16-wide chunks per stage
+constexpr int F16_NSLOT = 4;
+constexpr int F16_A_BYTES = (F16_BM / 32) * F16_KC * 1024;
+constexpr int F16_B_BYTES = (F16_BN / 32) * F16_KC * 1024;
+constexpr int F16_STAGE = F16_A_BYTES + F16_B_BYTES;
+constexpr int F16_ROWS_OFF = F16_NSLOT * F16_STAGE;
+constexpr int F16_LDS = F16_ROWS_OFF + 2 * F16_BM * 4;
+constexpr int F16_SROW = 144;  // padded bytes per staged output row of 64 bf16
+constexpr int F16_PER_STAGE = 4;
+static_assert(8 * F16_PER_STAGE * 1024 == F16_STAGE, "every wave copies 4 KiB of a stage");
+static_assert(8 * 32 * F16_SROW <= F16_ROWS_OFF, "the epilogue staging fits in the ring");
+
+template <int C>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (C & 0xF) | ((C >> 4) << 14));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+gemm_f16_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_scale, int64_t M, int K,
+                const uint8_t *__restrict__ W, int N, int Np, const float *__restrict__ mean,
+                const float *__restrict__ w1, const float *__restrict__ bias, uint16_t *__restrict__ y, int64_t ldy) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const uint32_t lds0 = lds_addr_of(smem);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int KCH = K / 16;
+  const int S = KCH / F16_KC;
+  const int64_t m0 = (int64_t)blockIdx.y * F16_BM;
+  const int n0 = blockIdx.x * F16_BN;
+  const int64_t mblocks = (M + 31) / 32;
+  const int nblocks = Np / 32;
+
+  // copy units of this wave: u = wave + 8 q; units 0..15 are A chunks (row
+  // block u / 2, chunk u % 2 of the stage), 16..31 the same for W; unit u
+  // lands at 1 KiB * u of the slot.  Blocks past the operand end re-read
+  // the last block (their outputs are never stored).
+  const uint8_t *cptr[F16_PER_STAGE];
+  uint32_t clds[F16_PER_STAGE];
+#pragma unroll
+  for (int q = 0; q < F16_PER_STAGE; ++q) {
+    const int u = wave + 8 * q;
+    if (u < 16) {
+      int64_t rb = m0 / 32 + u / 2;
+      if (rb > mblocks - 1) rb = mblocks - 1;
+      cptr[q] = A + (rb * KCH + u % 2) * 1024 + 16 * lane;
+    } else {
+      const int uu = u - 16;
+      int cb = n0 / 32 + uu / 2;
+      if (cb > nblocks - 1) cb = nblocks - 1;
+      cptr[q] = W + ((int64_t)cb * KCH + uu % 2) * 1024 + 16 * lane;
+    }
+    clds[q] = 1024u * u;
+  }
+  auto issue = [&](int slot, int st) {
+    const uint32_t base = lds0 + slot * F16_STAGE;
+#pragma unroll
+    for (int q = 0; q < F16_PER_STAGE; ++q) dma_lds16(cptr[q] + (int64_t)st * (F16_KC * 1024), base + clds[q]);
+  };
+
+  float *lds_alpha = reinterpret_cast<float *>(smem + F16_ROWS_OFF);
+  float *lds_mean = lds_alpha + F16_BM;
+  for (int t = threadIdx.x; t < F16_BM; t += 512) {
+    const int64_t row = m0 + t;
+    lds_alpha[t] = row < M ? a_scale[row] : 0.f;
+    lds_mean[t] = (mean && row < M) ? mean[row] : 0.f;
+  }
+
+  const int wm = wave >> 2, wn = wave & 3;
+  const int r = lane & 31, half = lane >> 5;
+  v16f acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = (v16f){};
+
+#pragma unroll
+  for (int p = 0; p < F16_NSLOT - 1; ++p)
+    if (p < S) issue(p, p);
+
+  for (int g = 0; g < S; ++g) {
+    // this wave's copies of stage g are done once at most the stages issued
+    // after it (g + 1, g + 2) are outstanding; this wave's LDS reads of stage
+    // g - 1 are done; after the barrier every wave's are, so stage g is
+    // visible and the slot of stage g - 1 can be refilled with g + 3
+    if (g + 2 < S) wait_vm<2 * F16_PER_STAGE>();
+    else if (g + 1 < S) wait_vm<F16_PER_STAGE>();
+    else wait_vm<0>();
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+    if (g + F16_NSLOT - 1 < S) issue((g + F16_NSLOT - 1) % F16_NSLOT, g + F16_NSLOT - 1);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint8_t *sa = smem + (g % F16_NSLOT) * F16_STAGE + 16 * lane;
+#pragma unroll
+    for (int kc = 0; kc < F16_KC; ++kc) {
+      v8h a[4], b[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const v8h *>(sa + ((wm * 4 + i) * F16_KC + kc) * 1024);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        b[j] = *reinterpret_cast<const v8h *>(sa + F16_A_BYTES + ((wn * 2 + j) * F16_KC + kc) * 1024);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // ---- epilogue: y = rho F + m w1 + b, bf16, staged per 32-row slab in this
+  // wave's own LDS area (the ring is free once every wave has passed the
+  // barrier) so that the global writes are 16-byte runs
+  __syncthreads();
+  float w1v[2] = {0.f, 0.f}, bv[2] = {0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int col = n0 + wn * 64 + 32 * j + r;
+    if (col < N) {
+      if (mean) w1v[j] = w1[col];
+      if (bias) bv[j] = bias[col];
+    }
+  }
+  uint8_t *stg = smem + wave * (32 * F16_SROW);
+  const bool vec_ok = ((reinterpret_cast<uintptr_t>(y) & 15) == 0) && (ldy % 8 == 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      // rows e4 * 8 + half * 4 + 0..3 of this 32-row slab
+      const int rl = wm * 128 + 32 * i + e4 * 8 + half * 4;
+      const float4 al4 = *reinterpret_cast<const float4 *>(lds_alpha + rl);
+      const float4 mu4 = *reinterpret_cast<const float4 *>(lds_mean + rl);
+      const float al[4] = {al4.x, al4.y, al4.z, al4.w}, mu[4] = {mu4.x, mu4.y, mu4.z, mu4.w};
+#pragma unroll
+      for (int e1 = 0; e1 < 4; ++e1) {
+        const int e = 4 * e4 + e1;
+        const int rr = e4 * 8 + half * 4 + e1;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          float v = al[e1] * acc[i][j][e];
+          if (mean) v = __builtin_fmaf(mu[e1], w1v[j], v);
+          if (bias) v = v + bv[j];
+          *reinterpret_cast<uint16_t *>(stg + rr * F16_SROW + (32 * j + r) * 2) = f32_to_bf16_rne(v);
+        }
+      }
+    }
+    const int cl = (lane & 7) * 8;
+    const int col = n0 + wn * 64 + cl;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int rr = (lane >> 3) + 8 * q;
+      const int64_t row = m0 + wm * 128 + 32 * i + rr;
+      const uint4 v = *reinterpret_cast<const uint4 *>(stg + rr * F16_SROW + cl * 2);
+      if (row >= M) continue;
+      uint16_t *dst = y + row * ldy + col;
+      if (vec_ok && col + 8 <= N) {
+        *reinterpret_cast<uint4 *>(dst) = v;
+      } else {
+        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          if (col + c < N) dst[c] = (uint16_t)(wv[c >> 1] >> (16 * (c & 1)));
+      }
+    }
+  }
+}
+
+// RN16(s * q) for an INT4 code q: the float32 product is made round-to-odd
+// (truncated toward zero, last bit set when inexact, the error coming exact
+// from an fma), and float32 has 13 bits more than float16, so rounding that
+// to float16 rounds the exact product once.
+__device__ __forceinline__ uint32_t rn16_scaled(float s, int q) {
+  const float fq = (float)q;
+  const float p = s * fq;
+  const float e = __builtin_fmaf(s, fq, -p);
+  uint32_t b = __float_as_uint(p);
+  if (e != 0.f) {
+    if ((e < 0.f) != (p < 0.f)) b -= 1u;  // |s q| < |p|: step toward zero
+    b |= 1u;
+  }
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)__uint_as_float(b));
+}
+
+// canonical INT4 nibbles + scales [N][K / group] -> W16 tiled [Np / 32][K / 16][1 KiB]
+// one thread per 16-byte lane piece; consecutive threads write consecutive pieces
+__global__ void prepack_w16_kernel(const uint8_t *__restrict__ w, const float *__restrict__ ws, int N, int Np, int K,
+                                   int group, uint8_t *__restrict__ out) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int KCH = K / 16;
+  const int64_t total = (int64_t)(Np / 32) * KCH * 64;
+  if (idx >= total) return;
+  const int l = (int)(idx & 63);
+  const int64_t cc = idx >> 6;
+  const int ch = (int)(cc % KCH);
+  const int64_t cb = cc / KCH;
+  const int64_t o = cb * 32 + (l & 31);
+  const int k0 = ch * 16 + 8 * (l >> 5);
+  uint32_t hv[4] = {0u, 0u, 0u, 0u};
+  if (o < N) {
+    const uint32_t nib = *reinterpret_cast<const uint32_t *>(w + o * (K / 2) + k0 / 2);
+    const float s = ws[o * (K / group) + k0 / group];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      int q = (int)((nib >> (4 * j)) & 0xF);
+      q = q >= 8 ? q - 16 : q;
+      hv[j >> 1] |= rn16_scaled(s, q) << (16 * (j & 1));
+    }
+  }
+  *reinterpret_cast<uint4 *>(out + idx * 16) = make_uint4(hv[0], hv[1], hv[2], hv[3]);
+}
+
+// canonical Lloyd-Max codes (nibbles or bytes, [M][ldc]) -> tiled float16
+// levels [Mp / 32][K / 16][1 KiB]; padding rows get zeros
+__global__ void lm_expand_kernel(const uint8_t *__restrict__ codes, int64_t ldc, int nibbles,
+                                 const uint16_t *__restrict__ levels, int nlev, int64_t M, int K,
+                                 uint8_t *__restrict__ out) {
+  __shared__ uint16_t lv[256];
+  for (int t = threadIdx.x; t < 256; t += blockDim.x) lv[t] = t < nlev ? levels[t] : (uint16_t)0;
+  __syncthreads();
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int KCH = K / 16;
+  const int64_t total = (M + 31) / 32 * KCH * 64;
+  if (idx >= total) return;
+  const int l = (int)(idx & 63);
+  const int64_t cc = idx >> 6;
+  const int ch = (int)(cc % KCH);
+  const int64_t row = (cc / KCH) * 32 + (l & 31);
+  const int k0 = ch * 16 + 8 * (l >> 5);
+  uint32_t hv[4] = {0u, 0u, 0u, 0u};
+  if (row < M) {
+    uint32_t c[8];
+    if (nibbles) {
+      const uint32_t wd = *reinterpret_cast<const uint32_t *>(codes + row * ldc + k0 / 2);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) c[j] = (wd >> (4 * j)) & 0xFu;
+    } else {
+      const uint2 wd = *reinterpret_cast<const uint2 *>(codes + row * ldc + k0);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) c[j] = ((j < 4 ? wd.x : wd.y) >> (8 * (j & 3))) & 0xFFu;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) hv[j >> 1] |= (uint32_t)lv[c[j]] << (16 * (j & 1));
+  }
+  *reinterpret_cast<uint4 *>(out + idx * 16) = make_uint4(hv[0], hv[1], hv[2], hv[3]);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_f16(const uint8_t *A, const float *a_scale, int64_t M, int K, const uint8_t *W, int N,
+                           const float *mean, const float *w1, const float *bias, uint16_t *y, int64_t ldy,
+                           hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  const int Np = (N + 31) / 32 * 32;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void *)gemm_f16_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       F16_LDS);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  dim3 grid((unsigned)((N + F16_BN - 1) / F16_BN), (unsigned)((M + F16_BM - 1) / F16_BM));
+  hipLaunchKernelGGL(gemm_f16_kernel, grid, dim3(512), F16_LDS, stream, A, a_scale, M, K, W, N, Np, mean, w1, bias, y,
+                     ldy);
+  return hipGetLastError();
+}
+
+hipError_t launch_prepack_w16(const uint8_t *w, const float *ws, int N, int K, int group, uint8_t *out,
+                              hipStream_t stream) {
+  if (N == 0) return hipSuccess;
+  const int Np = (N + 31) / 32 * 32;
+  const int64_t total = (int64_t)(Np / 32) * (K / 16) * 64;
+  hipLaunchKernelGGL(prepack_w16_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, w, ws, N, Np, K,
+                     group, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_lm_expand(const uint8_t *codes, int64_t ldc, int nibbles, const uint16_t *levels, int nlev,
+                            int64_t M, int K, uint8_t *out, hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  const int64_t total = (M + 31) / 32 * (K / 16) * 64;
+  hipLaunchKernelGGL(lm_expand_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, codes, ldc,
+                     nibbles, levels, nlev, M, K, out);
+  return hipGetLastError();
+}
+
+}  // namespace oq

@@ -319,11 +319,13 @@ hipError_t launch_weight_rpbh(const float *w, int N, int K, int64_t ldw, const R
 
 hipError_t launch_rpbh_quant(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotArgs &rot,
                              int center, float *mean, int out_mode, int qmax, void *out,
-                             int64_t ld_out_bytes, float *scale, hipStream_t stream, const PctlArgs *pctl) {
+                             int64_t ld_out_bytes, float *scale, hipStream_t stream, const PctlArgs *pctl,
+                             const LmArgs *lm) {
   if (M == 0) return hipSuccess;
   if (rpbh_wave_supported(d))
-    return launch_rpbh_wave(x, M, d, ldx, rot, center, mean, out_mode, qmax, out, ld_out_bytes, scale, stream, pctl);
-  if (pctl) return hipErrorInvalidValue;  // the percentile range exists in the wave kernel only
+    return launch_rpbh_wave(x, M, d, ldx, rot, center, mean, out_mode, qmax, out, ld_out_bytes, scale, stream, pctl, lm);
+  // the percentile range and the Lloyd-Max codes exist in the wave kernel only
+  if (pctl || lm || out_mode >= OUT_LM4) return hipErrorInvalidValue;
   switch (rot.rounds) {
     case 0: return launch_mode<0>(out_mode, x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, stream);
     case 1: return launch_mode<1>(out_mode, x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, stream);

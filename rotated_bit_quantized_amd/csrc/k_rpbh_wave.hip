@@ -31,7 +31,13 @@
 //   * the row range (absmax) is a wavefront reduction; with the percentile
 //     range (CentriQ Sec. 4.2 "Scale and grid") each lane keeps its four
 //     largest magnitudes and the wavefront merges those lists, which gives the
-//     order statistics the interpolated 0.9995-quantile needs for d <= 4096.
+//     order statistics the interpolated 0.9995-quantile needs for d <= 4096;
+//   * Lloyd-Max codes (OrbitQuant PR #25, "Default changes"; the codebook of
+//     the post-rotation marginal): the scale is the row's RMS, from a float64
+//     sum of squares reduced over the wavefront, and each code is the number
+//     of thresholds below u = v / rho, found by a binary search of |u| over
+//     the positive thresholds held in LDS (u <= 0 searches with the next
+//     float above |u|, so that a tie goes to the lower level).
 #include "oq_internal.h"
 
 #pragma clang fp contract(off)
@@ -189,12 +195,19 @@ __device__ __forceinline__ void store_fp6_pair(const float (&ta)[16], const floa
 }
 
 // LDS: [offset table: ROUNDS x SLOTS x 4 x 64 lanes x 4 ints][per wave: row copies]
-template <int SLOTS, int ROUNDS>
+// [Lloyd-Max modes: 128 float positive thresholds, 256 float16 levels, when
+// they fit in the 160 KiB; otherwise the kernel reads them from global memory]
+template <int SLOTS, int ROUNDS, bool LM>
 struct WaveLds {
   static constexpr int TABLE = (ROUNDS > 0 ? ROUNDS : 1) * SLOTS * 1024 * 4;
   static constexpr int ROWBUF = (ROUNDS == 2 ? 8 : 4) * SLOTS * 1024;  // 2 copies, float32 if 2 rounds
-  static constexpr int TOTAL = TABLE + WAVES_PER_WG * ROWBUF;
+  static constexpr int LM_OFF = TABLE + WAVES_PER_WG * ROWBUF;
+  static constexpr bool LM_LDS = LM && LM_OFF + 1024 <= 160 * 1024;
+  static constexpr int TOTAL = LM_OFF + (LM_LDS ? 128 * 4 + 256 * 2 : 0);
 };
+
+template <int mode>
+constexpr bool is_lm_mode() { return mode == OUT_LM4 || mode == OUT_LM8 || mode == OUT_LMF16; }
 
 // mode (OUT_*) is a template argument: one kernel body per output keeps the
 // register count of each near what its own path needs.
@@ -203,8 +216,9 @@ __global__ void __launch_bounds__(64 * WAVES_PER_WG)
 rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, const int32_t *__restrict__ perm,
                  const int8_t *__restrict__ signs, int h, float c_h, int pow4, int center,
                  float *__restrict__ mean_out, int qmax, void *__restrict__ out, int64_t ld_out_bytes,
-                 float *__restrict__ scale_out, PctlArgs pa) {
-  using L = WaveLds<SLOTS, ROUNDS>;
+                 float *__restrict__ scale_out, PctlArgs pa, LmArgs la) {
+  constexpr bool LM = is_lm_mode<mode>();
+  using L = WaveLds<SLOTS, ROUNDS, LM>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -282,6 +296,16 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
     for (int e = 0; e < 4; ++e)
       o[e] = i0 < d ? (pv[k][e] + (sv[k][e] < 0 ? d : 0)) * (r == 0 ? 2 : 4) : 0;
     reinterpret_cast<int4 *>(table)[((r * SLOTS + s) * 4 + jq) * 64 + l] = make_int4(o[0], o[1], o[2], o[3]);
+  }
+  // Lloyd-Max tables: pos[j] = thr[hh - 1 + j], j = 1 .. hh - 1 (the
+  // thresholds above the middle one, which is 0), and the levels
+  float *lm_pos = reinterpret_cast<float *>(lds_raw + L::LM_OFF);
+  uint16_t *lm_lv = reinterpret_cast<uint16_t *>(lds_raw + L::LM_OFF + 512);
+  const int hh = LM ? 1 << (la.bits - 1) : 1;
+  if constexpr (L::LM_LDS) {
+    const int t = threadIdx.x;
+    if (t >= 1 && t < hh) lm_pos[t] = la.thr[hh - 1 + t];
+    if (t < 2 * hh) lm_lv[t] = la.levels[t];
   }
   __syncthreads();
 
@@ -415,6 +439,75 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
       continue;
     }
 
+    if constexpr (LM) {
+      // rho = RN32(sqrt(S / d)), S the float64 sum of squares of the rotated
+      // values (c_all^2 exact); u = RN32(v RN32(1 / rho)) with the deferred
+      // factor and lane sign folded into the multiplier (exact)
+      double ss = 0.0;
+#pragma unroll
+      for (int s = 0; s < SLOTS; ++s)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (act[s]) ss += (double)v[s][j] * (double)v[s][j];
+      ss = wave_sum_d(ss);
+      const double c2 = (double)c_all * (double)c_all;
+      const float rho = fmaxf((float)__builtin_sqrt((ss * c2) / (double)d), 1e-10f);
+      if (lane == 0) scale_out[row] = rho;
+      const float inv = __fdiv_rn(1.0f, rho) * (c_all * sg);
+#pragma unroll
+      for (int s = 0; s < SLOTS; ++s) {
+        if (!act[s]) continue;
+        int q[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const float u = v[s][j] * inv;
+          const float au = fabsf(u);
+          const bool pos = u > 0.f;
+          const float key = pos ? au : __uint_as_float(__float_as_uint(au) + 1u);
+          int c = 0;
+#pragma unroll
+          for (int t = 6; t >= 0; --t) {
+            const int st = 1 << t;
+            if (st < hh) {
+              const float pv = L::LM_LDS ? lm_pos[c + st] : la.thr[hh - 1 + c + st];
+              c += pv < key ? st : 0;
+            }
+          }
+          q[j] = pos ? hh + c : hh - 1 - c;
+        }
+        const int base = 1024 * s + 16 * il;
+        char *orow = static_cast<char *>(out) + row * ld_out_bytes;
+        if constexpr (mode == OUT_LM8) {
+          uint32_t wd[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            wd[k] = (uint32_t)q[4 * k] | ((uint32_t)q[4 * k + 1] << 8) | ((uint32_t)q[4 * k + 2] << 16) |
+                    ((uint32_t)q[4 * k + 3] << 24);
+          *reinterpret_cast<uint4 *>(orow + base) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+        } else if constexpr (mode == OUT_LM4) {
+          uint32_t wd[2] = {0u, 0u};
+#pragma unroll
+          for (int j = 0; j < 16; ++j) wd[j >> 3] |= (uint32_t)q[j] << (4 * (j & 7));
+          *reinterpret_cast<uint2 *>(orow + base / 2) = make_uint2(wd[0], wd[1]);
+        } else {
+          // tiled float16: chunk (row / 32, k / 16) with k = base .. base + 15;
+          // values k % 16 < 8 go to lane row % 32, the rest to lane 32 + row % 32
+          uint32_t hv[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const uint32_t lo = L::LM_LDS ? lm_lv[q[2 * k]] : la.levels[q[2 * k]];
+            const uint32_t hi = L::LM_LDS ? lm_lv[q[2 * k + 1]] : la.levels[q[2 * k + 1]];
+            hv[k] = lo | (hi << 16);
+          }
+          char *chunk = static_cast<char *>(out) + ((row >> 5) * (int64_t)(d >> 4) + (base >> 4)) * 1024;
+          const int rr = (int)(row & 31);
+          *reinterpret_cast<uint4 *>(chunk + 16 * rr) = make_uint4(hv[0], hv[1], hv[2], hv[3]);
+          *reinterpret_cast<uint4 *>(chunk + 16 * (32 + rr)) = make_uint4(hv[4], hv[5], hv[6], hv[7]);
+        }
+      }
+      continue;
+    }
+
     float a = 0.f;
     if constexpr (PCTL) {
       // the four largest magnitudes of the row, t[0] >= .. >= t[3]; a lane's
@@ -523,8 +616,9 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
 
 template <int SLOTS, int ROUNDS, int MODE, bool PCTL>
 hipError_t launch_m(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotArgs &rot, int center, float *mean,
-                    int qmax, void *out, int64_t ld_out_bytes, float *scale, const PctlArgs &pa, hipStream_t stream) {
-  using L = WaveLds<SLOTS, ROUNDS>;
+                    int qmax, void *out, int64_t ld_out_bytes, float *scale, const PctlArgs &pa, const LmArgs &la,
+                    hipStream_t stream) {
+  using L = WaveLds<SLOTS, ROUNDS, is_lm_mode<MODE>()>;
   const size_t lds = (size_t)L::TOTAL;
   static bool attr_set = false;
   if (!attr_set && lds > 64 * 1024) {
@@ -541,43 +635,60 @@ hipError_t launch_m(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotA
   const int pow4 = ROUNDS && ((__builtin_ctz((unsigned)h) & 1) == 0);
   hipLaunchKernelGGL((rpbh_wave_kernel<SLOTS, ROUNDS, MODE, PCTL>), dim3((unsigned)grid), dim3(64 * WAVES_PER_WG), lds,
                      stream, x, M, d, ldx, rot.perm, rot.signs, h, rot.c_h, pow4, center, mean, qmax, out,
-                     ld_out_bytes, scale, pa);
+                     ld_out_bytes, scale, pa, la);
   return hipGetLastError();
 }
 
 template <int SLOTS, int ROUNDS, int MODE>
 hipError_t launch_p(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotArgs &rot, int center, float *mean,
-                    int qmax, void *out, int64_t ld_out_bytes, float *scale, const PctlArgs *pctl, hipStream_t stream) {
-  if (pctl) {
-    if constexpr (MODE == OUT_F32) return hipErrorInvalidValue;
-    else return launch_m<SLOTS, ROUNDS, MODE, true>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, *pctl, stream);
+                    int qmax, void *out, int64_t ld_out_bytes, float *scale, const PctlArgs *pctl, const LmArgs *lm,
+                    hipStream_t stream) {
+  const PctlArgs no_p{0, 0.0, 0.0, 1.0};
+  const LmArgs no_lm{1, nullptr, nullptr};
+  if constexpr (is_lm_mode<MODE>()) {
+    if (!lm || pctl) return hipErrorInvalidValue;
+    return launch_m<SLOTS, ROUNDS, MODE, false>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, no_p,
+                                                *lm, stream);
+  } else {
+    if (lm) return hipErrorInvalidValue;
+    if (pctl) {
+      if constexpr (MODE == OUT_F32) return hipErrorInvalidValue;
+      else return launch_m<SLOTS, ROUNDS, MODE, true>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale,
+                                                      *pctl, no_lm, stream);
+    }
+    return launch_m<SLOTS, ROUNDS, MODE, false>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, no_p,
+                                                no_lm, stream);
   }
-  return launch_m<SLOTS, ROUNDS, MODE, false>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale,
-                                              PctlArgs{0, 0.0, 0.0, 1.0}, stream);
 }
 
 template <int SLOTS, int ROUNDS>
 hipError_t launch_w(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotArgs &rot, int center, float *mean,
                     int mode, int qmax, void *out, int64_t ld_out_bytes, float *scale, const PctlArgs *pctl,
-                    hipStream_t stream) {
+                    const LmArgs *lm, hipStream_t stream) {
+#define OQ_MODE_CASE(MD) \
+  case MD: return launch_p<SLOTS, ROUNDS, MD>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, pctl, lm, stream);
   switch (mode) {
-    case OUT_F32: return launch_p<SLOTS, ROUNDS, OUT_F32>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, pctl, stream);
-    case OUT_I8: return launch_p<SLOTS, ROUNDS, OUT_I8>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, pctl, stream);
-    case OUT_I4: return launch_p<SLOTS, ROUNDS, OUT_I4>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, pctl, stream);
-    case OUT_FP6: return launch_p<SLOTS, ROUNDS, OUT_FP6>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, pctl, stream);
-    case OUT_FP6X2: return launch_p<SLOTS, ROUNDS, OUT_FP6X2>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, pctl, stream);
+    OQ_MODE_CASE(OUT_F32)
+    OQ_MODE_CASE(OUT_I8)
+    OQ_MODE_CASE(OUT_I4)
+    OQ_MODE_CASE(OUT_FP6)
+    OQ_MODE_CASE(OUT_FP6X2)
+    OQ_MODE_CASE(OUT_LM4)
+    OQ_MODE_CASE(OUT_LM8)
+    OQ_MODE_CASE(OUT_LMF16)
   }
+#undef OQ_MODE_CASE
   return hipErrorInvalidValue;
 }
 
 template <int SLOTS>
 hipError_t launch_r(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotArgs &rot, int center, float *mean,
                     int mode, int qmax, void *out, int64_t ld_out_bytes, float *scale, const PctlArgs *pctl,
-                    hipStream_t stream) {
+                    const LmArgs *lm, hipStream_t stream) {
   switch (rot.rounds) {
-    case 0: return launch_w<SLOTS, 0>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, pctl, stream);
-    case 1: return launch_w<SLOTS, 1>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, pctl, stream);
-    case 2: return launch_w<SLOTS, 2>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, pctl, stream);
+    case 0: return launch_w<SLOTS, 0>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, pctl, lm, stream);
+    case 1: return launch_w<SLOTS, 1>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, pctl, lm, stream);
+    case 2: return launch_w<SLOTS, 2>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, pctl, lm, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -588,14 +699,15 @@ bool rpbh_wave_supported(int d) { return d >= 16 && d <= 4096 && d % 16 == 0; }
 
 hipError_t launch_rpbh_wave(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotArgs &rot, int center,
                             float *mean, int mode, int qmax, void *out, int64_t ld_out_bytes, float *scale,
-                            hipStream_t stream, const PctlArgs *pctl) {
+                            hipStream_t stream, const PctlArgs *pctl, const LmArgs *lm) {
   if (M == 0) return hipSuccess;
   if (pctl && (pctl->rank < 2 || pctl->rank > 4)) return hipErrorInvalidValue;
+  if (lm && (lm->bits < 1 || lm->bits > 8 || (mode == OUT_LM4 && lm->bits > 4))) return hipErrorInvalidValue;
   switch ((d + 1023) / 1024) {
-    case 1: return launch_r<1>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, pctl, stream);
-    case 2: return launch_r<2>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, pctl, stream);
-    case 3: return launch_r<3>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, pctl, stream);
-    case 4: return launch_r<4>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, pctl, stream);
+    case 1: return launch_r<1>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, pctl, lm, stream);
+    case 2: return launch_r<2>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, pctl, lm, stream);
+    case 3: return launch_r<3>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, pctl, lm, stream);
+    case 4: return launch_r<4>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, pctl, lm, stream);
   }
   return hipErrorInvalidValue;
 }

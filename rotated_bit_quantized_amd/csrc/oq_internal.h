@@ -67,7 +67,15 @@ enum OutMode : int {
   OUT_W4G = 3,   // per-group INT4 codes + scales (offline weight fold)
   OUT_FP6 = 4,   // A4 codes as FP6 E2M3 in the tiled MFMA operand layout
   OUT_FP6X2 = 5, // A6 codes split q = 8 qh + ql into two tiled FP6 planes
+  OUT_LM4 = 6,   // Lloyd-Max level indices, packed two per byte (bits <= 4)
+  OUT_LM8 = 7,   // Lloyd-Max level indices, one byte each (bits <= 8)
+  OUT_LMF16 = 8, // Lloyd-Max levels as float16 in the tiled f16 MFMA layout
 };
+
+// bytes of the tiled float16 operand layout: rows padded to 32, one 1 KiB
+// chunk per (32 rows, 16 k); lane l of a chunk holds row l % 32, k 8 (l / 32)
+// .. + 7 as 8 consecutive float16
+__host__ __device__ inline int64_t tiled_f16_bytes(int64_t rows, int K) { return (rows + 31) / 32 * 32 * (int64_t)K * 2; }
 
 // -------------------------------------------------------- kernel launchers --
 struct RotArgs {
@@ -88,19 +96,30 @@ struct PctlArgs {
   double z;     // Phi^-1((1 + rho) / 2)
 };
 
+// Lloyd-Max codes (OrbitQuant's activation codebook): the token's RMS scale
+// and the nearest of 2^bits stored float16 levels, decided by the float32
+// thresholds between them (ascending, device memory).
+struct LmArgs {
+  int bits;                // 1..8
+  const float *thr;        // [2^bits - 1]
+  const uint16_t *levels;  // [2^bits] float16 bits
+};
+
 // K1: (center) -> RPBH rounds -> (quantize) per token row; pctl selects the
 // percentile range instead of absmax (integer outputs, rows the wave kernel
-// takes only).
+// takes only); the OUT_LM* modes take their codebook from lm (wave kernel
+// only).
 hipError_t launch_rpbh_quant(const uint16_t *x, int64_t M, int d, int64_t ldx,
                              const RotArgs &rot, int center, float *mean,
                              int out_mode, int qmax, void *out, int64_t ld_out_bytes,
-                             float *scale, hipStream_t stream, const PctlArgs *pctl = nullptr);
+                             float *scale, hipStream_t stream, const PctlArgs *pctl = nullptr,
+                             const LmArgs *lm = nullptr);
 
 // K1, one wavefront per row (activation rows of width d <= 4096).
 bool rpbh_wave_supported(int d);
 hipError_t launch_rpbh_wave(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotArgs &rot, int center,
                             float *mean, int mode, int qmax, void *out, int64_t ld_out_bytes, float *scale,
-                            hipStream_t stream, const PctlArgs *pctl = nullptr);
+                            hipStream_t stream, const PctlArgs *pctl = nullptr, const LmArgs *lm = nullptr);
 
 // K2: dense per-32 transform -> (MXFP4 quantize | float32 out); mx_out: 0 float32,
 // 1 row-major codes + E8M0, 2 tiled MXFP4 layout.
@@ -133,6 +152,23 @@ hipError_t launch_prepack_mx(const uint8_t *w, const uint8_t *w_e8m0, int N, int
 // bytes of the tiled MXFP4 codes of `rows` rows (rows padded to 32); the
 // scale words take a sixteenth of that
 inline int64_t tiled_mx_bytes(int64_t rows, int K) { return (rows + 31) / 32 * 32 * (int64_t)(K / 2); }
+
+// Lloyd-Max activation GEMM: tiled float16 levels x tiled W16 (float16 MFMA,
+// float32 sums), epilogue rho F + m w1 + b; K a multiple of 32.
+hipError_t launch_gemm_f16(const uint8_t *A, const float *a_scale, int64_t M, int K, const uint8_t *W, int N,
+                           const float *mean, const float *w1, const float *bias, uint16_t *y, int64_t ldy,
+                           hipStream_t stream);
+// canonical INT4 weights + group scales -> tiled W16 = RN16(s q)
+hipError_t launch_prepack_w16(const uint8_t *w, const float *ws, int N, int K, int group, uint8_t *out,
+                              hipStream_t stream);
+// canonical Lloyd-Max codes -> tiled float16 levels
+hipError_t launch_lm_expand(const uint8_t *codes, int64_t ldc, int nibbles, const uint16_t *levels, int nlev,
+                            int64_t M, int K, uint8_t *out, hipStream_t stream);
+
+// Host: Lloyd-Max levels of the unit-variance sphere marginal of width d
+// (ascending, 2^bits), solved to the fixed point of Lloyd's conditions;
+// returns the final max residual, or a negative value on failure.
+double lloyd_max_solve(int d, int bits, double *levels);
 
 // Offline weight preparation.
 hipError_t launch_weight_rpbh(const float *w, int N, int K, int64_t ldw, const RotArgs &rot,

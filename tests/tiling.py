@@ -98,3 +98,24 @@ def row_mask_mx(R: int, K: int) -> np.ndarray:
     live = (np.arange(Rp) < R).reshape(Rp // 32, 1, 1, 32, 1)
     return np.broadcast_to(live, (Rp // 32, G, 2, 32, 16)).reshape(-1)
 
+
+
+# ---------------------------------------------------------------- float16 tiles
+# Tiled float16 operand layout (include/oq.h, oq_tiled_f16_bytes): rows padded
+# to 32, chunk (r / 32, k / 16) of 512 float16 at ((r / 32) * (K / 16) + k / 16)
+# * 512; lane l = 32 * ((k % 16) // 8) + r % 32 holds k % 8 = 0..7 at 8 l.
+def tile_f16(vals: np.ndarray) -> np.ndarray:
+    """uint16 [R, K] -> tiled uint16 (R padded to 32 with zeros)."""
+    R, K = vals.shape
+    assert K % 16 == 0
+    Rp = (R + 31) // 32 * 32
+    v = np.zeros((Rp, K), dtype=np.uint16)
+    v[:R] = vals
+    return v.reshape(Rp // 32, 32, K // 16, 2, 8).transpose(0, 2, 3, 1, 4).reshape(-1).copy()
+
+
+def untile_f16(buf: np.ndarray, R: int, K: int) -> np.ndarray:
+    """tiled uint16 -> [R padded to 32, K]."""
+    Rp = (R + 31) // 32 * 32
+    b = np.asarray(buf).view(np.uint16)[: Rp * K]
+    return b.reshape(Rp // 32, K // 16, 2, 32, 8).transpose(0, 3, 1, 2, 4).reshape(Rp, K)
