@@ -27,6 +27,7 @@ METRIC = "rotated W4A8/W4A4 linear TOPS + rotate/quant µs/call at 4096 tokens; 
 PEAK_HBM_GBS = 8000.0
 PEAK_INT8_TOPS = 5000.0
 PEAK_FP4_TFLOPS = 10100.0
+PEAK_FP16_TFLOPS = 2500.0
 
 
 def _src_hash(names):
@@ -220,6 +221,60 @@ def _time_pctl(torch, oq, st, reps, warmup):
     return sum(v) / reps, v
 
 
+def _time_lm(torch, oq, WL, bits, reps=40, warmup=5):
+    """Lloyd-Max path on the 4096 x 3072 workload (RPBH h = 1024, one round;
+    outputs 3072 and 12288): the rotate -> Lloyd-Max writer into the tiled
+    float16 operand, then the float16-MFMA GEMM per linear.  Codebook and
+    weight dequantization are offline (untimed)."""
+    wl = WL.make_workload(2)
+    dev = torch.device("cuda:0")
+    M, K = wl.M, wl.K
+    lv, thr = oq.oq_lloyd_max_tables(K, bits)
+    lv_d = torch.from_numpy(lv.view("int16")).to(dev)
+    thr_d = torch.from_numpy(thr).to(dev)
+    rot = oq.Rotation.rpbh(torch.from_numpy(wl.perm).to(dev), torch.from_numpy(wl.signs).to(dev), wl.spec.block)
+    w16 = []
+    for W in wl.weights:
+        q = oq.oq_quant_weight(torch.from_numpy(W).to(dev), rot, oq.OQ_W4, 64)
+        w16.append((W.shape[0], oq.oq_prepack_w16(q["codes"], q["scales"], W.shape[0], K, 64)))
+    x0 = torch.from_numpy(wl.x_bits.view("int16")).to(dev)
+    xs = [x0] + [x0.clone() for _ in range(7)]
+    codes = torch.empty(oq.oq_tiled_f16_bytes(M, K), dtype=torch.uint8, device=dev)
+    scale = torch.empty(M, dtype=torch.float32, device=dev)
+    ys = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for N, _ in w16]
+
+    def launches(i):
+        out = [("rotate_quant", lambda: oq.oq_quant_act_lm(xs[i % len(xs)], rot, bits, lv_d, thr_d, tiled=True,
+                                                           codes=codes, scale=scale))]
+        for (N, w), y in zip(w16, ys):
+            out.append((f"gemm_n{N}", lambda N=N, w=w, y=y: oq.oq_gemm_lm(bits, codes, scale, w, N, tiled=True,
+                                                                           y=y, M=M, K=K)))
+        return out
+
+    for i in range(warmup):
+        for _, f in launches(i):
+            f()
+    torch.cuda.synchronize()
+    names = [n for n, _ in launches(0)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(reps)]
+    for i in range(reps):
+        ev[i][0].record()
+        for k, (_, f) in enumerate(launches(i)):
+            f()
+            ev[i][k + 1].record()
+    torch.cuda.synchronize()
+    per = {n: sum(ev[i][k].elapsed_time(ev[i][k + 1]) for i in range(reps)) / reps for k, n in enumerate(names)}
+    rq_bytes = M * (2 * K + 2 * K + 4)  # bf16 in, float16 levels out, rho
+    e = {"rotate_quant_us": round(per["rotate_quant"] * 1e3, 3),
+         "rotate_quant_hbm_frac": round(rq_bytes / (per["rotate_quant"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    for N, _ in w16:
+        t = per[f"gemm_n{N}"]
+        tf = 2.0 * M * K * N / (t * 1e-3) / 1e12
+        e[f"gemm_n{N}"] = {"us": round(t * 1e3, 2), "TFLOPS": round(tf, 1), "frac_fp16": round(tf / PEAK_FP16_TFLOPS, 4)}
+    e["step_ms"] = round(sum(per.values()), 4)
+    return e
+
+
 def _copy_reference(torch, nbytes=1 << 30, reps=3):
     """A plain device-to-device copy of known size, launched beside the
     profiled kernels so that HBM byte counters can be scaled by what they
@@ -381,6 +436,7 @@ def main():
             e["linear_fused_us"] = {"d_out": nf, "mean": round(fm * 1e3, 3)}
             side[s2.name] = e
         result["other_configs"] = side
+        result["lloyd_max_4096x3072"] = {f"A{b}": _time_lm(torch, oq, WL, b) for b in (4, 8)}
 
     if not args.no_cpu_baseline and not args.only_step:
         result["cpu_baseline"] = _cpu_baseline(WL)
