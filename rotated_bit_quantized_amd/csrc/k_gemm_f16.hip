@@ -27,17 +27,26 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int F16_BM = 256, F16_BN = 256;
-constexpr int F16_KC = 2;  // 16-wide chunks per stage
-constexpr int F16_NSLOT = 4;
-constexpr int F16_A_BYTES = (F16_BM / 32) * F16_KC * 1024;
-constexpr int F16_B_BYTES = (F16_BN / 32) * F16_KC * 1024;
-constexpr int F16_STAGE = F16_A_BYTES + F16_B_BYTES;
-constexpr int F16_ROWS_OFF = F16_NSLOT * F16_STAGE;
-constexpr int F16_LDS = F16_ROWS_OFF + 2 * F16_BM * 4;
 constexpr int F16_SROW = 144;  // padded bytes per staged output row of 64 bf16
-constexpr int F16_PER_STAGE = 4;
-static_assert(8 * F16_PER_STAGE * 1024 == F16_STAGE, "every wave copies 4 KiB of a stage");
-static_assert(8 * 32 * F16_SROW <= F16_ROWS_OFF, "the epilogue staging fits in the ring");
+
+// KC 16-wide chunks per stage, NSLOT stages in the LDS ring
+template <int KC, int NSLOT>
+struct F16C {
+  static constexpr int A_BYTES = (F16_BM / 32) * KC * 1024;
+  static constexpr int B_BYTES = (F16_BN / 32) * KC * 1024;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int ROWS_OFF = NSLOT * STAGE;
+  static constexpr int LDS = ROWS_OFF + 2 * F16_BM * 4;
+  static constexpr int PER_STAGE = 2 * KC;  // 1 KiB copies per wave per stage
+  static_assert(8 * PER_STAGE * 1024 == STAGE, "every wave copies the same share of a stage");
+  static_assert(8 * 32 * F16_SROW <= ROWS_OFF, "the epilogue staging fits in the ring");
+  static_assert(LDS <= 160 * 1024, "LDS");
+  // chunk 0 of stage g + 1 is read during stage g, so stage g + 1 must be in
+  // flight before stage g starts (NSLOT >= 3); the waits below count exactly
+  // for three or four slots
+  static_assert(NSLOT == 3 || NSLOT == 4, "ring depth");
+  static_assert(PER_STAGE * (NSLOT - 2) <= 63, "vmcnt range");
+};
 
 template <int C>
 __device__ __forceinline__ void wait_vm() {
@@ -45,49 +54,51 @@ __device__ __forceinline__ void wait_vm() {
 }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
+template <int KC, int NSLOT>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_f16_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_scale, int64_t M, int K,
                 const uint8_t *__restrict__ W, int N, int Np, const float *__restrict__ mean,
                 const float *__restrict__ w1, const float *__restrict__ bias, uint16_t *__restrict__ y, int64_t ldy) {
+  using C = F16C<KC, NSLOT>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const uint32_t lds0 = lds_addr_of(smem);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int KCH = K / 16;
-  const int S = KCH / F16_KC;
+  const int S = KCH / KC;
   const int64_t m0 = (int64_t)blockIdx.y * F16_BM;
   const int n0 = blockIdx.x * F16_BN;
   const int64_t mblocks = (M + 31) / 32;
   const int nblocks = Np / 32;
 
-  // copy units of this wave: u = wave + 8 q; units 0..15 are A chunks (row
-  // block u / 2, chunk u % 2 of the stage), 16..31 the same for W; unit u
-  // lands at 1 KiB * u of the slot.  Blocks past the operand end re-read
-  // the last block (their outputs are never stored).
-  const uint8_t *cptr[F16_PER_STAGE];
-  uint32_t clds[F16_PER_STAGE];
+  // copy units of this wave: u = wave + 8 q; units 0 .. 8 KC - 1 are A chunks
+  // (row block u / KC, chunk u % KC of the stage), the rest the same for W;
+  // unit u lands at 1 KiB * u of the slot.  Blocks past the operand end
+  // re-read the last block (their outputs are never stored).
+  const uint8_t *cptr[C::PER_STAGE];
+  uint32_t clds[C::PER_STAGE];
 #pragma unroll
-  for (int q = 0; q < F16_PER_STAGE; ++q) {
+  for (int q = 0; q < C::PER_STAGE; ++q) {
     const int u = wave + 8 * q;
-    if (u < 16) {
-      int64_t rb = m0 / 32 + u / 2;
+    if (u < 8 * KC) {
+      int64_t rb = m0 / 32 + u / KC;
       if (rb > mblocks - 1) rb = mblocks - 1;
-      cptr[q] = A + (rb * KCH + u % 2) * 1024 + 16 * lane;
+      cptr[q] = A + (rb * KCH + u % KC) * 1024 + 16 * lane;
     } else {
-      const int uu = u - 16;
-      int cb = n0 / 32 + uu / 2;
+      const int uu = u - 8 * KC;
+      int cb = n0 / 32 + uu / KC;
       if (cb > nblocks - 1) cb = nblocks - 1;
-      cptr[q] = W + ((int64_t)cb * KCH + uu % 2) * 1024 + 16 * lane;
+      cptr[q] = W + ((int64_t)cb * KCH + uu % KC) * 1024 + 16 * lane;
     }
     clds[q] = 1024u * u;
   }
   auto issue = [&](int slot, int st) {
-    const uint32_t base = lds0 + slot * F16_STAGE;
+    const uint32_t base = lds0 + slot * C::STAGE;
 #pragma unroll
-    for (int q = 0; q < F16_PER_STAGE; ++q) dma_lds16(cptr[q] + (int64_t)st * (F16_KC * 1024), base + clds[q]);
+    for (int q = 0; q < C::PER_STAGE; ++q) dma_lds16(cptr[q] + (int64_t)st * (KC * 1024), base + clds[q]);
   };
 
-  float *lds_alpha = reinterpret_cast<float *>(smem + F16_ROWS_OFF);
+  float *lds_alpha = reinterpret_cast<float *>(smem + C::ROWS_OFF);
   float *lds_mean = lds_alpha + F16_BM;
   for (int t = threadIdx.x; t < F16_BM; t += 512) {
     const int64_t row = m0 + t;
@@ -103,35 +114,70 @@ gemm_f16_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_scale
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = (v16f){};
 
+  // A fragment (row block wm * 4 + i, chunk kc) and B fragment (column block
+  // wn * 2 + j, chunk kc) of the stage in slot `slot`
+  const uint8_t *fa = smem + 16 * lane + (wm * 4) * KC * 1024;
+  const uint8_t *fb = smem + 16 * lane + C::A_BYTES + (wn * 2) * KC * 1024;
+  auto load = [&](v8h (&a)[4], v8h (&b)[2], int slot, int kc) {
 #pragma unroll
-  for (int p = 0; p < F16_NSLOT - 1; ++p)
+    for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const v8h *>(fa + slot * C::STAGE + (i * KC + kc) * 1024);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) b[j] = *reinterpret_cast<const v8h *>(fb + slot * C::STAGE + (j * KC + kc) * 1024);
+  };
+  auto mma = [&](const v8h (&a)[4], const v8h (&b)[2]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+  };
+
+  // Schedule: each stage starts with its first chunk's fragments in registers.
+  // Stage g: wait for this wave's copies of stage g + 1 and for its LDS
+  // reads, barrier (stage g + 1 is then visible everywhere and nobody reads
+  // the slot of stage g - 1 any more), refill that slot with stage
+  // g + NSLOT - 1; the fragments of the next chunk (of this stage, or chunk 0
+  // of stage g + 1) are read under the MFMAs of the current one.
+#pragma unroll
+  for (int p = 0; p < NSLOT - 1; ++p)
     if (p < S) issue(p, p);
+  // stage 0 is complete once at most the later prologue stages are outstanding
+  if constexpr (NSLOT >= 4) {
+    if (S > 2) wait_vm<2 * C::PER_STAGE>();
+    else if (S > 1) wait_vm<C::PER_STAGE>();
+    else wait_vm<0>();
+  } else {
+    if (S > 1) wait_vm<C::PER_STAGE>();
+    else wait_vm<0>();
+  }
+  __builtin_amdgcn_s_barrier();
+  v8h fr[2][4], gr[2][2];
+  load(fr[0], gr[0], 0, 0);
 
   for (int g = 0; g < S; ++g) {
-    // this wave's copies of stage g are done once at most the stages issued
-    // after it (g + 1, g + 2) are outstanding; this wave's LDS reads of stage
-    // g - 1 are done; after the barrier every wave's are, so stage g is
-    // visible and the slot of stage g - 1 can be refilled with g + 3
-    if (g + 2 < S) wait_vm<2 * F16_PER_STAGE>();
-    else if (g + 1 < S) wait_vm<F16_PER_STAGE>();
-    else wait_vm<0>();
+    // stages issued after g + 1 so far: g + 2 .. g + NSLOT - 2
+    if constexpr (NSLOT >= 4) {
+      if (g + 2 < S) wait_vm<(NSLOT - 3) * C::PER_STAGE>();
+      else wait_vm<0>();
+    } else {
+      wait_vm<0>();
+    }
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();
-    if (g + F16_NSLOT - 1 < S) issue((g + F16_NSLOT - 1) % F16_NSLOT, g + F16_NSLOT - 1);
+    if (g + NSLOT - 1 < S) issue((g + NSLOT - 1) % NSLOT, g + NSLOT - 1);
     __builtin_amdgcn_sched_barrier(0);
-    const uint8_t *sa = smem + (g % F16_NSLOT) * F16_STAGE + 16 * lane;
+    const int slot = g % NSLOT;
 #pragma unroll
-    for (int kc = 0; kc < F16_KC; ++kc) {
-      v8h a[4], b[2];
+    for (int kc = 0; kc < KC; ++kc) {
+      // after the last stage the final read targets a slot whose contents are never used
+      if (kc + 1 < KC) load(fr[(kc + 1) & 1], gr[(kc + 1) & 1], slot, kc + 1);
+      else load(fr[(kc + 1) & 1], gr[(kc + 1) & 1], (g + 1) % NSLOT, 0);
+      mma(fr[kc & 1], gr[kc & 1]);
+    }
+    if constexpr (KC & 1) {  // the next stage starts from buffer 0
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const v8h *>(sa + ((wm * 4 + i) * F16_KC + kc) * 1024);
+      for (int i = 0; i < 4; ++i) fr[0][i] = fr[1][i];
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        b[j] = *reinterpret_cast<const v8h *>(sa + F16_A_BYTES + ((wn * 2 + j) * F16_KC + kc) * 1024);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < 2; ++j) gr[0][j] = gr[1][j];
     }
   }
 
@@ -272,6 +318,24 @@ __global__ void lm_expand_kernel(const uint8_t *__restrict__ codes, int64_t ldc,
   *reinterpret_cast<uint4 *>(out + idx * 16) = make_uint4(hv[0], hv[1], hv[2], hv[3]);
 }
 
+template <int KC, int NSLOT>
+hipError_t launch_f16(const uint8_t *A, const float *a_scale, int64_t M, int K, const uint8_t *W, int N, int Np,
+                      const float *mean, const float *w1, const float *bias, uint16_t *y, int64_t ldy,
+                      hipStream_t stream) {
+  using C = F16C<KC, NSLOT>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void *)gemm_f16_kernel<KC, NSLOT>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  dim3 grid((unsigned)((N + F16_BN - 1) / F16_BN), (unsigned)((M + F16_BM - 1) / F16_BM));
+  hipLaunchKernelGGL((gemm_f16_kernel<KC, NSLOT>), grid, dim3(512), C::LDS, stream, A, a_scale, M, K, W, N, Np, mean,
+                     w1, bias, y, ldy);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm_f16(const uint8_t *A, const float *a_scale, int64_t M, int K, const uint8_t *W, int N,
@@ -279,17 +343,7 @@ hipError_t launch_gemm_f16(const uint8_t *A, const float *a_scale, int64_t M, in
                            hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   const int Np = (N + 31) / 32 * 32;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)gemm_f16_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       F16_LDS);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  dim3 grid((unsigned)((N + F16_BN - 1) / F16_BN), (unsigned)((M + F16_BM - 1) / F16_BM));
-  hipLaunchKernelGGL(gemm_f16_kernel, grid, dim3(512), F16_LDS, stream, A, a_scale, M, K, W, N, Np, mean, w1, bias, y,
-                     ldy);
-  return hipGetLastError();
+  return launch_f16<2, 4>(A, a_scale, M, K, W, N, Np, mean, w1, bias, y, ldy, stream);
 }
 
 hipError_t launch_prepack_w16(const uint8_t *w, const float *ws, int N, int K, int group, uint8_t *out,

@@ -443,12 +443,13 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
       // rho = RN32(sqrt(S / d)), S the float64 sum of squares of the rotated
       // values (c_all^2 exact); u = RN32(v RN32(1 / rho)) with the deferred
       // factor and lane sign folded into the multiplier (exact)
-      double ss = 0.0;
+      double ssp[4] = {0.0, 0.0, 0.0, 0.0};  // four partial sums: shorter dependency chains
 #pragma unroll
       for (int s = 0; s < SLOTS; ++s)
 #pragma unroll
         for (int j = 0; j < 16; ++j)
-          if (act[s]) ss += (double)v[s][j] * (double)v[s][j];
+          if (act[s]) ssp[j & 3] += (double)v[s][j] * (double)v[s][j];
+      double ss = (ssp[0] + ssp[1]) + (ssp[2] + ssp[3]);
       ss = wave_sum_d(ss);
       const double c2 = (double)c_all * (double)c_all;
       const float rho = fmaxf((float)__builtin_sqrt((ss * c2) / (double)d), 1e-10f);
@@ -457,24 +458,33 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
 #pragma unroll
       for (int s = 0; s < SLOTS; ++s) {
         if (!act[s]) continue;
-        int q[16];
+        // binary search one step at a time across the 16 values, so that
+        // their table reads are in flight together
+        float key[16];
+        bool pos[16];
+        int c[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const float u = v[s][j] * inv;
           const float au = fabsf(u);
-          const bool pos = u > 0.f;
-          const float key = pos ? au : __uint_as_float(__float_as_uint(au) + 1u);
-          int c = 0;
-#pragma unroll
-          for (int t = 6; t >= 0; --t) {
-            const int st = 1 << t;
-            if (st < hh) {
-              const float pv = L::LM_LDS ? lm_pos[c + st] : la.thr[hh - 1 + c + st];
-              c += pv < key ? st : 0;
-            }
-          }
-          q[j] = pos ? hh + c : hh - 1 - c;
+          pos[j] = u > 0.f;
+          key[j] = pos[j] ? au : __uint_as_float(__float_as_uint(au) + 1u);
+          c[j] = 0;
         }
+#pragma unroll
+        for (int t = 6; t >= 0; --t) {
+          const int st = 1 << t;
+          if (st < hh) {
+            float pv[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) pv[j] = L::LM_LDS ? lm_pos[c[j] + st] : la.thr[hh - 1 + c[j] + st];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) c[j] += pv[j] < key[j] ? st : 0;
+          }
+        }
+        int q[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) q[j] = pos[j] ? hh + c[j] : hh - 1 - c[j];
         const int base = 1024 * s + 16 * il;
         char *orow = static_cast<char *>(out) + row * ld_out_bytes;
         if constexpr (mode == OUT_LM8) {
