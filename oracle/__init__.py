@@ -34,5 +34,7 @@ Modules:
   linear    offline weight preparation and the whole forward pass
   lloyd_max Lloyd-Max codebook of the sphere marginal, nearest-level codes,
             the float16 dequantizing product
+  asym      asymmetric grouped INT4 weights (CentriQ Eq. 2, App. B.2): RTN
+            min-max scale and shift, stored offset codes, the corrected product
 """
-from . import hadamard, rotation, quant, gemm, linear, lloyd_max  # noqa: F401
+from . import hadamard, rotation, quant, gemm, linear, lloyd_max, asym  # noqa: F401
