@@ -368,6 +368,56 @@ int oq_gemm_lm(int32_t bits, int tiled, const void *qa, int64_t lda_bytes, const
                const float *w1, const float *bias, uint16_t *y, int64_t ldy, void *ws, size_t ws_bytes,
                hipStream_t stream);
 
+/*
+ * Asymmetric grouped INT4 weights (CentriQ Sec. 3 Eq. 2: W_g = sigma (Q - z),
+ * Q in 0..15, per-(row, group) scale sigma and shift z stored in 16 bits, RTN
+ * from the group minimum and maximum; App. B.2: codes stored as Q - 8, the
+ * correction C = sigma (z - 8) per row and 64-column group weighted by the
+ * group sums p of the activation codes).
+ */
+
+/*
+ * oq_quant_weight_asym -- offline: rotate each row as oq_quant_weight does,
+ * then per group of `group` columns sigma = RNbf16(RN32((max - min) / 15))
+ * (1 for a constant group), z = RNbf16(RN32(-min / sigma)),
+ * Q = clamp(RNE(RN32(RN32(w / sigma) + z)), 0, 15).
+ * codes: Q - 8 as 4-bit two's complement, [N][K/2]; sigma, zero: bfloat16
+ * bits [N][K/group]; w1 (nullable) as oq_quant_weight.  K % 64 == 0.
+ */
+int oq_quant_weight_asym(const float *w, int32_t N, int32_t K, int64_t ldw, const oq_rot *rot, int32_t group,
+                         uint8_t *codes, uint16_t *sigma, uint16_t *zero, float *w1, hipStream_t stream);
+
+/*
+ * oq_prepack_w4_asym -- repack asymmetric weights for oq_gemm_w4a4_asym:
+ * w_tiled (oq_tiled_bytes(N, K) bytes) holds q'/2 for q' = Q - 8 in the tiled
+ * FP6 layout; w_scale_t float32 [K/64][N rounded up to 32] = sigma;
+ * corr float32 [N rounded up to 32][K/64] = RN32(sigma RN32(z - 8)).
+ * Padding rows get zeros.  group must be 64.
+ */
+int oq_prepack_w4_asym(const uint8_t *w, const uint16_t *sigma, const uint16_t *zero, int32_t N, int32_t K,
+                       int32_t group, uint8_t *w_tiled, float *w_scale_t, float *corr, hipStream_t stream);
+
+/*
+ * oq_quant_act_gsum -- oq_quant_act for afmt OQ_A4 | OQ_TILED or
+ * OQ_A6 | OQ_TILED (OQ_SCALE_PCTL allowed), which also writes gsum float32
+ * [M][d/64], the sum of the codes of every 64-wide group (exact integers).
+ * d % 64 == 0, d <= 4096.
+ */
+int oq_quant_act_gsum(const uint16_t *x, int64_t M, int32_t d, int64_t ldx, const oq_rot *rot, int center, int afmt,
+                      void *codes, float *scale, float *gsum, float *mean, hipStream_t stream);
+
+/*
+ * oq_gemm_w4a4_asym -- tiled 4-bit activations times asymmetric weights:
+ *   y[t][o] = bf16_RNE( a_scale[t] * sum_g (sigma[o][g] acc_g[t][o]
+ *                        - corr[o][g] gsum[t][g]) + mean[t] w1[o] + bias[o] )
+ *   acc_g = exact sum over the group of q_a (Q - 8).
+ * afmt must be OQ_A4 | OQ_TILED; qa, a_scale, gsum from oq_quant_act_gsum;
+ * w_tiled, w_scale_t, corr from oq_prepack_w4_asym; K % 64 == 0.
+ */
+int oq_gemm_w4a4_asym(int afmt, const uint8_t *qa, const float *a_scale, const float *gsum, int64_t M, int32_t K,
+                      const uint8_t *w_tiled, const float *w_scale_t, const float *corr, int32_t N, const float *mean,
+                      const float *w1, const float *bias, uint16_t *y, int64_t ldy, hipStream_t stream);
+
 enum { OQ_OP_GEMM_W4A8 = 1, OQ_OP_GEMM_W4A4 = 2, OQ_OP_LINEAR = 3, OQ_OP_GEMM_LM = 4 };
 
 /* Scratch bytes a call needs (0 if none).  Pure host function.  For

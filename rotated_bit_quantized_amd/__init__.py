@@ -13,4 +13,5 @@ from ._binding import (  # noqa: F401
     lib, oq_center, oq_gemm_w4a4, oq_gemm_w4a8, oq_linear_fused, oq_quant_act, oq_quant_weight,
     oq_rotate, oq_workspace_bytes, oq_tiled_bytes, oq_prepack_w4, oq_tiled_mx_bytes, oq_prepack_mx,
     oq_lloyd_max_levels, oq_lloyd_max_tables, oq_tiled_f16_bytes, oq_quant_act_lm, oq_prepack_w16, oq_gemm_lm,
+    oq_quant_weight_asym, oq_prepack_w4_asym, oq_quant_act_gsum, oq_gemm_w4a4_asym,
 )

@@ -73,6 +73,11 @@ def _load():
         "oq_prepack_w16": ([vp, vp, i32, i32, i32, vp, vp], ctypes.c_int),
         "oq_gemm_lm": ([i32, ctypes.c_int, vp, i64, vp, i64, i32, vp, vp, i32, vp, vp, vp, vp, i64, vp, sz, vp],
                        ctypes.c_int),
+        "oq_quant_weight_asym": ([vp, i32, i32, i64, vp, i32, vp, vp, vp, vp, vp], ctypes.c_int),
+        "oq_prepack_w4_asym": ([vp, vp, vp, i32, i32, i32, vp, vp, vp, vp], ctypes.c_int),
+        "oq_quant_act_gsum": ([vp, i64, i32, i64, vp, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp], ctypes.c_int),
+        "oq_gemm_w4a4_asym": ([ctypes.c_int, vp, vp, vp, i64, i32, vp, vp, vp, i32, vp, vp, vp, vp, i64, vp],
+                              ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -85,7 +90,8 @@ _lib = _load()
 EXPORTED = ("oq_last_error", "oq_center", "oq_rotate", "oq_quant_act", "oq_quant_weight",
             "oq_gemm_w4a8", "oq_gemm_w4a4", "oq_linear_fused", "oq_workspace_bytes", "oq_tiled_bytes",
             "oq_prepack_w4", "oq_tiled_mx_bytes", "oq_prepack_mx", "oq_lloyd_max_levels", "oq_lloyd_max_tables",
-            "oq_tiled_f16_bytes", "oq_quant_act_lm", "oq_prepack_w16", "oq_gemm_lm")
+            "oq_tiled_f16_bytes", "oq_quant_act_lm", "oq_prepack_w16", "oq_gemm_lm", "oq_quant_weight_asym",
+            "oq_prepack_w4_asym", "oq_quant_act_gsum", "oq_gemm_w4a4_asym")
 
 
 def lib():
@@ -360,4 +366,63 @@ def oq_gemm_lm(bits: int, qa, a_scale, w16, N: int, levels=None, tiled: bool = F
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     _check(_lib.oq_gemm_lm(bits, int(tiled), _p(qa), lda, _p(a_scale), M, K, _p(levels), _p(w16), N, _p(mean),
                            _p(w1), _p(bias), _p(y), y.stride(0), _p(ws), wsb, _stream()))
+    return y
+
+
+# ---------------------------------------------------------------- asymmetric weights
+def oq_quant_weight_asym(w, rot: Optional[Rotation], group: int, codes=None, sigma=None, zero=None, w1=None,
+                         want_w1: bool = False):
+    N, K = w.shape
+    dev = _dev(w)
+    if codes is None:
+        codes = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    if sigma is None:
+        sigma = torch.empty((N, K // group), dtype=torch.int16, device=dev)
+    if zero is None:
+        zero = torch.empty((N, K // group), dtype=torch.int16, device=dev)
+    if want_w1 and w1 is None:
+        w1 = torch.empty(N, dtype=torch.float32, device=dev)
+    _check(_lib.oq_quant_weight_asym(_p(w), N, K, w.stride(0), _rref(rot), group, _p(codes), _p(sigma), _p(zero),
+                                     _p(w1), _stream()))
+    return {"codes": codes, "sigma": sigma, "zero": zero, "w1": w1}
+
+
+def oq_prepack_w4_asym(w, sigma, zero, N: int, K: int, group: int = 64):
+    dev = _dev(w)
+    Np = (N + 31) // 32 * 32
+    w_tiled = torch.empty(max(16, oq_tiled_bytes(N, K)), dtype=torch.uint8, device=dev)
+    w_scale_t = torch.empty((K // 64, Np), dtype=torch.float32, device=dev)
+    corr = torch.empty((Np, K // 64), dtype=torch.float32, device=dev)
+    _check(_lib.oq_prepack_w4_asym(_p(w), _p(sigma), _p(zero), N, K, group, _p(w_tiled), _p(w_scale_t), _p(corr),
+                                   _stream()))
+    return {"codes": w_tiled, "scales": w_scale_t, "corr": corr}
+
+
+def oq_quant_act_gsum(x, rot: Optional[Rotation], afmt: int, center: bool = False, codes=None, scale=None,
+                      gsum=None, mean=None):
+    x = _bits16(x)
+    M, d = x.shape
+    dev = _dev(x)
+    fmt = afmt & ~OQ_SCALE_PCTL
+    if codes is None:
+        planes = 2 if (fmt & ~OQ_TILED) == OQ_A6 else 1
+        codes = torch.empty(max(16, planes * oq_tiled_bytes(M, d)), dtype=torch.uint8, device=dev)
+    if scale is None:
+        scale = torch.empty(M, dtype=torch.float32, device=dev)
+    if gsum is None:
+        gsum = torch.empty((M, d // 64), dtype=torch.float32, device=dev)
+    if center and mean is None:
+        mean = torch.empty(M, dtype=torch.float32, device=dev)
+    _check(_lib.oq_quant_act_gsum(_p(x), M, d, x.stride(0), _rref(rot), int(center), afmt, _p(codes), _p(scale),
+                                  _p(gsum), _p(mean), _stream()))
+    return {"codes": codes, "scale": scale, "gsum": gsum, "mean": mean}
+
+
+def oq_gemm_w4a4_asym(qa, a_scale, gsum, w, N: int, M: int, K: int, mean=None, w1=None, bias=None, y=None,
+                      afmt: int = OQ_A4 | OQ_TILED):
+    """w: oq_prepack_w4_asym output (dict with codes, scales, corr)."""
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=_dev(qa))
+    _check(_lib.oq_gemm_w4a4_asym(afmt, _p(qa), _p(a_scale), _p(gsum), M, K, _p(w["codes"]), _p(w["scales"]),
+                                  _p(w["corr"]), N, _p(mean), _p(w1), _p(bias), _p(y), y.stride(0), _stream()))
     return y

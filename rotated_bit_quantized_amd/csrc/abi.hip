@@ -685,5 +685,87 @@ int oq_gemm_lm(int32_t bits, int tiled, const void *qa, int64_t lda_bytes, const
                     fn);
 }
 
+// ------------------------------------------------------ asymmetric weights
+int oq_quant_weight_asym(const float *w, int32_t N, int32_t K, int64_t ldw, const oq_rot *rot, int32_t group,
+                         uint8_t *codes, uint16_t *sigma, uint16_t *zero, float *w1, hipStream_t stream) {
+  const char *fn = "oq_quant_weight_asym";
+  if (N < 0) return fail(OQ_ERR_INVALID_ARG, "%s: N < 0", fn);
+  if (K < 64 || K > 16384 || K % 64) return fail(OQ_ERR_UNSUPPORTED, "%s: K=%d must be a multiple of 64 in [64, 16384]", fn, K);
+  if (group < 32 || group % 32 || K % group)
+    return fail(OQ_ERR_UNSUPPORTED, "%s: group=%d must be a multiple of 32 dividing K=%d", fn, group, K);
+  if (N == 0) return OQ_OK;
+  if (!w || !codes || !sigma || !zero) return fail(OQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (ldw < K) return fail(OQ_ERR_INVALID_ARG, "%s: ldw < K", fn);
+  if (!al16(w) || (ldw * 4) % 16 || !al16(codes)) return fail(OQ_ERR_ALIGNMENT, "%s: rows must be 16-byte aligned", fn);
+  if ((reinterpret_cast<uintptr_t>(sigma) | reinterpret_cast<uintptr_t>(zero)) & 1)
+    return fail(OQ_ERR_ALIGNMENT, "%s: sigma/zero misaligned", fn);
+  RotArgs ra;
+  int rc = rot_args(fn, rot, K, &ra);
+  if (rc) return rc;
+  g_err[0] = 0;
+  return hip_status(launch_weight_rpbh_asym(w, N, K, ldw, ra, group, codes, sigma, zero, w1, stream), fn);
+}
+
+int oq_prepack_w4_asym(const uint8_t *w, const uint16_t *sigma, const uint16_t *zero, int32_t N, int32_t K,
+                       int32_t group, uint8_t *w_tiled, float *w_scale_t, float *corr, hipStream_t stream) {
+  const char *fn = "oq_prepack_w4_asym";
+  if (N < 0) return fail(OQ_ERR_INVALID_ARG, "%s: N < 0", fn);
+  if (K <= 0 || K % 64) return fail(OQ_ERR_UNSUPPORTED, "%s: K=%d must be a positive multiple of 64", fn, K);
+  if (group != 64) return fail(OQ_ERR_UNSUPPORTED, "%s: group must be 64 (got %d)", fn, group);
+  if (N > 0 && (!w || !sigma || !zero || !w_tiled || !w_scale_t || !corr))
+    return fail(OQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (!al16(w) || !al16(w_tiled)) return fail(OQ_ERR_ALIGNMENT, "%s: misaligned", fn);
+  g_err[0] = 0;
+  return hip_status(launch_prepack_w4a(w, sigma, zero, N, K, w_tiled, w_scale_t, corr, stream), fn);
+}
+
+int oq_quant_act_gsum(const uint16_t *x, int64_t M, int32_t d, int64_t ldx, const oq_rot *rot, int center, int afmt,
+                      void *codes, float *scale, float *gsum, float *mean, hipStream_t stream) {
+  const char *fn = "oq_quant_act_gsum";
+  int rc = check_x(fn, x, M, d, ldx);
+  if (rc) return rc;
+  PctlArgs pa;
+  const PctlArgs *pp = nullptr;
+  if (afmt & OQ_SCALE_PCTL) {
+    afmt &= ~OQ_SCALE_PCTL;
+    rc = pctl_setup(fn, afmt, d, &pa);
+    if (rc) return rc;
+    pp = &pa;
+  }
+  if (afmt != (OQ_A4 | OQ_TILED) && afmt != (OQ_A6 | OQ_TILED))
+    return fail(OQ_ERR_UNSUPPORTED, "%s: group sums come with OQ_A4 | OQ_TILED or OQ_A6 | OQ_TILED codes", fn);
+  if (!rpbh_wave_supported(d) || d % 64)
+    return fail(OQ_ERR_UNSUPPORTED, "%s: d=%d must be a multiple of 64 up to 4096", fn, d);
+  if (M == 0) return OQ_OK;
+  if (!codes || !scale || !gsum) return fail(OQ_ERR_INVALID_ARG, "%s: NULL output", fn);
+  if (!al16(codes) || (reinterpret_cast<uintptr_t>(gsum) & 3)) return fail(OQ_ERR_ALIGNMENT, "%s: misaligned", fn);
+  if (center && !mean) return fail(OQ_ERR_INVALID_ARG, "%s: centering needs mean", fn);
+  RotArgs ra;
+  rc = rot_args(fn, rot, d, &ra);
+  if (rc) return rc;
+  const int base = afmt & ~OQ_TILED;
+  g_err[0] = 0;
+  return hip_status(launch_rpbh_quant(x, M, d, ldx, ra, center ? 1 : 0, mean, base == OQ_A4 ? OUT_FP6 : OUT_FP6X2,
+                                      qmax_of(base), codes, 0, scale, stream, pp, nullptr, gsum),
+                    fn);
+}
+
+int oq_gemm_w4a4_asym(int afmt, const uint8_t *qa, const float *a_scale, const float *gsum, int64_t M, int32_t K,
+                      const uint8_t *w_tiled, const float *w_scale_t, const float *corr, int32_t N, const float *mean,
+                      const float *w1, const float *bias, uint16_t *y, int64_t ldy, hipStream_t stream) {
+  const char *fn = "oq_gemm_w4a4_asym";
+  if (afmt != (OQ_A4 | OQ_TILED)) return fail(OQ_ERR_UNSUPPORTED, "%s: afmt must be OQ_A4 | OQ_TILED", fn);
+  int rc = check_gemm_common(fn, qa, 16, M, K, w_tiled, w_scale_t, N, y, ldy, 0);
+  if (rc) return rc;
+  if ((mean == nullptr) != (w1 == nullptr)) return fail(OQ_ERR_INVALID_ARG, "%s: mean and w1 must be given together", fn);
+  if (M == 0 || N == 0) return OQ_OK;
+  if (!a_scale || !gsum || !corr) return fail(OQ_ERR_INVALID_ARG, "%s: NULL scale, gsum or corr", fn);
+  g_err[0] = 0;
+  return hip_status(launch_gemm_fp6_asym(qa, a_scale, gsum, M, K, w_tiled, w_scale_t, corr, N, mean, w1, bias, y, ldy,
+                                         stream),
+                    fn);
+}
+
 }  // extern "C"
+
 

@@ -21,6 +21,15 @@
 //   one 16-byte and one 8-byte LDS read per lane, both conflict-free.
 // Weight scales are stored transposed, [K/64][N_padded] float32.
 //
+// Asymmetric weights (CentriQ Sec. 3 Eq. 2, stored as Q - 8 per App. B.2):
+// the codes q' = Q - 8 lie in [-8, 7]; -8 is no FP6 E2M3 value, but q'/2 is
+// (every half-integer in [-4, 3.5]), so the prepack stores q'/2 and the MFMA
+// takes an E8M0 scale of 2^1 for the weights: the group sums stay exact.  The
+// real shift leaves -sum_g C_g p_g (C = sigma (z - 8) per row and group, p the
+// group sums of the activation codes), a product of depth K/64 computed once
+// per tile before the main loop on bfloat16 matrix cores, with p and C split
+// into pieces that make every product exact in float32.
+//
 // Workgroup: WM x WN wavefronts, each computing 128 x 64 outputs (4 x 2 MFMA
 // tiles of 32 x 32).  The k loop walks the 64-wide groups; each group's A, B
 // and scale tiles are copied global -> LDS with global_load_lds_dwordx4
@@ -338,6 +347,65 @@ __global__ void prepack_w4_kernel(const uint8_t *__restrict__ w, const float *__
   if (half == 0) out_s[(int64_t)kg * Np + row] = row < N ? ws[(int64_t)row * G + kg] : 0.f;
 }
 
+// FP6 E2M3 bits of q'/2 for an asymmetric code q' in [-8, 7]: |q'|/2 in
+// {0, 0.5, .., 4} -> 0x00 0x04 0x08 0x0C 0x10 0x12 0x14 0x16 0x18, sign bit 5
+__device__ __forceinline__ uint32_t fp6_e2m3_of_half(int q) {
+  const uint32_t a = (uint32_t)(q < 0 ? -q : q);
+  const uint32_t code = a == 8 ? 0x18u : (__builtin_amdgcn_perm(0x16141210u, 0x0C080400u, a) & 0xFFu);
+  return code | (q < 0 ? 0x20u : 0u);
+}
+
+// canonical asymmetric codes q' = Q - 8 [N][K/2] + bfloat16 sigma, z [N][G] ->
+// tiled FP6 of q'/2, sigma transposed [G][Np] float32, C = RN32(sigma
+// RN32(z - 8)) [Np][G] float32 (padding rows: zero codes, scale and C)
+__global__ void prepack_w4a_kernel(const uint8_t *__restrict__ w, const uint16_t *__restrict__ sig,
+                                   const uint16_t *__restrict__ zero, int N, int Np, int K, uint8_t *__restrict__ out,
+                                   float *__restrict__ out_s, float *__restrict__ out_c) {
+  const int G = K / 64;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)Np * G * 2;
+  if (idx >= total) return;
+  const int half = (int)(idx & 1);
+  const int64_t rg = idx >> 1;
+  const int kg = (int)(rg % G);
+  const int row = (int)(rg / G);
+  uint32_t c[32];
+  if (row < N) {
+    const uint4 p = *reinterpret_cast<const uint4 *>(w + (int64_t)row * (K / 2) + kg * 32 + half * 16);
+    const uint32_t wd[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      int q = (int)((wd[j >> 3] >> (4 * (j & 7))) & 0xF);
+      q = q >= 8 ? q - 16 : q;
+      c[j] = fp6_e2m3_of_half(q);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) c[j] = 0;
+  }
+  uint32_t bits[6] = {0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const int b = 6 * j;
+    bits[b >> 5] |= c[j] << (b & 31);
+    if ((b & 31) > 26) bits[(b >> 5) + 1] |= c[j] >> (32 - (b & 31));
+  }
+  uint8_t *tile = out + ((int64_t)(row / 32) * G + kg) * CHUNK_TILE;
+  const int l = 32 * half + row % 32;
+  *reinterpret_cast<uint4 *>(tile + 16 * l) = make_uint4(bits[0], bits[1], bits[2], bits[3]);
+  *reinterpret_cast<uint2 *>(tile + 1024 + 8 * l) = make_uint2(bits[4], bits[5]);
+  if (half == 0) {
+    float sv = 0.f, cv = 0.f;
+    if (row < N) {
+      sv = __uint_as_float((uint32_t)sig[(int64_t)row * G + kg] << 16);
+      const float zv = __uint_as_float((uint32_t)zero[(int64_t)row * G + kg] << 16);
+      cv = sv * (zv - 8.0f);
+    }
+    out_s[(int64_t)kg * Np + row] = sv;
+    out_c[(int64_t)row * G + kg] = cv;
+  }
+}
+
 template <int WM, int WN, int PLANES, int NSTAGE>
 hipError_t launch_cfg(const uint8_t *A, int64_t a_plane_bytes, const float *a_scale, int64_t M, int K,
                       const uint8_t *W, const float *wst, int N, int Np, const float *mean, const float *w1,
@@ -404,12 +472,20 @@ struct V2C {
   static constexpr int PER_STAGE = 4;  // copy instructions per wave per stage
 };
 
-template <int NSLOT, bool PAIRED>
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) {
+  bf16x8_t r;
+  __builtin_memcpy(&r, &u, 16);
+  return r;
+}
+
+template <int NSLOT, bool PAIRED, bool ASYM>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_scale, int64_t M, int K,
                    const uint8_t *__restrict__ W, const float *__restrict__ wst, int N, int Np,
                    const float *__restrict__ mean, const float *__restrict__ w1, const float *__restrict__ bias,
-                   uint16_t *__restrict__ y, int64_t ldy) {
+                   uint16_t *__restrict__ y, int64_t ldy, const float *__restrict__ gsum,
+                   const float *__restrict__ corr) {
   using V2 = V2C<NSLOT>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const uint32_t lds0 = lds_addr_of(smem);
@@ -469,6 +545,69 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_sc
 #pragma unroll
       for (int e = 0; e < 16; ++e) F[i][j][e] = 0.f;
 
+  if constexpr (ASYM) {
+    // F = -sum_g C[o][g] p[t][g]: depth 8 G in bfloat16, slot 8 g + s holds
+    // piece s / 3 of p (p1 = p with its low three bits cleared, p2 = those
+    // bits: both exact in bfloat16 for |p| < 2048) against piece s % 3 of -C
+    // (the truncation split C = c1 + c2 + c3, each exactly a bfloat16); slots
+    // 6 and 7 are zero.  Lanes 0-31 take group 2 ch, lanes 32-63 group 2 ch + 1.
+    const int Gq = K / 64;
+    const int r0 = lane & 31, hf = lane >> 5;
+    int64_t prow[4];
+    int ccol[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t rr = m0 + (wave >> 2) * 128 + 32 * i + r0;
+      prow[i] = rr < M ? rr : M - 1;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int cc = n0 + (wave & 3) * 64 + 32 * j + r0;
+      ccol[j] = cc < Np ? cc : Np - 1;
+    }
+    v16f E[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) E[i][j] = (v16f){};
+    for (int ch = 0; ch < (Gq + 1) / 2; ++ch) {
+      const int g = 2 * ch + hf;
+      const bool gv = g < Gq;
+      const int gg = gv ? g : 0;
+      uint4 av[4], bv[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int pv = gv ? (int)gsum[prow[i] * Gq + gg] : 0;
+        const uint32_t h1 = __float_as_uint((float)(pv & ~7)) >> 16;
+        const uint32_t h2 = __float_as_uint((float)(pv & 7)) >> 16;
+        av[i] = make_uint4(h1 | (h1 << 16), h1 | (h2 << 16), h2 | (h2 << 16), 0u);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float cf = gv ? corr[(int64_t)ccol[j] * Gq + gg] : 0.f;
+        const uint32_t c1 = __float_as_uint(cf) & 0xFFFF0000u;
+        const float rem = cf - __uint_as_float(c1);
+        const uint32_t c2 = __float_as_uint(rem) & 0xFFFF0000u;
+        const uint32_t c3 = __float_as_uint(rem - __uint_as_float(c2));
+        const uint32_t n1 = (c1 ^ 0x80000000u) >> 16, n2 = (c2 ^ 0x80000000u) >> 16, n3 = (c3 ^ 0x80000000u) >> 16;
+        bv[j] = make_uint4(n1 | (n2 << 16), n3 | (n1 << 16), n2 | (n3 << 16), 0u);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          E[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av[i]), as_bf16x8(bv[j]), E[i][j], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) F[i][j][e] = E[i][j][e];
+  }
+  // E8M0 scale of the weight operand: 2^1 for the stored q'/2 of asymmetric codes
+  const int wsc = ASYM ? 128 : 127;
+
   float *lds_alpha = reinterpret_cast<float *>(smem + V2::ROWS_OFF);
   float *lds_mean = lds_alpha + V2::BM;
   for (int t = threadIdx.x; t < V2::BM; t += 512) {
@@ -508,7 +647,7 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_sc
     for (int t = 0; t < 8; ++t) {
       const int i = t >> 1;
       const v8i &bb = (t & 1) ? b1 : b0;
-      const v16f dt = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], bb, (v16f){}, 2, 2, 0, 127, 0, 127);
+      const v16f dt = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], bb, (v16f){}, 2, 2, 0, 127, 0, wsc);
       __builtin_amdgcn_sched_barrier(0);
       if (t > 0) {
         const int ip = (t - 1) >> 1, jp = (t - 1) & 1;
@@ -639,21 +778,21 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_sc
   }
 }
 
-template <int NSLOT, bool PAIRED>
+template <int NSLOT, bool PAIRED, bool ASYM>
 hipError_t launch_v2(const uint8_t *A, const float *a_scale, int64_t M, int K, const uint8_t *W, const float *wst,
                      int N, int Np, const float *mean, const float *w1, const float *bias, uint16_t *y, int64_t ldy,
-                     hipStream_t stream) {
+                     hipStream_t stream, const float *gsum = nullptr, const float *corr = nullptr) {
   using V2 = V2C<NSLOT>;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)gemm_fp6_v2_kernel<NSLOT, PAIRED>,
+    hipError_t e = hipFuncSetAttribute((const void *)gemm_fp6_v2_kernel<NSLOT, PAIRED, ASYM>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, V2::LDS_BYTES);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   dim3 grid((unsigned)((N + V2::BN - 1) / V2::BN), (unsigned)((M + V2::BM - 1) / V2::BM));
-  hipLaunchKernelGGL((gemm_fp6_v2_kernel<NSLOT, PAIRED>), grid, dim3(512), V2::LDS_BYTES, stream, A, a_scale, M, K, W, wst,
-                     N, Np, mean, w1, bias, y, ldy);
+  hipLaunchKernelGGL((gemm_fp6_v2_kernel<NSLOT, PAIRED, ASYM>), grid, dim3(512), V2::LDS_BYTES, stream, A, a_scale, M, K,
+                     W, wst, N, Np, mean, w1, bias, y, ldy, gsum, corr);
   return hipGetLastError();
 }
 
@@ -668,8 +807,28 @@ hipError_t launch_gemm_fp6(const uint8_t *A, int planes, const float *a_scale, i
   if (planes == 2) return launch_cfg<2, 4, 2, 3>(A, plane, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy, stream);
   // the prefetching kernel addresses operands with 32-bit offsets from their base
   if (tiled_bytes(M, K) < (int64_t(1) << 32) && tiled_bytes(Np, K) < (int64_t(1) << 32))
-    return launch_v2<FP6_SLOTS, FP6_PAIRED>(A, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy, stream);
+    return launch_v2<FP6_SLOTS, FP6_PAIRED, false>(A, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy, stream);
   return launch_cfg<2, 4, 1, FP6_STAGES>(A, plane, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy, stream);
+}
+
+hipError_t launch_gemm_fp6_asym(const uint8_t *A, const float *a_scale, const float *gsum, int64_t M, int K,
+                                const uint8_t *W, const float *wst, const float *corr, int N, const float *mean,
+                                const float *w1, const float *bias, uint16_t *y, int64_t ldy, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  const int Np = (N + 31) / 32 * 32;
+  if (!(tiled_bytes(M, K) < (int64_t(1) << 32) && tiled_bytes(Np, K) < (int64_t(1) << 32))) return hipErrorInvalidValue;
+  return launch_v2<FP6_SLOTS, FP6_PAIRED, true>(A, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy, stream, gsum,
+                                                corr);
+}
+
+hipError_t launch_prepack_w4a(const uint8_t *w, const uint16_t *sig, const uint16_t *zero, int N, int K, uint8_t *out,
+                              float *out_s, float *out_c, hipStream_t stream) {
+  if (N == 0) return hipSuccess;
+  const int Np = (N + 31) / 32 * 32;
+  const int64_t total = (int64_t)Np * (K / 64) * 2;
+  hipLaunchKernelGGL(prepack_w4a_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, w, sig, zero, N,
+                     Np, K, out, out_s, out_c);
+  return hipGetLastError();
 }
 
 hipError_t launch_prepack_w4(const uint8_t *w, const float *ws, int N, int K, uint8_t *out, float *out_s,

@@ -55,13 +55,18 @@ __device__ __forceinline__ void fwht16(float (&u)[E]) {
 // MODE OUT_W4G: symmetric INT4 per group of `group` coordinates (weights),
 //   scale_out [M][d/group]; mean_out, if set, receives the float64 row sum of
 //   the input rounded to float32 (w1 = W 1).
+// MODE OUT_W4A: asymmetric INT4 per group (CentriQ Sec. 3 Eq. 2, RTN from the
+//   group's minimum and maximum): sigma = RNbf16(RN32((max - min) / 15)) (1
+//   for a constant group), z = RNbf16(RN32(-min / sigma)), codes
+//   Q = clamp(RNE(RN32(RN32(w / sigma) + z)), 0, 15) stored as Q - 8;
+//   sigma bits to scale_out (as uint16), z bits to zero_out.
 template <int ROUNDS, int MODE, bool IN_F32>
 __global__ void __launch_bounds__(1024)
 rpbh_quant_kernel(const void *__restrict__ xin, int64_t M, int d, int64_t ldx,
                   const int32_t *__restrict__ perm, const int8_t *__restrict__ signs,
                   int h, float c_h, int center, float *__restrict__ mean_out,
                   int qmax, void *__restrict__ out, int64_t ld_out_bytes,
-                  float *__restrict__ scale_out, int group) {
+                  float *__restrict__ scale_out, int group, uint16_t *__restrict__ zero_out) {
   extern __shared__ float lds[];
   float *buf0 = lds;                      // [d]
   float *buf1 = lds + (ROUNDS == 2 ? d : 0);
@@ -113,7 +118,7 @@ rpbh_quant_kernel(const void *__restrict__ xin, int64_t M, int d, int64_t ldx,
       for (int j = 0; j < E; ++j) v[j] = 0.f;
     }
 
-    if (MODE == OUT_W4G) {
+    if (MODE == OUT_W4G || MODE == OUT_W4A) {
       if (mean_out) {  // w1 = row sum of the unrotated weight, float64 then RN32
         double s = 0.0;
 #pragma unroll
@@ -172,6 +177,41 @@ rpbh_quant_kernel(const void *__restrict__ xin, int64_t M, int d, int64_t ldx,
 #pragma unroll
         for (int k = 0; k < 4; ++k) dst[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
       }
+      continue;
+    }
+
+    if (MODE == OUT_W4A) {
+      // groups of `group` coordinates = group/16 consecutive lanes
+      float mn = v[0], mx = v[0];
+#pragma unroll
+      for (int j = 1; j < E; ++j) {
+        mn = fminf(mn, v[j]);
+        mx = fmaxf(mx, v[j]);
+      }
+      for (int m = 1; m < group / E; m <<= 1) {
+        mn = fminf(mn, __shfl_xor(mn, m));
+        mx = fmaxf(mx, __shfl_xor(mx, m));
+      }
+      const float r = mx - mn;
+      const uint16_t sb = r > 0.f ? f32_to_bf16_rne(__fdiv_rn(r, 15.0f)) : (uint16_t)0x3F80;  // 1.0
+      const float sig = __uint_as_float((uint32_t)sb << 16);
+      const uint16_t zb = f32_to_bf16_rne(__fdiv_rn(-mn, sig));
+      const float z = __uint_as_float((uint32_t)zb << 16);
+      if (!act) continue;
+      if ((base % group) == 0) {
+        const int64_t gi = row * (d / group) + base / group;
+        reinterpret_cast<uint16_t *>(scale_out)[gi] = sb;
+        zero_out[gi] = zb;
+      }
+      uint32_t wd[2] = {0u, 0u};
+#pragma unroll
+      for (int j = 0; j < E; ++j) {
+        const float tq = __builtin_rintf(__fdiv_rn(v[j], sig) + z);
+        const int q = (int)fminf(fmaxf(tq, 0.0f), 15.0f) - 8;
+        wd[j >> 3] |= (uint32_t)(q & 0xF) << (4 * (j & 7));
+      }
+      char *orow = reinterpret_cast<char *>(out) + row * ld_out_bytes;
+      *reinterpret_cast<uint2 *>(orow + base / 2) = make_uint2(wd[0], wd[1]);
       continue;
     }
 
@@ -272,7 +312,7 @@ rpbh_quant_kernel(const void *__restrict__ xin, int64_t M, int d, int64_t ldx,
 template <int ROUNDS, int MODE, bool IN_F32>
 hipError_t launch_t(const void *x, int64_t M, int d, int64_t ldx, const RotArgs &rot,
                     int center, float *mean, int qmax, void *out, int64_t ld_out_bytes,
-                    float *scale, int group, hipStream_t stream) {
+                    float *scale, int group, hipStream_t stream, uint16_t *zero = nullptr) {
   const int nact = d / E;
   const int threads = ((nact + 63) / 64) * 64;
   const size_t lds = sizeof(float) * ((size_t)ROUNDS * d + 16) + sizeof(double) * 16;
@@ -286,7 +326,7 @@ hipError_t launch_t(const void *x, int64_t M, int d, int64_t ldx, const RotArgs 
   }
   hipLaunchKernelGGL((rpbh_quant_kernel<ROUNDS, MODE, IN_F32>), dim3((unsigned)grid), dim3(threads), lds, stream,
                      x, M, d, ldx, rot.perm, rot.signs, rot.block, rot.c_h, center, mean, qmax, out,
-                     ld_out_bytes, scale, group);
+                     ld_out_bytes, scale, group, zero);
   return hipGetLastError();
 }
 
@@ -317,15 +357,28 @@ hipError_t launch_weight_rpbh(const float *w, int N, int K, int64_t ldw, const R
   return hipErrorInvalidValue;
 }
 
+hipError_t launch_weight_rpbh_asym(const float *w, int N, int K, int64_t ldw, const RotArgs &rot, int group,
+                                   uint8_t *codes, uint16_t *sigma, uint16_t *zero, float *w1, hipStream_t stream) {
+  if (N == 0) return hipSuccess;
+  float *sg = reinterpret_cast<float *>(sigma);  // carried as the scale pointer, written as uint16
+  switch (rot.rounds) {
+    case 0: return launch_t<0, OUT_W4A, true>(w, N, K, ldw, rot, 0, w1, 0, codes, K / 2, sg, group, stream, zero);
+    case 1: return launch_t<1, OUT_W4A, true>(w, N, K, ldw, rot, 0, w1, 0, codes, K / 2, sg, group, stream, zero);
+    case 2: return launch_t<2, OUT_W4A, true>(w, N, K, ldw, rot, 0, w1, 0, codes, K / 2, sg, group, stream, zero);
+  }
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_rpbh_quant(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotArgs &rot,
                              int center, float *mean, int out_mode, int qmax, void *out,
                              int64_t ld_out_bytes, float *scale, hipStream_t stream, const PctlArgs *pctl,
-                             const LmArgs *lm) {
+                             const LmArgs *lm, float *gsum) {
   if (M == 0) return hipSuccess;
   if (rpbh_wave_supported(d))
-    return launch_rpbh_wave(x, M, d, ldx, rot, center, mean, out_mode, qmax, out, ld_out_bytes, scale, stream, pctl, lm);
-  // the percentile range and the Lloyd-Max codes exist in the wave kernel only
-  if (pctl || lm || out_mode >= OUT_LM4) return hipErrorInvalidValue;
+    return launch_rpbh_wave(x, M, d, ldx, rot, center, mean, out_mode, qmax, out, ld_out_bytes, scale, stream, pctl, lm,
+                            gsum);
+  // the percentile range, the Lloyd-Max codes and the group sums exist in the wave kernel only
+  if (pctl || lm || gsum || out_mode >= OUT_LM4) return hipErrorInvalidValue;
   switch (rot.rounds) {
     case 0: return launch_mode<0>(out_mode, x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, stream);
     case 1: return launch_mode<1>(out_mode, x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, stream);

@@ -216,7 +216,7 @@ __global__ void __launch_bounds__(64 * WAVES_PER_WG)
 rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, const int32_t *__restrict__ perm,
                  const int8_t *__restrict__ signs, int h, float c_h, int pow4, int center,
                  float *__restrict__ mean_out, int qmax, void *__restrict__ out, int64_t ld_out_bytes,
-                 float *__restrict__ scale_out, PctlArgs pa, LmArgs la) {
+                 float *__restrict__ scale_out, PctlArgs pa, LmArgs la, float *__restrict__ gsum_out) {
   constexpr bool LM = is_lm_mode<mode>();
   using L = WaveLds<SLOTS, ROUNDS, LM>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
@@ -613,6 +613,25 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
           tbv[j] = rb + 0.0f;
         }
         const bool wa = act[s0], wb = two && act[two ? s0 + 1 : s0];
+        if (gsum_out) {
+          // sums of the codes of each 64-wide group: a lane holds 16 of them;
+          // index lanes il ^ 1 and il ^ 2 are physical lanes ^ 1 and ^ 2
+          float pa0 = 0.f, pb0 = 0.f;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            pa0 += ta[j];
+            pb0 += tbv[j];
+          }
+          pa0 += xlane(pa0, 0);
+          pa0 += xlane(pa0, 1);
+          pb0 += xlane(pb0, 0);
+          pb0 += xlane(pb0, 1);
+          if ((il & 3) == 0) {
+            float *gr = gsum_out + row * (int64_t)(d >> 6);
+            if (wa) gr[(1024 * s0 + 16 * il) >> 6] = pa0;
+            if (wb) gr[(1024 * (s0 + 1) + 16 * il) >> 6] = pb0;
+          }
+        }
         if (mode == OUT_FP6) {
           store_fp6_pair(ta, tbv, 0, tb, rr, 1024 * s0 + 16 * il, wa, wb);
         } else {
@@ -627,7 +646,7 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
 template <int SLOTS, int ROUNDS, int MODE, bool PCTL>
 hipError_t launch_m(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotArgs &rot, int center, float *mean,
                     int qmax, void *out, int64_t ld_out_bytes, float *scale, const PctlArgs &pa, const LmArgs &la,
-                    hipStream_t stream) {
+                    float *gsum, hipStream_t stream) {
   using L = WaveLds<SLOTS, ROUNDS, is_lm_mode<MODE>()>;
   const size_t lds = (size_t)L::TOTAL;
   static bool attr_set = false;
@@ -645,38 +664,39 @@ hipError_t launch_m(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotA
   const int pow4 = ROUNDS && ((__builtin_ctz((unsigned)h) & 1) == 0);
   hipLaunchKernelGGL((rpbh_wave_kernel<SLOTS, ROUNDS, MODE, PCTL>), dim3((unsigned)grid), dim3(64 * WAVES_PER_WG), lds,
                      stream, x, M, d, ldx, rot.perm, rot.signs, h, rot.c_h, pow4, center, mean, qmax, out,
-                     ld_out_bytes, scale, pa, la);
+                     ld_out_bytes, scale, pa, la, gsum);
   return hipGetLastError();
 }
 
 template <int SLOTS, int ROUNDS, int MODE>
 hipError_t launch_p(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotArgs &rot, int center, float *mean,
                     int qmax, void *out, int64_t ld_out_bytes, float *scale, const PctlArgs *pctl, const LmArgs *lm,
-                    hipStream_t stream) {
+                    float *gsum, hipStream_t stream) {
   const PctlArgs no_p{0, 0.0, 0.0, 1.0};
+  if (gsum && MODE != OUT_FP6 && MODE != OUT_FP6X2) return hipErrorInvalidValue;
   const LmArgs no_lm{1, nullptr, nullptr};
   if constexpr (is_lm_mode<MODE>()) {
     if (!lm || pctl) return hipErrorInvalidValue;
     return launch_m<SLOTS, ROUNDS, MODE, false>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, no_p,
-                                                *lm, stream);
+                                                *lm, gsum, stream);
   } else {
     if (lm) return hipErrorInvalidValue;
     if (pctl) {
       if constexpr (MODE == OUT_F32) return hipErrorInvalidValue;
       else return launch_m<SLOTS, ROUNDS, MODE, true>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale,
-                                                      *pctl, no_lm, stream);
+                                                      *pctl, no_lm, gsum, stream);
     }
     return launch_m<SLOTS, ROUNDS, MODE, false>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, no_p,
-                                                no_lm, stream);
+                                                no_lm, gsum, stream);
   }
 }
 
 template <int SLOTS, int ROUNDS>
 hipError_t launch_w(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotArgs &rot, int center, float *mean,
                     int mode, int qmax, void *out, int64_t ld_out_bytes, float *scale, const PctlArgs *pctl,
-                    const LmArgs *lm, hipStream_t stream) {
+                    const LmArgs *lm, float *gsum, hipStream_t stream) {
 #define OQ_MODE_CASE(MD) \
-  case MD: return launch_p<SLOTS, ROUNDS, MD>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, pctl, lm, stream);
+  case MD: return launch_p<SLOTS, ROUNDS, MD>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, pctl, lm, gsum, stream);
   switch (mode) {
     OQ_MODE_CASE(OUT_F32)
     OQ_MODE_CASE(OUT_I8)
@@ -694,11 +714,11 @@ hipError_t launch_w(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotA
 template <int SLOTS>
 hipError_t launch_r(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotArgs &rot, int center, float *mean,
                     int mode, int qmax, void *out, int64_t ld_out_bytes, float *scale, const PctlArgs *pctl,
-                    const LmArgs *lm, hipStream_t stream) {
+                    const LmArgs *lm, float *gsum, hipStream_t stream) {
   switch (rot.rounds) {
-    case 0: return launch_w<SLOTS, 0>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, pctl, lm, stream);
-    case 1: return launch_w<SLOTS, 1>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, pctl, lm, stream);
-    case 2: return launch_w<SLOTS, 2>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, pctl, lm, stream);
+    case 0: return launch_w<SLOTS, 0>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, pctl, lm, gsum, stream);
+    case 1: return launch_w<SLOTS, 1>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, pctl, lm, gsum, stream);
+    case 2: return launch_w<SLOTS, 2>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, pctl, lm, gsum, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -709,15 +729,15 @@ bool rpbh_wave_supported(int d) { return d >= 16 && d <= 4096 && d % 16 == 0; }
 
 hipError_t launch_rpbh_wave(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotArgs &rot, int center,
                             float *mean, int mode, int qmax, void *out, int64_t ld_out_bytes, float *scale,
-                            hipStream_t stream, const PctlArgs *pctl, const LmArgs *lm) {
+                            hipStream_t stream, const PctlArgs *pctl, const LmArgs *lm, float *gsum) {
   if (M == 0) return hipSuccess;
   if (pctl && (pctl->rank < 2 || pctl->rank > 4)) return hipErrorInvalidValue;
   if (lm && (lm->bits < 1 || lm->bits > 8 || (mode == OUT_LM4 && lm->bits > 4))) return hipErrorInvalidValue;
   switch ((d + 1023) / 1024) {
-    case 1: return launch_r<1>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, pctl, lm, stream);
-    case 2: return launch_r<2>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, pctl, lm, stream);
-    case 3: return launch_r<3>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, pctl, lm, stream);
-    case 4: return launch_r<4>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, pctl, lm, stream);
+    case 1: return launch_r<1>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, pctl, lm, gsum, stream);
+    case 2: return launch_r<2>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, pctl, lm, gsum, stream);
+    case 3: return launch_r<3>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, pctl, lm, gsum, stream);
+    case 4: return launch_r<4>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, pctl, lm, gsum, stream);
   }
   return hipErrorInvalidValue;
 }

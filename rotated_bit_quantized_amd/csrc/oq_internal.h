@@ -70,6 +70,7 @@ enum OutMode : int {
   OUT_LM4 = 6,   // Lloyd-Max level indices, packed two per byte (bits <= 4)
   OUT_LM8 = 7,   // Lloyd-Max level indices, one byte each (bits <= 8)
   OUT_LMF16 = 8, // Lloyd-Max levels as float16 in the tiled f16 MFMA layout
+  OUT_W4A = 9,   // asymmetric INT4 per group: codes Q - 8, bfloat16 scale and shift (weights)
 };
 
 // bytes of the tiled float16 operand layout: rows padded to 32, one 1 KiB
@@ -108,18 +109,20 @@ struct LmArgs {
 // K1: (center) -> RPBH rounds -> (quantize) per token row; pctl selects the
 // percentile range instead of absmax (integer outputs, rows the wave kernel
 // takes only); the OUT_LM* modes take their codebook from lm (wave kernel
-// only).
+// only); gsum (tiled FP6 modes, wave kernel only), if set, receives the sums
+// of the codes of every 64-wide group, float32 [M][d/64].
 hipError_t launch_rpbh_quant(const uint16_t *x, int64_t M, int d, int64_t ldx,
                              const RotArgs &rot, int center, float *mean,
                              int out_mode, int qmax, void *out, int64_t ld_out_bytes,
                              float *scale, hipStream_t stream, const PctlArgs *pctl = nullptr,
-                             const LmArgs *lm = nullptr);
+                             const LmArgs *lm = nullptr, float *gsum = nullptr);
 
 // K1, one wavefront per row (activation rows of width d <= 4096).
 bool rpbh_wave_supported(int d);
 hipError_t launch_rpbh_wave(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotArgs &rot, int center,
                             float *mean, int mode, int qmax, void *out, int64_t ld_out_bytes, float *scale,
-                            hipStream_t stream, const PctlArgs *pctl = nullptr, const LmArgs *lm = nullptr);
+                            hipStream_t stream, const PctlArgs *pctl = nullptr, const LmArgs *lm = nullptr,
+                            float *gsum = nullptr);
 
 // K2: dense per-32 transform -> (MXFP4 quantize | float32 out); mx_out: 0 float32,
 // 1 row-major codes + E8M0, 2 tiled MXFP4 layout.
@@ -141,6 +144,14 @@ hipError_t launch_gemm_fp6(const uint8_t *A, int planes, const float *a_scale, i
                            uint16_t *y, int64_t ldy, hipStream_t stream);
 hipError_t launch_prepack_w4(const uint8_t *w, const float *ws, int N, int K, uint8_t *out, float *out_s,
                              hipStream_t stream);
+// Tiled A4 x asymmetric INT4 weights (codes q'/2 with weight scale 2^1), with
+// F initialised to -sum_g corr[o][g] gsum[t][g] (single plane, group 64)
+hipError_t launch_gemm_fp6_asym(const uint8_t *A, const float *a_scale, const float *gsum, int64_t M, int K,
+                                const uint8_t *W, const float *wst, const float *corr, int N, const float *mean,
+                                const float *w1, const float *bias, uint16_t *y, int64_t ldy, hipStream_t stream);
+// canonical asymmetric codes + bfloat16 sigma, z -> tiled q'/2, sigma [G][Np], C [Np][G]
+hipError_t launch_prepack_w4a(const uint8_t *w, const uint16_t *sig, const uint16_t *zero, int N, int K, uint8_t *out,
+                              float *out_s, float *out_c, hipStream_t stream);
 
 // K5: MXFP4 x MXFP4 with E8M0 block scales (scaled FP4 MFMA); tiled_in: both
 // operands in the tiled MXFP4 layout (codes + scale words), else row-major.
@@ -174,6 +185,10 @@ double lloyd_max_solve(int d, int bits, double *levels);
 hipError_t launch_weight_rpbh(const float *w, int N, int K, int64_t ldw, const RotArgs &rot,
                               int group, uint8_t *codes, float *scales, float *w1,
                               hipStream_t stream);
+// asymmetric INT4 per group (CentriQ Eq. 2, RTN min-max): codes Q - 8 packed
+// [N][K/2], bfloat16 scale and shift [N][K/group] each
+hipError_t launch_weight_rpbh_asym(const float *w, int N, int K, int64_t ldw, const RotArgs &rot, int group,
+                                   uint8_t *codes, uint16_t *sigma, uint16_t *zero, float *w1, hipStream_t stream);
 hipError_t launch_weight_dense32(const float *w, int N, int K, int64_t ldw, const float *mats_w,
                                  uint8_t *codes, uint8_t *e8m0, float *w1, hipStream_t stream);
 

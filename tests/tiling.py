@@ -119,3 +119,38 @@ def untile_f16(buf: np.ndarray, R: int, K: int) -> np.ndarray:
     Rp = (R + 31) // 32 * 32
     b = np.asarray(buf).view(np.uint16)[: Rp * K]
     return b.reshape(Rp // 32, K // 16, 2, 32, 8).transpose(0, 3, 1, 2, 4).reshape(Rp, K)
+
+
+# E2M3 magnitudes from the format definition: bits e (2) m (3), e = 0 gives
+# m / 8, else 2^(e - 1) (1 + m / 8); used for values other than integers
+E2M3_MAGNITUDES = np.array([(m / 8.0) if e == 0 else 2.0 ** (e - 1) * (1 + m / 8.0)
+                            for e in range(4) for m in range(8)])
+
+
+def e2m3_bits(x) -> np.ndarray:
+    """E2M3 bit patterns of values that the format holds exactly."""
+    x = np.asarray(x, dtype=np.float64)
+    idx = np.array([np.flatnonzero(E2M3_MAGNITUDES == abs(v))[0] for v in x.ravel()], dtype=np.uint64)
+    sign = np.where(np.signbit(x.ravel()) & (x.ravel() != 0), np.uint64(0x20), np.uint64(0))
+    return (idx | sign).reshape(x.shape)
+
+
+def tile_values(vals: np.ndarray) -> np.ndarray:
+    """E2M3-exact values [R, K] -> tiled bytes (the layout of tile())."""
+    R, K = vals.shape
+    Rp = (R + 31) // 32 * 32
+    G = K // 64
+    f = np.zeros((Rp, K), dtype=np.uint64)
+    f[:R] = e2m3_bits(vals)
+    f = f.reshape(Rp, G, 2, 32)
+    st = np.zeros((Rp, G, 2, 24), dtype=np.uint8)
+    for j in range(32):
+        for b in range(6):
+            pos = 6 * j + b
+            bit = ((f[..., j] >> np.uint64(b)) & np.uint64(1)).astype(np.uint8)
+            st[..., pos // 8] |= (bit << (pos % 8)).astype(np.uint8)
+    st = st.reshape(Rp // 32, 32, G, 2, 24).transpose(0, 2, 3, 1, 4)
+    out = np.zeros((Rp // 32, G, 1536), dtype=np.uint8)
+    out[:, :, :1024] = st[..., :16].reshape(Rp // 32, G, 1024)
+    out[:, :, 1024:] = st[..., 16:].reshape(Rp // 32, G, 512)
+    return out.reshape(-1)
