@@ -275,6 +275,57 @@ def _time_lm(torch, oq, WL, bits, reps=40, warmup=5):
     return e
 
 
+def _time_asym(torch, oq, WL, reps=40, warmup=5):
+    """Asymmetric INT4 weights (CentriQ Eq. 2, codes Q - 8 with the group-sum
+    correction) on the 4096 x 3072 workload (RPBH h = 1024; outputs 3072 and
+    12288): the rotate/quant writer with group sums, then the tiled FP6 GEMM
+    whose accumulators start at -sum_g C p.  Weight quantization and prepack
+    are offline (untimed)."""
+    wl = WL.make_workload(2)
+    dev = torch.device("cuda:0")
+    M, K = wl.M, wl.K
+    rot = oq.Rotation.rpbh(torch.from_numpy(wl.perm).to(dev), torch.from_numpy(wl.signs).to(dev), wl.spec.block)
+    ws = []
+    for W in wl.weights:
+        q = oq.oq_quant_weight_asym(torch.from_numpy(W).to(dev), rot, 64)
+        ws.append((W.shape[0], oq.oq_prepack_w4_asym(q["codes"], q["sigma"], q["zero"], W.shape[0], K, 64)))
+    x0 = torch.from_numpy(wl.x_bits.view("int16")).to(dev)
+    xs = [x0] + [x0.clone() for _ in range(7)]
+    fmt = oq.OQ_A4 | oq.OQ_TILED
+    codes = torch.empty(oq.oq_tiled_bytes(M, K), dtype=torch.uint8, device=dev)
+    scale = torch.empty(M, dtype=torch.float32, device=dev)
+    gsum = torch.empty((K // 64, M), dtype=torch.float32, device=dev)
+    ys = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for N, _ in ws]
+
+    def launches(i):
+        out = [("rotate_quant", lambda: oq.oq_quant_act_gsum(xs[i % len(xs)], rot, fmt, codes=codes, scale=scale,
+                                                             gsum=gsum))]
+        for (N, w), y in zip(ws, ys):
+            out.append((f"gemm_n{N}", lambda N=N, w=w, y=y: oq.oq_gemm_w4a4_asym(codes, scale, gsum, w, N, M, K, y=y)))
+        return out
+
+    for i in range(warmup):
+        for _, f in launches(i):
+            f()
+    torch.cuda.synchronize()
+    names = [n for n, _ in launches(0)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(reps)]
+    for i in range(reps):
+        ev[i][0].record()
+        for k, (_, f) in enumerate(launches(i)):
+            f()
+            ev[i][k + 1].record()
+    torch.cuda.synchronize()
+    per = {n: sum(ev[i][k].elapsed_time(ev[i][k + 1]) for i in range(reps)) / reps for k, n in enumerate(names)}
+    e = {"rotate_quant_us": round(per["rotate_quant"] * 1e3, 3)}
+    for N, _ in ws:
+        t = per[f"gemm_n{N}"]
+        tops = 2.0 * M * K * N / (t * 1e-3) / 1e12
+        e[f"gemm_n{N}"] = {"us": round(t * 1e3, 2), "TOPS": round(tops, 1), "frac": round(tops / PEAK_INT8_TOPS, 4)}
+    e["step_ms"] = round(sum(per.values()), 4)
+    return e
+
+
 def _copy_reference(torch, nbytes=1 << 30, reps=3):
     """A plain device-to-device copy of known size, launched beside the
     profiled kernels so that HBM byte counters can be scaled by what they
@@ -437,6 +488,7 @@ def main():
             side[s2.name] = e
         result["other_configs"] = side
         result["lloyd_max_4096x3072"] = {f"A{b}": _time_lm(torch, oq, WL, b) for b in (4, 8)}
+        result["asym_w4a4_4096x3072"] = _time_asym(torch, oq, WL)
 
     if not args.no_cpu_baseline and not args.only_step:
         result["cpu_baseline"] = _cpu_baseline(WL)

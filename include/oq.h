@@ -391,16 +391,21 @@ int oq_quant_weight_asym(const float *w, int32_t N, int32_t K, int64_t ldw, cons
  * oq_prepack_w4_asym -- repack asymmetric weights for oq_gemm_w4a4_asym:
  * w_tiled (oq_tiled_bytes(N, K) bytes) holds q'/2 for q' = Q - 8 in the tiled
  * FP6 layout; w_scale_t float32 [K/64][N rounded up to 32] = sigma;
- * corr float32 [N rounded up to 32][K/64] = RN32(sigma RN32(z - 8)).
+ * corr [K/64][N rounded up to 32] pairs of uint32 (8 bytes, 8-byte aligned):
+ * C = RN32(sigma RN32(z - 8)) as the three bfloat16 pieces of its truncation
+ * split C = c1 + c2 + c3 (each exactly a bfloat16), stored negated as
+ * (-c1 | -c2 << 16, -c3); C = -(c1' + c2' + c3') recovers it exactly.
+ * (Both tables are group-major so that a row of outputs reads them as one run.)
  * Padding rows get zeros.  group must be 64.
  */
 int oq_prepack_w4_asym(const uint8_t *w, const uint16_t *sigma, const uint16_t *zero, int32_t N, int32_t K,
-                       int32_t group, uint8_t *w_tiled, float *w_scale_t, float *corr, hipStream_t stream);
+                       int32_t group, uint8_t *w_tiled, float *w_scale_t, uint32_t *corr, hipStream_t stream);
 
 /*
  * oq_quant_act_gsum -- oq_quant_act for afmt OQ_A4 | OQ_TILED or
  * OQ_A6 | OQ_TILED (OQ_SCALE_PCTL allowed), which also writes gsum float32
- * [M][d/64], the sum of the codes of every 64-wide group (exact integers).
+ * [d/64][M] (group-major), the sum of the codes of every 64-wide group
+ * (exact integers).
  * d % 64 == 0, d <= 4096.
  */
 int oq_quant_act_gsum(const uint16_t *x, int64_t M, int32_t d, int64_t ldx, const oq_rot *rot, int center, int afmt,
@@ -409,13 +414,13 @@ int oq_quant_act_gsum(const uint16_t *x, int64_t M, int32_t d, int64_t ldx, cons
 /*
  * oq_gemm_w4a4_asym -- tiled 4-bit activations times asymmetric weights:
  *   y[t][o] = bf16_RNE( a_scale[t] * sum_g (sigma[o][g] acc_g[t][o]
- *                        - corr[o][g] gsum[t][g]) + mean[t] w1[o] + bias[o] )
+ *                        - corr[g][o] gsum[g][t]) + mean[t] w1[o] + bias[o] )
  *   acc_g = exact sum over the group of q_a (Q - 8).
  * afmt must be OQ_A4 | OQ_TILED; qa, a_scale, gsum from oq_quant_act_gsum;
  * w_tiled, w_scale_t, corr from oq_prepack_w4_asym; K % 64 == 0.
  */
 int oq_gemm_w4a4_asym(int afmt, const uint8_t *qa, const float *a_scale, const float *gsum, int64_t M, int32_t K,
-                      const uint8_t *w_tiled, const float *w_scale_t, const float *corr, int32_t N, const float *mean,
+                      const uint8_t *w_tiled, const float *w_scale_t, const uint32_t *corr, int32_t N, const float *mean,
                       const float *w1, const float *bias, uint16_t *y, int64_t ldy, hipStream_t stream);
 
 enum { OQ_OP_GEMM_W4A8 = 1, OQ_OP_GEMM_W4A4 = 2, OQ_OP_LINEAR = 3, OQ_OP_GEMM_LM = 4 };

@@ -392,7 +392,7 @@ def oq_prepack_w4_asym(w, sigma, zero, N: int, K: int, group: int = 64):
     Np = (N + 31) // 32 * 32
     w_tiled = torch.empty(max(16, oq_tiled_bytes(N, K)), dtype=torch.uint8, device=dev)
     w_scale_t = torch.empty((K // 64, Np), dtype=torch.float32, device=dev)
-    corr = torch.empty((Np, K // 64), dtype=torch.float32, device=dev)
+    corr = torch.empty((K // 64, Np, 2), dtype=torch.int32, device=dev)
     _check(_lib.oq_prepack_w4_asym(_p(w), _p(sigma), _p(zero), N, K, group, _p(w_tiled), _p(w_scale_t), _p(corr),
                                    _stream()))
     return {"codes": w_tiled, "scales": w_scale_t, "corr": corr}
@@ -410,7 +410,7 @@ def oq_quant_act_gsum(x, rot: Optional[Rotation], afmt: int, center: bool = Fals
     if scale is None:
         scale = torch.empty(M, dtype=torch.float32, device=dev)
     if gsum is None:
-        gsum = torch.empty((M, d // 64), dtype=torch.float32, device=dev)
+        gsum = torch.empty((d // 64, M), dtype=torch.float32, device=dev)
     if center and mean is None:
         mean = torch.empty(M, dtype=torch.float32, device=dev)
     _check(_lib.oq_quant_act_gsum(_p(x), M, d, x.stride(0), _rref(rot), int(center), afmt, _p(codes), _p(scale),

@@ -707,14 +707,15 @@ int oq_quant_weight_asym(const float *w, int32_t N, int32_t K, int64_t ldw, cons
 }
 
 int oq_prepack_w4_asym(const uint8_t *w, const uint16_t *sigma, const uint16_t *zero, int32_t N, int32_t K,
-                       int32_t group, uint8_t *w_tiled, float *w_scale_t, float *corr, hipStream_t stream) {
+                       int32_t group, uint8_t *w_tiled, float *w_scale_t, uint32_t *corr, hipStream_t stream) {
   const char *fn = "oq_prepack_w4_asym";
   if (N < 0) return fail(OQ_ERR_INVALID_ARG, "%s: N < 0", fn);
   if (K <= 0 || K % 64) return fail(OQ_ERR_UNSUPPORTED, "%s: K=%d must be a positive multiple of 64", fn, K);
   if (group != 64) return fail(OQ_ERR_UNSUPPORTED, "%s: group must be 64 (got %d)", fn, group);
   if (N > 0 && (!w || !sigma || !zero || !w_tiled || !w_scale_t || !corr))
     return fail(OQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
-  if (!al16(w) || !al16(w_tiled)) return fail(OQ_ERR_ALIGNMENT, "%s: misaligned", fn);
+  if (!al16(w) || !al16(w_tiled) || (reinterpret_cast<uintptr_t>(corr) & 7))
+    return fail(OQ_ERR_ALIGNMENT, "%s: misaligned", fn);
   g_err[0] = 0;
   return hip_status(launch_prepack_w4a(w, sigma, zero, N, K, w_tiled, w_scale_t, corr, stream), fn);
 }
@@ -751,7 +752,7 @@ int oq_quant_act_gsum(const uint16_t *x, int64_t M, int32_t d, int64_t ldx, cons
 }
 
 int oq_gemm_w4a4_asym(int afmt, const uint8_t *qa, const float *a_scale, const float *gsum, int64_t M, int32_t K,
-                      const uint8_t *w_tiled, const float *w_scale_t, const float *corr, int32_t N, const float *mean,
+                      const uint8_t *w_tiled, const float *w_scale_t, const uint32_t *corr, int32_t N, const float *mean,
                       const float *w1, const float *bias, uint16_t *y, int64_t ldy, hipStream_t stream) {
   const char *fn = "oq_gemm_w4a4_asym";
   if (afmt != (OQ_A4 | OQ_TILED)) return fail(OQ_ERR_UNSUPPORTED, "%s: afmt must be OQ_A4 | OQ_TILED", fn);
@@ -760,6 +761,7 @@ int oq_gemm_w4a4_asym(int afmt, const uint8_t *qa, const float *a_scale, const f
   if ((mean == nullptr) != (w1 == nullptr)) return fail(OQ_ERR_INVALID_ARG, "%s: mean and w1 must be given together", fn);
   if (M == 0 || N == 0) return OQ_OK;
   if (!a_scale || !gsum || !corr) return fail(OQ_ERR_INVALID_ARG, "%s: NULL scale, gsum or corr", fn);
+  if (reinterpret_cast<uintptr_t>(corr) & 7) return fail(OQ_ERR_ALIGNMENT, "%s: corr must be 8-byte aligned", fn);
   g_err[0] = 0;
   return hip_status(launch_gemm_fp6_asym(qa, a_scale, gsum, M, K, w_tiled, w_scale_t, corr, N, mean, w1, bias, y, ldy,
                                          stream),

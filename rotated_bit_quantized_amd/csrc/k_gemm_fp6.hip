@@ -356,11 +356,13 @@ __device__ __forceinline__ uint32_t fp6_e2m3_of_half(int q) {
 }
 
 // canonical asymmetric codes q' = Q - 8 [N][K/2] + bfloat16 sigma, z [N][G] ->
-// tiled FP6 of q'/2, sigma transposed [G][Np] float32, C = RN32(sigma
-// RN32(z - 8)) [Np][G] float32 (padding rows: zero codes, scale and C)
+// tiled FP6 of q'/2, sigma transposed [G][Np] float32, and C = RN32(sigma
+// RN32(z - 8)) transposed [G][Np] as the three bfloat16 pieces of -C (the
+// truncation split C = c1 + c2 + c3, each exactly a bfloat16), packed as
+// (-c1 | -c2 << 16, -c3) (padding rows: zero codes, scale and C)
 __global__ void prepack_w4a_kernel(const uint8_t *__restrict__ w, const uint16_t *__restrict__ sig,
                                    const uint16_t *__restrict__ zero, int N, int Np, int K, uint8_t *__restrict__ out,
-                                   float *__restrict__ out_s, float *__restrict__ out_c) {
+                                   float *__restrict__ out_s, uint2 *__restrict__ out_c) {
   const int G = K / 64;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t total = (int64_t)Np * G * 2;
@@ -401,8 +403,13 @@ __global__ void prepack_w4a_kernel(const uint8_t *__restrict__ w, const uint16_t
       const float zv = __uint_as_float((uint32_t)zero[(int64_t)row * G + kg] << 16);
       cv = sv * (zv - 8.0f);
     }
+    const uint32_t c1 = __float_as_uint(cv) & 0xFFFF0000u;
+    const float rem = cv - __uint_as_float(c1);
+    const uint32_t c2 = __float_as_uint(rem) & 0xFFFF0000u;
+    const uint32_t c3 = __float_as_uint(rem - __uint_as_float(c2));
+    const uint32_t n1 = (c1 ^ 0x80000000u) >> 16, n2 = (c2 ^ 0x80000000u) >> 16, n3 = (c3 ^ 0x80000000u) >> 16;
     out_s[(int64_t)kg * Np + row] = sv;
-    out_c[(int64_t)row * G + kg] = cv;
+    out_c[(int64_t)kg * Np + row] = make_uint2(n1 | (n2 << 16), n3);
   }
 }
 
@@ -485,7 +492,7 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_sc
                    const uint8_t *__restrict__ W, const float *__restrict__ wst, int N, int Np,
                    const float *__restrict__ mean, const float *__restrict__ w1, const float *__restrict__ bias,
                    uint16_t *__restrict__ y, int64_t ldy, const float *__restrict__ gsum,
-                   const float *__restrict__ corr) {
+                   const uint2 *__restrict__ corr) {
   using V2 = V2C<NSLOT>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const uint32_t lds0 = lds_addr_of(smem);
@@ -496,6 +503,15 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_sc
   const int n0 = blockIdx.x * V2::BN;
   const int64_t mblocks = (M + 31) / 32;
   const int nblocks = Np / 32;
+
+  float F[4][2][16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) F[i][j][e] = 0.f;
+
 
   // ---- copy units of this wave (stage 0 addresses; k-group kg adds kg * 1536)
   const uint8_t *cbase[3];
@@ -537,74 +553,6 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_sc
   const int tail = 1024 - 8 * lane;
   const float *fs = reinterpret_cast<const float *>(smem + V2::A_BYTES + V2::B_BYTES) + wn * 64 + r;
 
-  float F[4][2][16];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) F[i][j][e] = 0.f;
-
-  if constexpr (ASYM) {
-    // F = -sum_g C[o][g] p[t][g]: depth 8 G in bfloat16, slot 8 g + s holds
-    // piece s / 3 of p (p1 = p with its low three bits cleared, p2 = those
-    // bits: both exact in bfloat16 for |p| < 2048) against piece s % 3 of -C
-    // (the truncation split C = c1 + c2 + c3, each exactly a bfloat16); slots
-    // 6 and 7 are zero.  Lanes 0-31 take group 2 ch, lanes 32-63 group 2 ch + 1.
-    const int Gq = K / 64;
-    const int r0 = lane & 31, hf = lane >> 5;
-    int64_t prow[4];
-    int ccol[2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t rr = m0 + (wave >> 2) * 128 + 32 * i + r0;
-      prow[i] = rr < M ? rr : M - 1;
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int cc = n0 + (wave & 3) * 64 + 32 * j + r0;
-      ccol[j] = cc < Np ? cc : Np - 1;
-    }
-    v16f E[4][2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) E[i][j] = (v16f){};
-    for (int ch = 0; ch < (Gq + 1) / 2; ++ch) {
-      const int g = 2 * ch + hf;
-      const bool gv = g < Gq;
-      const int gg = gv ? g : 0;
-      uint4 av[4], bv[2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int pv = gv ? (int)gsum[prow[i] * Gq + gg] : 0;
-        const uint32_t h1 = __float_as_uint((float)(pv & ~7)) >> 16;
-        const uint32_t h2 = __float_as_uint((float)(pv & 7)) >> 16;
-        av[i] = make_uint4(h1 | (h1 << 16), h1 | (h2 << 16), h2 | (h2 << 16), 0u);
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const float cf = gv ? corr[(int64_t)ccol[j] * Gq + gg] : 0.f;
-        const uint32_t c1 = __float_as_uint(cf) & 0xFFFF0000u;
-        const float rem = cf - __uint_as_float(c1);
-        const uint32_t c2 = __float_as_uint(rem) & 0xFFFF0000u;
-        const uint32_t c3 = __float_as_uint(rem - __uint_as_float(c2));
-        const uint32_t n1 = (c1 ^ 0x80000000u) >> 16, n2 = (c2 ^ 0x80000000u) >> 16, n3 = (c3 ^ 0x80000000u) >> 16;
-        bv[j] = make_uint4(n1 | (n2 << 16), n3 | (n1 << 16), n2 | (n3 << 16), 0u);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          E[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av[i]), as_bf16x8(bv[j]), E[i][j], 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) F[i][j][e] = E[i][j][e];
-  }
   // E8M0 scale of the weight operand: 2^1 for the stored q'/2 of asymmetric codes
   const int wsc = ASYM ? 128 : 127;
 
@@ -720,6 +668,88 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_sc
     }
   }
 
+  if constexpr (ASYM) {
+    // F -= sum_g C[o][g] p[t][g], after the main loop (its registers are free
+    // then): depth 8 G in bfloat16, slot 8 g + s holds piece s / 3 of p (p1 =
+    // p with its low three bits cleared, p2 = those bits: both exact in
+    // bfloat16 for |p| < 2048) against piece s % 3 of -C (the truncation
+    // split C = c1 + c2 + c3, each exactly a bfloat16); slots 6 and 7 are
+    // zero.  Lanes 0-31 take group 2 ch, lanes 32-63 group 2 ch + 1.  p and C
+    // are stored group-major, so the 32 rows (columns) of a fragment are one
+    // contiguous 128-byte read; the next pair of groups is loaded under the
+    // MFMAs of the current one.
+    const int Gq = K / 64;
+    const int r0 = lane & 31, hf = lane >> 5;
+    int prow[4], ccol[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t rr = m0 + wm * 128 + 32 * i + r0;
+      prow[i] = (int)(rr < M ? rr : M - 1);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int cc = n0 + wn * 64 + 32 * j + r0;
+      ccol[j] = cc < Np ? cc : Np - 1;
+    }
+    const int nch = (Gq + 1) / 2;
+    // a ring of PF prefetched steps: the loads of step ch + PF - 1 are issued
+    // before the MFMAs of step ch
+    constexpr int PF = 4;
+    float pn[PF][4];
+    uint2 cn[PF][2];
+    auto fetch = [&](float (&pd)[4], uint2 (&cd)[2], int ch) {
+      const int g = 2 * ch + hf;
+      const bool gv = ch < nch && g < Gq;
+      const int gg = gv ? g : Gq - 1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pd[i] = gsum[(int64_t)gg * M + prow[i]];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) cd[j] = corr[(int64_t)gg * Np + ccol[j]];
+      if (!gv) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pd[i] = 0.f;
+        cd[0] = cd[1] = make_uint2(0u, 0u);
+      }
+    };
+    auto step = [&](const float (&pc)[4], const uint2 (&cc2)[2]) {
+      uint4 av[4], bv[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // p1 = 8 floor(p / 8), p2 = p - p1, both exact (p is an integer below 2^11)
+        const float p1 = __builtin_floorf(pc[i] * 0.125f) * 8.0f;
+        const uint32_t b1 = __float_as_uint(p1), b2 = __float_as_uint(pc[i] - p1);
+        av[i] = make_uint4(__builtin_amdgcn_perm(b1, b1, 0x07060302u), __builtin_amdgcn_perm(b2, b1, 0x07060302u),
+                           __builtin_amdgcn_perm(b2, b2, 0x07060302u), 0u);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t x = cc2[j].x, yv = cc2[j].y;  // (n1 | n2 << 16), n3
+        bv[j] = make_uint4(x, (x << 16) | yv, __builtin_amdgcn_perm(yv, x, 0x05040302u), 0u);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          v16f acc;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[e] = F[i][j][e];
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av[i]), as_bf16x8(bv[j]), acc, 0, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 16; ++e) F[i][j][e] = acc[e];
+        }
+    };
+#pragma unroll
+    for (int q = 0; q < PF - 1; ++q) fetch(pn[q], cn[q], q);
+    // steps past nch fetch zeros and add nothing; the loop runs whole rings
+    for (int ch0 = 0; ch0 < nch; ch0 += PF) {
+#pragma unroll
+      for (int q = 0; q < PF; ++q) {
+        fetch(pn[(q + PF - 1) % PF], cn[(q + PF - 1) % PF], ch0 + q + PF - 1);
+        if (ch0 + q < nch) step(pn[q], cn[q]);
+      }
+    }
+  }
+
   // ---- epilogue: y = a_scale * F + mean * w1 + bias (same order as the other
   // kernels), bf16, staged per 32-row slab in this wave's own LDS area (no
   // workgroup barrier) so that the global writes are 16-byte runs
@@ -781,7 +811,7 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_sc
 template <int NSLOT, bool PAIRED, bool ASYM>
 hipError_t launch_v2(const uint8_t *A, const float *a_scale, int64_t M, int K, const uint8_t *W, const float *wst,
                      int N, int Np, const float *mean, const float *w1, const float *bias, uint16_t *y, int64_t ldy,
-                     hipStream_t stream, const float *gsum = nullptr, const float *corr = nullptr) {
+                     hipStream_t stream, const float *gsum = nullptr, const uint32_t *corr = nullptr) {
   using V2 = V2C<NSLOT>;
   static bool attr_set = false;
   if (!attr_set) {
@@ -792,7 +822,7 @@ hipError_t launch_v2(const uint8_t *A, const float *a_scale, int64_t M, int K, c
   }
   dim3 grid((unsigned)((N + V2::BN - 1) / V2::BN), (unsigned)((M + V2::BM - 1) / V2::BM));
   hipLaunchKernelGGL((gemm_fp6_v2_kernel<NSLOT, PAIRED, ASYM>), grid, dim3(512), V2::LDS_BYTES, stream, A, a_scale, M, K,
-                     W, wst, N, Np, mean, w1, bias, y, ldy, gsum, corr);
+                     W, wst, N, Np, mean, w1, bias, y, ldy, gsum, reinterpret_cast<const uint2 *>(corr));
   return hipGetLastError();
 }
 
@@ -812,7 +842,7 @@ hipError_t launch_gemm_fp6(const uint8_t *A, int planes, const float *a_scale, i
 }
 
 hipError_t launch_gemm_fp6_asym(const uint8_t *A, const float *a_scale, const float *gsum, int64_t M, int K,
-                                const uint8_t *W, const float *wst, const float *corr, int N, const float *mean,
+                                const uint8_t *W, const float *wst, const uint32_t *corr, int N, const float *mean,
                                 const float *w1, const float *bias, uint16_t *y, int64_t ldy, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   const int Np = (N + 31) / 32 * 32;
@@ -822,12 +852,12 @@ hipError_t launch_gemm_fp6_asym(const uint8_t *A, const float *a_scale, const fl
 }
 
 hipError_t launch_prepack_w4a(const uint8_t *w, const uint16_t *sig, const uint16_t *zero, int N, int K, uint8_t *out,
-                              float *out_s, float *out_c, hipStream_t stream) {
+                              float *out_s, uint32_t *out_c, hipStream_t stream) {
   if (N == 0) return hipSuccess;
   const int Np = (N + 31) / 32 * 32;
   const int64_t total = (int64_t)Np * (K / 64) * 2;
   hipLaunchKernelGGL(prepack_w4a_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, w, sig, zero, N,
-                     Np, K, out, out_s, out_c);
+                     Np, K, out, out_s, reinterpret_cast<uint2 *>(out_c));
   return hipGetLastError();
 }
 

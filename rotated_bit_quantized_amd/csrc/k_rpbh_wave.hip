@@ -626,10 +626,9 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
           pa0 += xlane(pa0, 1);
           pb0 += xlane(pb0, 0);
           pb0 += xlane(pb0, 1);
-          if ((il & 3) == 0) {
-            float *gr = gsum_out + row * (int64_t)(d >> 6);
-            if (wa) gr[(1024 * s0 + 16 * il) >> 6] = pa0;
-            if (wb) gr[(1024 * (s0 + 1) + 16 * il) >> 6] = pb0;
+          if ((il & 3) == 0) {  // group-major [d / 64][M]
+            if (wa) gsum_out[(int64_t)((1024 * s0 + 16 * il) >> 6) * M + row] = pa0;
+            if (wb) gsum_out[(int64_t)((1024 * (s0 + 1) + 16 * il) >> 6) * M + row] = pb0;
           }
         }
         if (mode == OUT_FP6) {

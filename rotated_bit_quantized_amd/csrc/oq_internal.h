@@ -110,7 +110,7 @@ struct LmArgs {
 // percentile range instead of absmax (integer outputs, rows the wave kernel
 // takes only); the OUT_LM* modes take their codebook from lm (wave kernel
 // only); gsum (tiled FP6 modes, wave kernel only), if set, receives the sums
-// of the codes of every 64-wide group, float32 [M][d/64].
+// of the codes of every 64-wide group, float32 group-major [d/64][M].
 hipError_t launch_rpbh_quant(const uint16_t *x, int64_t M, int d, int64_t ldx,
                              const RotArgs &rot, int center, float *mean,
                              int out_mode, int qmax, void *out, int64_t ld_out_bytes,
@@ -147,11 +147,12 @@ hipError_t launch_prepack_w4(const uint8_t *w, const float *ws, int N, int K, ui
 // Tiled A4 x asymmetric INT4 weights (codes q'/2 with weight scale 2^1), with
 // F initialised to -sum_g corr[o][g] gsum[t][g] (single plane, group 64)
 hipError_t launch_gemm_fp6_asym(const uint8_t *A, const float *a_scale, const float *gsum, int64_t M, int K,
-                                const uint8_t *W, const float *wst, const float *corr, int N, const float *mean,
+                                const uint8_t *W, const float *wst, const uint32_t *corr, int N, const float *mean,
                                 const float *w1, const float *bias, uint16_t *y, int64_t ldy, hipStream_t stream);
-// canonical asymmetric codes + bfloat16 sigma, z -> tiled q'/2, sigma [G][Np], C [Np][G]
+// canonical asymmetric codes + bfloat16 sigma, z -> tiled q'/2, sigma [G][Np],
+// -C as three bfloat16 pieces [G][Np][2] (uint32 pairs)
 hipError_t launch_prepack_w4a(const uint8_t *w, const uint16_t *sig, const uint16_t *zero, int N, int K, uint8_t *out,
-                              float *out_s, float *out_c, hipStream_t stream);
+                              float *out_s, uint32_t *out_c, hipStream_t stream);
 
 // K5: MXFP4 x MXFP4 with E8M0 block scales (scaled FP4 MFMA); tiled_in: both
 // operands in the tiled MXFP4 layout (codes + scale words), else row-major.

@@ -98,9 +98,17 @@ def test_prepack_w4_asym(oq, N, K):
     st = to_host(out["scales"])
     np.testing.assert_array_equal(st[:, :N], sig.T)
     assert not st[:, N:].any()
-    C = to_host(out["corr"])
-    np.testing.assert_array_equal(C[:N], OA.correction(sig, z))
-    assert C.shape == (Np, G) and not C[N:].any()
+    pk = to_host(out["corr"]).view(np.uint32)
+    assert pk.shape == (G, Np, 2)
+
+    def bf(bits):
+        return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+    # -C as three bfloat16 pieces: their exact sum is -C
+    C = -(bf(pk[..., 0] & 0xFFFF) + bf(pk[..., 0] >> 16) + bf(pk[..., 1] & 0xFFFF))
+    np.testing.assert_array_equal(C[:, :N], OA.correction(sig, z).T.astype(np.float64))
+    assert not C[:, N:].any()  # padding columns: C = 0 (stored as -0 pieces)
+    assert not (pk[..., 1] >> 16).any()
 
 
 @pytest.mark.parametrize("M,K,h,rounds,center,pctl", [(37, 1024, 128, 1, False, False), (70, 3072, 1024, 1, True, False),
@@ -127,7 +135,7 @@ def test_act_group_sums(oq, M, K, h, rounds, center, pctl):
     live = row_mask(M, K)
     np.testing.assert_array_equal(to_host(out["codes"])[live], to_host(plain["codes"])[live])
     np.testing.assert_array_equal(to_host(out["scale"]), to_host(canon["scale"]))
-    np.testing.assert_array_equal(to_host(out["gsum"]), OA.group_sums(codes, 64).astype(np.float32))
+    np.testing.assert_array_equal(to_host(out["gsum"]), OA.group_sums(codes, 64).astype(np.float32).T)
 
 
 GEMM_CASES = [(300, 1024, 520, True, True), (257, 512, 256, False, False), (33, 128, 40, False, True),
@@ -149,7 +157,7 @@ def test_gemm_asym(oq, M, K, N, center, bias):
     w1 = rng.standard_normal(N).astype(np.float32) if center else None
     b = rng.standard_normal(N).astype(np.float32) if bias else None
     w = oq.oq_prepack_w4_asym(to_dev(OQ.pack_int4(Q - 8)), to_dev(_bits(sig)), to_dev(_bits(z)), N, K, 64)
-    gs = OA.group_sums(qa, 64).astype(np.float32)
+    gs = np.ascontiguousarray(OA.group_sums(qa, 64).astype(np.float32).T)
     dev = lambda a: None if a is None else to_dev(a)  # noqa: E731
     y = oq.oq_gemm_w4a4_asym(to_dev(tile(qa)), to_dev(alpha), to_dev(gs), w, N, M, K, mean=dev(mean), w1=dev(w1),
                              bias=dev(b))
@@ -182,7 +190,7 @@ def test_asym_layer_full_size(oq):
     codes = OQ.unpack_int4(to_host(canon["codes"]).view(np.uint8))[rows]
     ref = OL.activations_int(wl.x_bits[rows], wl.perm, wl.signs, wl.spec.block, 4, False)
     check_codes(codes, ref["codes"], ref["flags"], "full-size codes")
-    np.testing.assert_array_equal(to_host(act["gsum"])[rows], OA.group_sums(codes, 64).astype(np.float32))
+    np.testing.assert_array_equal(to_host(act["gsum"])[:, rows], OA.group_sums(codes, 64).astype(np.float32).T)
     alpha = to_host(act["scale"])[rows]
     y_ref, S = OA.linear_asym(alpha, codes, qw, sig, OA.correction(sig, z), 64)
     frac = check_output(to_host(y)[rows], y_ref, S, 7 * (K // 64), "asym full-size output")
