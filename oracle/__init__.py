@@ -36,5 +36,7 @@ Modules:
             the float16 dequantizing product
   asym      asymmetric grouped INT4 weights (CentriQ Eq. 2, App. B.2): RTN
             min-max scale and shift, stored offset codes, the corrected product
+  kron      the factorised Paley x Sylvester rotation with zero padding
+            (CentriQ Sec. 4.2 "Rotation", App. B.1)
 """
-from . import hadamard, rotation, quant, gemm, linear, lloyd_max, asym  # noqa: F401
+from . import hadamard, rotation, quant, gemm, linear, lloyd_max, asym, kron  # noqa: F401

@@ -54,14 +54,15 @@ def scale_fp32(h: int) -> np.float32:
     return np.float32(1.0 / np.sqrt(float(h)))
 
 
-def fwht_fp32_canonical(u: np.ndarray, h: int) -> np.ndarray:
+def fwht_fp32_canonical(u: np.ndarray, h: int, scale: bool = True) -> np.ndarray:
     """Block Walsh-Hadamard in the canonical float32 order.
 
     The pages fix the matrix but not the evaluation order; the order used to
     define float32 results (and therefore the integer codes) is: butterfly
     stages with strides 1, 2, 4, ..., h/2 in that order, each butterfly
     (a, b) -> (a + b, a - b) rounded once to float32, then one float32
-    multiplication of every output by c_h = RN32(1/sqrt h)."""
+    multiplication of every output by c_h = RN32(1/sqrt h) (left out with
+    scale=False, for transforms that normalise once at the end)."""
     u = np.asarray(u, dtype=np.float32)
     d = u.shape[-1]
     if d % h:
@@ -78,5 +79,6 @@ def fwht_fp32_canonical(u: np.ndarray, h: int) -> np.ndarray:
         out[..., 1, :] = lo - hi
         a = out.reshape(lead + (d // h, h))
         s *= 2
-    a = a * scale_fp32(h)
+    if scale:
+        a = a * scale_fp32(h)
     return a.reshape(u.shape).astype(np.float32)
