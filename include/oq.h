@@ -55,7 +55,7 @@ enum {
 };
 
 /* rotation kinds */
-enum { OQ_ROT_RPBH = 1, OQ_ROT_DENSE32 = 2 };
+enum { OQ_ROT_RPBH = 1, OQ_ROT_DENSE32 = 2, OQ_ROT_KRON = 3 };
 
 /* activation code formats (the value is the bit width for integer codes) */
 enum { OQ_A8 = 8, OQ_A6 = 6, OQ_A4 = 4, OQ_MXFP4 = 0x104 };
@@ -422,6 +422,30 @@ int oq_quant_act_gsum(const uint16_t *x, int64_t M, int32_t d, int64_t ldx, cons
 int oq_gemm_w4a4_asym(int afmt, const uint8_t *qa, const float *a_scale, const float *gsum, int64_t M, int32_t K,
                       const uint8_t *w_tiled, const float *w_scale_t, const uint32_t *corr, int32_t N, const float *mean,
                       const float *w1, const float *bias, uint16_t *y, int64_t ldy, hipStream_t stream);
+
+/*
+ * Factorised Paley x Sylvester rotation (CentriQ Sec. 4.2 "Rotation", App.
+ * B.1): H = (H_m (x) H_b) / sqrt(m b) with H_b Sylvester (b = 2^k) and H_m
+ * a Paley matrix (m = 12, 44: type I with q = 11, 43; m = 36: type II with
+ * q = 17; m = 1: none), applied as vec(H_b X H_m^T) to the token reshaped
+ * column-major to X in R^{b x m}; a row of native width n < m b is centred
+ * over its n coordinates and then zero-padded to m b (centering precedes
+ * padding).  Descriptor: oq_rot{kind = OQ_ROT_KRON, d = n, block = b,
+ * rounds = m, perm = signs = mats = NULL}.  Every output of the rotation,
+ * and every code and weight column, has the padded width m b; the GEMMs take
+ * K = m b.  oq_rotate, oq_quant_act (integer formats, tiled or not, absmax
+ * scale) and oq_quant_weight / oq_quant_weight_asym accept it;
+ * oq_linear_fused, group sums, Lloyd-Max codes and the percentile scale do not.
+ * Float32 order: un-normalised Sylvester stages on each block, then the
+ * m-term sums in increasing c, then one multiply by RN32(1/sqrt(m b)).
+ */
+
+/*
+ * oq_kron_plan -- host function: the smallest admissible padded width
+ * n_pad = m * block >= n with m in {1, 12, 36, 44} and block a power of two
+ * of at least 16 (one thread's share of coordinates).  n <= 16384.
+ */
+int oq_kron_plan(int32_t n, int32_t *m, int32_t *block, int32_t *n_pad);
 
 enum { OQ_OP_GEMM_W4A8 = 1, OQ_OP_GEMM_W4A4 = 2, OQ_OP_LINEAR = 3, OQ_OP_GEMM_LM = 4 };
 

@@ -19,7 +19,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "liboq.so")
 
 OQ_OK, OQ_ERR_INVALID_ARG, OQ_ERR_UNSUPPORTED, OQ_ERR_ALIGNMENT, OQ_ERR_WORKSPACE, OQ_ERR_HIP = range(6)
-OQ_ROT_RPBH, OQ_ROT_DENSE32 = 1, 2
+OQ_ROT_RPBH, OQ_ROT_DENSE32, OQ_ROT_KRON = 1, 2, 3
 OQ_A8, OQ_A6, OQ_A4, OQ_MXFP4 = 8, 6, 4, 0x104
 OQ_W4, OQ_W_MXFP4 = 4, 0x104
 OQ_OP_GEMM_W4A8, OQ_OP_GEMM_W4A4, OQ_OP_LINEAR, OQ_OP_GEMM_LM = 1, 2, 3, 4
@@ -78,6 +78,7 @@ def _load():
         "oq_quant_act_gsum": ([vp, i64, i32, i64, vp, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp], ctypes.c_int),
         "oq_gemm_w4a4_asym": ([ctypes.c_int, vp, vp, vp, i64, i32, vp, vp, vp, i32, vp, vp, vp, vp, i64, vp],
                               ctypes.c_int),
+        "oq_kron_plan": ([i32, vp, vp, vp], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -91,7 +92,7 @@ EXPORTED = ("oq_last_error", "oq_center", "oq_rotate", "oq_quant_act", "oq_quant
             "oq_gemm_w4a8", "oq_gemm_w4a4", "oq_linear_fused", "oq_workspace_bytes", "oq_tiled_bytes",
             "oq_prepack_w4", "oq_tiled_mx_bytes", "oq_prepack_mx", "oq_lloyd_max_levels", "oq_lloyd_max_tables",
             "oq_tiled_f16_bytes", "oq_quant_act_lm", "oq_prepack_w16", "oq_gemm_lm", "oq_quant_weight_asym",
-            "oq_prepack_w4_asym", "oq_quant_act_gsum", "oq_gemm_w4a4_asym")
+            "oq_prepack_w4_asym", "oq_quant_act_gsum", "oq_gemm_w4a4_asym", "oq_kron_plan")
 
 
 def lib():
@@ -139,6 +140,18 @@ class Rotation:
         return Rotation(OQ_ROT_RPBH, perm.shape[-1], block, perm.shape[0], perm=perm, signs=signs)
 
     @staticmethod
+    def kron(n: int) -> "Rotation":
+        """The Paley x Sylvester rotation for native width n at the smallest
+        admissible padded width (oq_kron_plan)."""
+        m, b, npad = oq_kron_plan(n)
+        return Rotation(OQ_ROT_KRON, n, b, m)
+
+    @property
+    def width(self) -> int:
+        """Width of the rotated row (padded for the Kronecker rotation)."""
+        return self.rounds * self.block if self.kind == OQ_ROT_KRON else self.d
+
+    @staticmethod
     def dense32(mats_bits: torch.Tensor, mats_w: Optional[torch.Tensor] = None) -> "Rotation":
         d = mats_bits.shape[0] * 32
         return Rotation(OQ_ROT_DENSE32, d, 32, 1, mats=mats_bits.contiguous(),
@@ -168,7 +181,7 @@ def oq_rotate(rot: Rotation, x, center: bool = False, y=None, mean=None):
     M = x.shape[0]
     dev = _dev(x)
     if y is None:
-        y = torch.empty((M, rot.d), dtype=torch.float32, device=dev)
+        y = torch.empty((M, rot.width), dtype=torch.float32, device=dev)
     if center and mean is None:
         mean = torch.empty(M, dtype=torch.float32, device=dev)
     _check(_lib.oq_rotate(rot.ref(), _p(x), M, x.stride(0), int(center), _p(mean), _p(y), y.stride(0), _stream()))
@@ -180,6 +193,8 @@ def oq_quant_act(x, rot: Optional[Rotation], afmt: int, center: bool = False, co
     x = _bits16(x)
     M, d = x.shape
     dev = _dev(x)
+    if rot is not None and rot.kind == OQ_ROT_KRON:
+        d = rot.width  # codes have the padded width
     fmt = afmt & ~OQ_SCALE_PCTL  # the scale flag does not change the buffers
     mx_tiled = fmt == (OQ_MXFP4 | OQ_TILED)
     if codes is None and mx_tiled:
@@ -201,7 +216,7 @@ def oq_quant_act(x, rot: Optional[Rotation], afmt: int, center: bool = False, co
     if center and mean is None:
         mean = torch.empty(M, dtype=torch.float32, device=dev)
     ldc = 0 if fmt & OQ_TILED else codes.stride(0) * codes.element_size()
-    _check(_lib.oq_quant_act(_p(x), M, d, x.stride(0), _rref(rot), int(center), afmt, _p(codes),
+    _check(_lib.oq_quant_act(_p(x), M, x.shape[1], x.stride(0), _rref(rot), int(center), afmt, _p(codes),
                              ldc, _p(scale), _p(e8m0), _p(mean), _stream()))
     return {"codes": codes, "scale": scale, "e8m0": e8m0, "mean": mean}
 
@@ -210,11 +225,12 @@ def oq_quant_weight(w, rot: Optional[Rotation], wfmt: int, group: int, codes=Non
                     want_w1: bool = False):
     N, K = w.shape
     dev = _dev(w)
+    Kq = rot.width if rot is not None and rot.kind == OQ_ROT_KRON else K
     if codes is None:
-        codes = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+        codes = torch.empty((N, Kq // 2), dtype=torch.uint8, device=dev)
     if scales is None:
         scales = (torch.empty((N, K // 32), dtype=torch.uint8, device=dev) if wfmt == OQ_W_MXFP4
-                  else torch.empty((N, K // group), dtype=torch.float32, device=dev))
+                  else torch.empty((N, Kq // group), dtype=torch.float32, device=dev))
     if want_w1 and w1 is None:
         w1 = torch.empty(N, dtype=torch.float32, device=dev)
     _check(_lib.oq_quant_weight(_p(w), N, K, w.stride(0), _rref(rot), wfmt, group, _p(codes), _p(scales),
@@ -374,12 +390,13 @@ def oq_quant_weight_asym(w, rot: Optional[Rotation], group: int, codes=None, sig
                          want_w1: bool = False):
     N, K = w.shape
     dev = _dev(w)
+    Kq = rot.width if rot is not None and rot.kind == OQ_ROT_KRON else K
     if codes is None:
-        codes = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+        codes = torch.empty((N, Kq // 2), dtype=torch.uint8, device=dev)
     if sigma is None:
-        sigma = torch.empty((N, K // group), dtype=torch.int16, device=dev)
+        sigma = torch.empty((N, Kq // group), dtype=torch.int16, device=dev)
     if zero is None:
-        zero = torch.empty((N, K // group), dtype=torch.int16, device=dev)
+        zero = torch.empty((N, Kq // group), dtype=torch.int16, device=dev)
     if want_w1 and w1 is None:
         w1 = torch.empty(N, dtype=torch.float32, device=dev)
     _check(_lib.oq_quant_weight_asym(_p(w), N, K, w.stride(0), _rref(rot), group, _p(codes), _p(sigma), _p(zero),
@@ -426,3 +443,10 @@ def oq_gemm_w4a4_asym(qa, a_scale, gsum, w, N: int, M: int, K: int, mean=None, w
     _check(_lib.oq_gemm_w4a4_asym(afmt, _p(qa), _p(a_scale), _p(gsum), M, K, _p(w["codes"]), _p(w["scales"]),
                                   _p(w["corr"]), N, _p(mean), _p(w1), _p(bias), _p(y), y.stride(0), _stream()))
     return y
+
+
+def oq_kron_plan(n: int):
+    """Host call: (m, block, n_pad), the smallest admissible padded width."""
+    m, b, p = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(_lib.oq_kron_plan(n, ctypes.byref(m), ctypes.byref(b), ctypes.byref(p)))
+    return m.value, b.value, p.value

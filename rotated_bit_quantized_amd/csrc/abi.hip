@@ -60,7 +60,22 @@ int rot_args(const char *fn, const oq_rot *rot, int d, RotArgs *ra) {
   ra->perm = nullptr;
   ra->signs = nullptr;
   ra->c_h = 1.0f;
+  ra->kron_m = 0;
   if (!rot) return OQ_OK;
+  if (rot->kind == OQ_ROT_KRON) {
+    const int m = rot->rounds, b = rot->block;
+    if (rot->d != d) return fail(OQ_ERR_INVALID_ARG, "%s: rot->d=%d differs from d=%d", fn, rot->d, d);
+    if (m != 1 && m != 12 && m != 36 && m != 44)
+      return fail(OQ_ERR_UNSUPPORTED, "%s: Paley order m=%d must be 1, 12, 36 or 44", fn, m);
+    if (!is_pow2(b) || b < 16) return fail(OQ_ERR_UNSUPPORTED, "%s: block=%d must be a power of two >= 16", fn, b);
+    if ((int64_t)m * b < d || (int64_t)m * b > 16384)
+      return fail(OQ_ERR_UNSUPPORTED, "%s: padded width m*block=%lld must lie in [d, 16384]", fn, (long long)m * b);
+    ra->rounds = 1;
+    ra->block = b;
+    ra->kron_m = m;
+    ra->c_h = (float)(1.0 / std::sqrt((double)m * (double)b));
+    return OQ_OK;
+  }
   if (rot->kind != OQ_ROT_RPBH) return fail(OQ_ERR_INVALID_ARG, "%s: expected an RPBH rotation", fn);
   if (rot->d != d) return fail(OQ_ERR_INVALID_ARG, "%s: rot->d=%d differs from d=%d", fn, rot->d, d);
   if (!is_pow2(rot->block) || rot->block < 32 || rot->block > 1024)
@@ -237,7 +252,8 @@ int oq_rotate(const oq_rot *rot, const uint16_t *x, int64_t M, int64_t ldx, int 
   int rc = check_x("oq_rotate", x, M, d, ldx);
   if (rc) return rc;
   if (M > 0 && !y) return fail(OQ_ERR_INVALID_ARG, "oq_rotate: y is NULL");
-  if (ldy < d || !al16(y) || (ldy * 4) % 16) return fail(OQ_ERR_ALIGNMENT, "oq_rotate: bad y layout");
+  const int dy = rot->kind == OQ_ROT_KRON ? rot->rounds * rot->block : d;
+  if (ldy < dy || !al16(y) || (ldy * 4) % 16) return fail(OQ_ERR_ALIGNMENT, "oq_rotate: bad y layout");
   if (center && !mean) return fail(OQ_ERR_INVALID_ARG, "oq_rotate: centering needs mean");
   if (rot->kind == OQ_ROT_DENSE32) {
     if (center) return fail(OQ_ERR_UNSUPPORTED, "oq_rotate: centering with a DENSE32 rotation");
@@ -299,13 +315,15 @@ int oq_quant_act(const uint16_t *x, int64_t M, int32_t d, int64_t ldx, const oq_
   if (tiled) {
     if (base_fmt != OQ_A4 && base_fmt != OQ_A6)
       return fail(OQ_ERR_UNSUPPORTED, "oq_quant_act: the tiled layout exists for OQ_A4, OQ_A6 and OQ_MXFP4");
-    if (d % 64) return fail(OQ_ERR_UNSUPPORTED, "oq_quant_act: tiled codes need d %% 64 == 0 (d=%d)", d);
     if (e8m0) return fail(OQ_ERR_INVALID_ARG, "oq_quant_act: e8m0 must be NULL for integer codes");
     if (M > 0 && !scale) return fail(OQ_ERR_INVALID_ARG, "oq_quant_act: scale is NULL");
     if (center && !mean) return fail(OQ_ERR_INVALID_ARG, "oq_quant_act: centering needs mean");
     RotArgs ra;
     rc = rot_args("oq_quant_act", rot, d, &ra);
     if (rc) return rc;
+    if (rot_out_width(ra, d) % 64)
+      return fail(OQ_ERR_UNSUPPORTED, "oq_quant_act: tiled codes need a width multiple of 64 (%d)", rot_out_width(ra, d));
+    if (ra.kron_m && pp) return fail(OQ_ERR_UNSUPPORTED, "oq_quant_act: OQ_SCALE_PCTL with the Kronecker rotation");
     g_err[0] = 0;
     return hip_status(launch_rpbh_quant(x, M, d, ldx, ra, center ? 1 : 0, mean,
                                         base_fmt == OQ_A4 ? OUT_FP6 : OUT_FP6X2, qmax_of(base_fmt), codes, 0,
@@ -317,10 +335,12 @@ int oq_quant_act(const uint16_t *x, int64_t M, int32_t d, int64_t ldx, const oq_
   if (e8m0) return fail(OQ_ERR_INVALID_ARG, "oq_quant_act: e8m0 must be NULL for integer codes");
   if (M > 0 && !scale) return fail(OQ_ERR_INVALID_ARG, "oq_quant_act: scale is NULL");
   if (center && !mean) return fail(OQ_ERR_INVALID_ARG, "oq_quant_act: centering needs mean");
-  if (ldc_bytes < (afmt == OQ_A4 ? d / 2 : d)) return fail(OQ_ERR_INVALID_ARG, "oq_quant_act: ldc_bytes too small");
   RotArgs ra;
   rc = rot_args("oq_quant_act", rot, d, &ra);
   if (rc) return rc;
+  const int dq = rot_out_width(ra, d);
+  if (ldc_bytes < (afmt == OQ_A4 ? dq / 2 : dq)) return fail(OQ_ERR_INVALID_ARG, "oq_quant_act: ldc_bytes too small");
+  if (ra.kron_m && pp) return fail(OQ_ERR_UNSUPPORTED, "oq_quant_act: OQ_SCALE_PCTL with the Kronecker rotation");
   g_err[0] = 0;
   return hip_status(launch_rpbh_quant(x, M, d, ldx, ra, center ? 1 : 0, mean, afmt == OQ_A4 ? OUT_I4 : OUT_I8,
                                       qmax_of(afmt), codes, ldc_bytes, scale, stream, pp),
@@ -344,11 +364,12 @@ int oq_quant_weight(const float *w, int32_t N, int32_t K, int64_t ldw, const oq_
                       "oq_quant_weight");
   }
   if (wfmt != OQ_W4) return fail(OQ_ERR_INVALID_ARG, "oq_quant_weight: unknown wfmt %d", wfmt);
-  if (!is_pow2(group) || group < 32 || group > 1024 || K % group)
-    return fail(OQ_ERR_UNSUPPORTED, "oq_quant_weight: group=%d must be a power of two in [32, 1024] dividing K", group);
   RotArgs ra;
   int rc = rot_args("oq_quant_weight", rot, K, &ra);
   if (rc) return rc;
+  const int Kq = rot_out_width(ra, K);
+  if (!is_pow2(group) || group < 32 || group > 1024 || Kq % group)
+    return fail(OQ_ERR_UNSUPPORTED, "oq_quant_weight: group=%d must be a power of two in [32, 1024] dividing %d", group, Kq);
   g_err[0] = 0;
   return hip_status(launch_weight_rpbh(w, N, K, ldw, ra, group, codes, (float *)scales, w1, stream), "oq_quant_weight");
 }
@@ -468,6 +489,8 @@ int oq_linear_fused(const uint16_t *x, int64_t M, int32_t K, int64_t ldx, const 
   const char *fn = "oq_linear_fused";
   int rc = check_x(fn, x, M, K, ldx);
   if (rc) return rc;
+  if (rot && rot->kind == OQ_ROT_KRON)
+    return fail(OQ_ERR_UNSUPPORTED, "%s: the Kronecker rotation pads the width; call oq_quant_act and a GEMM", fn);
   PctlArgs pa;
   const PctlArgs *pp = nullptr;
   if (afmt & OQ_SCALE_PCTL) {
@@ -629,6 +652,7 @@ int oq_quant_act_lm(const uint16_t *x, int64_t M, int32_t d, int64_t ldx, const 
   RotArgs ra;
   rc = rot_args(fn, rot, d, &ra);
   if (rc) return rc;
+  if (ra.kron_m) return fail(OQ_ERR_UNSUPPORTED, "%s: Lloyd-Max codes with the Kronecker rotation", fn);
   const LmArgs la{bits, thresholds, levels_f16};
   const int mode = tiled ? OUT_LMF16 : (bits <= 4 ? OUT_LM4 : OUT_LM8);
   g_err[0] = 0;
@@ -702,6 +726,8 @@ int oq_quant_weight_asym(const float *w, int32_t N, int32_t K, int64_t ldw, cons
   RotArgs ra;
   int rc = rot_args(fn, rot, K, &ra);
   if (rc) return rc;
+  if (rot_out_width(ra, K) % group)
+    return fail(OQ_ERR_UNSUPPORTED, "%s: group=%d must divide the rotated width %d", fn, group, rot_out_width(ra, K));
   g_err[0] = 0;
   return hip_status(launch_weight_rpbh_asym(w, N, K, ldw, ra, group, codes, sigma, zero, w1, stream), fn);
 }
@@ -744,6 +770,7 @@ int oq_quant_act_gsum(const uint16_t *x, int64_t M, int32_t d, int64_t ldx, cons
   RotArgs ra;
   rc = rot_args(fn, rot, d, &ra);
   if (rc) return rc;
+  if (ra.kron_m) return fail(OQ_ERR_UNSUPPORTED, "%s: group sums with the Kronecker rotation", fn);
   const int base = afmt & ~OQ_TILED;
   g_err[0] = 0;
   return hip_status(launch_rpbh_quant(x, M, d, ldx, ra, center ? 1 : 0, mean, base == OQ_A4 ? OUT_FP6 : OUT_FP6X2,
@@ -768,6 +795,30 @@ int oq_gemm_w4a4_asym(int afmt, const uint8_t *qa, const float *a_scale, const f
                     fn);
 }
 
+// ---------------------------------------------------------- Kronecker rotation
+int oq_kron_plan(int32_t n, int32_t *m, int32_t *block, int32_t *n_pad) {
+  if (n < 1 || n > 16384) return fail(OQ_ERR_UNSUPPORTED, "oq_kron_plan: n=%d must lie in [1, 16384]", n);
+  if (!m || !block || !n_pad) return fail(OQ_ERR_INVALID_ARG, "oq_kron_plan: NULL output");
+  const int orders[4] = {1, 12, 36, 44};
+  int best = 0, bm = 0, bb = 0;
+  for (int i = 0; i < 4; ++i) {
+    int b = 16;  // blocks of at least 16 coordinates (one thread's share)
+    while (orders[i] * b < n) b *= 2;
+    if (best == 0 || orders[i] * b < best) {
+      best = orders[i] * b;
+      bm = orders[i];
+      bb = b;
+    }
+  }
+  if (best > 16384) return fail(OQ_ERR_UNSUPPORTED, "oq_kron_plan: no admissible width up to 16384 for n=%d", n);
+  *m = bm;
+  *block = bb;
+  *n_pad = best;
+  g_err[0] = 0;
+  return OQ_OK;
+}
+
 }  // extern "C"
+
 
 

@@ -36,6 +36,52 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;
 }
 
+// Row c' of the Paley factor H_m of the Kronecker rotation as a sign mask
+// (bit c set where H_m[c'][c] = -1), from the textbook constructions with
+// chi the quadratic character mod q (Euler's criterion) and the Jacobsthal
+// entries Q[i][j] = chi(j - i): m = 12, 44: type I, q = 11, 43,
+// H = I + [[0, 1^T], [-1, Q]]; m = 36: type II, q = 17, C = [[0, 1^T], [1, Q]],
+// H = [[C + I, C - I], [C - I, -C - I]] (CentriQ Sec. 3 "Hadamard rotation",
+// App. B.1).  m = 1 gives 0.
+__device__ int qchar(int a, int q) {
+  a %= q;
+  if (a < 0) a += q;
+  if (a == 0) return 0;
+  int r = 1, b = a, e = (q - 1) / 2;
+  while (e) {
+    if (e & 1) r = (r * b) % q;
+    b = (b * b) % q;
+    e >>= 1;
+  }
+  return r == 1 ? 1 : -1;
+}
+
+__device__ uint64_t paley_row_mask(int m, int cp) {
+  if (m == 1) return 0;
+  uint64_t msk = 0;
+  if (m == 12 || m == 44) {
+    const int q = m - 1;
+    for (int c = 0; c < m; ++c) {
+      int v;
+      if (cp == 0) v = 1;
+      else if (c == 0) v = -1;
+      else if (c == cp) v = 1;
+      else v = qchar(c - cp, q);
+      if (v < 0) msk |= (uint64_t)1 << c;
+    }
+  } else {  // m == 36, q = 17
+    const int bi = cp / 18, i = cp % 18;
+    for (int c = 0; c < m; ++c) {
+      const int bj = c / 18, j = c % 18;
+      const int cij = (i == 0 && j == 0) ? 0 : (i == 0 || j == 0) ? 1 : (i == j ? 0 : qchar(j - i, 17));
+      const int dij = i == j ? 1 : 0;
+      const int v = (bi == 0 && bj == 0) ? cij + dij : (bi == 1 && bj == 1) ? -cij - dij : cij - dij;
+      if (v < 0) msk |= (uint64_t)1 << c;
+    }
+  }
+  return msk;
+}
+
 // In-register butterflies over the 16 coordinates of one thread (strides 1..8).
 __device__ __forceinline__ void fwht16(float (&u)[E]) {
 #pragma unroll
@@ -60,13 +106,21 @@ __device__ __forceinline__ void fwht16(float (&u)[E]) {
 //   for a constant group), z = RNbf16(RN32(-min / sigma)), codes
 //   Q = clamp(RNE(RN32(RN32(w / sigma) + z)), 0, 15) stored as Q - 8;
 //   sigma bits to scale_out (as uint16), z bits to zero_out.
-template <int ROUNDS, int MODE, bool IN_F32>
+// KRON: the factorised rotation (H_m (x) H_h) / sqrt(d) of CentriQ Sec. 4.2
+// "Rotation" / App. B.1 instead of RPBH rounds (ROUNDS must be 1): the row
+// holds din native coordinates, centred over those, then zero-padded to d =
+// km h; the Sylvester factor runs on every block of h (un-normalised, the
+// usual stages), then out[c' h + r] = sum_c H_m[c'][c] u[c h + r] in
+// increasing c, then one multiply by c_h = RN32(1 / sqrt(d)).
+template <int ROUNDS, int MODE, bool IN_F32, bool KRON = false>
 __global__ void __launch_bounds__(1024)
 rpbh_quant_kernel(const void *__restrict__ xin, int64_t M, int d, int64_t ldx,
                   const int32_t *__restrict__ perm, const int8_t *__restrict__ signs,
                   int h, float c_h, int center, float *__restrict__ mean_out,
                   int qmax, void *__restrict__ out, int64_t ld_out_bytes,
-                  float *__restrict__ scale_out, int group, uint16_t *__restrict__ zero_out) {
+                  float *__restrict__ scale_out, int group, uint16_t *__restrict__ zero_out,
+                  int din, int km) {
+  static_assert(!KRON || ROUNDS == 1, "the Kronecker rotation is one transform");
   extern __shared__ float lds[];
   float *buf0 = lds;                      // [d]
   float *buf1 = lds + (ROUNDS == 2 ? d : 0);
@@ -84,8 +138,13 @@ rpbh_quant_kernel(const void *__restrict__ xin, int64_t M, int d, int64_t ldx,
   // per-thread gather offsets and sign masks, loaded once per workgroup
   int off[ROUNDS > 0 ? ROUNDS : 1][E];
   uint32_t smask[ROUNDS > 0 ? ROUNDS : 1][E];
+  const bool ldin = act && base < din;  // coordinates of the input row (the rest is padding)
+  uint64_t hmask = 0;
+  if constexpr (KRON) {
+    if (act) hmask = paley_row_mask(km, base / h);
+  }
 #pragma unroll
-  for (int r = 0; r < ROUNDS; ++r) {
+  for (int r = 0; r < (KRON ? 0 : ROUNDS); ++r) {
 #pragma unroll
     for (int j = 0; j < E; ++j) {
       const int i = act ? base + j : 0;
@@ -97,14 +156,14 @@ rpbh_quant_kernel(const void *__restrict__ xin, int64_t M, int d, int64_t ldx,
   for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
     __syncthreads();  // previous row's LDS readers are done
     float v[E];
-    if (act && IN_F32) {
+    if (ldin && IN_F32) {
       const float4 *src = reinterpret_cast<const float4 *>(static_cast<const float *>(xin) + row * ldx + base);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const float4 p = src[k];
         v[4 * k] = p.x; v[4 * k + 1] = p.y; v[4 * k + 2] = p.z; v[4 * k + 3] = p.w;
       }
-    } else if (act) {
+    } else if (ldin) {
       const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(xin) + row * ldx + base);
       const uint4 p0 = src[0], p1 = src[1];
       const uint32_t w[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
@@ -139,14 +198,79 @@ rpbh_quant_kernel(const void *__restrict__ xin, int64_t M, int d, int64_t ldx,
       __syncthreads();
       double tot = 0.0;
       for (int w = 0; w < nwaves; ++w) tot += redd[w];
-      const float m = (float)(tot / (double)d);
+      const float m = (float)(tot / (double)din);
+      if (ldin) {  // padding stays zero: centering precedes padding
 #pragma unroll
-      for (int j = 0; j < E; ++j) v[j] = v[j] - m;
+        for (int j = 0; j < E; ++j) v[j] = v[j] - m;
+      }
       if (t == 0) mean_out[row] = m;
     }
 
+    if constexpr (KRON) {
+      fwht16(v);
+      const int hw = h < 1024 ? h : 1024;
+      for (int s = E; s < hw; s <<= 1) {
+        const int m = s / E;
+        const float sg = (lane & m) ? -1.0f : 1.0f;
 #pragma unroll
-    for (int r = 0; r < ROUNDS; ++r) {
+        for (int j = 0; j < E; ++j) {
+          const float p = __shfl_xor(v[j], m);
+          v[j] = __builtin_fmaf(v[j], sg, p);
+        }
+      }
+      // strides of 1024 and more pair coordinates held by different
+      // wavefronts: exchange through LDS, same butterflies
+      for (int s = 1024; s < h; s <<= 1) {
+        if (act) {
+          float4 *dst = reinterpret_cast<float4 *>(buf0 + base);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) dst[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+        }
+        __syncthreads();
+        if (act) {
+          const bool hi = (base & s) != 0;
+          const float4 *src = reinterpret_cast<const float4 *>(buf0 + (base ^ s));
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float4 pp = src[k];
+            const float p4[4] = {pp.x, pp.y, pp.z, pp.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[4 * k + e] = hi ? p4[e] - v[4 * k + e] : v[4 * k + e] + p4[e];
+          }
+        }
+        __syncthreads();
+      }
+      if (act) {
+        float4 *dst = reinterpret_cast<float4 *>(buf0 + base);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) dst[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+      }
+      __syncthreads();
+      if (act) {
+        // this thread's 16 outputs share the block c' = base / h and sit at
+        // offsets r0 .. r0 + 15 of it
+        const int r0 = base % h;
+        float acc[E];
+        for (int c = 0; c < km; ++c) {
+          const float4 *src = reinterpret_cast<const float4 *>(buf0 + c * h + r0);
+          const bool neg = (hmask >> c) & 1;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float4 pp = src[k];
+            const float p4[4] = {pp.x, pp.y, pp.z, pp.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float t = neg ? -p4[e] : p4[e];
+              acc[4 * k + e] = c == 0 ? t : acc[4 * k + e] + t;
+            }
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < E; ++j) v[j] = acc[j] * c_h;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < (KRON ? 0 : ROUNDS); ++r) {
       float *buf = (r == 0) ? buf0 : buf1;
       if (act) {
         float4 *dst = reinterpret_cast<float4 *>(buf + base);
@@ -309,10 +433,10 @@ rpbh_quant_kernel(const void *__restrict__ xin, int64_t M, int d, int64_t ldx,
   }
 }
 
-template <int ROUNDS, int MODE, bool IN_F32>
+template <int ROUNDS, int MODE, bool IN_F32, bool KRON = false>
 hipError_t launch_t(const void *x, int64_t M, int d, int64_t ldx, const RotArgs &rot,
                     int center, float *mean, int qmax, void *out, int64_t ld_out_bytes,
-                    float *scale, int group, hipStream_t stream, uint16_t *zero = nullptr) {
+                    float *scale, int group, hipStream_t stream, uint16_t *zero = nullptr, int din = -1) {
   const int nact = d / E;
   const int threads = ((nact + 63) / 64) * 64;
   const size_t lds = sizeof(float) * ((size_t)ROUNDS * d + 16) + sizeof(double) * 16;
@@ -320,13 +444,13 @@ hipError_t launch_t(const void *x, int64_t M, int d, int64_t ldx, const RotArgs 
   int64_t grid = M < 4096 ? M : 4096;
   if (grid < 1) grid = 1;
   if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void *)rpbh_quant_kernel<ROUNDS, MODE, IN_F32>,
+    hipError_t e = hipFuncSetAttribute((const void *)rpbh_quant_kernel<ROUNDS, MODE, IN_F32, KRON>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((rpbh_quant_kernel<ROUNDS, MODE, IN_F32>), dim3((unsigned)grid), dim3(threads), lds, stream,
+  hipLaunchKernelGGL((rpbh_quant_kernel<ROUNDS, MODE, IN_F32, KRON>), dim3((unsigned)grid), dim3(threads), lds, stream,
                      x, M, d, ldx, rot.perm, rot.signs, rot.block, rot.c_h, center, mean, qmax, out,
-                     ld_out_bytes, scale, group, zero);
+                     ld_out_bytes, scale, group, zero, din < 0 ? d : din, KRON ? rot.kron_m : 0);
   return hipGetLastError();
 }
 
@@ -349,6 +473,11 @@ hipError_t launch_mode(int mode, const uint16_t *x, int64_t M, int d, int64_t ld
 hipError_t launch_weight_rpbh(const float *w, int N, int K, int64_t ldw, const RotArgs &rot, int group,
                               uint8_t *codes, float *scales, float *w1, hipStream_t stream) {
   if (N == 0) return hipSuccess;
+  if (rot.kron_m) {
+    const int Kp = rot_out_width(rot, K);
+    return launch_t<1, OUT_W4G, true, true>(w, N, Kp, ldw, rot, 0, w1, 7, codes, Kp / 2, scales, group, stream, nullptr,
+                                            K);
+  }
   switch (rot.rounds) {
     case 0: return launch_t<0, OUT_W4G, true>(w, N, K, ldw, rot, 0, w1, 7, codes, K / 2, scales, group, stream);
     case 1: return launch_t<1, OUT_W4G, true>(w, N, K, ldw, rot, 0, w1, 7, codes, K / 2, scales, group, stream);
@@ -361,6 +490,10 @@ hipError_t launch_weight_rpbh_asym(const float *w, int N, int K, int64_t ldw, co
                                    uint8_t *codes, uint16_t *sigma, uint16_t *zero, float *w1, hipStream_t stream) {
   if (N == 0) return hipSuccess;
   float *sg = reinterpret_cast<float *>(sigma);  // carried as the scale pointer, written as uint16
+  if (rot.kron_m) {
+    const int Kp = rot_out_width(rot, K);
+    return launch_t<1, OUT_W4A, true, true>(w, N, Kp, ldw, rot, 0, w1, 0, codes, Kp / 2, sg, group, stream, zero, K);
+  }
   switch (rot.rounds) {
     case 0: return launch_t<0, OUT_W4A, true>(w, N, K, ldw, rot, 0, w1, 0, codes, K / 2, sg, group, stream, zero);
     case 1: return launch_t<1, OUT_W4A, true>(w, N, K, ldw, rot, 0, w1, 0, codes, K / 2, sg, group, stream, zero);
@@ -374,6 +507,19 @@ hipError_t launch_rpbh_quant(const uint16_t *x, int64_t M, int d, int64_t ldx, c
                              int64_t ld_out_bytes, float *scale, hipStream_t stream, const PctlArgs *pctl,
                              const LmArgs *lm, float *gsum) {
   if (M == 0) return hipSuccess;
+  if (rot.kron_m) {
+    // the Kronecker rotation runs in the workgroup kernel at the padded width
+    if (pctl || lm || gsum) return hipErrorInvalidValue;
+    const int dp = rot_out_width(rot, d);
+    switch (out_mode) {
+      case OUT_F32: return launch_t<1, OUT_F32, false, true>(x, M, dp, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, 0, stream, nullptr, d);
+      case OUT_I8: return launch_t<1, OUT_I8, false, true>(x, M, dp, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, 0, stream, nullptr, d);
+      case OUT_I4: return launch_t<1, OUT_I4, false, true>(x, M, dp, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, 0, stream, nullptr, d);
+      case OUT_FP6: return launch_t<1, OUT_FP6, false, true>(x, M, dp, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, 0, stream, nullptr, d);
+      case OUT_FP6X2: return launch_t<1, OUT_FP6X2, false, true>(x, M, dp, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, 0, stream, nullptr, d);
+    }
+    return hipErrorInvalidValue;
+  }
   if (rpbh_wave_supported(d))
     return launch_rpbh_wave(x, M, d, ldx, rot, center, mean, out_mode, qmax, out, ld_out_bytes, scale, stream, pctl, lm,
                             gsum);

@@ -84,8 +84,12 @@ struct RotArgs {
   int block;             // h
   const int32_t *perm;   // [rounds][d]
   const int8_t *signs;   // [rounds][d]
-  float c_h;             // RN32(1/sqrt h)
+  float c_h;             // RN32(1/sqrt h); for the Kronecker rotation RN32(1/sqrt(m h))
+  int kron_m = 0;        // 0: RPBH rounds; else the order m of the Paley factor of (H_m (x) H_h)
 };
+
+// width of the rotated (and quantized) row: the padded m h for the Kronecker rotation
+inline int rot_out_width(const RotArgs &ra, int d) { return ra.kron_m ? ra.kron_m * ra.block : d; }
 
 // Percentile range of a token (CentriQ Sec. 4.2 "Scale and grid"):
 // r = RN32((q * gamma) / z), q = lo + frac (hi - lo) in float64, where lo and
