@@ -326,6 +326,66 @@ def _time_asym(torch, oq, WL, reps=40, warmup=5):
     return e
 
 
+def _time_kron(torch, oq, WL, reps=40, warmup=5):
+    """Paley x Sylvester rotation (CentriQ Sec. 4.2 "Rotation") for 4096-token
+    activations at a native width (3072 = 12 x 256) and at two widths that
+    pad (2240 -> 2304 = 36 x 64, 1920 -> 2048): the rotate/quant writer into
+    tiled A4 codes, and the GEMM at the padded width for 2240 (N = 2240)."""
+    dev = torch.device("cuda:0")
+    out = {}
+    rng = torch.Generator(device="cpu").manual_seed(7)
+    for n in (3072, 2240, 1920):
+        m, b, npad = oq.oq_kron_plan(n)
+        M = 4096
+        x = (torch.randn((M, n), generator=rng) * 2).to(torch.bfloat16).to(dev)
+        xs = [x] + [x.clone() for _ in range(7)]
+        rot = oq.Rotation.kron(n)
+        codes = torch.empty(oq.oq_tiled_bytes(M, npad), dtype=torch.uint8, device=dev)
+        scale = torch.empty(M, dtype=torch.float32, device=dev)
+        fmt = oq.OQ_A4 | oq.OQ_TILED
+
+        def rq(i):
+            oq.oq_quant_act(xs[i % len(xs)], rot, fmt, codes=codes, scale=scale)
+
+        for i in range(warmup):
+            rq(i)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record()
+        for i in range(reps):
+            rq(i)
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        t = sum(ev[i].elapsed_time(ev[i + 1]) for i in range(reps)) / reps
+        nbytes = M * (2 * n + npad * 3 // 4 + 4)  # bf16 in, 6-bit tiled codes out, scale
+        e = {"m": m, "block": b, "n_pad": npad, "rotate_quant_us": round(t * 1e3, 3),
+             "rotate_quant_hbm_frac": round(nbytes / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        if n == 2240:
+            N = n
+            W = (torch.randn((N, n), generator=rng) * 0.02).to(dev)
+            wq = oq.oq_quant_weight(W, rot, oq.OQ_W4, 64)
+            wt = oq.oq_prepack_w4(wq["codes"], wq["scales"], N, npad)
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+            def gm():
+                oq.oq_gemm_w4a4(fmt, codes, scale, wt["codes"], wt["scales"], N, 64, y=y, M=M, K=npad)
+
+            for _ in range(warmup):
+                gm()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                gm()
+            e1.record()
+            torch.cuda.synchronize()
+            tg = e0.elapsed_time(e1) / reps
+            e[f"gemm_n{N}_k{npad}_us"] = round(tg * 1e3, 2)
+            e["gemm_TOPS_on_native_k"] = round(2.0 * M * n * N / (tg * 1e-3) / 1e12, 1)
+        out[str(n)] = e
+    return out
+
+
 def _copy_reference(torch, nbytes=1 << 30, reps=3):
     """A plain device-to-device copy of known size, launched beside the
     profiled kernels so that HBM byte counters can be scaled by what they
@@ -489,6 +549,7 @@ def main():
         result["other_configs"] = side
         result["lloyd_max_4096x3072"] = {f"A{b}": _time_lm(torch, oq, WL, b) for b in (4, 8)}
         result["asym_w4a4_4096x3072"] = _time_asym(torch, oq, WL)
+        result["kron_rotation_4096"] = _time_kron(torch, oq, WL)
 
     if not args.no_cpu_baseline and not args.only_step:
         result["cpu_baseline"] = _cpu_baseline(WL)
