@@ -27,7 +27,7 @@
 // takes an E8M0 scale of 2^1 for the weights: the group sums stay exact.  The
 // real shift leaves -sum_g C_g p_g (C = sigma (z - 8) per row and group, p the
 // group sums of the activation codes), a product of depth K/64 computed once
-// per tile before the main loop on bfloat16 matrix cores, with p and C split
+// per tile after the main loop on bfloat16 matrix cores, with p and C split
 // into pieces that make every product exact in float32.
 //
 // Workgroup: WM x WN wavefronts, each computing 128 x 64 outputs (4 x 2 MFMA
@@ -36,6 +36,9 @@
 // (no register staging) into a 4-stage ring, one barrier per group.
 #include "oq_internal.h"
 
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
 #include <type_traits>
 
 #ifndef FP6_STAGES
@@ -466,34 +469,52 @@ __device__ __forceinline__ void wait_vm() {
 }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-template <int NSLOT_>
+// Workgroup shapes: 256 rows, 8 waves, each wave TI x TJ MFMA tiles of 32 x 32.
+//   TI = 4, TJ = 2: waves 2 (rows) x 4 (columns), 256 x 256 outputs;
+//   TI = 2, TJ = 3: waves 4 x 2, 256 x 192 outputs.
+// Every stage holds 8 A and 8 B tiles and 256 scales whatever the shape, so
+// every wave issues the same copies per stage (a 192-wide tile loads the two
+// column blocks past its end too and leaves them unread).
+template <int NSLOT_, int TI_, int TJ_>
 struct V2C {
-  static constexpr int WAVES = 8, BM = 256, BN = 256, NSLOT = NSLOT_;
-  static constexpr int A_BYTES = (BM / 32) * CHUNK_TILE, B_BYTES = (BN / 32) * CHUNK_TILE;
-  static constexpr int S_BYTES = BN * 4;
+  static constexpr int WAVES = 8, TI = TI_, TJ = TJ_, NSLOT = NSLOT_;
+  static constexpr int WAVES_M = 8 / TI, WAVES_N = 8 / WAVES_M;
+  static constexpr int BM = 32 * TI * WAVES_M, BN = 32 * TJ * WAVES_N;
+  static constexpr int A_BYTES = 8 * CHUNK_TILE, B_BYTES = 8 * CHUNK_TILE;
+  static constexpr int S_BYTES = 1024;
   static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
   static constexpr int ROWS_OFF = NSLOT * STAGE;
-  static constexpr int SROW = 144;  // padded bytes per staged output row of 64 bf16
+  static constexpr int SROW = 64 * TJ + 16;  // padded bytes per staged output row of 32 TJ bf16
   static constexpr int STG_OFF = ROWS_OFF + 2 * BM * 4;  // per-wave epilogue staging
   static constexpr int LDS_BYTES = STG_OFF + WAVES * 32 * SROW;
   static constexpr int PER_STAGE = 4;  // copy instructions per wave per stage
+  static_assert(BM == 256 && BN <= 256 && WAVES_M * WAVES_N == WAVES, "workgroup shape");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// two float32 values rounded to bfloat16 (nearest, ties to even): a in bits
+// 0..15, b in bits 16..31
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) {
   bf16x8_t r;
   __builtin_memcpy(&r, &u, 16);
   return r;
 }
 
-template <int NSLOT, bool PAIRED, bool ASYM>
+template <int NSLOT, bool PAIRED, bool ASYM, int TI, int TJ, bool EXTRA>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_scale, int64_t M, int K,
                    const uint8_t *__restrict__ W, const float *__restrict__ wst, int N, int Np,
                    const float *__restrict__ mean, const float *__restrict__ w1, const float *__restrict__ bias,
                    uint16_t *__restrict__ y, int64_t ldy, const float *__restrict__ gsum,
                    const uint2 *__restrict__ corr) {
-  using V2 = V2C<NSLOT>;
+  using V2 = V2C<NSLOT, TI, TJ>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const uint32_t lds0 = lds_addr_of(smem);
   const int lane = threadIdx.x & 63;
@@ -504,11 +525,11 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_sc
   const int64_t mblocks = (M + 31) / 32;
   const int nblocks = Np / 32;
 
-  float F[4][2][16];
+  float F[TI][TJ][16];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TJ; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) F[i][j][e] = 0.f;
 
@@ -546,12 +567,12 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_sc
     dma4_s(wst + (int64_t)kg * Np, soff, base + slds);
   };
 
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave / V2::WAVES_N, wn = wave % V2::WAVES_N;
   const int r = lane & 31, half = lane >> 5;
-  const uint8_t *fa = smem + (wm * 4) * CHUNK_TILE + 16 * lane;  // + 1024 - 8 lane: the 8-byte part
-  const uint8_t *fb = smem + V2::A_BYTES + (wn * 2) * CHUNK_TILE + 16 * lane;
+  const uint8_t *fa = smem + (wm * TI) * CHUNK_TILE + 16 * lane;  // + 1024 - 8 lane: the 8-byte part
+  const uint8_t *fb = smem + V2::A_BYTES + (wn * TJ) * CHUNK_TILE + 16 * lane;
   const int tail = 1024 - 8 * lane;
-  const float *fs = reinterpret_cast<const float *>(smem + V2::A_BYTES + V2::B_BYTES) + wn * 64 + r;
+  const float *fs = reinterpret_cast<const float *>(smem + V2::A_BYTES + V2::B_BYTES) + wn * 32 * TJ + r;
 
   // E8M0 scale of the weight operand: 2^1 for the stored q'/2 of asymmetric codes
   const int wsc = ASYM ? 128 : 127;
@@ -577,50 +598,50 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_sc
   else if (G > 1) wait_vm<V2::PER_STAGE>();
   else wait_vm<0>();
   __builtin_amdgcn_s_barrier();
-  v8i a[4], b0, b1;
-  float s0, s1, ns0 = 0.f, ns1 = 0.f;
+  v8i a[TI], b[TJ];
+  float sw[TJ], nsw[TJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) a[i] = frag_at(fa + i * CHUNK_TILE, fa + i * CHUNK_TILE + tail);
-  b0 = frag_at(fb, fb + tail);
-  b1 = frag_at(fb + CHUNK_TILE, fb + CHUNK_TILE + tail);
-  s0 = fs[0];
-  s1 = fs[32];
+  for (int i = 0; i < TI; ++i) a[i] = frag_at(fa + i * CHUNK_TILE, fa + i * CHUNK_TILE + tail);
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) {
+    b[j] = frag_at(fb + j * CHUNK_TILE, fb + j * CHUNK_TILE + tail);
+    sw[j] = fs[32 * j];
+    nsw[j] = 0.f;
+  }
 
   // one k-group: MFMAs of group g from registers, the next group's operands
   // (stage g+1, slot JN) read into the registers as they free up
   auto group = [&](auto jnc) {
     constexpr int JN = decltype(jnc)::value;
+    constexpr int NT = TI * TJ;
     v16f dprev;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int i = t >> 1;
-      const v8i &bb = (t & 1) ? b1 : b0;
-      const v16f dt = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], bb, (v16f){}, 2, 2, 0, 127, 0, wsc);
+    for (int t = 0; t < NT; ++t) {
+      const int i = t / TJ, j = t % TJ;
+      const v16f dt = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], (v16f){}, 2, 2, 0, 127, 0, wsc);
       __builtin_amdgcn_sched_barrier(0);
       if (t > 0) {
-        const int ip = (t - 1) >> 1, jp = (t - 1) & 1;
-        const float sp = jp ? s1 : s0;
+        const int ip = (t - 1) / TJ, jp = (t - 1) % TJ;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) F[ip][jp][e] = __builtin_fmaf(sp, dprev[e], F[ip][jp][e]);
+        for (int e = 0; e < 16; ++e) F[ip][jp][e] = __builtin_fmaf(sw[jp], dprev[e], F[ip][jp][e]);
       }
       // operands are reloaded with the next group's values right after their
-      // last MFMA: a[i] after tile 2i+1, b0 after tile 6, b1 after tile 7
+      // last MFMA: a[i] after tile (i, TJ - 1), b[j] after tile (TI - 1, j)
       // (after the last group this reads a settled slot that is never used)
-      if (t & 1) a[i] = frag_at(fa + JN * V2::STAGE + i * CHUNK_TILE, fa + JN * V2::STAGE + i * CHUNK_TILE + tail);
-      if (t == 6) b0 = frag_at(fb + JN * V2::STAGE, fb + JN * V2::STAGE + tail);
-      if (t == 7) {
-        b1 = frag_at(fb + JN * V2::STAGE + CHUNK_TILE, fb + JN * V2::STAGE + CHUNK_TILE + tail);
-        ns0 = fs[JN * V2::STAGE / 4];
-        ns1 = fs[JN * V2::STAGE / 4 + 32];
+      if (j == TJ - 1) a[i] = frag_at(fa + JN * V2::STAGE + i * CHUNK_TILE, fa + JN * V2::STAGE + i * CHUNK_TILE + tail);
+      if (i == TI - 1) b[j] = frag_at(fb + JN * V2::STAGE + j * CHUNK_TILE, fb + JN * V2::STAGE + j * CHUNK_TILE + tail);
+      if (t == NT - 1) {
+#pragma unroll
+        for (int jj = 0; jj < TJ; ++jj) nsw[jj] = fs[JN * V2::STAGE / 4 + 32 * jj];
       }
       __builtin_amdgcn_sched_barrier(0);
       dprev = dt;
     }
     // last tile: its MFMA was issued one tile ago
 #pragma unroll
-    for (int e = 0; e < 16; ++e) F[3][1][e] = __builtin_fmaf(s1, dprev[e], F[3][1][e]);
-    s0 = ns0;
-    s1 = ns1;
+    for (int e = 0; e < 16; ++e) F[TI - 1][TJ - 1][e] = __builtin_fmaf(sw[TJ - 1], dprev[e], F[TI - 1][TJ - 1][e]);
+#pragma unroll
+    for (int jj = 0; jj < TJ; ++jj) sw[jj] = nsw[jj];
   };
 
   if constexpr (!PAIRED) {
@@ -680,41 +701,42 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_sc
     // MFMAs of the current one.
     const int Gq = K / 64;
     const int r0 = lane & 31, hf = lane >> 5;
-    int prow[4], ccol[2];
+    int prow[TI], ccol[TJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t rr = m0 + wm * 128 + 32 * i + r0;
+    for (int i = 0; i < TI; ++i) {
+      const int64_t rr = m0 + wm * 32 * TI + 32 * i + r0;
       prow[i] = (int)(rr < M ? rr : M - 1);
     }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int cc = n0 + wn * 64 + 32 * j + r0;
+    for (int j = 0; j < TJ; ++j) {
+      const int cc = n0 + wn * 32 * TJ + 32 * j + r0;
       ccol[j] = cc < Np ? cc : Np - 1;
     }
     const int nch = (Gq + 1) / 2;
     // a ring of PF prefetched steps: the loads of step ch + PF - 1 are issued
     // before the MFMAs of step ch
     constexpr int PF = 4;
-    float pn[PF][4];
-    uint2 cn[PF][2];
-    auto fetch = [&](float (&pd)[4], uint2 (&cd)[2], int ch) {
+    float pn[PF][TI];
+    uint2 cn[PF][TJ];
+    auto fetch = [&](float (&pd)[TI], uint2 (&cd)[TJ], int ch) {
       const int g = 2 * ch + hf;
       const bool gv = ch < nch && g < Gq;
       const int gg = gv ? g : Gq - 1;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pd[i] = gsum[(int64_t)gg * M + prow[i]];
+      for (int i = 0; i < TI; ++i) pd[i] = gsum[(int64_t)gg * M + prow[i]];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) cd[j] = corr[(int64_t)gg * Np + ccol[j]];
+      for (int j = 0; j < TJ; ++j) cd[j] = corr[(int64_t)gg * Np + ccol[j]];
       if (!gv) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pd[i] = 0.f;
-        cd[0] = cd[1] = make_uint2(0u, 0u);
+        for (int i = 0; i < TI; ++i) pd[i] = 0.f;
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) cd[j] = make_uint2(0u, 0u);
       }
     };
-    auto step = [&](const float (&pc)[4], const uint2 (&cc2)[2]) {
-      uint4 av[4], bv[2];
+    auto step = [&](const float (&pc)[TI], const uint2 (&cc2)[TJ]) {
+      uint4 av[TI], bv[TJ];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < TI; ++i) {
         // p1 = 8 floor(p / 8), p2 = p - p1, both exact (p is an integer below 2^11)
         const float p1 = __builtin_floorf(pc[i] * 0.125f) * 8.0f;
         const uint32_t b1 = __float_as_uint(p1), b2 = __float_as_uint(pc[i] - p1);
@@ -722,14 +744,14 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_sc
                            __builtin_amdgcn_perm(b2, b2, 0x07060302u), 0u);
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < TJ; ++j) {
         const uint32_t x = cc2[j].x, yv = cc2[j].y;  // (n1 | n2 << 16), n3
         bv[j] = make_uint4(x, (x << 16) | yv, __builtin_amdgcn_perm(yv, x, 0x05040302u), 0u);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < TJ; ++j) {
           v16f acc;
 #pragma unroll
           for (int e = 0; e < 16; ++e) acc[e] = F[i][j][e];
@@ -753,11 +775,12 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_sc
   // ---- epilogue: y = a_scale * F + mean * w1 + bias (same order as the other
   // kernels), bf16, staged per 32-row slab in this wave's own LDS area (no
   // workgroup barrier) so that the global writes are 16-byte runs
-  float w1v[2] = {0.f, 0.f}, bv[2] = {0.f, 0.f};
+  float w1v[TJ], bv[TJ];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int col = n0 + wn * 64 + 32 * j + r;
-    if (col < N) {
+  for (int j = 0; j < TJ; ++j) {
+    const int col = n0 + wn * 32 * TJ + 32 * j + r;
+    w1v[j] = bv[j] = 0.f;
+    if (EXTRA && col < N) {
       if (mean) w1v[j] = w1[col];
       if (bias) bv[j] = bias[col];
     }
@@ -766,33 +789,44 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_sc
   uint8_t *stg = smem + V2::STG_OFF + wave * (32 * SROW);
   const bool vec_ok = ((reinterpret_cast<uintptr_t>(y) & 15) == 0) && (ldy % 8 == 0);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < TI; ++i) {
 #pragma unroll
     for (int e4 = 0; e4 < 4; ++e4) {
       // rows (e4 * 8 + half * 4 + 0..3) of this 32-row slab: one 16-byte read each
-      const int rl = wm * 128 + 32 * i + e4 * 8 + half * 4;
+      const int rl = wm * 32 * TI + 32 * i + e4 * 8 + half * 4;
       const float4 al4 = *reinterpret_cast<const float4 *>(lds_alpha + rl);
-      const float4 mu4 = mean ? *reinterpret_cast<const float4 *>(lds_mean + rl) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 mu4 = (EXTRA && mean) ? *reinterpret_cast<const float4 *>(lds_mean + rl)
+                                         : make_float4(0.f, 0.f, 0.f, 0.f);
       const float al[4] = {al4.x, al4.y, al4.z, al4.w}, mu[4] = {mu4.x, mu4.y, mu4.z, mu4.w};
 #pragma unroll
-      for (int e1 = 0; e1 < 4; ++e1) {
-        const int e = 4 * e4 + e1;
-        const int rr = e4 * 8 + half * 4 + e1;
+      for (int j = 0; j < TJ; ++j) {
+        float v[4];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          float v = al[e1] * F[i][j][e];
-          if (mean) v = __builtin_fmaf(mu[e1], w1v[j], v);
-          if (bias) v = v + bv[j];
-          *reinterpret_cast<uint16_t *>(stg + rr * SROW + (32 * j + r) * 2) = f32_to_bf16_rne(v);
+        for (int e1 = 0; e1 < 4; ++e1) {
+          v[e1] = al[e1] * F[i][j][4 * e4 + e1];
+          if constexpr (EXTRA) {
+            if (mean) v[e1] = __builtin_fmaf(mu[e1], w1v[j], v[e1]);
+            if (bias) v[e1] = v[e1] + bv[j];
+          }
+        }
+        // rows rr and rr + 1 of one column: one conversion, two 2-byte writes
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const int rr = e4 * 8 + half * 4 + 2 * p;
+          const uint32_t pk = bf16x2_rne(v[2 * p], v[2 * p + 1]);
+          *reinterpret_cast<uint16_t *>(stg + rr * SROW + (32 * j + r) * 2) = (uint16_t)pk;
+          *reinterpret_cast<uint16_t *>(stg + (rr + 1) * SROW + (32 * j + r) * 2) = (uint16_t)(pk >> 16);
         }
       }
     }
-    const int cl = (lane & 7) * 8;
-    const int col = n0 + wn * 64 + cl;
+    // the slab is 32 rows of 4 TJ 16-byte pieces: 2 TJ rounds of 64 pieces
+    constexpr int CPR = 4 * TJ;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int rr = (lane >> 3) + 8 * q;
-      const int64_t row = m0 + wm * 128 + 32 * i + rr;
+    for (int q = 0; q < 2 * TJ; ++q) {
+      const int piece = lane + 64 * q;
+      const int rr = piece / CPR, cl = (piece % CPR) * 8;
+      const int col = n0 + wn * 32 * TJ + cl;
+      const int64_t row = m0 + wm * 32 * TI + 32 * i + rr;
       const uint4 v = *reinterpret_cast<const uint4 *>(stg + rr * SROW + cl * 2);
       if (row >= M) continue;
       uint16_t *dst = y + row * ldy + col;
@@ -808,22 +842,76 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_sc
   }
 }
 
-template <int NSLOT, bool PAIRED, bool ASYM>
-hipError_t launch_v2(const uint8_t *A, const float *a_scale, int64_t M, int K, const uint8_t *W, const float *wst,
-                     int N, int Np, const float *mean, const float *w1, const float *bias, uint16_t *y, int64_t ldy,
-                     hipStream_t stream, const float *gsum = nullptr, const uint32_t *corr = nullptr) {
-  using V2 = V2C<NSLOT>;
+template <int NSLOT, bool PAIRED, bool ASYM, int TI, int TJ, bool EXTRA>
+hipError_t launch_v2_kernel(const uint8_t *A, const float *a_scale, int64_t M, int K, const uint8_t *W,
+                            const float *wst, int N, int Np, const float *mean, const float *w1, const float *bias,
+                            uint16_t *y, int64_t ldy, hipStream_t stream, const float *gsum, const uint32_t *corr) {
+  using V2 = V2C<NSLOT, TI, TJ>;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)gemm_fp6_v2_kernel<NSLOT, PAIRED, ASYM>,
+    hipError_t e = hipFuncSetAttribute((const void *)gemm_fp6_v2_kernel<NSLOT, PAIRED, ASYM, TI, TJ, EXTRA>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, V2::LDS_BYTES);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   dim3 grid((unsigned)((N + V2::BN - 1) / V2::BN), (unsigned)((M + V2::BM - 1) / V2::BM));
-  hipLaunchKernelGGL((gemm_fp6_v2_kernel<NSLOT, PAIRED, ASYM>), grid, dim3(512), V2::LDS_BYTES, stream, A, a_scale, M, K,
-                     W, wst, N, Np, mean, w1, bias, y, ldy, gsum, reinterpret_cast<const uint2 *>(corr));
+  hipLaunchKernelGGL((gemm_fp6_v2_kernel<NSLOT, PAIRED, ASYM, TI, TJ, EXTRA>), grid, dim3(512), V2::LDS_BYTES, stream,
+                     A, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy, gsum,
+                     reinterpret_cast<const uint2 *>(corr));
   return hipGetLastError();
+}
+
+// the epilogue without the rank-1 and bias terms when neither is given
+template <int NSLOT, bool PAIRED, bool ASYM, int TI, int TJ>
+hipError_t launch_v2_shape(const uint8_t *A, const float *a_scale, int64_t M, int K, const uint8_t *W,
+                           const float *wst, int N, int Np, const float *mean, const float *w1, const float *bias,
+                           uint16_t *y, int64_t ldy, hipStream_t stream, const float *gsum, const uint32_t *corr) {
+  if (mean || bias)
+    return launch_v2_kernel<NSLOT, PAIRED, ASYM, TI, TJ, true>(A, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy,
+                                                               stream, gsum, corr);
+  return launch_v2_kernel<NSLOT, PAIRED, ASYM, TI, TJ, false>(A, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy,
+                                                              stream, gsum, corr);
+}
+
+// Compute units of the current device (one workgroup of the v2 kernel fills a CU).
+int device_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+  cached[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+// The 256 x 192 shape when it needs fewer column-slots of work: waves of
+// workgroups (one per CU) times the tile width.  4096 x 3072 on 256 CUs: 192
+// tiles of 256 x 256 leave a quarter of the CUs idle, 256 tiles of 256 x 192
+// fill them; at 4096 x 12288 both shapes cost the same and 256 x 256 stays.
+// OQ_FP6_TILE_N=256 or 192 in the environment forces one shape (for tuning
+// and tests); any other value, or none, chooses as above.
+bool use_narrow(int64_t M, int N) {
+  if (const char *f = getenv("OQ_FP6_TILE_N")) {
+    if (strcmp(f, "256") == 0) return false;
+    if (strcmp(f, "192") == 0) return true;
+  }
+  const int64_t cus = device_cus();
+  const int64_t mt = (M + 255) / 256;
+  const int64_t w256 = (mt * ((N + 255) / 256) + cus - 1) / cus;
+  const int64_t w192 = (mt * ((N + 191) / 192) + cus - 1) / cus;
+  return w192 * 192 < w256 * 256;
+}
+
+template <int NSLOT, bool PAIRED, bool ASYM>
+hipError_t launch_v2(const uint8_t *A, const float *a_scale, int64_t M, int K, const uint8_t *W, const float *wst,
+                     int N, int Np, const float *mean, const float *w1, const float *bias, uint16_t *y, int64_t ldy,
+                     hipStream_t stream, const float *gsum = nullptr, const uint32_t *corr = nullptr) {
+  if (use_narrow(M, N))
+    return launch_v2_shape<NSLOT, PAIRED, ASYM, 2, 3>(A, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy, stream,
+                                                      gsum, corr);
+  return launch_v2_shape<NSLOT, PAIRED, ASYM, 4, 2>(A, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy, stream,
+                                                    gsum, corr);
 }
 
 }  // namespace

@@ -167,6 +167,28 @@ def test_gemm_asym(oq, M, K, N, center, bias):
     say("  within 1 bf16 ulp:", frac)
 
 
+@pytest.mark.parametrize("shape", ["256", "192"])
+@pytest.mark.parametrize("M,K,N", [(300, 1024, 520), (257, 512, 1000)])
+def test_gemm_asym_shapes(oq, monkeypatch, shape, M, K, N):
+    """Both workgroup shapes of the corrected GEMM, forced through OQ_FP6_TILE_N."""
+    say("case gemm asym shape", shape, M, K, N)
+    monkeypatch.setenv("OQ_FP6_TILE_N", shape)
+    rng = np.random.default_rng(M + 3 * N + K)
+    G = K // 64
+    qa = rng.integers(-7, 8, (M, K))
+    alpha = rng.uniform(0.05, 2.0, M).astype(np.float32)
+    Q = rng.integers(0, 16, (N, K))
+    sig = OA.bf16_rne(rng.uniform(1e-3, 1e-2, (N, G)).astype(np.float32))
+    z = OA.bf16_rne(rng.uniform(-1.0, 16.0, (N, G)).astype(np.float32))
+    b = rng.standard_normal(N).astype(np.float32)
+    w = oq.oq_prepack_w4_asym(to_dev(OQ.pack_int4(Q - 8)), to_dev(_bits(sig)), to_dev(_bits(z)), N, K, 64)
+    gs = np.ascontiguousarray(OA.group_sums(qa, 64).astype(np.float32).T)
+    y = oq.oq_gemm_w4a4_asym(to_dev(tile(qa)), to_dev(alpha), to_dev(gs), w, N, M, K, bias=to_dev(b))
+    torch.cuda.synchronize()
+    y_ref, S = OA.linear_asym(alpha, qa, Q, sig, OA.correction(sig, z), 64, bias=b)
+    check_output(to_host(y), y_ref, S, 7 * G, "asym gemm shape " + shape)
+
+
 def test_asym_layer_full_size(oq):
     """4096 x 3072 -> 3072 (the W4A4 DiT linear, RPBH h = 1024): weights
     quantized asymmetrically on the GPU, activations with group sums, the
