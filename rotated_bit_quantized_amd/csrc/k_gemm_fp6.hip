@@ -30,10 +30,11 @@
 // per tile after the main loop on bfloat16 matrix cores, with p and C split
 // into pieces that make every product exact in float32.
 //
-// Workgroup: WM x WN wavefronts, each computing 128 x 64 outputs (4 x 2 MFMA
-// tiles of 32 x 32).  The k loop walks the 64-wide groups; each group's A, B
-// and scale tiles are copied global -> LDS with global_load_lds_dwordx4
-// (no register staging) into a 4-stage ring, one barrier per group.
+// Both kernels walk the 64-wide k groups; each group's A, B and scale tiles
+// are copied global -> LDS with global_load_lds (no register staging) into a
+// ring of stages.  The two-plane kernel (6-bit activations) runs WM x WN
+// wavefronts of 128 x 64 outputs with one barrier per group; the single-plane
+// kernel's shapes and schedule are described at its definition.
 #include "oq_internal.h"
 
 #include <atomic>
@@ -438,18 +439,17 @@ hipError_t launch_cfg(const uint8_t *A, int64_t a_plane_bytes, const float *a_sc
 
 // ---------------------------------------------------------------------------
 // Single-plane kernel with the fragments of the next k-group prefetched into
-// registers while the current group computes.  Workgroup 256 x 256 (8 waves
-// of 128 x 64), a 3-slot ring of one k-group per slot, one barrier per group:
-//   group g start: own copies of stage g+1 done (vmcnt) and own LDS reads of
-//   slot g done (lgkmcnt) -> barrier -> refill slot g with stage g+3;
-//   during group g: A fragments of g+1 are loaded into a[i] right after the
-//   last MFMA that reads a[i]; B fragments and scales of g+1 go to a second
-//   set of registers.  So every group starts with its operands in registers.
-// Copies use an SGPR base per unit plus a loop-invariant per-lane offset;
-// every wave issues exactly 3 code units (1 KiB) and 1 scale unit (256 B,
-// waves w and w+4 copy the same bytes) per stage, so the vmcnt values are
-// compile-time constants.  The loop is unrolled by the ring depth, so LDS
-// addresses are immediates.
+// registers while the current group computes.  Workgroups of 8 or 4 waves
+// (shapes below), a 4-slot ring of one k-group per slot and one barrier per
+// two groups:
+//   before groups g, g+1: own copies of stages g+1, g+2 done (vmcnt) and own
+//   LDS reads done (lgkmcnt) -> barrier -> refill the two slots read during
+//   the previous two groups with stages g+3, g+4;
+//   during group g: each fragment of g+1 is loaded into its register right
+//   after the last MFMA of g that reads it, the scales of g+1 at the start.
+//   So every group starts with its operands in registers.
+// Copies use an SGPR base per unit plus a loop-invariant per-lane offset.
+// The loop is unrolled by the ring depth, so LDS addresses are immediates.
 // ---------------------------------------------------------------------------
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
@@ -469,27 +469,44 @@ __device__ __forceinline__ void wait_vm() {
 }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-// Workgroup shapes: 256 rows, 8 waves, each wave TI x TJ MFMA tiles of 32 x 32.
-//   TI = 4, TJ = 2: waves 2 (rows) x 4 (columns), 256 x 256 outputs;
-//   TI = 2, TJ = 3: waves 4 x 2, 256 x 192 outputs.
-// Every stage holds 8 A and 8 B tiles and 256 scales whatever the shape, so
-// every wave issues the same copies per stage (a 192-wide tile loads the two
-// column blocks past its end too and leaves them unread).
-template <int NSLOT_, int TI_, int TJ_>
+// Workgroup shapes: each wave computes TI x TJ MFMA tiles of 32 x 32.
+//   8 waves, TI = 4, TJ = 2: waves 2 (rows) x 4 (columns), 256 x 256 outputs;
+//   8 waves, TI = 2, TJ = 3: waves 4 x 2, 256 x 192 outputs;
+//   4 waves, TI = 4, TJ = 2: waves 2 x 2, 256 x 128 outputs;
+//   4 waves, TI = 2, TJ = 3: waves 2 x 2, 128 x 192 outputs.
+// An 8-wave stage holds 8 A and 8 B tiles and 256 scales whatever the shape
+// (a 192-wide tile loads the two column blocks past its end too and leaves
+// them unread); a 4-wave stage holds exactly its tiles.  The code bytes of a
+// stage are split evenly over the waves as U4 1 KiB units (16 bytes a lane)
+// and U1 256-byte units (4 bytes a lane), and every wave copies one 256-byte
+// chunk of scales, so all waves issue the same copies per stage and the
+// vmcnt values are compile-time constants.  4-wave workgroups fit two to a CU
+// (LDS under 80 KiB, the epilogue staging reusing the ring), so one
+// workgroup's barrier waits and epilogue overlap the other's main loop.
+template <int NSLOT_, int TI_, int TJ_, int WAVES_>
 struct V2C {
-  static constexpr int WAVES = 8, TI = TI_, TJ = TJ_, NSLOT = NSLOT_;
-  static constexpr int WAVES_M = 8 / TI, WAVES_N = 8 / WAVES_M;
+  static constexpr int WAVES = WAVES_, TI = TI_, TJ = TJ_, NSLOT = NSLOT_;
+  static constexpr int WAVES_M = WAVES == 8 ? 8 / TI : 2, WAVES_N = WAVES / WAVES_M;
   static constexpr int BM = 32 * TI * WAVES_M, BN = 32 * TJ * WAVES_N;
-  static constexpr int A_BYTES = 8 * CHUNK_TILE, B_BYTES = 8 * CHUNK_TILE;
-  static constexpr int S_BYTES = 1024;
+  static constexpr int A_BYTES = (WAVES == 8 ? 8 : BM / 32) * CHUNK_TILE;
+  static constexpr int B_BYTES = (WAVES == 8 ? 8 : BN / 32) * CHUNK_TILE;
+  static constexpr int S_CHUNKS = WAVES == 8 ? 4 : BN / 64;  // 256-byte scale chunks
+  static constexpr int S_BYTES = 256 * S_CHUNKS;
   static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
+  static constexpr int PER_WAVE = (A_BYTES + B_BYTES) / WAVES;
+  static constexpr int U4 = PER_WAVE / 1024, U1 = (PER_WAVE % 1024) / 256;
   static constexpr int ROWS_OFF = NSLOT * STAGE;
   static constexpr int SROW = 64 * TJ + 16;  // padded bytes per staged output row of 32 TJ bf16
-  static constexpr int STG_OFF = ROWS_OFF + 2 * BM * 4;  // per-wave epilogue staging
-  static constexpr int LDS_BYTES = STG_OFF + WAVES * 32 * SROW;
-  static constexpr int PER_STAGE = 4;  // copy instructions per wave per stage
-  static_assert(BM == 256 && BN <= 256 && WAVES_M * WAVES_N == WAVES, "workgroup shape");
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  // per-wave epilogue staging: its own region for 8 waves, the ring for 4
+  static constexpr int STG_OFF = WAVES == 8 ? ROWS_OFF + 2 * BM * 4 : 0;
+  static constexpr int LDS_BYTES = WAVES == 8 ? STG_OFF + WAVES * 32 * SROW : ROWS_OFF + 2 * BM * 4;
+  static constexpr int PER_STAGE = U4 + U1 + 1;  // copy instructions per wave per stage
+  static_assert(WAVES_M * WAVES_N == WAVES && BM <= 256 && BN <= 256, "workgroup shape");
+  static_assert((A_BYTES + B_BYTES) % WAVES == 0 && PER_WAVE % 256 == 0, "even copy split");
+  static_assert(A_BYTES % 1024 == 0 && (U1 == 0 || U4 * WAVES * 1024 >= A_BYTES), "units within one operand");
+  static_assert(BN % 64 == 0 || WAVES == 8, "whole scale chunks");
+  static_assert(WAVES == 8 || WAVES * 32 * SROW <= ROWS_OFF, "staging fits the ring");
+  static_assert(LDS_BYTES <= (WAVES == 8 ? 160 : 80) * 1024, "LDS budget");
 };
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -507,14 +524,14 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) {
   return r;
 }
 
-template <int NSLOT, bool PAIRED, bool ASYM, int TI, int TJ, bool EXTRA>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int NSLOT, bool PAIRED, bool ASYM, int TI, int TJ, int WAVES, bool EXTRA>
+__global__ void __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_scale, int64_t M, int K,
                    const uint8_t *__restrict__ W, const float *__restrict__ wst, int N, int Np,
                    const float *__restrict__ mean, const float *__restrict__ w1, const float *__restrict__ bias,
                    uint16_t *__restrict__ y, int64_t ldy, const float *__restrict__ gsum,
                    const uint2 *__restrict__ corr) {
-  using V2 = V2C<NSLOT, TI, TJ>;
+  using V2 = V2C<NSLOT, TI, TJ, WAVES>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const uint32_t lds0 = lds_addr_of(smem);
   const int lane = threadIdx.x & 63;
@@ -534,14 +551,20 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_sc
       for (int e = 0; e < 16; ++e) F[i][j][e] = 0.f;
 
 
-  // ---- copy units of this wave (stage 0 addresses; k-group kg adds kg * 1536)
-  const uint8_t *cbase[3];
-  uint32_t coff[3], clds[3];
+  // ---- copy units of this wave (stage 0 addresses; k-group kg adds kg * 1536):
+  // byte o of the stage's code region is byte o % 1536 of A row block
+  // m0 / 32 + o / 1536 below A_BYTES, else of B column block n0 / 32 + (o -
+  // A_BYTES) / 1536 (clamped to the last block: those bytes are never read)
+  constexpr int NU = V2::U4 + V2::U1;
+  const uint8_t *cbase[NU];
+  uint32_t coff[NU], clds[NU];
 #pragma unroll
-  for (int q = 0; q < 3; ++q) {
-    const int u = wave + 8 * q;  // 0..23: 12 A units then 12 B units
-    const int o = 1024 * u + 16 * lane;
-    if (u < 12) {
+  for (int q = 0; q < NU; ++q) {
+    const bool wide = q < V2::U4;
+    const uint32_t ubase = wide ? 1024u * (wave + WAVES * q)
+                                : 1024u * WAVES * V2::U4 + 256u * (wave + WAVES * (q - V2::U4));
+    const int o = (int)ubase + (wide ? 16 : 4) * lane;
+    if (ubase < (uint32_t)V2::A_BYTES) {  // a unit lies within one operand
       int64_t rb = m0 / 32 + o / CHUNK_TILE;
       if (rb > mblocks - 1) rb = mblocks - 1;
       cbase[q] = A;
@@ -553,9 +576,9 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_sc
       cbase[q] = W;
       coff[q] = (uint32_t)((int64_t)cb * G * CHUNK_TILE + oo % CHUNK_TILE);
     }
-    clds[q] = 1024u * u;
+    clds[q] = ubase;
   }
-  const int sc = wave & 3;  // scale chunk: columns n0 + 64 sc + lane
+  const int sc = wave % V2::S_CHUNKS;  // scale chunk: columns n0 + 64 sc + lane
   int scol = n0 + 64 * sc + lane;
   if (scol > Np - 1) scol = Np - 1;
   const uint32_t soff = 4u * scol, slds = V2::A_BYTES + V2::B_BYTES + 256u * sc;
@@ -563,7 +586,10 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_sc
   auto issue = [&](int slot, int kg) {
     const uint32_t base = lds0 + slot * V2::STAGE;
 #pragma unroll
-    for (int q = 0; q < 3; ++q) dma16_s(cbase[q] + (int64_t)kg * CHUNK_TILE, coff[q], base + clds[q]);
+    for (int q = 0; q < NU; ++q) {
+      if (q < V2::U4) dma16_s(cbase[q] + (int64_t)kg * CHUNK_TILE, coff[q], base + clds[q]);
+      else dma4_s(cbase[q] + (int64_t)kg * CHUNK_TILE, coff[q], base + clds[q]);
+    }
     dma4_s(wst + (int64_t)kg * Np, soff, base + slds);
   };
 
@@ -579,7 +605,7 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_sc
 
   float *lds_alpha = reinterpret_cast<float *>(smem + V2::ROWS_OFF);
   float *lds_mean = lds_alpha + V2::BM;
-  for (int t = threadIdx.x; t < V2::BM; t += 512) {
+  for (int t = threadIdx.x; t < V2::BM; t += 64 * WAVES) {
     const int64_t row = m0 + t;
     lds_alpha[t] = row < M ? a_scale[row] : 0.f;
     lds_mean[t] = (mean && row < M) ? mean[row] : 0.f;
@@ -611,17 +637,27 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_sc
 
   // one k-group: MFMAs of group g from registers, the next group's operands
   // (stage g+1, slot JN) read into the registers as they free up
+  // Tiles run with the longer operand list innermost (column-major when TI >
+  // TJ), so every fragment has at least min(TI, TJ) + 1 tiles between its
+  // reload and its next use; the next group's scales are read at the start.
+  constexpr bool JMAJOR = TI > TJ;
+  auto tile_i = [](int t) { return JMAJOR ? t % TI : t / TJ; };
+  auto tile_j = [](int t) { return JMAJOR ? t / TI : t % TJ; };
   auto group = [&](auto jnc) {
     constexpr int JN = decltype(jnc)::value;
     constexpr int NT = TI * TJ;
     v16f dprev;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const int i = t / TJ, j = t % TJ;
+      const int i = tile_i(t), j = tile_j(t);
       const v16f dt = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], (v16f){}, 2, 2, 0, 127, 0, wsc);
       __builtin_amdgcn_sched_barrier(0);
+      if (t == 0) {
+#pragma unroll
+        for (int jj = 0; jj < TJ; ++jj) nsw[jj] = fs[JN * V2::STAGE / 4 + 32 * jj];
+      }
       if (t > 0) {
-        const int ip = (t - 1) / TJ, jp = (t - 1) % TJ;
+        const int ip = tile_i(t - 1), jp = tile_j(t - 1);
 #pragma unroll
         for (int e = 0; e < 16; ++e) F[ip][jp][e] = __builtin_fmaf(sw[jp], dprev[e], F[ip][jp][e]);
       }
@@ -630,10 +666,6 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_sc
       // (after the last group this reads a settled slot that is never used)
       if (j == TJ - 1) a[i] = frag_at(fa + JN * V2::STAGE + i * CHUNK_TILE, fa + JN * V2::STAGE + i * CHUNK_TILE + tail);
       if (i == TI - 1) b[j] = frag_at(fb + JN * V2::STAGE + j * CHUNK_TILE, fb + JN * V2::STAGE + j * CHUNK_TILE + tail);
-      if (t == NT - 1) {
-#pragma unroll
-        for (int jj = 0; jj < TJ; ++jj) nsw[jj] = fs[JN * V2::STAGE / 4 + 32 * jj];
-      }
       __builtin_amdgcn_sched_barrier(0);
       dprev = dt;
     }
@@ -786,6 +818,11 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_sc
     }
   }
   constexpr int SROW = V2::SROW;
+  if constexpr (WAVES == 4) {
+    // the staging reuses the ring: every wave's reads of it are done
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+  }
   uint8_t *stg = smem + V2::STG_OFF + wave * (32 * SROW);
   const bool vec_ok = ((reinterpret_cast<uintptr_t>(y) & 15) == 0) && (ldy % 8 == 0);
 #pragma unroll
@@ -842,35 +879,35 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_sc
   }
 }
 
-template <int NSLOT, bool PAIRED, bool ASYM, int TI, int TJ, bool EXTRA>
+template <int NSLOT, bool PAIRED, bool ASYM, int TI, int TJ, int WAVES, bool EXTRA>
 hipError_t launch_v2_kernel(const uint8_t *A, const float *a_scale, int64_t M, int K, const uint8_t *W,
                             const float *wst, int N, int Np, const float *mean, const float *w1, const float *bias,
                             uint16_t *y, int64_t ldy, hipStream_t stream, const float *gsum, const uint32_t *corr) {
-  using V2 = V2C<NSLOT, TI, TJ>;
+  using V2 = V2C<NSLOT, TI, TJ, WAVES>;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)gemm_fp6_v2_kernel<NSLOT, PAIRED, ASYM, TI, TJ, EXTRA>,
+    hipError_t e = hipFuncSetAttribute((const void *)gemm_fp6_v2_kernel<NSLOT, PAIRED, ASYM, TI, TJ, WAVES, EXTRA>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, V2::LDS_BYTES);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   dim3 grid((unsigned)((N + V2::BN - 1) / V2::BN), (unsigned)((M + V2::BM - 1) / V2::BM));
-  hipLaunchKernelGGL((gemm_fp6_v2_kernel<NSLOT, PAIRED, ASYM, TI, TJ, EXTRA>), grid, dim3(512), V2::LDS_BYTES, stream,
-                     A, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy, gsum,
+  hipLaunchKernelGGL((gemm_fp6_v2_kernel<NSLOT, PAIRED, ASYM, TI, TJ, WAVES, EXTRA>), grid, dim3(64 * WAVES),
+                     V2::LDS_BYTES, stream, A, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy, gsum,
                      reinterpret_cast<const uint2 *>(corr));
   return hipGetLastError();
 }
 
 // the epilogue without the rank-1 and bias terms when neither is given
-template <int NSLOT, bool PAIRED, bool ASYM, int TI, int TJ>
+template <int NSLOT, bool PAIRED, bool ASYM, int TI, int TJ, int WAVES>
 hipError_t launch_v2_shape(const uint8_t *A, const float *a_scale, int64_t M, int K, const uint8_t *W,
                            const float *wst, int N, int Np, const float *mean, const float *w1, const float *bias,
                            uint16_t *y, int64_t ldy, hipStream_t stream, const float *gsum, const uint32_t *corr) {
   if (mean || bias)
-    return launch_v2_kernel<NSLOT, PAIRED, ASYM, TI, TJ, true>(A, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy,
-                                                               stream, gsum, corr);
-  return launch_v2_kernel<NSLOT, PAIRED, ASYM, TI, TJ, false>(A, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy,
-                                                              stream, gsum, corr);
+    return launch_v2_kernel<NSLOT, PAIRED, ASYM, TI, TJ, WAVES, true>(A, a_scale, M, K, W, wst, N, Np, mean, w1, bias,
+                                                                      y, ldy, stream, gsum, corr);
+  return launch_v2_kernel<NSLOT, PAIRED, ASYM, TI, TJ, WAVES, false>(A, a_scale, M, K, W, wst, N, Np, mean, w1, bias,
+                                                                     y, ldy, stream, gsum, corr);
 }
 
 // Compute units of the current device (one workgroup of the v2 kernel fills a CU).
@@ -885,33 +922,52 @@ int device_cus() {
   return v;
 }
 
-// The 256 x 192 shape when it needs fewer column-slots of work: waves of
-// workgroups (one per CU) times the tile width.  4096 x 3072 on 256 CUs: 192
-// tiles of 256 x 256 leave a quarter of the CUs idle, 256 tiles of 256 x 192
-// fill them; at 4096 x 12288 both shapes cost the same and 256 x 256 stays.
-// OQ_FP6_TILE_N=256 or 192 in the environment forces one shape (for tuning
-// and tests); any other value, or none, chooses as above.
-bool use_narrow(int64_t M, int N) {
-  if (const char *f = getenv("OQ_FP6_TILE_N")) {
-    if (strcmp(f, "256") == 0) return false;
-    if (strcmp(f, "192") == 0) return true;
+enum class Shape { W8_256x256, W8_256x192, W4_256x128, W4_128x192 };
+
+// Workgroup shape for an M x N product.  Large products take an 8-wave
+// shape, 256 x 192 when its whole waves of workgroups (one per CU) cover
+// fewer output columns than 256 x 256 (4096 x 3072 on 256 CUs: 256 tiles
+// instead of 192), else 256 x 256 (the two cost the same at 4096 x 12288 and
+// 256 x 256 runs 6% faster per output).  Products with fewer 256 x 256 tiles
+// than half the CUs take the 4-wave 128 x 192 shape: 2.7x more workgroups,
+// each with a CU to itself.  The 4-wave shapes match the 8-wave ones per
+// output when the CUs are full.
+// OQ_FP6_TILE=256x256, 256x192, 256x128 or 128x192 in the environment forces
+// one shape (for tuning and tests); any other value, or none, chooses.
+Shape pick_shape(int64_t M, int N) {
+  if (const char *f = getenv("OQ_FP6_TILE")) {
+    if (strcmp(f, "256x256") == 0) return Shape::W8_256x256;
+    if (strcmp(f, "256x192") == 0) return Shape::W8_256x192;
+    if (strcmp(f, "256x128") == 0) return Shape::W4_256x128;
+    if (strcmp(f, "128x192") == 0) return Shape::W4_128x192;
   }
   const int64_t cus = device_cus();
   const int64_t mt = (M + 255) / 256;
-  const int64_t w256 = (mt * ((N + 255) / 256) + cus - 1) / cus;
+  const int64_t t256 = mt * ((N + 255) / 256);
+  if (2 * t256 < cus) return Shape::W4_128x192;
+  const int64_t w256 = (t256 + cus - 1) / cus;
   const int64_t w192 = (mt * ((N + 191) / 192) + cus - 1) / cus;
-  return w192 * 192 < w256 * 256;
+  return w192 * 192 < w256 * 256 ? Shape::W8_256x192 : Shape::W8_256x256;
 }
 
 template <int NSLOT, bool PAIRED, bool ASYM>
 hipError_t launch_v2(const uint8_t *A, const float *a_scale, int64_t M, int K, const uint8_t *W, const float *wst,
                      int N, int Np, const float *mean, const float *w1, const float *bias, uint16_t *y, int64_t ldy,
                      hipStream_t stream, const float *gsum = nullptr, const uint32_t *corr = nullptr) {
-  if (use_narrow(M, N))
-    return launch_v2_shape<NSLOT, PAIRED, ASYM, 2, 3>(A, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy, stream,
-                                                      gsum, corr);
-  return launch_v2_shape<NSLOT, PAIRED, ASYM, 4, 2>(A, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy, stream,
-                                                    gsum, corr);
+  switch (pick_shape(M, N)) {
+    case Shape::W8_256x192:
+      return launch_v2_shape<NSLOT, PAIRED, ASYM, 2, 3, 8>(A, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy,
+                                                           stream, gsum, corr);
+    case Shape::W4_256x128:
+      return launch_v2_shape<NSLOT, PAIRED, ASYM, 4, 2, 4>(A, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy,
+                                                           stream, gsum, corr);
+    case Shape::W4_128x192:
+      return launch_v2_shape<NSLOT, PAIRED, ASYM, 2, 3, 4>(A, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy,
+                                                           stream, gsum, corr);
+    default:
+      return launch_v2_shape<NSLOT, PAIRED, ASYM, 4, 2, 8>(A, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy,
+                                                           stream, gsum, corr);
+  }
 }
 
 }  // namespace

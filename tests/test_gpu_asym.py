@@ -167,12 +167,12 @@ def test_gemm_asym(oq, M, K, N, center, bias):
     say("  within 1 bf16 ulp:", frac)
 
 
-@pytest.mark.parametrize("shape", ["256", "192"])
+@pytest.mark.parametrize("shape", ["256x256", "256x192", "256x128", "128x192"])
 @pytest.mark.parametrize("M,K,N", [(300, 1024, 520), (257, 512, 1000)])
 def test_gemm_asym_shapes(oq, monkeypatch, shape, M, K, N):
-    """Both workgroup shapes of the corrected GEMM, forced through OQ_FP6_TILE_N."""
+    """Every workgroup shape of the corrected GEMM, forced through OQ_FP6_TILE."""
     say("case gemm asym shape", shape, M, K, N)
-    monkeypatch.setenv("OQ_FP6_TILE_N", shape)
+    monkeypatch.setenv("OQ_FP6_TILE", shape)
     rng = np.random.default_rng(M + 3 * N + K)
     G = K // 64
     qa = rng.integers(-7, 8, (M, K))

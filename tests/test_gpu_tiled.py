@@ -131,15 +131,16 @@ def test_tiled_gemm(oq, M, N, K, afmt, rank1, bias):
     check_output(to_host(y_t), y_ref, S, K // 64, "tiled gemm")
 
 
-@pytest.mark.parametrize("shape", ["256", "192"])
+@pytest.mark.parametrize("shape", ["256x256", "256x192", "256x128", "128x192"])
 @pytest.mark.parametrize("M,N,K,rank1,bias", [(300, 520, 1024, True, True), (257, 1000, 512, False, True),
                                               (31, 32, 64, False, False), (600, 3072, 3072, True, False)])
 def test_tiled_gemm_shapes(oq, monkeypatch, shape, M, N, K, rank1, bias):
-    """Both workgroup shapes of the single-plane kernel (256 x 256 and
-    256 x 192 outputs), forced through OQ_FP6_TILE_N: bit-identical to the
-    canonical GEMM and within the bound of the oracle's product."""
+    """Every workgroup shape of the single-plane kernel (8 waves: 256 x 256,
+    256 x 192 outputs; 4 waves: 256 x 128, 128 x 192), forced through
+    OQ_FP6_TILE: bit-identical to the canonical GEMM and within the bound of
+    the oracle's product."""
     say("case tiled gemm shape", shape, M, N, K, rank1, bias)
-    monkeypatch.setenv("OQ_FP6_TILE_N", shape)
+    monkeypatch.setenv("OQ_FP6_TILE", shape)
     rng = np.random.default_rng(M + N * 7 + K)
     qa = rng.integers(-7, 8, size=(M, K))
     qw = rng.integers(-7, 8, size=(N, K))
