@@ -483,29 +483,32 @@ __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F
 // vmcnt values are compile-time constants.  4-wave workgroups fit two to a CU
 // (LDS under 80 KiB, the epilogue staging reusing the ring), so one
 // workgroup's barrier waits and epilogue overlap the other's main loop.
-template <int NSLOT_, int TI_, int TJ_, int WAVES_>
+template <int NSLOT_, int TI_, int TJ_, int WAVES_, int PLANES_>
 struct V2C {
-  static constexpr int WAVES = WAVES_, TI = TI_, TJ = TJ_, NSLOT = NSLOT_;
+  static constexpr int WAVES = WAVES_, TI = TI_, TJ = TJ_, NSLOT = NSLOT_, PLANES = PLANES_;
   static constexpr int WAVES_M = WAVES == 8 ? 8 / TI : 2, WAVES_N = WAVES / WAVES_M;
   static constexpr int BM = 32 * TI * WAVES_M, BN = 32 * TJ * WAVES_N;
-  static constexpr int A_BYTES = (WAVES == 8 ? 8 : BM / 32) * CHUNK_TILE;
+  static constexpr int A_BYTES = (WAVES == 8 ? 8 : BM / 32) * CHUNK_TILE;  // one plane
   static constexpr int B_BYTES = (WAVES == 8 ? 8 : BN / 32) * CHUNK_TILE;
   static constexpr int S_CHUNKS = WAVES == 8 ? 4 : BN / 64;  // 256-byte scale chunks
   static constexpr int S_BYTES = 256 * S_CHUNKS;
-  static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
-  static constexpr int PER_WAVE = (A_BYTES + B_BYTES) / WAVES;
+  static constexpr int B_OFF = PLANES * A_BYTES;  // A planes, then B, then the scales
+  static constexpr int STAGE = B_OFF + B_BYTES + S_BYTES;
+  static constexpr int PER_WAVE = (B_OFF + B_BYTES) / WAVES;
   static constexpr int U4 = PER_WAVE / 1024, U1 = (PER_WAVE % 1024) / 256;
   static constexpr int ROWS_OFF = NSLOT * STAGE;
   static constexpr int SROW = 64 * TJ + 16;  // padded bytes per staged output row of 32 TJ bf16
-  // per-wave epilogue staging: its own region for 8 waves, the ring for 4
-  static constexpr int STG_OFF = WAVES == 8 ? ROWS_OFF + 2 * BM * 4 : 0;
-  static constexpr int LDS_BYTES = WAVES == 8 ? STG_OFF + WAVES * 32 * SROW : ROWS_OFF + 2 * BM * 4;
+  // per-wave epilogue staging: its own region for single-plane 8-wave
+  // workgroups, else the ring (after a barrier)
+  static constexpr bool STG_RING = WAVES == 4 || PLANES == 2;
+  static constexpr int STG_OFF = STG_RING ? 0 : ROWS_OFF + 2 * BM * 4;
+  static constexpr int LDS_BYTES = STG_RING ? ROWS_OFF + 2 * BM * 4 : STG_OFF + WAVES * 32 * SROW;
   static constexpr int PER_STAGE = U4 + U1 + 1;  // copy instructions per wave per stage
   static_assert(WAVES_M * WAVES_N == WAVES && BM <= 256 && BN <= 256, "workgroup shape");
-  static_assert((A_BYTES + B_BYTES) % WAVES == 0 && PER_WAVE % 256 == 0, "even copy split");
-  static_assert(A_BYTES % 1024 == 0 && (U1 == 0 || U4 * WAVES * 1024 >= A_BYTES), "units within one operand");
+  static_assert((B_OFF + B_BYTES) % WAVES == 0 && PER_WAVE % 256 == 0, "even copy split");
+  static_assert(A_BYTES % 1024 == 0 && (U1 == 0 || U4 * WAVES * 1024 >= B_OFF), "units within one operand");
   static_assert(BN % 64 == 0 || WAVES == 8, "whole scale chunks");
-  static_assert(WAVES == 8 || WAVES * 32 * SROW <= ROWS_OFF, "staging fits the ring");
+  static_assert(!STG_RING || WAVES * 32 * SROW <= ROWS_OFF, "staging fits the ring");
   static_assert(LDS_BYTES <= (WAVES == 8 ? 160 : 80) * 1024, "LDS budget");
 };
 
@@ -524,14 +527,16 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) {
   return r;
 }
 
-template <int NSLOT, bool PAIRED, bool ASYM, int TI, int TJ, int WAVES, bool EXTRA>
+template <int NSLOT, bool PAIRED, bool ASYM, int TI, int TJ, int WAVES, bool EXTRA, int PLANES>
 __global__ void __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
-gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_scale, int64_t M, int K,
+gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, int64_t a_plane_bytes, const float *__restrict__ a_scale, int64_t M,
+                   int K,
                    const uint8_t *__restrict__ W, const float *__restrict__ wst, int N, int Np,
                    const float *__restrict__ mean, const float *__restrict__ w1, const float *__restrict__ bias,
                    uint16_t *__restrict__ y, int64_t ldy, const float *__restrict__ gsum,
                    const uint2 *__restrict__ corr) {
-  using V2 = V2C<NSLOT, TI, TJ, WAVES>;
+  using V2 = V2C<NSLOT, TI, TJ, WAVES, PLANES>;
+  static_assert(PLANES == 1 || !ASYM, "asymmetric weights take single-plane activations");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const uint32_t lds0 = lds_addr_of(smem);
   const int lane = threadIdx.x & 63;
@@ -552,9 +557,10 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_sc
 
 
   // ---- copy units of this wave (stage 0 addresses; k-group kg adds kg * 1536):
-  // byte o of the stage's code region is byte o % 1536 of A row block
-  // m0 / 32 + o / 1536 below A_BYTES, else of B column block n0 / 32 + (o -
-  // A_BYTES) / 1536 (clamped to the last block: those bytes are never read)
+  // byte o of the stage's code region is byte o % 1536 of row block m0 / 32 +
+  // (o % A_BYTES) / 1536 of A plane o / A_BYTES below B_OFF, else of B column
+  // block n0 / 32 + (o - B_OFF) / 1536 (clamped to the last block: those
+  // bytes are never read)
   constexpr int NU = V2::U4 + V2::U1;
   const uint8_t *cbase[NU];
   uint32_t coff[NU], clds[NU];
@@ -564,13 +570,14 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_sc
     const uint32_t ubase = wide ? 1024u * (wave + WAVES * q)
                                 : 1024u * WAVES * V2::U4 + 256u * (wave + WAVES * (q - V2::U4));
     const int o = (int)ubase + (wide ? 16 : 4) * lane;
-    if (ubase < (uint32_t)V2::A_BYTES) {  // a unit lies within one operand
-      int64_t rb = m0 / 32 + o / CHUNK_TILE;
+    if (ubase < (uint32_t)V2::B_OFF) {  // a unit lies within one operand (and plane)
+      const int pl = (int)ubase / V2::A_BYTES, oa = o - pl * V2::A_BYTES;
+      int64_t rb = m0 / 32 + oa / CHUNK_TILE;
       if (rb > mblocks - 1) rb = mblocks - 1;
-      cbase[q] = A;
-      coff[q] = (uint32_t)(rb * G * CHUNK_TILE + o % CHUNK_TILE);
+      cbase[q] = A + pl * a_plane_bytes;
+      coff[q] = (uint32_t)(rb * G * CHUNK_TILE + oa % CHUNK_TILE);
     } else {
-      const int oo = o - V2::A_BYTES;
+      const int oo = o - V2::B_OFF;
       int cb = n0 / 32 + oo / CHUNK_TILE;
       if (cb > nblocks - 1) cb = nblocks - 1;
       cbase[q] = W;
@@ -581,7 +588,7 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_sc
   const int sc = wave % V2::S_CHUNKS;  // scale chunk: columns n0 + 64 sc + lane
   int scol = n0 + 64 * sc + lane;
   if (scol > Np - 1) scol = Np - 1;
-  const uint32_t soff = 4u * scol, slds = V2::A_BYTES + V2::B_BYTES + 256u * sc;
+  const uint32_t soff = 4u * scol, slds = V2::B_OFF + V2::B_BYTES + 256u * sc;
 
   auto issue = [&](int slot, int kg) {
     const uint32_t base = lds0 + slot * V2::STAGE;
@@ -596,9 +603,9 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_sc
   const int wm = wave / V2::WAVES_N, wn = wave % V2::WAVES_N;
   const int r = lane & 31, half = lane >> 5;
   const uint8_t *fa = smem + (wm * TI) * CHUNK_TILE + 16 * lane;  // + 1024 - 8 lane: the 8-byte part
-  const uint8_t *fb = smem + V2::A_BYTES + (wn * TJ) * CHUNK_TILE + 16 * lane;
+  const uint8_t *fb = smem + V2::B_OFF + (wn * TJ) * CHUNK_TILE + 16 * lane;
   const int tail = 1024 - 8 * lane;
-  const float *fs = reinterpret_cast<const float *>(smem + V2::A_BYTES + V2::B_BYTES) + wn * 32 * TJ + r;
+  const float *fs = reinterpret_cast<const float *>(smem + V2::B_OFF + V2::B_BYTES) + wn * 32 * TJ + r;
 
   // E8M0 scale of the weight operand: 2^1 for the stored q'/2 of asymmetric codes
   const int wsc = ASYM ? 128 : 127;
@@ -624,10 +631,17 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_sc
   else if (G > 1) wait_vm<V2::PER_STAGE>();
   else wait_vm<0>();
   __builtin_amdgcn_s_barrier();
-  v8i a[TI], b[TJ];
+  // a[p][i]: plane p of A tile i (6-bit codes: the high plane floor(q / 8)
+  // runs with an E8M0 scale of 2^3, the low plane accumulates onto it)
+  v8i a[PLANES][TI], b[TJ];
   float sw[TJ], nsw[TJ];
 #pragma unroll
-  for (int i = 0; i < TI; ++i) a[i] = frag_at(fa + i * CHUNK_TILE, fa + i * CHUNK_TILE + tail);
+  for (int p = 0; p < PLANES; ++p)
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const uint8_t *t0 = fa + p * V2::A_BYTES + i * CHUNK_TILE;
+      a[p][i] = frag_at(t0, t0 + tail);
+    }
 #pragma unroll
   for (int j = 0; j < TJ; ++j) {
     b[j] = frag_at(fb + j * CHUNK_TILE, fb + j * CHUNK_TILE + tail);
@@ -650,7 +664,13 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_sc
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int i = tile_i(t), j = tile_j(t);
-      const v16f dt = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], (v16f){}, 2, 2, 0, 127, 0, wsc);
+      v16f dt;
+      if constexpr (PLANES == 1) {
+        dt = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[0][i], b[j], (v16f){}, 2, 2, 0, 127, 0, wsc);
+      } else {
+        dt = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[0][i], b[j], (v16f){}, 2, 2, 0, 130, 0, wsc);
+        dt = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[1][i], b[j], dt, 2, 2, 0, 127, 0, wsc);
+      }
       __builtin_amdgcn_sched_barrier(0);
       if (t == 0) {
 #pragma unroll
@@ -664,7 +684,13 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_sc
       // operands are reloaded with the next group's values right after their
       // last MFMA: a[i] after tile (i, TJ - 1), b[j] after tile (TI - 1, j)
       // (after the last group this reads a settled slot that is never used)
-      if (j == TJ - 1) a[i] = frag_at(fa + JN * V2::STAGE + i * CHUNK_TILE, fa + JN * V2::STAGE + i * CHUNK_TILE + tail);
+      if (j == TJ - 1) {
+#pragma unroll
+        for (int p = 0; p < PLANES; ++p) {
+          const uint8_t *t0 = fa + JN * V2::STAGE + p * V2::A_BYTES + i * CHUNK_TILE;
+          a[p][i] = frag_at(t0, t0 + tail);
+        }
+      }
       if (i == TI - 1) b[j] = frag_at(fb + JN * V2::STAGE + j * CHUNK_TILE, fb + JN * V2::STAGE + j * CHUNK_TILE + tail);
       __builtin_amdgcn_sched_barrier(0);
       dprev = dt;
@@ -818,7 +844,7 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_sc
     }
   }
   constexpr int SROW = V2::SROW;
-  if constexpr (WAVES == 4) {
+  if constexpr (V2::STG_RING) {
     // the staging reuses the ring: every wave's reads of it are done
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();
@@ -879,35 +905,39 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_sc
   }
 }
 
-template <int NSLOT, bool PAIRED, bool ASYM, int TI, int TJ, int WAVES, bool EXTRA>
-hipError_t launch_v2_kernel(const uint8_t *A, const float *a_scale, int64_t M, int K, const uint8_t *W,
-                            const float *wst, int N, int Np, const float *mean, const float *w1, const float *bias,
-                            uint16_t *y, int64_t ldy, hipStream_t stream, const float *gsum, const uint32_t *corr) {
-  using V2 = V2C<NSLOT, TI, TJ, WAVES>;
+template <int NSLOT, bool PAIRED, bool ASYM, int TI, int TJ, int WAVES, bool EXTRA, int PLANES>
+hipError_t launch_v2_kernel(const uint8_t *A, int64_t plane, const float *a_scale, int64_t M, int K,
+                            const uint8_t *W, const float *wst, int N, int Np, const float *mean, const float *w1,
+                            const float *bias, uint16_t *y, int64_t ldy, hipStream_t stream, const float *gsum,
+                            const uint32_t *corr) {
+  using V2 = V2C<NSLOT, TI, TJ, WAVES, PLANES>;
+  auto kern = gemm_fp6_v2_kernel<NSLOT, PAIRED, ASYM, TI, TJ, WAVES, EXTRA, PLANES>;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)gemm_fp6_v2_kernel<NSLOT, PAIRED, ASYM, TI, TJ, WAVES, EXTRA>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, V2::LDS_BYTES);
+    hipError_t e =
+        hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, V2::LDS_BYTES);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   dim3 grid((unsigned)((N + V2::BN - 1) / V2::BN), (unsigned)((M + V2::BM - 1) / V2::BM));
-  hipLaunchKernelGGL((gemm_fp6_v2_kernel<NSLOT, PAIRED, ASYM, TI, TJ, WAVES, EXTRA>), grid, dim3(64 * WAVES),
-                     V2::LDS_BYTES, stream, A, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy, gsum,
-                     reinterpret_cast<const uint2 *>(corr));
+  hipLaunchKernelGGL(kern, grid, dim3(64 * WAVES), V2::LDS_BYTES, stream, A, plane, a_scale, M, K, W, wst, N, Np, mean,
+                     w1, bias, y, ldy, gsum, reinterpret_cast<const uint2 *>(corr));
   return hipGetLastError();
 }
 
 // the epilogue without the rank-1 and bias terms when neither is given
-template <int NSLOT, bool PAIRED, bool ASYM, int TI, int TJ, int WAVES>
-hipError_t launch_v2_shape(const uint8_t *A, const float *a_scale, int64_t M, int K, const uint8_t *W,
-                           const float *wst, int N, int Np, const float *mean, const float *w1, const float *bias,
-                           uint16_t *y, int64_t ldy, hipStream_t stream, const float *gsum, const uint32_t *corr) {
+template <int NSLOT, bool PAIRED, bool ASYM, int TI, int TJ, int WAVES, int PLANES = 1>
+hipError_t launch_v2_shape(const uint8_t *A, int64_t plane, const float *a_scale, int64_t M, int K,
+                           const uint8_t *W, const float *wst, int N, int Np, const float *mean, const float *w1,
+                           const float *bias, uint16_t *y, int64_t ldy, hipStream_t stream, const float *gsum,
+                           const uint32_t *corr) {
   if (mean || bias)
-    return launch_v2_kernel<NSLOT, PAIRED, ASYM, TI, TJ, WAVES, true>(A, a_scale, M, K, W, wst, N, Np, mean, w1, bias,
-                                                                      y, ldy, stream, gsum, corr);
-  return launch_v2_kernel<NSLOT, PAIRED, ASYM, TI, TJ, WAVES, false>(A, a_scale, M, K, W, wst, N, Np, mean, w1, bias,
-                                                                     y, ldy, stream, gsum, corr);
+    return launch_v2_kernel<NSLOT, PAIRED, ASYM, TI, TJ, WAVES, true, PLANES>(A, plane, a_scale, M, K, W, wst, N, Np,
+                                                                              mean, w1, bias, y, ldy, stream, gsum,
+                                                                              corr);
+  return launch_v2_kernel<NSLOT, PAIRED, ASYM, TI, TJ, WAVES, false, PLANES>(A, plane, a_scale, M, K, W, wst, N, Np,
+                                                                             mean, w1, bias, y, ldy, stream, gsum,
+                                                                             corr);
 }
 
 // Compute units of the current device (one workgroup of the v2 kernel fills a CU).
@@ -956,16 +986,16 @@ hipError_t launch_v2(const uint8_t *A, const float *a_scale, int64_t M, int K, c
                      hipStream_t stream, const float *gsum = nullptr, const uint32_t *corr = nullptr) {
   switch (pick_shape(M, N)) {
     case Shape::W8_256x192:
-      return launch_v2_shape<NSLOT, PAIRED, ASYM, 2, 3, 8>(A, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy,
+      return launch_v2_shape<NSLOT, PAIRED, ASYM, 2, 3, 8>(A, 0, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy,
                                                            stream, gsum, corr);
     case Shape::W4_256x128:
-      return launch_v2_shape<NSLOT, PAIRED, ASYM, 4, 2, 4>(A, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy,
+      return launch_v2_shape<NSLOT, PAIRED, ASYM, 4, 2, 4>(A, 0, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy,
                                                            stream, gsum, corr);
     case Shape::W4_128x192:
-      return launch_v2_shape<NSLOT, PAIRED, ASYM, 2, 3, 4>(A, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy,
+      return launch_v2_shape<NSLOT, PAIRED, ASYM, 2, 3, 4>(A, 0, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy,
                                                            stream, gsum, corr);
     default:
-      return launch_v2_shape<NSLOT, PAIRED, ASYM, 4, 2, 8>(A, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy,
+      return launch_v2_shape<NSLOT, PAIRED, ASYM, 4, 2, 8>(A, 0, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy,
                                                            stream, gsum, corr);
   }
 }
@@ -978,9 +1008,16 @@ hipError_t launch_gemm_fp6(const uint8_t *A, int planes, const float *a_scale, i
   if (M == 0 || N == 0) return hipSuccess;
   const int Np = (N + 31) / 32 * 32;
   const int64_t plane = tiled_bytes(M, K);
-  if (planes == 2) return launch_cfg<2, 4, 2, 3>(A, plane, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy, stream);
   // the prefetching kernel addresses operands with 32-bit offsets from their base
-  if (tiled_bytes(M, K) < (int64_t(1) << 32) && tiled_bytes(Np, K) < (int64_t(1) << 32))
+  const bool off32 = tiled_bytes(M, K) < (int64_t(1) << 32) && tiled_bytes(Np, K) < (int64_t(1) << 32);
+  if (planes == 2) {
+    // two A planes: the 256 x 192 shape, whose registers hold both planes' fragments
+    if (off32)
+      return launch_v2_shape<FP6_SLOTS, FP6_PAIRED, false, 2, 3, 8, 2>(A, plane, a_scale, M, K, W, wst, N, Np, mean,
+                                                                       w1, bias, y, ldy, stream, nullptr, nullptr);
+    return launch_cfg<2, 4, 2, 3>(A, plane, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy, stream);
+  }
+  if (off32)
     return launch_v2<FP6_SLOTS, FP6_PAIRED, false>(A, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy, stream);
   return launch_cfg<2, 4, 1, FP6_STAGES>(A, plane, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy, stream);
 }
