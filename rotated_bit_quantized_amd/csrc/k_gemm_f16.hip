@@ -14,11 +14,18 @@
 // k 8 (l / 32) .. + 7) finds its 8 float16 at chunk + 16 l, so a fragment is
 // one 16-byte LDS read per lane, conflict-free.
 //
-// Workgroup 256 x 256 outputs, 8 wavefronts in a 2 x 4 grid, each 128 x 64
-// (4 x 2 MFMA tiles accumulated in place).  k advances in stages of 32 (two
-// chunks per 32-row block): every wave copies 4 KiB of each stage global ->
-// LDS with global_load_lds_dwordx4 into a 4-slot ring, one barrier per stage.
+// Workgroup of 8 wavefronts, each TI x TJ MFMA tiles of 32 x 32 accumulated
+// in place: TI = 4, TJ = 2 in a 2 x 4 grid (256 x 256 outputs) or TI = 2,
+// TJ = 3 in a 4 x 2 grid (256 x 192, for products whose 256 x 256 tiles
+// would leave CUs idle).  k advances in stages of 32 (two chunks per 32-row
+// block): every wave copies 4 KiB of each stage global -> LDS with
+// global_load_lds_dwordx4 into a 4-slot ring, one barrier per stage.  A
+// stage always holds 8 row blocks and 8 column blocks (a 192-wide tile
+// loads two column blocks past its end and leaves them unread).
 #include "oq_internal.h"
+
+#include <cstdlib>
+#include <cstring>
 
 namespace oq {
 namespace {
@@ -26,20 +33,24 @@ namespace {
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int F16_BM = 256, F16_BN = 256;
-constexpr int F16_SROW = 144;  // padded bytes per staged output row of 64 bf16
+constexpr int F16_BM = 256;
 
-// KC 16-wide chunks per stage, NSLOT stages in the LDS ring
-template <int KC, int NSLOT>
+// KC 16-wide chunks per stage, NSLOT stages in the LDS ring, TI x TJ tiles per wave
+template <int KC, int NSLOT, int TI_ = 4, int TJ_ = 2>
 struct F16C {
+  static constexpr int TI = TI_, TJ = TJ_;
+  static constexpr int WAVES_M = 8 / TI, WAVES_N = 8 / WAVES_M;
+  static constexpr int BN = 32 * TJ * WAVES_N;
+  static constexpr int SROW = 64 * TJ + 16;  // padded bytes per staged output row of 32 TJ bf16
   static constexpr int A_BYTES = (F16_BM / 32) * KC * 1024;
-  static constexpr int B_BYTES = (F16_BN / 32) * KC * 1024;
+  static constexpr int B_BYTES = 8 * KC * 1024;
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int ROWS_OFF = NSLOT * STAGE;
   static constexpr int LDS = ROWS_OFF + 2 * F16_BM * 4;
   static constexpr int PER_STAGE = 2 * KC;  // 1 KiB copies per wave per stage
   static_assert(8 * PER_STAGE * 1024 == STAGE, "every wave copies the same share of a stage");
-  static_assert(8 * 32 * F16_SROW <= ROWS_OFF, "the epilogue staging fits in the ring");
+  static_assert(8 * 32 * SROW <= ROWS_OFF, "the epilogue staging fits in the ring");
+  static_assert(32 * TI * WAVES_M == F16_BM && BN <= 256, "workgroup shape");
   static_assert(LDS <= 160 * 1024, "LDS");
   // chunk 0 of stage g + 1 is read during stage g, so stage g + 1 must be in
   // flight before stage g starts (NSLOT >= 3); the waits below count exactly
@@ -54,12 +65,12 @@ __device__ __forceinline__ void wait_vm() {
 }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-template <int KC, int NSLOT>
+template <int KC, int NSLOT, int TI, int TJ>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_f16_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_scale, int64_t M, int K,
                 const uint8_t *__restrict__ W, int N, int Np, const float *__restrict__ mean,
                 const float *__restrict__ w1, const float *__restrict__ bias, uint16_t *__restrict__ y, int64_t ldy) {
-  using C = F16C<KC, NSLOT>;
+  using C = F16C<KC, NSLOT, TI, TJ>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const uint32_t lds0 = lds_addr_of(smem);
   const int lane = threadIdx.x & 63;
@@ -67,7 +78,7 @@ gemm_f16_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_scale
   const int KCH = K / 16;
   const int S = KCH / KC;
   const int64_t m0 = (int64_t)blockIdx.y * F16_BM;
-  const int n0 = blockIdx.x * F16_BN;
+  const int n0 = blockIdx.x * C::BN;
   const int64_t mblocks = (M + 31) / 32;
   const int nblocks = Np / 32;
 
@@ -106,29 +117,29 @@ gemm_f16_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_scale
     lds_mean[t] = (mean && row < M) ? mean[row] : 0.f;
   }
 
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const int r = lane & 31, half = lane >> 5;
-  v16f acc[4][2];
+  v16f acc[TI][TJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = (v16f){};
+    for (int j = 0; j < TJ; ++j) acc[i][j] = (v16f){};
 
-  // A fragment (row block wm * 4 + i, chunk kc) and B fragment (column block
-  // wn * 2 + j, chunk kc) of the stage in slot `slot`
-  const uint8_t *fa = smem + 16 * lane + (wm * 4) * KC * 1024;
-  const uint8_t *fb = smem + 16 * lane + C::A_BYTES + (wn * 2) * KC * 1024;
-  auto load = [&](v8h (&a)[4], v8h (&b)[2], int slot, int kc) {
+  // A fragment (row block wm * TI + i, chunk kc) and B fragment (column block
+  // wn * TJ + j, chunk kc) of the stage in slot `slot`
+  const uint8_t *fa = smem + 16 * lane + (wm * TI) * KC * 1024;
+  const uint8_t *fb = smem + 16 * lane + C::A_BYTES + (wn * TJ) * KC * 1024;
+  auto load = [&](v8h (&a)[TI], v8h (&b)[TJ], int slot, int kc) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const v8h *>(fa + slot * C::STAGE + (i * KC + kc) * 1024);
+    for (int i = 0; i < TI; ++i) a[i] = *reinterpret_cast<const v8h *>(fa + slot * C::STAGE + (i * KC + kc) * 1024);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) b[j] = *reinterpret_cast<const v8h *>(fb + slot * C::STAGE + (j * KC + kc) * 1024);
+    for (int j = 0; j < TJ; ++j) b[j] = *reinterpret_cast<const v8h *>(fb + slot * C::STAGE + (j * KC + kc) * 1024);
   };
-  auto mma = [&](const v8h (&a)[4], const v8h (&b)[2]) {
+  auto mma = [&](const v8h (&a)[TI], const v8h (&b)[TJ]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < TJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
   };
 
   // Schedule: each stage starts with its first chunk's fragments in registers.
@@ -150,7 +161,7 @@ gemm_f16_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_scale
     else wait_vm<0>();
   }
   __builtin_amdgcn_s_barrier();
-  v8h fr[2][4], gr[2][2];
+  v8h fr[2][TI], gr[2][TJ];
   load(fr[0], gr[0], 0, 0);
 
   for (int g = 0; g < S; ++g) {
@@ -175,9 +186,9 @@ gemm_f16_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_scale
     }
     if constexpr (KC & 1) {  // the next stage starts from buffer 0
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fr[0][i] = fr[1][i];
+      for (int i = 0; i < TI; ++i) fr[0][i] = fr[1][i];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) gr[0][j] = gr[1][j];
+      for (int j = 0; j < TJ; ++j) gr[0][j] = gr[1][j];
     }
   }
 
@@ -185,23 +196,25 @@ gemm_f16_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_scale
   // wave's own LDS area (the ring is free once every wave has passed the
   // barrier) so that the global writes are 16-byte runs
   __syncthreads();
-  float w1v[2] = {0.f, 0.f}, bv[2] = {0.f, 0.f};
+  constexpr int SROW = C::SROW;
+  float w1v[TJ], bv[TJ];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int col = n0 + wn * 64 + 32 * j + r;
+  for (int j = 0; j < TJ; ++j) {
+    const int col = n0 + wn * 32 * TJ + 32 * j + r;
+    w1v[j] = bv[j] = 0.f;
     if (col < N) {
       if (mean) w1v[j] = w1[col];
       if (bias) bv[j] = bias[col];
     }
   }
-  uint8_t *stg = smem + wave * (32 * F16_SROW);
+  uint8_t *stg = smem + wave * (32 * SROW);
   const bool vec_ok = ((reinterpret_cast<uintptr_t>(y) & 15) == 0) && (ldy % 8 == 0);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < TI; ++i) {
 #pragma unroll
     for (int e4 = 0; e4 < 4; ++e4) {
       // rows e4 * 8 + half * 4 + 0..3 of this 32-row slab
-      const int rl = wm * 128 + 32 * i + e4 * 8 + half * 4;
+      const int rl = wm * 32 * TI + 32 * i + e4 * 8 + half * 4;
       const float4 al4 = *reinterpret_cast<const float4 *>(lds_alpha + rl);
       const float4 mu4 = *reinterpret_cast<const float4 *>(lds_mean + rl);
       const float al[4] = {al4.x, al4.y, al4.z, al4.w}, mu[4] = {mu4.x, mu4.y, mu4.z, mu4.w};
@@ -210,21 +223,23 @@ gemm_f16_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_scale
         const int e = 4 * e4 + e1;
         const int rr = e4 * 8 + half * 4 + e1;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < TJ; ++j) {
           float v = al[e1] * acc[i][j][e];
           if (mean) v = __builtin_fmaf(mu[e1], w1v[j], v);
           if (bias) v = v + bv[j];
-          *reinterpret_cast<uint16_t *>(stg + rr * F16_SROW + (32 * j + r) * 2) = f32_to_bf16_rne(v);
+          *reinterpret_cast<uint16_t *>(stg + rr * SROW + (32 * j + r) * 2) = f32_to_bf16_rne(v);
         }
       }
     }
-    const int cl = (lane & 7) * 8;
-    const int col = n0 + wn * 64 + cl;
+    // the slab is 32 rows of 4 TJ 16-byte pieces: 2 TJ rounds of 64 pieces
+    constexpr int CPR = 4 * TJ;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int rr = (lane >> 3) + 8 * q;
-      const int64_t row = m0 + wm * 128 + 32 * i + rr;
-      const uint4 v = *reinterpret_cast<const uint4 *>(stg + rr * F16_SROW + cl * 2);
+    for (int q = 0; q < 2 * TJ; ++q) {
+      const int piece = lane + 64 * q;
+      const int rr = piece / CPR, cl = (piece % CPR) * 8;
+      const int col = n0 + wn * 32 * TJ + cl;
+      const int64_t row = m0 + wm * 32 * TI + 32 * i + rr;
+      const uint4 v = *reinterpret_cast<const uint4 *>(stg + rr * SROW + cl * 2);
       if (row >= M) continue;
       uint16_t *dst = y + row * ldy + col;
       if (vec_ok && col + 8 <= N) {
@@ -318,22 +333,41 @@ __global__ void lm_expand_kernel(const uint8_t *__restrict__ codes, int64_t ldc,
   *reinterpret_cast<uint4 *>(out + idx * 16) = make_uint4(hv[0], hv[1], hv[2], hv[3]);
 }
 
-template <int KC, int NSLOT>
+template <int KC, int NSLOT, int TI, int TJ>
 hipError_t launch_f16(const uint8_t *A, const float *a_scale, int64_t M, int K, const uint8_t *W, int N, int Np,
                       const float *mean, const float *w1, const float *bias, uint16_t *y, int64_t ldy,
                       hipStream_t stream) {
-  using C = F16C<KC, NSLOT>;
+  using C = F16C<KC, NSLOT, TI, TJ>;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)gemm_f16_kernel<KC, NSLOT>,
+    hipError_t e = hipFuncSetAttribute((const void *)gemm_f16_kernel<KC, NSLOT, TI, TJ>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  dim3 grid((unsigned)((N + F16_BN - 1) / F16_BN), (unsigned)((M + F16_BM - 1) / F16_BM));
-  hipLaunchKernelGGL((gemm_f16_kernel<KC, NSLOT>), grid, dim3(512), C::LDS, stream, A, a_scale, M, K, W, N, Np, mean,
-                     w1, bias, y, ldy);
+  dim3 grid((unsigned)((N + C::BN - 1) / C::BN), (unsigned)((M + F16_BM - 1) / F16_BM));
+  hipLaunchKernelGGL((gemm_f16_kernel<KC, NSLOT, TI, TJ>), grid, dim3(512), C::LDS, stream, A, a_scale, M, K, W, N, Np,
+                     mean, w1, bias, y, ldy);
   return hipGetLastError();
+}
+
+// 256 x 192 tiles when their whole waves of workgroups (one per CU) cover
+// fewer output columns than 256 x 256 tiles (4096 x 3072 on 256 CUs: 256
+// tiles instead of 192).  OQ_F16_TILE=256x256 or 256x192 in the environment
+// forces one (for tuning and tests).
+bool f16_narrow(int64_t M, int N) {
+  if (const char *f = getenv("OQ_F16_TILE")) {
+    if (strcmp(f, "256x256") == 0) return false;
+    if (strcmp(f, "256x192") == 0) return true;
+  }
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  const int64_t mt = (M + 255) / 256;
+  const int64_t w256 = (mt * ((N + 255) / 256) + cus - 1) / cus;
+  const int64_t w192 = (mt * ((N + 191) / 192) + cus - 1) / cus;
+  return w192 * 192 < w256 * 256;
 }
 
 }  // namespace
@@ -343,7 +377,8 @@ hipError_t launch_gemm_f16(const uint8_t *A, const float *a_scale, int64_t M, in
                            hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   const int Np = (N + 31) / 32 * 32;
-  return launch_f16<2, 4>(A, a_scale, M, K, W, N, Np, mean, w1, bias, y, ldy, stream);
+  if (f16_narrow(M, N)) return launch_f16<2, 4, 2, 3>(A, a_scale, M, K, W, N, Np, mean, w1, bias, y, ldy, stream);
+  return launch_f16<2, 4, 4, 2>(A, a_scale, M, K, W, N, Np, mean, w1, bias, y, ldy, stream);
 }
 
 hipError_t launch_prepack_w16(const uint8_t *w, const float *ws, int N, int K, int group, uint8_t *out,

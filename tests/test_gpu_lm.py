@@ -164,6 +164,28 @@ def test_gemm_lm(oq, M, K, N, bits, center, bias):
     say("  within 1 bf16 ulp:", frac)
 
 
+@pytest.mark.parametrize("shape", ["256x256", "256x192"])
+@pytest.mark.parametrize("M,K,N,bits", [(300, 1024, 520, 4), (257, 512, 1000, 8), (600, 3072, 3072, 4)])
+def test_gemm_lm_shapes(oq, monkeypatch, shape, M, K, N, bits):
+    """Both workgroup shapes of the float16 GEMM, forced through OQ_F16_TILE."""
+    say("case gemm lm shape", shape, M, K, N, bits)
+    monkeypatch.setenv("OQ_F16_TILE", shape)
+    rng = np.random.default_rng(M + 5 * N + K)
+    c16, thr, c16_d, _ = _tables(oq, K, bits)
+    codes = rng.integers(0, 1 << bits, (M, K)).astype(np.uint8)
+    rho = rng.uniform(0.05, 3.0, M).astype(np.float32)
+    qw = rng.integers(-7, 8, (N, K))
+    sw = rng.uniform(0.001, 0.02, (N, K // 64)).astype(np.float32)
+    mean = rng.standard_normal(M).astype(np.float32)
+    w1 = rng.standard_normal(N).astype(np.float32)
+    w16 = oq.oq_prepack_w16(to_dev(OQ.pack_int4(qw)), to_dev(sw), N, K, 64)
+    packed = OQ.pack_nibbles(codes) if bits <= 4 else codes
+    y = oq.oq_gemm_lm(bits, to_dev(packed), to_dev(rho), w16, N, levels=c16_d, mean=to_dev(mean), w1=to_dev(w1))
+    torch.cuda.synchronize()
+    y_ref, S = LM.linear_lm(codes, rho, c16, LM.weights_f16(qw, sw, 64), mean, w1, None)
+    check_output(to_host(y), y_ref, S, K, "lm gemm shape " + shape)
+
+
 def test_gemm_lm_empty_and_zero(oq):
     K, N, bits = 64, 40, 4
     c16, thr, c16_d, _ = _tables(oq, K, bits)
