@@ -36,52 +36,6 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;
 }
 
-// Row c' of the Paley factor H_m of the Kronecker rotation as a sign mask
-// (bit c set where H_m[c'][c] = -1), from the textbook constructions with
-// chi the quadratic character mod q (Euler's criterion) and the Jacobsthal
-// entries Q[i][j] = chi(j - i): m = 12, 44: type I, q = 11, 43,
-// H = I + [[0, 1^T], [-1, Q]]; m = 36: type II, q = 17, C = [[0, 1^T], [1, Q]],
-// H = [[C + I, C - I], [C - I, -C - I]] (CentriQ Sec. 3 "Hadamard rotation",
-// App. B.1).  m = 1 gives 0.
-__device__ int qchar(int a, int q) {
-  a %= q;
-  if (a < 0) a += q;
-  if (a == 0) return 0;
-  int r = 1, b = a, e = (q - 1) / 2;
-  while (e) {
-    if (e & 1) r = (r * b) % q;
-    b = (b * b) % q;
-    e >>= 1;
-  }
-  return r == 1 ? 1 : -1;
-}
-
-__device__ uint64_t paley_row_mask(int m, int cp) {
-  if (m == 1) return 0;
-  uint64_t msk = 0;
-  if (m == 12 || m == 44) {
-    const int q = m - 1;
-    for (int c = 0; c < m; ++c) {
-      int v;
-      if (cp == 0) v = 1;
-      else if (c == 0) v = -1;
-      else if (c == cp) v = 1;
-      else v = qchar(c - cp, q);
-      if (v < 0) msk |= (uint64_t)1 << c;
-    }
-  } else {  // m == 36, q = 17
-    const int bi = cp / 18, i = cp % 18;
-    for (int c = 0; c < m; ++c) {
-      const int bj = c / 18, j = c % 18;
-      const int cij = (i == 0 && j == 0) ? 0 : (i == 0 || j == 0) ? 1 : (i == j ? 0 : qchar(j - i, 17));
-      const int dij = i == j ? 1 : 0;
-      const int v = (bi == 0 && bj == 0) ? cij + dij : (bi == 1 && bj == 1) ? -cij - dij : cij - dij;
-      if (v < 0) msk |= (uint64_t)1 << c;
-    }
-  }
-  return msk;
-}
-
 // In-register butterflies over the 16 coordinates of one thread (strides 1..8).
 __device__ __forceinline__ void fwht16(float (&u)[E]) {
 #pragma unroll
@@ -508,8 +462,13 @@ hipError_t launch_rpbh_quant(const uint16_t *x, int64_t M, int d, int64_t ldx, c
                              const LmArgs *lm, float *gsum) {
   if (M == 0) return hipSuccess;
   if (rot.kron_m) {
-    // the Kronecker rotation runs in the workgroup kernel at the padded width
+    // the Kronecker rotation runs at the padded width: on the wave kernel for
+    // the shapes it covers, else on the workgroup kernel
     if (pctl || lm || gsum) return hipErrorInvalidValue;
+    const bool wave_mode = out_mode == OUT_F32 || out_mode == OUT_I8 || out_mode == OUT_I4 || out_mode == OUT_FP6 ||
+                           out_mode == OUT_FP6X2;
+    if (wave_mode && rpbh_wave_kron_supported(rot.kron_m, rot.block, d))
+      return launch_rpbh_wave_kron(x, M, d, ldx, rot, center, mean, out_mode, qmax, out, ld_out_bytes, scale, stream);
     const int dp = rot_out_width(rot, d);
     switch (out_mode) {
       case OUT_F32: return launch_t<1, OUT_F32, false, true>(x, M, dp, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, 0, stream, nullptr, d);

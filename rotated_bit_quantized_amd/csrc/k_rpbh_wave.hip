@@ -32,6 +32,15 @@
 //     range (CentriQ Sec. 4.2 "Scale and grid") each lane keeps its four
 //     largest magnitudes and the wavefront merges those lists, which gives the
 //     order statistics the interpolated 0.9995-quantile needs for d <= 4096;
+//   * the factorised rotation (H_m (x) H_b) / sqrt(n') of CentriQ Sec. 4.2
+//     "Rotation" / App. B.1 (template KM = m > 1): lanes load the index-lane
+//     chunks of the row directly (centred over the native width, zero
+//     padding), the Sylvester stages run as above on every block of b, the
+//     row goes through the wave's LDS buffer with true signs, each lane reads
+//     its b / 64 coordinates of every block, forms the m-term sums of the
+//     Paley factor in increasing block order (the signs are compile-time
+//     constants), multiplies by RN32(1 / sqrt(n')) and writes them back, and
+//     the quantiser reads the row in its usual layout;
 //   * Lloyd-Max codes (OrbitQuant PR #25, "Default changes"; the codebook of
 //     the post-rotation marginal): the scale is the row's RMS, from a float64
 //     sum of squares reduced over the wavefront, and each code is the number
@@ -194,6 +203,83 @@ __device__ __forceinline__ void store_fp6_pair(const float (&ta)[16], const floa
   }
 }
 
+// Factorised rotation shapes on the wave path: m = 12 with b = 64, 128, 256
+// (n' = 768, 1536, 3072) and m = 36, 44 with b = 64 (n' = 2304, 2816); a
+// lane holds BPL = b / 64 coordinates of every block in the Paley stage.
+template <int KM, int SLOTS>
+struct KronShape {
+  static constexpr int BPL = KM == 12 ? (SLOTS == 3 ? 4 : SLOTS) : 1;
+  static constexpr int B = 64 * BPL;
+  static_assert(KM * B <= 1024 * SLOTS && KM * B > 1024 * (SLOTS - 1), "width fills the slots");
+};
+
+template <int KM>
+struct PaleyMasks {
+  uint64_t m[KM];
+  constexpr PaleyMasks() : m{} {
+    for (int r = 0; r < KM; ++r) m[r] = paley_row_mask(KM, r);
+  }
+};
+
+// Paley stage of the factorised rotation on a row held as index-lane chunks
+// (values times sg are the Sylvester outputs): out[c' B + i] = c_h *
+// sum_c H_m[c'][c] u[c B + i], the sum in increasing c, through the wave's
+// LDS buffer bf (n' floats); on return v holds the rotated row, true signs.
+template <int SLOTS, int KM>
+__device__ __forceinline__ void kron_paley(float (&v)[SLOTS][16], float *bf, int lane, int il, const bool (&act)[SLOTS],
+                                           float sg, float c_h) {
+  using KS = KronShape<KM, SLOTS>;
+  constexpr int BPL = KS::BPL, B = KS::B;
+  constexpr PaleyMasks<KM> H{};
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s) {
+    if (!act[s]) continue;
+    float4 *dst = reinterpret_cast<float4 *>(bf + 1024 * s + 16 * il);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      dst[k] = make_float4(v[s][4 * k] * sg, v[s][4 * k + 1] * sg, v[s][4 * k + 2] * sg, v[s][4 * k + 3] * sg);
+  }
+  // the wave's own LDS writes are ordered before its reads
+  float u[KM][BPL];
+#pragma unroll
+  for (int c = 0; c < KM; ++c) {
+    const float *src = bf + c * B + BPL * lane;
+    if constexpr (BPL == 4) {
+      const float4 t = *reinterpret_cast<const float4 *>(src);
+      u[c][0] = t.x; u[c][1] = t.y; u[c][2] = t.z; u[c][3] = t.w;
+    } else if constexpr (BPL == 2) {
+      const float2 t = *reinterpret_cast<const float2 *>(src);
+      u[c][0] = t.x; u[c][1] = t.y;
+    } else {
+      u[c][0] = src[0];
+    }
+  }
+#pragma unroll
+  for (int cp = 0; cp < KM; ++cp) {
+    float y[BPL];
+#pragma unroll
+    for (int k = 0; k < BPL; ++k) {
+      float acc = (H.m[cp] & 1) ? -u[0][k] : u[0][k];
+#pragma unroll
+      for (int c = 1; c < KM; ++c) acc = ((H.m[cp] >> c) & 1) ? acc - u[c][k] : acc + u[c][k];
+      y[k] = acc * c_h;
+    }
+    float *dst = bf + cp * B + BPL * lane;  // the coordinates this lane read
+    if constexpr (BPL == 4) *reinterpret_cast<float4 *>(dst) = make_float4(y[0], y[1], y[2], y[3]);
+    else if constexpr (BPL == 2) *reinterpret_cast<float2 *>(dst) = make_float2(y[0], y[1]);
+    else dst[0] = y[0];
+  }
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s) {
+    const float4 *src = reinterpret_cast<const float4 *>(bf + 1024 * s + 16 * il);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float4 t = act[s] ? src[k] : make_float4(0.f, 0.f, 0.f, 0.f);
+      v[s][4 * k] = t.x; v[s][4 * k + 1] = t.y; v[s][4 * k + 2] = t.z; v[s][4 * k + 3] = t.w;
+    }
+  }
+}
+
 // LDS: [offset table: ROUNDS x SLOTS x 4 x 64 lanes x 4 ints][per wave: row copies]
 // [Lloyd-Max modes: 128 float positive thresholds, 256 float16 levels, when
 // they fit in the 160 KiB; otherwise the kernel reads them from global memory]
@@ -211,12 +297,15 @@ constexpr bool is_lm_mode() { return mode == OUT_LM4 || mode == OUT_LM8 || mode 
 
 // mode (OUT_*) is a template argument: one kernel body per output keeps the
 // register count of each near what its own path needs.
-template <int SLOTS, int ROUNDS, int mode, bool PCTL>
+// KM > 0: the factorised rotation with Paley order KM (ROUNDS 0, h = b, din
+// the native width); otherwise din is unused.
+template <int SLOTS, int ROUNDS, int mode, bool PCTL, int KM = 0>
 __global__ void __launch_bounds__(64 * WAVES_PER_WG)
 rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, const int32_t *__restrict__ perm,
                  const int8_t *__restrict__ signs, int h, float c_h, int pow4, int center,
                  float *__restrict__ mean_out, int qmax, void *__restrict__ out, int64_t ld_out_bytes,
-                 float *__restrict__ scale_out, PctlArgs pa, LmArgs la, float *__restrict__ gsum_out) {
+                 float *__restrict__ scale_out, PctlArgs pa, LmArgs la, float *__restrict__ gsum_out, int din) {
+  static_assert(KM == 0 || (ROUNDS == 0 && !PCTL && !is_lm_mode<mode>()), "factorised rotation: plain absmax modes");
   constexpr bool LM = is_lm_mode<mode>();
   using L = WaveLds<SLOTS, ROUNDS, LM>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
@@ -227,13 +316,16 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
   const int nlog = __builtin_ctz((unsigned)h) - 4;  // a Hadamard block spans 2^nlog lanes
   const int il = index_lane(lane, nlog);             // this lane holds coordinates 16 il + j of each slot
 
-  // act: this lane's coordinates of slot s exist (index lane); ld: its
-  // physical 16-coordinate chunk of the row exists (loads, first-round copies)
+  // act: this lane's coordinates of slot s exist (index lane); ld: the
+  // 16-coordinate chunk it loads exists (its physical chunk, or for the
+  // factorised rotation its index-lane chunk of the native row)
+  const int ll = KM ? il : lane;
+  const int dload = KM ? din : d;
   bool act[SLOTS], ld[SLOTS];
 #pragma unroll
   for (int s = 0; s < SLOTS; ++s) {
     act[s] = 1024 * s + 16 * il < d;
-    ld[s] = 1024 * s + 16 * lane < d;
+    ld[s] = 1024 * s + 16 * ll < dload;
   }
   const float c_all = (ROUNDS == 0 || !pow4) ? 1.0f : (ROUNDS == 2 ? c_h * c_h : c_h);  // deferred, exact
   float cst[6];
@@ -241,6 +333,7 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
   for (int k = 0; k < 6; ++k) cst[k] = ((il >> k) & 1) ? -1.0f : 1.0f;
   // sign the lane-bit stages leave on this lane's values
   const float sg = (__builtin_popcount(il & ((1 << nlog) - 1)) & 1) ? -1.0f : 1.0f;
+  const float sgq = KM ? 1.0f : sg;  // the sign the quantiser sees (the Paley stage removes it)
   const int neg_from = 2 * d;  // first-round byte offsets at or above this hit the -x copy
 
   // ---- offset table: byte offsets into this wave's [+row | -row] buffer;
@@ -276,7 +369,7 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
     const uint16_t *xr = x + (rr < M ? rr : M - 1) * ldx;
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s) {
-      const uint4 *src = reinterpret_cast<const uint4 *>(xr + (ld[s] ? 1024 * s + 16 * lane : 0));
+      const uint4 *src = reinterpret_cast<const uint4 *>(xr + (ld[s] ? 1024 * s + 16 * ll : 0));
       nxt[s][0] = src[0];
       nxt[s][1] = src[1];
     }
@@ -331,7 +424,7 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
           if (ld[s]) sum += (double)bf16_lo(w[k]) + (double)bf16_hi(w[k]);
       }
       sum = wave_sum_d(sum);
-      m = (float)(sum / (double)d);
+      m = (float)(sum / (double)dload);
       if (lane == 0) mean_out[row] = m;
     }
 
@@ -391,6 +484,11 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
       }
     }
 
+    if constexpr (KM > 0) {
+      fwht_row<SLOTS>(v, nlog, cst);
+      kron_paley<SLOTS, KM>(v, reinterpret_cast<float *>(buf), lane, il, act, sg, c_h);
+    }
+
     if (ROUNDS == 2) {
       // second-round writer: float32 +row and -row; the lane's values are
       // sg times the first round's outputs, so sg picks the copy they go to
@@ -427,7 +525,7 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
     }
 
     if (mode == OUT_F32) {
-      const float co = c_all * sg;  // exact: both are powers of two up to sign
+      const float co = c_all * sgq;  // exact: both are powers of two up to sign
 #pragma unroll
       for (int s = 0; s < SLOTS; ++s) {
         if (!act[s] || !out) continue;
@@ -454,7 +552,7 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
       const double c2 = (double)c_all * (double)c_all;
       const float rho = fmaxf((float)__builtin_sqrt((ss * c2) / (double)d), 1e-10f);
       if (lane == 0) scale_out[row] = rho;
-      const float inv = __fdiv_rn(1.0f, rho) * (c_all * sg);
+      const float inv = __fdiv_rn(1.0f, rho) * (c_all * sgq);
 #pragma unroll
       for (int s = 0; s < SLOTS; ++s) {
         if (!act[s]) continue;
@@ -561,7 +659,7 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
     }
     const float fq = (float)qmax;
     const float alpha = __fdiv_rn(a, fq);
-    const float inv = __fdiv_rn(fq, a) * (c_all * sg);  // exact rescale: deferred factor and lane sign
+    const float inv = __fdiv_rn(fq, a) * (c_all * sgq);  // exact rescale: deferred factor and lane sign
     if (lane == 0) scale_out[row] = alpha;
 
 #pragma unroll
@@ -642,15 +740,15 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
   }
 }
 
-template <int SLOTS, int ROUNDS, int MODE, bool PCTL>
+template <int SLOTS, int ROUNDS, int MODE, bool PCTL, int KM = 0>
 hipError_t launch_m(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotArgs &rot, int center, float *mean,
                     int qmax, void *out, int64_t ld_out_bytes, float *scale, const PctlArgs &pa, const LmArgs &la,
-                    float *gsum, hipStream_t stream) {
+                    float *gsum, hipStream_t stream, int din = 0) {
   using L = WaveLds<SLOTS, ROUNDS, is_lm_mode<MODE>()>;
   const size_t lds = (size_t)L::TOTAL;
   static bool attr_set = false;
   if (!attr_set && lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void *)rpbh_wave_kernel<SLOTS, ROUNDS, MODE, PCTL>,
+    hipError_t e = hipFuncSetAttribute((const void *)rpbh_wave_kernel<SLOTS, ROUNDS, MODE, PCTL, KM>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
@@ -659,11 +757,11 @@ hipError_t launch_m(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotA
   int64_t grid = (M + 2 * WAVES_PER_WG - 1) / (2 * WAVES_PER_WG);
   if (grid > 1024) grid = 1024;
   if (grid < 1) grid = 1;
-  const int h = ROUNDS ? rot.block : 16;
+  const int h = (ROUNDS || KM) ? rot.block : 16;
   const int pow4 = ROUNDS && ((__builtin_ctz((unsigned)h) & 1) == 0);
-  hipLaunchKernelGGL((rpbh_wave_kernel<SLOTS, ROUNDS, MODE, PCTL>), dim3((unsigned)grid), dim3(64 * WAVES_PER_WG), lds,
-                     stream, x, M, d, ldx, rot.perm, rot.signs, h, rot.c_h, pow4, center, mean, qmax, out,
-                     ld_out_bytes, scale, pa, la, gsum);
+  hipLaunchKernelGGL((rpbh_wave_kernel<SLOTS, ROUNDS, MODE, PCTL, KM>), dim3((unsigned)grid), dim3(64 * WAVES_PER_WG),
+                     lds, stream, x, M, d, ldx, rot.perm, rot.signs, h, rot.c_h, pow4, center, mean, qmax, out,
+                     ld_out_bytes, scale, pa, la, gsum, din);
   return hipGetLastError();
 }
 
@@ -722,7 +820,51 @@ hipError_t launch_r(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotA
   return hipErrorInvalidValue;
 }
 
+template <int SLOTS, int KM>
+hipError_t launch_kron_w(const uint16_t *x, int64_t M, int dp, int din, int64_t ldx, const RotArgs &rot, int center,
+                         float *mean, int mode, int qmax, void *out, int64_t ld_out_bytes, float *scale,
+                         hipStream_t stream) {
+  const PctlArgs no_p{0, 0.0, 0.0, 1.0};
+  const LmArgs no_lm{1, nullptr, nullptr};
+#define OQ_KRON_CASE(MD)                                                                                        \
+  case MD:                                                                                                      \
+    return launch_m<SLOTS, 0, MD, false, KM>(x, M, dp, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, \
+                                             no_p, no_lm, nullptr, stream, din);
+  switch (mode) {
+    OQ_KRON_CASE(OUT_F32)
+    OQ_KRON_CASE(OUT_I8)
+    OQ_KRON_CASE(OUT_I4)
+    OQ_KRON_CASE(OUT_FP6)
+    OQ_KRON_CASE(OUT_FP6X2)
+  }
+#undef OQ_KRON_CASE
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
+
+bool rpbh_wave_kron_supported(int km, int b, int din) {
+  if (din % 16 != 0) return false;
+  return (km == 12 && (b == 64 || b == 128 || b == 256)) || ((km == 36 || km == 44) && b == 64);
+}
+
+hipError_t launch_rpbh_wave_kron(const uint16_t *x, int64_t M, int din, int64_t ldx, const RotArgs &rot, int center,
+                                 float *mean, int mode, int qmax, void *out, int64_t ld_out_bytes, float *scale,
+                                 hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  const int km = rot.kron_m, b = rot.block;
+  if (!rpbh_wave_kron_supported(km, b, din)) return hipErrorInvalidValue;
+  const int dp = km * b;
+  if (km == 12 && b == 64)
+    return launch_kron_w<1, 12>(x, M, dp, din, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, stream);
+  if (km == 12 && b == 128)
+    return launch_kron_w<2, 12>(x, M, dp, din, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, stream);
+  if (km == 12)
+    return launch_kron_w<3, 12>(x, M, dp, din, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, stream);
+  if (km == 36)
+    return launch_kron_w<3, 36>(x, M, dp, din, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, stream);
+  return launch_kron_w<3, 44>(x, M, dp, din, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, stream);
+}
 
 bool rpbh_wave_supported(int d) { return d >= 16 && d <= 4096 && d % 16 == 0; }
 

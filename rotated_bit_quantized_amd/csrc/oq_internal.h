@@ -21,6 +21,52 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+// Row c' of the Paley factor H_m of the Kronecker rotation as a sign mask
+// (bit c set where H_m[c'][c] = -1), from the textbook constructions with
+// chi the quadratic character mod q (Euler's criterion) and the Jacobsthal
+// entries Q[i][j] = chi(j - i): m = 12, 44: type I, q = 11, 43,
+// H = I + [[0, 1^T], [-1, Q]]; m = 36: type II, q = 17, C = [[0, 1^T], [1, Q]],
+// H = [[C + I, C - I], [C - I, -C - I]] (CentriQ Sec. 3 "Hadamard rotation",
+// App. B.1).  m = 1 gives 0.
+__host__ __device__ constexpr int qchar(int a, int q) {
+  a %= q;
+  if (a < 0) a += q;
+  if (a == 0) return 0;
+  int r = 1, b = a, e = (q - 1) / 2;
+  while (e) {
+    if (e & 1) r = (r * b) % q;
+    b = (b * b) % q;
+    e >>= 1;
+  }
+  return r == 1 ? 1 : -1;
+}
+
+__host__ __device__ constexpr uint64_t paley_row_mask(int m, int cp) {
+  if (m == 1) return 0;
+  uint64_t msk = 0;
+  if (m == 12 || m == 44) {
+    const int q = m - 1;
+    for (int c = 0; c < m; ++c) {
+      int v = 0;
+      if (cp == 0) v = 1;
+      else if (c == 0) v = -1;
+      else if (c == cp) v = 1;
+      else v = qchar(c - cp, q);
+      if (v < 0) msk |= (uint64_t)1 << c;
+    }
+  } else {  // m == 36, q = 17
+    const int bi = cp / 18, i = cp % 18;
+    for (int c = 0; c < m; ++c) {
+      const int bj = c / 18, j = c % 18;
+      const int cij = (i == 0 && j == 0) ? 0 : (i == 0 || j == 0) ? 1 : (i == j ? 0 : qchar(j - i, 17));
+      const int dij = i == j ? 1 : 0;
+      const int v = (bi == 0 && bj == 0) ? cij + dij : (bi == 1 && bj == 1) ? -cij - dij : cij - dij;
+      if (v < 0) msk |= (uint64_t)1 << c;
+    }
+  }
+  return msk;
+}
+
 // FP6 E2M3 bit pattern of an integer code q in [-7, 7] (exact: sign bit 5,
 // exponent bits 4..3 with bias 1, mantissa bits 2..0).  The magnitude goes
 // through an 8-entry byte table held in two dwords (v_perm_b32).
@@ -123,6 +169,13 @@ hipError_t launch_rpbh_quant(const uint16_t *x, int64_t M, int d, int64_t ldx,
 
 // K1, one wavefront per row (activation rows of width d <= 4096).
 bool rpbh_wave_supported(int d);
+// Factorised rotation on the wave kernel: Paley order km and Sylvester
+// block b with km = 12, b in {64, 128, 256} or km in {36, 44}, b = 64, and a
+// native width din that is a multiple of 16.
+bool rpbh_wave_kron_supported(int km, int b, int din);
+hipError_t launch_rpbh_wave_kron(const uint16_t *x, int64_t M, int din, int64_t ldx, const RotArgs &rot, int center,
+                                 float *mean, int mode, int qmax, void *out, int64_t ld_out_bytes, float *scale,
+                                 hipStream_t stream);
 hipError_t launch_rpbh_wave(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotArgs &rot, int center,
                             float *mean, int mode, int qmax, void *out, int64_t ld_out_bytes, float *scale,
                             hipStream_t stream, const PctlArgs *pctl = nullptr, const LmArgs *lm = nullptr,
