@@ -6,7 +6,10 @@ at the padded width, and the product on those codes, against oracle/kron.py.
 Widths cover every Paley order and the padding cases: 1152 = 36 x 32 and
 2816 = 44 x 64 and 3072 = 12 x 256 (native), 2240 -> 2304 = 36 x 64 and
 5120 -> 5632 = 44 x 128 (padded), 1920 -> 2048 (m = 1, Sylvester stages
-across wavefronts), 12288 = 12 x 1024."""
+across wavefronts), 12288 = 12 x 1024.  The wavefront-per-row kernel takes
+m = 12 with b = 64, 128, 256 and m = 36, 44 with b = 64 (768, 1504 -> 1536,
+2240, 2704 -> 2816, 2816, 3008 -> 3072, 3072); the other widths run on the
+workgroup kernel."""
 import sys
 
 import numpy as np
@@ -18,6 +21,7 @@ from oracle import kron as KR
 from oracle import linear as OL
 from oracle import quant as OQ
 from parity import check_codes, check_output, check_rotated, to_dev, to_host
+from tiling import row_mask, split_a6, tile
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -51,7 +55,8 @@ def _oracle_rot(xb, n, center):
     return x32, mean
 
 
-WIDTHS = [(1152, False), (2816, True), (3072, False), (2240, True), (5120, False), (1920, True), (12288, False)]
+WIDTHS = [(1152, False), (2816, True), (3072, False), (2240, True), (5120, False), (1920, True), (12288, False),
+          (768, True), (1504, False), (2704, True), (3008, True)]
 
 
 @pytest.mark.parametrize("n,center", WIDTHS)
@@ -75,7 +80,8 @@ def test_kron_rotate(oq, n, center):
 
 
 @pytest.mark.parametrize("n,center,afmt", [(1152, True, 8), (2240, False, 4), (2816, False, 6), (1920, True, 4),
-                                           (3072, False, 4)])
+                                           (3072, False, 4), (1504, True, 4), (768, False, 6), (3008, True, 8),
+                                           (2704, True, 6)])
 def test_kron_quant_act(oq, n, center, afmt):
     m, b, npad = oq.oq_kron_plan(n)
     say("case kron quant", n, center, afmt)
@@ -95,6 +101,15 @@ def test_kron_quant_act(oq, n, center, afmt):
     np.testing.assert_array_equal(to_host(out["scale"]), alpha)
     if tiled is not None:
         np.testing.assert_array_equal(to_host(tiled["scale"]), to_host(out["scale"]))
+        got = to_host(tiled["codes"])
+        plane = oq.oq_tiled_bytes(M, npad)
+        live = row_mask(M, npad)
+        if afmt == 4:
+            np.testing.assert_array_equal(got[:plane][live], tile(codes)[live])
+        else:
+            qh, ql = split_a6(codes)
+            np.testing.assert_array_equal(got[:plane][live], tile(qh)[live])
+            np.testing.assert_array_equal(got[plane:2 * plane][live], tile(ql)[live])
 
 
 @pytest.mark.parametrize("n,N,group", [(1152, 70, 64), (2240, 40, 64), (1920, 33, 128)])
