@@ -33,7 +33,8 @@
 //     largest magnitudes and the wavefront merges those lists, which gives the
 //     order statistics the interpolated 0.9995-quantile needs for d <= 4096;
 //   * the factorised rotation (H_m (x) H_b) / sqrt(n') of CentriQ Sec. 4.2
-//     "Rotation" / App. B.1 (template KM = m > 1): lanes load the index-lane
+//     "Rotation" / App. B.1 (template KM = m; m = 1 is the Sylvester
+//     transform of the whole row, up to 4096 wide): lanes load the index-lane
 //     chunks of the row directly (centred over the native width, zero
 //     padding), the Sylvester stages run as above on every block of b, the
 //     row goes through the wave's LDS buffer with true signs, each lane reads
@@ -333,7 +334,7 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
   for (int k = 0; k < 6; ++k) cst[k] = ((il >> k) & 1) ? -1.0f : 1.0f;
   // sign the lane-bit stages leave on this lane's values
   const float sg = (__builtin_popcount(il & ((1 << nlog) - 1)) & 1) ? -1.0f : 1.0f;
-  const float sgq = KM ? 1.0f : sg;  // the sign the quantiser sees (the Paley stage removes it)
+  const float sgq = KM > 1 ? 1.0f : sg;  // the sign the quantiser sees (the Paley stage removes it)
   const int neg_from = 2 * d;  // first-round byte offsets at or above this hit the -x copy
 
   // ---- offset table: byte offsets into this wave's [+row | -row] buffer;
@@ -484,9 +485,32 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
       }
     }
 
-    if constexpr (KM > 0) {
+    if constexpr (KM > 1) {
       fwht_row<SLOTS>(v, nlog, cst);
       kron_paley<SLOTS, KM>(v, reinterpret_cast<float *>(buf), lane, il, act, sg, c_h);
+    } else if constexpr (KM == 1) {
+      // H_1 = 1: the Sylvester transform of the whole padded row; blocks of
+      // 2048 and 4096 add in-register stages across slots (strides 1024,
+      // 2048; a lane's slots share its sign), then one multiply by c_h
+      fwht_row<SLOTS>(v, nlog, cst);
+#pragma unroll
+      for (int st = 1; st < SLOTS; st <<= 1)
+        if (1024 * 2 * st <= h) {
+#pragma unroll
+          for (int s = 0; s < SLOTS; ++s)
+            if ((s & st) == 0 && s + st < SLOTS) {
+#pragma unroll
+              for (int j = 0; j < 16; ++j) {
+                const float a0 = v[s][j], b0 = v[s + st][j];
+                v[s][j] = a0 + b0;
+                v[s + st][j] = a0 - b0;
+              }
+            }
+        }
+#pragma unroll
+      for (int s = 0; s < SLOTS; ++s)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[s][j] = v[s][j] * c_h;
     }
 
     if (ROUNDS == 2) {
@@ -845,7 +869,8 @@ hipError_t launch_kron_w(const uint16_t *x, int64_t M, int dp, int din, int64_t 
 
 bool rpbh_wave_kron_supported(int km, int b, int din) {
   if (din % 16 != 0) return false;
-  return (km == 12 && (b == 64 || b == 128 || b == 256)) || ((km == 36 || km == 44) && b == 64);
+  return (km == 1 && b >= 16 && b <= 4096 && (b <= 1024 || b == 2048 || b == 4096)) ||
+         (km == 12 && (b == 64 || b == 128 || b == 256)) || ((km == 36 || km == 44) && b == 64);
 }
 
 hipError_t launch_rpbh_wave_kron(const uint16_t *x, int64_t M, int din, int64_t ldx, const RotArgs &rot, int center,
@@ -855,6 +880,12 @@ hipError_t launch_rpbh_wave_kron(const uint16_t *x, int64_t M, int din, int64_t 
   const int km = rot.kron_m, b = rot.block;
   if (!rpbh_wave_kron_supported(km, b, din)) return hipErrorInvalidValue;
   const int dp = km * b;
+  if (km == 1 && b <= 1024)
+    return launch_kron_w<1, 1>(x, M, dp, din, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, stream);
+  if (km == 1 && b == 2048)
+    return launch_kron_w<2, 1>(x, M, dp, din, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, stream);
+  if (km == 1)
+    return launch_kron_w<4, 1>(x, M, dp, din, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, stream);
   if (km == 12 && b == 64)
     return launch_kron_w<1, 12>(x, M, dp, din, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, stream);
   if (km == 12 && b == 128)

@@ -170,8 +170,9 @@ hipError_t launch_rpbh_quant(const uint16_t *x, int64_t M, int d, int64_t ldx,
 // K1, one wavefront per row (activation rows of width d <= 4096).
 bool rpbh_wave_supported(int d);
 // Factorised rotation on the wave kernel: Paley order km and Sylvester
-// block b with km = 12, b in {64, 128, 256} or km in {36, 44}, b = 64, and a
-// native width din that is a multiple of 16.
+// block b with km = 1, b <= 1024 or b in {2048, 4096}; km = 12, b in {64,
+// 128, 256}; or km in {36, 44}, b = 64; and a native width din that is a
+// multiple of 16.
 bool rpbh_wave_kron_supported(int km, int b, int din);
 hipError_t launch_rpbh_wave_kron(const uint16_t *x, int64_t M, int din, int64_t ldx, const RotArgs &rot, int center,
                                  float *mean, int mode, int qmax, void *out, int64_t ld_out_bytes, float *scale,

@@ -7,9 +7,10 @@ Widths cover every Paley order and the padding cases: 1152 = 36 x 32 and
 2816 = 44 x 64 and 3072 = 12 x 256 (native), 2240 -> 2304 = 36 x 64 and
 5120 -> 5632 = 44 x 128 (padded), 1920 -> 2048 (m = 1, Sylvester stages
 across wavefronts), 12288 = 12 x 1024.  The wavefront-per-row kernel takes
-m = 12 with b = 64, 128, 256 and m = 36, 44 with b = 64 (768, 1504 -> 1536,
-2240, 2704 -> 2816, 2816, 3008 -> 3072, 3072); the other widths run on the
-workgroup kernel."""
+m = 1 up to 4096 wide (496 -> 512, 1008 -> 1024, 1920 and 2000 -> 2048,
+3504 -> 4096), m = 12 with b = 64, 128, 256 and m = 36, 44 with b = 64
+(768, 1504 -> 1536, 2240, 2704 -> 2816, 2816, 3008 -> 3072, 3072); the
+other widths run on the workgroup kernel."""
 import sys
 
 import numpy as np
@@ -56,7 +57,8 @@ def _oracle_rot(xb, n, center):
 
 
 WIDTHS = [(1152, False), (2816, True), (3072, False), (2240, True), (5120, False), (1920, True), (12288, False),
-          (768, True), (1504, False), (2704, True), (3008, True)]
+          (768, True), (1504, False), (2704, True), (3008, True), (1008, False), (496, True), (3504, True),
+          (2000, False)]
 
 
 @pytest.mark.parametrize("n,center", WIDTHS)
@@ -81,7 +83,7 @@ def test_kron_rotate(oq, n, center):
 
 @pytest.mark.parametrize("n,center,afmt", [(1152, True, 8), (2240, False, 4), (2816, False, 6), (1920, True, 4),
                                            (3072, False, 4), (1504, True, 4), (768, False, 6), (3008, True, 8),
-                                           (2704, True, 6)])
+                                           (2704, True, 6), (3504, False, 4), (496, True, 8)])
 def test_kron_quant_act(oq, n, center, afmt):
     m, b, npad = oq.oq_kron_plan(n)
     say("case kron quant", n, center, afmt)
