@@ -53,6 +53,9 @@ RPBH_CASES = [
     (3, 1024, 256, 1, False),
     (4, 2048, 512, 2, False),
     (1, 4096, 1024, 2, True),
+    # past the wavefront kernel's 4096: the workgroup kernel, up to the 16384 limit
+    (3, 8192, 1024, 2, True),
+    (2, 16384, 512, 1, False),
 ]
 
 
@@ -83,6 +86,26 @@ def test_quant_act_int(oq, M, K, h, rounds, center, afmt):
     say("case quant_act", M, K, h, rounds, center, afmt)
     perm, signs = _meta(K, h, rounds, K + 3 * h)
     xb = _x(M, K, M + K, scale=3.0, mean=-1.5 if center else 0.0)
+    rot = oq.Rotation.rpbh(to_dev(perm), to_dev(signs), h)
+    out = oq.oq_quant_act(to_dev(xb), rot, afmt, center=center)
+    torch.cuda.synchronize()
+    ref = OL.activations_int(xb, perm, signs, h, afmt, center)
+    codes = to_host(out["codes"])
+    if afmt == 4:
+        codes = OQ.unpack_int4(codes.view(np.uint8))
+    check_codes(codes.astype(np.int32), ref["codes"], ref["flags"], "act codes")
+    np.testing.assert_array_equal(to_host(out["scale"]), ref["alpha"])
+    if center:
+        np.testing.assert_array_equal(to_host(out["mean"]), ref["mean"])
+
+
+@pytest.mark.parametrize("M,K,h,rounds,center,afmt", [(5, 8192, 1024, 2, True, 4), (3, 16384, 256, 1, False, 8),
+                                                      (4, 6144, 1024, 1, False, 6)])
+def test_quant_act_widest(oq, M, K, h, rounds, center, afmt):
+    """Widths above 4096 (the workgroup kernel) up to the 16384 limit."""
+    say("case quant_act widest", M, K, h, rounds, center, afmt)
+    perm, signs = _meta(K, h, rounds, K + h)
+    xb = _x(M, K, M + 3 * K, scale=2.0, mean=1.0 if center else 0.0)
     rot = oq.Rotation.rpbh(to_dev(perm), to_dev(signs), h)
     out = oq.oq_quant_act(to_dev(xb), rot, afmt, center=center)
     torch.cuda.synchronize()
