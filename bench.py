@@ -294,7 +294,7 @@ def _time_asym(torch, oq, WL, reps=40, warmup=5):
     fmt = oq.OQ_A4 | oq.OQ_TILED
     codes = torch.empty(oq.oq_tiled_bytes(M, K), dtype=torch.uint8, device=dev)
     scale = torch.empty(M, dtype=torch.float32, device=dev)
-    gsum = torch.empty((K // 64, M), dtype=torch.float32, device=dev)
+    gsum = torch.empty((K // 64, M), dtype=torch.int32, device=dev)
     ys = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for N, _ in ws]
 
     def launches(i):

@@ -403,23 +403,26 @@ int oq_prepack_w4_asym(const uint8_t *w, const uint16_t *sigma, const uint16_t *
 
 /*
  * oq_quant_act_gsum -- oq_quant_act for afmt OQ_A4 | OQ_TILED or
- * OQ_A6 | OQ_TILED (OQ_SCALE_PCTL allowed), which also writes gsum float32
- * [d/64][M] (group-major), the sum of the codes of every 64-wide group
- * (exact integers).
+ * OQ_A6 | OQ_TILED (OQ_SCALE_PCTL allowed), which also writes gsum uint32
+ * [d/64][M] (group-major): the sum p of the codes of every 64-wide group
+ * (an integer, |p| < 2048) as the operand word of oq_gemm_w4a4_asym, two
+ * bfloat16 values whose sum is p exactly: p1 = 8 floor(p / 8) in bits 0-15
+ * and p2 = p - p1 (0..7) in bits 16-31.
  * d % 64 == 0, d <= 4096.
  */
 int oq_quant_act_gsum(const uint16_t *x, int64_t M, int32_t d, int64_t ldx, const oq_rot *rot, int center, int afmt,
-                      void *codes, float *scale, float *gsum, float *mean, hipStream_t stream);
+                      void *codes, float *scale, uint32_t *gsum, float *mean, hipStream_t stream);
 
 /*
  * oq_gemm_w4a4_asym -- tiled 4-bit activations times asymmetric weights:
  *   y[t][o] = bf16_RNE( a_scale[t] * sum_g (sigma[o][g] acc_g[t][o]
  *                        - corr[g][o] gsum[g][t]) + mean[t] w1[o] + bias[o] )
  *   acc_g = exact sum over the group of q_a (Q - 8).
- * afmt must be OQ_A4 | OQ_TILED; qa, a_scale, gsum from oq_quant_act_gsum;
+ * afmt must be OQ_A4 | OQ_TILED; qa, a_scale, gsum (the packed group sums
+ * described above) from oq_quant_act_gsum;
  * w_tiled, w_scale_t, corr from oq_prepack_w4_asym; K % 64 == 0.
  */
-int oq_gemm_w4a4_asym(int afmt, const uint8_t *qa, const float *a_scale, const float *gsum, int64_t M, int32_t K,
+int oq_gemm_w4a4_asym(int afmt, const uint8_t *qa, const float *a_scale, const uint32_t *gsum, int64_t M, int32_t K,
                       const uint8_t *w_tiled, const float *w_scale_t, const uint32_t *corr, int32_t N, const float *mean,
                       const float *w1, const float *bias, uint16_t *y, int64_t ldy, hipStream_t stream);
 

@@ -426,8 +426,8 @@ def oq_quant_act_gsum(x, rot: Optional[Rotation], afmt: int, center: bool = Fals
         codes = torch.empty(max(16, planes * oq_tiled_bytes(M, d)), dtype=torch.uint8, device=dev)
     if scale is None:
         scale = torch.empty(M, dtype=torch.float32, device=dev)
-    if gsum is None:
-        gsum = torch.empty((d // 64, M), dtype=torch.float32, device=dev)
+    if gsum is None:  # one word per (group, row): two bfloat16 pieces of the group sum
+        gsum = torch.empty((d // 64, M), dtype=torch.int32, device=dev)
     if center and mean is None:
         mean = torch.empty(M, dtype=torch.float32, device=dev)
     _check(_lib.oq_quant_act_gsum(_p(x), M, d, x.stride(0), _rref(rot), int(center), afmt, _p(codes), _p(scale),

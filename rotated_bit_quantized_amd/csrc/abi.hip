@@ -747,7 +747,7 @@ int oq_prepack_w4_asym(const uint8_t *w, const uint16_t *sigma, const uint16_t *
 }
 
 int oq_quant_act_gsum(const uint16_t *x, int64_t M, int32_t d, int64_t ldx, const oq_rot *rot, int center, int afmt,
-                      void *codes, float *scale, float *gsum, float *mean, hipStream_t stream) {
+                      void *codes, float *scale, uint32_t *gsum, float *mean, hipStream_t stream) {
   const char *fn = "oq_quant_act_gsum";
   int rc = check_x(fn, x, M, d, ldx);
   if (rc) return rc;
@@ -778,7 +778,7 @@ int oq_quant_act_gsum(const uint16_t *x, int64_t M, int32_t d, int64_t ldx, cons
                     fn);
 }
 
-int oq_gemm_w4a4_asym(int afmt, const uint8_t *qa, const float *a_scale, const float *gsum, int64_t M, int32_t K,
+int oq_gemm_w4a4_asym(int afmt, const uint8_t *qa, const float *a_scale, const uint32_t *gsum, int64_t M, int32_t K,
                       const uint8_t *w_tiled, const float *w_scale_t, const uint32_t *corr, int32_t N, const float *mean,
                       const float *w1, const float *bias, uint16_t *y, int64_t ldy, hipStream_t stream) {
   const char *fn = "oq_gemm_w4a4_asym";

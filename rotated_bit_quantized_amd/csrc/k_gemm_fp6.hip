@@ -533,7 +533,7 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, int64_t a_plane_bytes, const f
                    int K,
                    const uint8_t *__restrict__ W, const float *__restrict__ wst, int N, int Np,
                    const float *__restrict__ mean, const float *__restrict__ w1, const float *__restrict__ bias,
-                   uint16_t *__restrict__ y, int64_t ldy, const float *__restrict__ gsum,
+                   uint16_t *__restrict__ y, int64_t ldy, const uint32_t *__restrict__ gsum,
                    const uint2 *__restrict__ corr) {
   using V2 = V2C<NSLOT, TI, TJ, WAVES, PLANES>;
   static_assert(PLANES == 1 || !ASYM, "asymmetric weights take single-plane activations");
@@ -750,34 +750,31 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, int64_t a_plane_bytes, const f
   if constexpr (ASYM) {
     // F -= sum_g C[o][g] p[t][g], after the main loop (its registers are free
     // then): depth 8 G in bfloat16, slot 8 g + s holds piece s / 3 of p (p1 =
-    // p with its low three bits cleared, p2 = those bits: both exact in
-    // bfloat16 for |p| < 2048) against piece s % 3 of -C (the truncation
-    // split C = c1 + c2 + c3, each exactly a bfloat16); slots 6 and 7 are
-    // zero.  Lanes 0-31 take group 2 ch, lanes 32-63 group 2 ch + 1.  p and C
-    // are stored group-major, so the 32 rows (columns) of a fragment are one
-    // contiguous 128-byte read; the next pair of groups is loaded under the
-    // MFMAs of the current one.
+    // 8 floor(p / 8) and p2 = p - p1, exact bfloat16 for |p| < 2048, stored
+    // as one word by the activation writer) against piece s % 3 of -C (the
+    // truncation split C = c1 + c2 + c3 stored by the prepack); slots 6 and
+    // 7 are zero.  Lanes 0-31 take group 2 ch, lanes 32-63 group 2 ch + 1.
+    // p and C are stored group-major, so the 32 rows (columns) of a fragment
+    // are one contiguous read; a ring of PF steps is loaded ahead of the
+    // MFMAs.  Every product is exact in float32.
     const int Gq = K / 64;
-    const int r0 = lane & 31, hf = lane >> 5;
     int prow[TI], ccol[TJ];
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
-      const int64_t rr = m0 + wm * 32 * TI + 32 * i + r0;
+      const int64_t rr = m0 + wm * 32 * TI + 32 * i + r;
       prow[i] = (int)(rr < M ? rr : M - 1);
     }
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
-      const int cc = n0 + wn * 32 * TJ + 32 * j + r0;
+      const int cc = n0 + wn * 32 * TJ + 32 * j + r;
       ccol[j] = cc < Np ? cc : Np - 1;
     }
     const int nch = (Gq + 1) / 2;
-    // a ring of PF prefetched steps: the loads of step ch + PF - 1 are issued
-    // before the MFMAs of step ch
     constexpr int PF = 4;
-    float pn[PF][TI];
+    uint32_t pn[PF][TI];
     uint2 cn[PF][TJ];
-    auto fetch = [&](float (&pd)[TI], uint2 (&cd)[TJ], int ch) {
-      const int g = 2 * ch + hf;
+    auto fetch = [&](uint32_t (&pd)[TI], uint2 (&cd)[TJ], int ch) {
+      const int g = 2 * ch + half;
       const bool gv = ch < nch && g < Gq;
       const int gg = gv ? g : Gq - 1;
 #pragma unroll
@@ -786,20 +783,17 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, int64_t a_plane_bytes, const f
       for (int j = 0; j < TJ; ++j) cd[j] = corr[(int64_t)gg * Np + ccol[j]];
       if (!gv) {
 #pragma unroll
-        for (int i = 0; i < TI; ++i) pd[i] = 0.f;
+        for (int i = 0; i < TI; ++i) pd[i] = 0u;
 #pragma unroll
         for (int j = 0; j < TJ; ++j) cd[j] = make_uint2(0u, 0u);
       }
     };
-    auto step = [&](const float (&pc)[TI], const uint2 (&cc2)[TJ]) {
+    auto step = [&](const uint32_t (&pc)[TI], const uint2 (&cc2)[TJ]) {
       uint4 av[TI], bv[TJ];
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
-        // p1 = 8 floor(p / 8), p2 = p - p1, both exact (p is an integer below 2^11)
-        const float p1 = __builtin_floorf(pc[i] * 0.125f) * 8.0f;
-        const uint32_t b1 = __float_as_uint(p1), b2 = __float_as_uint(pc[i] - p1);
-        av[i] = make_uint4(__builtin_amdgcn_perm(b1, b1, 0x07060302u), __builtin_amdgcn_perm(b2, b1, 0x07060302u),
-                           __builtin_amdgcn_perm(b2, b2, 0x07060302u), 0u);
+        const uint32_t w = pc[i];  // p1 | p2 << 16
+        av[i] = make_uint4(__builtin_amdgcn_perm(w, w, 0x01000100u), w, __builtin_amdgcn_perm(w, w, 0x03020302u), 0u);
       }
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
@@ -908,7 +902,7 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, int64_t a_plane_bytes, const f
 template <int NSLOT, bool PAIRED, bool ASYM, int TI, int TJ, int WAVES, bool EXTRA, int PLANES>
 hipError_t launch_v2_kernel(const uint8_t *A, int64_t plane, const float *a_scale, int64_t M, int K,
                             const uint8_t *W, const float *wst, int N, int Np, const float *mean, const float *w1,
-                            const float *bias, uint16_t *y, int64_t ldy, hipStream_t stream, const float *gsum,
+                            const float *bias, uint16_t *y, int64_t ldy, hipStream_t stream, const uint32_t *gsum,
                             const uint32_t *corr) {
   using V2 = V2C<NSLOT, TI, TJ, WAVES, PLANES>;
   auto kern = gemm_fp6_v2_kernel<NSLOT, PAIRED, ASYM, TI, TJ, WAVES, EXTRA, PLANES>;
@@ -929,7 +923,7 @@ hipError_t launch_v2_kernel(const uint8_t *A, int64_t plane, const float *a_scal
 template <int NSLOT, bool PAIRED, bool ASYM, int TI, int TJ, int WAVES, int PLANES = 1>
 hipError_t launch_v2_shape(const uint8_t *A, int64_t plane, const float *a_scale, int64_t M, int K,
                            const uint8_t *W, const float *wst, int N, int Np, const float *mean, const float *w1,
-                           const float *bias, uint16_t *y, int64_t ldy, hipStream_t stream, const float *gsum,
+                           const float *bias, uint16_t *y, int64_t ldy, hipStream_t stream, const uint32_t *gsum,
                            const uint32_t *corr) {
   if (mean || bias)
     return launch_v2_kernel<NSLOT, PAIRED, ASYM, TI, TJ, WAVES, true, PLANES>(A, plane, a_scale, M, K, W, wst, N, Np,
@@ -983,21 +977,19 @@ Shape pick_shape(int64_t M, int N) {
 template <int NSLOT, bool PAIRED, bool ASYM>
 hipError_t launch_v2(const uint8_t *A, const float *a_scale, int64_t M, int K, const uint8_t *W, const float *wst,
                      int N, int Np, const float *mean, const float *w1, const float *bias, uint16_t *y, int64_t ldy,
-                     hipStream_t stream, const float *gsum = nullptr, const uint32_t *corr = nullptr) {
-  switch (pick_shape(M, N)) {
-    case Shape::W8_256x192:
-      return launch_v2_shape<NSLOT, PAIRED, ASYM, 2, 3, 8>(A, 0, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy,
-                                                           stream, gsum, corr);
-    case Shape::W4_256x128:
-      return launch_v2_shape<NSLOT, PAIRED, ASYM, 4, 2, 4>(A, 0, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy,
-                                                           stream, gsum, corr);
-    case Shape::W4_128x192:
-      return launch_v2_shape<NSLOT, PAIRED, ASYM, 2, 3, 4>(A, 0, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy,
-                                                           stream, gsum, corr);
-    default:
-      return launch_v2_shape<NSLOT, PAIRED, ASYM, 4, 2, 8>(A, 0, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy,
-                                                           stream, gsum, corr);
-  }
+                     hipStream_t stream, const uint32_t *gsum = nullptr, const uint32_t *corr = nullptr) {
+  const Shape sh = pick_shape(M, N);
+  if (sh == Shape::W8_256x192)
+    return launch_v2_shape<NSLOT, PAIRED, ASYM, 2, 3, 8>(A, 0, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy,
+                                                         stream, gsum, corr);
+  if (sh == Shape::W4_256x128)
+    return launch_v2_shape<NSLOT, PAIRED, ASYM, 4, 2, 4>(A, 0, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy,
+                                                         stream, gsum, corr);
+  if (sh == Shape::W4_128x192)
+    return launch_v2_shape<NSLOT, PAIRED, ASYM, 2, 3, 4>(A, 0, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy,
+                                                         stream, gsum, corr);
+  return launch_v2_shape<NSLOT, PAIRED, ASYM, 4, 2, 8>(A, 0, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy,
+                                                       stream, gsum, corr);
 }
 
 }  // namespace
@@ -1022,7 +1014,7 @@ hipError_t launch_gemm_fp6(const uint8_t *A, int planes, const float *a_scale, i
   return launch_cfg<2, 4, 1, FP6_STAGES>(A, plane, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy, stream);
 }
 
-hipError_t launch_gemm_fp6_asym(const uint8_t *A, const float *a_scale, const float *gsum, int64_t M, int K,
+hipError_t launch_gemm_fp6_asym(const uint8_t *A, const float *a_scale, const uint32_t *gsum, int64_t M, int K,
                                 const uint8_t *W, const float *wst, const uint32_t *corr, int N, const float *mean,
                                 const float *w1, const float *bias, uint16_t *y, int64_t ldy, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;

@@ -459,7 +459,7 @@ hipError_t launch_weight_rpbh_asym(const float *w, int N, int K, int64_t ldw, co
 hipError_t launch_rpbh_quant(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotArgs &rot,
                              int center, float *mean, int out_mode, int qmax, void *out,
                              int64_t ld_out_bytes, float *scale, hipStream_t stream, const PctlArgs *pctl,
-                             const LmArgs *lm, float *gsum) {
+                             const LmArgs *lm, uint32_t *gsum) {
   if (M == 0) return hipSuccess;
   if (rot.kron_m) {
     // the Kronecker rotation runs at the padded width: on the wave kernel for

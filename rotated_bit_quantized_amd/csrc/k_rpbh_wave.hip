@@ -281,6 +281,14 @@ __device__ __forceinline__ void kron_paley(float (&v)[SLOTS][16], float *bf, int
   }
 }
 
+// A group sum p of integer codes (|p| < 2048) as the word the corrected GEMM
+// reads: bfloat16 p1 = 8 floor(p / 8) in bits 0-15 and p2 = p - p1 in bits
+// 16-31, both exact.
+__device__ __forceinline__ uint32_t gsum_pieces(float p) {
+  const float p1 = __builtin_floorf(p * 0.125f) * 8.0f;
+  return (__float_as_uint(p1) >> 16) | (__float_as_uint(p - p1) & 0xFFFF0000u);
+}
+
 // LDS: [offset table: ROUNDS x SLOTS x 4 x 64 lanes x 4 ints][per wave: row copies]
 // [Lloyd-Max modes: 128 float positive thresholds, 256 float16 levels, when
 // they fit in the 160 KiB; otherwise the kernel reads them from global memory]
@@ -305,7 +313,7 @@ __global__ void __launch_bounds__(64 * WAVES_PER_WG)
 rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, const int32_t *__restrict__ perm,
                  const int8_t *__restrict__ signs, int h, float c_h, int pow4, int center,
                  float *__restrict__ mean_out, int qmax, void *__restrict__ out, int64_t ld_out_bytes,
-                 float *__restrict__ scale_out, PctlArgs pa, LmArgs la, float *__restrict__ gsum_out, int din) {
+                 float *__restrict__ scale_out, PctlArgs pa, LmArgs la, uint32_t *__restrict__ gsum_out, int din) {
   static_assert(KM == 0 || (ROUNDS == 0 && !PCTL && !is_lm_mode<mode>()), "factorised rotation: plain absmax modes");
   constexpr bool LM = is_lm_mode<mode>();
   using L = WaveLds<SLOTS, ROUNDS, LM>;
@@ -748,9 +756,9 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
           pa0 += xlane(pa0, 1);
           pb0 += xlane(pb0, 0);
           pb0 += xlane(pb0, 1);
-          if ((il & 3) == 0) {  // group-major [d / 64][M]
-            if (wa) gsum_out[(int64_t)((1024 * s0 + 16 * il) >> 6) * M + row] = pa0;
-            if (wb) gsum_out[(int64_t)((1024 * (s0 + 1) + 16 * il) >> 6) * M + row] = pb0;
+          if ((il & 3) == 0) {  // group-major [d / 64][M], as two bfloat16 pieces
+            if (wa) gsum_out[(int64_t)((1024 * s0 + 16 * il) >> 6) * M + row] = gsum_pieces(pa0);
+            if (wb) gsum_out[(int64_t)((1024 * (s0 + 1) + 16 * il) >> 6) * M + row] = gsum_pieces(pb0);
           }
         }
         if (mode == OUT_FP6) {
@@ -767,7 +775,7 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
 template <int SLOTS, int ROUNDS, int MODE, bool PCTL, int KM = 0>
 hipError_t launch_m(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotArgs &rot, int center, float *mean,
                     int qmax, void *out, int64_t ld_out_bytes, float *scale, const PctlArgs &pa, const LmArgs &la,
-                    float *gsum, hipStream_t stream, int din = 0) {
+                    uint32_t *gsum, hipStream_t stream, int din = 0) {
   using L = WaveLds<SLOTS, ROUNDS, is_lm_mode<MODE>()>;
   const size_t lds = (size_t)L::TOTAL;
   static bool attr_set = false;
@@ -792,7 +800,7 @@ hipError_t launch_m(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotA
 template <int SLOTS, int ROUNDS, int MODE>
 hipError_t launch_p(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotArgs &rot, int center, float *mean,
                     int qmax, void *out, int64_t ld_out_bytes, float *scale, const PctlArgs *pctl, const LmArgs *lm,
-                    float *gsum, hipStream_t stream) {
+                    uint32_t *gsum, hipStream_t stream) {
   const PctlArgs no_p{0, 0.0, 0.0, 1.0};
   if (gsum && MODE != OUT_FP6 && MODE != OUT_FP6X2) return hipErrorInvalidValue;
   const LmArgs no_lm{1, nullptr, nullptr};
@@ -815,7 +823,7 @@ hipError_t launch_p(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotA
 template <int SLOTS, int ROUNDS>
 hipError_t launch_w(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotArgs &rot, int center, float *mean,
                     int mode, int qmax, void *out, int64_t ld_out_bytes, float *scale, const PctlArgs *pctl,
-                    const LmArgs *lm, float *gsum, hipStream_t stream) {
+                    const LmArgs *lm, uint32_t *gsum, hipStream_t stream) {
 #define OQ_MODE_CASE(MD) \
   case MD: return launch_p<SLOTS, ROUNDS, MD>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, pctl, lm, gsum, stream);
   switch (mode) {
@@ -835,7 +843,7 @@ hipError_t launch_w(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotA
 template <int SLOTS>
 hipError_t launch_r(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotArgs &rot, int center, float *mean,
                     int mode, int qmax, void *out, int64_t ld_out_bytes, float *scale, const PctlArgs *pctl,
-                    const LmArgs *lm, float *gsum, hipStream_t stream) {
+                    const LmArgs *lm, uint32_t *gsum, hipStream_t stream) {
   switch (rot.rounds) {
     case 0: return launch_w<SLOTS, 0>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, pctl, lm, gsum, stream);
     case 1: return launch_w<SLOTS, 1>(x, M, d, ldx, rot, center, mean, mode, qmax, out, ld_out_bytes, scale, pctl, lm, gsum, stream);
@@ -901,7 +909,7 @@ bool rpbh_wave_supported(int d) { return d >= 16 && d <= 4096 && d % 16 == 0; }
 
 hipError_t launch_rpbh_wave(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotArgs &rot, int center,
                             float *mean, int mode, int qmax, void *out, int64_t ld_out_bytes, float *scale,
-                            hipStream_t stream, const PctlArgs *pctl, const LmArgs *lm, float *gsum) {
+                            hipStream_t stream, const PctlArgs *pctl, const LmArgs *lm, uint32_t *gsum) {
   if (M == 0) return hipSuccess;
   if (pctl && (pctl->rank < 2 || pctl->rank > 4)) return hipErrorInvalidValue;
   if (lm && (lm->bits < 1 || lm->bits > 8 || (mode == OUT_LM4 && lm->bits > 4))) return hipErrorInvalidValue;

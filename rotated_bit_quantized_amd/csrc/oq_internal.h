@@ -159,13 +159,14 @@ struct LmArgs {
 // K1: (center) -> RPBH rounds -> (quantize) per token row; pctl selects the
 // percentile range instead of absmax (integer outputs, rows the wave kernel
 // takes only); the OUT_LM* modes take their codebook from lm (wave kernel
-// only); gsum (tiled FP6 modes, wave kernel only), if set, receives the sums
-// of the codes of every 64-wide group, float32 group-major [d/64][M].
+// only); gsum (tiled FP6 modes, wave kernel only), if set, receives the sum p
+// of the codes of every 64-wide group, group-major [d/64][M], as one word of
+// two bfloat16 pieces (8 floor(p / 8) in bits 0-15, the rest in bits 16-31).
 hipError_t launch_rpbh_quant(const uint16_t *x, int64_t M, int d, int64_t ldx,
                              const RotArgs &rot, int center, float *mean,
                              int out_mode, int qmax, void *out, int64_t ld_out_bytes,
                              float *scale, hipStream_t stream, const PctlArgs *pctl = nullptr,
-                             const LmArgs *lm = nullptr, float *gsum = nullptr);
+                             const LmArgs *lm = nullptr, uint32_t *gsum = nullptr);
 
 // K1, one wavefront per row (activation rows of width d <= 4096).
 bool rpbh_wave_supported(int d);
@@ -180,7 +181,7 @@ hipError_t launch_rpbh_wave_kron(const uint16_t *x, int64_t M, int din, int64_t 
 hipError_t launch_rpbh_wave(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotArgs &rot, int center,
                             float *mean, int mode, int qmax, void *out, int64_t ld_out_bytes, float *scale,
                             hipStream_t stream, const PctlArgs *pctl = nullptr, const LmArgs *lm = nullptr,
-                            float *gsum = nullptr);
+                            uint32_t *gsum = nullptr);
 
 // K2: dense per-32 transform -> (MXFP4 quantize | float32 out); mx_out: 0 float32,
 // 1 row-major codes + E8M0, 2 tiled MXFP4 layout.
@@ -204,7 +205,7 @@ hipError_t launch_prepack_w4(const uint8_t *w, const float *ws, int N, int K, ui
                              hipStream_t stream);
 // Tiled A4 x asymmetric INT4 weights (codes q'/2 with weight scale 2^1), with
 // F initialised to -sum_g corr[o][g] gsum[t][g] (single plane, group 64)
-hipError_t launch_gemm_fp6_asym(const uint8_t *A, const float *a_scale, const float *gsum, int64_t M, int K,
+hipError_t launch_gemm_fp6_asym(const uint8_t *A, const float *a_scale, const uint32_t *gsum, int64_t M, int K,
                                 const uint8_t *W, const float *wst, const uint32_t *corr, int N, const float *mean,
                                 const float *w1, const float *bias, uint16_t *y, int64_t ldy, hipStream_t stream);
 // canonical asymmetric codes + bfloat16 sigma, z -> tiled q'/2, sigma [G][Np],

@@ -49,6 +49,23 @@ def _bits(a):
     return (np.asarray(a, np.float32).view(np.uint32) >> 16).astype(np.uint16)
 
 
+def _gsum_words(p):
+    """Group sums as the GEMM's operand words: bfloat16 8 floor(p / 8) in
+    bits 0-15 and p - 8 floor(p / 8) in bits 16-31 (both exact)."""
+    p = np.asarray(p, np.int64)
+    p1 = (np.floor(p / 8) * 8).astype(np.float32)
+    p2 = (p - p1.astype(np.int64)).astype(np.float32)
+    return ((p1.view(np.uint32) >> 16) | (p2.view(np.uint32) & 0xFFFF0000)).astype(np.uint32).view(np.int32)
+
+
+def _gsum_values(words):
+    """The group sums a word array holds (the sum of its two bfloat16 pieces)."""
+    w = np.asarray(words).view(np.uint32)
+    lo = (w << 16).view(np.float32).astype(np.float64)
+    hi = (w & 0xFFFF0000).view(np.float32).astype(np.float64)
+    return lo + hi
+
+
 def _weights(N, K, seed):
     rng = np.random.default_rng(seed)
     W = rng.standard_normal((N, K)) * 0.02 + rng.uniform(-0.01, 0.03, (N, 1))
@@ -135,7 +152,10 @@ def test_act_group_sums(oq, M, K, h, rounds, center, pctl):
     live = row_mask(M, K)
     np.testing.assert_array_equal(to_host(out["codes"])[live], to_host(plain["codes"])[live])
     np.testing.assert_array_equal(to_host(out["scale"]), to_host(canon["scale"]))
-    np.testing.assert_array_equal(to_host(out["gsum"]), OA.group_sums(codes, 64).astype(np.float32).T)
+    ref_p = OA.group_sums(codes, 64).T
+    got = to_host(out["gsum"])
+    np.testing.assert_array_equal(_gsum_values(got), ref_p.astype(np.float64))
+    np.testing.assert_array_equal(got.view(np.uint32), _gsum_words(ref_p).view(np.uint32))
 
 
 GEMM_CASES = [(300, 1024, 520, True, True), (257, 512, 256, False, False), (33, 128, 40, False, True),
@@ -157,7 +177,7 @@ def test_gemm_asym(oq, M, K, N, center, bias):
     w1 = rng.standard_normal(N).astype(np.float32) if center else None
     b = rng.standard_normal(N).astype(np.float32) if bias else None
     w = oq.oq_prepack_w4_asym(to_dev(OQ.pack_int4(Q - 8)), to_dev(_bits(sig)), to_dev(_bits(z)), N, K, 64)
-    gs = np.ascontiguousarray(OA.group_sums(qa, 64).astype(np.float32).T)
+    gs = np.ascontiguousarray(_gsum_words(OA.group_sums(qa, 64).T))
     dev = lambda a: None if a is None else to_dev(a)  # noqa: E731
     y = oq.oq_gemm_w4a4_asym(to_dev(tile(qa)), to_dev(alpha), to_dev(gs), w, N, M, K, mean=dev(mean), w1=dev(w1),
                              bias=dev(b))
@@ -168,9 +188,10 @@ def test_gemm_asym(oq, M, K, N, center, bias):
 
 
 @pytest.mark.parametrize("shape", ["256x256", "256x192", "256x128", "128x192"])
-@pytest.mark.parametrize("M,K,N", [(300, 1024, 520), (257, 512, 1000)])
+@pytest.mark.parametrize("M,K,N", [(300, 1024, 520), (257, 512, 1000), (64, 192, 96)])
 def test_gemm_asym_shapes(oq, monkeypatch, shape, M, K, N):
-    """Every workgroup shape of the corrected GEMM, forced through OQ_FP6_TILE."""
+    """Every workgroup shape of the corrected GEMM, forced through OQ_FP6_TILE;
+    K = 192 leaves the last pair of groups with one group."""
     say("case gemm asym shape", shape, M, K, N)
     monkeypatch.setenv("OQ_FP6_TILE", shape)
     rng = np.random.default_rng(M + 3 * N + K)
@@ -182,7 +203,7 @@ def test_gemm_asym_shapes(oq, monkeypatch, shape, M, K, N):
     z = OA.bf16_rne(rng.uniform(-1.0, 16.0, (N, G)).astype(np.float32))
     b = rng.standard_normal(N).astype(np.float32)
     w = oq.oq_prepack_w4_asym(to_dev(OQ.pack_int4(Q - 8)), to_dev(_bits(sig)), to_dev(_bits(z)), N, K, 64)
-    gs = np.ascontiguousarray(OA.group_sums(qa, 64).astype(np.float32).T)
+    gs = np.ascontiguousarray(_gsum_words(OA.group_sums(qa, 64).T))
     y = oq.oq_gemm_w4a4_asym(to_dev(tile(qa)), to_dev(alpha), to_dev(gs), w, N, M, K, bias=to_dev(b))
     torch.cuda.synchronize()
     y_ref, S = OA.linear_asym(alpha, qa, Q, sig, OA.correction(sig, z), 64, bias=b)
@@ -212,7 +233,8 @@ def test_asym_layer_full_size(oq):
     codes = OQ.unpack_int4(to_host(canon["codes"]).view(np.uint8))[rows]
     ref = OL.activations_int(wl.x_bits[rows], wl.perm, wl.signs, wl.spec.block, 4, False)
     check_codes(codes, ref["codes"], ref["flags"], "full-size codes")
-    np.testing.assert_array_equal(to_host(act["gsum"])[:, rows], OA.group_sums(codes, 64).astype(np.float32).T)
+    np.testing.assert_array_equal(_gsum_values(to_host(act["gsum"])[:, rows]),
+                                  OA.group_sums(codes, 64).T.astype(np.float64))
     alpha = to_host(act["scale"])[rows]
     y_ref, S = OA.linear_asym(alpha, codes, qw, sig, OA.correction(sig, z), 64)
     frac = check_output(to_host(y)[rows], y_ref, S, 7 * (K // 64), "asym full-size output")
