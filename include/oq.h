@@ -239,7 +239,10 @@ int oq_gemm_w4a8(const int8_t *qa, int64_t lda, const float *a_scale, int64_t M,
  *   afmt OQ_A4 | OQ_TILED or OQ_A6 | OQ_TILED: qa in the tiled layout (from
  *     oq_quant_act with the same afmt; lda_bytes ignored), w and w_scale
  *     from oq_prepack_w4, group 64; output bit-identical to the canonical
- *     path on the same codes.
+ *     path on the same codes.  The library picks the workgroup shape from
+ *     M, N and the CU count; the environment variable OQ_FP6_TILE (256x256,
+ *     256x192, 256x128 or 128x192; OQ_A4 only) forces one, for tuning.  The
+ *     result does not depend on the shape.
  *   afmt OQ_MXFP4: qa E2M1 nibbles, a_scale uint8 E8M0 [M][K/32]; w E2M1
  *     nibbles [N][K/2], w_scale uint8 E8M0 [N][K/32]; group must be 32;
  *     y = bf16_RNE( sum_blocks 2^(ea+ew) sum_k fp4(a) fp4(w) + bias[o] );
@@ -362,6 +365,9 @@ int oq_prepack_w16(const uint8_t *w, const float *w_scale, int32_t N, int32_t K,
  *   ws, which needs oq_workspace_bytes(OQ_OP_GEMM_LM, M, K, N, 0) bytes.
  * w16_tiled from oq_prepack_w16; a_scale float32 [M]; mean and w1 both NULL
  * or both set; bias nullable; y bf16 [M][ldy].  K % 32 == 0.
+ * The workgroup shape (256 x 256 or 256 x 192 outputs) follows M, N and the
+ * CU count; OQ_F16_TILE=256x256 or 256x192 in the environment forces one.
+ * The result does not depend on the shape.
  */
 int oq_gemm_lm(int32_t bits, int tiled, const void *qa, int64_t lda_bytes, const float *a_scale, int64_t M,
                int32_t K, const uint16_t *levels_f16, const uint16_t *w16_tiled, int32_t N, const float *mean,
