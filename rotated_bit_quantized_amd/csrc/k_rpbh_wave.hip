@@ -50,6 +50,8 @@
 //     float above |u|, so that a tie goes to the lower level).
 #include "oq_internal.h"
 
+#include <type_traits>
+
 #pragma clang fp contract(off)
 
 namespace oq {
@@ -139,16 +141,26 @@ __device__ __forceinline__ void fwht_row(float (&v)[SLOTS][16], int n, const flo
   if (n > 3)
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s) dpp_stage<3>(v[s], c[3]);
+  // distances 16 and 32 go through the LDS crossbar: a slot's 16 exchanges
+  // are issued before its accumulates, so that their latencies overlap
   if (n > 4)
 #pragma unroll
-    for (int s = 0; s < SLOTS; ++s)
+    for (int s = 0; s < SLOTS; ++s) {
+      float p[16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) v[s][j] = __builtin_fmaf(xlane(v[s][j], 4), c[4], v[s][j]);
+      for (int j = 0; j < 16; ++j) p[j] = xlane(v[s][j], 4);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[s][j] = __builtin_fmaf(p[j], c[4], v[s][j]);
+    }
   if (n > 5)
 #pragma unroll
-    for (int s = 0; s < SLOTS; ++s)
+    for (int s = 0; s < SLOTS; ++s) {
+      float p[16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) v[s][j] = __builtin_fmaf(xlane(v[s][j], 5), c[5], v[s][j]);
+      for (int j = 0; j < 16; ++j) p[j] = xlane(v[s][j], 5);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[s][j] = __builtin_fmaf(p[j], c[5], v[s][j]);
+    }
 }
 
 // Stores the 16 codes of two slots (a: coordinates base..base+15, b: the same
@@ -469,21 +481,32 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
       // centering: s x - s m = s RN32(x - m), one rounding.  Lanes past the
       // row end read word 0: their blocks are never stored and are left out
       // of the range
+      // (the centring test is hoisted out of the element loop: without it
+      // the gather is a read and a shift per element)
+      auto gather = [&](auto cc) {
+        constexpr bool CEN = decltype(cc)::value;
 #pragma unroll
-      for (int s = 0; s < SLOTS; ++s) {
-        const int4 *tb = reinterpret_cast<const int4 *>(table) + (s * 4) * 64 + lane;
+        for (int s = 0; s < SLOTS; ++s) {
+          const int4 *tb = reinterpret_cast<const int4 *>(table) + (s * 4) * 64 + lane;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int4 o4 = tb[k * 64];
-          const int oo[4] = {o4.x, o4.y, o4.z, o4.w};
+          for (int k = 0; k < 4; ++k) {
+            const int4 o4 = tb[k * 64];
+            const int oo[4] = {o4.x, o4.y, o4.z, o4.w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float g = __uint_as_float((uint32_t)(*reinterpret_cast<const uint16_t *>(buf + oo[e])) << 16);
-            const float mm = oo[e] >= neg_from ? -m : m;
-            v[s][4 * k + e] = center ? g - mm : g;
+            for (int e = 0; e < 4; ++e) {
+              const float g = __uint_as_float((uint32_t)(*reinterpret_cast<const uint16_t *>(buf + oo[e])) << 16);
+              if constexpr (CEN) {
+                const float mm = oo[e] >= neg_from ? -m : m;
+                v[s][4 * k + e] = g - mm;
+              } else {
+                v[s][4 * k + e] = g;
+              }
+            }
           }
         }
-      }
+      };
+      if (center) gather(std::true_type{});
+      else gather(std::false_type{});
       fwht_row<SLOTS>(v, nlog, cst);
       if (!pow4) {
 #pragma unroll
