@@ -1,6 +1,7 @@
 """Offline weight preparation and the whole rotated low-bit linear forward pass.
 
-Parity pins: tests/test_oracle_linear.py.
+Parity pins: tests/test_oracle_gemm.py (the forward pass, w_1, the offset
+invariance) and tests/test_oracle_rotation.py (the weight-side transform).
 
 Sources:
   CentriQ Sec. 3 "Hadamard rotation" (W x = (W H^T)(H x): the rotation is
@@ -37,10 +38,12 @@ def prepare_weight_rpbh(W, perm, signs, block, group):
             "packed": quant.pack_int4(q), "w1": row_sums_fp32(W)}
 
 
-def prepare_weight_dense32(W, t_wgt):
-    """w'_b = T_w,b w_b per 32-block (T_w the inverse-transpose of the
-    activation transform), rounded once to float32, then MXFP4."""
-    wr = rotation.dense32_fp64(np.asarray(W, dtype=np.float32), t_wgt).astype(np.float32)
+def prepare_weight_dense32(W, t_act_bits):
+    """w'_b = T_w,b w_b per 32-block with T_w,b = T_b^{-T} formed here from the
+    stored bfloat16 activation transforms (WUSH review, "Core claim"), in
+    float64 and rounded once to float32, then MXFP4."""
+    t_w = rotation.dense32_weight_transform(t_act_bits)
+    wr = rotation.dense32_fp64(np.asarray(W, dtype=np.float32), t_w).astype(np.float32)
     codes, sb, eflag, bflag = quant.quant_mx(wr)
     return {"rotated": wr, "codes": codes, "scale_bytes": sb, "flags": eflag,
             "block_flags": bflag, "packed": quant.pack_nibbles(codes)}
@@ -63,10 +66,10 @@ def activations_int(x_bits, perm, signs, block, afmt_bits, center, pctl=False):
 def activations_mx(x_bits, t_act_bits):
     x32 = quant.bf16_to_f32(x_bits)
     T = quant.bf16_to_f32(t_act_bits)
-    v = rotation.dense32_fp32(x32, T)
+    v, n_int = rotation.dense32_fp32(x32, T)
     codes, sb, eflag, bflag = quant.quant_mx(v)
     return {"rotated": v, "codes": codes, "scale_bytes": sb, "flags": eflag,
-            "block_flags": bflag, "packed": quant.pack_nibbles(codes)}
+            "block_flags": bflag, "packed": quant.pack_nibbles(codes), "exact_int_sums": n_int}
 
 
 def linear_int(act, wprep, group, bias=None):

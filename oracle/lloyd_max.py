@@ -176,19 +176,6 @@ def rms_scale(v32: np.ndarray) -> np.ndarray:
     return np.maximum(rms_f64(v32).astype(np.float32), EPS32)
 
 
-def rms_near_midpoint(v32: np.ndarray) -> np.ndarray:
-    """Tokens whose float64 RMS lies within 1e-12 (relative) of a float32
-    rounding midpoint: a sum of squares taken in another (equally valid)
-    float64 order may round rho to the neighbouring float32 there."""
-    r = rms_f64(v32)
-    f = r.astype(np.float32)
-    up = np.nextafter(f, np.float32(np.inf)).astype(np.float64)
-    dn = np.nextafter(f, np.float32(-np.inf)).astype(np.float64)
-    f = f.astype(np.float64)
-    gap = np.minimum(np.abs(0.5 * (f + up) - r), np.abs(0.5 * (f + dn) - r))
-    return gap <= 1e-12 * np.abs(r)
-
-
 def boundary_flags(v32: np.ndarray, rho: np.ndarray, thr32: np.ndarray) -> np.ndarray:
     """Elements whose u = RN32(v RN32(1 / rho)) lies within 1e-6 (relative)
     of a decision threshold (the rounding-boundary exemption)."""

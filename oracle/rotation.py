@@ -21,6 +21,8 @@ B_h.  Two rounds compose as R = R_2 R_1.
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
 from .hadamard import block_hadamard_fp64, fwht_fp32_canonical, sylvester
@@ -67,8 +69,83 @@ def dense32_fp64(x: np.ndarray, T: np.ndarray) -> np.ndarray:
     return v.reshape(x.shape)
 
 
-def dense32_fp32(x: np.ndarray, T: np.ndarray) -> np.ndarray:
-    """The per-block transform rounded once to float32.  With bfloat16 T and
-    bfloat16 x every product has at most 16 significant bits and a 32-term sum
-    is exact in float64, so this is the correctly rounded value."""
-    return dense32_fp64(x, T).astype(np.float32)
+def dense32_weight_transform(t_bits: np.ndarray) -> np.ndarray:
+    """Weight side of the per-block pair (WUSH review, "Core claim": the
+    weights take the inverse-transpose of the activation transform,
+    T_w = T_x^{-T}), formed in float64 from the stored bfloat16 matrices:
+    returns float64 [nb][32][32] with T_w,b = (T_b^{-1})^T."""
+    T = (np.asarray(t_bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return np.transpose(np.linalg.inv(T), (0, 2, 1))
+
+
+def _exponent(a: np.ndarray) -> np.ndarray:
+    """floor(log2 |a|) of the nonzero entries (float64 array), NaN at zeros."""
+    a = np.abs(np.asarray(a, dtype=np.float64))
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, np.nan)))
+    return e
+
+
+def _rn32_scaled_int(n: int, e: int) -> np.float32:
+    """RN32 (ties to even) of the exact value n * 2^e (Python integers)."""
+    if n == 0:
+        return np.float32(0.0)
+    sign = -1 if n < 0 else 1
+    n = abs(n)
+    lsb = max(n.bit_length() + e - 24, -149)   # weight of the last kept bit
+    shift = lsb - e
+    if shift > 0:
+        q, r = divmod(n, 1 << shift)
+        half = 1 << (shift - 1)
+        if r > half or (r == half and (q & 1)):
+            q += 1
+    else:
+        q = n << (-shift)
+    return np.float32(sign * math.ldexp(q, lsb))
+
+
+def _bf16_parts(a: float):
+    """(integer mantissa, exponent) with a = m * 2^e exactly (a float)."""
+    m, e = math.frexp(a)
+    return int(m * (1 << 53)), e - 53
+
+
+def dense32_fp32(x32: np.ndarray, T: np.ndarray):
+    """v_b = T_b x_b per 32-block rounded once to float32: the exact sum of the
+    exact products, then RN32.
+
+    With bfloat16 T and x each product has at most 16 significant bits, so a
+    32-term float64 sum is exact whenever the exponents floor(log2 |T_ij x_j|)
+    of one output's nonzero products span at most 32 (every partial sum is then
+    a multiple of the smallest product's last bit below 2^53 of them).  That is
+    checked for every output; the rest are summed exactly in integers.  Returns
+    (v float32, number of outputs summed in integers)."""
+    x = np.asarray(x32, dtype=np.float64)
+    Tm = np.asarray(T, dtype=np.float64)
+    v = dense32_fp64(x, Tm).astype(np.float32)
+    d = x.shape[-1]
+    xr = x.reshape(-1, d // 32, 32)
+    vr = v.reshape(-1, d // 32, 32)
+    eT = _exponent(Tm)                                   # [nb, 32, 32]
+    ex = _exponent(xr)                                   # [rows, nb, 32]
+    # conservative span per (row, block, output): largest exponent sum minus
+    # smallest, each bounded separately
+    tmax, tmin = np.nanmax(eT, axis=-1, initial=-np.inf), np.nanmin(eT, axis=-1, initial=np.inf)
+    xmax, xmin = np.nanmax(ex, axis=-1, initial=-np.inf), np.nanmin(ex, axis=-1, initial=np.inf)
+    loose = (xmax[:, :, None] + tmax[None]) - (xmin[:, :, None] + tmin[None])
+    suspect = np.argwhere(loose > 32)
+    exact_int = 0
+    for r, b in {(int(r), int(b)) for r, b, _ in suspect}:
+        span = ex[r, b][None, :] + eT[b]                 # [32 outputs, 32 terms]
+        hi = np.nanmax(span, axis=-1, initial=-np.inf)
+        lo = np.nanmin(span, axis=-1, initial=np.inf)
+        for i in np.nonzero(hi - lo > 32)[0]:
+            parts = [(_bf16_parts(float(Tm[b, i, j])), _bf16_parts(float(xr[r, b, j])))
+                     for j in range(32) if Tm[b, i, j] != 0 and xr[r, b, j] != 0]
+            if not parts:
+                continue
+            emin = min(pt[1] + px[1] for pt, px in parts)
+            n = sum(pt[0] * px[0] << (pt[1] + px[1] - emin) for pt, px in parts)
+            vr[r, b, i] = _rn32_scaled_int(n, emin)
+            exact_int += 1
+    return v, exact_int

@@ -120,12 +120,52 @@ def test_weight_prep_and_forward_small_config():
 def test_mx_forward_small_config():
     wl = WL.make_workload(5, M=8, K=256, Ns=(32,))
     act = L.activations_mx(wl.x_bits, wl.t_act_bits)
-    wp = L.prepare_weight_dense32(wl.weights[0], wl.t_wgt)
+    wp = L.prepare_weight_dense32(wl.weights[0], wl.t_act_bits)
     y, S = L.linear_mx(act, wp)
     ref = wl.x_f32.astype(np.float64) @ wl.weights[0].T.astype(np.float64)
     rel = np.linalg.norm(y - ref) / np.linalg.norm(ref)
     assert rel < 0.3
-    # the transform pair cancels exactly up to float32 rounding of T_w
+    # the transform pair cancels to float64 rounding
     T = Q.bf16_to_f32(wl.t_act_bits)
-    lhs = R.dense32_fp64(wl.weights[0], wl.t_wgt) @ R.dense32_fp64(wl.x_f32, T).T
-    np.testing.assert_allclose(lhs, ref.T, rtol=0, atol=1e-5 * np.abs(ref).max())
+    Tw = R.dense32_weight_transform(wl.t_act_bits)
+    lhs = R.dense32_fp64(wl.weights[0], Tw) @ R.dense32_fp64(wl.x_f32, T).T
+    np.testing.assert_allclose(lhs, ref.T, rtol=0, atol=1e-12 * np.abs(ref).max())
+
+
+def test_w1_golden_unrotated_row_sums():
+    # CentriQ Sec. 4.2 Eq. 4: w_1 = W 1 from the unrotated, unquantized weight
+    from conftest import read_golden
+    vals = {l.split()[0]: [float(t) for t in l.split()[1:]] for l in read_golden("w1_rowsum.txt")}
+    d = 32
+    W = np.stack([np.ones(d), np.arange(d) / 8.0]).astype(np.float32)
+    perm = np.arange(d, dtype=np.int32)[None]
+    signs = np.ones((1, d), dtype=np.int8)
+    wp = L.prepare_weight_rpbh(W, perm, signs, 32, 32)
+    np.testing.assert_array_equal(wp["w1"], np.array(vals["w1"], dtype=np.float32))
+    # the sum of the folded rows is the other (wrong) reading
+    np.testing.assert_allclose(wp["rotated"].astype(np.float64).sum(axis=1), vals["rotated_sum"], atol=1e-6)
+    assert np.all(np.abs(np.array(vals["rotated_sum"]) - np.array(vals["w1"])) > 1.0)
+
+
+def test_w1_is_the_correctly_rounded_exact_row_sum():
+    # Eq. 4 with the exact row sum rounded once to float32: compared with a
+    # rational-arithmetic sum of the unrotated float32 weight, rounded by
+    # locating it between its float32 neighbours
+    from fractions import Fraction
+    rng = np.random.default_rng(35)
+    d, h, N = 256, 128, 12
+    perm = np.stack([rng.permutation(d)]).astype(np.int32)
+    signs = np.where(rng.integers(0, 2, size=(1, d)) == 1, 1, -1).astype(np.int8)
+    W = (rng.standard_normal((N, d)) * 0.02 + rng.normal(0, 0.01, size=(N, 1))).astype(np.float32)
+    w1 = L.prepare_weight_rpbh(W, perm, signs, h, 64)["w1"]
+    for o in range(N):
+        exact = sum(Fraction(float(v)) for v in W[o])
+        f = w1[o]
+        lo = Fraction(float(np.nextafter(f, np.float32(-np.inf))))
+        hi = Fraction(float(np.nextafter(f, np.float32(np.inf))))
+        here = Fraction(float(f))
+        # f is the float32 nearest to the exact sum
+        assert abs(exact - here) <= abs(exact - lo) and abs(exact - here) <= abs(exact - hi)
+    # a w1 taken from the rotated weight is far off
+    wr = L.prepare_weight_rpbh(W, perm, signs, h, 64)["rotated"].astype(np.float64).sum(axis=1)
+    assert np.max(np.abs(wr - w1)) > 1e-3

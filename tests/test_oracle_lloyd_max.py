@@ -195,3 +195,21 @@ def test_linear_lm_against_loop():
             ref = float(rho[t]) * acc + float(mean[t]) * float(w1[o]) + float(b[o])
             assert abs(float(y[t, o]) - ref) <= 1e-6 * abs(ref) + 1e-12
             assert S[t, o] >= abs(ref) - 1e-9
+
+
+def test_rms_scale_rounds_the_exact_sum_once_then_to_float32():
+    # rho = RN32(sqrt(RN64(S) / d)) with S the exact sum of squares.  Tokens of
+    # d = 64 built so that rho sits at or next to the float32 midpoint
+    # 1 + 2^-24 between 1 and 1 + 2^-23 (all coordinates bfloat16 values):
+    #   A: 60 ones, 2, 2^-9, 2^-9, c = 2^-21: S = 64 + 2^-17 + 2^-42 =
+    #      64 (1 + 2^-24)^2 exactly, rho is the midpoint -> even -> 1;
+    #   B: c = 2^-21 (1 + 2^-7): S exceeds A's by 2^-48 + 2^-56, less than
+    #      half a float64 ulp at 64 (2^-47), so RN64(S) is A's S -> 1 (a sum
+    #      carried in more precision would round up);
+    #   C: c = 1.5 2^-21: S exceeds A's by 1.25 2^-42 -> 1 + 2^-23;
+    #   D: c = 1.5 2^-22: S is 0.4375 2^-42 below A's -> 1.
+    def tok(c):
+        return np.array([1.0] * 60 + [2.0, 2.0 ** -9, 2.0 ** -9, c], dtype=np.float32)
+    v = np.stack([tok(2.0 ** -21), tok(2.0 ** -21 * (1 + 2.0 ** -7)), tok(1.5 * 2.0 ** -21), tok(1.5 * 2.0 ** -22)])
+    up = np.float32(1.0 + 2.0 ** -23)
+    np.testing.assert_array_equal(LM.rms_scale(v), np.array([1.0, 1.0, up, 1.0], dtype=np.float32))

@@ -1,4 +1,6 @@
 """Pins of oracle/rotation.py (CPU only)."""
+import math
+
 import numpy as np
 import pytest
 
@@ -112,3 +114,61 @@ def test_dense32_transform_pair():
     v = R.dense32_fp64(e, T)
     np.testing.assert_array_equal(v[:32], 0)
     np.testing.assert_allclose(v[32:64], T[1][:, 8])
+
+
+def test_dense32_weight_transform_is_the_inverse_transpose():
+    # WUSH review "Core claim": T_w = T_x^{-T}.  Pinned by the pair identity
+    # (T_w w) . (T x) = w . x on the stored bfloat16 matrices, and by
+    # T_w^T T = I; the transform family is not orthogonal (diag(s) with s in
+    # [0.5, 2]), so an inverse without the transpose fails both.
+    import workloads as WL
+    wl = WL.make_workload(5, M=3, K=128, Ns=(4,))
+    T = WL.bf16_bits_to_f32(wl.t_act_bits).astype(np.float64)
+    Tw = R.dense32_weight_transform(wl.t_act_bits)
+    for b in range(T.shape[0]):
+        np.testing.assert_allclose(Tw[b].T @ T[b], np.eye(32), rtol=0, atol=1e-13)
+    x = wl.x_f32.astype(np.float64)
+    w = wl.weights[0].astype(np.float64)
+    lhs = R.dense32_fp64(w, Tw) @ R.dense32_fp64(x, T).T
+    np.testing.assert_allclose(lhs, w @ x.T, rtol=0, atol=1e-12 * np.abs(w @ x.T).max())
+    wrong = R.dense32_fp64(w, np.linalg.inv(T)) @ R.dense32_fp64(x, T).T
+    assert np.max(np.abs(wrong - w @ x.T)) > 1e-3 * np.abs(w @ x.T).max()
+
+
+def test_rn32_of_scaled_integers():
+    # the integer rounding helper against numpy's float64 -> float32
+    # conversion (round to nearest even) wherever the value is exact in float64
+    rng = np.random.default_rng(40)
+    for _ in range(2000):
+        n = int(rng.integers(-(1 << 52), 1 << 52))
+        e = int(rng.integers(-170, 60))
+        assert R._rn32_scaled_int(n, e) == np.float32(math.ldexp(n, e))
+    # ties: 1 + 2^-24 is halfway between 1 and 1 + 2^-23 -> even (1);
+    # 1 + 3 2^-24 halfway between 1 + 2^-23 and 1 + 2^-22 -> even (1 + 2^-22)
+    assert R._rn32_scaled_int((1 << 24) + 1, -24) == np.float32(1.0)
+    assert R._rn32_scaled_int((1 << 24) + 3, -24) == np.float32(1.0 + 2.0 ** -22)
+    assert R._rn32_scaled_int(-((1 << 24) + 1), -24) == np.float32(-1.0)
+
+
+def test_dense32_fp32_is_the_exact_sum_rounded_once():
+    # T_b x_b with products 1, 2^-24 and 2^-80: the exact sum lies just above
+    # the float32 midpoint 1 + 2^-24, so it rounds up to 1 + 2^-23; a float64
+    # sum drops the 2^-80 and the tie then goes to the even neighbour 1
+    T = np.zeros((1, 32, 32))
+    T[0, 0, :3] = 1.0
+    T[0, 1, :2] = 1.0           # 1 + 2^-24 exactly: a true tie -> 1
+    T[0, 2, 0] = 0.5            # a plain product
+    x = np.zeros((1, 32), dtype=np.float32)
+    x[0, :3] = [1.0, 2.0 ** -24, 2.0 ** -80]
+    v, n_int = R.dense32_fp32(x, T)
+    assert v[0, 0] == np.float32(1.0 + 2.0 ** -23)
+    assert v[0, 1] == np.float32(1.0)
+    assert v[0, 2] == np.float32(0.5)
+    assert n_int >= 1
+    assert R.dense32_fp64(x, T).astype(np.float32)[0, 0] == np.float32(1.0)   # the float64 shortcut
+    # ordinary data: the exponent-span check passes and the float64 sum is used
+    import workloads as WL
+    wl = WL.make_workload(5, M=64, K=256, Ns=(4,))
+    T = WL.bf16_bits_to_f32(wl.t_act_bits)
+    v, n_int = R.dense32_fp32(wl.x_f32, T)
+    np.testing.assert_array_equal(v, R.dense32_fp64(wl.x_f32, T).astype(np.float32))

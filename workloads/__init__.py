@@ -27,8 +27,8 @@ Bit conventions (inputs are defined by their bits):
   * weights: float32;
   * permutation: int32 [rounds][d], used as a gather u[i] = v[perm[i]];
   * signs: int8 [rounds][d] in {-1, +1};
-  * dense transforms: bfloat16 bits [d/32][32][32] row-major (activation
-    side) and their float32 inverse-transposes (weight side).
+  * dense transforms: bfloat16 bits [d/32][32][32] row-major (the activation
+    side; the weight side is derived from them by whoever consumes them).
 """
 from __future__ import annotations
 
@@ -110,7 +110,6 @@ class LinearWorkload:
     perm: Optional[np.ndarray]         # int32 [rounds, K]
     signs: Optional[np.ndarray]        # int8 [rounds, K]
     t_act_bits: Optional[np.ndarray]   # uint16 [K/32, 32, 32] bfloat16 bits
-    t_wgt: Optional[np.ndarray]        # float32 [K/32, 32, 32]
     weights: list                      # float32 [N, K] per linear
 
     @property
@@ -155,28 +154,22 @@ def _rotation_metadata(spec: ConfigSpec, K: int):
     return np.stack(perms), np.stack(signs)
 
 
-def _dense32_pair(spec: ConfigSpec, K: int):
-    """Seeded per-32-block transform pair: T_b = (H32/sqrt 32) diag(s_b) Q_b
-    stored as bfloat16 (activation side) and the float32 inverse-transpose of
-    that stored matrix (weight side)."""
+def _dense32_mats(spec: ConfigSpec, K: int):
+    """Seeded per-32-block transforms T_b = (H32/sqrt 32) diag(s_b) Q_b with
+    s_b log-uniform on [0.5, 2] and Q_b Haar orthogonal, stored as bfloat16."""
     from scipy.linalg import hadamard  # library construction of the +-1 Sylvester matrix
     nb = K // 32
     gd = rng_for(spec.cid, STREAM_T_DIAG)
     go = rng_for(spec.cid, STREAM_T_ORTH)
     h = hadamard(32).astype(np.float64) / np.sqrt(32.0)
     t_bits = np.empty((nb, 32, 32), dtype=np.uint16)
-    t_w = np.empty((nb, 32, 32), dtype=np.float32)
     for b in range(nb):
         s = np.exp(gd.uniform(np.log(0.5), np.log(2.0), size=32))
         a = go.standard_normal((32, 32))
         q, r = np.linalg.qr(a)
         q = q * np.sign(np.diag(r))[None, :]
-        t = h @ np.diag(s) @ q
-        tb = f32_to_bf16_bits(t.astype(np.float32))
-        t_bits[b] = tb
-        t_stored = bf16_bits_to_f32(tb).astype(np.float64)
-        t_w[b] = np.linalg.inv(t_stored).T.astype(np.float32)
-    return t_bits, t_w
+        t_bits[b] = f32_to_bf16_bits((h @ np.diag(s) @ q).astype(np.float32))
+    return t_bits
 
 
 def make_workload(cid: int, M: Optional[int] = None, K: Optional[int] = None,
@@ -192,13 +185,13 @@ def make_workload(cid: int, M: Optional[int] = None, K: Optional[int] = None,
     if K % spec.block or K % spec.group:
         raise ValueError("K must be a multiple of the block and the group")
     x_bits = _activations(spec, M, K)
-    perm = signs = t_bits = t_w = None
+    perm = signs = t_bits = None
     if spec.rot == "rpbh":
         perm, signs = _rotation_metadata(spec, K)
     else:
-        t_bits, t_w = _dense32_pair(spec, K)
+        t_bits = _dense32_mats(spec, K)
     weights = []
     for i, n in enumerate(Ns):
         gw = rng_for(spec.cid, STREAM_W0 if i == 0 else STREAM_W1 + (i - 1) * 10)
         weights.append(gw.normal(0.0, 0.02, size=(n, K)).astype(np.float32))
-    return LinearWorkload(spec, M, K, Ns, x_bits, perm, signs, t_bits, t_w, weights)
+    return LinearWorkload(spec, M, K, Ns, x_bits, perm, signs, t_bits, weights)
