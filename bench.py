@@ -68,8 +68,7 @@ def _setup(torch, oq, WL, cid, n_sets_bytes=600 << 20):
                 t = oq.oq_prepack_w4(w["codes"], w["scales"], W.shape[0], wl.K)
                 w["codes"], w["scales"] = t["codes"], t["scales"]
     else:
-        rot = oq.Rotation.dense32(torch.from_numpy(wl.t_act_bits.view("int16")).to(dev),
-                                  torch.from_numpy(wl.t_wgt).to(dev))
+        rot = oq.Rotation.dense32(torch.from_numpy(wl.t_act_bits.view("int16")).to(dev))
         ws = [oq.oq_quant_weight(torch.from_numpy(W).to(dev), rot, oq.OQ_W_MXFP4, 32) for W in wl.weights]
         st["tiled"] = wl.K % 128 == 0
         if st["tiled"]:  # offline: repack into the MFMA operand layout

@@ -128,14 +128,15 @@ size_t oq_tiled_mx_bytes(int64_t rows, int32_t K);
  *   1, 2, ..., h/2, each add/subtract rounded once, then a multiply by
  *   RN32(1/sqrt h).
  *
- * OQ_ROT_DENSE32 -- WUSH review "Core claim": one transform per 32-block.
+ * OQ_ROT_DENSE32 -- WUSH review "Core claim": one transform per 32-block,
+ *   activations take T_b and weights its inverse-transpose T_b^{-T}.
  *   mats: bfloat16 [d/32][32][32] row-major, v_b = T_b x_b, 16-byte aligned.
- *   d % 32 == 0.
- *   For weights (oq_quant_weight) mats_w is used instead: float32
- *   [d/32][32][32], the inverse-transposes T_b^{-T}.
- *   Activation-side float32 results are the exact value of T_b x_b rounded
- *   once to float32 (bf16 x bf16 products summed in float64, which is exact
- *   for ordinary activations).
+ *   d % 32 == 0.  Weights (oq_quant_weight) use the same mats: the library
+ *   forms T_b^{-T} itself in float64 (Gauss-Jordan with partial pivoting);
+ *   every T_b must be invertible.
+ *   Activation-side float32 results are T_b x_b rounded once to float32,
+ *   the bf16 x bf16 products summed in float64 (exact whenever the products
+ *   of one output span at most 32 binades, as ordinary activations do).
  */
 typedef struct {
   int32_t kind;
@@ -145,7 +146,6 @@ typedef struct {
   const int32_t *perm;
   const int8_t *signs;
   const uint16_t *mats;
-  const float *mats_w;
 } oq_rot;
 
 /* Message of the last failed call on this thread ("" if none). */
@@ -202,8 +202,8 @@ int oq_quant_act(const uint16_t *x, int64_t M, int32_t d, int64_t ldx,
  * rotation": W x = (W H^T)(H x); App. B.1: the weight absorbs P^T H^T;
  * Eq. 4: w1 = W 1 in float32 from the unquantized weight).
  *   Each row w of W [N][ldw] (float32) becomes R w (the same rotation as the
- *   activations; for DENSE32 the inverse-transposes rot->mats_w are applied,
- *   in float64 with one rounding to float32), then:
+ *   activations; for DENSE32 the inverse-transposes of rot->mats, applied in
+ *   float64 with one rounding to float32), then:
  *   wfmt OQ_W4: symmetric absmax INT4 per (row, group of `group` input
  *     columns), codes packed two per byte [N][K/2], scales float32 [N][K/group];
  *   wfmt OQ_W_MXFP4: E2M1 codes [N][K/2] and E8M0 bytes [N][K/32] (group 32).
@@ -242,7 +242,10 @@ int oq_gemm_w4a8(const int8_t *qa, int64_t lda, const float *a_scale, int64_t M,
  *     path on the same codes.  The library picks the workgroup shape from
  *     M, N and the CU count; the environment variable OQ_FP6_TILE (256x256,
  *     256x192, 256x128 or 128x192; OQ_A4 only) forces one, for tuning.  The
- *     result does not depend on the shape.
+ *     result does not depend on the shape.  One activation plane
+ *     (oq_tiled_bytes(M, K)) and the weights (oq_tiled_bytes(N, K)) must each
+ *     stay below 4 GiB (the kernel's 32-bit operand offsets); larger requests
+ *     fail with OQ_ERR_UNSUPPORTED (split M or N).
  *   afmt OQ_MXFP4: qa E2M1 nibbles, a_scale uint8 E8M0 [M][K/32]; w E2M1
  *     nibbles [N][K/2], w_scale uint8 E8M0 [N][K/32]; group must be 32;
  *     y = bf16_RNE( sum_blocks 2^(ea+ew) sum_k fp4(a) fp4(w) + bias[o] );

@@ -42,7 +42,6 @@ class oq_rot(ctypes.Structure):
         ("perm", ctypes.c_void_p),
         ("signs", ctypes.c_void_p),
         ("mats", ctypes.c_void_p),
-        ("mats_w", ctypes.c_void_p),
     ]
 
 
@@ -118,6 +117,45 @@ def _dev(t: torch.Tensor):
     return t.device
 
 
+def _need(t: Optional[torch.Tensor], nbytes: int, what: str, dtypes=None, optional: bool = False):
+    """Argument check before a call: t is a GPU tensor of one of `dtypes`,
+    contiguous, holding at least `nbytes` bytes (the library reads or writes
+    that many from its base)."""
+    if t is None:
+        if optional:
+            return
+        raise OQError(OQ_ERR_INVALID_ARG, f"{what} is required")
+    if not t.is_cuda:
+        raise OQError(OQ_ERR_INVALID_ARG, f"{what} must live on the GPU")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise OQError(OQ_ERR_INVALID_ARG, f"{what} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise OQError(OQ_ERR_INVALID_ARG, f"{what} must be contiguous")
+    if t.numel() * t.element_size() < nbytes:
+        raise OQError(OQ_ERR_INVALID_ARG, f"{what} holds {t.numel() * t.element_size()} bytes, {nbytes} needed")
+
+
+_F32 = (torch.float32,)
+_BYTES = (torch.uint8, torch.int8)
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _out_y(y: Optional[torch.Tensor], M: int, N: int, dev) -> torch.Tensor:
+    """The bfloat16 output [M][>= N] (allocated when not given)."""
+    if y is None:
+        return torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    if (not y.is_cuda or y.dtype not in _BF16 or y.dim() != 2 or y.shape[0] < M or y.shape[1] < N
+            or y.stride(1) != 1):
+        raise OQError(OQ_ERR_INVALID_ARG, f"y must be a GPU bfloat16 matrix of at least {M} x {N} with unit column stride")
+    return y
+
+
+def _epilogue_args(M: int, N: int, mean, w1, bias):
+    _need(mean, 4 * M, "mean", _F32, optional=True)
+    _need(w1, 4 * N, "w1", _F32, optional=True)
+    _need(bias, 4 * N, "bias", _F32, optional=True)
+
+
 def _bits16(x: torch.Tensor) -> torch.Tensor:
     if x.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
         raise OQError(OQ_ERR_INVALID_ARG, "bfloat16 input expected (or its 16-bit pattern)")
@@ -127,11 +165,10 @@ def _bits16(x: torch.Tensor) -> torch.Tensor:
 class Rotation:
     """Host descriptor plus the device arrays it points to (kept alive here)."""
 
-    def __init__(self, kind: int, d: int, block: int = 0, rounds: int = 0, perm=None, signs=None,
-                 mats=None, mats_w=None):
+    def __init__(self, kind: int, d: int, block: int = 0, rounds: int = 0, perm=None, signs=None, mats=None):
         self.kind, self.d, self.block, self.rounds = kind, d, block, rounds
-        self.perm, self.signs, self.mats, self.mats_w = perm, signs, mats, mats_w
-        self.c = oq_rot(kind, d, block, rounds, _p(perm), _p(signs), _p(mats), _p(mats_w))
+        self.perm, self.signs, self.mats = perm, signs, mats
+        self.c = oq_rot(kind, d, block, rounds, _p(perm), _p(signs), _p(mats))
 
     @staticmethod
     def rpbh(perm: torch.Tensor, signs: torch.Tensor, block: int) -> "Rotation":
@@ -152,10 +189,11 @@ class Rotation:
         return self.rounds * self.block if self.kind == OQ_ROT_KRON else self.d
 
     @staticmethod
-    def dense32(mats_bits: torch.Tensor, mats_w: Optional[torch.Tensor] = None) -> "Rotation":
+    def dense32(mats_bits: torch.Tensor) -> "Rotation":
+        """Per-32-block transforms T_b (bfloat16 bits [d/32][32][32]); the
+        weight side uses their inverse-transposes, formed by the library."""
         d = mats_bits.shape[0] * 32
-        return Rotation(OQ_ROT_DENSE32, d, 32, 1, mats=mats_bits.contiguous(),
-                        mats_w=None if mats_w is None else mats_w.to(torch.float32).contiguous())
+        return Rotation(OQ_ROT_DENSE32, d, 32, 1, mats=mats_bits.contiguous())
 
     def ref(self):
         return ctypes.byref(self.c)
@@ -241,8 +279,14 @@ def oq_quant_weight(w, rot: Optional[Rotation], wfmt: int, group: int, codes=Non
 def oq_gemm_w4a8(qa, a_scale, w, w_scale, N: int, group: int, mean=None, w1=None, bias=None, y=None,
                  ws=None):
     M, K = qa.shape
-    if y is None:
-        y = torch.empty((M, N), dtype=torch.bfloat16, device=_dev(qa))
+    if qa.dtype not in _BYTES or qa.stride(1) != 1:
+        raise OQError(OQ_ERR_INVALID_ARG, "qa must be an int8 matrix with unit column stride")
+    _need(a_scale, 4 * M, "a_scale", _F32)
+    if M and N and group > 0:
+        _need(w, N * K // 2, "w", _BYTES)
+        _need(w_scale, 4 * N * (K // group), "w_scale", _F32)
+    _epilogue_args(M, N, mean, w1, bias)
+    y = _out_y(y, M, N, _dev(qa))
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     _check(_lib.oq_gemm_w4a8(_p(qa), qa.stride(0), _p(a_scale), M, K, _p(w), _p(w_scale), N, group, _p(mean),
                              _p(w1), _p(bias), _p(y), y.stride(0), _p(ws), wsb, _stream()))
@@ -255,12 +299,34 @@ def oq_gemm_w4a4(afmt: int, qa, a_scale, w, w_scale, N: int, group: int, mean=No
         if M is None or K is None:
             raise OQError(OQ_ERR_INVALID_ARG, "tiled operands need explicit M and K")
         lda = 0
+        if M > 0 and N > 0 and K > 0:
+            if afmt == (OQ_MXFP4 | OQ_TILED):
+                _need(qa, oq_tiled_mx_bytes(M, K), "qa", _BYTES)
+                _need(a_scale, oq_tiled_mx_bytes(M, K) // 16, "a_scale", _BYTES)
+                _need(w, oq_tiled_mx_bytes(N, K), "w", _BYTES)
+                _need(w_scale, oq_tiled_mx_bytes(N, K) // 16, "w_scale", _BYTES)
+            else:
+                planes = 2 if (afmt & ~OQ_TILED) == OQ_A6 else 1
+                _need(qa, planes * oq_tiled_bytes(M, K), "qa", _BYTES)
+                _need(a_scale, 4 * M, "a_scale", _F32)
+                _need(w, oq_tiled_bytes(N, K), "w", _BYTES)
+                _need(w_scale, 4 * (K // 64) * ((N + 31) // 32 * 32), "w_scale", _F32)
     else:
         M = qa.shape[0]
         K = qa.shape[1] * 2
         lda = qa.stride(0) * qa.element_size()
-    if y is None:
-        y = torch.empty((M, N), dtype=torch.bfloat16, device=_dev(qa))
+        if qa.dtype not in _BYTES or qa.stride(1) != 1:
+            raise OQError(OQ_ERR_INVALID_ARG, "qa must be a uint8 matrix with unit column stride")
+        if M > 0 and N > 0:
+            _need(w, N * K // 2, "w", _BYTES)
+            if afmt == OQ_MXFP4:
+                _need(a_scale, M * (K // 32), "a_scale", _BYTES)
+                _need(w_scale, N * (K // 32), "w_scale", _BYTES)
+            elif group > 0:
+                _need(a_scale, 4 * M, "a_scale", _F32)
+                _need(w_scale, 4 * N * (K // group), "w_scale", _F32)
+    _epilogue_args(M, N, mean, w1, bias)
+    y = _out_y(y, M, N, _dev(qa))
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     _check(_lib.oq_gemm_w4a4(afmt, _p(qa), lda, _p(a_scale), M, K, _p(w),
                              _p(w_scale), N, group, _p(mean), _p(w1), _p(bias), _p(y), y.stride(0), _p(ws), wsb,
@@ -306,8 +372,22 @@ def oq_linear_fused(x, rot: Optional[Rotation], center: bool, afmt: int, w, w_sc
     x = _bits16(x)
     M, K = x.shape
     dev = _dev(x)
-    if y is None:
-        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    fmt = afmt & ~OQ_SCALE_PCTL
+    if M > 0 and N > 0:
+        if fmt == (OQ_MXFP4 | OQ_TILED):
+            _need(w, oq_tiled_mx_bytes(N, K), "w", _BYTES)
+            _need(w_scale, oq_tiled_mx_bytes(N, K) // 16, "w_scale", _BYTES)
+        elif fmt & OQ_TILED:
+            _need(w, oq_tiled_bytes(N, K), "w", _BYTES)
+            _need(w_scale, 4 * (K // 64) * ((N + 31) // 32 * 32), "w_scale", _F32)
+        else:
+            _need(w, N * K // 2, "w", _BYTES)
+            if fmt == OQ_MXFP4:
+                _need(w_scale, N * (K // 32), "w_scale", _BYTES)
+            elif group > 0:
+                _need(w_scale, 4 * N * (K // group), "w_scale", _F32)
+    _epilogue_args(M, N, None, w1, bias)
+    y = _out_y(y, M, N, dev)
     if ws is None:
         ws = torch.empty(max(1, oq_workspace_bytes(OQ_OP_LINEAR, M, K, N, afmt)), dtype=torch.uint8, device=dev)
     _check(_lib.oq_linear_fused(_p(x), M, K, x.stride(0), _rref(rot), int(center), afmt, _p(w), _p(w_scale), N,
@@ -370,6 +450,8 @@ def oq_gemm_lm(bits: int, qa, a_scale, w16, N: int, levels=None, tiled: bool = F
         if M is None or K is None:
             raise OQError(OQ_ERR_INVALID_ARG, "tiled operands need explicit M and K")
         lda = 0
+        if M > 0 and N > 0 and K > 0:
+            _need(qa, oq_tiled_f16_bytes(M, K), "qa")
     else:
         M = qa.shape[0]
         K = qa.shape[1] * (2 if bits <= 4 else 1)
@@ -377,8 +459,11 @@ def oq_gemm_lm(bits: int, qa, a_scale, w16, N: int, levels=None, tiled: bool = F
         if ws is None:
             ws = torch.empty(max(16, oq_workspace_bytes(OQ_OP_GEMM_LM, M, K, N, 0)), dtype=torch.uint8,
                              device=_dev(qa))
-    if y is None:
-        y = torch.empty((M, N), dtype=torch.bfloat16, device=_dev(qa))
+    if M > 0 and N > 0 and K > 0:
+        _need(a_scale, 4 * M, "a_scale", _F32)
+        _need(w16, oq_tiled_f16_bytes(N, K), "w16")
+    _epilogue_args(M, N, mean, w1, bias)
+    y = _out_y(y, M, N, _dev(qa))
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     _check(_lib.oq_gemm_lm(bits, int(tiled), _p(qa), lda, _p(a_scale), M, K, _p(levels), _p(w16), N, _p(mean),
                            _p(w1), _p(bias), _p(y), y.stride(0), _p(ws), wsb, _stream()))
@@ -438,8 +523,16 @@ def oq_quant_act_gsum(x, rot: Optional[Rotation], afmt: int, center: bool = Fals
 def oq_gemm_w4a4_asym(qa, a_scale, gsum, w, N: int, M: int, K: int, mean=None, w1=None, bias=None, y=None,
                       afmt: int = OQ_A4 | OQ_TILED):
     """w: oq_prepack_w4_asym output (dict with codes, scales, corr)."""
-    if y is None:
-        y = torch.empty((M, N), dtype=torch.bfloat16, device=_dev(qa))
+    if M > 0 and N > 0 and K > 0:
+        Np = (N + 31) // 32 * 32
+        _need(qa, oq_tiled_bytes(M, K), "qa", _BYTES)
+        _need(a_scale, 4 * M, "a_scale", _F32)
+        _need(gsum, 4 * (K // 64) * M, "gsum")
+        _need(w["codes"], oq_tiled_bytes(N, K), "w codes", _BYTES)
+        _need(w["scales"], 4 * (K // 64) * Np, "w scales", _F32)
+        _need(w["corr"], 8 * (K // 64) * Np, "w corr")
+    _epilogue_args(M, N, mean, w1, bias)
+    y = _out_y(y, M, N, _dev(qa))
     _check(_lib.oq_gemm_w4a4_asym(afmt, _p(qa), _p(a_scale), _p(gsum), M, K, _p(w["codes"]), _p(w["scales"]),
                                   _p(w["corr"]), N, _p(mean), _p(w1), _p(bias), _p(y), y.stride(0), _stream()))
     return y

@@ -22,7 +22,6 @@ FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",
 ]
@@ -32,19 +31,39 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into liboq.so; returns the library path."""
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC] + FLAGS + ["-I", os.path.join(ROOT, "include")] + sources() + ["-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    proc = subprocess.run(cmd, capture_output=True, text=True)
-    msgs = [ln for ln in (proc.stdout + proc.stderr).splitlines()
-            if "packed-fp32-ops" not in ln and "recognized feature" not in ln]
-    if proc.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
-    if verbose and msgs:
-        print("\n".join(msgs), file=sys.stderr)
+def _filter(text):
+    return [ln for ln in text.splitlines() if "packed-fp32-ops" not in ln and "recognized feature" not in ln]
+
+
+def build(verbose: bool = False, jobs: int = 0) -> str:
+    """Compile every HIP source (one hipcc process per file, in parallel) and
+    link them into liboq.so; returns the library path."""
+    import concurrent.futures
+    import tempfile
+    jobs = jobs or min(8, os.cpu_count() or 1)
+    with tempfile.TemporaryDirectory(prefix="oq_build_") as tmpd:
+        def compile_one(src):
+            obj = os.path.join(tmpd, os.path.basename(src) + ".o")
+            cmd = [HIPCC] + FLAGS + ["-I", os.path.join(ROOT, "include"), "-c", src, "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            proc = subprocess.run(cmd, capture_output=True, text=True)
+            return src, obj, proc.returncode, _filter(proc.stdout + proc.stderr)
+
+        with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
+            results = list(ex.map(compile_one, sources()))
+        errors = [f"{os.path.basename(src)}:\n" + "\n".join(msgs) for src, _, rc, msgs in results if rc != 0]
+        if errors:
+            raise RuntimeError("hipcc failed:\n" + "\n".join(errors))
+        if verbose:
+            for src, _, _, msgs in results:
+                if msgs:
+                    print("\n".join(msgs), file=sys.stderr)
+        tmp = LIB + ".tmp"
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + [obj for _, obj, _, _ in results] + ["-o", tmp]
+        proc = subprocess.run(cmd, capture_output=True, text=True)
+        if proc.returncode != 0:
+            raise RuntimeError("link failed:\n" + "\n".join(_filter(proc.stdout + proc.stderr)))
     os.replace(tmp, LIB)
     return LIB
 

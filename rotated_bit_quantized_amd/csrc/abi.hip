@@ -91,11 +91,11 @@ int rot_args(const char *fn, const oq_rot *rot, int d, RotArgs *ra) {
   return OQ_OK;
 }
 
-int check_dense(const char *fn, const oq_rot *rot, int d, bool weights) {
+int check_dense(const char *fn, const oq_rot *rot, int d) {
   if (rot->d != d) return fail(OQ_ERR_INVALID_ARG, "%s: rot->d=%d differs from d=%d", fn, rot->d, d);
   if (d % 32) return fail(OQ_ERR_INVALID_ARG, "%s: d=%d must be a multiple of 32", fn, d);
-  if (weights ? !rot->mats_w : !rot->mats) return fail(OQ_ERR_INVALID_ARG, "%s: transform matrices are NULL", fn);
-  if (!weights && (reinterpret_cast<uintptr_t>(rot->mats) & 15))
+  if (!rot->mats) return fail(OQ_ERR_INVALID_ARG, "%s: transform matrices are NULL", fn);
+  if (reinterpret_cast<uintptr_t>(rot->mats) & 15)
     return fail(OQ_ERR_ALIGNMENT, "%s: rot->mats must be 16-byte aligned", fn);
   return OQ_OK;
 }
@@ -257,7 +257,7 @@ int oq_rotate(const oq_rot *rot, const uint16_t *x, int64_t M, int64_t ldx, int 
   if (center && !mean) return fail(OQ_ERR_INVALID_ARG, "oq_rotate: centering needs mean");
   if (rot->kind == OQ_ROT_DENSE32) {
     if (center) return fail(OQ_ERR_UNSUPPORTED, "oq_rotate: centering with a DENSE32 rotation");
-    rc = check_dense("oq_rotate", rot, d, false);
+    rc = check_dense("oq_rotate", rot, d);
     if (rc) return rc;
     g_err[0] = 0;
     return hip_status(launch_dense32(x, M, d, ldx, rot->mats, 0, y, ldy * 4, nullptr, stream), "oq_rotate");
@@ -293,7 +293,7 @@ int oq_quant_act(const uint16_t *x, int64_t M, int32_t d, int64_t ldx, const oq_
     if (M > 0 && !e8m0) return fail(OQ_ERR_INVALID_ARG, "oq_quant_act: e8m0 is NULL");
     if (reinterpret_cast<uintptr_t>(e8m0) & 3) return fail(OQ_ERR_ALIGNMENT, "oq_quant_act: e8m0 must be 4-byte aligned");
     if (scale) return fail(OQ_ERR_INVALID_ARG, "oq_quant_act: scale must be NULL for MXFP4");
-    rc = check_dense("oq_quant_act", rot, d, false);
+    rc = check_dense("oq_quant_act", rot, d);
     if (rc) return rc;
     g_err[0] = 0;
     return hip_status(launch_dense32(x, M, d, ldx, rot->mats, 2, codes, 0, e8m0, stream), "oq_quant_act");
@@ -305,7 +305,7 @@ int oq_quant_act(const uint16_t *x, int64_t M, int32_t d, int64_t ldx, const oq_
     if (ldc_bytes < d / 2) return fail(OQ_ERR_INVALID_ARG, "oq_quant_act: ldc_bytes < d/2");
     if (M > 0 && !e8m0) return fail(OQ_ERR_INVALID_ARG, "oq_quant_act: e8m0 is NULL");
     if (scale) return fail(OQ_ERR_INVALID_ARG, "oq_quant_act: scale must be NULL for MXFP4");
-    rc = check_dense("oq_quant_act", rot, d, false);
+    rc = check_dense("oq_quant_act", rot, d);
     if (rc) return rc;
     g_err[0] = 0;
     return hip_status(launch_dense32(x, M, d, ldx, rot->mats, 1, codes, ldc_bytes, e8m0, stream), "oq_quant_act");
@@ -357,10 +357,10 @@ int oq_quant_weight(const float *w, int32_t N, int32_t K, int64_t ldw, const oq_
   if (wfmt == OQ_W_MXFP4) {
     if (!rot || rot->kind != OQ_ROT_DENSE32) return fail(OQ_ERR_UNSUPPORTED, "oq_quant_weight: MXFP4 weights need DENSE32");
     if (w1) return fail(OQ_ERR_UNSUPPORTED, "oq_quant_weight: w1 is produced for OQ_W4 only");
-    int rc = check_dense("oq_quant_weight", rot, K, true);
+    int rc = check_dense("oq_quant_weight", rot, K);
     if (rc) return rc;
     g_err[0] = 0;
-    return hip_status(launch_weight_dense32(w, N, K, ldw, rot->mats_w, codes, (uint8_t *)scales, nullptr, stream),
+    return hip_status(launch_weight_dense32(w, N, K, ldw, rot->mats, codes, (uint8_t *)scales, nullptr, stream),
                       "oq_quant_weight");
   }
   if (wfmt != OQ_W4) return fail(OQ_ERR_INVALID_ARG, "oq_quant_weight: unknown wfmt %d", wfmt);
@@ -415,6 +415,8 @@ int oq_gemm_w4a4(int afmt, const uint8_t *qa, int64_t lda_bytes, const void *a_s
     if (base_fmt != OQ_A4 && base_fmt != OQ_A6)
       return fail(OQ_ERR_UNSUPPORTED, "oq_gemm_w4a4: tiled operands exist for OQ_A4, OQ_A6 and OQ_MXFP4");
     if (group != 64) return fail(OQ_ERR_UNSUPPORTED, "oq_gemm_w4a4: tiled GEMM needs group 64 (got %d)", group);
+    if (!fp6_offsets_fit(M, N, K))
+      return fail(OQ_ERR_UNSUPPORTED, "oq_gemm_w4a4: a tiled operand plane exceeds 4 GiB (split M or N)");
     rc = check_int_epilogue("oq_gemm_w4a4", K, group, mean, w1);
     if (rc) return rc;
     if (M > 0 && N > 0 && !a_scale) return fail(OQ_ERR_INVALID_ARG, "oq_gemm_w4a4: a_scale is NULL");
@@ -483,10 +485,17 @@ size_t oq_workspace_bytes(int op, int64_t M, int32_t K, int32_t N, int afmt) {
   return linear_ws(M, K, afmt & ~OQ_SCALE_PCTL).total;
 }
 
-int oq_linear_fused(const uint16_t *x, int64_t M, int32_t K, int64_t ldx, const oq_rot *rot, int center, int afmt,
-                    const uint8_t *w, const void *w_scale, int32_t N, int32_t group, const float *w1, const float *bias,
-                    uint16_t *y, int64_t ldy, void *ws, size_t ws_bytes, hipStream_t stream) {
-  const char *fn = "oq_linear_fused";
+}  // extern "C"
+
+namespace oq {
+namespace {
+
+// The whole layer into a given workspace (validation first, then K1 and the
+// GEMM on `stream`); shared by oq_linear_fused and oq_linear_fused_noalloc.
+int linear_fused_impl(const char *fn, const uint16_t *x, int64_t M, int32_t K, int64_t ldx, const oq_rot *rot,
+                      int center, int afmt, const uint8_t *w, const void *w_scale, int32_t N, int32_t group,
+                      const float *w1, const float *bias, uint16_t *y, int64_t ldy, void *ws, size_t ws_bytes,
+                      hipStream_t stream) {
   int rc = check_x(fn, x, M, K, ldx);
   if (rc) return rc;
   if (rot && rot->kind == OQ_ROT_KRON)
@@ -512,7 +521,7 @@ int oq_linear_fused(const uint16_t *x, int64_t M, int32_t K, int64_t ldx, const 
     if (rc) return rc;
     if (reinterpret_cast<uintptr_t>(w_scale) & 3)
       return fail(OQ_ERR_ALIGNMENT, "%s: tiled E8M0 scale words must be 4-byte aligned", fn);
-    rc = check_dense(fn, rot, K, false);
+    rc = check_dense(fn, rot, K);
     if (rc) return rc;
     char *wsb = static_cast<char *>(ws);
     uint8_t *codes = reinterpret_cast<uint8_t *>(wsb + L.codes);
@@ -528,6 +537,7 @@ int oq_linear_fused(const uint16_t *x, int64_t M, int32_t K, int64_t ldx, const 
       return fail(OQ_ERR_UNSUPPORTED, "%s: tiled operands exist for OQ_A4, OQ_A6 and OQ_MXFP4", fn);
     if (K % 64) return fail(OQ_ERR_UNSUPPORTED, "%s: tiled operands need K %% 64 == 0", fn);
     if (group != 64) return fail(OQ_ERR_UNSUPPORTED, "%s: tiled GEMM needs group 64 (got %d)", fn, group);
+    if (!fp6_offsets_fit(M, N, K)) return fail(OQ_ERR_UNSUPPORTED, "%s: a tiled operand plane exceeds 4 GiB (split M or N)", fn);
     const LinearWs L = linear_ws(M, K, afmt);
     if (M > 0 && (!ws || ws_bytes < L.total))
       return fail(OQ_ERR_WORKSPACE, "%s: workspace of %zu bytes required (got %zu)", fn, L.total, ws_bytes);
@@ -565,7 +575,7 @@ int oq_linear_fused(const uint16_t *x, int64_t M, int32_t K, int64_t ldx, const 
     if (!rot || rot->kind != OQ_ROT_DENSE32) return fail(OQ_ERR_UNSUPPORTED, "%s: MXFP4 needs a DENSE32 rotation", fn);
     if (center || w1) return fail(OQ_ERR_UNSUPPORTED, "%s: centering is not defined for MXFP4 here", fn);
     if (group != 32) return fail(OQ_ERR_INVALID_ARG, "%s: MXFP4 blocks are 32 (group=%d)", fn, group);
-    rc = check_dense(fn, rot, K, false);
+    rc = check_dense(fn, rot, K);
     if (rc) return rc;
     uint8_t *e8 = reinterpret_cast<uint8_t *>(wsb + L.scale);
     g_err[0] = 0;
@@ -589,6 +599,19 @@ int oq_linear_fused(const uint16_t *x, int64_t M, int32_t K, int64_t ldx, const 
   return hip_status(launch_gemm_int(codes, L.ldc, afmt == OQ_A4 ? 1 : 0, scale, M, K, w, (const float *)w_scale, N, group,
                                     center ? mean : nullptr, center ? w1 : nullptr, bias, y, ldy, stream),
                     fn);
+}
+
+
+}  // namespace
+}  // namespace oq
+
+extern "C" {
+
+int oq_linear_fused(const uint16_t *x, int64_t M, int32_t K, int64_t ldx, const oq_rot *rot, int center, int afmt,
+                    const uint8_t *w, const void *w_scale, int32_t N, int32_t group, const float *w1, const float *bias,
+                    uint16_t *y, int64_t ldy, void *ws, size_t ws_bytes, hipStream_t stream) {
+  return linear_fused_impl("oq_linear_fused", x, M, K, ldx, rot, center, afmt, w, w_scale, N, group, w1, bias, y,
+                           ldy, ws, ws_bytes, stream);
 }
 
 // ------------------------------------------------------------ Lloyd-Max path
@@ -789,6 +812,7 @@ int oq_gemm_w4a4_asym(int afmt, const uint8_t *qa, const float *a_scale, const u
   if (M == 0 || N == 0) return OQ_OK;
   if (!a_scale || !gsum || !corr) return fail(OQ_ERR_INVALID_ARG, "%s: NULL scale, gsum or corr", fn);
   if (reinterpret_cast<uintptr_t>(corr) & 7) return fail(OQ_ERR_ALIGNMENT, "%s: corr must be 8-byte aligned", fn);
+  if (!fp6_offsets_fit(M, N, K)) return fail(OQ_ERR_UNSUPPORTED, "%s: a tiled operand plane exceeds 4 GiB (split M or N)", fn);
   g_err[0] = 0;
   return hip_status(launch_gemm_fp6_asym(qa, a_scale, gsum, M, K, w_tiled, w_scale_t, corr, N, mean, w1, bias, y, ldy,
                                          stream),

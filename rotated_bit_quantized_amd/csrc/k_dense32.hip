@@ -8,9 +8,11 @@
 //   of v * 2^-e with ties to the even code, saturating at 6, sign kept.
 //
 // Two kernels.  dense32_kernel (float32 rotated output for oq_rotate, and the
-// weight side) accumulates the transform in float64 and rounds once to
-// float32; for bf16 x bf16 products the float64 sum is exact for ordinary
-// data, so v = RN32(T_b x_b).  Lanes are rows there; the block's matrix is
+// weight side, which forms T_b^{-T} itself) accumulates the transform in
+// float64 and rounds once to float32.  For bf16 x bf16 products the float64
+// sum is exact whenever one output's products span at most 32 binades, which
+// ordinary activations meet; beyond that its error is at most 2^-47 of the
+// sum of the product magnitudes.  Lanes are rows there; the block's matrix is
 // staged in LDS as float64 and read as a broadcast.
 // dense32_mx_mfma_kernel (the activation MXFP4 path) forms the products on the
 // matrix cores and falls back to the same exact float64 sum wherever the
@@ -30,12 +32,58 @@ __device__ __forceinline__ uint32_t e2m1_code(float t) {
   return c | ((__float_as_uint(t) >> 28) & 8u);
 }
 
-// IN_F32 selects the weight-side variant: float32 rows and float32 matrices.
+// Weight side of the pair: T[i][j] = (T_b^{-1})[j][i] from the bfloat16 T_b
+// (WUSH review, "Core claim": T_w = T_x^{-T}).  Gauss-Jordan elimination with
+// partial pivoting on [T_b | I] in float64, one column of the 32 x 64
+// augmented matrix per thread of the 64; the pivot is the first row of
+// largest magnitude, read by every thread from a copy of the pivot column.
+// Every workgroup that needs block b forms the same inverse (same operations
+// in the same order).  T_b is invertible for the transforms this layer is
+// built for (cond <= 4); a singular block gives non-finite weights.
+__device__ void stage_inverse_transpose(const uint16_t *__restrict__ tb, double *__restrict__ T,
+                                        double *__restrict__ aug, double *__restrict__ fcol) {
+  const int t = threadIdx.x;  // column of [T_b | I]
+  for (int i = 0; i < 32; ++i)
+    aug[i * 64 + t] = t < 32 ? (double)__uint_as_float((uint32_t)tb[i * 32 + t] << 16) : (t - 32 == i ? 1.0 : 0.0);
+  __syncthreads();
+  for (int k = 0; k < 32; ++k) {
+    if (t < 32) fcol[t] = aug[t * 64 + k];
+    __syncthreads();
+    int p = k;
+    double best = fabs(fcol[k]);
+    for (int i = k + 1; i < 32; ++i) {
+      const double a = fabs(fcol[i]);
+      if (a > best) {
+        best = a;
+        p = i;
+      }
+    }
+    const double piv = fcol[p];
+    const double rk = aug[p * 64 + t] / piv;  // the new pivot row (old row p), scaled
+    const double old_k = aug[k * 64 + t];
+    aug[p * 64 + t] = old_k;                   // old row k moves to row p
+    aug[k * 64 + t] = rk;
+    for (int i = 0; i < 32; ++i) {
+      if (i == k) continue;
+      const double f = i == p ? fcol[k] : fcol[i];  // factor of the row now at i
+      aug[i * 64 + t] = aug[i * 64 + t] - f * rk;
+    }
+    __syncthreads();
+  }
+  // T[i][j] = inverse[j][i] = aug[j][32 + i]
+  for (int e = t; e < 1024; e += 64) T[e] = aug[(e & 31) * 64 + 32 + (e >> 5)];
+  __syncthreads();
+}
+
+// IN_F32 selects the weight-side variant: float32 rows, and the matrices are
+// the inverse-transposes of the bfloat16 activation transforms.
 template <bool IN_F32, bool MX_OUT>
 __global__ void __launch_bounds__(64)
-dense32_kernel(const void *__restrict__ xin, int64_t M, int d, int64_t ldx, const void *__restrict__ mats,
+dense32_kernel(const void *__restrict__ xin, int64_t M, int d, int64_t ldx, const uint16_t *__restrict__ mats,
                void *__restrict__ out, int64_t ld_out_bytes, uint8_t *__restrict__ e8m0) {
   __shared__ double T[32 * 32];
+  __shared__ double aug[IN_F32 ? 32 * 64 : 1];
+  __shared__ double fcol[32];
   const int64_t row = (int64_t)blockIdx.x * 64 + threadIdx.x;
   const bool ok = row < M;
   const int nb = d / 32;
@@ -43,13 +91,13 @@ dense32_kernel(const void *__restrict__ xin, int64_t M, int d, int64_t ldx, cons
   const int b1 = min(b0 + BPW, nb);
   for (int b = b0; b < b1; ++b) {
     __syncthreads();
-    for (int e = threadIdx.x; e < 1024; e += 64) {
-      if (IN_F32)
-        T[e] = (double)static_cast<const float *>(mats)[(int64_t)b * 1024 + e];
-      else
-        T[e] = (double)__uint_as_float((uint32_t)static_cast<const uint16_t *>(mats)[(int64_t)b * 1024 + e] << 16);
+    if (IN_F32) {
+      stage_inverse_transpose(mats + (int64_t)b * 1024, T, aug, fcol);
+    } else {
+      for (int e = threadIdx.x; e < 1024; e += 64)
+        T[e] = (double)__uint_as_float((uint32_t)mats[(int64_t)b * 1024 + e] << 16);
+      __syncthreads();
     }
-    __syncthreads();
     if (!ok) continue;
     double xd[32];
     if (IN_F32) {
@@ -398,7 +446,7 @@ dense32_mx_mfma_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t
 }
 
 template <bool IN_F32, bool MX_OUT>
-hipError_t launch(const void *x, int64_t M, int d, int64_t ldx, const void *mats, void *out,
+hipError_t launch(const void *x, int64_t M, int d, int64_t ldx, const uint16_t *mats, void *out,
                   int64_t ld_out_bytes, uint8_t *e8m0, hipStream_t stream) {
   if (M == 0) return hipSuccess;
   const int nb = d / 32;
@@ -427,10 +475,10 @@ hipError_t launch_dense32(const uint16_t *x, int64_t M, int d, int64_t ldx, cons
   return launch<false, false>(x, M, d, ldx, mats, out, ld_out_bytes, e8m0, stream);
 }
 
-hipError_t launch_weight_dense32(const float *w, int N, int K, int64_t ldw, const float *mats_w,
+hipError_t launch_weight_dense32(const float *w, int N, int K, int64_t ldw, const uint16_t *mats,
                                  uint8_t *codes, uint8_t *e8m0, float *w1, hipStream_t stream) {
   (void)w1;
-  return launch<true, true>(w, N, K, ldw, mats_w, codes, K / 2, e8m0, stream);
+  return launch<true, true>(w, N, K, ldw, mats, codes, K / 2, e8m0, stream);
 }
 
 }  // namespace oq

@@ -43,8 +43,10 @@
 //     constants), multiplies by RN32(1 / sqrt(n')) and writes them back, and
 //     the quantiser reads the row in its usual layout;
 //   * Lloyd-Max codes (OrbitQuant PR #25, "Default changes"; the codebook of
-//     the post-rotation marginal): the scale is the row's RMS, from a float64
-//     sum of squares reduced over the wavefront, and each code is the number
+//     the post-rotation marginal): the scale is the row's RMS from the exact
+//     sum of squares rounded to float64 (a float64 wavefront sum, recomputed
+//     exactly in integers where its error could reach the float32
+//     rounding of the RMS), and each code is the number
 //     of thresholds below u = v / rho, found by a binary search of |u| over
 //     the positive thresholds held in LDS (u <= 0 searches with the next
 //     float above |u|, so that a tie goes to the lower level).
@@ -78,6 +80,91 @@ __device__ __forceinline__ double wave_sum_d(double v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
   return v;
+}
+
+// True when r (>= 0, float64) lies within 2^-44 r of a float32 rounding
+// midpoint, i.e. where a float64 value carrying a few dozen ulps of error
+// might round to another float32 than the exact one.
+__device__ __forceinline__ bool near_f32_midpoint(double r) {
+  const float f = (float)r;
+  if (r == 0.0 || !(f < __builtin_inff())) return false;
+  const double fu = (double)nextafterf(f, __builtin_inff());
+  const double fd = (double)nextafterf(f, 0.0f);
+  const double mu = 0.5 * ((double)f + fu), md = 0.5 * ((double)f + fd);  // exact
+  return fabs(r - mu) <= r * 0x1p-44 || fabs(r - md) <= r * 0x1p-44;
+}
+
+// RN64 of the exact sum of v^2 over a wavefront's n values per lane (the
+// entries with act false are skipped).  v = m 2^q with m < 2^24 an integer,
+// so v^2 = m^2 2^(2q) is placed at bit 2q + 298 >= 0 of a 608-bit integer
+// held as 19 32-bit limbs; the wavefront adds its 32-bit pieces into 64-bit
+// LDS counters (at most 4096 pieces of < 2^32 each per counter), every lane
+// propagates the carries and rounds the integer to 53 bits, ties to even.
+// cnt: 19 uint64 of LDS owned by this wavefront.
+template <int SLOTS>
+__device__ double exact_sumsq_rn64(const float (&v)[SLOTS][16], const bool (&act)[SLOTS], int lane,
+                                   unsigned long long *cnt) {
+  if (lane < 19) cnt[lane] = 0ull;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s) {
+    if (!act[s]) continue;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t u = __float_as_uint(v[s][j]);
+      const uint32_t eb = (u >> 23) & 0xFF, mb = u & 0x7FFFFF;
+      const uint64_t m = eb ? (uint64_t)(mb | 0x800000u) : (uint64_t)mb;
+      if (m == 0) continue;
+      const int p = 2 * ((eb ? (int)eb : 1) - 150) + 298;  // bit of m^2's last bit
+      const uint64_t t = m * m;                              // < 2^48
+      const int i = p >> 5, sh = p & 31;
+      const uint64_t lo = t << sh;
+      const uint64_t hi = sh ? t >> (64 - sh) : 0ull;
+      atomicAdd(&cnt[i], lo & 0xFFFFFFFFull);
+      atomicAdd(&cnt[i + 1], lo >> 32);
+      if (hi) atomicAdd(&cnt[i + 2], hi);
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  uint32_t L[19];
+  uint64_t carry = 0;
+#pragma unroll
+  for (int k = 0; k < 19; ++k) {
+    const uint64_t c = cnt[k] + carry;
+    L[k] = (uint32_t)c;
+    carry = c >> 32;
+  }
+  int top = -1;
+#pragma unroll
+  for (int k = 0; k < 19; ++k)
+    if (L[k]) top = k;
+  if (top < 0) return 0.0;
+  uint32_t a = 0, b = 0, c = 0;  // limbs top, top - 1, top - 2 (zero below limb 0)
+  bool sticky = false;
+#pragma unroll
+  for (int k = 0; k < 19; ++k) {
+    if (k == top) a = L[k];
+    if (k == top - 1) b = L[k];
+    if (k == top - 2) c = L[k];
+    if (k < top - 2) sticky |= L[k] != 0;
+  }
+  const int bpos = 31 - __builtin_clz(a);  // leading bit of the top limb
+  const int sdrop = bpos + 12;              // bits of the 96-bit window below the 53 kept
+  const uint64_t hi64 = ((uint64_t)a << 32) | b;
+  uint64_t mant;
+  bool half, rest;
+  if (sdrop >= 32) {
+    const int s2 = sdrop - 32;
+    mant = hi64 >> s2;
+    half = s2 > 0 ? ((hi64 >> (s2 - 1)) & 1ull) != 0 : (c >> 31) != 0;
+    rest = (s2 > 1 && (hi64 & ((1ull << (s2 - 1)) - 1ull)) != 0) || (s2 > 0 ? c != 0 : (c & 0x7FFFFFFFu) != 0);
+  } else {
+    mant = (hi64 << (32 - sdrop)) | (c >> sdrop);
+    half = ((c >> (sdrop - 1)) & 1u) != 0;
+    rest = (c & ((1u << (sdrop - 1)) - 1u)) != 0;
+  }
+  if (half && (rest || sticky || (mant & 1ull))) ++mant;  // 2^53 is still exact
+  return __builtin_ldexp((double)mant, 32 * (top - 2) + sdrop - 298);
 }
 
 // Index lane of physical lane `lane` when a Hadamard block spans 2^n lanes.
@@ -603,9 +690,20 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
         for (int j = 0; j < 16; ++j)
           if (act[s]) ssp[j & 3] += (double)v[s][j] * (double)v[s][j];
       double ss = (ssp[0] + ssp[1]) + (ssp[2] + ssp[3]);
-      ss = wave_sum_d(ss);
+      ss = wave_sum_d(ss);  // the same bits on every lane (xor butterfly)
       const double c2 = (double)c_all * (double)c_all;
-      const float rho = fmaxf((float)__builtin_sqrt((ss * c2) / (double)d), 1e-10f);
+      // Every partial sum above is reached by at most 24 additions of
+      // nonnegative terms (16 per lane chain, 2, then 6 across the
+      // wavefront), so the square root below is within 16 float64 ulps of the
+      // reference value
+      // sqrt(RN64(S) / d) of the exact sum S.  Only when it lies within 2^-44
+      // of a float32 rounding midpoint can RN32 differ; then S is recomputed
+      // exactly (the branch is uniform over the wavefront).
+      double r64 = __builtin_sqrt((ss * c2) / (double)d);
+      if (near_f32_midpoint(r64))
+        r64 = __builtin_sqrt((exact_sumsq_rn64<SLOTS>(v, act, lane, reinterpret_cast<unsigned long long *>(buf)) * c2) /
+                             (double)d);
+      const float rho = fmaxf((float)r64, 1e-10f);
       if (lane == 0) scale_out[row] = rho;
       const float inv = __fdiv_rn(1.0f, rho) * (c_all * sgq);
 #pragma unroll

@@ -103,6 +103,11 @@ __device__ __forceinline__ uint32_t fp6_e2m3_of_int(int q) {
 
 // bytes of one plane of the tiled FP6 operand layout (rows padded to 32)
 __host__ __device__ inline int64_t tiled_bytes(int64_t rows, int K) { return (rows + 31) / 32 * (K / 64) * 1536; }
+// The tiled FP6 GEMM addresses each operand with 32-bit offsets from its base:
+// one plane of activations and the weights must each stay below 4 GiB.
+inline bool fp6_offsets_fit(int64_t M, int N, int K) {
+  return tiled_bytes(M, K) < (int64_t(1) << 32) && tiled_bytes(N, K) < (int64_t(1) << 32);
+}
 
 // activation code formats used inside the library (values of the public enum
 // for the integer widths; internal operand layouts are separate constants)
@@ -249,7 +254,7 @@ hipError_t launch_weight_rpbh(const float *w, int N, int K, int64_t ldw, const R
 // [N][K/2], bfloat16 scale and shift [N][K/group] each
 hipError_t launch_weight_rpbh_asym(const float *w, int N, int K, int64_t ldw, const RotArgs &rot, int group,
                                    uint8_t *codes, uint16_t *sigma, uint16_t *zero, float *w1, hipStream_t stream);
-hipError_t launch_weight_dense32(const float *w, int N, int K, int64_t ldw, const float *mats_w,
+hipError_t launch_weight_dense32(const float *w, int N, int K, int64_t ldw, const uint16_t *mats,
                                  uint8_t *codes, uint8_t *e8m0, float *w1, hipStream_t stream);
 
 }  // namespace oq

@@ -57,11 +57,11 @@ def test_validation_rejects_before_launch(oq):
     rc = lib.oq_quant_act(fake, 4, 1024, 1028, None, 0, oq.OQ_A8, fake, 1024, fake, None, None, None)
     assert rc == oq.OQ_ERR_ALIGNMENT
     # bad block size
-    rot = oq._binding.oq_rot(oq.OQ_ROT_RPBH, 1024, 96, 1, fake, fake, None, None)
+    rot = oq._binding.oq_rot(oq.OQ_ROT_RPBH, 1024, 96, 1, fake, fake, None)
     rc = lib.oq_quant_act(fake, 4, 1024, 1024, ctypes.byref(rot), 0, oq.OQ_A8, fake, 1024, fake, None, None, None)
     assert rc == oq.OQ_ERR_UNSUPPORTED and "block" in _err(oq)
     # three rounds
-    rot = oq._binding.oq_rot(oq.OQ_ROT_RPBH, 1024, 128, 3, fake, fake, None, None)
+    rot = oq._binding.oq_rot(oq.OQ_ROT_RPBH, 1024, 128, 3, fake, fake, None)
     rc = lib.oq_quant_act(fake, 4, 1024, 1024, ctypes.byref(rot), 0, oq.OQ_A8, fake, 1024, fake, None, None, None)
     assert rc == oq.OQ_ERR_UNSUPPORTED
     # MXFP4 without a dense transform
@@ -89,3 +89,21 @@ def test_binding_requires_device_tensors(oq):
     x = torch.zeros((2, 64), dtype=torch.int16)
     with pytest.raises(oq.OQError):
         oq.oq_quant_act(x, None, oq.OQ_A8)
+
+
+def test_tiled_gemm_rejects_operands_beyond_32bit_offsets(oq):
+    # the tiled FP6 GEMM addresses each operand plane with 32-bit offsets; a
+    # plane of 4 GiB or more is refused during validation (nothing launched)
+    lib = oq._binding.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    M, K, N = 1 << 22, 1536, 256          # oq_tiled_bytes(M, K) = 4.5 GiB
+    assert oq.oq_tiled_bytes(M, K) >= 1 << 32
+    rc = lib.oq_gemm_w4a4(oq.OQ_A4 | oq.OQ_TILED, fake, 0, fake, M, K, fake, fake, N, 64, None, None, None,
+                          fake, N, None, 0, None)
+    assert rc == oq.OQ_ERR_UNSUPPORTED and "4 GiB" in _err(oq)
+    rc = lib.oq_gemm_w4a4(oq.OQ_A4 | oq.OQ_TILED, fake, 0, fake, 256, K, fake, fake, M, 64, None, None, None,
+                          fake, M, None, 0, None)
+    assert rc == oq.OQ_ERR_UNSUPPORTED
+    rc = lib.oq_gemm_w4a4_asym(oq.OQ_A4 | oq.OQ_TILED, fake, fake, fake, M, K, fake, fake, fake, N, None, None,
+                               None, fake, N, None)
+    assert rc == oq.OQ_ERR_UNSUPPORTED

@@ -254,11 +254,10 @@ def test_dense32_mx_every_element(oq):
 def test_weight_dense32(oq):
     say("case weight dense32")
     wl = WL.make_workload(5, M=4, K=512, Ns=(48,))
-    Tw = to_dev(wl.t_wgt)
-    rot = oq.Rotation.dense32(to_dev(wl.t_act_bits), Tw)
+    rot = oq.Rotation.dense32(to_dev(wl.t_act_bits))
     out = oq.oq_quant_weight(to_dev(wl.weights[0]), rot, oq.OQ_W_MXFP4, 32)
     torch.cuda.synchronize()
-    ref = OL.prepare_weight_dense32(wl.weights[0], wl.t_wgt)
+    ref = OL.prepare_weight_dense32(wl.weights[0], wl.t_act_bits)
     sb = to_host(out["scales"])
     ok_blocks = ~ref["block_flags"]
     assert np.all((sb == ref["scale_bytes"]) | ~ok_blocks)

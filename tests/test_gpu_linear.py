@@ -49,7 +49,7 @@ def _gpu_layer(oq, wl, n_index=0, rows=None):
                                     mean=act["mean"], w1=w1)
         y = oq.oq_linear_fused(x, rot, s.center, s.afmt, wq["codes"], wq["scales"], N, s.group, w1=w1)
     else:
-        rot = oq.Rotation.dense32(to_dev(wl.t_act_bits), to_dev(wl.t_wgt))
+        rot = oq.Rotation.dense32(to_dev(wl.t_act_bits))
         wq = oq.oq_quant_weight(to_dev(W), rot, oq.OQ_W_MXFP4, 32)
         act = oq.oq_quant_act(x, rot, oq.OQ_MXFP4)
         y_sep = oq.oq_gemm_w4a4(oq.OQ_MXFP4, act["codes"], act["e8m0"], wq["codes"], wq["scales"], N, 32)
@@ -91,7 +91,7 @@ def _check_layer(wl, g, rows=None, wrows=None):
         frac = check_output(g["y"], y_ref, S, wl.K // s.group, "layer output")
     else:
         wsel = slice(None) if wrows is None else wrows
-        wref = OL.prepare_weight_dense32(W[wsel], wl.t_wgt)
+        wref = OL.prepare_weight_dense32(W[wsel], wl.t_act_bits)
         flags = wref["flags"] | np.repeat(wref["block_flags"], 32, axis=1)
         check_codes(OQ.unpack_nibbles(g["wcodes"][wsel]), wref["codes"], flags, "mx weight codes")
         aref = OL.activations_mx(xb, wl.t_act_bits)
@@ -131,5 +131,5 @@ def test_layer_full_size_sampled(oq, cid, n_index):
 
 def _check_layer_sampled(wl, g, rows, wrows):
     sub = WL.LinearWorkload(wl.spec, len(rows), wl.K, wl.Ns, wl.x_bits[rows], wl.perm, wl.signs,
-                            wl.t_act_bits, wl.t_wgt, wl.weights)
+                            wl.t_act_bits, wl.weights)
     return _check_layer(sub, g, rows=None, wrows=wrows)

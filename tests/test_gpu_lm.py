@@ -5,9 +5,8 @@ the float16 weight prepack, and the float16-MFMA GEMM, against the oracle
 
 Rules:
   * codes: bit-exact except elements the oracle flags within 1e-6 of a
-    threshold; rho: bit-exact except tokens whose float64 RMS lies within
-    1e-12 of a float32 midpoint (none are expected; such tokens are left out
-    of the code comparison);
+    threshold; rho: bit-exact on every token (the kernel rounds the exact sum
+    of squares, recomputing it in integers near a float32 midpoint);
   * tiled levels: equal to the stored level of the canonical code, bit for bit;
   * W16: bit-exact against RN16(s q);
   * outputs: |y - y*| <= ulp_bf16(y*) + (K + 3) 2^-24 S, y* the oracle's
@@ -63,8 +62,7 @@ def _oracle_act(xb, perm, signs, h, center, thr):
         x32 = OQ.center(x32, m)
     v = OR.rpbh_fp32(x32, perm, signs, h) if perm is not None else x32
     q, rho = LM.quant_token_lm(v, thr)
-    return {"v": v, "codes": q, "rho": rho, "mean": m, "flags": LM.boundary_flags(v, rho, thr),
-            "rho_flag": LM.rms_near_midpoint(v)}
+    return {"v": v, "codes": q, "rho": rho, "mean": m, "flags": LM.boundary_flags(v, rho, thr)}
 
 
 def _unpack(codes, bits):
@@ -101,19 +99,44 @@ def test_lm_activations(oq, M, K, h, rounds, center, bits):
     tiled = oq.oq_quant_act_lm(to_dev(xb), rot, bits, c16_d, thr_d, tiled=True, center=center)
     torch.cuda.synchronize()
     ref = _oracle_act(xb, perm, signs, h, center, thr)
-    ok = ~ref["rho_flag"]
     rho = to_host(canon["scale"])
-    np.testing.assert_array_equal(rho[ok], ref["rho"][ok])
+    np.testing.assert_array_equal(rho, ref["rho"])
     np.testing.assert_array_equal(to_host(tiled["scale"]), rho)
     if center:
         np.testing.assert_array_equal(to_host(canon["mean"]), ref["mean"])
     codes = _unpack(to_host(canon["codes"]), bits)
-    n = check_codes(codes[ok], ref["codes"][ok], ref["flags"][ok], "lm codes")
+    n = check_codes(codes, ref["codes"], ref["flags"], "lm codes")
     if M > 2:
         assert np.all(codes[1] == (1 << (bits - 1)) - 1)  # zero token: the lower central level
     t = untile_f16(to_host(tiled["codes"]).view(np.uint16), M, K)[:M]
     np.testing.assert_array_equal(t, c16.view(np.uint16)[codes])
     say("  flagged mismatches", n)
+
+
+def test_lm_rho_at_float32_midpoints(oq):
+    """Tokens whose RMS sits at or within 2^-48 of the float32 midpoint
+    1 + 2^-24 (no rotation, d = 64): rho must be the oracle's RN32(sqrt(RN64(S)
+    / d)) of the exact sum S, which the kernel recomputes in integers there.
+    The third token's exact S lies above the midpoint's, but RN64(S) is the
+    midpoint's, so rho is 1; the fourth rounds up; the rest are scaled copies
+    (by powers of two, which keep every square exact) and an ordinary token."""
+    say("case lm rho midpoints")
+    base = [1.0] * 60 + [2.0, 2.0 ** -9, 2.0 ** -9]
+    toks = [base + [c] for c in (2.0 ** -21, 1.5 * 2.0 ** -22, 2.0 ** -21 * (1 + 2.0 ** -7), 1.5 * 2.0 ** -21)]
+    toks = toks + [[v * 2.0 ** k for v in t] for t in toks for k in (-20, 17)]
+    x = np.array(toks, dtype=np.float32)
+    assert np.array_equal(WL.bf16_bits_to_f32(WL.f32_to_bf16_bits(x)), x)  # every coordinate is a bfloat16 value
+    x = np.concatenate([x, np.random.default_rng(5).standard_normal((1, 64)).astype(np.float32)])
+    xb = WL.f32_to_bf16_bits(x)
+    c16, thr, c16_d, thr_d = _tables(oq, 64, 4)
+    out = oq.oq_quant_act_lm(to_dev(xb), None, 4, c16_d, thr_d, tiled=False)
+    torch.cuda.synchronize()
+    ref = _oracle_act(xb, None, None, 0, False, thr)
+    rho = to_host(out["scale"])
+    np.testing.assert_array_equal(rho, ref["rho"])
+    assert rho[0] == np.float32(1.0) and rho[2] == np.float32(1.0)
+    assert rho[3] == np.float32(1.0 + 2.0 ** -23)
+    check_codes(_unpack(to_host(out["codes"]), 4), ref["codes"], ref["flags"], "lm codes at rho midpoints")
 
 
 @pytest.mark.parametrize("N,K,group", [(70, 256, 64), (256, 1024, 128), (33, 96, 32)])
@@ -225,9 +248,8 @@ def test_lm_layer_full_size(oq, bits, Ns):
     ref = _oracle_act(wl.x_bits[rows], wl.perm, wl.signs, wl.spec.block, False, thr)
     codes = _unpack(to_host(canon["codes"])[rows], bits)
     rho = to_host(canon["scale"])[rows]
-    ok = ~ref["rho_flag"]
-    np.testing.assert_array_equal(rho[ok], ref["rho"][ok])
-    check_codes(codes[ok], ref["codes"][ok], ref["flags"][ok], "lm full-size codes")
+    np.testing.assert_array_equal(rho, ref["rho"])
+    check_codes(codes, ref["codes"], ref["flags"], "lm full-size codes")
     y_ref, S = LM.linear_lm(codes, rho, c16, LM.weights_f16(q, s, 64))
     frac = check_output(to_host(y)[rows], y_ref, S, K, "lm full-size output")
     say("  within 1 bf16 ulp:", frac)

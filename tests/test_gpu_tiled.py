@@ -91,8 +91,8 @@ GEMM_CASES = [
     (513, 96, 640, 6, True, False),
     (31, 32, 64, 4, False, True),
     (1, 256, 128, 6, False, False),
-    # more 256 x 256 tiles than CUs: the persistent kernel gives some
-    # workgroups two tiles (the second case has 10 groups per tile, 2 mod 4)
+    # more 256 x 256 tiles than CUs: more than one round of workgroups
+    # (the second case has 10 groups per tile, 2 mod 4)
     (4352, 4096, 512, 4, False, False),
     (4352, 4096, 640, 4, True, True),
 ]

@@ -88,7 +88,7 @@ def test_tiled_mx_gemm(oq, M, N, K, bias):
 def test_tiled_mx_layer(oq, M, N):
     say("case tiled mx layer", M, N)
     wl = WL.make_workload(5, M=M, K=1024, Ns=(N,))
-    rot = oq.Rotation.dense32(to_dev(wl.t_act_bits), to_dev(wl.t_wgt))
+    rot = oq.Rotation.dense32(to_dev(wl.t_act_bits))
     wq = oq.oq_quant_weight(to_dev(wl.weights[0]), rot, oq.OQ_W_MXFP4, 32)
     wt = oq.oq_prepack_mx(wq["codes"], wq["scales"], N, 1024)
     x = to_dev(wl.x_bits)
