@@ -61,3 +61,16 @@ def test_tile_mx_placement():
     m = row_mask_mx(R, K).reshape(Rp // 32, G, 2, 32, 16)
     assert m[1, :, :, 7].all() and not m[1, :, :, 8].any()
 
+
+
+def test_layout_readers_invert_the_writers():
+    from tiling import tile, tile_mx, untile, untile_mx
+    rng = np.random.default_rng(21)
+    q = rng.integers(-7, 8, size=(70, 256))
+    np.testing.assert_array_equal(untile(tile(q), 70, 256), q)
+    c = rng.integers(0, 256, size=(45, 128)).astype(np.uint8)
+    e = rng.integers(0, 256, size=(45, 8)).astype(np.uint8)
+    tc, ts = tile_mx(c, e)
+    c2, e2 = untile_mx(tc, ts, 45, 256)
+    np.testing.assert_array_equal(c2, c)
+    np.testing.assert_array_equal(e2, e)

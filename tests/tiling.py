@@ -154,3 +154,38 @@ def tile_values(vals: np.ndarray) -> np.ndarray:
     out[:, :, :1024] = st[..., :16].reshape(Rp // 32, G, 1024)
     out[:, :, 1024:] = st[..., 16:].reshape(Rp // 32, G, 512)
     return out.reshape(-1)
+
+
+# ------------------------------------------------------------- layout readers
+def untile(buf: np.ndarray, R: int, K: int) -> np.ndarray:
+    """Tiled FP6 bytes (one plane) -> int codes [R, K]: the inverse of tile(),
+    decoding each 6-bit field as E2M3 (sign bit 5, exponent bits 4..3 with
+    bias 1, mantissa bits 2..0); every field must hold an integer value."""
+    Rp = (R + 31) // 32 * 32
+    G = K // 64
+    b = np.asarray(buf).view(np.uint8)[: Rp // 32 * G * 1536].reshape(Rp // 32, G, 1536)
+    st = np.zeros((Rp // 32, G, 2, 32, 24), dtype=np.uint8)            # [rb, kg, h, r, 24]
+    st[..., :16] = b[:, :, :1024].reshape(Rp // 32, G, 2, 32, 16)
+    st[..., 16:] = b[:, :, 1024:].reshape(Rp // 32, G, 2, 32, 8)
+    bits = np.unpackbits(st, axis=-1, bitorder="little")                # [.., 192]
+    fields = bits.reshape(st.shape[:-1] + (32, 6)).astype(np.int64)
+    f = np.zeros(fields.shape[:-1], dtype=np.int64)
+    for k in range(6):
+        f |= fields[..., k] << k
+    mag = E2M3_MAGNITUDES[f & 0x1F]
+    val = np.where(f & 0x20, -mag, mag)
+    assert np.all(val == np.rint(val)), "non-integer FP6 field"
+    codes = val.astype(np.int64).transpose(0, 3, 1, 2, 4).reshape(Rp, K)  # [rb, r, kg, h, j]
+    return codes[:R]
+
+
+def untile_mx(buf: np.ndarray, sbuf: np.ndarray, R: int, K: int):
+    """Tiled MXFP4 codes and scale words -> (row-major code bytes [R, K/2],
+    E8M0 bytes [R, K/32]): the inverse of tile_mx()."""
+    Rp = (R + 31) // 32 * 32
+    G = K // 64
+    t = np.asarray(buf).view(np.uint8)[: Rp * K // 2].reshape(Rp // 32, G, 2, 32, 16)
+    codes = t.transpose(0, 3, 1, 2, 4).reshape(Rp, K // 2)
+    sc = np.asarray(sbuf).view(np.uint8)[: Rp * K // 32].reshape(K // 128, Rp, 4)
+    e8m0 = sc.transpose(1, 0, 2).reshape(Rp, K // 32)
+    return codes[:R], e8m0[:R]
