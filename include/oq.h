@@ -274,6 +274,29 @@ int oq_linear_fused(const uint16_t *x, int64_t M, int32_t K, int64_t ldx,
                     void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * oq_linear_fused_noalloc -- oq_linear_fused for callers that cannot allocate
+ * device memory or pass a workspace: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  Same arguments, formats
+ * and result as oq_linear_fused (bit for bit), without ws / ws_bytes: the
+ * codes, scales and means go to a static scratch array of
+ * OQ_NOALLOC_SCRATCH_BYTES (32 MiB) that the library holds on every GPU it
+ * runs on until the process ends (its device address is looked up once per
+ * device, on the first call there).  A layer whose
+ * oq_workspace_bytes(OQ_OP_LINEAR, M, K, N, afmt) exceeds that size fails
+ * with OQ_ERR_WORKSPACE before anything is enqueued.  The call allocates
+ * nothing.  Every call on one GPU shares that GPU's scratch, which keeps the
+ * last call's contents (nothing in it needs to start at zero): calls that
+ * overlap on one GPU (several streams or host threads at once) race; serialise
+ * them, for instance on one stream.
+ */
+#define OQ_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int oq_linear_fused_noalloc(const uint16_t *x, int64_t M, int32_t K, int64_t ldx,
+                            const oq_rot *rot, int center, int afmt,
+                            const uint8_t *w, const void *w_scale, int32_t N, int32_t group,
+                            const float *w1, const float *bias, uint16_t *y, int64_t ldy,
+                            hipStream_t stream);
+
+/*
  * oq_prepack_w4 -- repack canonical INT4 weights (oq_quant_weight OQ_W4
  * output: codes [N][K/2], scales float32 [N][K/64]) into the tiled FP6
  * layout for OQ_TILED GEMMs.  Values are unchanged (every INT4 code is an

@@ -59,6 +59,8 @@ def _load():
         "oq_gemm_w4a8": ([vp, i64, vp, i64, i32, vp, vp, i32, i32, vp, vp, vp, vp, i64, vp, sz, vp], ctypes.c_int),
         "oq_gemm_w4a4": ([ctypes.c_int, vp, i64, vp, i64, i32, vp, vp, i32, i32, vp, vp, vp, vp, i64, vp, sz, vp], ctypes.c_int),
         "oq_linear_fused": ([vp, i64, i32, i64, vp, ctypes.c_int, ctypes.c_int, vp, vp, i32, i32, vp, vp, vp, i64, vp, sz, vp], ctypes.c_int),
+        "oq_linear_fused_noalloc": ([vp, i64, i32, i64, vp, ctypes.c_int, ctypes.c_int, vp, vp, i32, i32, vp, vp, vp,
+                                     i64, vp], ctypes.c_int),
         "oq_workspace_bytes": ([ctypes.c_int, i64, i32, i32, ctypes.c_int], sz),
         "oq_tiled_bytes": ([i64, i32], sz),
         "oq_prepack_w4": ([vp, vp, i32, i32, i32, vp, vp, vp], ctypes.c_int),
@@ -91,7 +93,8 @@ EXPORTED = ("oq_last_error", "oq_center", "oq_rotate", "oq_quant_act", "oq_quant
             "oq_gemm_w4a8", "oq_gemm_w4a4", "oq_linear_fused", "oq_workspace_bytes", "oq_tiled_bytes",
             "oq_prepack_w4", "oq_tiled_mx_bytes", "oq_prepack_mx", "oq_lloyd_max_levels", "oq_lloyd_max_tables",
             "oq_tiled_f16_bytes", "oq_quant_act_lm", "oq_prepack_w16", "oq_gemm_lm", "oq_quant_weight_asym",
-            "oq_prepack_w4_asym", "oq_quant_act_gsum", "oq_gemm_w4a4_asym", "oq_kron_plan")
+            "oq_prepack_w4_asym", "oq_quant_act_gsum", "oq_gemm_w4a4_asym", "oq_kron_plan",
+            "oq_linear_fused_noalloc")
 
 
 def lib():
@@ -392,6 +395,23 @@ def oq_linear_fused(x, rot: Optional[Rotation], center: bool, afmt: int, w, w_sc
         ws = torch.empty(max(1, oq_workspace_bytes(OQ_OP_LINEAR, M, K, N, afmt)), dtype=torch.uint8, device=dev)
     _check(_lib.oq_linear_fused(_p(x), M, K, x.stride(0), _rref(rot), int(center), afmt, _p(w), _p(w_scale), N,
                                 group, _p(w1), _p(bias), _p(y), y.stride(0), _p(ws), ws.numel(), _stream()))
+    return y
+
+
+OQ_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def oq_linear_fused_noalloc(x, rot: Optional[Rotation], center: bool, afmt: int, w, w_scale, N: int, group: int,
+                            w1=None, bias=None, y=None):
+    """oq_linear_fused without a workspace: the library's static per-GPU
+    scratch holds the codes (calls on one GPU must not overlap)."""
+    x = _bits16(x)
+    M, K = x.shape
+    dev = _dev(x)
+    _epilogue_args(M, N, None, w1, bias)
+    y = _out_y(y, M, N, dev)
+    _check(_lib.oq_linear_fused_noalloc(_p(x), M, K, x.stride(0), _rref(rot), int(center), afmt, _p(w), _p(w_scale),
+                                        N, group, _p(w1), _p(bias), _p(y), y.stride(0), _stream()))
     return y
 
 

@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "oq_internal.h"
 
@@ -602,6 +603,35 @@ int linear_fused_impl(const char *fn, const uint16_t *x, int64_t M, int32_t K, i
 }
 
 
+// Scratch of oq_linear_fused_noalloc: one copy per GPU, held by the loaded
+// code object until the process ends.  Host code uses the device address that
+// hipGetSymbolAddress returns for the current device, never the array's name.
+constexpr size_t NOALLOC_BYTES = OQ_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[NOALLOC_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[MAX_DEVICES] = {};
+
+// Device address of the current device's scratch, looked up on the first
+// call on that device.
+int scratch_for_current_device(const char *fn, void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, fn);
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(OQ_ERR_UNSUPPORTED, "%s: device %d beyond %d", fn, dev, MAX_DEVICES);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, fn);
+    if (!p) return fail(OQ_ERR_HIP, "%s: no device address for the scratch array", fn);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return OQ_OK;
+}
+
 }  // namespace
 }  // namespace oq
 
@@ -612,6 +642,22 @@ int oq_linear_fused(const uint16_t *x, int64_t M, int32_t K, int64_t ldx, const 
                     uint16_t *y, int64_t ldy, void *ws, size_t ws_bytes, hipStream_t stream) {
   return linear_fused_impl("oq_linear_fused", x, M, K, ldx, rot, center, afmt, w, w_scale, N, group, w1, bias, y,
                            ldy, ws, ws_bytes, stream);
+}
+
+int oq_linear_fused_noalloc(const uint16_t *x, int64_t M, int32_t K, int64_t ldx, const oq_rot *rot, int center,
+                            int afmt, const uint8_t *w, const void *w_scale, int32_t N, int32_t group,
+                            const float *w1, const float *bias, uint16_t *y, int64_t ldy, hipStream_t stream) {
+  const char *fn = "oq_linear_fused_noalloc";
+  if (M < 0 || K <= 0) return fail(OQ_ERR_INVALID_ARG, "%s: bad M or K", fn);
+  const size_t need = oq_workspace_bytes(OQ_OP_LINEAR, M, K, N, afmt);
+  if (need > NOALLOC_BYTES)
+    return fail(OQ_ERR_WORKSPACE, "%s: this layer needs %zu bytes of scratch; the static scratch holds %zu (use "
+                "oq_linear_fused with a workspace)", fn, need, NOALLOC_BYTES);
+  void *ws = nullptr;
+  int rc = scratch_for_current_device(fn, &ws);
+  if (rc) return rc;
+  return linear_fused_impl(fn, x, M, K, ldx, rot, center, afmt, w, w_scale, N, group, w1, bias, y, ldy, ws,
+                           NOALLOC_BYTES, stream);
 }
 
 // ------------------------------------------------------------ Lloyd-Max path
