@@ -499,7 +499,99 @@ def _cpu_baseline(WL, cid=2, target_s=12.0):
     return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": threads if threads else cores, "kind": "oracle",
             "sample": f"{rows} of {wl.M} tokens of the 4096x3072 W4A4 workload through rotate+quantize and both "
                       f"linears (3072 and 12288 outputs), {dt:.1f} s wall on {cores} host cores "
-                      f"(BLAS threads {threads})"}
+                      f"(BLAS threads {threads})",
+            "per_config": _cpu_config_table(WL)}
+
+
+def _measured_denominators(torch, oq):
+    """Roofline denominators measured on this device at its current clock:
+    HBM as a plain device-to-device copy of 1 GiB (bytes read + written per
+    second), and the sustained rate of each matrix-core instruction the
+    kernels issue (oq_probe_mfma: independent instructions on every SIMD,
+    nothing else).  Best of three timed launches after one untimed."""
+    out = {}
+    n = 1 << 30
+    a = torch.empty(n // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, 2.0 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    out["hbm_copy_GBs"] = round(best, 1)
+    del a, b
+    sink = None
+    for name, kind, iters in (("fp6", oq.OQ_PROBE_FP6, 2000), ("fp4", oq.OQ_PROBE_FP4, 2000),
+                              ("int8", oq.OQ_PROBE_I8, 2000), ("f16", oq.OQ_PROBE_F16, 1000),
+                              ("bf16", oq.OQ_PROBE_BF16, 1000)):
+        ops, sink = oq.oq_probe_mfma(kind, iters, sink)
+        torch.cuda.synchronize()
+        best = 0.0
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            oq.oq_probe_mfma(kind, iters, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            best = max(best, ops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+        out[f"mfma_{name}_TFLOPs"] = round(best, 1)
+    out["note"] = ("hbm: 1 GiB torch device copy, 2 bytes moved per byte copied; mfma_*: oq_probe_mfma, "
+                   "32x32 instructions of each type back to back on every SIMD (int8 in TOPS)")
+    return out
+
+
+def _cpu_config_table(WL, tokens=64, outputs=512):
+    """The oracle per workload, split into rotate+quantize and GEMM+epilogue:
+    `tokens` tokens (all 256 of the 256-token workload) against the first
+    `outputs` rows of each weight (the oracle's GEMM time is linear in the
+    output count; weight preparation is offline and not timed).  The 256-token
+    W4A8 workload is also run with the BLAS pool held to one thread."""
+    from oracle import linear as OL
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:
+        threadpool_limits = None
+    table = {}
+
+    def run(cid, nt, no):
+        wl = WL.make_workload(cid)
+        s = wl.spec
+        nt = min(nt, wl.M)
+        xb = wl.x_bits[:nt]
+        if s.rot == "rpbh":
+            wps = [OL.prepare_weight_rpbh(W[:no], wl.perm, wl.signs, s.block, s.group) for W in wl.weights]
+            t0 = time.perf_counter()
+            act = OL.activations_int(xb, wl.perm, wl.signs, s.block, s.afmt, s.center)
+            t1 = time.perf_counter()
+            for wp in wps:
+                OL.linear_int(act, wp, s.group)
+        else:
+            wps = [OL.prepare_weight_dense32(W[:no], wl.t_act_bits) for W in wl.weights]
+            t0 = time.perf_counter()
+            act = OL.activations_mx(xb, wl.t_act_bits)
+            t1 = time.perf_counter()
+            for wp in wps:
+                OL.linear_mx(act, wp)
+        t2 = time.perf_counter()
+        ops = 2.0 * nt * wl.K * no * len(wl.weights)
+        return s.name, {"tokens": nt, "outputs_per_linear": no, "linears": len(wl.weights),
+                        "rotate_quant_us_per_token": round((t1 - t0) / nt * 1e6, 2),
+                        "gemm_epilogue_us_per_token": round((t2 - t1) / nt * 1e6, 2),
+                        "gemm_epilogue_TOPS": round(ops / max(t2 - t1, 1e-9) / 1e12, 5)}
+
+    for cid in (1, 2, 3, 4, 5):
+        name, e = run(cid, 256 if cid == 1 else tokens, outputs if cid != 1 else 1024)
+        table[name] = e
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            name, e = run(1, 256, 1024)
+        table[name + "_1thread"] = e
+    return table
 
 
 def main():
@@ -575,6 +667,11 @@ def main():
     }
 
     if not args.only_step:
+        meas = _measured_denominators(torch, oq)
+        result["measured_peaks"] = meas
+        result["roofline"]["frac_of_measured_int8"] = round(achieved / meas["mfma_int8_TFLOPs"], 4)
+        result["roofline"]["frac_of_measured_fp6"] = round(achieved / meas["mfma_fp6_TFLOPs"], 4)
+        result["rotate_quant_frac_of_measured_hbm"] = round(rq_bytes / (rq_us * 1e-6) / 1e9 / meas["hbm_copy_GBs"], 4)
         nf, fm, fv = _time_fused(torch, oq, st, max(20, args.steps // 2), 5)
         result["linear_fused_us"] = {"d_out": nf, "mean": round(fm * 1e3, 3), **_dist_us(fv)}
         pm, pv = _time_pctl(torch, oq, st, max(20, args.steps // 2), 5)

@@ -482,6 +482,28 @@ int oq_gemm_w4a4_asym(int afmt, const uint8_t *qa, const float *a_scale, const u
  */
 int oq_kron_plan(int32_t n, int32_t *m, int32_t *block, int32_t *n_pad);
 
+/*
+ * oq_probe_mfma -- measurement helper, not part of the layer: the rate one
+ * matrix-core instruction sustains on the calling device at its current clock
+ * (a roofline denominator beside the published dense peak, which assumes the
+ * top clock).  Launches, on `stream`, two workgroups of four wavefronts per
+ * CU that each issue iters x 32 independent instructions of the kind
+ * (four accumulator chains, operands in registers, no memory traffic), and
+ * returns in *ops the operation count of that launch (2 M N K per
+ * instruction); the caller times the launch (for instance with events on the
+ * stream) and divides.  sink: device float32 buffer of at least
+ * oq_probe_sink_elems() elements (written, values meaningless).  Kinds:
+ * OQ_PROBE_FP6 and OQ_PROBE_FP4 (v_mfma_scale_f32_32x32x64_f8f6f4 with both
+ * operands FP6 E2M3 / FP4 E2M1, unit scales: the instructions of the tiled
+ * INT4 and MXFP4 GEMMs), OQ_PROBE_FP8 (the same instruction on FP8 E4M3),
+ * OQ_PROBE_I8 (v_mfma_i32_32x32x32_i8), OQ_PROBE_BF16, OQ_PROBE_F16
+ * (v_mfma_f32_32x32x16_bf16 / _f16).  1 <= iters <= 2^20 (a launch of 2^20
+ * iterations runs for about a second), else OQ_ERR_INVALID_ARG.
+ */
+enum { OQ_PROBE_FP6 = 1, OQ_PROBE_FP4 = 2, OQ_PROBE_FP8 = 3, OQ_PROBE_I8 = 4, OQ_PROBE_BF16 = 5, OQ_PROBE_F16 = 6 };
+int oq_probe_mfma(int kind, int32_t iters, float *sink, double *ops, hipStream_t stream);
+size_t oq_probe_sink_elems(void);
+
 enum { OQ_OP_GEMM_W4A8 = 1, OQ_OP_GEMM_W4A4 = 2, OQ_OP_LINEAR = 3, OQ_OP_GEMM_LM = 4 };
 
 /* Scratch bytes a call needs (0 if none).  Pure host function.  For

@@ -59,6 +59,8 @@ def _load():
         "oq_gemm_w4a8": ([vp, i64, vp, i64, i32, vp, vp, i32, i32, vp, vp, vp, vp, i64, vp, sz, vp], ctypes.c_int),
         "oq_gemm_w4a4": ([ctypes.c_int, vp, i64, vp, i64, i32, vp, vp, i32, i32, vp, vp, vp, vp, i64, vp, sz, vp], ctypes.c_int),
         "oq_linear_fused": ([vp, i64, i32, i64, vp, ctypes.c_int, ctypes.c_int, vp, vp, i32, i32, vp, vp, vp, i64, vp, sz, vp], ctypes.c_int),
+        "oq_probe_mfma": ([ctypes.c_int, i32, vp, ctypes.POINTER(ctypes.c_double), vp], ctypes.c_int),
+        "oq_probe_sink_elems": ([], sz),
         "oq_linear_fused_noalloc": ([vp, i64, i32, i64, vp, ctypes.c_int, ctypes.c_int, vp, vp, i32, i32, vp, vp, vp,
                                      i64, vp], ctypes.c_int),
         "oq_workspace_bytes": ([ctypes.c_int, i64, i32, i32, ctypes.c_int], sz),
@@ -94,7 +96,7 @@ EXPORTED = ("oq_last_error", "oq_center", "oq_rotate", "oq_quant_act", "oq_quant
             "oq_prepack_w4", "oq_tiled_mx_bytes", "oq_prepack_mx", "oq_lloyd_max_levels", "oq_lloyd_max_tables",
             "oq_tiled_f16_bytes", "oq_quant_act_lm", "oq_prepack_w16", "oq_gemm_lm", "oq_quant_weight_asym",
             "oq_prepack_w4_asym", "oq_quant_act_gsum", "oq_gemm_w4a4_asym", "oq_kron_plan",
-            "oq_linear_fused_noalloc")
+            "oq_linear_fused_noalloc", "oq_probe_mfma", "oq_probe_sink_elems")
 
 
 def lib():
@@ -396,6 +398,20 @@ def oq_linear_fused(x, rot: Optional[Rotation], center: bool, afmt: int, w, w_sc
     _check(_lib.oq_linear_fused(_p(x), M, K, x.stride(0), _rref(rot), int(center), afmt, _p(w), _p(w_scale), N,
                                 group, _p(w1), _p(bias), _p(y), y.stride(0), _p(ws), ws.numel(), _stream()))
     return y
+
+
+OQ_PROBE_FP6, OQ_PROBE_FP4, OQ_PROBE_FP8, OQ_PROBE_I8, OQ_PROBE_BF16, OQ_PROBE_F16 = 1, 2, 3, 4, 5, 6
+
+
+def oq_probe_mfma(kind: int, iters: int, sink=None):
+    """Launches the matrix-core rate probe on the current stream; returns
+    (operation count of the launch, sink).  The caller times it."""
+    if sink is None:
+        sink = torch.empty(int(_lib.oq_probe_sink_elems()), dtype=torch.float32, device="cuda")
+    _need(sink, 4 * int(_lib.oq_probe_sink_elems()), "sink", _F32)
+    ops = ctypes.c_double(0.0)
+    _check(_lib.oq_probe_mfma(kind, iters, _p(sink), ctypes.byref(ops), _stream()))
+    return ops.value, sink
 
 
 OQ_NOALLOC_SCRATCH_BYTES = 32 << 20

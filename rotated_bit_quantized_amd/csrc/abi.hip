@@ -865,6 +865,18 @@ int oq_gemm_w4a4_asym(int afmt, const uint8_t *qa, const float *a_scale, const u
                     fn);
 }
 
+// ------------------------------------------------------ measurement helper
+size_t oq_probe_sink_elems(void) { return (size_t)probe_blocks() * 256; }
+
+int oq_probe_mfma(int kind, int32_t iters, float *sink, double *ops, hipStream_t stream) {
+  const char *fn = "oq_probe_mfma";
+  if (kind < OQ_PROBE_FP6 || kind > OQ_PROBE_F16) return fail(OQ_ERR_INVALID_ARG, "%s: unknown kind %d", fn, kind);
+  if (iters < 1 || iters > (1 << 20)) return fail(OQ_ERR_INVALID_ARG, "%s: iters=%d must lie in [1, 2^20]", fn, iters);
+  if (!sink || !ops) return fail(OQ_ERR_INVALID_ARG, "%s: NULL sink or ops", fn);
+  g_err[0] = 0;
+  return hip_status(launch_mfma_probe(kind, iters, sink, stream, ops), fn);
+}
+
 // ---------------------------------------------------------- Kronecker rotation
 int oq_kron_plan(int32_t n, int32_t *m, int32_t *block, int32_t *n_pad) {
   if (n < 1 || n > 16384) return fail(OQ_ERR_UNSUPPORTED, "oq_kron_plan: n=%d must lie in [1, 16384]", n);

@@ -669,17 +669,6 @@ hipError_t launch_v2_shape(const uint8_t *A, int64_t plane, const float *a_scale
                                                                              corr);
 }
 
-// Compute units of the current device (one workgroup of the v2 kernel fills a CU).
-int device_cus() {
-  static std::atomic<int> cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int v = cached[dev].load(std::memory_order_relaxed);
-  if (v > 0) return v;
-  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-  cached[dev].store(v, std::memory_order_relaxed);
-  return v;
-}
 
 enum class Shape { W8_256x256, W8_256x192, W4_256x128, W4_128x192 };
 
@@ -728,6 +717,18 @@ hipError_t launch_v2(const uint8_t *A, const float *a_scale, int64_t M, int K, c
 }
 
 }  // namespace
+
+// Compute units of the current device (one workgroup of the 8-wave kernels fills a CU).
+int device_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+  cached[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
 
 hipError_t launch_gemm_fp6(const uint8_t *A, int planes, const float *a_scale, int64_t M, int K, const uint8_t *W,
                            const float *wst, int N, const float *mean, const float *w1, const float *bias,

@@ -257,4 +257,11 @@ hipError_t launch_weight_rpbh_asym(const float *w, int N, int K, int64_t ldw, co
 hipError_t launch_weight_dense32(const float *w, int N, int K, int64_t ldw, const uint16_t *mats,
                                  uint8_t *codes, uint8_t *e8m0, float *w1, hipStream_t stream);
 
+// Compute units of the current device (cached per device).
+int device_cus();
+// Matrix-core rate probe (oq_probe_mfma): launches it and returns the number
+// of operations (2 M N K per instruction) one launch performs in *ops.
+hipError_t launch_mfma_probe(int kind, int iters, float *sink, hipStream_t stream, double *ops);
+int probe_blocks();
+
 }  // namespace oq
