@@ -604,6 +604,11 @@ def main():
     ap.add_argument("--only-step", action="store_true", help="time the step only (for profilers)")
     ap.add_argument("--copy-ref", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration under a profiler)")
+    ap.add_argument("--profile-config", type=int, default=0, metavar="CID",
+                    help="run only workload CID's step, launched eagerly (for profilers), and print its times")
+    ap.add_argument("--profile-leg", choices=["lm4", "lm8", "asym", "kron"], default=None,
+                    help="run only one side leg (Lloyd-Max 4/8-bit, asymmetric weights, Kronecker rotation) "
+                         "and print its times (for profilers)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU; --gpus must be 1 (the layer would shard by "
@@ -615,6 +620,20 @@ def main():
     import workloads as WL
 
     torch.cuda.set_device(0)
+    if args.profile_leg:
+        leg = args.profile_leg
+        r = (_time_lm(torch, oq, WL, int(leg[2:])) if leg.startswith("lm") else
+             _time_asym(torch, oq, WL) if leg == "asym" else _time_kron(torch, oq, WL))
+        print(json.dumps({"leg": leg, **r}), flush=True)
+        return
+    if args.profile_config:
+        st = _setup(torch, oq, WL, args.profile_config)
+        ms_e, _, per_c, _ = _time(torch, oq, st, args.steps, args.warmup)
+        if args.copy_ref:
+            _copy_reference(torch)
+        print(json.dumps({"workload": st["spec"].name, "eager_ms_per_step": round(ms_e, 5),
+                          "per_launch_us": {n: round(v * 1e3, 3) for n, v in per_c.items()}}), flush=True)
+        return
     st = _setup(torch, oq, WL, 2)
     wl, s = st["wl"], st["spec"]
     M, K = wl.M, wl.K
