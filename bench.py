@@ -528,7 +528,7 @@ def _measured_denominators(torch, oq):
     sink = None
     for name, kind, iters in (("fp6", oq.OQ_PROBE_FP6, 2000), ("fp4", oq.OQ_PROBE_FP4, 2000),
                               ("int8", oq.OQ_PROBE_I8, 2000), ("f16", oq.OQ_PROBE_F16, 1000),
-                              ("bf16", oq.OQ_PROBE_BF16, 1000)):
+                              ("bf16", oq.OQ_PROBE_BF16, 1000), ("fp6_with_group_update", oq.OQ_PROBE_FP6_UPDATE, 4000)):
         ops, sink = oq.oq_probe_mfma(kind, iters, sink)
         torch.cuda.synchronize()
         best = 0.0
@@ -541,7 +541,9 @@ def _measured_denominators(torch, oq):
             best = max(best, ops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
         out[f"mfma_{name}_TFLOPs"] = round(best, 1)
     out["note"] = ("hbm: 1 GiB torch device copy, 2 bytes moved per byte copied; mfma_*: oq_probe_mfma, "
-                   "32x32 instructions of each type back to back on every SIMD (int8 in TOPS)")
+                   "32x32 instructions of each type back to back on every SIMD (int8 in TOPS); "
+                   "mfma_fp6_with_group_update: each FP6 MFMA followed by the 16 fp32 group-scale updates of "
+                   "the previous tile, the INT4 GEMM's arithmetic without memory traffic")
     return out
 
 
@@ -690,6 +692,8 @@ def main():
         result["measured_peaks"] = meas
         result["roofline"]["frac_of_measured_int8"] = round(achieved / meas["mfma_int8_TFLOPs"], 4)
         result["roofline"]["frac_of_measured_fp6"] = round(achieved / meas["mfma_fp6_TFLOPs"], 4)
+        result["roofline"]["frac_of_measured_fp6_with_group_update"] = round(
+            achieved / meas["mfma_fp6_with_group_update_TFLOPs"], 4)
         result["rotate_quant_frac_of_measured_hbm"] = round(rq_bytes / (rq_us * 1e-6) / 1e9 / meas["hbm_copy_GBs"], 4)
         nf, fm, fv = _time_fused(torch, oq, st, max(20, args.steps // 2), 5)
         result["linear_fused_us"] = {"d_out": nf, "mean": round(fm * 1e3, 3), **_dist_us(fv)}

@@ -497,10 +497,15 @@ int oq_kron_plan(int32_t n, int32_t *m, int32_t *block, int32_t *n_pad);
  * operands FP6 E2M3 / FP4 E2M1, unit scales: the instructions of the tiled
  * INT4 and MXFP4 GEMMs), OQ_PROBE_FP8 (the same instruction on FP8 E4M3),
  * OQ_PROBE_I8 (v_mfma_i32_32x32x32_i8), OQ_PROBE_BF16, OQ_PROBE_F16
- * (v_mfma_f32_32x32x16_bf16 / _f16).  1 <= iters <= 2^20 (a launch of 2^20
- * iterations runs for about a second), else OQ_ERR_INVALID_ARG.
+ * (v_mfma_f32_32x32x16_bf16 / _f16), and OQ_PROBE_FP6_UPDATE: the tiled INT4
+ * GEMM's arithmetic without memory traffic, each FP6 MFMA followed by the 16
+ * float32 group-scale updates of the previous tile (8 MFMAs per iteration and
+ * wavefront; *ops counts 2 M N K of the MFMAs), the rate the fp32 update
+ * leaves to that GEMM.  1 <= iters <= 2^20 (a launch of 2^20 iterations runs
+ * for about a second), else OQ_ERR_INVALID_ARG.
  */
-enum { OQ_PROBE_FP6 = 1, OQ_PROBE_FP4 = 2, OQ_PROBE_FP8 = 3, OQ_PROBE_I8 = 4, OQ_PROBE_BF16 = 5, OQ_PROBE_F16 = 6 };
+enum { OQ_PROBE_FP6 = 1, OQ_PROBE_FP4 = 2, OQ_PROBE_FP8 = 3, OQ_PROBE_I8 = 4, OQ_PROBE_BF16 = 5, OQ_PROBE_F16 = 6,
+       OQ_PROBE_FP6_UPDATE = 7 };
 int oq_probe_mfma(int kind, int32_t iters, float *sink, double *ops, hipStream_t stream);
 size_t oq_probe_sink_elems(void);
 

@@ -16,4 +16,5 @@ from ._binding import (  # noqa: F401
     oq_quant_weight_asym, oq_prepack_w4_asym, oq_quant_act_gsum, oq_gemm_w4a4_asym, oq_kron_plan,
     oq_linear_fused_noalloc, OQ_NOALLOC_SCRATCH_BYTES,
     oq_probe_mfma, OQ_PROBE_FP6, OQ_PROBE_FP4, OQ_PROBE_FP8, OQ_PROBE_I8, OQ_PROBE_BF16, OQ_PROBE_F16,
+    OQ_PROBE_FP6_UPDATE,
 )

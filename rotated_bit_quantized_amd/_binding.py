@@ -401,6 +401,7 @@ def oq_linear_fused(x, rot: Optional[Rotation], center: bool, afmt: int, w, w_sc
 
 
 OQ_PROBE_FP6, OQ_PROBE_FP4, OQ_PROBE_FP8, OQ_PROBE_I8, OQ_PROBE_BF16, OQ_PROBE_F16 = 1, 2, 3, 4, 5, 6
+OQ_PROBE_FP6_UPDATE = 7
 
 
 def oq_probe_mfma(kind: int, iters: int, sink=None):

@@ -870,7 +870,7 @@ size_t oq_probe_sink_elems(void) { return (size_t)probe_blocks() * 256; }
 
 int oq_probe_mfma(int kind, int32_t iters, float *sink, double *ops, hipStream_t stream) {
   const char *fn = "oq_probe_mfma";
-  if (kind < OQ_PROBE_FP6 || kind > OQ_PROBE_F16) return fail(OQ_ERR_INVALID_ARG, "%s: unknown kind %d", fn, kind);
+  if (kind < OQ_PROBE_FP6 || kind > OQ_PROBE_FP6_UPDATE) return fail(OQ_ERR_INVALID_ARG, "%s: unknown kind %d", fn, kind);
   if (iters < 1 || iters > (1 << 20)) return fail(OQ_ERR_INVALID_ARG, "%s: iters=%d must lie in [1, 2^20]", fn, iters);
   if (!sink || !ops) return fail(OQ_ERR_INVALID_ARG, "%s: NULL sink or ops", fn);
   g_err[0] = 0;

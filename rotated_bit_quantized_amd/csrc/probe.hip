@@ -21,6 +21,49 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 constexpr int PROBE_CHAINS = 4;
 constexpr int PROBE_UNROLL = 8;  // instructions per chain per loop iteration
 
+// The FP6 GEMM's own arithmetic without memory: per step one FP6 MFMA with
+// a zero accumulator (the exact group sum of a 32 x 32 tile) and the 16
+// float32 updates F += s * sum of the previous tile's result, eight tiles per
+// group, as the tiled INT4 GEMM's main loop issues them; iters groups.
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+fp6_update_probe_kernel(int iters, float *__restrict__ sink) {
+  const int t = threadIdx.x;
+  float F[8][16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) F[i][e] = 0.f;
+  v8i A[4], B[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) A[i] = (v8i){t, 0x11111111 * i, 0x02020202, 0x03030303, 0x04040404, 0x05050505, 0, 0};
+#pragma unroll
+  for (int j = 0; j < 2; ++j) B[j] = (v8i){0x01010101, t + j, 0x02020202, 0x01010101, 0x03030303, 0x01010101, 0, 0};
+  const float s0 = 1.0f + 1e-3f * (t & 63), s1 = 1.0f - 1e-3f * (t & 63);
+  for (int it = 0; it < iters; ++it) {
+    v16f dprev = (v16f){};
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+      const int i = tt % 4, j = tt / 4;
+      const v16f dt = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[i], B[j], (v16f){}, 2, 2, 0, 127, 0, 127);
+      __builtin_amdgcn_sched_barrier(0);
+      if (tt > 0) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) F[tt - 1][e] = __builtin_fmaf(j ? s1 : s0, dprev[e], F[tt - 1][e]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      dprev = dt;
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) F[7][e] = __builtin_fmaf(s1, dprev[e], F[7][e]);
+  }
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc += F[i][e];
+  sink[(int64_t)blockIdx.x * blockDim.x + t] = acc;
+}
+
 template <int KIND>
 __global__ void __launch_bounds__(256) mfma_probe_kernel(int iters, float *__restrict__ sink) {
   const int t = threadIdx.x;
@@ -79,6 +122,7 @@ double probe_ops(int kind) {
     case OQ_PROBE_FP4:
     case OQ_PROBE_FP8: return 2.0 * 32 * 32 * 64;
     case OQ_PROBE_I8: return 2.0 * 32 * 32 * 32;
+    case OQ_PROBE_FP6_UPDATE: return 2.0 * 32 * 32 * 64;
     default: return 2.0 * 32 * 32 * 16;
   }
 }
@@ -89,6 +133,11 @@ int probe_blocks() { return 2 * device_cus(); }
 
 hipError_t launch_mfma_probe(int kind, int iters, float *sink, hipStream_t stream, double *ops) {
   const int blocks = probe_blocks();  // two workgroups of 4 wavefronts per CU: two wavefronts per SIMD
+  if (kind == OQ_PROBE_FP6_UPDATE) {  // 8 MFMAs per wavefront per iteration
+    *ops = probe_ops(kind) * (double)blocks * 4.0 * (double)iters * 8;
+    hipLaunchKernelGGL(fp6_update_probe_kernel, dim3(blocks), dim3(256), 0, stream, iters, sink);
+    return hipGetLastError();
+  }
   *ops = probe_ops(kind) * (double)blocks * 4.0 * (double)iters * PROBE_UNROLL * PROBE_CHAINS;
   switch (kind) {
     case OQ_PROBE_FP6: hipLaunchKernelGGL(mfma_probe_kernel<OQ_PROBE_FP6>, dim3(blocks), dim3(256), 0, stream, iters, sink); break;

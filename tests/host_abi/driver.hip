@@ -483,7 +483,8 @@ void kron_plan_probe() {
   double ops = 0.0;
   EXPECT(oq_probe_mfma(OQ_PROBE_FP6, 10, sink, &ops, nullptr), OQ_OK, 1);
   EXPECT(oq_probe_mfma(0, 10, sink, &ops, nullptr), OQ_ERR_INVALID_ARG, 0);
-  EXPECT(oq_probe_mfma(7, 10, sink, &ops, nullptr), OQ_ERR_INVALID_ARG, 0);
+  EXPECT(oq_probe_mfma(OQ_PROBE_FP6_UPDATE, 10, sink, &ops, nullptr), OQ_OK, 1);
+  EXPECT(oq_probe_mfma(8, 10, sink, &ops, nullptr), OQ_ERR_INVALID_ARG, 0);
   EXPECT(oq_probe_mfma(OQ_PROBE_F16, 0, sink, &ops, nullptr), OQ_ERR_INVALID_ARG, 0);
   EXPECT(oq_probe_mfma(OQ_PROBE_F16, (1 << 20) + 1, sink, &ops, nullptr), OQ_ERR_INVALID_ARG, 0);
   EXPECT(oq_probe_mfma(OQ_PROBE_F16, 10, nullptr, &ops, nullptr), OQ_ERR_INVALID_ARG, 0);

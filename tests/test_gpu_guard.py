@@ -196,11 +196,11 @@ def test_guarded_mx_layer(oq):
     assert torch.equal(y.t.view(torch.int16), yf.t.view(torch.int16)), "fused layer differs from the two-call path"
 
 
-@pytest.mark.parametrize("kind", ["FP6", "FP4", "FP8", "I8", "BF16", "F16"])
+@pytest.mark.parametrize("kind", ["FP6", "FP4", "FP8", "I8", "BF16", "F16", "FP6_UPDATE"])
 def test_probe_rate_below_peak(oq, kind):
     """The probe completes, is deterministic, and its rate stays below the
     published dense peak of its type at the top clock (TFLOP/s or TOPS)."""
-    peak = {"FP6": 10100, "FP4": 10100, "FP8": 5000, "I8": 5000, "BF16": 2500, "F16": 2500}[kind]
+    peak = {"FP6": 10100, "FP4": 10100, "FP8": 5000, "I8": 5000, "BF16": 2500, "F16": 2500, "FP6_UPDATE": 10100}[kind]
     k = getattr(oq, "OQ_PROBE_" + kind)
     ops, sink = oq.oq_probe_mfma(k, 200)
     torch.cuda.synchronize()
