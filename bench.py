@@ -99,6 +99,9 @@ def _setup(torch, oq, WL, cid, n_sets_bytes=600 << 20):
         st["scale"] = torch.empty(M, dtype=torch.float32, device=dev)
         st["e8m0"] = None
     st["mean"] = torch.empty(M, dtype=torch.float32, device=dev) if s.center else None
+    # the optional scratch that lets a small W4A8 product split across K
+    nws = max(oq.oq_workspace_bytes(oq.OQ_OP_GEMM_W4A8, M, K, W.shape[0], 0) for W in wl.weights)
+    st["gemm_ws"] = torch.empty(max(16, nws), dtype=torch.uint8, device=dev)
     st["ys"] = [torch.empty((M, W.shape[0]), dtype=torch.bfloat16, device=dev) for W in wl.weights]
     st["rot"], st["ws"] = rot, ws
     return st
@@ -130,7 +133,8 @@ def _launches(oq, st, i):
                                                          w1=wq["w1"], y=y))
         else:
             f = (lambda wq=wq, y=y, N=N: oq.oq_gemm_w4a8(st["codes"], st["scale"], wq["codes"], wq["scales"], N,
-                                                         s.group, mean=st["mean"], w1=wq["w1"], y=y))
+                                                         s.group, mean=st["mean"], w1=wq["w1"], y=y,
+                                                         ws=st["gemm_ws"]))
         out.append((f"gemm_n{N}", f))
     return out
 

@@ -291,6 +291,7 @@ def oq_gemm_w4a8(qa, a_scale, w, w_scale, N: int, group: int, mean=None, w1=None
         _need(w, N * K // 2, "w", _BYTES)
         _need(w_scale, 4 * N * (K // group), "w_scale", _F32)
     _epilogue_args(M, N, mean, w1, bias)
+    _need(ws, 0, "ws", optional=True)
     y = _out_y(y, M, N, _dev(qa))
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     _check(_lib.oq_gemm_w4a8(_p(qa), qa.stride(0), _p(a_scale), M, K, _p(w), _p(w_scale), N, group, _p(mean),

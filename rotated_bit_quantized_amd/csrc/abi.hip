@@ -378,15 +378,15 @@ int oq_quant_weight(const float *w, int32_t N, int32_t K, int64_t ldw, const oq_
 int oq_gemm_w4a8(const int8_t *qa, int64_t lda, const float *a_scale, int64_t M, int32_t K, const uint8_t *w,
                  const float *w_scale, int32_t N, int32_t group, const float *mean, const float *w1,
                  const float *bias, uint16_t *y, int64_t ldy, void *ws, size_t ws_bytes, hipStream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
   int rc = check_gemm_common("oq_gemm_w4a8", qa, lda, M, K, w, w_scale, N, y, ldy, K);
   if (rc) return rc;
   rc = check_int_epilogue("oq_gemm_w4a8", K, group, mean, w1);
   if (rc) return rc;
   if (M > 0 && !a_scale) return fail(OQ_ERR_INVALID_ARG, "oq_gemm_w4a8: a_scale is NULL");
+  if (ws && !al16(ws)) return fail(OQ_ERR_ALIGNMENT, "oq_gemm_w4a8: workspace must be 16-byte aligned");
   g_err[0] = 0;
-  return hip_status(launch_gemm_int(qa, lda, 0, a_scale, M, K, w, w_scale, N, group, mean, w1, bias, y, ldy, stream),
+  return hip_status(launch_gemm_int(qa, lda, 0, a_scale, M, K, w, w_scale, N, group, mean, w1, bias, y, ldy, stream,
+                                    ws, ws ? ws_bytes : 0),
                     "oq_gemm_w4a8");
 }
 
@@ -479,9 +479,9 @@ int oq_prepack_mx(const uint8_t *w, const uint8_t *w_e8m0, int32_t N, int32_t K,
 }
 
 size_t oq_workspace_bytes(int op, int64_t M, int32_t K, int32_t N, int afmt) {
-  (void)N;
   if (M < 0 || K <= 0) return 0;
   if (op == OQ_OP_GEMM_LM) return (afmt & OQ_TILED) ? 0 : (size_t)tiled_f16_bytes(M, K);
+  if (op == OQ_OP_GEMM_W4A8) return N > 0 ? int_gemm_split_bytes(M, N, K) : 0;
   if (op != OQ_OP_LINEAR) return 0;
   return linear_ws(M, K, afmt & ~OQ_SCALE_PCTL).total;
 }

@@ -43,19 +43,32 @@ __device__ __forceinline__ v4i unpack16(uint2 p) {
   return r;
 }
 
-template <bool A_NIB>
+// SPLIT: workgroup z of gridDim.z takes the groups [z c, min((z + 1) c, K /
+// group)) with c = ceil((K / group) / gridDim.z) and writes its float32 sum
+// of s_g acc_g to part[z][M][N] (no epilogue); split_reduce_kernel adds the
+// partial sums in z order and applies the epilogue.
+template <bool A_NIB, bool SPLIT>
 __global__ void __launch_bounds__(256)
 gemm_int_kernel(const uint8_t *__restrict__ qa, int64_t lda, const float *__restrict__ a_scale,
                 int64_t M, int K, const uint8_t *__restrict__ w, const float *__restrict__ w_scale,
                 int N, int group, const float *__restrict__ mean, const float *__restrict__ w1,
-                const float *__restrict__ bias, uint16_t *__restrict__ y, int64_t ldy) {
+                const float *__restrict__ bias, uint16_t *__restrict__ y, int64_t ldy, float *__restrict__ part) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t m0 = (int64_t)blockIdx.y * 128 + (wave >> 1) * 64;
   const int n0 = blockIdx.x * 128 + (wave & 1) * 64;
   const int r32 = lane & 31;
   const int half = lane >> 5;
-  const int G = K / group;
+  const int Gall = K / group;
+  // this workgroup's groups [gb, ge)
+  int gb = 0, ge = Gall;
+  if constexpr (SPLIT) {
+    const int c = (Gall + (int)gridDim.z - 1) / (int)gridDim.z;
+    gb = (int)blockIdx.z * c;
+    ge = gb + c < Gall ? gb + c : Gall;
+    if (gb > ge) gb = ge;
+  }
+  const int G = ge;  // loads and folds stop at group ge
 
   int64_t arow[2];
   bool aok[2];
@@ -100,12 +113,12 @@ gemm_int_kernel(const uint8_t *__restrict__ qa, int64_t lda, const float *__rest
   // s + D - 1 are loaded while step s computes, from a ring of D register
   // sets, so that the latency of the plain global loads is covered
   constexpr int D = 8;
-  const int SPG = group / 32, S = K / 32;
+  const int SPG = group / 32, S = (ge - gb) * SPG, st0 = gb * SPG;
   typedef typename std::conditional<A_NIB, uint2, uint4>::type RawA;
   RawA ra[D][2];
   uint2 rw[D][2];
   float rs[D][2];  // the group scales of each loaded step's group
-  int gl = 0, kl = 0;  // group and step within it of the next load (loads run in step order)
+  int gl = gb, kl = 0;  // group and step within it of the next load (loads run in step order)
   // Loads are unconditional, from rows and steps clamped into range: rows
   // past M or N only feed outputs that are never stored, and steps past the
   // end are never computed, so no branch splits the copy queue.
@@ -116,10 +129,10 @@ gemm_int_kernel(const uint8_t *__restrict__ qa, int64_t lda, const float *__rest
     arc[i] = (aok[i] ? arow[i] : M - 1) * lda;
     wrc[i] = (int64_t)(wok[i] ? wrow[i] : N - 1) * (K / 2);
   }
-  const float *wsc0 = w_scale + (int64_t)(wok[0] ? wrow[0] : N - 1) * G;
-  const float *wsc1 = w_scale + (int64_t)(wok[1] ? wrow[1] : N - 1) * G;
+  const float *wsc0 = w_scale + (int64_t)(wok[0] ? wrow[0] : N - 1) * Gall;  // rows of K / group scales
+  const float *wsc1 = w_scale + (int64_t)(wok[1] ? wrow[1] : N - 1) * Gall;
   auto load = [&](int slot, int st) {
-    const int k = 32 * (st < S ? st : S - 1) + 16 * half;
+    const int k = 32 * (st0 + (st < S ? st : S - 1)) + 16 * half;
     const int gq = gl < G ? gl : G - 1;
     rs[slot][0] = wsc0[gq];
     rs[slot][1] = wsc1[gq];
@@ -135,6 +148,7 @@ gemm_int_kernel(const uint8_t *__restrict__ qa, int64_t lda, const float *__rest
     }
   };
   v16i acc[2][2];
+  if (S > 0) {
 #pragma unroll
   for (int q = 0; q < D - 1; ++q) load(q, q);
   for (int s0 = 0; s0 < S; s0 += D) {
@@ -177,6 +191,25 @@ gemm_int_kernel(const uint8_t *__restrict__ qa, int64_t lda, const float *__rest
       }
     }
   }
+  }
+
+  if constexpr (SPLIT) {
+    float *pz = part + (int64_t)blockIdx.z * M * N;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + 32 * i + (r >> 2) * 8 + half * 4 + (r & 3);
+        if (row >= M) continue;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int col = n0 + 32 * j + r32;
+          if (col < N) pz[row * N + col] = F[i][j][r];
+        }
+      }
+    }
+    return;
+  }
 
   __shared__ float s_alpha[128], s_mean[128];
   if (threadIdx.x < 128) {
@@ -207,20 +240,70 @@ gemm_int_kernel(const uint8_t *__restrict__ qa, int64_t lda, const float *__rest
   }
 }
 
+// y = bf16( a_scale[t] (part[0] + part[1] + ... + part[S-1]) + mean[t] w1[o]
+// + bias[o] ), the partial sums added in split order; four outputs a thread.
+__global__ void __launch_bounds__(256)
+split_reduce_kernel(const float *__restrict__ part, int S, int64_t M, int N, const float *__restrict__ a_scale,
+                    const float *__restrict__ mean, const float *__restrict__ w1, const float *__restrict__ bias,
+                    uint16_t *__restrict__ y, int64_t ldy) {
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // quad of outputs
+  const int nq = (N + 3) / 4;
+  const int64_t row = q / nq;
+  if (row >= M) return;
+  const int c0 = (int)(q % nq) * 4;
+  float F[4] = {0.f, 0.f, 0.f, 0.f};
+  const bool quad = (N & 3) == 0;  // then every quad is whole and 16-byte aligned
+  for (int z = 0; z < S; ++z) {
+    const float *pz = part + ((int64_t)z * M + row) * N + c0;
+    float p[4];
+    if (quad) {
+      const float4 v = *reinterpret_cast<const float4 *>(pz);
+      p[0] = v.x, p[1] = v.y, p[2] = v.z, p[3] = v.w;
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) p[c] = c0 + c < N ? pz[c] : 0.f;
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) F[c] = z == 0 ? p[c] : F[c] + p[c];
+  }
+  const float al = a_scale[row];
+  const float mu = mean ? mean[row] : 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int col = c0 + c;
+    if (col >= N) continue;
+    float v = al * F[c];
+    if (mean) v = __builtin_fmaf(mu, w1[col], v);
+    if (bias) v = v + bias[col];
+    y[row * ldy + col] = f32_to_bf16_rne(v);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gemm_int(const void *qa, int64_t lda_bytes, int a_is_nibble, const float *a_scale,
                            int64_t M, int K, const uint8_t *w, const float *w_scale, int N, int group,
                            const float *mean, const float *w1, const float *bias, uint16_t *y,
-                           int64_t ldy, hipStream_t stream) {
+                           int64_t ldy, hipStream_t stream, void *ws, size_t ws_bytes) {
   if (M == 0 || N == 0) return hipSuccess;
   dim3 grid((unsigned)((N + 127) / 128), (unsigned)((M + 127) / 128));
+  const int S = a_is_nibble ? 1 : int_gemm_splits(M, N, K, group);
+  if (S > 1 && ws && ws_bytes >= (size_t)S * (size_t)M * (size_t)N * 4) {
+    float *part = static_cast<float *>(ws);
+    grid.z = (unsigned)S;
+    hipLaunchKernelGGL((gemm_int_kernel<false, true>), grid, dim3(256), 0, stream, (const uint8_t *)qa, lda_bytes,
+                       a_scale, M, K, w, w_scale, N, group, mean, w1, bias, y, ldy, part);
+    const int64_t quads = M * ((N + 3) / 4);
+    hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, stream, part, S, M,
+                       N, a_scale, mean, w1, bias, y, ldy);
+    return hipGetLastError();
+  }
   if (a_is_nibble)
-    hipLaunchKernelGGL((gemm_int_kernel<true>), grid, dim3(256), 0, stream, (const uint8_t *)qa, lda_bytes,
-                       a_scale, M, K, w, w_scale, N, group, mean, w1, bias, y, ldy);
+    hipLaunchKernelGGL((gemm_int_kernel<true, false>), grid, dim3(256), 0, stream, (const uint8_t *)qa, lda_bytes,
+                       a_scale, M, K, w, w_scale, N, group, mean, w1, bias, y, ldy, nullptr);
   else
-    hipLaunchKernelGGL((gemm_int_kernel<false>), grid, dim3(256), 0, stream, (const uint8_t *)qa, lda_bytes,
-                       a_scale, M, K, w, w_scale, N, group, mean, w1, bias, y, ldy);
+    hipLaunchKernelGGL((gemm_int_kernel<false, false>), grid, dim3(256), 0, stream, (const uint8_t *)qa, lda_bytes,
+                       a_scale, M, K, w, w_scale, N, group, mean, w1, bias, y, ldy, nullptr);
   return hipGetLastError();
 }
 

@@ -196,11 +196,32 @@ hipError_t launch_dense32(const uint16_t *x, int64_t M, int d, int64_t ldx,
 
 // K3/K4: integer-coded activations x packed INT4 weights, fp32 group epilogue.
 //   a_is_nibble: activations packed two per byte (A4) instead of int8.
+//   ws: for int8 activations, scratch of float32 partial sums; with at least
+//   int_gemm_splits(M, N, K, group) x M x N x 4 bytes a small product runs
+//   split across K (then the partial sums are added in split order);
+//   otherwise, or when NULL, in one pass.
 hipError_t launch_gemm_int(const void *qa, int64_t lda_bytes, int a_is_nibble,
                            const float *a_scale, int64_t M, int K,
                            const uint8_t *w, const float *w_scale, int N, int group,
                            const float *mean, const float *w1, const float *bias,
-                           uint16_t *y, int64_t ldy, hipStream_t stream);
+                           uint16_t *y, int64_t ldy, hipStream_t stream, void *ws = nullptr,
+                           size_t ws_bytes = 0);
+// Workgroups of the W4A8 GEMM across K: enough 128 x 128 tiles fill the
+// device alone; below half of its 256 CUs, the groups are split so that
+// every CU gets a workgroup (at most one split per group).
+inline int int_gemm_splits(int64_t M, int N, int K, int group) {
+  if (M <= 0 || N <= 0 || K <= 0 || group <= 0) return 1;
+  const int64_t tiles = ((N + 127) / 128) * ((M + 127) / 128);
+  if (tiles >= 128) return 1;
+  int64_t s = (256 + tiles - 1) / tiles;
+  if (s > K / group) s = K / group;
+  return s < 1 ? 1 : (int)s;
+}
+// scratch that lets every group size split (0 when the product needs none)
+inline size_t int_gemm_split_bytes(int64_t M, int N, int K) {
+  const int s = int_gemm_splits(M, N, K, 32);  // the most splits any group allows
+  return s > 1 ? (size_t)s * (size_t)M * (size_t)N * 4 : 0;
+}
 
 // Tiled FP6 GEMM (A4: planes = 1, A6: planes = 2); weights from prepack.
 hipError_t launch_gemm_fp6(const uint8_t *A, int planes, const float *a_scale, int64_t M, int K, const uint8_t *W,

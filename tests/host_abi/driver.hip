@@ -238,6 +238,14 @@ void gemms() {
                       nullptr, Y, 64, nullptr, 0, nullptr), OQ_ERR_INVALID_ARG, 0);
   EXPECT(oq_gemm_w4a8(reinterpret_cast<const int8_t *>(P), 256, S, -5, 256, P, S, 64, 128, nullptr, nullptr, nullptr, Y,
                       64, nullptr, 0, nullptr), OQ_ERR_INVALID_ARG, 0);
+  // optional split scratch: one 128 x 128 tile splits into min(256, K / 32) = 8 parts
+  TRUE(oq_workspace_bytes(OQ_OP_GEMM_W4A8, 5, 256, 64, 0) == 8u * 5 * 64 * 4);
+  TRUE(oq_workspace_bytes(OQ_OP_GEMM_W4A8, 2048, 256, 2048, 0) == 0);  // 256 tiles: one pass
+  TRUE(oq_workspace_bytes(OQ_OP_GEMM_W4A8, 5, 256, 0, 0) == 0);
+  EXPECT(oq_gemm_w4a8(reinterpret_cast<const int8_t *>(P), 256, S, 5, 256, P, S, 64, 128, nullptr, nullptr, nullptr, Y,
+                      64, P, 10240, nullptr), OQ_OK, 1);
+  EXPECT(oq_gemm_w4a8(reinterpret_cast<const int8_t *>(P), 256, S, 5, 256, P, S, 64, 128, nullptr, nullptr, nullptr, Y,
+                      64, Q4, 10240, nullptr), OQ_ERR_ALIGNMENT, 0);
 
   EXPECT(oq_gemm_w4a4(OQ_A4 | OQ_TILED, P, 0, S, 5, 256, P, S, 64, 64, nullptr, nullptr, nullptr, Y, 64, nullptr, 0,
                       nullptr), OQ_OK, 1);

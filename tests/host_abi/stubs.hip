@@ -38,7 +38,8 @@ hipError_t launch_dense32(const uint16_t *, int64_t, int, int64_t, const uint16_
   return rec("dense32", out);
 }
 hipError_t launch_gemm_int(const void *, int64_t, int, const float *, int64_t, int, const uint8_t *, const float *,
-                           int, int, const float *, const float *, const float *, uint16_t *y, int64_t, hipStream_t) {
+                           int, int, const float *, const float *, const float *, uint16_t *y, int64_t, hipStream_t,
+                           void *, size_t) {
   return rec("gemm_int", y);
 }
 hipError_t launch_gemm_fp6(const uint8_t *, int, const float *, int64_t, int, const uint8_t *, const float *, int,

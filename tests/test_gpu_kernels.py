@@ -308,6 +308,46 @@ def test_gemm_int(oq, M, N, K, group, afmt, rank1, bias):
     say("  within 1 bf16 ulp:", frac)
 
 
+@pytest.mark.parametrize("M,N,K,group,qmax,rank1,bias", [(256, 1024, 1024, 128, 127, False, False),
+                                                          (77, 200, 512, 64, 127, True, True),
+                                                          (1, 32, 256, 32, 31, True, False),
+                                                          (130, 136, 1024, 128, 127, False, True),
+                                                          (64, 96, 192, 32, 127, False, False)])
+def test_gemm_w4a8_split(oq, M, N, K, group, qmax, rank1, bias):
+    """The W4A8 product split across K through the optional scratch: against
+    the oracle under the output rule with the extra float32 additions of the
+    partial sums counted, repeatable bit for bit, and the one-pass call on
+    the same inputs within the same rule."""
+    say("case gemm_w4a8 split", M, N, K, group, qmax, rank1, bias)
+    rng = np.random.default_rng(7 * M + N + K)
+    qa = _rand_codes(rng, M, K, qmax)
+    qa[0, :] = qmax
+    qw = _rand_codes(rng, N, K, 7)
+    alpha = rng.uniform(0.01, 1.0, size=M).astype(np.float32)
+    sw = rng.uniform(1e-3, 1e-2, size=(N, K // group)).astype(np.float32)
+    mean = rng.normal(0, 3, size=M).astype(np.float32) if rank1 else None
+    w1 = rng.normal(0, 0.5, size=N).astype(np.float32) if rank1 else None
+    b = rng.normal(0, 0.1, size=N).astype(np.float32) if bias else None
+    args = dict(mean=None if mean is None else to_dev(mean), w1=None if w1 is None else to_dev(w1),
+                bias=None if b is None else to_dev(b))
+    nbytes = oq.oq_workspace_bytes(oq.OQ_OP_GEMM_W4A8, M, K, N, 0)
+    tiles = -(-N // 128) * -(-M // 128)
+    splits = 1 if tiles >= 128 else min(-(-256 // tiles), K // group)
+    assert (nbytes > 0) == (splits > 1)
+    ws = torch.zeros(max(16, nbytes), dtype=torch.uint8, device="cuda")
+    A, W, SW, AL = to_dev(qa.astype(np.int8)), to_dev(OQ.pack_int4(qw)), to_dev(sw), to_dev(alpha)
+    y1 = oq.oq_gemm_w4a8(A, AL, W, SW, N, group, ws=ws, **args)
+    y2 = oq.oq_gemm_w4a8(A, AL, W, SW, N, group, ws=ws, **args)
+    y0 = oq.oq_gemm_w4a8(A, AL, W, SW, N, group, **args)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), "split product not repeatable"
+    acc = OG.group_acc(qa, qw, group)
+    y_ref, S = OG.epilogue_int(alpha, acc, sw, mean, w1, b)
+    frac = check_output(to_host(y1), y_ref, S, K // group + splits, "gemm_w4a8 split")
+    check_output(to_host(y0), y_ref, S, K // group, "gemm_w4a8 one pass")
+    say(f"  {splits} splits, within 1 bf16 ulp: {frac}")
+
+
 @pytest.mark.parametrize("M,N,K,bias", [(130, 96, 256, True), (64, 256, 4096, True), (7, 32, 64, True),
                                          (300, 600, 1152, True), (1, 40, 128, False), (513, 257, 384, False),
                                          (260, 300, 192, True)])
