@@ -24,7 +24,11 @@
 //     1, 2 (quad_perm), and for the half-row and row mirrors, which pair
 //     lane l with l ^ 7 and l ^ 15: lanes are renumbered so that those
 //     pairings flip exactly one index bit (index_lane below).  Distances 16
-//     and 32 use ds_swizzle and ds_bpermute;
+//     and 32 stay in the VALU too: v_permlane16_swap / v_permlane32_swap
+//     exchange row or half-wave pieces of two values so that every lane
+//     holds both operands of one butterfly, the lane forms a + b and a - b
+//     (true signs: both partners carry the same lane sign), and a second
+//     swap puts the results back;
 //   * when h is a power of 4, 1/sqrt(h) is a power of two: the per-round
 //     multiply is exact and is deferred into the quantization scale
 //     (identical codes and scales; the float32 output mode applies it);
@@ -200,11 +204,47 @@ __device__ __forceinline__ void dpp_stage(float (&v)[16], float c) {
   if constexpr (K == 3) asm(OQ_FMAC_DPP16("row_mirror") : OQ_V16_OPERANDS(v) : "v"(c));
 }
 
+// Butterflies between lanes 16 (D = 16) or 32 (D = 32) apart, the lower
+// lane taking a + b and the upper a - b.  For each pair of values (v[j],
+// v[j+1]) one swap leaves, in every lane, the lower and the upper operand of
+// one butterfly (value j in the lower lanes of each pair, j + 1 in the upper
+// ones); the lane forms the sum and the difference, and the same swap of
+// (sum, difference) returns each result to its lane and value.
+template <int D>
+__device__ __forceinline__ void swap_stage(float (&v)[16]) {
+#pragma unroll
+  for (int j = 0; j < 16; j += 2) {
+    const uint32_t a = __float_as_uint(v[j]), b = __float_as_uint(v[j + 1]);
+    uint32_t lo, hi;
+    if constexpr (D == 16) {
+      const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+      lo = r[0];
+      hi = r[1];
+    } else {
+      const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+      lo = r[0];
+      hi = r[1];
+    }
+    const float sum = __uint_as_float(lo) + __uint_as_float(hi);
+    const float dif = __uint_as_float(lo) - __uint_as_float(hi);
+    if constexpr (D == 16) {
+      const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(sum), __float_as_uint(dif), false, false);
+      v[j] = __uint_as_float(q[0]);
+      v[j + 1] = __uint_as_float(q[1]);
+    } else {
+      const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(sum), __float_as_uint(dif), false, false);
+      v[j] = __uint_as_float(q[0]);
+      v[j + 1] = __uint_as_float(q[1]);
+    }
+  }
+}
+
 // Un-normalised FWHT of each 2^(n+4)-coordinate block; stage order strides
 // 1, 2, ..., as in the oracle.  c[k] = -1 where index-lane bit k is set.
-// On return lane values carry the sign (-1)^popcount(index lane mod 2^n).
+// On return lane values carry the sign (-1)^popcount(index lane mod
+// 2^min(n, 4)): the DPP stages leave it, the swap stages keep it.
 template <int SLOTS>
-__device__ __forceinline__ void fwht_row(float (&v)[SLOTS][16], int n, const float (&c)[6]) {
+__device__ __forceinline__ void fwht_row(float (&v)[SLOTS][16], int n, const float (&c)[4]) {
 #pragma unroll
   for (int s = 0; s < SLOTS; ++s)
 #pragma unroll
@@ -228,26 +268,12 @@ __device__ __forceinline__ void fwht_row(float (&v)[SLOTS][16], int n, const flo
   if (n > 3)
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s) dpp_stage<3>(v[s], c[3]);
-  // distances 16 and 32 go through the LDS crossbar: a slot's 16 exchanges
-  // are issued before its accumulates, so that their latencies overlap
   if (n > 4)
 #pragma unroll
-    for (int s = 0; s < SLOTS; ++s) {
-      float p[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) p[j] = xlane(v[s][j], 4);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) v[s][j] = __builtin_fmaf(p[j], c[4], v[s][j]);
-    }
+    for (int s = 0; s < SLOTS; ++s) swap_stage<16>(v[s]);
   if (n > 5)
 #pragma unroll
-    for (int s = 0; s < SLOTS; ++s) {
-      float p[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) p[j] = xlane(v[s][j], 5);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) v[s][j] = __builtin_fmaf(p[j], c[5], v[s][j]);
-    }
+    for (int s = 0; s < SLOTS; ++s) swap_stage<32>(v[s]);
 }
 
 // Stores the 16 codes of two slots (a: coordinates base..base+15, b: the same
@@ -436,11 +462,11 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
     ld[s] = 1024 * s + 16 * ll < dload;
   }
   const float c_all = (ROUNDS == 0 || !pow4) ? 1.0f : (ROUNDS == 2 ? c_h * c_h : c_h);  // deferred, exact
-  float cst[6];
+  float cst[4];
 #pragma unroll
-  for (int k = 0; k < 6; ++k) cst[k] = ((il >> k) & 1) ? -1.0f : 1.0f;
+  for (int k = 0; k < 4; ++k) cst[k] = ((il >> k) & 1) ? -1.0f : 1.0f;
   // sign the lane-bit stages leave on this lane's values
-  const float sg = (__builtin_popcount(il & ((1 << nlog) - 1)) & 1) ? -1.0f : 1.0f;
+  const float sg = (__builtin_popcount(il & ((1 << (nlog < 4 ? nlog : 4)) - 1)) & 1) ? -1.0f : 1.0f;
   const float sgq = KM > 1 ? 1.0f : sg;  // the sign the quantiser sees (the Paley stage removes it)
   const int neg_from = 2 * d;  // first-round byte offsets at or above this hit the -x copy
 
