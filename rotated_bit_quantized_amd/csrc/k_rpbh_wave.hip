@@ -68,21 +68,56 @@ constexpr int WAVES_PER_WG = 4;
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned v6u __attribute__((ext_vector_type(6)));
 
+// Partner of this lane in step lg of a butterfly network over the wavefront,
+// all on the VALU: lane ^ 1 and lane ^ 2 (quad_perm), then l <-> 7 - l
+// within 8 lanes (row_half_mirror), l <-> 15 - l within 16 (row_mirror),
+// rows 16 lanes apart (v_permlane16_swap) and halves 32 apart
+// (v_permlane32_swap).  After steps 0..k every group of 2^(k+1) lanes has
+// met, so a symmetric combination (max, a top-k merge, a commutative add)
+// over all six steps leaves the same value on every lane.
 __device__ __forceinline__ float xlane(float v, int lg) {
   const int iv = __float_as_int(v);
   switch (lg) {
-    case 0: return __int_as_float(__builtin_amdgcn_mov_dpp(iv, 0xB1, 0xF, 0xF, true));  // lane ^ 1
-    case 1: return __int_as_float(__builtin_amdgcn_mov_dpp(iv, 0x4E, 0xF, 0xF, true));  // lane ^ 2
-    case 2: return __int_as_float(__builtin_amdgcn_ds_swizzle(iv, 0x1F | (4 << 10)));
-    case 3: return __int_as_float(__builtin_amdgcn_ds_swizzle(iv, 0x1F | (8 << 10)));
-    case 4: return __int_as_float(__builtin_amdgcn_ds_swizzle(iv, 0x1F | (16 << 10)));
-    default: return __shfl_xor(v, 32);
+    case 0: return __int_as_float(__builtin_amdgcn_mov_dpp(iv, 0xB1, 0xF, 0xF, true));   // lane ^ 1
+    case 1: return __int_as_float(__builtin_amdgcn_mov_dpp(iv, 0x4E, 0xF, 0xF, true));   // lane ^ 2
+    case 2: return __int_as_float(__builtin_amdgcn_mov_dpp(iv, 0x141, 0xF, 0xF, true));  // row_half_mirror
+    case 3: return __int_as_float(__builtin_amdgcn_mov_dpp(iv, 0x140, 0xF, 0xF, true));  // row_mirror
+    case 4: {
+      // (value of the even row, value of the odd row) of each row pair
+      const auto r = __builtin_amdgcn_permlane16_swap((uint32_t)iv, (uint32_t)iv, false, false);
+      return __uint_as_float((__lane_id() & 16) ? r[0] : r[1]);
+    }
+    default: {
+      const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)iv, (uint32_t)iv, false, false);
+      return __uint_as_float((__lane_id() & 32) ? r[0] : r[1]);
+    }
   }
 }
 
+// Wavefront sum of a float64 over the network above, the pair's two values
+// added in the same order in both lanes (lower row or half first), so every
+// lane ends with the same bits.
 __device__ __forceinline__ double wave_sum_d(double v) {
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  for (int lg = 0; lg < 4; ++lg) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const float lo = xlane(__uint_as_float((uint32_t)u), lg), hi = xlane(__uint_as_float((uint32_t)(u >> 32)), lg);
+    v += __builtin_bit_cast(double, ((uint64_t)__float_as_uint(hi) << 32) | __float_as_uint(lo));
+  }
+  {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const auto rl = __builtin_amdgcn_permlane16_swap((uint32_t)u, (uint32_t)u, false, false);
+    const auto rh = __builtin_amdgcn_permlane16_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+    v = __builtin_bit_cast(double, ((uint64_t)rh[0] << 32) | rl[0]) +
+        __builtin_bit_cast(double, ((uint64_t)rh[1] << 32) | rl[1]);
+  }
+  {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const auto rl = __builtin_amdgcn_permlane32_swap((uint32_t)u, (uint32_t)u, false, false);
+    const auto rh = __builtin_amdgcn_permlane32_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+    v = __builtin_bit_cast(double, ((uint64_t)rh[0] << 32) | rl[0]) +
+        __builtin_bit_cast(double, ((uint64_t)rh[1] << 32) | rl[1]);
+  }
   return v;
 }
 
@@ -716,7 +751,7 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
         for (int j = 0; j < 16; ++j)
           if (act[s]) ssp[j & 3] += (double)v[s][j] * (double)v[s][j];
       double ss = (ssp[0] + ssp[1]) + (ssp[2] + ssp[3]);
-      ss = wave_sum_d(ss);  // the same bits on every lane (xor butterfly)
+      ss = wave_sum_d(ss);  // the same bits on every lane
       const double c2 = (double)c_all * (double)c_all;
       // Every partial sum above is reached by at most 24 additions of
       // nonnegative terms (16 per lane chain, 2, then 6 across the
