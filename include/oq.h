@@ -248,9 +248,10 @@ int oq_gemm_w4a8(const int8_t *qa, int64_t lda, const float *a_scale, int64_t M,
  *     oq_quant_act with the same afmt; lda_bytes ignored), w and w_scale
  *     from oq_prepack_w4, group 64; output bit-identical to the canonical
  *     path on the same codes.  The library picks the workgroup shape from
- *     M, N and the CU count; the environment variable OQ_FP6_TILE (256x256,
- *     256x192, 256x128 or 128x192; OQ_A4 only) forces one, for tuning.  The
- *     result does not depend on the shape.  One activation plane
+ *     M, N and the CU count; the environment variable OQ_FP6_TILE forces
+ *     one, for tuning: 256x256, 256x192, 256x128w8 (eight waves), 256x128
+ *     (four waves) or 128x192 for OQ_A4; 256x192 or 256x128w8 for OQ_A6.
+ *     The result does not depend on the shape.  One activation plane
  *     (oq_tiled_bytes(M, K)) and the weights (oq_tiled_bytes(N, K)) must each
  *     stay below 4 GiB (the kernel's 32-bit operand offsets); larger requests
  *     fail with OQ_ERR_UNSUPPORTED (split M or N).

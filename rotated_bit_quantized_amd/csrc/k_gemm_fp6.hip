@@ -207,11 +207,14 @@ __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F
 // Workgroup shapes: each wave computes TI x TJ MFMA tiles of 32 x 32.
 //   8 waves, TI = 4, TJ = 2: waves 2 (rows) x 4 (columns), 256 x 256 outputs;
 //   8 waves, TI = 2, TJ = 3: waves 4 x 2, 256 x 192 outputs;
+//   8 waves, TI = 2, TJ = 2: waves 4 x 2, 256 x 128 outputs;
 //   4 waves, TI = 4, TJ = 2: waves 2 x 2, 256 x 128 outputs;
 //   4 waves, TI = 2, TJ = 3: waves 2 x 2, 128 x 192 outputs.
-// An 8-wave stage holds 8 A and 8 B tiles and 256 scales whatever the shape
-// (a 192-wide tile loads the two column blocks past its end too and leaves
-// them unread); a 4-wave stage holds exactly its tiles.  The code bytes of a
+// An 8-wave stage holds 8 A tiles per plane and 256 scales whatever the
+// shape, and exactly its B tiles where that splits the copies evenly over
+// the waves (256 and 128 wide); a 192-wide tile loads the two column blocks
+// past its end too and leaves them unread.  A 4-wave stage holds exactly its
+// tiles.  The code bytes of a
 // stage are split evenly over the waves as U4 1 KiB units (16 bytes a lane)
 // and U1 256-byte units (4 bytes a lane), and every wave copies one 256-byte
 // chunk of scales, so all waves issue the same copies per stage and the
@@ -224,7 +227,7 @@ struct V2C {
   static constexpr int WAVES_M = WAVES == 8 ? 8 / TI : 2, WAVES_N = WAVES / WAVES_M;
   static constexpr int BM = 32 * TI * WAVES_M, BN = 32 * TJ * WAVES_N;
   static constexpr int A_BYTES = (WAVES == 8 ? 8 : BM / 32) * CHUNK_TILE;  // one plane
-  static constexpr int B_BYTES = (WAVES == 8 ? 8 : BN / 32) * CHUNK_TILE;
+  static constexpr int B_BYTES = (WAVES == 8 && BN == 192 ? 8 : BN / 32) * CHUNK_TILE;
   static constexpr int S_CHUNKS = WAVES == 8 ? 4 : BN / 64;  // 256-byte scale chunks
   static constexpr int S_BYTES = 256 * S_CHUNKS;
   static constexpr int B_OFF = PLANES * A_BYTES;  // A planes, then B, then the scales
@@ -670,32 +673,46 @@ hipError_t launch_v2_shape(const uint8_t *A, int64_t plane, const float *a_scale
 }
 
 
-enum class Shape { W8_256x256, W8_256x192, W4_256x128, W4_128x192 };
+enum class Shape { W8_256x256, W8_256x192, W8_256x128, W4_256x128, W4_128x192 };
 
-// Workgroup shape for an M x N product.  Large products take an 8-wave
-// shape, 256 x 192 when its whole waves of workgroups (one per CU) cover
-// fewer output columns than 256 x 256 (4096 x 3072 on 256 CUs: 256 tiles
-// instead of 192), else 256 x 256 (the two cost the same at 4096 x 12288 and
-// 256 x 256 runs 6% faster per output).  Products with fewer 256 x 256 tiles
-// than half the CUs take the 4-wave 128 x 192 shape: 2.7x more workgroups,
-// each with a CU to itself.  The 4-wave shapes match the 8-wave ones per
-// output when the CUs are full.
-// OQ_FP6_TILE=256x256, 256x192, 256x128 or 128x192 in the environment forces
-// one shape (for tuning and tests); any other value, or none, chooses.
-Shape pick_shape(int64_t M, int N) {
+// Output columns one CU covers with a 256-row shape of width w: whole waves
+// of workgroups (one per CU) times w.
+int64_t covered_columns(int64_t M, int N, int w, int64_t cus) {
+  const int64_t tiles = (M + 255) / 256 * ((N + w - 1) / w);
+  return (tiles + cus - 1) / cus * w;
+}
+
+// Workgroup shape for an M x N product.  Large products take the 8-wave
+// shape whose whole waves of workgroups (one per CU) cover the fewest output
+// columns, the wider one on a tie (per output 256 x 256 runs 6% faster than
+// 256 x 192): 4096 x 3072 on 256 CUs takes 256 x 192 (256 tiles instead of
+// 192 of 256 x 256), 4096 x 12288 256 x 256.  Single-plane products with
+// fewer 256 x 256 tiles than half the CUs take the 4-wave 128 x 192 shape:
+// 2.7x more workgroups, each with a CU to itself.  The 4-wave shapes match
+// the 8-wave ones per output when the CUs are full.  Two-plane (6-bit)
+// products choose between the 8-wave 256 x 192 and 256 x 128 shapes only
+// (4096 x 1920: 240 tiles of 256 x 128 instead of 160 of 256 x 192).
+// OQ_FP6_TILE=256x256, 256x192, 256x128w8, 256x128 or 128x192 in the
+// environment forces one shape (for tuning and tests; two-plane products
+// take 256x192 or 256x128w8 only); any other value, or none, chooses.
+Shape pick_shape(int64_t M, int N, int planes = 1) {
   if (const char *f = getenv("OQ_FP6_TILE")) {
-    if (strcmp(f, "256x256") == 0) return Shape::W8_256x256;
     if (strcmp(f, "256x192") == 0) return Shape::W8_256x192;
-    if (strcmp(f, "256x128") == 0) return Shape::W4_256x128;
-    if (strcmp(f, "128x192") == 0) return Shape::W4_128x192;
+    if (strcmp(f, "256x128w8") == 0) return Shape::W8_256x128;
+    if (planes == 1) {
+      if (strcmp(f, "256x256") == 0) return Shape::W8_256x256;
+      if (strcmp(f, "256x128") == 0) return Shape::W4_256x128;
+      if (strcmp(f, "128x192") == 0) return Shape::W4_128x192;
+    }
   }
   const int64_t cus = device_cus();
-  const int64_t mt = (M + 255) / 256;
-  const int64_t t256 = mt * ((N + 255) / 256);
+  const int64_t c192 = covered_columns(M, N, 192, cus), c128 = covered_columns(M, N, 128, cus);
+  if (planes == 2) return c128 < c192 ? Shape::W8_256x128 : Shape::W8_256x192;
+  const int64_t t256 = (M + 255) / 256 * ((N + 255) / 256);
   if (2 * t256 < cus) return Shape::W4_128x192;
-  const int64_t w256 = (t256 + cus - 1) / cus;
-  const int64_t w192 = (mt * ((N + 191) / 192) + cus - 1) / cus;
-  return w192 * 192 < w256 * 256 ? Shape::W8_256x192 : Shape::W8_256x256;
+  const int64_t c256 = covered_columns(M, N, 256, cus);
+  if (c256 <= c192 && c256 <= c128) return Shape::W8_256x256;
+  return c192 <= c128 ? Shape::W8_256x192 : Shape::W8_256x128;
 }
 
 template <int NSLOT, bool PAIRED, bool ASYM>
@@ -705,6 +722,9 @@ hipError_t launch_v2(const uint8_t *A, const float *a_scale, int64_t M, int K, c
   const Shape sh = pick_shape(M, N);
   if (sh == Shape::W8_256x192)
     return launch_v2_shape<NSLOT, PAIRED, ASYM, 2, 3, 8>(A, 0, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy,
+                                                         stream, gsum, corr);
+  if (sh == Shape::W8_256x128)
+    return launch_v2_shape<NSLOT, PAIRED, ASYM, 2, 2, 8>(A, 0, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy,
                                                          stream, gsum, corr);
   if (sh == Shape::W4_256x128)
     return launch_v2_shape<NSLOT, PAIRED, ASYM, 4, 2, 4>(A, 0, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy,
@@ -738,9 +758,13 @@ hipError_t launch_gemm_fp6(const uint8_t *A, int planes, const float *a_scale, i
   const int64_t plane = tiled_bytes(M, K);
   // the kernel addresses operands with 32-bit offsets from their base
   if (!fp6_offsets_fit(M, N, K)) return hipErrorInvalidValue;
-  if (planes == 2)  // two A planes: the 256 x 192 shape, whose registers hold both planes' fragments
+  if (planes == 2) {  // two A planes: 8-wave shapes with two A tiles per wave (both planes' fragments held)
+    if (pick_shape(M, N, 2) == Shape::W8_256x128)
+      return launch_v2_shape<FP6_SLOTS, FP6_PAIRED, false, 2, 2, 8, 2>(A, plane, a_scale, M, K, W, wst, N, Np, mean,
+                                                                       w1, bias, y, ldy, stream, nullptr, nullptr);
     return launch_v2_shape<FP6_SLOTS, FP6_PAIRED, false, 2, 3, 8, 2>(A, plane, a_scale, M, K, W, wst, N, Np, mean,
                                                                      w1, bias, y, ldy, stream, nullptr, nullptr);
+  }
   return launch_v2<FP6_SLOTS, FP6_PAIRED, false>(A, a_scale, M, K, W, wst, N, Np, mean, w1, bias, y, ldy, stream);
 }
 

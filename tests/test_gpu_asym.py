@@ -187,7 +187,7 @@ def test_gemm_asym(oq, M, K, N, center, bias):
     say("  within 1 bf16 ulp:", frac)
 
 
-@pytest.mark.parametrize("shape", ["256x256", "256x192", "256x128", "128x192"])
+@pytest.mark.parametrize("shape", ["256x256", "256x192", "256x128w8", "256x128", "128x192"])
 @pytest.mark.parametrize("M,K,N", [(300, 1024, 520), (257, 512, 1000), (64, 192, 96)])
 def test_gemm_asym_shapes(oq, monkeypatch, shape, M, K, N):
     """Every workgroup shape of the corrected GEMM, forced through OQ_FP6_TILE;

@@ -131,14 +131,14 @@ def test_tiled_gemm(oq, M, N, K, afmt, rank1, bias):
     check_output(to_host(y_t), y_ref, S, K // 64, "tiled gemm")
 
 
-@pytest.mark.parametrize("shape", ["256x256", "256x192", "256x128", "128x192"])
+@pytest.mark.parametrize("shape", ["256x256", "256x192", "256x128w8", "256x128", "128x192"])
 @pytest.mark.parametrize("M,N,K,rank1,bias", [(300, 520, 1024, True, True), (257, 1000, 512, False, True),
                                               (31, 32, 64, False, False), (600, 3072, 3072, True, False)])
 def test_tiled_gemm_shapes(oq, monkeypatch, shape, M, N, K, rank1, bias):
     """Every workgroup shape of the single-plane kernel (8 waves: 256 x 256,
-    256 x 192 outputs; 4 waves: 256 x 128, 128 x 192), forced through
-    OQ_FP6_TILE: bit-identical to the canonical GEMM and within the bound of
-    the oracle's product."""
+    256 x 192, 256 x 128 outputs; 4 waves: 256 x 128, 128 x 192), forced
+    through OQ_FP6_TILE: bit-identical to the canonical GEMM and within the
+    bound of the oracle's product."""
     say("case tiled gemm shape", shape, M, N, K, rank1, bias)
     monkeypatch.setenv("OQ_FP6_TILE", shape)
     rng = np.random.default_rng(M + N * 7 + K)
@@ -161,6 +161,41 @@ def test_tiled_gemm_shapes(oq, monkeypatch, shape, M, N, K, rank1, bias):
     assert torch.equal(y_t.view(torch.int16), y_c.view(torch.int16)), "tiled and canonical GEMMs differ"
     y_ref, S = OG.epilogue_int(alpha, OG.group_acc(qa, qw, 64), sw, mean, w1, b)
     check_output(to_host(y_t), y_ref, S, K // 64, "tiled gemm shape " + shape)
+
+
+@pytest.mark.parametrize("shape", ["256x192", "256x128w8"])
+@pytest.mark.parametrize("M,N,K,rank1,bias", [(300, 520, 1024, True, True), (513, 1000, 640, False, True),
+                                              (31, 32, 64, False, False), (4352, 4096, 256, False, False)])
+def test_tiled_gemm_two_plane_shapes(oq, monkeypatch, shape, M, N, K, rank1, bias):
+    """Both workgroup shapes of the two-plane (6-bit activation) kernel,
+    forced through OQ_FP6_TILE, including more tiles than CUs: bit-identical
+    to the canonical W4A8 GEMM on the same codes and within the bound of the
+    oracle's product."""
+    say("case tiled gemm two-plane shape", shape, M, N, K, rank1, bias)
+    monkeypatch.setenv("OQ_FP6_TILE", shape)
+    rng = np.random.default_rng(M * 5 + N + K * 3)
+    qa = rng.integers(-31, 32, size=(M, K))
+    qa[0] = 31
+    qa[-1] = -31
+    qw = rng.integers(-7, 8, size=(N, K))
+    alpha = rng.uniform(0.01, 1.0, size=M).astype(np.float32)
+    sw = rng.uniform(1e-3, 1e-2, size=(N, K // 64)).astype(np.float32)
+    mean = rng.normal(0, 3, size=M).astype(np.float32) if rank1 else None
+    w1 = rng.normal(0, 0.5, size=N).astype(np.float32) if rank1 else None
+    b = rng.normal(0, 0.1, size=N).astype(np.float32) if bias else None
+    kw = dict(mean=None if mean is None else to_dev(mean), w1=None if w1 is None else to_dev(w1),
+              bias=None if b is None else to_dev(b))
+    wpk = to_dev(OQ.pack_int4(qw))
+    wt = oq.oq_prepack_w4(wpk, to_dev(sw), N, K)
+    qh, ql = split_a6(qa)
+    at = np.concatenate([tile(qh), tile(ql)])
+    y_c = oq.oq_gemm_w4a8(to_dev(qa.astype(np.int8)), to_dev(alpha), wpk, to_dev(sw), N, 64, **kw)
+    y_t = oq.oq_gemm_w4a4(oq.OQ_A6 | oq.OQ_TILED, to_dev(at), to_dev(alpha), wt["codes"], wt["scales"], N, 64,
+                          M=M, K=K, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(y_t.view(torch.int16), y_c.view(torch.int16)), "two-plane tiled and canonical GEMMs differ"
+    y_ref, S = OG.epilogue_int(alpha, OG.group_acc(qa, qw, 64), sw, mean, w1, b)
+    check_output(to_host(y_t), y_ref, S, K // 64, "two-plane tiled gemm shape " + shape)
 
 
 @pytest.mark.parametrize("cid,M,N", [(2, 300, 256), (3, 260, 384), (4, 520, 512)])
