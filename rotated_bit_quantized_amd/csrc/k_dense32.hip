@@ -162,10 +162,11 @@ dense32_kernel(const void *__restrict__ xin, int64_t M, int d, int64_t ldx, cons
 // to one ulp per addition (truncation allowed), is off by at most
 // 34 * 2^-23 s_i; flushed subnormal products add at most 2^-120.  With the
 // RN32 step, s' >= s (1 - 2^-17) and the roundings of S' -+ D below,
-// D = 2^-17 max_i s'_i + 2^-119 bounds |v_i - S'_i| for every output of the
-// block.  An element's code is taken from S' when the codes of S'_i - D and
-// S'_i + D agree (E2M1 rounding is monotone), the block exponent when the
-// exponents of a' - D and a' + D agree (a' = max |S'|); otherwise the value is
+// D_i = 2^-17 s'_i + 2^-119 bounds |v_i - S'_i|, and the block's largest,
+// D = max_i D_i, bounds that of every output of the block.  An element's code
+// is taken from S' when the codes of S'_i - D_i and S'_i + D_i agree (E2M1
+// rounding is monotone), the block exponent when the exponents of a' - D and
+// a' + D agree (a' = max |S'|); otherwise the value is
 // recomputed exactly from the bf16 operands in LDS (float64 sum of the exact
 // products in input order, rounded once, as in the float32 path above) and the
 // code, or the whole block, is redone from exact values.
@@ -306,25 +307,35 @@ dense32_mx_mfma_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t
       }
       am = max_halves(am);
       sm = max_halves(sm);
+      // the block exponent is certain when the exponents of the largest
+      // |S'| -+ the largest bound D_i agree; each code when the codes of
+      // S'_i -+ D_i agree, D_i = 2^-17 s_i + 2^-119 its own bound
       const float da = __builtin_fmaf(sm, 0x1p-17f, 0x1p-119f);
       int e = mx_exponent(am);
       // tiny blocks (e < -100, e.g. all zero) always take the exact path
       const bool blk = e < -100 || mx_exponent(fmaxf(am - da, 0.f)) != mx_exponent(am + da);
       float sc = __uint_as_float((uint32_t)(127 + max(e, -126)) << 23);  // 2^e, normal
+      float dl[16], dh[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float di = __builtin_fmaf(sig[b & 1][r], 0x1p-17f, 0x1p-119f);
+        dl[r] = ac[r] - di;
+        dh[r] = ac[r] + di;
+      }
       // codes of S' - D and S' + D; word k nibble n is register r = 8 k + n
       uint32_t wl[2], wh[2];
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const int r = 8 * k;
         uint32_t ol = 0u, oh = 0u;
-        ol = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(ol, ac[r] - da, ac[r + 1] - da, sc, 0);
-        oh = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(oh, ac[r] + da, ac[r + 1] + da, sc, 0);
-        ol = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(ol, ac[r + 2] - da, ac[r + 3] - da, sc, 1);
-        oh = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(oh, ac[r + 2] + da, ac[r + 3] + da, sc, 1);
-        ol = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(ol, ac[r + 4] - da, ac[r + 5] - da, sc, 2);
-        oh = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(oh, ac[r + 4] + da, ac[r + 5] + da, sc, 2);
-        ol = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(ol, ac[r + 6] - da, ac[r + 7] - da, sc, 3);
-        oh = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(oh, ac[r + 6] + da, ac[r + 7] + da, sc, 3);
+        ol = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(ol, dl[r], dl[r + 1], sc, 0);
+        oh = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(oh, dh[r], dh[r + 1], sc, 0);
+        ol = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(ol, dl[r + 2], dl[r + 3], sc, 1);
+        oh = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(oh, dh[r + 2], dh[r + 3], sc, 1);
+        ol = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(ol, dl[r + 4], dl[r + 5], sc, 2);
+        oh = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(oh, dh[r + 4], dh[r + 5], sc, 2);
+        ol = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(ol, dl[r + 6], dl[r + 7], sc, 3);
+        oh = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(oh, dh[r + 6], dh[r + 7], sc, 3);
         wl[k] = ol;
         wh[k] = oh;
       }
