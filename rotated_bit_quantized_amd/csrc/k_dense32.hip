@@ -359,12 +359,14 @@ dense32_mx_mfma_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t
           xin[2 * s] = h ? p : o;
           xin[2 * s + 1] = h ? o : p;
         }
-        // exact value of output r of this lane's token: float64 sum of the
-        // exact products in input order, rounded once
+        // exact value of output r of this lane's token (r may differ from
+        // lane to lane): four float64 partial sums of the exact products,
+        // each exact, as is their total, whenever the products span at most
+        // 32 binades; rounded once to float32
         auto exact = [&](int r) -> float {
           const int i = 8 * (r >> 2) + 4 * h + (r & 3);
           const uint4 *trow = reinterpret_cast<const uint4 *>(&Ts[0][b * 1024 + i * 32]);
-          double s64 = 0.0;
+          double sp[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const uint4 tw = trow[q];
@@ -372,27 +374,35 @@ dense32_mx_mfma_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t
             const uint32_t xws[4] = {xin[q].x, xin[q].y, xin[q].z, xin[q].w};
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-              s64 = __builtin_fma((double)bf16_lo(tws[k]), (double)bf16_lo(xws[k]), s64);
-              s64 = __builtin_fma((double)bf16_hi(tws[k]), (double)bf16_hi(xws[k]), s64);
+              sp[k] = __builtin_fma((double)bf16_lo(tws[k]), (double)bf16_lo(xws[k]), sp[k]);
+              sp[k] = __builtin_fma((double)bf16_hi(tws[k]), (double)bf16_hi(xws[k]), sp[k]);
             }
           }
-          return (float)s64;
+          return (float)((sp[0] + sp[1]) + (sp[2] + sp[3]));
         };
         // certain exponent: redo the outputs whose two codes differ and
-        // patch their nibbles
-        const bool el = valid && !blk;
-#pragma unroll 1
-        for (int r = 0; r < 16; ++r) {
-          const bool f = el && (((r < 8 ? d0 : d1) >> (4 * (r & 7))) & 0xFu) != 0u;
-          if (__ballot(f) == 0ull) continue;
-          if (f) {
+        // patch their nibbles, one flagged output per lane per pass (the
+        // lanes' outputs differ; a single pass is the common case)
+        uint32_t fm = 0u;  // bit r: nibble r of the two code words differs
+        if (valid && !blk) {
+#pragma unroll
+          for (int n = 0; n < 8; ++n) {
+            fm |= (((d0 >> (4 * n)) & 0xFu) != 0u ? 1u : 0u) << n;
+            fm |= (((d1 >> (4 * n)) & 0xFu) != 0u ? 1u : 0u) << (n + 8);
+          }
+        }
+        while (__ballot(fm != 0u) != 0ull) {
+          if (fm != 0u) {
+            const int r = __builtin_ctz(fm);
+            fm &= fm - 1u;
             const float ve = exact(r);
             const uint32_t c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, ve, ve, sc, 0) & 0xFu;
             const int sh = 4 * (r & 7);
+            const uint32_t keep = ~(0xFu << sh);
             if (r < 8)
-              wl[0] = (wl[0] & ~(0xFu << sh)) | (c << sh);
+              wl[0] = (wl[0] & keep) | (c << sh);
             else
-              wl[1] = (wl[1] & ~(0xFu << sh)) | (c << sh);
+              wl[1] = (wl[1] & keep) | (c << sh);
           }
         }
         // uncertain exponent (both lanes of the token): redo all 32 outputs,
