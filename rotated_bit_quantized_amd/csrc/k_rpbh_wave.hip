@@ -9,7 +9,10 @@
 //   * each wave keeps its row in LDS twice, as +x and -x; the gather offset
 //     of output i points into the copy whose sign is s_r[i], so the gather
 //     applies the sign.  The offsets of every round live in a workgroup LDS
-//     table written once, read per row with 16-byte loads;
+//     table written once, read per row with 16-byte loads.  With one round
+//     and no centring the row is kept once, each coordinate's sign applied
+//     as it is written (a sign mask scattered through the permutation), and
+//     8-wave workgroups run 4 waves per SIMD;
 //   * the first round gathers bfloat16 copies (the loaded words and their
 //     sign-flipped twins, no conversion on the write side); centering
 //     subtracts s_i m after the gather, which equals s_i RN32(x - m);
@@ -449,14 +452,24 @@ __device__ __forceinline__ uint32_t gsum_pieces(float p) {
   return (__float_as_uint(p1) >> 16) | (__float_as_uint(p - p1) & 0xFFFF0000u);
 }
 
-// LDS: [offset table: ROUNDS x SLOTS x 4 x 64 lanes x 4 ints][per wave: row copies]
+// LDS: [offset table: ROUNDS x SLOTS x 4 x 64 lanes x 4 ints]
+// [single-copy mode: bf16 sign mask of every input coordinate, SLOTS x 1024 x 2 bytes]
+// [per wave: row copies]
 // [Lloyd-Max modes: 128 float positive thresholds, 256 float16 levels, when
 // they fit in the 160 KiB; otherwise the kernel reads them from global memory]
-template <int SLOTS, int ROUNDS, bool LM>
+// Single-copy mode (ONE: one round, no centring, absmax or percentile
+// codes): each wave keeps one bf16 copy of its row with the signs applied as
+// it is written, so the row buffer is a quarter of the two-copy float32 /
+// half of the two-copy bf16 one, and workgroups of 8 waves run 4 waves per
+// SIMD (two per CU at d <= 3072).
+template <int SLOTS, int ROUNDS, bool LM, bool ONE = false>
 struct WaveLds {
+  static constexpr int W = ONE ? 8 : WAVES_PER_WG;  // waves per workgroup
   static constexpr int TABLE = (ROUNDS > 0 ? ROUNDS : 1) * SLOTS * 1024 * 4;
-  static constexpr int ROWBUF = (ROUNDS == 2 ? 8 : 4) * SLOTS * 1024;  // 2 copies, float32 if 2 rounds
-  static constexpr int LM_OFF = TABLE + WAVES_PER_WG * ROWBUF;
+  static constexpr int SMASK = ONE ? SLOTS * 1024 * 2 : 0;
+  // one bf16 copy; else 2 copies, float32 if 2 rounds
+  static constexpr int ROWBUF = ONE ? 2 * SLOTS * 1024 : (ROUNDS == 2 ? 8 : 4) * SLOTS * 1024;
+  static constexpr int LM_OFF = TABLE + SMASK + W * ROWBUF;
   static constexpr bool LM_LDS = LM && LM_OFF + 1024 <= 160 * 1024;
   static constexpr int TOTAL = LM_OFF + (LM_LDS ? 128 * 4 + 256 * 2 : 0);
 };
@@ -468,20 +481,25 @@ constexpr bool is_lm_mode() { return mode == OUT_LM4 || mode == OUT_LM8 || mode 
 // register count of each near what its own path needs.
 // KM > 0: the factorised rotation with Paley order KM (ROUNDS 0, h = b, din
 // the native width); otherwise din is unused.
-template <int SLOTS, int ROUNDS, int mode, bool PCTL, int KM = 0>
-__global__ void __launch_bounds__(64 * WAVES_PER_WG)
+template <int SLOTS, int ROUNDS, int mode, bool PCTL, int KM = 0, bool ONE = false>
+__global__ void __launch_bounds__(64 * (ONE ? 8 : WAVES_PER_WG))
+__attribute__((amdgpu_waves_per_eu(ONE ? 4 : 1)))
 rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, const int32_t *__restrict__ perm,
-                 const int8_t *__restrict__ signs, int h, float c_h, int pow4, int center,
+                 const int8_t *__restrict__ signs, int h, float c_h, int pow4, int center_arg,
                  float *__restrict__ mean_out, int qmax, void *__restrict__ out, int64_t ld_out_bytes,
                  float *__restrict__ scale_out, PctlArgs pa, LmArgs la, uint32_t *__restrict__ gsum_out, int din) {
   static_assert(KM == 0 || (ROUNDS == 0 && !PCTL && !is_lm_mode<mode>()), "factorised rotation: plain absmax modes");
+  static_assert(!ONE || (ROUNDS == 1 && KM == 0 && !is_lm_mode<mode>()), "single copy: one round, absmax/percentile");
   constexpr bool LM = is_lm_mode<mode>();
-  using L = WaveLds<SLOTS, ROUNDS, LM>;
+  using L = WaveLds<SLOTS, ROUNDS, LM, ONE>;
+  constexpr int W = L::W;
+  const int center = ONE ? 0 : center_arg;  // the single-copy kernel is launched without centring
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   int *table = reinterpret_cast<int *>(lds_raw);
-  uint8_t *buf = lds_raw + L::TABLE + wave * L::ROWBUF;
+  uint16_t *smask = reinterpret_cast<uint16_t *>(lds_raw + L::TABLE);
+  uint8_t *buf = lds_raw + L::TABLE + L::SMASK + wave * L::ROWBUF;
   const int nlog = __builtin_ctz((unsigned)h) - 4;  // a Hadamard block spans 2^nlog lanes
   const int il = index_lane(lane, nlog);             // this lane holds coordinates 16 il + j of each slot
 
@@ -508,14 +526,13 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
   // ---- offset table: byte offsets into this wave's [+row | -row] buffer;
   // first-round copies are bf16 (2 bytes), second-round copies float32.
   // Entry (r, s, lane l, j) is coordinate 1024 s + 16 index_lane(l) + j;
-  // each task fills 4 consecutive j.  All its loads are issued before the
-  // first row's, so the table is built while that row is in flight.
+  // each task fills 4 consecutive j.
   constexpr int TASKS = (ROUNDS > 0 ? ROUNDS : 0) * SLOTS * 256;
-  constexpr int NT = (TASKS + 64 * WAVES_PER_WG - 1) / (64 * WAVES_PER_WG);
+  constexpr int NT = (TASKS + 64 * W - 1) / (64 * W);
   int pv[NT > 0 ? NT : 1][4], sv[NT > 0 ? NT : 1][4];
 #pragma unroll
   for (int k = 0; k < NT; ++k) {
-    const int q = threadIdx.x + k * 64 * WAVES_PER_WG;
+    const int q = threadIdx.x + k * 64 * W;
     const int r = q / (SLOTS * 256), rem = q % (SLOTS * 256);
     const int s = rem / 256, l = (rem / 4) % 64, j0 = 4 * (rem % 4);
     const int i0 = 1024 * s + 16 * index_lane(l, nlog) + j0;
@@ -529,13 +546,14 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
     }
   }
 
-  const int64_t step = (int64_t)gridDim.x * WAVES_PER_WG;
-  // the next row's words are loaded while the current row is processed (the
-  // index is clamped to the last row, so the final prefetch stays in bounds);
-  // lanes beyond the row end read their own first word instead
+  const int64_t step = (int64_t)gridDim.x * W;
+  // the next row's words are loaded while the current row is processed; the
+  // last row of a wave reloads its own words (cached) rather than another
+  // row, so the final prefetches of all waves do not meet on one row; lanes
+  // beyond the row end read their own first word instead
   uint4 nxt[SLOTS][2];
   auto load_row = [&](int64_t rr) {
-    const uint16_t *xr = x + (rr < M ? rr : M - 1) * ldx;
+    const uint16_t *xr = x + rr * ldx;
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s) {
       const uint4 *src = reinterpret_cast<const uint4 *>(xr + (ld[s] ? 1024 * s + 16 * ll : 0));
@@ -543,20 +561,35 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
       nxt[s][1] = src[1];
     }
   };
-  int64_t row = (int64_t)blockIdx.x * WAVES_PER_WG + wave;
-  load_row(row);  // unconditional (clamped index): the table's waits then leave it in flight
+  int64_t row = (int64_t)blockIdx.x * W + wave;
 
+  if constexpr (ONE) {
+    // the sign mask starts at zero, so a perm that is not a permutation (the
+    // caller's contract) still gives deterministic, in-bounds results
+    for (int i = threadIdx.x; i < SLOTS * 128; i += 64 * W) reinterpret_cast<uint4 *>(smask)[i] = make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+  }
 #pragma unroll
   for (int k = 0; k < NT; ++k) {
-    const int q = threadIdx.x + k * 64 * WAVES_PER_WG;
+    const int q = threadIdx.x + k * 64 * W;
     if (q >= TASKS) continue;
     const int r = q / (SLOTS * 256), rem = q % (SLOTS * 256);
     const int s = rem / 256, l = (rem / 4) % 64, jq = rem % 4;
     const int i0 = 1024 * s + 16 * index_lane(l, nlog) + 4 * jq;
     int o[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      o[e] = i0 < d ? (pv[k][e] + (sv[k][e] < 0 ? d : 0)) * (r == 0 ? 2 : 4) : 0;
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (ONE) {
+        // the row copy is signed as it is written: the sign of output i0 + e
+        // goes to the input coordinate it gathers (a permutation: every
+        // coordinate below d is written once)
+        const int pc = min(max(pv[k][e], 0), d - 1);
+        o[e] = i0 < d ? 2 * pc : 0;
+        if (i0 < d) smask[pc] = sv[k][e] < 0 ? 0x8000u : 0u;
+      } else {
+        o[e] = i0 < d ? (pv[k][e] + (sv[k][e] < 0 ? d : 0)) * (r == 0 ? 2 : 4) : 0;
+      }
+    }
     reinterpret_cast<int4 *>(table)[((r * SLOTS + s) * 4 + jq) * 64 + l] = make_int4(o[0], o[1], o[2], o[3]);
   }
   // Lloyd-Max tables: pos[j] = thr[hh - 1 + j], j = 1 .. hh - 1 (the
@@ -564,6 +597,10 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
   float *lm_pos = reinterpret_cast<float *>(lds_raw + L::LM_OFF);
   uint16_t *lm_lv = reinterpret_cast<uint16_t *>(lds_raw + L::LM_OFF + 512);
   const int hh = LM ? 1 << (la.bits - 1) : 1;
+  // the first row is requested once the table's own loads have returned:
+  // issued earlier, they would queue behind every wave's row (the chip-wide
+  // first burst) and the table would wait for it
+  load_row(row < M ? row : M - 1);
   if constexpr (L::LM_LDS) {
     const int t = threadIdx.x;
     if (t >= 1 && t < hh) lm_pos[t] = la.thr[hh - 1 + t];
@@ -579,7 +616,7 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
       raw[s][0] = nxt[s][0];
       raw[s][1] = nxt[s][1];
     }
-    load_row(row + step);
+    load_row(row + step < M ? row + step : row);
 
     float m = 0.f;
     if (center) {
@@ -611,18 +648,28 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
     }
 
     if (ROUNDS >= 1) {
-      // first-round writer: bf16 +row and -row at natural coordinates
+      // first-round writer: bf16 +row and -row at natural coordinates, or
+      // (single copy) the row with each coordinate's sign applied
 #pragma unroll
       for (int s = 0; s < SLOTS; ++s) {
         if (!ld[s]) continue;
         const int p0 = 1024 * s + 16 * lane;
         uint4 *dp = reinterpret_cast<uint4 *>(buf + 2 * p0);
-        uint4 *dn = reinterpret_cast<uint4 *>(buf + 2 * (p0 + d));
+        if constexpr (ONE) {
+          const uint4 *sm = reinterpret_cast<const uint4 *>(smask + p0);
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const uint4 w = raw[s][k];
-          dp[k] = w;
-          dn[k] = make_uint4(w.x ^ 0x80008000u, w.y ^ 0x80008000u, w.z ^ 0x80008000u, w.w ^ 0x80008000u);
+          for (int k = 0; k < 2; ++k) {
+            const uint4 w = raw[s][k], m = sm[k];
+            dp[k] = make_uint4(w.x ^ m.x, w.y ^ m.y, w.z ^ m.z, w.w ^ m.w);
+          }
+        } else {
+          uint4 *dn = reinterpret_cast<uint4 *>(buf + 2 * (p0 + d));
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const uint4 w = raw[s][k];
+            dp[k] = w;
+            dn[k] = make_uint4(w.x ^ 0x80008000u, w.y ^ 0x80008000u, w.z ^ 0x80008000u, w.w ^ 0x80008000u);
+          }
         }
       }
       // gather (the wave's own LDS writes are ordered before its reads);
@@ -954,26 +1001,37 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
   }
 }
 
-template <int SLOTS, int ROUNDS, int MODE, bool PCTL, int KM = 0>
+template <int SLOTS, int ROUNDS, int MODE, bool PCTL, int KM = 0, bool ONE = false>
 hipError_t launch_m(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotArgs &rot, int center, float *mean,
                     int qmax, void *out, int64_t ld_out_bytes, float *scale, const PctlArgs &pa, const LmArgs &la,
                     uint32_t *gsum, hipStream_t stream, int din = 0) {
-  using L = WaveLds<SLOTS, ROUNDS, is_lm_mode<MODE>()>;
+  using L = WaveLds<SLOTS, ROUNDS, is_lm_mode<MODE>(), ONE>;
   const size_t lds = (size_t)L::TOTAL;
   static bool attr_set = false;
   if (!attr_set && lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void *)rpbh_wave_kernel<SLOTS, ROUNDS, MODE, PCTL, KM>,
+    hipError_t e = hipFuncSetAttribute((const void *)rpbh_wave_kernel<SLOTS, ROUNDS, MODE, PCTL, KM, ONE>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  // two or more rows per wave so the offset table is amortised
-  int64_t grid = (M + 2 * WAVES_PER_WG - 1) / (2 * WAVES_PER_WG);
-  if (grid > 1024) grid = 1024;
+  int64_t grid;
+  if constexpr (ONE) {
+    // one row per wave while every workgroup fits on the chip at once
+    // (workgroups per CU: the LDS allows 160 KiB / TOTAL, the registers of
+    // 4 waves per SIMD two), more rows per wave beyond
+    const int64_t per_cu = (int64_t)(160 * 1024 / L::TOTAL) < 2 ? (int64_t)(160 * 1024 / L::TOTAL) : 2;
+    const int64_t cap = per_cu * device_cus();
+    grid = (M + L::W - 1) / L::W;
+    if (grid > cap) grid = cap;
+  } else {
+    // two or more rows per wave so the offset table is amortised
+    grid = (M + 2 * L::W - 1) / (2 * L::W);
+    if (grid > 1024) grid = 1024;
+  }
   if (grid < 1) grid = 1;
   const int h = (ROUNDS || KM) ? rot.block : 16;
   const int pow4 = ROUNDS && ((__builtin_ctz((unsigned)h) & 1) == 0);
-  hipLaunchKernelGGL((rpbh_wave_kernel<SLOTS, ROUNDS, MODE, PCTL, KM>), dim3((unsigned)grid), dim3(64 * WAVES_PER_WG),
+  hipLaunchKernelGGL((rpbh_wave_kernel<SLOTS, ROUNDS, MODE, PCTL, KM, ONE>), dim3((unsigned)grid), dim3(64 * L::W),
                      lds, stream, x, M, d, ldx, rot.perm, rot.signs, h, rot.c_h, pow4, center, mean, qmax, out,
                      ld_out_bytes, scale, pa, la, gsum, din);
   return hipGetLastError();
@@ -992,11 +1050,22 @@ hipError_t launch_p(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotA
                                                 *lm, gsum, stream);
   } else {
     if (lm) return hipErrorInvalidValue;
+    // one round without centring: the single-copy kernel, for the widths
+    // and outputs whose registers fit 4 waves per SIMD (128) without spills
+    constexpr bool ONE_OK = ROUNDS == 1 && SLOTS <= 3 && !(MODE == OUT_FP6X2 && SLOTS > 1);
+    const bool one = ONE_OK && !center;
     if (pctl) {
       if constexpr (MODE == OUT_F32) return hipErrorInvalidValue;
-      else return launch_m<SLOTS, ROUNDS, MODE, true>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale,
-                                                      *pctl, no_lm, gsum, stream);
+      else if (one)
+        return launch_m<SLOTS, ROUNDS, MODE, true, 0, ONE_OK>(x, M, d, ldx, rot, center, mean, qmax, out,
+                                                              ld_out_bytes, scale, *pctl, no_lm, gsum, stream);
+      else
+        return launch_m<SLOTS, ROUNDS, MODE, true>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale,
+                                                   *pctl, no_lm, gsum, stream);
     }
+    if (one)
+      return launch_m<SLOTS, ROUNDS, MODE, false, 0, ONE_OK>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes,
+                                                             scale, no_p, no_lm, gsum, stream);
     return launch_m<SLOTS, ROUNDS, MODE, false>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, no_p,
                                                 no_lm, gsum, stream);
   }

@@ -37,7 +37,10 @@ def _meta(K, h, rounds, seed):
 
 
 @pytest.mark.parametrize("M,K,h,rounds,center,afmt", [(37, 1024, 128, 1, False, 4), (70, 3072, 1024, 1, True, 4),
-                                                      (33, 1920, 128, 2, False, 6), (5, 256, 32, 1, True, 6)])
+                                                      (33, 1920, 128, 2, False, 6), (5, 256, 32, 1, True, 6),
+                                                      # one round, no centring (single row copy): more rows
+                                                      # than waves on the chip, a ragged tail, one-slot A6
+                                                      (9000, 3072, 1024, 1, False, 4), (77, 1024, 1024, 1, False, 6)])
 def test_tiled_activation_writer(oq, M, K, h, rounds, center, afmt):
     say("case tiled act", M, K, h, rounds, center, afmt)
     perm, signs = _meta(K, h, rounds, 11)
