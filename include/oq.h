@@ -400,8 +400,9 @@ int oq_prepack_w16(const uint8_t *w, const float *w_scale, int32_t N, int32_t K,
  *   ws, which needs oq_workspace_bytes(OQ_OP_GEMM_LM, M, K, N, 0) bytes.
  * w16_tiled from oq_prepack_w16; a_scale float32 [M]; mean and w1 both NULL
  * or both set; bias nullable; y bf16 [M][ldy].  K % 32 == 0.
- * The workgroup shape (256 x 256 or 256 x 192 outputs) follows M, N and the
- * CU count; OQ_F16_TILE=256x256 or 256x192 in the environment forces one.
+ * The workgroup shape (256 x 384, 256 x 256 or 256 x 192 outputs) follows M, N and the
+ * CU count; OQ_F16_TILE=256x384, 256x256 or 256x192 in the environment forces
+ * one.
  * The result does not depend on the shape.
  */
 int oq_gemm_lm(int32_t bits, int tiled, const void *qa, int64_t lda_bytes, const float *a_scale, int64_t M,

@@ -15,13 +15,16 @@
 // one 16-byte LDS read per lane, conflict-free.
 //
 // Workgroup of 8 wavefronts, each TI x TJ MFMA tiles of 32 x 32 accumulated
-// in place: TI = 4, TJ = 2 in a 2 x 4 grid (256 x 256 outputs) or TI = 2,
-// TJ = 3 in a 4 x 2 grid (256 x 192, for products whose 256 x 256 tiles
-// would leave CUs idle).  k advances in stages of 32 (two chunks per 32-row
-// block): every wave copies 4 KiB of each stage global -> LDS with
-// global_load_lds_dwordx4 into a 4-slot ring, one barrier per stage.  A
-// stage always holds 8 row blocks and 8 column blocks (a 192-wide tile
-// loads two column blocks past its end and leaves them unread).
+// in place: TI = 4, TJ = 2 in a 2 x 4 grid (256 x 256 outputs), TI = 4,
+// TJ = 3 in a 2 x 4 grid (256 x 384: a third less LDS reading per MFMA, the
+// accumulators in AGPRs) or TI = 2, TJ = 3 in a 4 x 2 grid (256 x 192, for
+// products whose wider tiles would leave CUs idle).  k advances in stages of
+// 32 (two chunks per 32-row block): every wave copies the same share of
+// each stage global -> LDS with global_load_lds_dwordx4 into a ring of
+// stages (4 slots; 3 for the 384-wide tile), one barrier per stage.  A stage
+// holds 8 row blocks and the tile's column blocks (a 192-wide tile loads
+// two column blocks past its end and leaves them unread, so that the copies
+// split evenly over the waves).
 #include "oq_internal.h"
 
 #include <cstdlib>
@@ -42,15 +45,20 @@ struct F16C {
   static constexpr int WAVES_M = 8 / TI, WAVES_N = 8 / WAVES_M;
   static constexpr int BN = 32 * TJ * WAVES_N;
   static constexpr int SROW = 64 * TJ + 16;  // padded bytes per staged output row of 32 TJ bf16
+  static constexpr int B_BLOCKS = BN == 192 ? 8 : BN / 32;
   static constexpr int A_BYTES = (F16_BM / 32) * KC * 1024;
-  static constexpr int B_BYTES = 8 * KC * 1024;
+  static constexpr int B_BYTES = B_BLOCKS * KC * 1024;
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int ROWS_OFF = NSLOT * STAGE;
   static constexpr int LDS = ROWS_OFF + 2 * F16_BM * 4;
-  static constexpr int PER_STAGE = 2 * KC;  // 1 KiB copies per wave per stage
+  static constexpr int PER_STAGE = (8 + B_BLOCKS) * KC / 8;  // 1 KiB copies per wave per stage
+  // more than 8 tiles per wave: one register per fragment, reloaded right
+  // after its last MFMA of the chunk (a second set would not fit beside
+  // the accumulators)
+  static constexpr bool SINGLE = TI * TJ > 8;
   static_assert(8 * PER_STAGE * 1024 == STAGE, "every wave copies the same share of a stage");
   static_assert(8 * 32 * SROW <= ROWS_OFF, "the epilogue staging fits in the ring");
-  static_assert(32 * TI * WAVES_M == F16_BM && BN <= 256, "workgroup shape");
+  static_assert(32 * TI * WAVES_M == F16_BM && BN <= 384, "workgroup shape");
   static_assert(LDS <= 160 * 1024, "LDS");
   // chunk 0 of stage g + 1 is read during stage g, so stage g + 1 must be in
   // flight before stage g starts (NSLOT >= 3); the waits below count exactly
@@ -161,6 +169,39 @@ gemm_f16_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_scale
     else wait_vm<0>();
   }
   __builtin_amdgcn_s_barrier();
+  if constexpr (C::SINGLE) {
+    // tiles column-major (i fastest), so a[i] is reloaded after tile
+    // (i, TJ - 1) and b[j] after tile (TI - 1, j), each at least TI tiles
+    // before its next use
+    v8h a[TI], b[TJ];
+    load(a, b, 0, 0);
+    for (int g = 0; g < S; ++g) {
+      if constexpr (NSLOT >= 4) {
+        if (g + 2 < S) wait_vm<(NSLOT - 3) * C::PER_STAGE>();
+        else wait_vm<0>();
+      } else {
+        wait_vm<0>();
+      }
+      wait_lgkm0();
+      __builtin_amdgcn_s_barrier();
+      if (g + NSLOT - 1 < S) issue((g + NSLOT - 1) % NSLOT, g + NSLOT - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      const int slot = g % NSLOT;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        // the next chunk: this stage's next, or chunk 0 of the next stage
+        // (after the last stage a slot whose contents are never used)
+        const int ns = kc + 1 < KC ? slot : (g + 1) % NSLOT, nk = kc + 1 < KC ? kc + 1 : 0;
+#pragma unroll
+        for (int t = 0; t < TI * TJ; ++t) {
+          const int i = t % TI, j = t / TI;
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+          if (j == TJ - 1) a[i] = *reinterpret_cast<const v8h *>(fa + ns * C::STAGE + (i * KC + nk) * 1024);
+          if (i == TI - 1) b[j] = *reinterpret_cast<const v8h *>(fb + ns * C::STAGE + (j * KC + nk) * 1024);
+        }
+      }
+    }
+  } else {
   v8h fr[2][TI], gr[2][TJ];
   load(fr[0], gr[0], 0, 0);
 
@@ -190,6 +231,8 @@ gemm_f16_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_scale
 #pragma unroll
       for (int j = 0; j < TJ; ++j) gr[0][j] = gr[1][j];
     }
+  }
+
   }
 
   // ---- epilogue: y = rho F + m w1 + b, bf16, staged per 32-row slab in this
@@ -351,23 +394,23 @@ hipError_t launch_f16(const uint8_t *A, const float *a_scale, int64_t M, int K, 
   return hipGetLastError();
 }
 
-// 256 x 192 tiles when their whole waves of workgroups (one per CU) cover
-// fewer output columns than 256 x 256 tiles (4096 x 3072 on 256 CUs: 256
-// tiles instead of 192).  OQ_F16_TILE=256x256 or 256x192 in the environment
-// forces one (for tuning and tests).
-bool f16_narrow(int64_t M, int N) {
+// Tile width: the one whose whole waves of workgroups (one per CU) cover the
+// fewest output columns, the wider on a tie (4096 x 3072 on 256 CUs: 256
+// tiles of 256 x 192; 4096 x 12288: 512 tiles of 256 x 384).
+// OQ_F16_TILE=256x384, 256x256 or 256x192 in the environment forces one
+// (for tuning and tests).
+int f16_width(int64_t M, int N) {
   if (const char *f = getenv("OQ_F16_TILE")) {
-    if (strcmp(f, "256x256") == 0) return false;
-    if (strcmp(f, "256x192") == 0) return true;
+    if (strcmp(f, "256x384") == 0) return 384;
+    if (strcmp(f, "256x256") == 0) return 256;
+    if (strcmp(f, "256x192") == 0) return 192;
   }
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    cus = 256;
+  const int64_t cus = device_cus();
   const int64_t mt = (M + 255) / 256;
-  const int64_t w256 = (mt * ((N + 255) / 256) + cus - 1) / cus;
-  const int64_t w192 = (mt * ((N + 191) / 192) + cus - 1) / cus;
-  return w192 * 192 < w256 * 256;
+  auto covered = [&](int w) { return (mt * ((N + w - 1) / w) + cus - 1) / cus * w; };
+  const int64_t c384 = covered(384), c256 = covered(256), c192 = covered(192);
+  if (c384 <= c256 && c384 <= c192) return 384;
+  return c256 <= c192 ? 256 : 192;
 }
 
 }  // namespace
@@ -377,7 +420,9 @@ hipError_t launch_gemm_f16(const uint8_t *A, const float *a_scale, int64_t M, in
                            hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   const int Np = (N + 31) / 32 * 32;
-  if (f16_narrow(M, N)) return launch_f16<2, 4, 2, 3>(A, a_scale, M, K, W, N, Np, mean, w1, bias, y, ldy, stream);
+  const int w = f16_width(M, N);
+  if (w == 192) return launch_f16<2, 4, 2, 3>(A, a_scale, M, K, W, N, Np, mean, w1, bias, y, ldy, stream);
+  if (w == 384) return launch_f16<2, 3, 4, 3>(A, a_scale, M, K, W, N, Np, mean, w1, bias, y, ldy, stream);
   return launch_f16<2, 4, 4, 2>(A, a_scale, M, K, W, N, Np, mean, w1, bias, y, ldy, stream);
 }
 

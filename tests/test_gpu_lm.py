@@ -187,10 +187,12 @@ def test_gemm_lm(oq, M, K, N, bits, center, bias):
     say("  within 1 bf16 ulp:", frac)
 
 
-@pytest.mark.parametrize("shape", ["256x256", "256x192"])
-@pytest.mark.parametrize("M,K,N,bits", [(300, 1024, 520, 4), (257, 512, 1000, 8), (600, 3072, 3072, 4)])
+@pytest.mark.parametrize("shape", ["256x384", "256x256", "256x192"])
+@pytest.mark.parametrize("M,K,N,bits", [(300, 1024, 520, 4), (257, 512, 1000, 8), (600, 3072, 3072, 4),
+                                        (2100, 256, 12288, 4)])
 def test_gemm_lm_shapes(oq, monkeypatch, shape, M, K, N, bits):
-    """Both workgroup shapes of the float16 GEMM, forced through OQ_F16_TILE."""
+    """Every workgroup shape of the float16 GEMM, forced through OQ_F16_TILE,
+    on ragged sizes and on more tiles than CUs."""
     say("case gemm lm shape", shape, M, K, N, bits)
     monkeypatch.setenv("OQ_F16_TILE", shape)
     rng = np.random.default_rng(M + 5 * N + K)
