@@ -685,13 +685,15 @@ int64_t covered_columns(int64_t M, int N, int w, int64_t cus) {
 // Workgroup shape for an M x N product.  Large products take the 8-wave
 // shape whose whole waves of workgroups (one per CU) cover the fewest output
 // columns, the wider one on a tie (per output 256 x 256 runs 6% faster than
-// 256 x 192): 4096 x 3072 on 256 CUs takes 256 x 192 (256 tiles instead of
-// 192 of 256 x 256), 4096 x 12288 256 x 256.  Single-plane products with
-// fewer 256 x 256 tiles than half the CUs take the 4-wave 128 x 192 shape:
-// 2.7x more workgroups, each with a CU to itself.  The 4-wave shapes match
-// the 8-wave ones per output when the CUs are full.  Two-plane (6-bit)
-// products choose between the 8-wave 256 x 192 and 256 x 128 shapes only
-// (4096 x 1920: 240 tiles of 256 x 128 instead of 160 of 256 x 192).
+// 256 x 192), 256 x 128 only where it covers less than 5/6 of the others:
+// 4096 x 3072 on 256 CUs takes 256 x 192 (256 tiles instead of 192 of
+// 256 x 256), 4096 x 12288 256 x 256.  Single-plane products with fewer
+// 256 x 256 tiles than half the CUs take the 4-wave 128 x 192 shape: 2.7x
+// more workgroups, each with a CU to itself.  The 4-wave shapes match the
+// 8-wave ones per output when the CUs are full.  Two-plane (6-bit) products
+// choose between the 8-wave 256 x 192 and 256 x 128 shapes only (4096 x
+// 1920: 240 tiles of 256 x 128 instead of 160 of 256 x 192; 4096 x 7680
+// stays with 256 x 192).
 // OQ_FP6_TILE=256x256, 256x192, 256x128w8, 256x128 or 128x192 in the
 // environment forces one shape (for tuning and tests; two-plane products
 // take 256x192 or 256x128w8 only); any other value, or none, chooses.
@@ -707,12 +709,16 @@ Shape pick_shape(int64_t M, int N, int planes = 1) {
   }
   const int64_t cus = device_cus();
   const int64_t c192 = covered_columns(M, N, 192, cus), c128 = covered_columns(M, N, 128, cus);
-  if (planes == 2) return c128 < c192 ? Shape::W8_256x128 : Shape::W8_256x192;
+  // a column of the 256 x 128 shape costs about 1.2 times one of the wider
+  // shapes (more fragment reads per MFMA), so it is taken only where it
+  // covers that much less
+  const bool narrow = 6 * c128 < 5 * c192;
+  if (planes == 2) return narrow ? Shape::W8_256x128 : Shape::W8_256x192;
   const int64_t t256 = (M + 255) / 256 * ((N + 255) / 256);
   if (2 * t256 < cus) return Shape::W4_128x192;
   const int64_t c256 = covered_columns(M, N, 256, cus);
-  if (c256 <= c192 && c256 <= c128) return Shape::W8_256x256;
-  return c192 <= c128 ? Shape::W8_256x192 : Shape::W8_256x128;
+  if (narrow && 6 * c128 < 5 * c256) return Shape::W8_256x128;
+  return c256 <= c192 ? Shape::W8_256x256 : Shape::W8_256x192;
 }
 
 template <int NSLOT, bool PAIRED, bool ASYM>
