@@ -10,9 +10,10 @@
 //     of output i points into the copy whose sign is s_r[i], so the gather
 //     applies the sign.  The offsets of every round live in a workgroup LDS
 //     table written once, read per row with 16-byte loads.  With one round
-//     and no centring the row is kept once, each coordinate's sign applied
-//     as it is written (a sign mask scattered through the permutation), and
-//     8-wave workgroups run 4 waves per SIMD;
+//     the row is kept once, each coordinate's sign applied as it is written
+//     (a sign mask scattered through the permutation; centring adds the same
+//     mask into the sign of m), and 8-wave workgroups run 4 waves per SIMD
+//     (4-wave ones at 3 per SIMD when centring);
 //   * the first round gathers bfloat16 copies (the loaded words and their
 //     sign-flipped twins, no conversion on the write side); centering
 //     subtracts s_i m after the gather, which equals s_i RN32(x - m);
@@ -457,14 +458,16 @@ __device__ __forceinline__ uint32_t gsum_pieces(float p) {
 // [per wave: row copies]
 // [Lloyd-Max modes: 128 float positive thresholds, 256 float16 levels, when
 // they fit in the 160 KiB; otherwise the kernel reads them from global memory]
-// Single-copy mode (ONE: one round, no centring, absmax or percentile
-// codes): each wave keeps one bf16 copy of its row with the signs applied as
-// it is written, so the row buffer is a quarter of the two-copy float32 /
-// half of the two-copy bf16 one, and workgroups of 8 waves run 4 waves per
-// SIMD (two per CU at d <= 3072).
-template <int SLOTS, int ROUNDS, bool LM, bool ONE = false>
+// Single-copy mode (ONE: one round, absmax or percentile codes): each wave
+// keeps one bf16 copy of its row with the signs applied as it is written, so
+// the row buffer is half of the two-copy one, and workgroups of 8 waves run
+// 4 waves per SIMD (two per CU at d <= 3072); centred (CEN1), 4-wave
+// workgroups at 3 per SIMD.
+template <int SLOTS, int ROUNDS, bool LM, bool ONE = false, bool CEN1 = false>
 struct WaveLds {
-  static constexpr int W = ONE ? 8 : WAVES_PER_WG;  // waves per workgroup
+  // waves per workgroup: the centred single-copy body needs up to 168
+  // registers (3 waves per SIMD), so it runs 4-wave workgroups, three per CU
+  static constexpr int W = ONE ? (CEN1 ? 4 : 8) : WAVES_PER_WG;
   static constexpr int TABLE = (ROUNDS > 0 ? ROUNDS : 1) * SLOTS * 1024 * 4;
   static constexpr int SMASK = ONE ? SLOTS * 1024 * 2 : 0;
   // one bf16 copy; else 2 copies, float32 if 2 rounds
@@ -481,19 +484,20 @@ constexpr bool is_lm_mode() { return mode == OUT_LM4 || mode == OUT_LM8 || mode 
 // register count of each near what its own path needs.
 // KM > 0: the factorised rotation with Paley order KM (ROUNDS 0, h = b, din
 // the native width); otherwise din is unused.
-template <int SLOTS, int ROUNDS, int mode, bool PCTL, int KM = 0, bool ONE = false>
-__global__ void __launch_bounds__(64 * (ONE ? 8 : WAVES_PER_WG))
-__attribute__((amdgpu_waves_per_eu(ONE ? 4 : 1)))
+template <int SLOTS, int ROUNDS, int mode, bool PCTL, int KM = 0, bool ONE = false, bool CEN1 = false>
+__global__ void __launch_bounds__(64 * (ONE ? (CEN1 ? 4 : 8) : WAVES_PER_WG))
+__attribute__((amdgpu_waves_per_eu(ONE ? (CEN1 ? 3 : 4) : 1)))
 rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, const int32_t *__restrict__ perm,
                  const int8_t *__restrict__ signs, int h, float c_h, int pow4, int center_arg,
                  float *__restrict__ mean_out, int qmax, void *__restrict__ out, int64_t ld_out_bytes,
                  float *__restrict__ scale_out, PctlArgs pa, LmArgs la, uint32_t *__restrict__ gsum_out, int din) {
   static_assert(KM == 0 || (ROUNDS == 0 && !PCTL && !is_lm_mode<mode>()), "factorised rotation: plain absmax modes");
   static_assert(!ONE || (ROUNDS == 1 && KM == 0 && !is_lm_mode<mode>()), "single copy: one round, absmax/percentile");
+  static_assert(!CEN1 || ONE, "centring is a compile-time choice of the single-copy kernel");
   constexpr bool LM = is_lm_mode<mode>();
-  using L = WaveLds<SLOTS, ROUNDS, LM, ONE>;
+  using L = WaveLds<SLOTS, ROUNDS, LM, ONE, CEN1>;
   constexpr int W = L::W;
-  const int center = ONE ? 0 : center_arg;  // the single-copy kernel is launched without centring
+  const int center = ONE ? (CEN1 ? 1 : 0) : center_arg;  // compile-time in the single-copy kernel
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -690,7 +694,13 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const float g = __uint_as_float((uint32_t)(*reinterpret_cast<const uint16_t *>(buf + oo[e])) << 16);
-              if constexpr (CEN) {
+              if constexpr (CEN && ONE) {
+                // the copy holds s x; s m is m with the coordinate's sign
+                // mask added into its sign bit (the same byte offset in the
+                // mask table), so s x - s m = s RN32(x - m) as before
+                const uint32_t sb = *reinterpret_cast<const uint16_t *>(reinterpret_cast<const uint8_t *>(smask) + oo[e]);
+                v[s][4 * k + e] = g - __uint_as_float((sb << 16) + __float_as_uint(m));
+              } else if constexpr (CEN) {
                 const float mm = oo[e] >= neg_from ? -m : m;
                 v[s][4 * k + e] = g - mm;
               } else {
@@ -1001,15 +1011,15 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
   }
 }
 
-template <int SLOTS, int ROUNDS, int MODE, bool PCTL, int KM = 0, bool ONE = false>
+template <int SLOTS, int ROUNDS, int MODE, bool PCTL, int KM = 0, bool ONE = false, bool CEN1 = false>
 hipError_t launch_m(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotArgs &rot, int center, float *mean,
                     int qmax, void *out, int64_t ld_out_bytes, float *scale, const PctlArgs &pa, const LmArgs &la,
                     uint32_t *gsum, hipStream_t stream, int din = 0) {
-  using L = WaveLds<SLOTS, ROUNDS, is_lm_mode<MODE>(), ONE>;
+  using L = WaveLds<SLOTS, ROUNDS, is_lm_mode<MODE>(), ONE, CEN1>;
   const size_t lds = (size_t)L::TOTAL;
   static bool attr_set = false;
   if (!attr_set && lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void *)rpbh_wave_kernel<SLOTS, ROUNDS, MODE, PCTL, KM, ONE>,
+    hipError_t e = hipFuncSetAttribute((const void *)rpbh_wave_kernel<SLOTS, ROUNDS, MODE, PCTL, KM, ONE, CEN1>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
@@ -1017,9 +1027,11 @@ hipError_t launch_m(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotA
   int64_t grid;
   if constexpr (ONE) {
     // one row per wave while every workgroup fits on the chip at once
-    // (workgroups per CU: the LDS allows 160 KiB / TOTAL, the registers of
-    // 4 waves per SIMD two), more rows per wave beyond
-    const int64_t per_cu = (int64_t)(160 * 1024 / L::TOTAL) < 2 ? (int64_t)(160 * 1024 / L::TOTAL) : 2;
+    // (workgroups per CU: the LDS allows 160 KiB / TOTAL, the registers
+    // two of 8 waves at 4 per SIMD, three of 4 waves at 3 per SIMD), more
+    // rows per wave beyond
+    const int64_t by_regs = CEN1 ? 3 : 2, by_lds = 160 * 1024 / L::TOTAL;
+    const int64_t per_cu = by_lds < by_regs ? by_lds : by_regs;
     const int64_t cap = per_cu * device_cus();
     grid = (M + L::W - 1) / L::W;
     if (grid > cap) grid = cap;
@@ -1031,7 +1043,7 @@ hipError_t launch_m(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotA
   if (grid < 1) grid = 1;
   const int h = (ROUNDS || KM) ? rot.block : 16;
   const int pow4 = ROUNDS && ((__builtin_ctz((unsigned)h) & 1) == 0);
-  hipLaunchKernelGGL((rpbh_wave_kernel<SLOTS, ROUNDS, MODE, PCTL, KM, ONE>), dim3((unsigned)grid), dim3(64 * L::W),
+  hipLaunchKernelGGL((rpbh_wave_kernel<SLOTS, ROUNDS, MODE, PCTL, KM, ONE, CEN1>), dim3((unsigned)grid), dim3(64 * L::W),
                      lds, stream, x, M, d, ldx, rot.perm, rot.signs, h, rot.c_h, pow4, center, mean, qmax, out,
                      ld_out_bytes, scale, pa, la, gsum, din);
   return hipGetLastError();
@@ -1050,20 +1062,25 @@ hipError_t launch_p(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotA
                                                 *lm, gsum, stream);
   } else {
     if (lm) return hipErrorInvalidValue;
-    // one round without centring: the single-copy kernel, for the widths
+    // one round: the single-copy kernel (centred or not), for the widths
     // and outputs whose registers fit 4 waves per SIMD (128) without spills
     constexpr bool ONE_OK = ROUNDS == 1 && SLOTS <= 3 && !(MODE == OUT_FP6X2 && SLOTS > 1);
-    const bool one = ONE_OK && !center;
     if (pctl) {
       if constexpr (MODE == OUT_F32) return hipErrorInvalidValue;
-      else if (one)
+      else if (ONE_OK && center)
+        return launch_m<SLOTS, ROUNDS, MODE, true, 0, ONE_OK, ONE_OK>(x, M, d, ldx, rot, center, mean, qmax, out,
+                                                                      ld_out_bytes, scale, *pctl, no_lm, gsum, stream);
+      else if (ONE_OK)
         return launch_m<SLOTS, ROUNDS, MODE, true, 0, ONE_OK>(x, M, d, ldx, rot, center, mean, qmax, out,
                                                               ld_out_bytes, scale, *pctl, no_lm, gsum, stream);
       else
         return launch_m<SLOTS, ROUNDS, MODE, true>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale,
                                                    *pctl, no_lm, gsum, stream);
     }
-    if (one)
+    if (ONE_OK && center)
+      return launch_m<SLOTS, ROUNDS, MODE, false, 0, ONE_OK, ONE_OK>(x, M, d, ldx, rot, center, mean, qmax, out,
+                                                                     ld_out_bytes, scale, no_p, no_lm, gsum, stream);
+    if (ONE_OK)
       return launch_m<SLOTS, ROUNDS, MODE, false, 0, ONE_OK>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes,
                                                              scale, no_p, no_lm, gsum, stream);
     return launch_m<SLOTS, ROUNDS, MODE, false>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, no_p,
