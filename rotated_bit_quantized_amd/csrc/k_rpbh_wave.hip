@@ -465,9 +465,10 @@ __device__ __forceinline__ uint32_t gsum_pieces(float p) {
 // workgroups at 3 per SIMD.
 template <int SLOTS, int ROUNDS, bool LM, bool ONE = false, bool CEN1 = false>
 struct WaveLds {
-  // waves per workgroup: the centred single-copy body needs up to 168
-  // registers (3 waves per SIMD), so it runs 4-wave workgroups, three per CU
-  static constexpr int W = ONE ? (CEN1 ? 4 : 8) : WAVES_PER_WG;
+  // waves per workgroup: the centred and the Lloyd-Max single-copy bodies
+  // need up to 168 registers (3 waves per SIMD), so they run 4-wave
+  // workgroups, three per CU
+  static constexpr int W = ONE ? (CEN1 || LM ? 4 : 8) : WAVES_PER_WG;
   static constexpr int TABLE = (ROUNDS > 0 ? ROUNDS : 1) * SLOTS * 1024 * 4;
   static constexpr int SMASK = ONE ? SLOTS * 1024 * 2 : 0;
   // one bf16 copy; else 2 copies, float32 if 2 rounds
@@ -485,14 +486,14 @@ constexpr bool is_lm_mode() { return mode == OUT_LM4 || mode == OUT_LM8 || mode 
 // KM > 0: the factorised rotation with Paley order KM (ROUNDS 0, h = b, din
 // the native width); otherwise din is unused.
 template <int SLOTS, int ROUNDS, int mode, bool PCTL, int KM = 0, bool ONE = false, bool CEN1 = false>
-__global__ void __launch_bounds__(64 * (ONE ? (CEN1 ? 4 : 8) : WAVES_PER_WG))
-__attribute__((amdgpu_waves_per_eu(ONE ? (CEN1 ? 3 : 4) : 1)))
+__global__ void __launch_bounds__(64 * (ONE ? (CEN1 || is_lm_mode<mode>() ? 4 : 8) : WAVES_PER_WG))
+__attribute__((amdgpu_waves_per_eu(ONE ? (CEN1 || is_lm_mode<mode>() ? 3 : 4) : 1)))
 rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, const int32_t *__restrict__ perm,
                  const int8_t *__restrict__ signs, int h, float c_h, int pow4, int center_arg,
                  float *__restrict__ mean_out, int qmax, void *__restrict__ out, int64_t ld_out_bytes,
                  float *__restrict__ scale_out, PctlArgs pa, LmArgs la, uint32_t *__restrict__ gsum_out, int din) {
   static_assert(KM == 0 || (ROUNDS == 0 && !PCTL && !is_lm_mode<mode>()), "factorised rotation: plain absmax modes");
-  static_assert(!ONE || (ROUNDS == 1 && KM == 0 && !is_lm_mode<mode>()), "single copy: one round, absmax/percentile");
+  static_assert(!ONE || (ROUNDS == 1 && KM == 0), "single copy: one round");
   static_assert(!CEN1 || ONE, "centring is a compile-time choice of the single-copy kernel");
   constexpr bool LM = is_lm_mode<mode>();
   using L = WaveLds<SLOTS, ROUNDS, LM, ONE, CEN1>;
@@ -1030,7 +1031,7 @@ hipError_t launch_m(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotA
     // (workgroups per CU: the LDS allows 160 KiB / TOTAL, the registers
     // two of 8 waves at 4 per SIMD, three of 4 waves at 3 per SIMD), more
     // rows per wave beyond
-    const int64_t by_regs = CEN1 ? 3 : 2, by_lds = 160 * 1024 / L::TOTAL;
+    const int64_t by_regs = CEN1 || is_lm_mode<MODE>() ? 3 : 2, by_lds = 160 * 1024 / L::TOTAL;
     const int64_t per_cu = by_lds < by_regs ? by_lds : by_regs;
     const int64_t cap = per_cu * device_cus();
     grid = (M + L::W - 1) / L::W;
@@ -1058,6 +1059,13 @@ hipError_t launch_p(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotA
   const LmArgs no_lm{1, nullptr, nullptr};
   if constexpr (is_lm_mode<MODE>()) {
     if (!lm || pctl) return hipErrorInvalidValue;
+    constexpr bool ONE_OK = ROUNDS == 1 && SLOTS <= 3;
+    if (ONE_OK && center)
+      return launch_m<SLOTS, ROUNDS, MODE, false, 0, ONE_OK, ONE_OK>(x, M, d, ldx, rot, center, mean, qmax, out,
+                                                                     ld_out_bytes, scale, no_p, *lm, gsum, stream);
+    if (ONE_OK)
+      return launch_m<SLOTS, ROUNDS, MODE, false, 0, ONE_OK>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes,
+                                                             scale, no_p, *lm, gsum, stream);
     return launch_m<SLOTS, ROUNDS, MODE, false>(x, M, d, ldx, rot, center, mean, qmax, out, ld_out_bytes, scale, no_p,
                                                 *lm, gsum, stream);
   } else {
