@@ -569,8 +569,9 @@ rpbh_wave_kernel(const uint16_t *__restrict__ x, int64_t M, int d, int64_t ldx, 
   int64_t row = (int64_t)blockIdx.x * W + wave;
 
   if constexpr (ONE) {
-    // the sign mask starts at zero, so a perm that is not a permutation (the
-    // caller's contract) still gives deterministic, in-bounds results
+    // the sign mask starts at zero and the scatter index is clamped, so a
+    // perm that is not a permutation (outside the caller's contract) gives
+    // unspecified codes but no access outside the mask
     for (int i = threadIdx.x; i < SLOTS * 128; i += 64 * W) reinterpret_cast<uint4 *>(smask)[i] = make_uint4(0u, 0u, 0u, 0u);
     __syncthreads();
   }
