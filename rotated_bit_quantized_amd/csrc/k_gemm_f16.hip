@@ -381,13 +381,9 @@ hipError_t launch_f16(const uint8_t *A, const float *a_scale, int64_t M, int K, 
                       const float *mean, const float *w1, const float *bias, uint16_t *y, int64_t ldy,
                       hipStream_t stream) {
   using C = F16C<KC, NSLOT, TI, TJ>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)gemm_f16_kernel<KC, NSLOT, TI, TJ>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<bool> attr_set[64];
+  const hipError_t e = lds_limit_once((const void *)gemm_f16_kernel<KC, NSLOT, TI, TJ>, C::LDS, attr_set);
+  if (e != hipSuccess) return e;
   dim3 grid((unsigned)((N + C::BN - 1) / C::BN), (unsigned)((M + F16_BM - 1) / F16_BM));
   hipLaunchKernelGGL((gemm_f16_kernel<KC, NSLOT, TI, TJ>), grid, dim3(512), C::LDS, stream, A, a_scale, M, K, W, N, Np,
                      mean, w1, bias, y, ldy);

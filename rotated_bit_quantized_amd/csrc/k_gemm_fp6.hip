@@ -644,13 +644,9 @@ hipError_t launch_v2_kernel(const uint8_t *A, int64_t plane, const float *a_scal
                             const uint32_t *corr) {
   using V2 = V2C<NSLOT, TI, TJ, WAVES, PLANES>;
   auto kern = gemm_fp6_v2_kernel<NSLOT, PAIRED, ASYM, TI, TJ, WAVES, EXTRA, PLANES>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e =
-        hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, V2::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<bool> attr_set[64];
+  const hipError_t e = lds_limit_once((const void *)kern, V2::LDS_BYTES, attr_set);
+  if (e != hipSuccess) return e;
   dim3 grid((unsigned)((N + V2::BN - 1) / V2::BN), (unsigned)((M + V2::BM - 1) / V2::BM));
   hipLaunchKernelGGL(kern, grid, dim3(64 * WAVES), V2::LDS_BYTES, stream, A, plane, a_scale, M, K, W, wst, N, Np, mean,
                      w1, bias, y, ldy, gsum, reinterpret_cast<const uint2 *>(corr));

@@ -624,15 +624,8 @@ hipError_t launch_mx_pf(const uint8_t *qa, const uint8_t *ea, int64_t M, int K, 
   using C = MxP<WM, WN, TM, TN>;
   auto kern = gemm_mx_pf_kernel<WM, WN, TM, TN, REMAP>;
   static std::atomic<bool> attr_set[64];
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
+  const hipError_t e = lds_limit_once((const void *)kern, C::LDS_BYTES, attr_set);
   if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if (!attr_set[dev].load(std::memory_order_acquire)) {
-    e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_set[dev].store(true, std::memory_order_release);
-  }
   dim3 grid((unsigned)((N + C::BN - 1) / C::BN), (unsigned)((M + C::BM - 1) / C::BM));
   hipLaunchKernelGGL(kern, grid, dim3(64 * C::WAVES), C::LDS_BYTES, stream, qa, ea, M, K, w, ew, N, bias, y, ldy);
   return hipGetLastError();

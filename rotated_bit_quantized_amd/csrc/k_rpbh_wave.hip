@@ -1019,12 +1019,11 @@ hipError_t launch_m(const uint16_t *x, int64_t M, int d, int64_t ldx, const RotA
                     uint32_t *gsum, hipStream_t stream, int din = 0) {
   using L = WaveLds<SLOTS, ROUNDS, is_lm_mode<MODE>(), ONE, CEN1>;
   const size_t lds = (size_t)L::TOTAL;
-  static bool attr_set = false;
-  if (!attr_set && lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void *)rpbh_wave_kernel<SLOTS, ROUNDS, MODE, PCTL, KM, ONE, CEN1>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  static std::atomic<bool> attr_set[64];
+  if (lds > 64 * 1024) {
+    const hipError_t e =
+        lds_limit_once((const void *)rpbh_wave_kernel<SLOTS, ROUNDS, MODE, PCTL, KM, ONE, CEN1>, (int)lds, attr_set);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   int64_t grid;
   if constexpr (ONE) {

@@ -4,9 +4,27 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/oq.h"
 
 namespace oq {
+
+// Raises a kernel's dynamic LDS limit to `bytes` on the current device, once
+// per device (the attribute is held per device); `done` is that kernel's own
+// set of flags.
+inline hipError_t lds_limit_once(const void *kern, int bytes, std::atomic<bool> (&done)[64]) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (!done[dev].load(std::memory_order_acquire)) {
+    e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e != hipSuccess) return e;
+    done[dev].store(true, std::memory_order_release);
+  }
+  return hipSuccess;
+}
 
 // ------------------------------------------------------------------ errors --
 void set_error(const char *fmt, ...);
