@@ -224,15 +224,20 @@ int oq_quant_weight(const float *w, int32_t N, int32_t K, int64_t ldw,
  * qa int8 [M][lda]; a_scale float32 [M]; w uint8 [N][K/2] (canonical
  * nibbles); w_scale float32 [N][K/group]; mean and w1 both NULL or both set;
  * bias nullable; y bf16 [M][ldy].  group: multiple of 32 dividing K.
+ * A product of fewer than 128 output tiles of 128 x 128 with K <= 4096 runs
+ * one wavefront per 32 x 32 output tile (operands staged through LDS from
+ * coalesced loads), with no scratch and the one-pass kernel's arithmetic:
+ * the two give identical bits.  OQ_INT_SMALL=0 in the environment turns
+ * this routing off.
  * ws/ws_bytes: optional device scratch (16-byte aligned, else
- * OQ_ERR_ALIGNMENT).  A product of fewer than 128 output tiles of 128 x 128
- * given at least oq_workspace_bytes(OQ_OP_GEMM_W4A8, M, K, N, 0) bytes runs
- * split across K on more workgroups: each writes the float32 sum of its
- * groups' s_g acc_g to ws, and a second launch adds those sums in split
- * order and applies the epilogue (a different float32 summation order from
- * the one-pass kernel, within the same rounding bound).  Without scratch, or
- * with less, the product runs in one pass; the result is deterministic
- * either way.
+ * OQ_ERR_ALIGNMENT).  Another product of fewer than 128 such tiles (K >
+ * 4096, or the routing above turned off) given at least
+ * oq_workspace_bytes(OQ_OP_GEMM_W4A8, M, K, N, 0) bytes runs split across K
+ * on more workgroups: each writes the float32 sum of its groups' s_g acc_g
+ * to ws, and a second launch adds those sums in split order and applies the
+ * epilogue (a different float32 summation order from the one-pass kernel,
+ * within the same rounding bound).  Without scratch, or with less, the
+ * product runs in one pass; the result is deterministic either way.
  */
 int oq_gemm_w4a8(const int8_t *qa, int64_t lda, const float *a_scale, int64_t M, int32_t K,
                  const uint8_t *w, const float *w_scale, int32_t N, int32_t group,
@@ -524,7 +529,8 @@ enum { OQ_OP_GEMM_W4A8 = 1, OQ_OP_GEMM_W4A4 = 2, OQ_OP_LINEAR = 3, OQ_OP_GEMM_LM
 /* Scratch bytes a call needs (0 if none).  Pure host function.  For
  * OQ_OP_GEMM_LM, afmt is OQ_TILED for tiled activations, else 0.  For
  * OQ_OP_GEMM_W4A8 (afmt ignored), the optional scratch of the split
- * product, enough for any group size (0 when the product runs in one pass). */
+ * product, enough for any group size (0 when the product runs in one pass
+ * or on the 32 x 32 tile kernel). */
 size_t oq_workspace_bytes(int op, int64_t M, int32_t K, int32_t N, int afmt);
 
 #ifdef __cplusplus

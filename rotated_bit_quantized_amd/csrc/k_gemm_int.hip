@@ -25,6 +25,7 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // 8 bytes of 4-bit two's-complement codes -> 16 sign-extended int8, same order
 __device__ __forceinline__ v4i unpack16(uint2 p) {
@@ -240,6 +241,138 @@ gemm_int_kernel(const uint8_t *__restrict__ qa, int64_t lda, const float *__rest
   }
 }
 
+// Small products of 8-bit activations (fewer 128 x 128 output tiles than
+// half the CUs, K <= 4096): one wavefront per 32 x 32 output tile over the
+// whole of K, groups in order, the same fold and epilogue arithmetic as
+// gemm_int_kernel, so the two give identical bits.  The operands go through
+// LDS in chunks of 512 k read with coalesced 16-byte loads (each row's chunk
+// is one contiguous run: 16 loads cover the 32 activation rows, 8 the 32
+// weight rows, all in flight at once); the next chunk's loads are issued
+// before the current chunk is computed.  LDS rows are padded (528 and 272
+// bytes) so the fragment reads are free of bank conflicts.  256 x 1024 x
+// 1024 then runs 256 single-wave workgroups.
+constexpr int SM_KC = 512;               // k per chunk
+constexpr int SM_AROW = SM_KC + 16;      // LDS bytes per activation row of a chunk
+constexpr int SM_WROW = SM_KC / 2 + 16;  // LDS bytes per weight row (4-bit codes)
+constexpr int SM_NG = SM_KC / 32;        // most groups that end in one chunk
+constexpr int SM_LDS = 32 * SM_AROW + 32 * SM_WROW + (SM_NG * 32 + 2 * 32) * 4;
+
+__global__ void __launch_bounds__(64)
+gemm_int_small_kernel(const uint8_t *__restrict__ qa, int64_t lda, const float *__restrict__ a_scale, int64_t M,
+                      int K, const uint8_t *__restrict__ w, const float *__restrict__ w_scale, int N, int group,
+                      const float *__restrict__ mean, const float *__restrict__ w1, const float *__restrict__ bias,
+                      uint16_t *__restrict__ y, int64_t ldy) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint8_t *la = smem;
+  uint8_t *lw = smem + 32 * SM_AROW;
+  float *ls = reinterpret_cast<float *>(smem + 32 * SM_AROW + 32 * SM_WROW);  // [group - first of chunk][column]
+  float *l_alpha = ls + SM_NG * 32, *l_mean = l_alpha + 32;
+  const int lane = threadIdx.x;
+  const int64_t m0 = (int64_t)blockIdx.y * 32;
+  const int n0 = blockIdx.x * 32;
+  const int r32 = lane & 31, half = lane >> 5;
+  const int G = K / group, SPG = group / 32;
+
+  // epilogue operands; the row scales and means through LDS (a lane's 16
+  // outputs lie in 16 rows)
+  if (lane < 32) {
+    const int64_t row = m0 + lane < M ? m0 + lane : M - 1;
+    l_alpha[lane] = a_scale[row];
+    l_mean[lane] = mean ? mean[row] : 0.f;
+  }
+  const int col = n0 + r32;
+  const float w1v = (mean && col < N) ? w1[col] : 0.f;
+  const float bv = (bias && col < N) ? bias[col] : 0.f;
+
+  // chunk loads, unconditional from clamped rows and offsets (bytes past the
+  // chunk's end and rows past M or N are loaded but never read): activation
+  // load i covers row 2 i + lane / 32, bytes 16 (lane % 32) of its chunk;
+  // weight load i covers row 4 i + lane / 16, bytes 16 (lane % 16); scale
+  // load j covers group 2 j + lane / 32 of those ending in the chunk, column
+  // lane % 32.  Native vectors: a struct copy from global memory would stay
+  // in scratch.
+  u32x4 ra[16], rw[8];
+  float rs[8];
+#define OQ_SMALL_LOAD(KN)                                                                                    \
+  do {                                                                                                       \
+    const int kn_ = (KN), L_ = K - kn_ < SM_KC ? K - kn_ : SM_KC;                                            \
+    const int ba_ = 16 * (lane & 31) < L_ ? 16 * (lane & 31) : L_ - 16;                                      \
+    const int bw_ = 16 * (lane & 15) < L_ / 2 ? 16 * (lane & 15) : L_ / 2 - 16;                              \
+    _Pragma("unroll") for (int i = 0; i < 16; ++i) {                                                         \
+      int64_t row = m0 + 2 * i + (lane >> 5);                                                                \
+      if (row > M - 1) row = M - 1;                                                                          \
+      ra[i] = *reinterpret_cast<const u32x4 *>(qa + row * lda + kn_ + ba_);                                  \
+    }                                                                                                        \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                                          \
+      int wr = n0 + 4 * i + (lane >> 4);                                                                     \
+      if (wr > N - 1) wr = N - 1;                                                                            \
+      rw[i] = *reinterpret_cast<const u32x4 *>(w + (int64_t)wr * (K / 2) + kn_ / 2 + bw_);                   \
+    }                                                                                                        \
+    _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                                          \
+      const int idx = lane + 64 * j;                                                                         \
+      int c = n0 + (idx & 31), g = kn_ / group + (idx >> 5);                                                 \
+      if (c > N - 1) c = N - 1;                                                                              \
+      if (g > G - 1) g = G - 1;                                                                              \
+      rs[j] = w_scale[(int64_t)c * G + g];                                                                   \
+    }                                                                                                        \
+  } while (0)
+
+  float F[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) F[e] = 0.f;
+  v16i acc = (v16i){};
+  OQ_SMALL_LOAD(0);
+  for (int kc = 0; kc < K; kc += SM_KC) {
+    // a wave's LDS accesses complete in order: the previous chunk's reads
+    // are done before these writes land
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      *reinterpret_cast<u32x4 *>(la + (2 * i + (lane >> 5)) * SM_AROW + 16 * (lane & 31)) = ra[i];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      *reinterpret_cast<u32x4 *>(lw + (4 * i + (lane >> 4)) * SM_WROW + 16 * (lane & 15)) = rw[i];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ls[lane + 64 * j] = rs[j];
+    OQ_SMALL_LOAD(kc + SM_KC < K ? kc + SM_KC : kc);  // the last chunk reloads itself (cached, unused)
+    const int steps = (K - kc < SM_KC ? K - kc : SM_KC) / 32;
+    const int gq0 = kc / group;
+    // fragments of step s + 1 are read while step s multiplies
+    const uint8_t *fa = la + r32 * SM_AROW + 16 * half, *fw = lw + r32 * SM_WROW + 8 * half;
+    u32x4 pa = *reinterpret_cast<const u32x4 *>(fa);
+    uint2 pw = *reinterpret_cast<const uint2 *>(fw);
+    for (int s = 0; s < steps; ++s) {
+      const int sn = s + 1 < steps ? s + 1 : s;
+      const u32x4 na = *reinterpret_cast<const u32x4 *>(fa + 32 * sn);
+      const uint2 nw = *reinterpret_cast<const uint2 *>(fw + 16 * sn);
+      acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(v4i, pa), unpack16(pw), acc, 0, 0, 0);
+      pa = na;
+      pw = nw;
+      const int gs = kc / 32 + s;
+      if ((gs + 1) % SPG == 0) {
+        const float sw = ls[(gs / SPG - gq0) * 32 + r32];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) F[e] = __builtin_fmaf(sw, (float)acc[e], F[e]);
+        acc = (v16i){};
+      }
+    }
+  }
+#undef OQ_SMALL_LOAD
+
+  // y = a_scale * F + mean * w1 + bias (gemm_int_kernel's order); lane (r,
+  // half) holds rows 8 (e / 4) + 4 half + e % 4 of column n0 + r
+  if (col >= N) return;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int rl = (e >> 2) * 8 + half * 4 + (e & 3);
+    const int64_t row = m0 + rl;
+    if (row >= M) continue;
+    float v = l_alpha[rl] * F[e];
+    if (mean) v = __builtin_fmaf(l_mean[rl], w1v, v);
+    if (bias) v = v + bv;
+    y[row * ldy + col] = f32_to_bf16_rne(v);
+  }
+}
+
 // y = bf16( a_scale[t] (part[0] + part[1] + ... + part[S-1]) + mean[t] w1[o]
 // + bias[o] ), the partial sums added in split order; four outputs a thread.
 __global__ void __launch_bounds__(256)
@@ -286,6 +419,12 @@ hipError_t launch_gemm_int(const void *qa, int64_t lda_bytes, int a_is_nibble, c
                            const float *mean, const float *w1, const float *bias, uint16_t *y,
                            int64_t ldy, hipStream_t stream, void *ws, size_t ws_bytes) {
   if (M == 0 || N == 0) return hipSuccess;
+  if (!a_is_nibble && int_gemm_small(M, N, K)) {
+    hipLaunchKernelGGL(gemm_int_small_kernel, dim3((unsigned)((N + 31) / 32), (unsigned)((M + 31) / 32)), dim3(64),
+                       SM_LDS, stream, (const uint8_t *)qa, lda_bytes, a_scale, M, K, w, w_scale, N, group, mean, w1,
+                       bias, y, ldy);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)((N + 127) / 128), (unsigned)((M + 127) / 128));
   const int S = a_is_nibble ? 1 : int_gemm_splits(M, N, K, group);
   if (S > 1 && ws && ws_bytes >= (size_t)S * (size_t)M * (size_t)N * 4) {

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <cstdlib>
 
 #include "../../include/oq.h"
 
@@ -235,8 +236,19 @@ inline int int_gemm_splits(int64_t M, int N, int K, int group) {
   if (s > K / group) s = K / group;
   return s < 1 ? 1 : (int)s;
 }
+// Small W4A8 products (8-bit activations, fewer 128 x 128 tiles than half the
+// CUs, K <= 4096) run one wavefront per 32 x 32 output tile over the whole
+// of K, with no scratch.  OQ_INT_SMALL=0 in the environment turns this off
+// (then the split or one-pass kernel runs them).
+inline bool int_gemm_small(int64_t M, int N, int K) {
+  if (M <= 0 || N <= 0 || K <= 0 || K > 4096) return false;
+  if (((N + 127) / 128) * ((M + 127) / 128) >= 128) return false;
+  const char *e = getenv("OQ_INT_SMALL");
+  return !(e && e[0] == '0');
+}
 // scratch that lets every group size split (0 when the product needs none)
 inline size_t int_gemm_split_bytes(int64_t M, int N, int K) {
+  if (int_gemm_small(M, N, K)) return 0;
   const int s = int_gemm_splits(M, N, K, 32);  // the most splits any group allows
   return s > 1 ? (size_t)s * (size_t)M * (size_t)N * 4 : 0;
 }

@@ -238,8 +238,11 @@ void gemms() {
                       nullptr, Y, 64, nullptr, 0, nullptr), OQ_ERR_INVALID_ARG, 0);
   EXPECT(oq_gemm_w4a8(reinterpret_cast<const int8_t *>(P), 256, S, -5, 256, P, S, 64, 128, nullptr, nullptr, nullptr, Y,
                       64, nullptr, 0, nullptr), OQ_ERR_INVALID_ARG, 0);
-  // optional split scratch: one 128 x 128 tile splits into min(256, K / 32) = 8 parts
-  TRUE(oq_workspace_bytes(OQ_OP_GEMM_W4A8, 5, 256, 64, 0) == 8u * 5 * 64 * 4);
+  // optional split scratch: none for a small product with K <= 4096 (the 32
+  // x 32 tile kernel); beyond, one 128 x 128 tile splits into min(256, K /
+  // 32) = 256 parts
+  TRUE(oq_workspace_bytes(OQ_OP_GEMM_W4A8, 5, 256, 64, 0) == 0);
+  TRUE(oq_workspace_bytes(OQ_OP_GEMM_W4A8, 5, 8192, 64, 0) == 256u * 5 * 64 * 4);
   TRUE(oq_workspace_bytes(OQ_OP_GEMM_W4A8, 2048, 256, 2048, 0) == 0);  // 256 tiles: one pass
   TRUE(oq_workspace_bytes(OQ_OP_GEMM_W4A8, 5, 256, 0, 0) == 0);
   EXPECT(oq_gemm_w4a8(reinterpret_cast<const int8_t *>(P), 256, S, 5, 256, P, S, 64, 128, nullptr, nullptr, nullptr, Y,

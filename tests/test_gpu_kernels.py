@@ -308,18 +308,14 @@ def test_gemm_int(oq, M, N, K, group, afmt, rank1, bias):
     say("  within 1 bf16 ulp:", frac)
 
 
-@pytest.mark.parametrize("M,N,K,group,qmax,rank1,bias", [(256, 1024, 1024, 128, 127, False, False),
-                                                          (77, 200, 512, 64, 127, True, True),
-                                                          (1, 32, 256, 32, 31, True, False),
-                                                          (130, 136, 1024, 128, 127, False, True),
-                                                          (64, 96, 192, 32, 127, False, False)])
-def test_gemm_w4a8_split(oq, M, N, K, group, qmax, rank1, bias):
-    """The W4A8 product split across K through the optional scratch: against
-    the oracle under the output rule with the extra float32 additions of the
-    partial sums counted, repeatable bit for bit, and the one-pass call on
-    the same inputs within the same rule."""
-    say("case gemm_w4a8 split", M, N, K, group, qmax, rank1, bias)
-    rng = np.random.default_rng(7 * M + N + K)
+def _small_product(M, N, K):
+    """The library's routing of W4A8 products: fewer 128 x 128 tiles than 128
+    and K <= 4096 run the single-wave 32 x 32 tile kernel."""
+    return K <= 4096 and -(-N // 128) * -(-M // 128) < 128
+
+
+def _w4a8_case(M, N, K, group, qmax, rank1, bias, seed):
+    rng = np.random.default_rng(seed)
     qa = _rand_codes(rng, M, K, qmax)
     qa[0, :] = qmax
     qw = _rand_codes(rng, N, K, 7)
@@ -330,22 +326,69 @@ def test_gemm_w4a8_split(oq, M, N, K, group, qmax, rank1, bias):
     b = rng.normal(0, 0.1, size=N).astype(np.float32) if bias else None
     args = dict(mean=None if mean is None else to_dev(mean), w1=None if w1 is None else to_dev(w1),
                 bias=None if b is None else to_dev(b))
+    dev = (to_dev(qa.astype(np.int8)), to_dev(alpha), to_dev(OQ.pack_int4(qw)), to_dev(sw))
+    acc = OG.group_acc(qa, qw, group)
+    y_ref, S = OG.epilogue_int(alpha, acc, sw, mean, w1, b)
+    return dev, args, y_ref, S
+
+
+@pytest.mark.parametrize("M,N,K,group,qmax,rank1,bias", [(256, 1024, 1024, 128, 127, False, False),
+                                                          (77, 200, 512, 64, 127, True, True),
+                                                          (1, 32, 256, 32, 31, True, False),
+                                                          (130, 136, 1024, 128, 127, False, True),
+                                                          (64, 96, 192, 32, 127, False, False),
+                                                          (64, 96, 8192, 128, 127, True, True)])
+def test_gemm_w4a8_split(oq, M, N, K, group, qmax, rank1, bias, monkeypatch):
+    """The W4A8 product split across K through the optional scratch (small
+    products with K <= 4096 reach it with OQ_INT_SMALL=0, larger K by
+    default): against the oracle under the output rule with the extra
+    float32 additions of the partial sums counted, repeatable bit for bit,
+    and the one-pass call on the same inputs within the same rule."""
+    say("case gemm_w4a8 split", M, N, K, group, qmax, rank1, bias)
+    if _small_product(M, N, K):
+        monkeypatch.setenv("OQ_INT_SMALL", "0")
+    (A, AL, W, SW), args, y_ref, S = _w4a8_case(M, N, K, group, qmax, rank1, bias, 7 * M + N + K)
     nbytes = oq.oq_workspace_bytes(oq.OQ_OP_GEMM_W4A8, M, K, N, 0)
     tiles = -(-N // 128) * -(-M // 128)
     splits = 1 if tiles >= 128 else min(-(-256 // tiles), K // group)
     assert (nbytes > 0) == (splits > 1)
     ws = torch.zeros(max(16, nbytes), dtype=torch.uint8, device="cuda")
-    A, W, SW, AL = to_dev(qa.astype(np.int8)), to_dev(OQ.pack_int4(qw)), to_dev(sw), to_dev(alpha)
     y1 = oq.oq_gemm_w4a8(A, AL, W, SW, N, group, ws=ws, **args)
     y2 = oq.oq_gemm_w4a8(A, AL, W, SW, N, group, ws=ws, **args)
     y0 = oq.oq_gemm_w4a8(A, AL, W, SW, N, group, **args)
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), "split product not repeatable"
-    acc = OG.group_acc(qa, qw, group)
-    y_ref, S = OG.epilogue_int(alpha, acc, sw, mean, w1, b)
     frac = check_output(to_host(y1), y_ref, S, K // group + splits, "gemm_w4a8 split")
     check_output(to_host(y0), y_ref, S, K // group, "gemm_w4a8 one pass")
     say(f"  {splits} splits, within 1 bf16 ulp: {frac}")
+
+
+@pytest.mark.parametrize("M,N,K,group,qmax,rank1,bias", [(256, 1024, 1024, 128, 127, False, False),
+                                                          (45, 70, 1088, 64, 127, True, True),
+                                                          (1, 32, 256, 32, 31, True, False),
+                                                          (97, 33, 2048, 1024, 127, False, True),
+                                                          (40, 300, 4096, 32, 127, True, False),
+                                                          (512, 200, 1920, 64, 31, False, True),
+                                                          (7, 1000, 64, 32, 127, False, False)])
+def test_gemm_w4a8_small(oq, M, N, K, group, qmax, rank1, bias, monkeypatch):
+    """Small W4A8 products on the single-wave 32 x 32 tile kernel (chunks of
+    512 k, a ragged last chunk, groups of 32 to 1024, the largest spanning
+    two chunks, ragged M and N): against the oracle under the output rule,
+    and bit-identical to the one-pass kernel (OQ_INT_SMALL=0, no scratch),
+    whose fold and epilogue arithmetic it repeats."""
+    say("case gemm_w4a8 small", M, N, K, group, qmax, rank1, bias)
+    assert _small_product(M, N, K)
+    (A, AL, W, SW), args, y_ref, S = _w4a8_case(M, N, K, group, qmax, rank1, bias, 11 * M + N + K)
+    assert oq.oq_workspace_bytes(oq.OQ_OP_GEMM_W4A8, M, K, N, 0) == 0
+    ys = oq.oq_gemm_w4a8(A, AL, W, SW, N, group, **args)
+    ys2 = oq.oq_gemm_w4a8(A, AL, W, SW, N, group, **args)
+    monkeypatch.setenv("OQ_INT_SMALL", "0")
+    y0 = oq.oq_gemm_w4a8(A, AL, W, SW, N, group, **args)
+    torch.cuda.synchronize()
+    assert torch.equal(ys.view(torch.int16), ys2.view(torch.int16)), "small product not repeatable"
+    frac = check_output(to_host(ys), y_ref, S, K // group, "gemm_w4a8 small")
+    assert torch.equal(ys.view(torch.int16), y0.view(torch.int16)), "small and one-pass kernels differ"
+    say(f"  within 1 bf16 ulp: {frac}")
 
 
 @pytest.mark.parametrize("M,N,K,bias", [(130, 96, 256, True), (64, 256, 4096, True), (7, 32, 64, True),
