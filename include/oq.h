@@ -225,10 +225,10 @@ int oq_quant_weight(const float *w, int32_t N, int32_t K, int64_t ldw,
  * nibbles); w_scale float32 [N][K/group]; mean and w1 both NULL or both set;
  * bias nullable; y bf16 [M][ldy].  group: multiple of 32 dividing K.
  * A product of fewer than 128 output tiles of 128 x 128 with K <= 4096 runs
- * one wavefront per 32 x 32 output tile (operands staged through LDS from
- * coalesced loads), with no scratch and the one-pass kernel's arithmetic:
- * the two give identical bits.  OQ_INT_SMALL=0 in the environment turns
- * this routing off.
+ * one 4-wavefront workgroup per 32 x 32 output tile (operands staged through
+ * LDS from coalesced loads), with no scratch and the one-pass kernel's
+ * arithmetic: the two give identical bits.  OQ_INT_SMALL=0 in the
+ * environment turns this routing off.
  * ws/ws_bytes: optional device scratch (16-byte aligned, else
  * OQ_ERR_ALIGNMENT).  Another product of fewer than 128 such tiles (K >
  * 4096, or the routing above turned off) given at least

@@ -242,22 +242,25 @@ gemm_int_kernel(const uint8_t *__restrict__ qa, int64_t lda, const float *__rest
 }
 
 // Small products of 8-bit activations (fewer 128 x 128 output tiles than
-// half the CUs, K <= 4096): one wavefront per 32 x 32 output tile over the
-// whole of K, groups in order, the same fold and epilogue arithmetic as
-// gemm_int_kernel, so the two give identical bits.  The operands go through
-// LDS in chunks of 512 k read with coalesced 16-byte loads (each row's chunk
-// is one contiguous run: 16 loads cover the 32 activation rows, 8 the 32
-// weight rows, all in flight at once); the next chunk's loads are issued
-// before the current chunk is computed.  LDS rows are padded (528 and 272
-// bytes) so the fragment reads are free of bank conflicts.  256 x 1024 x
-// 1024 then runs 256 single-wave workgroups.
-constexpr int SM_KC = 512;               // k per chunk
+// half the CUs, K <= 4096): a workgroup of 4 wavefronts per 32 x 32 output
+// tile, each wavefront one 16 x 16 quarter over the whole of K with
+// v_mfma_i32_16x16x64_i8, groups in order, the same fold and epilogue
+// arithmetic as gemm_int_kernel (the integer group sums are exact whatever
+// the MFMA shape), so the two give identical bits.  The tile's operands go
+// through LDS in chunks of 1024 k read with coalesced 16-byte loads (each
+// row's chunk is one contiguous run; a wavefront loads 8 activation rows and
+// 8 weight rows, 16 loads a lane, all in flight at once); the next chunk's
+// loads are issued before the current chunk is computed.  LDS rows are
+// padded (1040 and 528 bytes) so the fragment reads are free of bank
+// conflicts.  256 x 1024 x 1024 then runs 256 workgroups, one round trip to
+// memory each.
+constexpr int SM_KC = 1024;              // k per chunk
 constexpr int SM_AROW = SM_KC + 16;      // LDS bytes per activation row of a chunk
 constexpr int SM_WROW = SM_KC / 2 + 16;  // LDS bytes per weight row (4-bit codes)
 constexpr int SM_NG = SM_KC / 32;        // most groups that end in one chunk
 constexpr int SM_LDS = 32 * SM_AROW + 32 * SM_WROW + (SM_NG * 32 + 2 * 32) * 4;
 
-__global__ void __launch_bounds__(64)
+__global__ void __launch_bounds__(256)
 gemm_int_small_kernel(const uint8_t *__restrict__ qa, int64_t lda, const float *__restrict__ a_scale, int64_t M,
                       int K, const uint8_t *__restrict__ w, const float *__restrict__ w_scale, int N, int group,
                       const float *__restrict__ mean, const float *__restrict__ w1, const float *__restrict__ bias,
@@ -267,103 +270,116 @@ gemm_int_small_kernel(const uint8_t *__restrict__ qa, int64_t lda, const float *
   uint8_t *lw = smem + 32 * SM_AROW;
   float *ls = reinterpret_cast<float *>(smem + 32 * SM_AROW + 32 * SM_WROW);  // [group - first of chunk][column]
   float *l_alpha = ls + SM_NG * 32, *l_mean = l_alpha + 32;
-  const int lane = threadIdx.x;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int64_t m0 = (int64_t)blockIdx.y * 32;
   const int n0 = blockIdx.x * 32;
-  const int r32 = lane & 31, half = lane >> 5;
+  const int r16 = lane & 15, q = lane >> 4;        // fragment row (column) and k quarter
+  const int wr = 16 * (wave >> 1), wc = 16 * (wave & 1);  // this wave's quarter of the tile
   const int G = K / group, SPG = group / 32;
 
-  // epilogue operands; the row scales and means through LDS (a lane's 16
-  // outputs lie in 16 rows)
-  if (lane < 32) {
-    const int64_t row = m0 + lane < M ? m0 + lane : M - 1;
-    l_alpha[lane] = a_scale[row];
-    l_mean[lane] = mean ? mean[row] : 0.f;
+  // epilogue operands; the row scales and means through LDS (a lane's 4
+  // outputs lie in 4 rows)
+  if (t < 32) {
+    const int64_t row = m0 + t < M ? m0 + t : M - 1;
+    l_alpha[t] = a_scale[row];
+    l_mean[t] = mean ? mean[row] : 0.f;
   }
-  const int col = n0 + r32;
+  const int col = n0 + wc + r16;
   const float w1v = (mean && col < N) ? w1[col] : 0.f;
   const float bv = (bias && col < N) ? bias[col] : 0.f;
 
   // chunk loads, unconditional from clamped rows and offsets (bytes past the
-  // chunk's end and rows past M or N are loaded but never read): activation
-  // load i covers row 2 i + lane / 32, bytes 16 (lane % 32) of its chunk;
-  // weight load i covers row 4 i + lane / 16, bytes 16 (lane % 16); scale
-  // load j covers group 2 j + lane / 32 of those ending in the chunk, column
-  // lane % 32.  Native vectors: a struct copy from global memory would stay
-  // in scratch.
-  u32x4 ra[16], rw[8];
-  float rs[8];
+  // chunk's end and rows past M or N are loaded but never read): wave v's
+  // activation load i covers row 8 v + i, bytes 16 lane of its chunk; its
+  // weight load i covers row 8 v + 2 i + lane / 32, bytes 16 (lane % 32);
+  // scale load j covers group 8 j + t / 32 of those ending in the chunk,
+  // column t % 32.  Native vectors: a struct copy from global memory would
+  // stay in scratch.
+  u32x4 ra[8], rw[4];
+  float rs[4];
 #define OQ_SMALL_LOAD(KN)                                                                                    \
   do {                                                                                                       \
     const int kn_ = (KN), L_ = K - kn_ < SM_KC ? K - kn_ : SM_KC;                                            \
-    const int ba_ = 16 * (lane & 31) < L_ ? 16 * (lane & 31) : L_ - 16;                                      \
-    const int bw_ = 16 * (lane & 15) < L_ / 2 ? 16 * (lane & 15) : L_ / 2 - 16;                              \
-    _Pragma("unroll") for (int i = 0; i < 16; ++i) {                                                         \
-      int64_t row = m0 + 2 * i + (lane >> 5);                                                                \
+    const int ba_ = 16 * lane < L_ ? 16 * lane : L_ - 16;                                                    \
+    const int bw_ = 16 * (lane & 31) < L_ / 2 ? 16 * (lane & 31) : L_ / 2 - 16;                              \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                                          \
+      int64_t row = m0 + 8 * wave + i;                                                                       \
       if (row > M - 1) row = M - 1;                                                                          \
       ra[i] = *reinterpret_cast<const u32x4 *>(qa + row * lda + kn_ + ba_);                                  \
     }                                                                                                        \
-    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                                          \
-      int wr = n0 + 4 * i + (lane >> 4);                                                                     \
-      if (wr > N - 1) wr = N - 1;                                                                            \
-      rw[i] = *reinterpret_cast<const u32x4 *>(w + (int64_t)wr * (K / 2) + kn_ / 2 + bw_);                   \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                          \
+      int wrow = n0 + 8 * wave + 2 * i + (lane >> 5);                                                        \
+      if (wrow > N - 1) wrow = N - 1;                                                                        \
+      rw[i] = *reinterpret_cast<const u32x4 *>(w + (int64_t)wrow * (K / 2) + kn_ / 2 + bw_);                 \
     }                                                                                                        \
-    _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                                          \
-      const int idx = lane + 64 * j;                                                                         \
-      int c = n0 + (idx & 31), g = kn_ / group + (idx >> 5);                                                 \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                                          \
+      int c = n0 + (t & 31), g = kn_ / group + 8 * j + (t >> 5);                                             \
       if (c > N - 1) c = N - 1;                                                                              \
       if (g > G - 1) g = G - 1;                                                                              \
       rs[j] = w_scale[(int64_t)c * G + g];                                                                   \
     }                                                                                                        \
   } while (0)
 
-  float F[16];
-#pragma unroll
-  for (int e = 0; e < 16; ++e) F[e] = 0.f;
-  v16i acc = (v16i){};
+  float F[4] = {0.f, 0.f, 0.f, 0.f};
+  v4i acc = (v4i){};
   OQ_SMALL_LOAD(0);
   for (int kc = 0; kc < K; kc += SM_KC) {
-    // a wave's LDS accesses complete in order: the previous chunk's reads
-    // are done before these writes land
+    if (kc > 0) __syncthreads();  // every wave's reads of the previous chunk are done
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      *reinterpret_cast<u32x4 *>(la + (2 * i + (lane >> 5)) * SM_AROW + 16 * (lane & 31)) = ra[i];
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4 *>(la + (8 * wave + i) * SM_AROW + 16 * lane) = ra[i];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      *reinterpret_cast<u32x4 *>(lw + (4 * i + (lane >> 4)) * SM_WROW + 16 * (lane & 15)) = rw[i];
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4 *>(lw + (8 * wave + 2 * i + (lane >> 5)) * SM_WROW + 16 * (lane & 31)) = rw[i];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) ls[lane + 64 * j] = rs[j];
-    OQ_SMALL_LOAD(kc + SM_KC < K ? kc + SM_KC : kc);  // the last chunk reloads itself (cached, unused)
-    const int steps = (K - kc < SM_KC ? K - kc : SM_KC) / 32;
+    for (int j = 0; j < 4; ++j) ls[t + 256 * j] = rs[j];
+    __syncthreads();
+    if (kc + SM_KC < K) OQ_SMALL_LOAD(kc + SM_KC);
+    const int steps = (K - kc < SM_KC ? K - kc : SM_KC) / 64;
     const int gq0 = kc / group;
-    // fragments of step s + 1 are read while step s multiplies
-    const uint8_t *fa = la + r32 * SM_AROW + 16 * half, *fw = lw + r32 * SM_WROW + 8 * half;
+    // fragments of step s + 1 are read while step s multiplies: lane (r, q)
+    // holds k 16 q .. 16 q + 15 of the step's 64 for row (column) r
+    const uint8_t *fa = la + (wr + r16) * SM_AROW + 16 * q, *fw = lw + (wc + r16) * SM_WROW + 8 * q;
     u32x4 pa = *reinterpret_cast<const u32x4 *>(fa);
     uint2 pw = *reinterpret_cast<const uint2 *>(fw);
     for (int s = 0; s < steps; ++s) {
       const int sn = s + 1 < steps ? s + 1 : s;
-      const u32x4 na = *reinterpret_cast<const u32x4 *>(fa + 32 * sn);
-      const uint2 nw = *reinterpret_cast<const uint2 *>(fw + 16 * sn);
-      acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(v4i, pa), unpack16(pw), acc, 0, 0, 0);
+      const u32x4 na = *reinterpret_cast<const u32x4 *>(fa + 64 * sn);
+      const uint2 nw = *reinterpret_cast<const uint2 *>(fw + 32 * sn);
+      const v4i A = __builtin_bit_cast(v4i, pa), B = unpack16(pw);
       pa = na;
       pw = nw;
-      const int gs = kc / 32 + s;
-      if ((gs + 1) % SPG == 0) {
-        const float sw = ls[(gs / SPG - gq0) * 32 + r32];
+      if (SPG == 1) {
+        // groups of 32: the step's two groups in turn, each MFMA with the
+        // other group's activation bytes (lanes of the other k halves) zeroed
+        const v4i Z = (v4i){};
 #pragma unroll
-        for (int e = 0; e < 16; ++e) F[e] = __builtin_fmaf(sw, (float)acc[e], F[e]);
-        acc = (v16i){};
+        for (int hh = 0; hh < 2; ++hh) {
+          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8((q >> 1) == hh ? A : Z, B, acc, 0, 0, 0);
+          const float sw = ls[(2 * s + hh) * 32 + wc + r16];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) F[e] = __builtin_fmaf(sw, (float)acc[e], F[e]);
+          acc = (v4i){};
+        }
+      } else {
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, acc, 0, 0, 0);
+        const int k_end = kc + 64 * s + 64;
+        if (k_end % group == 0) {
+          const float sw = ls[(k_end / group - 1 - gq0) * 32 + wc + r16];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) F[e] = __builtin_fmaf(sw, (float)acc[e], F[e]);
+          acc = (v4i){};
+        }
       }
     }
   }
 #undef OQ_SMALL_LOAD
 
   // y = a_scale * F + mean * w1 + bias (gemm_int_kernel's order); lane (r,
-  // half) holds rows 8 (e / 4) + 4 half + e % 4 of column n0 + r
+  // q) holds rows 4 q + e of column r of the wave's quarter
   if (col >= N) return;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const int rl = (e >> 2) * 8 + half * 4 + (e & 3);
+  for (int e = 0; e < 4; ++e) {
+    const int rl = wr + 4 * q + e;
     const int64_t row = m0 + rl;
     if (row >= M) continue;
     float v = l_alpha[rl] * F[e];
@@ -420,7 +436,7 @@ hipError_t launch_gemm_int(const void *qa, int64_t lda_bytes, int a_is_nibble, c
                            int64_t ldy, hipStream_t stream, void *ws, size_t ws_bytes) {
   if (M == 0 || N == 0) return hipSuccess;
   if (!a_is_nibble && int_gemm_small(M, N, K)) {
-    hipLaunchKernelGGL(gemm_int_small_kernel, dim3((unsigned)((N + 31) / 32), (unsigned)((M + 31) / 32)), dim3(64),
+    hipLaunchKernelGGL(gemm_int_small_kernel, dim3((unsigned)((N + 31) / 32), (unsigned)((M + 31) / 32)), dim3(256),
                        SM_LDS, stream, (const uint8_t *)qa, lda_bytes, a_scale, M, K, w, w_scale, N, group, mean, w1,
                        bias, y, ldy);
     return hipGetLastError();

@@ -237,9 +237,9 @@ inline int int_gemm_splits(int64_t M, int N, int K, int group) {
   return s < 1 ? 1 : (int)s;
 }
 // Small W4A8 products (8-bit activations, fewer 128 x 128 tiles than half the
-// CUs, K <= 4096) run one wavefront per 32 x 32 output tile over the whole
-// of K, with no scratch.  OQ_INT_SMALL=0 in the environment turns this off
-// (then the split or one-pass kernel runs them).
+// CUs, K <= 4096) run one 4-wave workgroup per 32 x 32 output tile over the
+// whole of K, with no scratch.  OQ_INT_SMALL=0 in the environment turns this
+// off (then the split or one-pass kernel runs them).
 inline bool int_gemm_small(int64_t M, int N, int K) {
   if (M <= 0 || N <= 0 || K <= 0 || K > 4096) return false;
   if (((N + 127) / 128) * ((M + 127) / 128) >= 128) return false;

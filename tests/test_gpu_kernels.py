@@ -310,7 +310,7 @@ def test_gemm_int(oq, M, N, K, group, afmt, rank1, bias):
 
 def _small_product(M, N, K):
     """The library's routing of W4A8 products: fewer 128 x 128 tiles than 128
-    and K <= 4096 run the single-wave 32 x 32 tile kernel."""
+    and K <= 4096 run the 32 x 32 tile kernel (4 waves of 16 x 16)."""
     return K <= 4096 and -(-N // 128) * -(-M // 128) < 128
 
 
@@ -369,11 +369,12 @@ def test_gemm_w4a8_split(oq, M, N, K, group, qmax, rank1, bias, monkeypatch):
                                                           (97, 33, 2048, 1024, 127, False, True),
                                                           (40, 300, 4096, 32, 127, True, False),
                                                           (512, 200, 1920, 64, 31, False, True),
-                                                          (7, 1000, 64, 32, 127, False, False)])
+                                                          (7, 1000, 64, 32, 127, False, False),
+                                                          (64, 64, 4096, 2048, 127, True, True)])
 def test_gemm_w4a8_small(oq, M, N, K, group, qmax, rank1, bias, monkeypatch):
-    """Small W4A8 products on the single-wave 32 x 32 tile kernel (chunks of
-    512 k, a ragged last chunk, groups of 32 to 1024, the largest spanning
-    two chunks, ragged M and N): against the oracle under the output rule,
+    """Small W4A8 products on the 32 x 32 tile kernel (chunks of 1024 k, a
+    ragged last chunk, groups of 32 to 2048, the largest spanning two
+    chunks, ragged M and N): against the oracle under the output rule,
     and bit-identical to the one-pass kernel (OQ_INT_SMALL=0, no scratch),
     whose fold and epilogue arithmetic it repeats."""
     say("case gemm_w4a8 small", M, N, K, group, qmax, rank1, bias)
