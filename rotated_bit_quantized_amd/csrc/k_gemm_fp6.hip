@@ -298,30 +298,37 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, int64_t a_plane_bytes, const f
   // byte o of the stage's code region is byte o % 1536 of row block m0 / 32 +
   // (o % A_BYTES) / 1536 of A plane o / A_BYTES below B_OFF, else of B column
   // block n0 / 32 + (o - B_OFF) / 1536 (clamped to the last block: those
-  // bytes are never read)
-  constexpr int NU = V2::U4 + V2::U1;
-  const uint8_t *cbase[NU];
-  uint32_t coff[NU], clds[NU];
+  // bytes are never read).
+  // In the paired 8-wave schedule, waves 0-3 issue the copies of waves w and
+  // w + 4 (and each scale chunk once): the two waves sharing a SIMD run at
+  // different speeds (the older one wins issue arbitration and then waits at
+  // the barrier), so the copies go to the one with time to spare.
+  constexpr bool HALF_COPY = PAIRED && WAVES == 8;
+  constexpr int NU = V2::U4 + V2::U1, NC = HALF_COPY ? 2 * NU : NU;
+  const bool copier = !HALF_COPY || wave < WAVES / 2;
+  const uint8_t *cbase[NC];
+  uint32_t coff[NC], clds[NC];
 #pragma unroll
-  for (int q = 0; q < NU; ++q) {
+  for (int u = 0; u < NC; ++u) {
+    const int q = u % NU, v = wave + (u / NU) * (WAVES / 2);  // the unit's owner in the even split
     const bool wide = q < V2::U4;
-    const uint32_t ubase = wide ? 1024u * (wave + WAVES * q)
-                                : 1024u * WAVES * V2::U4 + 256u * (wave + WAVES * (q - V2::U4));
+    const uint32_t ubase = wide ? 1024u * (v + WAVES * q)
+                                : 1024u * WAVES * V2::U4 + 256u * (v + WAVES * (q - V2::U4));
     const int o = (int)ubase + (wide ? 16 : 4) * lane;
     if (ubase < (uint32_t)V2::B_OFF) {  // a unit lies within one operand (and plane)
       const int pl = (int)ubase / V2::A_BYTES, oa = o - pl * V2::A_BYTES;
       int64_t rb = m0 / 32 + oa / CHUNK_TILE;
       if (rb > mblocks - 1) rb = mblocks - 1;
-      cbase[q] = A + pl * a_plane_bytes;
-      coff[q] = (uint32_t)(rb * G * CHUNK_TILE + oa % CHUNK_TILE);
+      cbase[u] = A + pl * a_plane_bytes;
+      coff[u] = (uint32_t)(rb * G * CHUNK_TILE + oa % CHUNK_TILE);
     } else {
       const int oo = o - V2::B_OFF;
       int cb = n0 / 32 + oo / CHUNK_TILE;
       if (cb > nblocks - 1) cb = nblocks - 1;
-      cbase[q] = W;
-      coff[q] = (uint32_t)((int64_t)cb * G * CHUNK_TILE + oo % CHUNK_TILE);
+      cbase[u] = W;
+      coff[u] = (uint32_t)((int64_t)cb * G * CHUNK_TILE + oo % CHUNK_TILE);
     }
-    clds[q] = ubase;
+    clds[u] = ubase;
   }
   const int sc = wave % V2::S_CHUNKS;  // scale chunk: columns n0 + 64 sc + lane
   int scol = n0 + 64 * sc + lane;
@@ -329,11 +336,12 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, int64_t a_plane_bytes, const f
   const uint32_t soff = 4u * scol, slds = V2::B_OFF + V2::B_BYTES + 256u * sc;
 
   auto issue = [&](int slot, int kg) {
+    if (!copier) return;
     const uint32_t base = lds0 + slot * V2::STAGE;
 #pragma unroll
-    for (int q = 0; q < NU; ++q) {
-      if (q < V2::U4) dma16_s(cbase[q] + (int64_t)kg * CHUNK_TILE, coff[q], base + clds[q]);
-      else dma4_s(cbase[q] + (int64_t)kg * CHUNK_TILE, coff[q], base + clds[q]);
+    for (int u = 0; u < NC; ++u) {
+      if (u % NU < V2::U4) dma16_s(cbase[u] + (int64_t)kg * CHUNK_TILE, coff[u], base + clds[u]);
+      else dma4_s(cbase[u] + (int64_t)kg * CHUNK_TILE, coff[u], base + clds[u]);
     }
     dma4_s(wst + (int64_t)kg * Np, soff, base + slds);
   };
@@ -583,16 +591,23 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, int64_t a_plane_bytes, const f
   }
   uint8_t *stg = smem + V2::STG_OFF + wave * (32 * SROW);
   const bool vec_ok = ((reinterpret_cast<uintptr_t>(y) & 15) == 0) && (ldy % 8 == 0);
+  // per slab, the LDS reads are issued together ahead of their uses (the row
+  // scales before the arithmetic, the staged pieces before the stores), so
+  // each waits for LDS once rather than once per read
 #pragma unroll
   for (int i = 0; i < TI; ++i) {
+    // rows (e4 * 8 + half * 4 + 0..3) of this 32-row slab: one 16-byte read each
+    float4 al4[4], mu4[4];
 #pragma unroll
     for (int e4 = 0; e4 < 4; ++e4) {
-      // rows (e4 * 8 + half * 4 + 0..3) of this 32-row slab: one 16-byte read each
       const int rl = wm * 32 * TI + 32 * i + e4 * 8 + half * 4;
-      const float4 al4 = *reinterpret_cast<const float4 *>(lds_alpha + rl);
-      const float4 mu4 = (EXTRA && mean) ? *reinterpret_cast<const float4 *>(lds_mean + rl)
-                                         : make_float4(0.f, 0.f, 0.f, 0.f);
-      const float al[4] = {al4.x, al4.y, al4.z, al4.w}, mu[4] = {mu4.x, mu4.y, mu4.z, mu4.w};
+      al4[e4] = *reinterpret_cast<const float4 *>(lds_alpha + rl);
+      mu4[e4] = (EXTRA && mean) ? *reinterpret_cast<const float4 *>(lds_mean + rl) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      const float al[4] = {al4[e4].x, al4[e4].y, al4[e4].z, al4[e4].w};
+      const float mu[4] = {mu4[e4].x, mu4[e4].y, mu4[e4].z, mu4[e4].w};
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
         float v[4];
@@ -615,14 +630,21 @@ gemm_fp6_v2_kernel(const uint8_t *__restrict__ A, int64_t a_plane_bytes, const f
       }
     }
     // the slab is 32 rows of 4 TJ 16-byte pieces: 2 TJ rounds of 64 pieces
+    // (a wave's LDS accesses complete in order: the reads see the writes)
     constexpr int CPR = 4 * TJ;
+    uint4 pv[2 * TJ];
+#pragma unroll
+    for (int q = 0; q < 2 * TJ; ++q) {
+      const int piece = lane + 64 * q;
+      pv[q] = *reinterpret_cast<const uint4 *>(stg + (piece / CPR) * SROW + (piece % CPR) * 16);
+    }
 #pragma unroll
     for (int q = 0; q < 2 * TJ; ++q) {
       const int piece = lane + 64 * q;
       const int rr = piece / CPR, cl = (piece % CPR) * 8;
       const int col = n0 + wn * 32 * TJ + cl;
       const int64_t row = m0 + wm * 32 * TI + 32 * i + rr;
-      const uint4 v = *reinterpret_cast<const uint4 *>(stg + rr * SROW + cl * 2);
+      const uint4 v = pv[q];
       if (row >= M) continue;
       uint16_t *dst = y + row * ldy + col;
       if (vec_ok && col + 8 <= N) {
