@@ -30,11 +30,10 @@
 // per tile after the main loop on bfloat16 matrix cores, with p and C split
 // into pieces that make every product exact in float32.
 //
-// Both kernels walk the 64-wide k groups; each group's A, B and scale tiles
+// The kernel walks the 64-wide k groups; each group's A, B and scale tiles
 // are copied global -> LDS with global_load_lds (no register staging) into a
-// ring of stages.  The two-plane kernel (6-bit activations) runs WM x WN
-// wavefronts of 128 x 64 outputs with one barrier per group; the single-plane
-// kernel's shapes and schedule are described at its definition.
+// ring of stages.  Single-plane (4-bit) and two-plane (6-bit) activations run
+// the same kernel; its shapes and schedule are described at its definition.
 #include "oq_internal.h"
 
 #include <atomic>
@@ -218,7 +217,9 @@ __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F
 // stage are split evenly over the waves as U4 1 KiB units (16 bytes a lane)
 // and U1 256-byte units (4 bytes a lane), and every wave copies one 256-byte
 // chunk of scales, so all waves issue the same copies per stage and the
-// vmcnt values are compile-time constants.  4-wave workgroups fit two to a CU
+// vmcnt values are compile-time constants.  (The paired schedule of 8-wave
+// workgroups hands the units of waves w + 4 to waves w and copies each scale
+// chunk once; it waits for all copies before each barrier.)  4-wave workgroups fit two to a CU
 // (LDS under 80 KiB, the epilogue staging reusing the ring), so one
 // workgroup's barrier waits and epilogue overlap the other's main loop.
 template <int NSLOT_, int TI_, int TJ_, int WAVES_, int PLANES_>
