@@ -164,6 +164,24 @@ def _time(torch, oq, st, steps, warmup):
     return total, wall / steps * 1e3, per, samples
 
 
+def _settle(torch, run_one, seconds):
+    """Runs the step (run_one(i) enqueues step i) for at least `seconds` of
+    wall time, untimed, so that the timed steps see the clock the GPU holds
+    under this load rather than its ramp from idle (a few ms of timed work
+    otherwise lands on a lower clock).  Returns the steps run."""
+    if seconds <= 0:
+        return 0
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(25):
+            run_one(n)
+            n += 1
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return n
+
+
 def _capture(torch, oq, st):
     """One HIP graph per input buffer, each holding the step's launches (K1
     and both linears) with that buffer as input; captured after an eager
@@ -605,6 +623,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-s", type=float, default=1.0,
+                    help="untimed seconds of the step run before the warm-ups of each timed section, so the "
+                         "timed steps see the clock the GPU holds under load (0 turns it off)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-config side table")
     ap.add_argument("--only-step", action="store_true", help="time the step only (for profilers)")
@@ -645,8 +666,14 @@ def main():
     M, K = wl.M, wl.K
     # per-launch durations from the step launched eagerly (events between the
     # kernels), then the step itself as replays of captured graphs
+    def eager_step(i):
+        for _, f in _launches(oq, st, i):
+            f()
+
+    settle_eager = _settle(torch, eager_step, args.settle_s)
     ms_eager, _, per, samples = _time(torch, oq, st, args.steps, args.warmup)
     graphs = _capture(torch, oq, st)
+    settle_graph = _settle(torch, lambda i: graphs[i % len(graphs)].replay(), args.settle_s)
     ms_step, wall_ms = _time_graphs(torch, graphs, args.steps, args.warmup)
     del graphs
     if args.copy_ref:
@@ -667,6 +694,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"seconds": args.settle_s, "eager_steps": settle_eager, "graph_replays": settle_graph,
+                   "note": "untimed steps run before the warm-ups so the timed steps see the loaded clock"},
         "ms_per_step": round(ms_step, 5),
         "launch": "one HIP graph per step (K1 and both linears), replayed; per-launch times from the same step "
                   "launched eagerly",
@@ -712,8 +741,15 @@ def main():
             del st
             torch.cuda.empty_cache()
             st = _setup(torch, oq, WL, cid)
+
+            def side_step(i, st=st):
+                for _, f in _launches(oq, st, i):
+                    f()
+
+            _settle(torch, side_step, min(args.settle_s, 0.3))
             ms_e, _, per_c, _ = _time(torch, oq, st, max(20, args.steps // 5), 5)
             graphs = _capture(torch, oq, st)
+            _settle(torch, lambda i: graphs[i % len(graphs)].replay(), min(args.settle_s, 0.3))
             ms, _ = _time_graphs(torch, graphs, max(20, args.steps // 5), 5)
             del graphs
             w2, s2 = st["wl"], st["spec"]
