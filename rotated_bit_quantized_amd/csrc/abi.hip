@@ -607,7 +607,7 @@ int linear_fused_impl(const char *fn, const uint16_t *x, int64_t M, int32_t K, i
 // code object until the process ends.  Host code uses the device address that
 // hipGetSymbolAddress returns for the current device, never the array's name.
 constexpr size_t NOALLOC_BYTES = OQ_NOALLOC_SCRATCH_BYTES;
-__device__ __align__(256) uint8_t scratch[NOALLOC_BYTES];
+static __device__ __align__(256) uint8_t scratch[NOALLOC_BYTES];
 
 constexpr int MAX_DEVICES = 64;
 std::mutex g_scratch_mu;
