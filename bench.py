@@ -471,7 +471,7 @@ def _time_kron(torch, oq, WL, reps=40, warmup=5):
         e1.record()
         torch.cuda.synchronize()
         t = e0.elapsed_time(e1) / reps  # back-to-back launches
-        nbytes = M * (2 * n + npad * 3 // 4 + 4)  # bf16 in, 6-bit tiled codes out, scale
+        nbytes = M * (2 * n + npad // 2 + 4)  # bf16 in, INT4 codes of the padded width out, scale
         e = {"m": m, "block": b, "n_pad": npad, "rotate_quant_us": round(t * 1e3, 3),
              "rotate_quant_hbm_frac": round(nbytes / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
         if n == 2240:
@@ -528,10 +528,14 @@ def _gpu_state():
 
 
 def _act_bytes(spec, M, K):
+    """Algorithmic bytes of one rotate+quantise launch: the bf16 input, the
+    codes (8-bit, and 6-bit stored one per byte as the W4A6 workload states
+    them; 4-bit two per byte), a float32 scale per token and the float32 mean
+    when centred; MXFP4: E2M1 codes, one E8M0 byte per 32 and the bf16 32 x 32
+    transform of every block, read once."""
     if spec.afmt == 0x104:
-        return M * K * 2 + M * K // 2 + M * K // 32
-    # densely packed codes: 8, 6 or 4 bits each
-    code = {8: M * K, 6: M * K * 3 // 4}.get(spec.afmt, M * K // 2)
+        return M * K * 2 + M * K // 2 + M * K // 32 + (K // 32) * 32 * 32 * 2
+    code = M * K if spec.afmt in (8, 6) else M * K // 2
     return M * K * 2 + code + 4 * M + (4 * M if spec.center else 0)
 
 
