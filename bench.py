@@ -38,10 +38,10 @@ def _src_hash(names):
     return h.hexdigest()[:16]
 
 
-def _traffic(profile_name, src_names):
+def _traffic(profile_name, src_names, profiles_dir=None):
     """HBM bytes per launch from a committed counter summary, if it was taken
     on the current kernel source; otherwise None."""
-    p = os.path.join(ROOT, "profiles", profile_name)
+    p = os.path.join(profiles_dir or os.path.join(ROOT, "profiles"), profile_name)
     if not os.path.exists(p):
         return None
     try:

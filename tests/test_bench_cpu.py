@@ -44,24 +44,14 @@ def test_gemm_operation_counts(cid, N, gops):
     assert round(2.0 * s.M * s.K * N / 1e9, 2 if gops > 1 else 3) == gops
 
 
-def test_traffic_needs_the_current_source(tmp_path, monkeypatch):
-    prof = tmp_path / "profiles"
-    prof.mkdir()
+def test_traffic_needs_the_current_source(tmp_path):
     src = "k_gemm_fp6.hip"
     good = {"source_sha1": bench._src_hash([src]), "hbm_bytes_per_launch": 12345}
-    (prof / "good.json").write_text(json.dumps(good))
-    (prof / "stale.json").write_text(json.dumps({**good, "source_sha1": "0" * 16}))
-    (prof / "broken.json").write_text("{")
-    # the profile folder is looked up under ROOT; the sources stay the repository's
-    real_join = os.path.join
-
-    def join(*parts):
-        if len(parts) >= 2 and parts[0] == bench.ROOT and parts[1] == "profiles":
-            return real_join(str(prof), *parts[2:])
-        return real_join(*parts)
-
-    monkeypatch.setattr(bench.os.path, "join", join)
-    assert bench._traffic("good.json", [src]) == 12345
-    assert bench._traffic("stale.json", [src]) is None
-    assert bench._traffic("broken.json", [src]) is None
-    assert bench._traffic("missing.json", [src]) is None
+    (tmp_path / "good.json").write_text(json.dumps(good))
+    (tmp_path / "stale.json").write_text(json.dumps({**good, "source_sha1": "0" * 16}))
+    (tmp_path / "broken.json").write_text("{")
+    d = str(tmp_path)
+    assert bench._traffic("good.json", [src], d) == 12345
+    assert bench._traffic("stale.json", [src], d) is None
+    assert bench._traffic("broken.json", [src], d) is None
+    assert bench._traffic("missing.json", [src], d) is None
